@@ -1,0 +1,181 @@
+// Prefill attention on gfx950 matrix cores: causal grouped-query attention of
+// M query rows (positions start..start+M-1) over the cached keys 0..pos of one
+// sequence, softmax(q k^T / sqrt(d)) v per head ("LLMs on the ANE", "What's
+// inside": decomposed causal attention; KV head h / G serves query head h).
+//
+// Formulated transposed so that every softmax statistic is lane-local:
+//   S^T = K Q^T      (A = K tile rows = keys, B = Q^T columns = queries)
+//   O^T += V^T P^T   (A = V^T tile rows = channels, B = P^T)
+// With v_mfma_f32_32x32x16_f16 a lane owns one query column, so the running
+// max / sum / rescale of the online softmax need one cross-lane step (the
+// partner half-wave).  The accumulator layout of S^T is reused directly as the
+// B operand of the second product by permuting the key order inside each
+// 16-key step; the V^T tile is read from LDS with the same permutation.
+//
+// Workgroup: 4 waves, each one query head x 32 query rows; the heads of a
+// workgroup share one KV head, so each K / V^T tile (64 keys) is staged in LDS
+// once for all of them.
+#include "common.h"
+#include "kernels.h"
+
+namespace dpk {
+
+namespace {
+
+constexpr int THREADS = 256;
+constexpr int BKV = 64;
+constexpr int D = 128;
+constexpr int KSTR = D + 8;     // halfs per K row in LDS
+constexpr int VSTR = BKV + 8;   // halfs per V^T row in LDS
+constexpr float LOG2E = 1.4426950408889634f;
+
+__global__ __launch_bounds__(THREADS, 2) void attn_prefill_kernel(AttnPrefillArgs a, int heads_per_wg, int rb_per_wg,
+                                                                    int n_rb) {
+  __shared__ __attribute__((aligned(16))) _Float16 Ks[BKV][KSTR];
+  __shared__ __attribute__((aligned(16))) _Float16 Vs[D][VSTR];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int G = a.n_heads / a.n_kv;
+  // longest (latest) row blocks first
+  const int rbw = (n_rb - 1 - (int)blockIdx.x);
+  const int head0 = blockIdx.y * heads_per_wg;
+  const int g = head0 / G;
+  const int head = head0 + wave % heads_per_wg;
+  const int r0 = (rbw * rb_per_wg + wave / heads_per_wg) * 32;  // this wave's first query row
+  const int wg_r1 = min(a.M, (rbw + 1) * rb_per_wg * 32);         // workgroup's last row + 1
+  const int q32 = lane & 31, hh = lane >> 5;
+  const int qrow = r0 + q32;
+  const bool row_ok = qrow < a.M;
+  const int qpos = a.start + (row_ok ? qrow : a.M - 1);
+  const float c = a.scale * LOG2E;
+
+  // Q^T fragments: lane (query q32, k-group hh) holds q[16 s + 8 hh .. +7]
+  f16x8 qf[D / 16];
+  {
+    const _Float16* qp = a.q + ((size_t)(row_ok ? qrow : a.M - 1) * a.n_heads + head) * D;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) qf[s] = *(const f16x8*)(qp + 16 * s + 8 * hh);
+  }
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) o[i][v] = 0.f;
+  float mrun = -INFINITY, lrun = 0.f;
+
+  const _Float16* Kg = (const _Float16*)a.kv.base + kv_slab(a.kv, a.seq, a.layer, 0, g);
+  const _Float16* Vg = (const _Float16*)a.kv.base + kv_slab(a.kv, a.seq, a.layer, 1, g);
+  const int kend = a.start + wg_r1;  // keys [0, kend) are visible to some row here
+  const int wave_kend = a.start + min(a.M, r0 + 32);
+  for (int k0 = 0; k0 < kend; k0 += BKV) {
+    __syncthreads();
+    // stage K [64 keys][128] and V^T [128][64 keys]
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + THREADS * i;  // 0..1023
+      const int kr = idx >> 4, kc = (idx & 15) * 8;
+      const int key = min(k0 + kr, kend - 1);
+      *(u32x4*)&Ks[kr][kc] = *(const u32x4*)(Kg + (size_t)key * D + kc);
+      const int vr = idx >> 3, vc = (idx & 7) * 8;
+      // the V^T row stride (kv.max_seq) is a multiple of 64, so the 8-key
+      // load stays inside the row; keys at or past kend are zeroed (the
+      // cache there may hold any bit pattern, and 0 * NaN would poison O)
+      f16x8 vv = *(const f16x8*)(Vg + (size_t)vr * a.kv.max_seq + k0 + vc);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (k0 + vc + e >= kend) vv[e] = (_Float16)0.f;
+      *(f16x8*)&Vs[vr][vc] = vv;
+    }
+    __syncthreads();
+    if (k0 >= wave_kend) continue;  // every key of this tile is after this wave's rows
+    // S^T for two blocks of 32 keys
+    f32x16 s[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[b][v] = 0.f;
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) {
+        const f16x8 kf = *(const f16x8*)&Ks[b * 32 + q32][16 * st + 8 * hh];
+        s[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[st], s[b], 0, 0, 0);
+      }
+    }
+    // mask + online softmax (log2 domain); lane key index = 8(v/4) + 4hh + v%4
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = k0 + b * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
+        float x = s[b][v] * c;
+        if (key > qpos || key >= kend) x = -INFINITY;
+        s[b][v] = x;
+        tmax = fmaxf(tmax, x);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float mnew = fmaxf(mrun, tmax);
+    const float alpha = (mrun == -INFINITY) ? 0.f : exp2f(mrun - mnew);
+    float psum = 0.f;
+    f16x8 pf[2][2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = (s[b][v] == -INFINITY) ? 0.f : exp2f(s[b][v] - mnew);
+        psum += p;
+        pf[b][v >> 3][v & 7] = (_Float16)p;
+      }
+    psum += __shfl_xor(psum, 32, 64);
+    lrun = lrun * alpha + psum;
+    mrun = mnew;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
+    // O^T += V^T P^T; key slots of k-group hh in step (b, t):
+    //   b*32 + 16t + {4hh..4hh+3, 8+4hh..8+4hh+3}
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int kb = b * 32 + 16 * t + 4 * hh;
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) {
+          const int dr = i * 32 + q32;
+          const u32x2 lo = *(const u32x2*)&Vs[dr][kb];
+          const u32x2 hi = *(const u32x2*)&Vs[dr][kb + 8];
+          const u32x4 vw = {lo.x, lo.y, hi.x, hi.y};
+          o[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vw), pf[b][t], o[i], 0, 0, 0);
+        }
+      }
+  }
+  if (!row_ok) return;
+  const float inv = 1.0f / lrun;
+  _Float16* op = a.out + (size_t)qrow * a.n_heads * D + (size_t)head * D;
+  // O^T block i: channel = 32 i + 8 (v/4) + 4 hh + v%4 for query q32
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+      f16x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = (_Float16)(o[i][4 * v4 + e] * inv);
+      *(f16x4*)(op + 32 * i + 8 * v4 + 4 * hh) = w;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t stream) {
+  if (a.d != D || a.kv.is_f32 || a.kv.max_seq % BKV) return hipErrorInvalidValue;
+  const int G = a.n_heads / a.n_kv;
+  const int hpw = G < 4 ? G : 4;
+  if (G % hpw || 4 % hpw) return hipErrorInvalidValue;
+  const int rbpw = 4 / hpw;
+  const int n_rb = (a.M + 32 * rbpw - 1) / (32 * rbpw);
+  dim3 grid(n_rb, a.n_heads / hpw);
+  hipLaunchKernelGGL(attn_prefill_kernel, grid, dim3(THREADS), 0, stream, a, hpw, rbpw, n_rb);
+  return hipGetLastError();
+}
+
+}  // namespace dpk

@@ -1,0 +1,109 @@
+// Shared device/host definitions for the dpk kernels (gfx950 / CDNA4).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define DPK_DEV __device__ __forceinline__
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+namespace dpk {
+
+// One row of a forward call: the token it embeds, the position it occupies
+// and the KV-cache slot (sequence) it belongs to.  A row attends to every
+// cached key of its sequence at positions <= pos.
+struct RowParam {
+  int32_t token;
+  int32_t pos;
+  int32_t seq;
+  int32_t pad;
+};
+
+// Weight formats of the linear layers.
+enum WFmt : int { W_F32 = 0, W_BF16 = 1, W_Q4 = 2 };
+
+DPK_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+DPK_DEV float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+DPK_DEV float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// round-to-nearest-even fp32 -> bf16 bits (finite inputs)
+DPK_DEV uint32_t f32_to_bf16_bits(float f) {
+  uint32_t b = __float_as_uint(f);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return b >> 16;
+}
+
+// x = hi + lo with hi = bf16(x), lo = bf16(x - hi); |x - hi - lo| <= 2^-17 |x|
+DPK_DEV void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
+  hi = f32_to_bf16_bits(x);
+  float r = x - __uint_as_float(hi << 16);
+  lo = f32_to_bf16_bits(r);
+}
+
+DPK_DEV _Float16 f32_to_f16(float f) { return (_Float16)f; }
+
+// ---------------------------------------------------------------- wave reductions
+DPK_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+DPK_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+// (value, index) max with lowest index on ties
+DPK_DEV void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float ov = __shfl_xor(v, o, 64);
+    int oi = __shfl_xor(i, o, 64);
+    if (ov > v || (ov == v && oi < i)) {
+      v = ov;
+      i = oi;
+    }
+  }
+}
+
+// Block-wide sum over blockDim.x threads (multiple of 64); red has >= 16 floats.
+DPK_DEV float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, nw = blockDim.x >> 6;
+  __syncthreads();
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < nw; ++i) t += red[i];
+  return t;
+}
+
+// Last-arriving-workgroup election.  Every workgroup calls this once after
+// its global writes; exactly one (the last) gets true, and it observes all the
+// other workgroups' writes.  The counter is reset for the next launch.
+DPK_DEV bool last_block_arrive(unsigned* counter, unsigned expected, int* smem_flag) {
+  __threadfence();  // release this thread's global writes at device scope
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned prev = atomicAdd(counter, 1u);
+    int last = (prev == expected - 1);
+    if (last) {
+      atomicExch(counter, 0u);
+    }
+    *smem_flag = last;
+  }
+  __syncthreads();
+  bool last = *smem_flag != 0;
+  if (last) __threadfence();
+  return last;
+}
+
+DPK_DEV float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+}  // namespace dpk

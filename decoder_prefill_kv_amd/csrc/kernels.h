@@ -1,0 +1,146 @@
+// Kernel launch interface of the dpk library (internal; not part of the C ABI).
+#pragma once
+#include "common.h"
+
+namespace dpk {
+
+// KV cache: one slab per (sequence, layer, K|V, kv head).
+//   K   [max_seq][head_dim]   (row per position)
+//   V^T [head_dim][max_seq]   (row per channel, positions contiguous)
+// Element type fp16 (bf16/q4 models) or fp32 (fp32 models).
+struct KVDesc {
+  void* base;
+  int is_f32;
+  int n_layers, n_kv, max_seq, d;
+};
+
+__host__ __device__ inline size_t kv_slab(const KVDesc& kv, int seq, int layer, int which, int head) {
+  return ((((size_t)seq * kv.n_layers + layer) * 2 + which) * kv.n_kv + head) * (size_t)kv.max_seq * kv.d;
+}
+// which = 0: K element (pos, e); which = 1: V element (pos, e)
+__host__ __device__ inline size_t kv_offset(const KVDesc& kv, int seq, int layer, int which, int head,
+                                            int e, int pos) {
+  const size_t s = kv_slab(kv, seq, layer, which, head);
+  return which == 0 ? s + (size_t)pos * kv.d + e : s + (size_t)e * kv.max_seq + pos;
+}
+DPK_DEV void kv_store(const KVDesc& kv, size_t off, float v) {
+  if (kv.is_f32)
+    ((float*)kv.base)[off] = v;
+  else
+    ((_Float16*)kv.base)[off] = (_Float16)v;
+}
+
+enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_HEAD = 4 };
+
+struct SkinnyArgs {
+  int M, K, N;  // activation rows (<=16), input dim, output rows
+  int fmt;      // W_BF16 | W_Q4
+  const void* w[3];         // bf16 [rows][K] or q4 codes uint32 [rows][K/8]
+  const uint16_t* sc[3];    // q4 scales bf16 [rows][K/64]
+  const uint16_t* bi[3];    // q4 biases bf16 [rows][K/64]
+  int seg_end[3];           // cumulative row ends of the stacked segments
+  int seg_rows[3];          // rows of each segment (load clamp)
+  const float* x;
+  int ldx;
+  const float* rs;          // [M] row norm scale or null
+  const uint16_t* gain;     // bf16 [K] or null
+  int ksplit, kchunk, rows_per_wg, n_blocks;
+  float* part;              // [ksplit][M][n_blocks*rows]
+  unsigned* counters;       // [1 + n_blocks], zero between launches
+  int epi;
+  float* out;               // STORE/RESID/SWIGLU/HEAD target
+  int ldo;
+  float* sq;                // RESID: [M][n_blocks]
+  float* rs_out;            // RESID: [M]
+  float eps;
+  // QKV epilogue
+  const RowParam* rows_param;
+  const uint16_t* qn;       // bf16 [d] or null
+  const uint16_t* kn;
+  const float* rope_cos;    // [max_seq][d/2]
+  const float* rope_sin;
+  float* qout;              // [M][n_heads][d]
+  int n_heads, layer;
+  KVDesc kv;
+  // HEAD epilogue
+  float* cand_val;          // [M][n_blocks]
+  int* cand_idx;
+  int* argmax_out;          // [M]
+};
+
+size_t skinny_lds_bytes(int M, int kchunk, int rows, int fmt);
+hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t stream);
+
+// ---- decode attention (split-K over the context, merged in-kernel)
+struct AttnDecodeArgs {
+  int M;                      // rows
+  int n_heads, n_kv, d;
+  const RowParam* rows_param;
+  const float* q;             // [M][n_heads][d] (normed, roped)
+  KVDesc kv;
+  int layer;
+  int chunk;                  // positions per workgroup
+  int max_chunks;             // grid.x
+  float* part;                // [M][n_heads][max_chunks][d + 2]
+  unsigned* counters;         // [M * n_kv]
+  float* out;                 // [M][n_heads*d] fp32
+  float scale;                // 1/sqrt(d)
+};
+hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t stream);
+
+// ---- misc
+hipError_t launch_rope_table(float* cos_t, float* sin_t, int max_seq, int d, double theta,
+                             hipStream_t stream);
+// h[m] = E[token_m] (fp32 / bf16 / q4 table); rs[m] = rsqrt(mean(h^2)+eps) if rs != null
+hipError_t launch_embed(int M, int H, int fmt, const void* table, const uint16_t* sc, const uint16_t* bi,
+                        const RowParam* rp, const int32_t* ids_dev, int vocab, float* h, float* rs,
+                        float eps, int* err_flag, hipStream_t stream);
+// y[m] = x[m] * rsqrt(mean(x^2)+eps) * g, fp16 or fp32 output; g is fp32 or bf16
+hipError_t launch_rmsnorm_rows(int M, int H, const float* x, int ldx, const void* g, int g_is_f32,
+                               float eps, void* y, int y_is_f16, int ldy, hipStream_t stream);
+// prefill: qkv fp32 [M][(Hq+2Hkv)d] -> q (fp16 or fp32 [M][Hq][d]), K/V into the cache
+hipError_t launch_qk_rope_kv(int M, const float* qkv, int n_heads, int n_kv, int d, int qk_norm,
+                             const void* qn, const void* kn, int g_is_f32, float eps,
+                             const float* rope_cos, const float* rope_sin, const RowParam* rp,
+                             void* q_out, int q_is_f16, KVDesc kv, int layer, hipStream_t stream);
+// fp32-weight GEMV / small GEMM for any M (VALU): out[m][n] (=|+=) sum_k W[n][k] x[m][k]
+// mode 0 store, 1 add, 2 swiglu (gate=W, up=W2)
+hipError_t launch_gemv_f32(int M, int N, int K, const float* W, const float* W2, const float* x, int ldx,
+                           float* out, int ldo, int mode, hipStream_t stream);
+// argmax per row over [M][N] logits (lowest index on ties)
+hipError_t launch_argmax_rows(int M, int N, const float* logits, int ld, int* out, hipStream_t stream);
+// residual add out += in
+hipError_t launch_add(int n, const float* in, float* out, hipStream_t stream);
+// bf16 -> fp16 / q4 -> fp16 weight conversion for the prefill GEMM operands
+hipError_t launch_bf16_to_f16(const uint16_t* src, _Float16* dst, size_t n, hipStream_t stream);
+hipError_t launch_q4_to_f16(const uint32_t* codes, const uint16_t* sc, const uint16_t* bi, int rows, int K,
+                            _Float16* dst, hipStream_t stream);
+hipError_t launch_f32_to_f16(const float* src, _Float16* dst, size_t n, hipStream_t stream);
+
+// ---- prefill GEMM (fp16 MFMA): C[m][n] = sum_k A[m][k] B[n][k]
+enum GemmEpi : int { GEMM_STORE_F32 = 0, GEMM_ADD_F32 = 1, GEMM_SWIGLU_F16 = 2 };
+struct GemmArgs {
+  int M, N, K;
+  const _Float16* A; int lda;
+  const _Float16* B; int ldb;     // [N][K]; for SWIGLU rows [0,N) gate, B2 up
+  const _Float16* B2;
+  int epi;
+  float* C; int ldc;              // STORE/ADD
+  _Float16* C16; int ldc16;       // SWIGLU
+};
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+
+// ---- prefill attention (fp16 MFMA, causal over the cache)
+struct AttnPrefillArgs {
+  int M;               // query rows, at positions start..start+M-1 of sequence seq
+  int start, seq;
+  int n_heads, n_kv, d;
+  const _Float16* q;   // [M][n_heads][d]
+  KVDesc kv;
+  int layer;
+  _Float16* out;       // [M][n_heads*d]
+  float scale;
+};
+hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t stream);
+
+}  // namespace dpk

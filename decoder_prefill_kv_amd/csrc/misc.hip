@@ -1,0 +1,279 @@
+// Small kernels of the forward pass: RoPE tables, embedding gather, row
+// RMSNorm, the prefill QK-norm / RoPE / KV-cache write, the fp32-weight GEMV,
+// row argmax and weight-format conversions.
+#include "common.h"
+#include "kernels.h"
+
+namespace dpk {
+
+namespace {
+
+// cos/sin of pos * theta^(-2i/d), evaluated in double on the device, stored fp32.
+__global__ void rope_table_kernel(float* cos_t, float* sin_t, int max_seq, int d, double theta) {
+  const int hd2 = d / 2;
+  const size_t n = (size_t)max_seq * hd2;
+  for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < n; idx += (size_t)gridDim.x * blockDim.x) {
+    const int pos = (int)(idx / hd2), i = (int)(idx % hd2);
+    const double inv = pow(theta, -2.0 * (double)i / (double)d);
+    const double ang = (double)pos * inv;
+    cos_t[idx] = (float)cos(ang);
+    sin_t[idx] = (float)sin(ang);
+  }
+}
+
+// one workgroup per row; token from RowParam (or ids_dev when given)
+__global__ void embed_kernel(int H, int fmt, const void* table, const uint16_t* sc, const uint16_t* bi,
+                             const RowParam* rp, const int32_t* ids_dev, int vocab, float* h, float* rs,
+                             float eps, int* err_flag) {
+  __shared__ float red[32];
+  const int m = blockIdx.x;
+  int tok = ids_dev ? ids_dev[m] : rp[m].token;
+  if (tok < 0 || tok >= vocab) {
+    if (threadIdx.x == 0 && err_flag) atomicOr(err_flag, 1);
+    tok = 0;
+  }
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < H; k += blockDim.x) {
+    float v;
+    if (fmt == W_F32) {
+      v = ((const float*)table)[(size_t)tok * H + k];
+    } else if (fmt == W_BF16) {
+      v = bf16_to_f32(((const uint16_t*)table)[(size_t)tok * H + k]);
+    } else {  // MLX 4-bit: w = s * c + b, group 64 along the row
+      const uint32_t word = ((const uint32_t*)table)[(size_t)tok * (H / 8) + k / 8];
+      const float c = (float)((word >> (4 * (k & 7))) & 0xF);
+      const size_t g = (size_t)tok * (H / 64) + k / 64;
+      v = bf16_to_f32(sc[g]) * c + bf16_to_f32(bi[g]);
+    }
+    h[(size_t)m * H + k] = v;
+    ss += v * v;
+  }
+  if (rs) {
+    ss = block_sum(ss, red);
+    if (threadIdx.x == 0) rs[m] = rsqrtf(ss / (float)H + eps);
+  }
+}
+
+__global__ void rmsnorm_rows_kernel(int H, const float* x, int ldx, const void* g, int g_is_f32, float eps,
+                                    void* y, int y_is_f16, int ldy) {
+  __shared__ float red[32];
+  const int m = blockIdx.x;
+  const float* xr = x + (size_t)m * ldx;
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < H; k += blockDim.x) ss += xr[k] * xr[k];
+  ss = block_sum(ss, red);
+  const float r = rsqrtf(ss / (float)H + eps);
+  for (int k = threadIdx.x; k < H; k += blockDim.x) {
+    const float gk = g_is_f32 ? ((const float*)g)[k] : bf16_to_f32(((const uint16_t*)g)[k]);
+    const float v = xr[k] * r * gk;
+    if (y_is_f16)
+      ((_Float16*)y)[(size_t)m * ldy + k] = (_Float16)v;
+    else
+      ((float*)y)[(size_t)m * ldy + k] = v;
+  }
+}
+
+// grid (M, n_heads + 2*n_kv); one workgroup of 64 threads per (row, head)
+__global__ void qk_rope_kv_kernel(const float* qkv, int n_heads, int n_kv, int d, int qk_norm, const void* qn,
+                                  const void* kn, int g_is_f32, float eps, const float* rope_cos,
+                                  const float* rope_sin, const RowParam* rp, void* q_out, int q_is_f16,
+                                  KVDesc kv, int layer) {
+  const int m = blockIdx.x, hh = blockIdx.y, lane = threadIdx.x;
+  const int ld = (n_heads + 2 * n_kv) * d;
+  const float* src = qkv + (size_t)m * ld + (size_t)hh * d;
+  const RowParam r = rp[m];
+  const int hd2 = d / 2;
+  if (hh >= n_heads + n_kv) {  // v head -> V^T slab
+    const int vh = hh - n_heads - n_kv;
+    for (int e = lane; e < d; e += 64) kv_store(kv, kv_offset(kv, r.seq, layer, 1, vh, e, r.pos), src[e]);
+    return;
+  }
+  const bool is_q = hh < n_heads;
+  float scale = 1.f;
+  if (qk_norm) {
+    float ss = 0.f;
+    for (int e = lane; e < d; e += 64) ss += src[e] * src[e];
+    ss = wave_sum(ss);
+    scale = rsqrtf(ss / (float)d + eps);
+  }
+  const void* g = is_q ? qn : kn;
+  for (int e = lane; e < hd2; e += 64) {
+    float x1 = src[e] * scale, x2 = src[e + hd2] * scale;
+    if (qk_norm && g) {
+      if (g_is_f32) {
+        x1 *= ((const float*)g)[e];
+        x2 *= ((const float*)g)[e + hd2];
+      } else {
+        x1 *= bf16_to_f32(((const uint16_t*)g)[e]);
+        x2 *= bf16_to_f32(((const uint16_t*)g)[e + hd2]);
+      }
+    }
+    const float c = rope_cos[(size_t)r.pos * hd2 + e], s = rope_sin[(size_t)r.pos * hd2 + e];
+    const float y1 = x1 * c - x2 * s, y2 = x2 * c + x1 * s;
+    if (is_q) {
+      const size_t o = ((size_t)m * n_heads + hh) * d;
+      if (q_is_f16) {
+        ((_Float16*)q_out)[o + e] = (_Float16)y1;
+        ((_Float16*)q_out)[o + e + hd2] = (_Float16)y2;
+      } else {
+        ((float*)q_out)[o + e] = y1;
+        ((float*)q_out)[o + e + hd2] = y2;
+      }
+    } else {
+      const int kh = hh - n_heads;
+      const size_t o = kv_offset(kv, r.seq, layer, 0, kh, 0, r.pos);
+      kv_store(kv, o + e, y1);
+      kv_store(kv, o + e + hd2, y2);
+    }
+  }
+}
+
+// fp32 weights: one wave per output n, all M rows; mode 0 store, 1 add, 2 swiglu
+__global__ void gemv_f32_kernel(int M, int N, int K, const float* W, const float* W2, const float* x, int ldx,
+                                float* out, int ldo, int mode) {
+  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (wave >= N) return;
+  const float* w = W + (size_t)wave * K;
+  const float* w2 = W2 ? W2 + (size_t)wave * K : nullptr;
+  for (int m = 0; m < M; ++m) {
+    const float* xr = x + (size_t)m * ldx;
+    float s = 0.f, s2 = 0.f;
+    for (int k = lane; k < K; k += 64) {
+      s += w[k] * xr[k];
+      if (mode == 2) s2 += w2[k] * xr[k];
+    }
+    s = wave_sum(s);
+    if (mode == 2) s2 = wave_sum(s2);
+    if (lane == 0) {
+      float* o = out + (size_t)m * ldo + wave;
+      if (mode == 0) *o = s;
+      else if (mode == 1) *o += s;
+      else *o = silu(s) * s2;
+    }
+  }
+}
+
+__global__ void argmax_rows_kernel(int N, const float* logits, int ld, int* out) {
+  __shared__ float sv[16];
+  __shared__ int si[16];
+  const int m = blockIdx.x;
+  const float* r = logits + (size_t)m * ld;
+  float best = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int n = threadIdx.x; n < N; n += blockDim.x) {
+    const float v = r[n];
+    if (v > best || (v == best && n < bi)) { best = v; bi = n; }
+  }
+  wave_argmax(best, bi);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { sv[w] = best; si[w] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    best = sv[0];
+    bi = si[0];
+    for (int i = 1; i < (int)(blockDim.x >> 6); ++i)
+      if (sv[i] > best || (sv[i] == best && si[i] < bi)) { best = sv[i]; bi = si[i]; }
+    out[m] = bi;
+  }
+}
+
+__global__ void add_kernel(int n, const float* in, float* out) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) out[i] += in[i];
+}
+
+__global__ void bf16_to_f16_kernel(const uint16_t* src, _Float16* dst, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = (_Float16)bf16_to_f32(src[i]);
+}
+
+__global__ void f32_to_f16_kernel(const float* src, _Float16* dst, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = (_Float16)src[i];
+}
+
+__global__ void q4_to_f16_kernel(const uint32_t* codes, const uint16_t* sc, const uint16_t* bi, int rows, int K,
+                                 _Float16* dst) {
+  const size_t n = (size_t)rows * K;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    const size_t r = i / K;
+    const int k = (int)(i % K);
+    const uint32_t word = codes[r * (K / 8) + k / 8];
+    const float c = (float)((word >> (4 * (k & 7))) & 0xF);
+    const size_t g = r * (K / 64) + k / 64;
+    dst[i] = (_Float16)(bf16_to_f32(sc[g]) * c + bf16_to_f32(bi[g]));
+  }
+}
+
+inline int grid_for(size_t n, int threads) {
+  size_t b = (n + threads - 1) / threads;
+  return (int)(b > 65536 ? 65536 : (b < 1 ? 1 : b));
+}
+
+}  // namespace
+
+hipError_t launch_rope_table(float* cos_t, float* sin_t, int max_seq, int d, double theta, hipStream_t stream) {
+  hipLaunchKernelGGL(rope_table_kernel, dim3(grid_for((size_t)max_seq * d / 2, 256)), dim3(256), 0, stream, cos_t,
+                     sin_t, max_seq, d, theta);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed(int M, int H, int fmt, const void* table, const uint16_t* sc, const uint16_t* bi,
+                        const RowParam* rp, const int32_t* ids_dev, int vocab, float* h, float* rs, float eps,
+                        int* err_flag, hipStream_t stream) {
+  hipLaunchKernelGGL(embed_kernel, dim3(M), dim3(256), 0, stream, H, fmt, table, sc, bi, rp, ids_dev, vocab, h, rs,
+                     eps, err_flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_rows(int M, int H, const float* x, int ldx, const void* g, int g_is_f32, float eps,
+                               void* y, int y_is_f16, int ldy, hipStream_t stream) {
+  hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(M), dim3(256), 0, stream, H, x, ldx, g, g_is_f32, eps, y, y_is_f16,
+                     ldy);
+  return hipGetLastError();
+}
+
+hipError_t launch_qk_rope_kv(int M, const float* qkv, int n_heads, int n_kv, int d, int qk_norm, const void* qn,
+                             const void* kn, int g_is_f32, float eps, const float* rope_cos, const float* rope_sin,
+                             const RowParam* rp, void* q_out, int q_is_f16, KVDesc kv, int layer,
+                             hipStream_t stream) {
+  hipLaunchKernelGGL(qk_rope_kv_kernel, dim3(M, n_heads + 2 * n_kv), dim3(64), 0, stream, qkv, n_heads, n_kv, d,
+                     qk_norm, qn, kn, g_is_f32, eps, rope_cos, rope_sin, rp, q_out, q_is_f16, kv, layer);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_f32(int M, int N, int K, const float* W, const float* W2, const float* x, int ldx,
+                           float* out, int ldo, int mode, hipStream_t stream) {
+  hipLaunchKernelGGL(gemv_f32_kernel, dim3((N + 3) / 4), dim3(256), 0, stream, M, N, K, W, W2, x, ldx, out, ldo,
+                     mode);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax_rows(int M, int N, const float* logits, int ld, int* out, hipStream_t stream) {
+  hipLaunchKernelGGL(argmax_rows_kernel, dim3(M), dim3(1024), 0, stream, N, logits, ld, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_add(int n, const float* in, float* out, hipStream_t stream) {
+  hipLaunchKernelGGL(add_kernel, dim3(grid_for(n, 256)), dim3(256), 0, stream, n, in, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_bf16_to_f16(const uint16_t* src, _Float16* dst, size_t n, hipStream_t stream) {
+  hipLaunchKernelGGL(bf16_to_f16_kernel, dim3(grid_for(n, 256)), dim3(256), 0, stream, src, dst, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_f32_to_f16(const float* src, _Float16* dst, size_t n, hipStream_t stream) {
+  hipLaunchKernelGGL(f32_to_f16_kernel, dim3(grid_for(n, 256)), dim3(256), 0, stream, src, dst, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_q4_to_f16(const uint32_t* codes, const uint16_t* sc, const uint16_t* bi, int rows, int K,
+                            _Float16* dst, hipStream_t stream) {
+  hipLaunchKernelGGL(q4_to_f16_kernel, dim3(grid_for((size_t)rows * K, 256)), dim3(256), 0, stream, codes, sc, bi,
+                     rows, K, dst);
+  return hipGetLastError();
+}
+
+}  // namespace dpk

@@ -1,0 +1,786 @@
+// C-ABI runtime: configuration and weight validation, workspace carving and
+// the per-call launch sequences of prefill, decode and verify.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <map>
+#include <string>
+#include <vector>
+
+#include "../../include/dpk.h"
+#include "common.h"
+#include "kernels.h"
+
+using namespace dpk;
+
+namespace {
+
+thread_local std::string g_err;
+
+dpk_status fail(dpk_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+constexpr int SKINNY_MAX = 16;  // rows handled by the weight-streaming path
+constexpr int KSPLIT_MAX = 16;  // K splits of one weight-streaming launch
+constexpr int ALIGN = 256;
+
+struct LinearW {
+  const void* w = nullptr;        // bf16 / f32 data or q4 codes
+  const uint16_t* sc = nullptr;   // q4
+  const uint16_t* bi = nullptr;   // q4
+  int rows = 0, cols = 0;
+};
+
+struct LayerW {
+  LinearW q, k, v, o, gate, up, down;
+  const void* in_norm = nullptr;
+  const void* post_norm = nullptr;
+  const void* q_norm = nullptr;
+  const void* k_norm = nullptr;
+  // prefill operands (fp16, in the prep buffer)
+  _Float16 *qkv16 = nullptr, *o16 = nullptr, *gate16 = nullptr, *up16 = nullptr, *down16 = nullptr;
+};
+
+}  // namespace
+
+struct dpk_model {
+  dpk_config cfg;
+  int fmt = 0;
+  int Nqkv = 0;
+  std::vector<LayerW> layers;
+  LinearW embed, head;
+  const void* final_norm = nullptr;
+  bool bound = false, loaded = false, failed = false;
+  // caller buffers
+  void* kv = nullptr;
+  void* scratch = nullptr;
+  void* prep = nullptr;
+  KVDesc kvd{};
+  // carved scratch
+  float *rope_cos = nullptr, *rope_sin = nullptr;
+  RowParam* rows_dev = nullptr;
+  float *h = nullptr, *rs = nullptr, *qkv = nullptr, *y32 = nullptr, *qbuf = nullptr, *attn_o = nullptr,
+        *act = nullptr, *part = nullptr, *sink = nullptr, *sq = nullptr, *cand_val = nullptr, *attn_part = nullptr;
+  int* cand_idx = nullptr;
+  _Float16 *y16 = nullptr, *q16 = nullptr, *o16 = nullptr, *act16 = nullptr;
+  unsigned *counters = nullptr, *attn_counters = nullptr;
+  int* err_flag = nullptr;
+  int* argmax_sink = nullptr;
+  int rows_f32 = 0;       // rows of the fp32 activation buffers
+  int attn_chunks_cap = 0;
+  size_t part_floats = 0;
+  // pinned staging for row parameters
+  static constexpr int NSTAGE = 4;
+  RowParam* stage[NSTAGE] = {};
+  hipEvent_t stage_ev[NSTAGE] = {};
+  bool stage_used[NSTAGE] = {};
+  int stage_next = 0;
+  int32_t* acc_host = nullptr;  // pinned readback for verify
+  std::vector<int32_t> seq_len;
+};
+
+namespace {
+
+size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+struct ScratchLayout {
+  size_t rope_cos, rope_sin, rows, h, rs, qkv, y32, qbuf, attn_o, act, part, sink, sq, cand_val, cand_idx, attn_part,
+      y16, q16, o16, act16, counters, attn_counters, err, argmax_sink, total;
+  int rows_f32, attn_chunks_cap;
+  size_t part_floats;
+};
+
+int nblocks_max(const dpk_config& c) {
+  const int Nqkv = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
+  int nb = 0;
+  for (int n : {Nqkv / 64, c.hidden / 64, c.intermediate / 32, (c.vocab + 63) / 64}) nb = n > nb ? n : nb;
+  return nb;
+}
+
+ScratchLayout scratch_layout(const dpk_config& c) {
+  ScratchLayout L{};
+  const size_t R = c.max_rows, H = c.hidden, I = c.intermediate, d = c.head_dim;
+  const size_t Nqkv = (c.n_heads + 2 * c.n_kv_heads) * d, Qd = (size_t)c.n_heads * d;
+  const bool f32 = c.weight_format == DPK_FMT_F32;
+  const size_t Rf = f32 ? R : SKINNY_MAX;
+  L.rows_f32 = (int)Rf;
+  L.attn_chunks_cap = (c.max_seq + 63) / 64;
+  const size_t nbm = nblocks_max(c);
+  size_t nmax = Nqkv;
+  if (2 * I > nmax) nmax = 2 * I;
+  if (H > nmax) nmax = H;
+  if ((size_t)c.vocab > nmax) nmax = c.vocab;
+  L.part_floats = (size_t)KSPLIT_MAX * SKINNY_MAX * nmax;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = up(o + bytes);
+    return at;
+  };
+  L.rope_cos = take((size_t)c.max_seq * d / 2 * 4);
+  L.rope_sin = take((size_t)c.max_seq * d / 2 * 4);
+  L.rows = take(R * sizeof(RowParam));
+  L.h = take(R * H * 4);
+  L.rs = take(R * 4);
+  L.qkv = take(R * Nqkv * 4);
+  L.y32 = take(Rf * H * 4);
+  L.qbuf = take(Rf * Qd * 4);
+  L.attn_o = take(Rf * Qd * 4);
+  L.act = take(Rf * I * 4);
+  L.part = take(L.part_floats * 4);
+  L.sink = take((size_t)SKINNY_MAX * c.vocab * 4);
+  L.sq = take(SKINNY_MAX * nbm * 4);
+  L.cand_val = take(SKINNY_MAX * nbm * 4);
+  L.cand_idx = take(SKINNY_MAX * nbm * 4);
+  L.attn_part = take((size_t)(f32 ? R : SKINNY_MAX) * c.n_heads * L.attn_chunks_cap * (d + 2) * 4);
+  L.y16 = take(f32 ? 0 : R * H * 2);
+  L.q16 = take(f32 ? 0 : R * Qd * 2);
+  L.o16 = take(f32 ? 0 : R * Qd * 2);
+  L.act16 = take(f32 ? 0 : R * I * 2);
+  L.counters = take((1 + nbm) * 4);
+  L.attn_counters = take((size_t)(f32 ? R : SKINNY_MAX) * c.n_kv_heads * 4);
+  L.err = take(4);
+  L.argmax_sink = take(SKINNY_MAX * 4);
+  L.total = o;
+  return L;
+}
+
+size_t prep_bytes(const dpk_config& c) {
+  if (c.weight_format == DPK_FMT_F32) return 0;
+  const size_t H = c.hidden, I = c.intermediate, d = c.head_dim;
+  const size_t Nqkv = (c.n_heads + 2 * c.n_kv_heads) * d, Qd = (size_t)c.n_heads * d;
+  size_t per = up(Nqkv * H * 2) + up(H * Qd * 2) + 2 * up(I * H * 2) + up(H * I * 2);
+  return per * c.n_layers;
+}
+
+// positions per KV slab row: max_seq rounded up to a multiple of 64 so that
+// 64-key tiles never leave a row
+int kv_seq(const dpk_config& c) { return (c.max_seq + 63) / 64 * 64; }
+
+size_t kv_bytes(const dpk_config& c) {
+  const size_t elt = c.weight_format == DPK_FMT_F32 ? 4 : 2;
+  return (size_t)c.max_batch * c.n_layers * 2 * c.n_kv_heads * kv_seq(c) * c.head_dim * elt;
+}
+
+#define HIP_TRY(expr)                                                                  \
+  do {                                                                                 \
+    hipError_t _e = (expr);                                                            \
+    if (_e != hipSuccess) {                                                            \
+      md->failed = true;                                                               \
+      return fail(DPK_EHIP, "%s failed: %s (%s:%d)", #expr, hipGetErrorString(_e), __FILE__, __LINE__); \
+    }                                                                                  \
+  } while (0)
+
+dpk_status check_ready(const dpk_model* md) {
+  if (!md) return fail(DPK_EINVAL, "null model");
+  if (md->failed) return fail(DPK_ESTATE, "model is in a failed state after an earlier HIP error");
+  if (!md->bound) return fail(DPK_ESTATE, "workspace not bound (call dpk_bind_workspace)");
+  if (!md->loaded) return fail(DPK_ESTATE, "weights not loaded (call dpk_load_weights)");
+  return DPK_OK;
+}
+
+// Stage row parameters into pinned memory and enqueue the upload.
+dpk_status upload_rows(dpk_model* md, const RowParam* rows, int n, hipStream_t st) {
+  int s = md->stage_next;
+  md->stage_next = (s + 1) % dpk_model::NSTAGE;
+  if (md->stage_used[s]) HIP_TRY(hipEventSynchronize(md->stage_ev[s]));
+  memcpy(md->stage[s], rows, sizeof(RowParam) * n);
+  HIP_TRY(hipMemcpyAsync(md->rows_dev, md->stage[s], sizeof(RowParam) * n, hipMemcpyHostToDevice, st));
+  HIP_TRY(hipEventRecord(md->stage_ev[s], st));
+  md->stage_used[s] = true;
+  return DPK_OK;
+}
+
+// Smallest K split that fits the activation chunk in 64 KB of LDS, grown until
+// the launch has ~1024 workgroups (4 per compute unit).
+int choose_ksplit(int K, int nblocks, int M, int rows, int fmt) {
+  int best = 0;
+  for (int ks = 1; ks <= KSPLIT_MAX; ks *= 2) {
+    if (K % (ks * 256) != 0) break;
+    const int kchunk = K / ks;
+    if (skinny_lds_bytes(M, kchunk, rows, fmt) > 64 * 1024) continue;
+    best = ks;
+    if ((long)nblocks * ks >= 1024) break;
+  }
+  return best;
+}
+
+// One weight-streaming GEMV launch (M <= 16).
+dpk_status skinny(dpk_model* md, int M, const float* x, int ldx, const float* rs, const void* gain,
+                  const LinearW* segs, int nseg, int epi, float* out, int ldo, hipStream_t st,
+                  int layer = 0) {
+  const dpk_config& c = md->cfg;
+  SkinnyArgs a{};
+  a.M = M;
+  a.K = segs[0].cols;
+  a.fmt = md->fmt == DPK_FMT_Q4G64 ? W_Q4 : W_BF16;
+  int n = 0;
+  for (int i = 0; i < 3; ++i) {
+    const LinearW& s = segs[i < nseg ? i : nseg - 1];
+    a.w[i] = s.w;
+    a.sc[i] = s.sc;
+    a.bi[i] = s.bi;
+    if (i < nseg) n += s.rows;
+    a.seg_end[i] = n;
+    a.seg_rows[i] = s.rows;
+  }
+  a.N = (epi == EPI_SWIGLU) ? segs[0].rows : n;
+  a.rows_per_wg = (epi == EPI_QKV) ? c.head_dim : 64;
+  const int rows_total = (epi == EPI_SWIGLU) ? 2 * segs[0].rows : n;
+  a.n_blocks = (rows_total + a.rows_per_wg - 1) / a.rows_per_wg;
+  if (rows_total % a.rows_per_wg != 0)
+    return fail(DPK_EINVAL, "output rows %d not a multiple of %d", rows_total, a.rows_per_wg);
+  a.ksplit = choose_ksplit(a.K, a.n_blocks, M, a.rows_per_wg, a.fmt);
+  if (a.ksplit == 0) return fail(DPK_EINVAL, "no K split for K=%d M=%d", a.K, M);
+  a.kchunk = a.K / a.ksplit;
+  if ((size_t)a.ksplit * M * a.n_blocks * a.rows_per_wg > md->part_floats)
+    return fail(DPK_EINVAL, "partial buffer too small");
+  a.x = x;
+  a.ldx = ldx;
+  a.rs = rs;
+  a.gain = (const uint16_t*)gain;
+  a.part = md->part;
+  a.counters = md->counters;
+  a.epi = epi;
+  a.out = out;
+  a.ldo = ldo;
+  a.sq = md->sq;
+  a.rs_out = md->rs;
+  a.eps = c.rms_eps;
+  a.rows_param = md->rows_dev;
+  a.rope_cos = md->rope_cos;
+  a.rope_sin = md->rope_sin;
+  a.qout = md->qbuf;
+  a.n_heads = c.n_heads;
+  a.layer = layer;
+  a.kv = md->kvd;
+  a.cand_val = md->cand_val;
+  a.cand_idx = md->cand_idx;
+  if (epi == EPI_QKV) {
+    const LayerW& L = md->layers[layer];
+    a.qn = c.qk_norm ? (const uint16_t*)L.q_norm : nullptr;
+    a.kn = c.qk_norm ? (const uint16_t*)L.k_norm : nullptr;
+    if (!c.qk_norm) return fail(DPK_EINVAL, "fused QKV epilogue needs qk_norm");
+  }
+  HIP_TRY(launch_skinny(a, st));
+  return DPK_OK;
+}
+
+dpk_status attn_decode(dpk_model* md, int M, int max_ctx, const float* q, float* out, int layer, hipStream_t st) {
+  const dpk_config& c = md->cfg;
+  AttnDecodeArgs a{};
+  a.M = M;
+  a.n_heads = c.n_heads;
+  a.n_kv = c.n_kv_heads;
+  a.d = c.head_dim;
+  a.rows_param = md->rows_dev;
+  a.q = q;
+  a.kv = md->kvd;
+  a.layer = layer;
+  int target = 512 / (M * c.n_kv_heads);
+  if (target < 1) target = 1;
+  int subs = (max_ctx + 63) / 64;
+  int per = (subs + target - 1) / target;
+  if (per < 1) per = 1;
+  a.chunk = 64 * per;
+  a.max_chunks = (max_ctx + a.chunk - 1) / a.chunk;
+  if (a.max_chunks > md->attn_chunks_cap) return fail(DPK_EINVAL, "attention chunk cap");
+  a.part = md->attn_part;
+  a.counters = md->attn_counters;
+  a.out = out;
+  a.scale = 1.0f / sqrtf((float)c.head_dim);
+  HIP_TRY(launch_attn_decode(a, st));
+  return DPK_OK;
+}
+
+// Final norm + lm_head + greedy argmax for `rows` rows of x (weight-streaming
+// path).  x' = x * rs * gain; logits go to the caller's buffer or a sink.
+dpk_status head(dpk_model* md, int rows, const float* x, const float* rs, const void* gain, float* logits,
+                int32_t* argmax, hipStream_t st) {
+  const dpk_config& c = md->cfg;
+  const int H = c.hidden;
+  const LinearW& hw = md->head;
+  SkinnyArgs h{};
+  h.M = rows;
+  h.K = H;
+  h.fmt = md->fmt == DPK_FMT_Q4G64 ? W_Q4 : W_BF16;
+  for (int i = 0; i < 3; ++i) {
+    h.w[i] = hw.w;
+    h.sc[i] = hw.sc;
+    h.bi[i] = hw.bi;
+    h.seg_end[i] = hw.rows;
+    h.seg_rows[i] = hw.rows;
+  }
+  h.N = hw.rows;
+  h.rows_per_wg = 64;
+  h.n_blocks = (hw.rows + 63) / 64;
+  h.ksplit = choose_ksplit(H, h.n_blocks, rows, 64, h.fmt);
+  if (h.ksplit == 0) return fail(DPK_EINVAL, "no K split for the head");
+  h.kchunk = H / h.ksplit;
+  if ((size_t)h.ksplit * rows * h.n_blocks * 64 > md->part_floats) return fail(DPK_EINVAL, "partial buffer too small");
+  h.x = x;
+  h.ldx = H;
+  h.rs = rs;
+  h.gain = (const uint16_t*)gain;
+  h.part = md->part;
+  h.counters = md->counters;
+  h.epi = EPI_HEAD;
+  h.out = logits ? logits : md->sink;
+  h.ldo = c.vocab;
+  h.eps = c.rms_eps;
+  h.cand_val = md->cand_val;
+  h.cand_idx = md->cand_idx;
+  h.argmax_out = argmax ? argmax : md->argmax_sink;
+  HIP_TRY(launch_skinny(h, st));
+  return DPK_OK;
+}
+
+// Rows whose parameters are already in md->rows_dev.  M <= 16, bf16 / q4
+// weights.  Writes logits/argmax for rows [head_r0, head_r0 + head_n).
+dpk_status forward_skinny(dpk_model* md, int M, int max_ctx, const int32_t* ids_dev, int head_r0, int head_n,
+                          float* logits, int32_t* argmax, hipStream_t st) {
+  const dpk_config& c = md->cfg;
+  const int H = c.hidden;
+  HIP_TRY(launch_embed(M, H, md->fmt == DPK_FMT_Q4G64 ? W_Q4 : W_BF16, md->embed.w, md->embed.sc, md->embed.bi,
+                       md->rows_dev, ids_dev, c.vocab, md->h, md->rs, c.rms_eps, md->err_flag, st));
+  dpk_status s;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const LayerW& L = md->layers[l];
+    LinearW qkv[3] = {L.q, L.k, L.v};
+    if ((s = skinny(md, M, md->h, H, md->rs, L.in_norm, qkv, 3, EPI_QKV, nullptr, 0, st, l))) return s;
+    if ((s = attn_decode(md, M, max_ctx, md->qbuf, md->attn_o, l, st))) return s;
+    if ((s = skinny(md, M, md->attn_o, c.n_heads * c.head_dim, nullptr, nullptr, &L.o, 1, EPI_RESID, md->h, H, st)))
+      return s;
+    LinearW gu[2] = {L.gate, L.up};
+    if ((s = skinny(md, M, md->h, H, md->rs, L.post_norm, gu, 2, EPI_SWIGLU, md->act, c.intermediate, st))) return s;
+    if ((s = skinny(md, M, md->act, c.intermediate, nullptr, nullptr, &L.down, 1, EPI_RESID, md->h, H, st)))
+      return s;
+  }
+  if (head_n > 0) return head(md, head_n, md->h + (size_t)head_r0 * H, md->rs + head_r0, md->final_norm, logits, argmax, st);
+  return DPK_OK;
+}
+
+// Prefill block of M > 16 rows of one sequence at positions start..start+M-1
+// (bf16 / q4 models): fp16 MFMA GEMMs over the prep copy of the weights,
+// flash attention over the cache, then the head on the last row.
+dpk_status forward_gemm(dpk_model* md, int M, int start, int seq, bool want_head, float* logits, int32_t* argmax,
+                        hipStream_t st) {
+  const dpk_config& c = md->cfg;
+  const int H = c.hidden, I = c.intermediate, d = c.head_dim, Qd = c.n_heads * d;
+  HIP_TRY(launch_embed(M, H, md->fmt == DPK_FMT_Q4G64 ? W_Q4 : W_BF16, md->embed.w, md->embed.sc, md->embed.bi,
+                       md->rows_dev, nullptr, c.vocab, md->h, nullptr, c.rms_eps, md->err_flag, st));
+  for (int l = 0; l < c.n_layers; ++l) {
+    const LayerW& L = md->layers[l];
+    HIP_TRY(launch_rmsnorm_rows(M, H, md->h, H, L.in_norm, 0, c.rms_eps, md->y16, 1, H, st));
+    GemmArgs g{};
+    g.M = M; g.N = md->Nqkv; g.K = H;
+    g.A = md->y16; g.lda = H; g.B = L.qkv16; g.ldb = H;
+    g.epi = GEMM_STORE_F32; g.C = md->qkv; g.ldc = md->Nqkv;
+    HIP_TRY(launch_gemm(g, st));
+    HIP_TRY(launch_qk_rope_kv(M, md->qkv, c.n_heads, c.n_kv_heads, d, c.qk_norm, L.q_norm, L.k_norm, 0, c.rms_eps,
+                              md->rope_cos, md->rope_sin, md->rows_dev, md->q16, 1, md->kvd, l, st));
+    AttnPrefillArgs at{};
+    at.M = M; at.start = start; at.seq = seq;
+    at.n_heads = c.n_heads; at.n_kv = c.n_kv_heads; at.d = d;
+    at.q = md->q16; at.kv = md->kvd; at.layer = l; at.out = md->o16;
+    at.scale = 1.0f / sqrtf((float)d);
+    HIP_TRY(launch_attn_prefill(at, st));
+    g = GemmArgs{};
+    g.M = M; g.N = H; g.K = Qd;
+    g.A = md->o16; g.lda = Qd; g.B = L.o16; g.ldb = Qd;
+    g.epi = GEMM_ADD_F32; g.C = md->h; g.ldc = H;
+    HIP_TRY(launch_gemm(g, st));
+    HIP_TRY(launch_rmsnorm_rows(M, H, md->h, H, L.post_norm, 0, c.rms_eps, md->y16, 1, H, st));
+    g = GemmArgs{};
+    g.M = M; g.N = I; g.K = H;
+    g.A = md->y16; g.lda = H; g.B = L.gate16; g.B2 = L.up16; g.ldb = H;
+    g.epi = GEMM_SWIGLU_F16; g.C16 = md->act16; g.ldc16 = I;
+    HIP_TRY(launch_gemm(g, st));
+    g = GemmArgs{};
+    g.M = M; g.N = H; g.K = I;
+    g.A = md->act16; g.lda = I; g.B = L.down16; g.ldb = I;
+    g.epi = GEMM_ADD_F32; g.C = md->h; g.ldc = H;
+    HIP_TRY(launch_gemm(g, st));
+  }
+  if (!want_head) return DPK_OK;
+  // final RMSNorm of the last row (fp32), then the weight-streaming head
+  HIP_TRY(launch_rmsnorm_rows(1, H, md->h + (size_t)(M - 1) * H, H, md->final_norm, 0, c.rms_eps, md->y32, 0, H, st));
+  return head(md, 1, md->y32, nullptr, nullptr, logits, argmax, st);
+}
+
+// fp32 weights (any M <= max_rows): plain kernels.
+dpk_status forward_f32(dpk_model* md, int M, int max_ctx, const int32_t* ids_dev, int head_r0, int head_n,
+                       float* logits, int32_t* argmax, hipStream_t st) {
+  const dpk_config& c = md->cfg;
+  const int H = c.hidden, d = c.head_dim, Qd = c.n_heads * d, KVd = c.n_kv_heads * d;
+  const int Nqkv = Qd + 2 * KVd;
+  HIP_TRY(launch_embed(M, H, W_F32, md->embed.w, nullptr, nullptr, md->rows_dev, ids_dev, c.vocab, md->h, nullptr,
+                       c.rms_eps, md->err_flag, st));
+  for (int l = 0; l < c.n_layers; ++l) {
+    const LayerW& L = md->layers[l];
+    HIP_TRY(launch_rmsnorm_rows(M, H, md->h, H, L.in_norm, 1, c.rms_eps, md->y32, 0, H, st));
+    HIP_TRY(launch_gemv_f32(M, Qd, H, (const float*)L.q.w, nullptr, md->y32, H, md->qkv, Nqkv, 0, st));
+    HIP_TRY(launch_gemv_f32(M, KVd, H, (const float*)L.k.w, nullptr, md->y32, H, md->qkv + Qd, Nqkv, 0, st));
+    HIP_TRY(launch_gemv_f32(M, KVd, H, (const float*)L.v.w, nullptr, md->y32, H, md->qkv + Qd + KVd, Nqkv, 0, st));
+    HIP_TRY(launch_qk_rope_kv(M, md->qkv, c.n_heads, c.n_kv_heads, d, c.qk_norm, L.q_norm, L.k_norm, 1, c.rms_eps,
+                              md->rope_cos, md->rope_sin, md->rows_dev, md->qbuf, 0, md->kvd, l, st));
+    dpk_status s = attn_decode(md, M, max_ctx, md->qbuf, md->attn_o, l, st);
+    if (s) return s;
+    HIP_TRY(launch_gemv_f32(M, H, Qd, (const float*)L.o.w, nullptr, md->attn_o, Qd, md->h, H, 1, st));
+    HIP_TRY(launch_rmsnorm_rows(M, H, md->h, H, L.post_norm, 1, c.rms_eps, md->y32, 0, H, st));
+    HIP_TRY(launch_gemv_f32(M, c.intermediate, H, (const float*)L.gate.w, (const float*)L.up.w, md->y32, H, md->act,
+                            c.intermediate, 2, st));
+    HIP_TRY(launch_gemv_f32(M, H, c.intermediate, (const float*)L.down.w, nullptr, md->act, c.intermediate, md->h, H,
+                            1, st));
+  }
+  if (head_n > 0) {
+    HIP_TRY(launch_rmsnorm_rows(head_n, H, md->h + (size_t)head_r0 * H, H, md->final_norm, 1, c.rms_eps, md->y32, 0,
+                                H, st));
+    float* dst = logits ? logits : md->sink;
+    HIP_TRY(launch_gemv_f32(head_n, c.vocab, H, (const float*)md->head.w, nullptr, md->y32, H, dst, c.vocab, 0, st));
+    if (argmax) HIP_TRY(launch_argmax_rows(head_n, c.vocab, dst, c.vocab, argmax, st));
+  }
+  return DPK_OK;
+}
+
+// Rows already uploaded; pick the path by format and row count.
+dpk_status forward_rows(dpk_model* md, int M, int max_ctx, const int32_t* ids_dev, int head_r0, int head_n,
+                        float* logits, int32_t* argmax, hipStream_t st) {
+  if (md->fmt == DPK_FMT_F32) return forward_f32(md, M, max_ctx, ids_dev, head_r0, head_n, logits, argmax, st);
+  return forward_skinny(md, M, max_ctx, ids_dev, head_r0, head_n, logits, argmax, st);
+}
+
+int max_rows_for_path(const dpk_model* md) {
+  return md->fmt == DPK_FMT_F32 ? md->cfg.max_rows : SKINNY_MAX;
+}
+
+}  // namespace
+
+// ============================================================================ C ABI
+
+extern "C" {
+
+const char* dpk_last_error(void) { return g_err.c_str(); }
+
+dpk_status dpk_create(const dpk_config* cfg, dpk_model** out) {
+  if (!cfg || !out) return fail(DPK_EINVAL, "null argument");
+  const dpk_config& c = *cfg;
+  if (c.n_layers < 1 || c.hidden < 1 || c.n_heads < 1 || c.n_kv_heads < 1 || c.intermediate < 1 || c.vocab < 1)
+    return fail(DPK_EINVAL, "sizes must be positive");
+  if (c.head_dim != 64 && c.head_dim != 128) return fail(DPK_EINVAL, "head_dim must be 64 or 128");
+  if (c.n_heads % c.n_kv_heads) return fail(DPK_EINVAL, "n_heads must be a multiple of n_kv_heads");
+  if (c.n_heads / c.n_kv_heads > 8) return fail(DPK_EINVAL, "at most 8 query heads per KV head");
+  if (c.hidden % 256 || c.intermediate % 256 || (c.n_heads * c.head_dim) % 256)
+    return fail(DPK_EINVAL, "hidden, intermediate and n_heads*head_dim must be multiples of 256");
+  if (c.weight_format < 0 || c.weight_format > 2) return fail(DPK_EINVAL, "unknown weight_format");
+  if (c.weight_format != DPK_FMT_F32 && c.head_dim != 128) return fail(DPK_EINVAL, "bf16/q4 need head_dim 128");
+  if (c.weight_format != DPK_FMT_F32 && !c.qk_norm) return fail(DPK_EINVAL, "bf16/q4 path needs qk_norm");
+  if (c.weight_format != DPK_FMT_F32 && c.vocab % 64) return fail(DPK_EINVAL, "bf16/q4 need vocab % 64 == 0");
+  if (c.max_batch < 1 || c.max_seq < 1 || c.max_rows < SKINNY_MAX)
+    return fail(DPK_EINVAL, "max_batch, max_seq >= 1 and max_rows >= 16 required");
+  if (!(c.rms_eps >= 0.0f) || !(c.rope_theta > 0.0)) return fail(DPK_EINVAL, "bad eps / theta");
+  dpk_model* md = new (std::nothrow) dpk_model();
+  if (!md) return fail(DPK_ENOMEM, "out of host memory");
+  md->cfg = c;
+  md->fmt = c.weight_format;
+  md->Nqkv = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
+  md->layers.resize(c.n_layers);
+  md->seq_len.assign(c.max_batch, 0);
+  *out = md;
+  g_err.clear();
+  return DPK_OK;
+}
+
+dpk_status dpk_workspace_size(const dpk_model* md, size_t* kvb, size_t* scb, size_t* prb) {
+  if (!md || !kvb || !scb || !prb) return fail(DPK_EINVAL, "null argument");
+  *kvb = kv_bytes(md->cfg);
+  *scb = scratch_layout(md->cfg).total;
+  *prb = prep_bytes(md->cfg);
+  return DPK_OK;
+}
+
+dpk_status dpk_bind_workspace(dpk_model* md, void* kv, void* scratch, void* prep, void* stream) {
+  if (!md || !kv || !scratch) return fail(DPK_EINVAL, "null argument");
+  if (md->failed) return fail(DPK_ESTATE, "model failed");
+  if (prep_bytes(md->cfg) && !prep) return fail(DPK_EINVAL, "prep buffer required for this format");
+  if (((uintptr_t)kv | (uintptr_t)scratch | (uintptr_t)prep) % ALIGN) return fail(DPK_EINVAL, "buffers must be 256-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  const dpk_config& c = md->cfg;
+  const ScratchLayout L = scratch_layout(c);
+  char* s = (char*)scratch;
+  md->kv = kv;
+  md->scratch = scratch;
+  md->prep = prep;
+  md->kvd.base = kv;
+  md->kvd.is_f32 = md->fmt == DPK_FMT_F32;
+  md->kvd.n_layers = c.n_layers;
+  md->kvd.n_kv = c.n_kv_heads;
+  md->kvd.max_seq = kv_seq(c);
+  md->kvd.d = c.head_dim;
+  md->rope_cos = (float*)(s + L.rope_cos);
+  md->rope_sin = (float*)(s + L.rope_sin);
+  md->rows_dev = (RowParam*)(s + L.rows);
+  md->h = (float*)(s + L.h);
+  md->rs = (float*)(s + L.rs);
+  md->qkv = (float*)(s + L.qkv);
+  md->y32 = (float*)(s + L.y32);
+  md->qbuf = (float*)(s + L.qbuf);
+  md->attn_o = (float*)(s + L.attn_o);
+  md->act = (float*)(s + L.act);
+  md->part = (float*)(s + L.part);
+  md->sink = (float*)(s + L.sink);
+  md->sq = (float*)(s + L.sq);
+  md->cand_val = (float*)(s + L.cand_val);
+  md->cand_idx = (int*)(s + L.cand_idx);
+  md->attn_part = (float*)(s + L.attn_part);
+  md->y16 = (_Float16*)(s + L.y16);
+  md->q16 = (_Float16*)(s + L.q16);
+  md->o16 = (_Float16*)(s + L.o16);
+  md->act16 = (_Float16*)(s + L.act16);
+  md->counters = (unsigned*)(s + L.counters);
+  md->attn_counters = (unsigned*)(s + L.attn_counters);
+  md->err_flag = (int*)(s + L.err);
+  md->argmax_sink = (int*)(s + L.argmax_sink);
+  md->rows_f32 = L.rows_f32;
+  md->attn_chunks_cap = L.attn_chunks_cap;
+  md->part_floats = L.part_floats;
+  for (int i = 0; i < dpk_model::NSTAGE; ++i) {
+    if (!md->stage[i]) HIP_TRY(hipHostMalloc((void**)&md->stage[i], sizeof(RowParam) * c.max_rows, hipHostMallocDefault));
+    if (!md->stage_ev[i]) HIP_TRY(hipEventCreateWithFlags(&md->stage_ev[i], hipEventDisableTiming));
+  }
+  if (!md->acc_host) HIP_TRY(hipHostMalloc((void**)&md->acc_host, sizeof(int32_t) * 32, hipHostMallocDefault));
+  HIP_TRY(hipMemsetAsync(md->counters, 0, (1 + nblocks_max(c)) * 4, st));
+  HIP_TRY(hipMemsetAsync(md->attn_counters, 0, (size_t)(md->fmt == DPK_FMT_F32 ? c.max_rows : SKINNY_MAX) * c.n_kv_heads * 4, st));
+  HIP_TRY(hipMemsetAsync(md->err_flag, 0, 4, st));
+  HIP_TRY(launch_rope_table(md->rope_cos, md->rope_sin, c.max_seq, c.head_dim, c.rope_theta, st));
+  md->bound = true;
+  return DPK_OK;
+}
+
+dpk_status dpk_load_weights(dpk_model* md, const dpk_tensor* t, int32_t n, void* stream) {
+  if (!md || (!t && n)) return fail(DPK_EINVAL, "null argument");
+  if (md->failed) return fail(DPK_ESTATE, "model failed");
+  if (!md->bound) return fail(DPK_ESTATE, "bind the workspace before loading weights");
+  const dpk_config& c = md->cfg;
+  const int fmt = md->fmt;
+  const int gdt = fmt == DPK_FMT_F32 ? DPK_DT_F32 : DPK_DT_BF16;
+  struct Want {
+    int dtype;
+    int64_t rows, cols;
+    const void** slot;
+    bool seen;
+  };
+  std::map<std::string, Want> want;
+  const int H = c.hidden, I = c.intermediate, d = c.head_dim, Qd = c.n_heads * d, KVd = c.n_kv_heads * d;
+  std::vector<LinearW*> lin_slots;
+  std::vector<std::string> lin_names;
+  auto add_linear = [&](const std::string& name, LinearW* lw, int rows, int cols) {
+    lw->rows = rows;
+    lw->cols = cols;
+    if (fmt == DPK_FMT_Q4G64) {
+      want[name + ".codes"] = {DPK_DT_U32, rows, cols / 8, &lw->w, false};
+      want[name + ".scales"] = {DPK_DT_BF16, rows, cols / 64, (const void**)&lw->sc, false};
+      want[name + ".biases"] = {DPK_DT_BF16, rows, cols / 64, (const void**)&lw->bi, false};
+    } else {
+      want[name] = {fmt == DPK_FMT_F32 ? DPK_DT_F32 : DPK_DT_BF16, rows, cols, &lw->w, false};
+    }
+  };
+  auto add_gain = [&](const std::string& name, const void** slot, int len) { want[name] = {gdt, 1, len, slot, false}; };
+  add_linear("embed_tokens", &md->embed, c.vocab, H);
+  if (!c.tied_embedding) add_linear("lm_head", &md->head, c.vocab, H);
+  add_gain("norm", &md->final_norm, H);
+  for (int l = 0; l < c.n_layers; ++l) {
+    LayerW& L = md->layers[l];
+    const std::string p = "layers." + std::to_string(l) + ".";
+    add_linear(p + "self_attn.q_proj", &L.q, Qd, H);
+    add_linear(p + "self_attn.k_proj", &L.k, KVd, H);
+    add_linear(p + "self_attn.v_proj", &L.v, KVd, H);
+    add_linear(p + "self_attn.o_proj", &L.o, H, Qd);
+    add_linear(p + "mlp.gate_proj", &L.gate, I, H);
+    add_linear(p + "mlp.up_proj", &L.up, I, H);
+    add_linear(p + "mlp.down_proj", &L.down, H, I);
+    add_gain(p + "input_layernorm", &L.in_norm, H);
+    add_gain(p + "post_attention_layernorm", &L.post_norm, H);
+    if (c.qk_norm) {
+      add_gain(p + "self_attn.q_norm", &L.q_norm, d);
+      add_gain(p + "self_attn.k_norm", &L.k_norm, d);
+    }
+  }
+  for (int i = 0; i < n; ++i) {
+    if (!t[i].name) return fail(DPK_EINVAL, "tensor %d has no name", i);
+    auto it = want.find(t[i].name);
+    if (it == want.end()) return fail(DPK_EINVAL, "unexpected tensor '%s'", t[i].name);
+    Want& w = it->second;
+    if (w.seen) return fail(DPK_EINVAL, "tensor '%s' given twice", t[i].name);
+    if (!t[i].data) return fail(DPK_EINVAL, "tensor '%s' has a null data pointer", t[i].name);
+    if (t[i].dtype != w.dtype) return fail(DPK_EINVAL, "tensor '%s': dtype %d, expected %d", t[i].name, t[i].dtype, w.dtype);
+    if (t[i].rows != w.rows || t[i].cols != w.cols)
+      return fail(DPK_EINVAL, "tensor '%s': shape [%lld, %lld], expected [%lld, %lld]", t[i].name,
+                  (long long)t[i].rows, (long long)t[i].cols, (long long)w.rows, (long long)w.cols);
+    if ((uintptr_t)t[i].data % 16) return fail(DPK_EINVAL, "tensor '%s' must be 16-byte aligned", t[i].name);
+    w.seen = true;
+  }
+  for (auto& kv : want)
+    if (!kv.second.seen) return fail(DPK_EINVAL, "missing tensor '%s'", kv.first.c_str());
+  for (int i = 0; i < n; ++i) *want[t[i].name].slot = t[i].data;
+  if (c.tied_embedding) md->head = md->embed;
+  // prefill operand copies
+  hipStream_t st = (hipStream_t)stream;
+  if (fmt != DPK_FMT_F32) {
+    char* p = (char*)md->prep;
+    auto conv = [&](const LinearW& w, _Float16* dst) -> hipError_t {
+      if (fmt == DPK_FMT_BF16) return launch_bf16_to_f16((const uint16_t*)w.w, dst, (size_t)w.rows * w.cols, st);
+      return launch_q4_to_f16((const uint32_t*)w.w, w.sc, w.bi, w.rows, w.cols, dst, st);
+    };
+    for (int l = 0; l < c.n_layers; ++l) {
+      LayerW& L = md->layers[l];
+      L.qkv16 = (_Float16*)p;
+      HIP_TRY(conv(L.q, L.qkv16));
+      HIP_TRY(conv(L.k, L.qkv16 + (size_t)Qd * H));
+      HIP_TRY(conv(L.v, L.qkv16 + (size_t)(Qd + KVd) * H));
+      p += up((size_t)md->Nqkv * H * 2);
+      L.o16 = (_Float16*)p;
+      HIP_TRY(conv(L.o, L.o16));
+      p += up((size_t)H * Qd * 2);
+      L.gate16 = (_Float16*)p;
+      HIP_TRY(conv(L.gate, L.gate16));
+      p += up((size_t)I * H * 2);
+      L.up16 = (_Float16*)p;
+      HIP_TRY(conv(L.up, L.up16));
+      p += up((size_t)I * H * 2);
+      L.down16 = (_Float16*)p;
+      HIP_TRY(conv(L.down, L.down16));
+      p += up((size_t)H * I * 2);
+    }
+  }
+  md->loaded = true;
+  return DPK_OK;
+}
+
+dpk_status dpk_prefill(dpk_model* md, int32_t seq, const int32_t* ids, int32_t n, float* logits, int32_t* argmax,
+                       void* stream) {
+  dpk_status s = check_ready(md);
+  if (s) return s;
+  const dpk_config& c = md->cfg;
+  if (!ids) return fail(DPK_EINVAL, "null ids");
+  if (n < 1) return fail(DPK_EINVAL, "n must be >= 1");
+  if (seq < 0 || seq >= c.max_batch) return fail(DPK_ERANGE, "seq %d outside [0, %d)", seq, c.max_batch);
+  if (n > c.max_seq) return fail(DPK_ERANGE, "prompt of %d tokens exceeds max_seq %d", n, c.max_seq);
+  for (int i = 0; i < n; ++i)
+    if (ids[i] < 0 || ids[i] >= c.vocab) return fail(DPK_ERANGE, "id %d at %d outside [0, %d)", ids[i], i, c.vocab);
+  hipStream_t st = (hipStream_t)stream;
+  const bool gemm_path = md->fmt != DPK_FMT_F32 && !(c.flags & DPK_FLAG_PREFILL_STREAM) && n > SKINNY_MAX;
+  const int chunk = gemm_path ? c.max_rows : max_rows_for_path(md);
+  std::vector<RowParam> rows(chunk);
+  for (int r0 = 0; r0 < n; r0 += chunk) {
+    const int M = (n - r0 < chunk) ? n - r0 : chunk;
+    for (int i = 0; i < M; ++i) rows[i] = RowParam{ids[r0 + i], r0 + i, seq, 0};
+    if ((s = upload_rows(md, rows.data(), M, st))) return s;
+    const bool last = r0 + M == n;
+    if (gemm_path && M > SKINNY_MAX)
+      s = forward_gemm(md, M, r0, seq, last, logits, argmax, st);
+    else
+      s = forward_rows(md, M, r0 + M, nullptr, M - 1, last ? 1 : 0, logits, argmax, st);
+    if (s) return s;
+  }
+  md->seq_len[seq] = n;
+  return DPK_OK;
+}
+
+dpk_status dpk_decode_step(dpk_model* md, int32_t batch, const int32_t* seqs, const int32_t* ids,
+                           const int32_t* ids_dev, const int32_t* pos, float* logits, int32_t* argmax, void* stream) {
+  dpk_status s = check_ready(md);
+  if (s) return s;
+  const dpk_config& c = md->cfg;
+  if (!seqs || !pos || (!ids && !ids_dev) || !argmax) return fail(DPK_EINVAL, "null argument");
+  if (batch < 1 || batch > SKINNY_MAX) return fail(DPK_EINVAL, "batch must be in [1, 16]");
+  RowParam rows[SKINNY_MAX];
+  int max_ctx = 0;
+  for (int b = 0; b < batch; ++b) {
+    if (seqs[b] < 0 || seqs[b] >= c.max_batch) return fail(DPK_ERANGE, "seq %d outside [0, %d)", seqs[b], c.max_batch);
+    for (int b2 = 0; b2 < b; ++b2)
+      if (seqs[b2] == seqs[b]) return fail(DPK_EINVAL, "slot %d appears twice in one step", seqs[b]);
+    if (pos[b] < 0 || pos[b] >= c.max_seq) return fail(DPK_ERANGE, "pos %d outside [0, %d)", pos[b], c.max_seq);
+    if (pos[b] > md->seq_len[seqs[b]])
+      return fail(DPK_ERANGE, "pos %d beyond the cursor %d of slot %d", pos[b], md->seq_len[seqs[b]], seqs[b]);
+    if (!ids_dev && (ids[b] < 0 || ids[b] >= c.vocab)) return fail(DPK_ERANGE, "id %d outside [0, %d)", ids[b], c.vocab);
+    rows[b] = RowParam{ids_dev ? 0 : ids[b], pos[b], seqs[b], 0};
+    if (pos[b] + 1 > max_ctx) max_ctx = pos[b] + 1;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  if ((s = upload_rows(md, rows, batch, st))) return s;
+  if ((s = forward_rows(md, batch, max_ctx, ids_dev, 0, batch, logits, argmax, st))) return s;
+  for (int b = 0; b < batch; ++b) md->seq_len[seqs[b]] = pos[b] + 1;
+  return DPK_OK;
+}
+
+dpk_status dpk_verify(dpk_model* md, int32_t seq, const int32_t* ids, int32_t kp1, int32_t pos, float* logits,
+                      int32_t* argmax, int32_t* accepted, void* stream) {
+  dpk_status s = check_ready(md);
+  if (s) return s;
+  const dpk_config& c = md->cfg;
+  if (!ids || !argmax || !accepted) return fail(DPK_EINVAL, "null argument");
+  if (kp1 < 1 || kp1 > SKINNY_MAX) return fail(DPK_EINVAL, "k_plus_1 must be in [1, 16]");
+  if (seq < 0 || seq >= c.max_batch) return fail(DPK_ERANGE, "seq %d outside [0, %d)", seq, c.max_batch);
+  if (pos < 0 || pos > md->seq_len[seq]) return fail(DPK_ERANGE, "pos %d beyond the cursor %d", pos, md->seq_len[seq]);
+  if (pos + kp1 > c.max_seq) return fail(DPK_ERANGE, "pos + k_plus_1 = %d exceeds max_seq %d", pos + kp1, c.max_seq);
+  RowParam rows[SKINNY_MAX];
+  for (int i = 0; i < kp1; ++i) {
+    if (ids[i] < 0 || ids[i] >= c.vocab) return fail(DPK_ERANGE, "id %d outside [0, %d)", ids[i], c.vocab);
+    rows[i] = RowParam{ids[i], pos + i, seq, 0};
+  }
+  hipStream_t st = (hipStream_t)stream;
+  if ((s = upload_rows(md, rows, kp1, st))) return s;
+  if ((s = forward_rows(md, kp1, pos + kp1, nullptr, 0, kp1, logits, argmax, st))) return s;
+  HIP_TRY(hipMemcpyAsync(md->acc_host, argmax, sizeof(int32_t) * kp1, hipMemcpyDeviceToHost, st));
+  HIP_TRY(hipStreamSynchronize(st));
+  int m = 0;
+  while (m < kp1 - 1 && ids[m + 1] == md->acc_host[m]) ++m;
+  *accepted = m;
+  md->seq_len[seq] = pos + m + 1;
+  return DPK_OK;
+}
+
+dpk_status dpk_seq_length(const dpk_model* md, int32_t seq, int32_t* length) {
+  if (!md || !length) return fail(DPK_EINVAL, "null argument");
+  if (seq < 0 || seq >= md->cfg.max_batch) return fail(DPK_ERANGE, "seq outside range");
+  *length = md->seq_len[seq];
+  return DPK_OK;
+}
+
+dpk_status dpk_check_device_errors(dpk_model* md, void* stream) {
+  if (!md) return fail(DPK_EINVAL, "null model");
+  if (!md->bound) return fail(DPK_ESTATE, "workspace not bound");
+  hipStream_t st = (hipStream_t)stream;
+  int flag = 0;
+  HIP_TRY(hipMemcpyAsync(&flag, md->err_flag, 4, hipMemcpyDeviceToHost, st));
+  HIP_TRY(hipStreamSynchronize(st));
+  if (flag) {
+    HIP_TRY(hipMemsetAsync(md->err_flag, 0, 4, st));
+    return fail(DPK_ERANGE, "a device-side token id was outside [0, vocab)");
+  }
+  return DPK_OK;
+}
+
+void dpk_destroy(dpk_model* md) {
+  if (!md) return;
+  for (int i = 0; i < dpk_model::NSTAGE; ++i) {
+    if (md->stage_ev[i]) {
+      (void)hipEventSynchronize(md->stage_ev[i]);
+      (void)hipEventDestroy(md->stage_ev[i]);
+    }
+    if (md->stage[i]) (void)hipHostFree(md->stage[i]);
+  }
+  if (md->acc_host) (void)hipHostFree(md->acc_host);
+  delete md;
+}
+
+}  // extern "C"

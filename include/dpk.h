@@ -1,0 +1,179 @@
+/*
+ * dpk: forward pass of a dense pre-norm decoder (Llama / Qwen3 style) on one
+ * AMD Instinct MI355X (gfx950): prompt prefill, single-token KV-cache decode,
+ * batched decode and greedy speculative verify.
+ *
+ * The operations follow the pages this library was built from:
+ *  - the block (RMSNorm -> QKV -> RoPE -> grouped-query causal attention ->
+ *    SwiGLU MLP, residuals) and the Qwen3 per-head QK-norm before RoPE:
+ *    "LLMs on the ANE" (ANEForge docs), sections "What's inside" and
+ *    "Correctness";
+ *  - prefill returns the next-token logits of a whole prompt, decode feeds one
+ *    token against a resident KV cache: same page, "API" and "Prefill and
+ *    decode";
+ *  - the per-token decode order and the on-GPU greedy argmax: Butter
+ *    architecture notes, single-token decode and GPU sampling diagrams;
+ *  - MLX 4-bit affine weights (w = scale * code + bias, group 64): oxinfer
+ *    0.0.5 docs, "MLX checkpoints";
+ *  - greedy verify (accept while draft == argmax, one bonus token, rollback by
+ *    moving the cache cursor): Butter notes, speculative decoding loop.
+ *
+ * Conventions
+ *  - All device pointers are HIP device addresses; "host" arrays are ordinary
+ *    host memory read before the call returns.
+ *  - The caller allocates and owns every device buffer (weights, KV cache,
+ *    scratch, prefill weight copy, outputs) and keeps them alive until
+ *    dpk_destroy.  The library owns only the handle, pinned staging for
+ *    per-call row parameters and a few events.
+ *  - `stream` is a hipStream_t passed as void* (NULL = default stream).  All
+ *    device work is enqueued on it; calls return after enqueue, except
+ *    dpk_verify (which waits to return the accepted count).  Calls on one
+ *    model must be issued on one stream, or serialized by the caller.
+ *  - Every entry point validates its arguments before enqueuing anything; on
+ *    a validation error nothing is enqueued and the model state is unchanged.
+ *    A HIP failure returns DPK_EHIP and marks the model failed: later calls
+ *    return DPK_ESTATE.  dpk_last_error() describes the last failure on the
+ *    calling thread.
+ */
+#ifndef DPK_H
+#define DPK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DPK_OK = 0,
+  DPK_EINVAL = -1, /* null pointer, bad name / shape / dtype, n < 1 */
+  DPK_ERANGE = -2, /* id outside [0, vocab), pos > cursor, pos + n > max_seq, seq >= max_batch */
+  DPK_ESTATE = -3, /* weights or workspace not bound, or the model failed earlier */
+  DPK_ENOMEM = -4, /* host allocation failed */
+  DPK_EHIP = -5    /* a HIP runtime call failed */
+} dpk_status;
+
+/* Storage format of the linear layers (q, k, v, o, gate, up, down, head). */
+typedef enum {
+  DPK_FMT_F32 = 0,  /* fp32 weights, fp32 KV cache */
+  DPK_FMT_BF16 = 1, /* bf16 weights, fp16 KV cache */
+  DPK_FMT_Q4G64 = 2 /* MLX 4-bit affine, group 64 along the input dim; fp16 KV cache */
+} dpk_format;
+
+/* Element types of dpk_tensor entries. */
+typedef enum { DPK_DT_F32 = 0, DPK_DT_BF16 = 1, DPK_DT_U32 = 2 } dpk_dtype;
+
+typedef struct {
+  int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, intermediate, vocab;
+  float rms_eps;          /* RMSNorm epsilon (all norms) */
+  double rope_theta;      /* RoPE base; inv_freq_i = theta^(-2i/head_dim), half-split pairs */
+  int32_t qk_norm;        /* 1: per-head RMSNorm of q and k before RoPE (Qwen3) */
+  int32_t tied_embedding; /* 1: the lm_head is the embedding table */
+  int32_t weight_format;  /* dpk_format */
+  int32_t max_batch;      /* KV-cache sequence slots */
+  int32_t max_seq;        /* positions per slot */
+  int32_t max_rows;       /* rows per internal forward chunk (>= 16); longer prompts are chunked */
+  int32_t flags;          /* DPK_FLAG_* */
+} dpk_config;
+
+/* Prefill through the weight-streaming (decode) kernels in chunks of 16 rows
+ * instead of the MFMA GEMM path (bf16 / q4 formats). */
+#define DPK_FLAG_PREFILL_STREAM 1
+
+/*
+ * One weight tensor.  Names (transformers-style):
+ *   embed_tokens, lm_head (absent when tied), norm,
+ *   layers.{i}.input_layernorm, layers.{i}.post_attention_layernorm,
+ *   layers.{i}.self_attn.{q,k,v,o}_proj, layers.{i}.self_attn.{q,k}_norm (qk_norm only),
+ *   layers.{i}.mlp.{gate,up,down}_proj.
+ * Linear weights are [out, in] row-major.  Norm gains are 1-D ([hidden] or
+ * [head_dim], rows = 1) and have the dtype of the format (F32 for DPK_FMT_F32,
+ * BF16 otherwise).  In DPK_FMT_Q4G64 each linear tensor (including
+ * embed_tokens / lm_head) is three entries: "<name>.codes" U32 [out, in/8]
+ * (element 8w+j in bits 4j..4j+3 of word w), "<name>.scales" and
+ * "<name>.biases" BF16 [out, in/64].
+ */
+typedef struct {
+  const char* name;
+  const void* data; /* device address */
+  int32_t dtype;    /* dpk_dtype */
+  int64_t rows, cols;
+} dpk_tensor;
+
+typedef struct dpk_model dpk_model;
+
+/* Validate the configuration and create a handle.  Supported shapes:
+ * head_dim 64 or 128, n_heads a multiple of n_kv_heads with at most 8 query
+ * heads per KV head, hidden and intermediate multiples of 256; bf16 / q4
+ * models need head_dim 128.  Does not touch the GPU. */
+dpk_status dpk_create(const dpk_config* cfg, dpk_model** out);
+
+/* Bytes of the three caller-provided device buffers:
+ *   kv:      max_batch x n_layers x {K, V} x n_kv_heads x S x head_dim elements with
+ *            S = max_seq rounded up to a multiple of 64 (fp32 for DPK_FMT_F32, fp16
+ *            otherwise); K rows per position, V stored transposed (positions
+ *            contiguous per channel);
+ *   scratch: activations, partial sums, counters, RoPE tables (256-byte aligned);
+ *   prep:    fp16 copy of the linear layers used as prefill MFMA operands
+ *            (0 for DPK_FMT_F32). */
+dpk_status dpk_workspace_size(const dpk_model* m, size_t* kv_bytes, size_t* scratch_bytes,
+                              size_t* prep_bytes);
+
+/* Bind the buffers (device addresses, 256-byte aligned, sizes as above).
+ * Enqueues the RoPE table and counter initialisation on `stream`. */
+dpk_status dpk_bind_workspace(dpk_model* m, void* kv, void* scratch, void* prep, void* stream);
+
+/* Register the weights.  Every expected tensor must appear exactly once with
+ * the expected dtype and shape; unknown names are an error.  Enqueues the
+ * conversion of the linear layers into the prep buffer on `stream`.  Requires
+ * dpk_bind_workspace first. */
+dpk_status dpk_load_weights(dpk_model* m, const dpk_tensor* tensors, int32_t n, void* stream);
+
+/* Prefill: overwrite sequence slot `seq` with the n prompt ids (host array) at
+ * positions 0..n-1, set its cursor to n, and write the next-token logits
+ * (fp32 [vocab], device) and, if argmax_dev is not NULL, the greedy id (int32
+ * [1], device; lowest index on ties).  logits_dev may be NULL. */
+dpk_status dpk_prefill(dpk_model* m, int32_t seq, const int32_t* ids, int32_t n, float* logits_dev,
+                       int32_t* argmax_dev, void* stream);
+
+/* Decode one token for each of `batch` rows (batch <= 16).  Row b feeds token
+ * ids[b] at position pos[b] of slot seqs[b] (host arrays; slots distinct).
+ * Requires pos[b] <= cursor and pos[b] < max_seq; writes K/V at pos[b],
+ * attends to positions 0..pos[b] and sets the cursor to pos[b] + 1 (an earlier
+ * pos rolls the slot back).  If ids_dev is not NULL the tokens are read from
+ * that device int32 [batch] array instead of `ids` (for example the previous
+ * step's argmax output); out-of-range device ids are replaced by 0 and
+ * reported by dpk_check_device_errors.  Outputs: logits fp32 [batch, vocab]
+ * (nullable) and argmax int32 [batch] (device). */
+dpk_status dpk_decode_step(dpk_model* m, int32_t batch, const int32_t* seqs, const int32_t* ids,
+                           const int32_t* ids_dev, const int32_t* pos, float* logits_dev,
+                           int32_t* argmax_dev, void* stream);
+
+/* Greedy speculative verify of k_plus_1 <= 16 tokens [t, d_1..d_K] (host) at
+ * positions pos..pos+K of slot `seq` (pos <= cursor): one forward pass that is
+ * causal within the block and sees cached positions 0..pos-1.  Writes logits
+ * fp32 [K+1, vocab] (nullable) and argmax int32 [K+1] (device), waits for the
+ * stream, and returns in *accepted the number m of leading drafts with
+ * d_{i+1} == argmax[i]; the cursor becomes pos + m + 1 and argmax[m] is the
+ * bonus token. */
+dpk_status dpk_verify(dpk_model* m, int32_t seq, const int32_t* ids, int32_t k_plus_1, int32_t pos,
+                      float* logits_dev, int32_t* argmax_dev, int32_t* accepted, void* stream);
+
+/* Current cursor (cached positions) of a slot. */
+dpk_status dpk_seq_length(const dpk_model* m, int32_t seq, int32_t* length);
+
+/* Synchronize `stream` and report device-side input errors seen since the last
+ * check (out-of-range device token ids): DPK_ERANGE if any, else DPK_OK. */
+dpk_status dpk_check_device_errors(dpk_model* m, void* stream);
+
+/* Message of the last failure on the calling thread (valid until the next
+ * call on this thread); "" if none. */
+const char* dpk_last_error(void);
+
+void dpk_destroy(dpk_model* m);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DPK_H */

@@ -1,0 +1,81 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and validates configurations and call order before touching
+the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "dpk.h")).read()
+    return sorted(set(re.findall(r"\b(dpk_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def dpk():
+    import decoder_prefill_kv_amd as dpk
+    return dpk
+
+
+def test_library_exports_every_header_symbol(dpk):
+    lib = ctypes.CDLL(dpk.library_path())
+    names = header_functions()
+    assert "dpk_prefill" in names and "dpk_verify" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(dpk.SYMBOLS)
+
+
+def cfg_ok(dpk, **kw):
+    c = dict(n_layers=2, hidden=1024, n_heads=16, n_kv_heads=8, head_dim=128, intermediate=3072,
+             vocab=151936, rms_eps=1e-6, rope_theta=1e6, qk_norm=1, tied_embedding=1,
+             weight_format=dpk.FMT_BF16, max_batch=2, max_seq=640, max_rows=64, flags=0)
+    c.update(kw)
+    return dpk.Config(**c)
+
+
+@pytest.mark.parametrize("bad", [dict(head_dim=96), dict(n_kv_heads=3), dict(hidden=1000),
+                                 dict(max_rows=8), dict(weight_format=7), dict(vocab=0),
+                                 dict(n_heads=32, n_kv_heads=2), dict(vocab=151937)])
+def test_create_rejects_bad_config(dpk, bad):
+    with pytest.raises(dpk.DpkError) as e:
+        dpk.create(cfg_ok(dpk, **bad))
+    assert e.value.status == dpk.DPK_EINVAL
+    assert dpk.last_error()
+
+
+def test_workspace_sizes_and_call_order(dpk):
+    h = dpk.create(cfg_ok(dpk))
+    try:
+        kv, sc, pr = dpk.workspace_size(h)
+        # 2 slots x 2 layers x {K,V} x 8 heads x 640 x 128 x fp16
+        assert kv == 2 * 2 * 2 * 8 * 640 * 128 * 2
+        assert sc > 0 and pr == 2 * (4096 * 1024 + 1024 * 2048 + 2 * 3072 * 1024 + 1024 * 3072) * 2
+        for call in (lambda: dpk.prefill(h, 0, [1, 2, 3], stream=0),
+                     lambda: dpk.decode_step(h, [0], [1], [0], None, stream=0),
+                     lambda: dpk.verify(h, 0, [1, 2], 0, None, stream=0)):
+            with pytest.raises(dpk.DpkError) as e:
+                call()
+            assert e.value.status in (dpk.DPK_ESTATE, dpk.DPK_EINVAL)
+        with pytest.raises(dpk.DpkError) as e:
+            dpk.prefill(h, 0, [1, 2, 3], stream=0)
+        assert e.value.status == dpk.DPK_ESTATE and "not bound" in dpk.last_error()
+        with pytest.raises(dpk.DpkError) as e:
+            dpk.load_weights(h, [], stream=0)
+        assert e.value.status == dpk.DPK_ESTATE
+    finally:
+        dpk.destroy(h)
+
+
+def test_fp32_format_needs_no_prep(dpk):
+    h = dpk.create(cfg_ok(dpk, weight_format=dpk.FMT_F32, head_dim=64, n_heads=4, n_kv_heads=2, hidden=256,
+                          intermediate=768, vocab=4096, qk_norm=0, tied_embedding=0))
+    try:
+        kv, sc, pr = dpk.workspace_size(h)
+        assert pr == 0 and kv == 2 * 2 * 2 * 2 * 640 * 64 * 4  # 640 is a multiple of 64
+    finally:
+        dpk.destroy(h)

@@ -1,0 +1,119 @@
+"""GPU parity: the HIP path against the CPU oracle on the same seeded inputs.
+
+Every comparison is element-wise over full logit vectors, teacher-forced on
+the oracle's greedy ids (prefill logits, then each decode step)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import TOL, check_ids, compare_logits, gpu_teacher_forced, oracle_greedy
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dpk():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import decoder_prefill_kv_amd as dpk
+    return dpk
+
+
+STREAM = 1  # DPK_FLAG_PREFILL_STREAM: prefill through the decode kernels
+CASES = [
+    # (name, config, prompt length, decode steps, Decoder kwargs); weight-
+    # streaming prefill first, then the MFMA GEMM prefill path
+    ("tiny", synth.TINY, 16, 16, {}),
+    ("q06b-L2-stream", synth.Q06B.with_(n_layers=2), 40, 8, dict(flags=STREAM)),
+    ("q06b_q4-L2-stream", synth.Q06B_Q4.with_(n_layers=2), 37, 6, dict(flags=STREAM)),
+    ("q8b-L1-v4096-stream", synth.Q8B.with_(n_layers=1, vocab=4096), 21, 5, dict(flags=STREAM)),
+    ("q06b-L2-gemm", synth.Q06B.with_(n_layers=2), 40, 8, {}),
+    ("q06b_q4-L2-gemm", synth.Q06B_Q4.with_(n_layers=2), 37, 6, {}),
+    ("q8b-L1-v4096-gemm", synth.Q8B.with_(n_layers=1, vocab=4096), 21, 5, {}),
+    ("q06b-L2-chunked", synth.Q06B.with_(n_layers=2), 300, 4, dict(max_rows=128)),
+    ("q8b-L2-v4096-chunked", synth.Q8B.with_(n_layers=2, vocab=4096), 600, 4, dict(max_rows=256)),
+]
+
+
+@pytest.mark.parametrize("name,cfg,P,N,kw", CASES, ids=[c[0] for c in CASES])
+def test_prefill_and_decode_match_oracle(dpk, name, cfg, P, N, kw):
+    print("\n[parity] %s P=%d N=%d %s" % (name, P, N, kw), flush=True)
+    w = synth.make_weights(cfg, 0)
+    prompt = synth.prompt_ids(cfg, P, 0)
+    _, run = oracle_greedy(cfg, w, prompt, N)
+    args = dict(max_rows=64)
+    args.update(kw)
+    dec = dpk.Decoder(cfg, w, max_batch=1, max_seq=P + N, **args)
+    logits, ids = gpu_teacher_forced(dec, prompt, run["ids"], N)
+    torch.cuda.synchronize()
+    tol = TOL[cfg.weight_format]
+    worst = 0.0
+    for i in range(N + 1):
+        worst = max(worst, compare_logits(logits[i], run["logits"][i], tol, "%s step %d" % (name, i)))
+    check_ids(ids, run["logits"], run["ids"], name)
+    print("[parity] %s worst max-abs %.3g" % (name, worst), flush=True)
+    dec.close()
+
+
+def test_prefill_without_outputs_then_decode(dpk):
+    # prefill with neither logits nor argmax buffers (both optional)
+    cfg = synth.Q06B.with_(n_layers=2)
+    w = synth.make_weights(cfg, 0)
+    prompt = synth.prompt_ids(cfg, 20, 0)
+    _, run = oracle_greedy(cfg, w, prompt, 1)
+    dec = dpk.Decoder(cfg, w, max_batch=1, max_seq=24, max_rows=64)
+    for flags_prompt in (prompt[:5], prompt):   # stream-sized and GEMM-sized
+        dec.prefill(0, [int(t) for t in flags_prompt])
+    lg, am = dec.logits_buffer(1), dec.argmax_buffer(1)
+    dec.decode_step([0], [run["ids"][0]], [20], am, lg)
+    compare_logits(lg[0].cpu(), run["logits"][1], TOL["bf16"], "decode after bare prefill")
+    dec.close()
+
+
+def test_verify_matches_oracle(dpk):
+    cfg = synth.Q06B.with_(n_layers=2)
+    w = synth.make_weights(cfg, 0)
+    P, K = 33, 5
+    prompt = synth.prompt_ids(cfg, P, 0)
+    m, run = oracle_greedy(cfg, w, prompt, K + 1)
+    g = run["ids"]
+    drafts = synth.corrupt_drafts(cfg, np.array(g[1:K + 1]), 0.3, 0, 0)
+    drafts[3] = (g[4] + 1) % cfg.vocab  # at least one rejection
+    ids_in = [g[0]] + [int(x) for x in drafts]
+    c = m.new_cache(P + K + 1)
+    m.forward_block(c, prompt, 0)
+    ref = oracle.verify(m, c, ids_in, P)
+    dec = dpk.Decoder(cfg, w, max_batch=1, max_seq=P + K + 1, max_rows=64)
+    lg = dec.logits_buffer(K + 1)
+    am = dec.argmax_buffer(K + 1)
+    dec.prefill(0, [int(t) for t in prompt])
+    acc = dec.verify(0, ids_in, P, am, lg)
+    for i in range(K + 1):
+        compare_logits(lg[i].cpu(), ref["logits"][i], TOL["bf16"], "verify row %d" % i)
+    check_ids(am.cpu().tolist(), list(ref["logits"]), ref["argmax"], "verify")
+    assert acc == ref["accepted"]
+    assert dec.seq_length(0) == P + acc + 1
+    dec.close()
+
+
+def test_batched_decode_matches_oracle(dpk):
+    cfg = synth.Q06B.with_(n_layers=2)
+    w = synth.make_weights(cfg, 0)
+    lens = [9, 23, 17]
+    N = 4
+    prompts = [synth.prompt_ids(cfg, L, 0, index=b) for b, L in enumerate(lens)]
+    runs = [oracle_greedy(cfg, w, p, N)[1] for p in prompts]
+    dec = dpk.Decoder(cfg, w, max_batch=4, max_seq=64, max_rows=64)
+    B = len(lens)
+    for b in range(B):
+        dec.prefill(b + 1, [int(t) for t in prompts[b]])  # slots 1..3
+    lg = dec.logits_buffer(B)
+    am = dec.argmax_buffer(B)
+    for s in range(N):
+        toks = [runs[b]["ids"][s] for b in range(B)]
+        dec.decode_step([b + 1 for b in range(B)], toks, [lens[b] + s for b in range(B)], am, lg)
+        for b in range(B):
+            compare_logits(lg[b].cpu(), runs[b]["logits"][s + 1], TOL["bf16"], "batch row %d step %d" % (b, s))
+    dec.close()
