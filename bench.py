@@ -1,0 +1,198 @@
+#!/usr/bin/env python3
+"""Benchmark of the dense-decoder hot path on one MI355X.
+
+One step = one pass of the workload: prefill of a random-id prompt (MFMA GEMM
+path), then greedy decode steps at batch 1 that feed the previous step's
+on-device argmax back as the next token.  Weights are seeded synthetic
+N(0, 0.02) bf16 (or MLX-style 4-bit), resident in HBM before timing starts.
+
+Prints one JSON line: value = decode tok/s (whole job, one GPU), plus prefill
+tok/s, a roofline object for the dominant kernel (decode weight streaming,
+HBM bound) and one for the prefill GEMMs (MFMA bound), and the CPU oracle's
+rate on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 matrix throughput
+
+WORKLOADS = {
+    # name: (config, prompt, decode steps, description)
+    "q8b": ("q8b", 2048, 256, "Qwen3-8B-shaped bf16 decoder (36 layers, hidden 4096, 32/8 heads, d 128, MLP 12288, "
+                              "vocab 151936, untied head): prefill 2048 random ids, then 256 greedy decode steps, "
+                              "batch 1"),
+    "q06b": ("q06b", 512, 128, "Qwen3-0.6B-shaped bf16 decoder (28 layers, hidden 1024, 16/8 heads, d 128, "
+                               "MLP 3072, vocab 151936, tied head): prefill 512, then 128 greedy decode steps"),
+    "q06b_q4": ("q06b_q4", 2048, 128, "Qwen3-0.6B-shaped decoder, MLX 4-bit affine g64 linears incl. tied head: "
+                                      "prefill 2048, then 128 greedy decode steps"),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(cfg, w):
+    """The oracle (float64, weights widened per use) on a bounded sample: one
+    decode step of the full model at an empty cache."""
+    import torch
+    import oracle
+    m = oracle.OracleModel(cfg, w, torch.float64, cache_weights=False)
+    cache = m.new_cache(4)
+    t0 = time.perf_counter()
+    m.forward_step(cache, 1, 0)
+    dt = time.perf_counter() - t0
+    return {"value": 1.0 / dt, "unit": "tok/s", "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": "1 decode step (step path, fp64, weights widened from bf16 per use) of the full model "
+                      "at position 0; %.1f s" % dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="q8b", choices=sorted(WORKLOADS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel profiled pass")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import decoder_prefill_kv_amd as dpk
+
+    cname, P, N, desc = WORKLOADS[args.workload]
+    cfg = synth.CONFIGS[cname]
+    t0 = time.time()
+    w = synth.make_weights(cfg, args.seed)
+    log("[bench] weights generated in %.1f s" % (time.time() - t0))
+    prompt = [int(t) for t in synth.prompt_ids(cfg, P, args.seed)]
+    torch.cuda.init()
+    stream = torch.cuda.current_stream()
+    t0 = time.time()
+    dec = dpk.Decoder(cfg, w, max_batch=1, max_seq=P + N, max_rows=P)
+    torch.cuda.synchronize()
+    log("[bench] weights on device in %.1f s (kv %.2f GB, scratch %.2f GB, prep %.2f GB)"
+        % ((time.time() - t0,) + tuple(x / 1e9 for x in dec.sizes)))
+    lg = dec.logits_buffer(1)
+    am = dec.argmax_buffer(1)
+
+    def one_step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        dec.prefill(0, prompt, lg, am)
+        if ev:
+            ev[1].record(stream)
+        for s in range(N):
+            dec.decode_step([0], None, [P + s], am, lg, ids_dev=am)
+        if ev:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        one_step()
+        torch.cuda.synchronize()
+        log("[bench] warmup %d done" % i)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        one_step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    log("[bench] timed %d steps: %.1f ms/step (prefill %.2f ms, decode %.1f ms)"
+        % (args.steps, wall * 1e3 / args.steps, pre_ms, dec_ms))
+    decode_tps = N / (dec_ms / 1e3)
+    prefill_tps = P / (pre_ms / 1e3)
+
+    # algorithmic work of the workload
+    H, L, d = cfg.hidden, cfg.n_layers, cfg.head_dim
+    n_lin = cfg.n_linear_params()
+    head_params = cfg.vocab * H
+    wbytes = {"bf16": 2.0, "f32": 4.0, "q4": 0.5 + 4.0 / 64}[cfg.weight_format]
+    kv_elt = 4 if cfg.weight_format == "f32" else 2
+    kv_per_pos = 2 * L * cfg.n_kv_heads * d * kv_elt
+    mean_ctx = P + (N + 1) / 2.0
+    decode_bytes_tok = (n_lin + head_params) * wbytes + kv_per_pos * mean_ctx
+    prefill_flops = 2.0 * n_lin * P + 4.0 * L * cfg.n_heads * d * P * (P + 1) / 2 + 2.0 * head_params
+
+    roof = None
+    roof_prefill = None
+    kernels = None
+    if not args.no_profile:
+        dpk.profile_begin(dec.handle, 200000)
+        one_step()
+        stats = dpk.profile_end(dec.handle)
+        kernels = {k: {"launches": v["launches"], "avg_us": round(1e3 * v["total_ms"] / v["launches"], 2),
+                       "total_ms": round(v["total_ms"], 3)} for k, v in stats.items()}
+        dec_cls = {k: v for k, v in stats.items() if k.startswith("gemv") or k.startswith("attn.decode")}
+        dom = max(dec_cls, key=lambda k: dec_cls[k]["total_ms"])
+        v = stats[dom]
+        avg_s = v["total_ms"] / 1e3 / v["launches"]
+        ach = v["bytes"] / v["launches"] / avg_s / 1e9
+        roof = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "bytes_per_launch": v["bytes"] / v["launches"], "avg_launch_us": round(avg_s * 1e6, 2)}
+        gem = {k: v for k, v in stats.items() if k.startswith("gemm")}
+        if gem:
+            domg = max(gem, key=lambda k: gem[k]["total_ms"])
+            g = gem[domg]
+            avg_g = g["total_ms"] / 1e3 / g["launches"]
+            achg = g["flops"] / g["launches"] / avg_g / 1e12
+            roof_prefill = {"bound": "mfma", "kernel": domg, "achieved": round(achg, 1), "peak": MFMA_PEAK_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(achg / MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                            "flops_per_launch": g["flops"] / g["launches"], "avg_launch_us": round(avg_g * 1e6, 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(cfg, w)
+        log("[bench] cpu oracle: %.4f tok/s" % cpu["value"])
+
+    out = {
+        "metric": "decode tok/s & prefill tok/s, 8B-shaped bf16, 1 MI355X; % HBM / MFMA peak",
+        "value": round(decode_tps, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.weight_format == "bf16" else cfg.weight_format,
+        "data": "synthetic (seeded N(0,0.02) weights, uniform random prompt ids)",
+        "config": {"workload": desc, "prompt_tokens": P, "decode_steps": N, "batch": 1},
+        "decode_tok_s": round(decode_tps, 2),
+        "prefill_tok_s": round(prefill_tps, 1),
+        "prefill_ms": round(pre_ms, 3),
+        "decode_ms_per_token": round(dec_ms / N, 4),
+        "decode_hbm_frac": round(decode_bytes_tok * decode_tps / 1e9 / HBM_PEAK_GBS, 4),
+        "decode_bytes_per_token": decode_bytes_tok,
+        "prefill_mfma_frac": round(prefill_flops / (pre_ms / 1e3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+        "prefill_flops": prefill_flops,
+        "prefill_dtype": "fp16 operands, fp32 accumulation",
+        "roofline": roof,
+        "roofline_prefill": roof_prefill,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    dec.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

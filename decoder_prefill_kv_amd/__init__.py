@@ -25,8 +25,8 @@ FMT_F32, FMT_BF16, FMT_Q4G64 = 0, 1, 2
 FLAG_PREFILL_STREAM = 1
 DT_F32, DT_BF16, DT_U32 = 0, 1, 2
 SYMBOLS = ["dpk_create", "dpk_workspace_size", "dpk_bind_workspace", "dpk_load_weights", "dpk_prefill",
-           "dpk_decode_step", "dpk_verify", "dpk_seq_length", "dpk_check_device_errors", "dpk_last_error",
-           "dpk_destroy"]
+           "dpk_decode_step", "dpk_verify", "dpk_seq_length", "dpk_check_device_errors", "dpk_profile_begin",
+           "dpk_profile_end", "dpk_last_error", "dpk_destroy"]
 
 
 class DpkError(RuntimeError):
@@ -49,6 +49,11 @@ class Tensor(ctypes.Structure):
                 ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
 
 
+class KernelStat(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double),
+                ("bytes", ctypes.c_double), ("flops", ctypes.c_double)]
+
+
 def library_path() -> str:
     return _SO
 
@@ -69,6 +74,8 @@ def _load():
         "dpk_verify": [vp, i32, p32, i32, i32, vp, vp, p32, vp],
         "dpk_seq_length": [vp, i32, p32],
         "dpk_check_device_errors": [vp, vp],
+        "dpk_profile_begin": [vp, i32],
+        "dpk_profile_end": [vp, ctypes.POINTER(KernelStat), i32, p32],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -81,11 +88,19 @@ def _load():
     return lib
 
 
-_lib = _load()
+_lib_handle = None
+
+
+def lib():
+    """The loaded library (loaded on first use; raises if it is not built)."""
+    global _lib_handle
+    if _lib_handle is None:
+        _lib_handle = _load()
+    return _lib_handle
 
 
 def last_error() -> str:
-    return _lib.dpk_last_error().decode()
+    return lib().dpk_last_error().decode()
 
 
 def _check(st: int):
@@ -112,28 +127,28 @@ def _stream(stream) -> Optional[int]:
 # ------------------------------------------------------------------ C names
 def create(cfg: Config) -> int:
     h = ctypes.c_void_p()
-    _check(_lib.dpk_create(ctypes.byref(cfg), ctypes.byref(h)))
+    _check(lib().dpk_create(ctypes.byref(cfg), ctypes.byref(h)))
     return h.value
 
 
 def workspace_size(model: int):
     a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
-    _check(_lib.dpk_workspace_size(model, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    _check(lib().dpk_workspace_size(model, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
     return a.value, b.value, c.value
 
 
 def bind_workspace(model: int, kv: int, scratch: int, prep: Optional[int], stream=None):
-    _check(_lib.dpk_bind_workspace(model, kv, scratch, prep, _stream(stream)))
+    _check(lib().dpk_bind_workspace(model, kv, scratch, prep, _stream(stream)))
 
 
 def load_weights(model: int, tensors: Sequence[Tensor], stream=None):
     arr = (Tensor * len(tensors))(*tensors)
-    _check(_lib.dpk_load_weights(model, arr, len(tensors), _stream(stream)))
+    _check(lib().dpk_load_weights(model, arr, len(tensors), _stream(stream)))
 
 
 def prefill(model: int, seq: int, ids: Sequence[int], logits_dev=None, argmax_dev=None, stream=None):
     a, p = _i32(ids)
-    _check(_lib.dpk_prefill(model, seq, p, len(a), _ptr(logits_dev), _ptr(argmax_dev), _stream(stream)))
+    _check(lib().dpk_prefill(model, seq, p, len(a), _ptr(logits_dev), _ptr(argmax_dev), _stream(stream)))
 
 
 def decode_step(model: int, seqs: Sequence[int], ids: Optional[Sequence[int]], pos: Sequence[int], argmax_dev,
@@ -144,30 +159,47 @@ def decode_step(model: int, seqs: Sequence[int], ids: Optional[Sequence[int]], p
         i, ip = _i32(ids)
     else:
         ip = None
-    _check(_lib.dpk_decode_step(model, len(s), sp, ip, _ptr(ids_dev), qp, _ptr(logits_dev), _ptr(argmax_dev),
+    _check(lib().dpk_decode_step(model, len(s), sp, ip, _ptr(ids_dev), qp, _ptr(logits_dev), _ptr(argmax_dev),
                                 _stream(stream)))
 
 
 def verify(model: int, seq: int, ids: Sequence[int], pos: int, argmax_dev, logits_dev=None, stream=None) -> int:
     a, p = _i32(ids)
     acc = ctypes.c_int32()
-    _check(_lib.dpk_verify(model, seq, p, len(a), pos, _ptr(logits_dev), _ptr(argmax_dev), ctypes.byref(acc),
+    _check(lib().dpk_verify(model, seq, p, len(a), pos, _ptr(logits_dev), _ptr(argmax_dev), ctypes.byref(acc),
                            _stream(stream)))
     return acc.value
 
 
 def seq_length(model: int, seq: int) -> int:
     v = ctypes.c_int32()
-    _check(_lib.dpk_seq_length(model, seq, ctypes.byref(v)))
+    _check(lib().dpk_seq_length(model, seq, ctypes.byref(v)))
     return v.value
 
 
 def check_device_errors(model: int, stream=None):
-    _check(_lib.dpk_check_device_errors(model, _stream(stream)))
+    _check(lib().dpk_check_device_errors(model, _stream(stream)))
+
+
+def profile_begin(model: int, max_launches: int = 100000):
+    _check(lib().dpk_profile_begin(model, max_launches))
+
+
+def profile_end(model: int):
+    """-> {class name: dict(launches, total_ms, bytes, flops)}"""
+    arr = (KernelStat * 64)()
+    n = ctypes.c_int32()
+    st = lib().dpk_profile_end(model, arr, 64, ctypes.byref(n))
+    out = {}
+    for i in range(min(n.value, 64)):
+        k = arr[i]
+        out[k.name.decode()] = dict(launches=k.launches, total_ms=k.total_ms, bytes=k.bytes, flops=k.flops)
+    _check(st)
+    return out
 
 
 def destroy(model: int):
-    _lib.dpk_destroy(model)
+    lib().dpk_destroy(model)
 
 
 # ------------------------------------------------------------------ convenience

@@ -84,24 +84,39 @@ DPK_DEV float block_sum(float v, float* red) {
   return t;
 }
 
+// Device-coherent access (agent-scope relaxed atomics: sc1 loads/stores that
+// bypass the non-coherent per-XCD L2 state) for data handed from one
+// workgroup to another inside a launch.
+DPK_DEV void coh_store(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DPK_DEV void coh_store(int* p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DPK_DEV float coh_load(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+DPK_DEV int coh_load(const int* p) {
+  return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Last-arriving-workgroup election.  Every workgroup calls this once after
-// its global writes; exactly one (the last) gets true, and it observes all the
-// other workgroups' writes.  The counter is reset for the next launch.
+// writing the data it hands over with coh_store; exactly one (the last) gets
+// true and may then read all of it with coh_load.  The counter is reset for
+// the next launch.
+//
+// No release/acquire fences: on multi-XCD gfx950 those are whole-L2
+// write-back / invalidate operations, far too slow to run once per workgroup.
+// Instead the handed-over data never lives in a non-coherent cache (coh_*),
+// each wave waits until its coherent stores have completed before the
+// barrier, and only then does one thread count in.
 DPK_DEV bool last_block_arrive(unsigned* counter, unsigned expected, int* smem_flag) {
-  __threadfence();  // release this thread's global writes at device scope
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
   __syncthreads();
   if (threadIdx.x == 0) {
-    unsigned prev = atomicAdd(counter, 1u);
-    int last = (prev == expected - 1);
-    if (last) {
-      atomicExch(counter, 0u);
-    }
+    const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = (prev == expected - 1);
+    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *smem_flag = last;
   }
   __syncthreads();
-  bool last = *smem_flag != 0;
-  if (last) __threadfence();
-  return last;
+  return *smem_flag != 0;
 }
 
 DPK_DEV float silu(float z) { return z / (1.0f + __expf(-z)); }

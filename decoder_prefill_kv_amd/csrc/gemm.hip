@@ -7,7 +7,9 @@
 // The operands are fp16 rather than bf16: every weight of the bf16 model is
 // exactly representable in fp16 (magnitudes >= 2^-17; smaller ones round with
 // an absolute error below 2^-25), and fp16 activations carry three more
-// mantissa bits, which the logits tolerance needs on deep models.
+// mantissa bits, which the logits tolerance needs on deep models.  Where that
+// is still not enough (the QKV projection), A is given as [A_hi | A_lo] with
+// K = 2 Kb and B is read twice, which computes (A_hi + A_lo) B^T.
 //
 // Tile 256 x 256 x 64, 4 waves in a 2 x 2 layout, each wave 128 x 128 from
 // 4 x 4 v_mfma_f32_32x32x16_f16 blocks (256 fp32 accumulators per lane).
@@ -61,12 +63,14 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs a) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   u32x4 ra[BM / 32], rb[BN / 32];
+  const int Kb = a.Kb ? a.Kb : a.K;
   auto gload = [&](int kt) {
     const int ko = kt * BK;
+    const int kob = ko < Kb ? ko : ko - Kb;  // B is read twice when A = [hi | lo]
 #pragma unroll
     for (int i = 0; i < BM / 32; ++i) ra[i] = *(const u32x4*)(Ag[i] + ko);
 #pragma unroll
-    for (int i = 0; i < BN / 32; ++i) rb[i] = *(const u32x4*)(Bg[i] + ko);
+    for (int i = 0; i < BN / 32; ++i) rb[i] = *(const u32x4*)(Bg[i] + kob);
   };
   auto lstore = [&](int st) {
 #pragma unroll
@@ -144,6 +148,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs a) {
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.K % BK || a.M < 1) return hipErrorInvalidValue;
+  if (a.Kb && (a.Kb % BK || (a.K != a.Kb && a.K != 2 * a.Kb))) return hipErrorInvalidValue;
   const int ntile = (a.epi == GEMM_SWIGLU_F16) ? BN / 2 : BN;
   if (a.N % ntile) return hipErrorInvalidValue;
   dim3 grid(a.N / ntile, (a.M + BM - 1) / BM);

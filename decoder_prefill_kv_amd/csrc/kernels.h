@@ -79,7 +79,7 @@ struct AttnDecodeArgs {
   const float* q;             // [M][n_heads][d] (normed, roped)
   KVDesc kv;
   int layer;
-  int chunk;                  // positions per workgroup
+  int chunk;                  // positions per workgroup (attn_decode_chunk())
   int max_chunks;             // grid.x
   float* part;                // [M][n_heads][max_chunks][d + 2]
   unsigned* counters;         // [M * n_kv]
@@ -87,6 +87,7 @@ struct AttnDecodeArgs {
   float scale;                // 1/sqrt(d)
 };
 hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t stream);
+int attn_decode_chunk();  // positions per decode-attention workgroup
 
 // ---- misc
 hipError_t launch_rope_table(float* cos_t, float* sin_t, int max_seq, int d, double theta,
@@ -95,7 +96,8 @@ hipError_t launch_rope_table(float* cos_t, float* sin_t, int max_seq, int d, dou
 hipError_t launch_embed(int M, int H, int fmt, const void* table, const uint16_t* sc, const uint16_t* bi,
                         const RowParam* rp, const int32_t* ids_dev, int vocab, float* h, float* rs,
                         float eps, int* err_flag, hipStream_t stream);
-// y[m] = x[m] * rsqrt(mean(x^2)+eps) * g, fp16 or fp32 output; g is fp32 or bf16
+// y[m] = x[m] * rsqrt(mean(x^2)+eps) * g; y_is_f16: 0 fp32, 1 fp16, 2 fp16 hi
+// in columns [0, H) and fp16 lo (= y - hi) in [H, 2H); g is fp32 or bf16
 hipError_t launch_rmsnorm_rows(int M, int H, const float* x, int ldx, const void* g, int g_is_f32,
                                float eps, void* y, int y_is_f16, int ldy, hipStream_t stream);
 // prefill: qkv fp32 [M][(Hq+2Hkv)d] -> q (fp16 or fp32 [M][Hq][d]), K/V into the cache
@@ -121,6 +123,7 @@ hipError_t launch_f32_to_f16(const float* src, _Float16* dst, size_t n, hipStrea
 enum GemmEpi : int { GEMM_STORE_F32 = 0, GEMM_ADD_F32 = 1, GEMM_SWIGLU_F16 = 2 };
 struct GemmArgs {
   int M, N, K;
+  int Kb;                         // K of B (0: = K); K = 2 Kb multiplies [A_hi | A_lo] by [B | B]
   const _Float16* A; int lda;
   const _Float16* B; int ldb;     // [N][K]; for SWIGLU rows [0,N) gate, B2 up
   const _Float16* B2;

@@ -66,10 +66,15 @@ __global__ void rmsnorm_rows_kernel(int H, const float* x, int ldx, const void* 
   for (int k = threadIdx.x; k < H; k += blockDim.x) {
     const float gk = g_is_f32 ? ((const float*)g)[k] : bf16_to_f32(((const uint16_t*)g)[k]);
     const float v = xr[k] * r * gk;
-    if (y_is_f16)
+    if (y_is_f16 == 2) {  // fp16 hi in [0, H), fp16 lo = v - hi in [H, 2H)
+      const _Float16 hi = (_Float16)v;
+      ((_Float16*)y)[(size_t)m * ldy + k] = hi;
+      ((_Float16*)y)[(size_t)m * ldy + H + k] = (_Float16)(v - (float)hi);
+    } else if (y_is_f16) {
       ((_Float16*)y)[(size_t)m * ldy + k] = (_Float16)v;
-    else
+    } else {
       ((float*)y)[(size_t)m * ldy + k] = v;
+    }
   }
 }
 

@@ -85,6 +85,16 @@ struct dpk_model {
   int stage_next = 0;
   int32_t* acc_host = nullptr;  // pinned readback for verify
   std::vector<int32_t> seq_len;
+  // optional per-launch timing (dpk_profile_begin / dpk_profile_end)
+  struct ProfRec {
+    int cls;
+    double bytes, flops;
+  };
+  bool prof = false;
+  int prof_max = 0;
+  std::vector<hipEvent_t> prof_ev;
+  std::vector<ProfRec> prof_rec;
+  long prof_dropped = 0;
 };
 
 namespace {
@@ -141,7 +151,7 @@ ScratchLayout scratch_layout(const dpk_config& c) {
   L.cand_val = take(SKINNY_MAX * nbm * 4);
   L.cand_idx = take(SKINNY_MAX * nbm * 4);
   L.attn_part = take((size_t)(f32 ? R : SKINNY_MAX) * c.n_heads * L.attn_chunks_cap * (d + 2) * 4);
-  L.y16 = take(f32 ? 0 : R * H * 2);
+  L.y16 = take(f32 ? 0 : R * H * 2 * 2);
   L.q16 = take(f32 ? 0 : R * Qd * 2);
   L.o16 = take(f32 ? 0 : R * Qd * 2);
   L.act16 = take(f32 ? 0 : R * I * 2);
@@ -179,6 +189,36 @@ size_t kv_bytes(const dpk_config& c) {
     }                                                                                  \
   } while (0)
 
+enum KClass : int {
+  K_GEMV_QKV, K_GEMV_O, K_GEMV_GATEUP, K_GEMV_DOWN, K_GEMV_HEAD, K_ATTN_DECODE, K_EMBED, K_GEMM_QKV, K_GEMM_O,
+  K_GEMM_GATEUP, K_GEMM_DOWN, K_ATTN_PREFILL, K_QK_ROPE_KV, K_RMSNORM, K_GEMV_F32, K_OTHER, K_NCLASS
+};
+const char* const kclass_name[K_NCLASS] = {
+    "gemv.qkv", "gemv.o", "gemv.gate_up", "gemv.down", "gemv.head", "attn.decode", "embed", "gemm.qkv", "gemm.o",
+    "gemm.gate_up", "gemm.down", "attn.prefill", "qk_rope_kv", "rmsnorm", "gemv.f32", "other"};
+
+// Event pair around one launch when profiling is on.
+struct ProfScope {
+  dpk_model* md;
+  hipStream_t st;
+  int idx = -1;
+  ProfScope(dpk_model* m, hipStream_t s, int cls, double bytes, double flops) : md(m), st(s) {
+    if (!md->prof) return;
+    if ((int)md->prof_rec.size() >= md->prof_max) {
+      ++md->prof_dropped;
+      return;
+    }
+    idx = (int)md->prof_rec.size();
+    md->prof_rec.push_back({cls, bytes, flops});
+    (void)hipEventRecord(md->prof_ev[2 * idx], st);
+  }
+  ~ProfScope() {
+    if (idx >= 0) (void)hipEventRecord(md->prof_ev[2 * idx + 1], st);
+  }
+};
+
+double wbytes_per_elem(int fmt) { return fmt == DPK_FMT_F32 ? 4.0 : fmt == DPK_FMT_BF16 ? 2.0 : 0.5 + 4.0 / 64.0; }
+
 dpk_status check_ready(const dpk_model* md) {
   if (!md) return fail(DPK_EINVAL, "null model");
   if (md->failed) return fail(DPK_ESTATE, "model is in a failed state after an earlier HIP error");
@@ -214,7 +254,7 @@ int choose_ksplit(int K, int nblocks, int M, int rows, int fmt) {
 }
 
 // One weight-streaming GEMV launch (M <= 16).
-dpk_status skinny(dpk_model* md, int M, const float* x, int ldx, const float* rs, const void* gain,
+dpk_status skinny(dpk_model* md, int cls, int M, const float* x, int ldx, const float* rs, const void* gain,
                   const LinearW* segs, int nseg, int epi, float* out, int ldo, hipStream_t st,
                   int layer = 0) {
   const dpk_config& c = md->cfg;
@@ -270,11 +310,18 @@ dpk_status skinny(dpk_model* md, int M, const float* x, int ldx, const float* rs
     a.kn = c.qk_norm ? (const uint16_t*)L.k_norm : nullptr;
     if (!c.qk_norm) return fail(DPK_EINVAL, "fused QKV epilogue needs qk_norm");
   }
-  HIP_TRY(launch_skinny(a, st));
+  {
+    const double nrows = (epi == EPI_SWIGLU) ? 2.0 * a.N : (double)a.N;
+    const double wb = nrows * a.K * wbytes_per_elem(md->fmt);
+    const double io = (double)M * a.K * 4 + (double)M * a.N * 4;
+    ProfScope ps(md, st, cls, wb + io, 2.0 * M * nrows * a.K);
+    HIP_TRY(launch_skinny(a, st));
+  }
   return DPK_OK;
 }
 
-dpk_status attn_decode(dpk_model* md, int M, int max_ctx, const float* q, float* out, int layer, hipStream_t st) {
+dpk_status attn_decode(dpk_model* md, int M, int max_ctx, const float* q, float* out, int layer, hipStream_t st,
+                       double kv_positions) {
   const dpk_config& c = md->cfg;
   AttnDecodeArgs a{};
   a.M = M;
@@ -285,19 +332,20 @@ dpk_status attn_decode(dpk_model* md, int M, int max_ctx, const float* q, float*
   a.q = q;
   a.kv = md->kvd;
   a.layer = layer;
-  int target = 512 / (M * c.n_kv_heads);
-  if (target < 1) target = 1;
-  int subs = (max_ctx + 63) / 64;
-  int per = (subs + target - 1) / target;
-  if (per < 1) per = 1;
-  a.chunk = 64 * per;
+  a.chunk = attn_decode_chunk();
   a.max_chunks = (max_ctx + a.chunk - 1) / a.chunk;
   if (a.max_chunks > md->attn_chunks_cap) return fail(DPK_EINVAL, "attention chunk cap");
   a.part = md->attn_part;
   a.counters = md->attn_counters;
   a.out = out;
   a.scale = 1.0f / sqrtf((float)c.head_dim);
-  HIP_TRY(launch_attn_decode(a, st));
+  {
+    const double elt = md->kvd.is_f32 ? 4 : 2;
+    const double kvb = kv_positions * 2.0 * c.n_kv_heads * c.head_dim * elt;
+    const double io = 2.0 * M * c.n_heads * c.head_dim * 4;
+    ProfScope ps(md, st, K_ATTN_DECODE, kvb + io, 4.0 * kv_positions * c.n_heads * c.head_dim);
+    HIP_TRY(launch_attn_decode(a, st));
+  }
   return DPK_OK;
 }
 
@@ -339,29 +387,40 @@ dpk_status head(dpk_model* md, int rows, const float* x, const float* rs, const 
   h.cand_val = md->cand_val;
   h.cand_idx = md->cand_idx;
   h.argmax_out = argmax ? argmax : md->argmax_sink;
-  HIP_TRY(launch_skinny(h, st));
+  {
+    const double wb = (double)hw.rows * H * wbytes_per_elem(md->fmt);
+    ProfScope ps(md, st, K_GEMV_HEAD, wb + (double)rows * H * 4 + (double)rows * hw.rows * 4, 2.0 * rows * hw.rows * H);
+    HIP_TRY(launch_skinny(h, st));
+  }
   return DPK_OK;
 }
 
 // Rows whose parameters are already in md->rows_dev.  M <= 16, bf16 / q4
 // weights.  Writes logits/argmax for rows [head_r0, head_r0 + head_n).
 dpk_status forward_skinny(dpk_model* md, int M, int max_ctx, const int32_t* ids_dev, int head_r0, int head_n,
-                          float* logits, int32_t* argmax, hipStream_t st) {
+                          float* logits, int32_t* argmax, hipStream_t st, double kv_positions) {
   const dpk_config& c = md->cfg;
   const int H = c.hidden;
-  HIP_TRY(launch_embed(M, H, md->fmt == DPK_FMT_Q4G64 ? W_Q4 : W_BF16, md->embed.w, md->embed.sc, md->embed.bi,
-                       md->rows_dev, ids_dev, c.vocab, md->h, md->rs, c.rms_eps, md->err_flag, st));
+  {
+    ProfScope ps(md, st, K_EMBED, (double)M * H * 6, 0);
+    HIP_TRY(launch_embed(M, H, md->fmt == DPK_FMT_Q4G64 ? W_Q4 : W_BF16, md->embed.w, md->embed.sc, md->embed.bi,
+                         md->rows_dev, ids_dev, c.vocab, md->h, md->rs, c.rms_eps, md->err_flag, st));
+  }
   dpk_status s;
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& L = md->layers[l];
     LinearW qkv[3] = {L.q, L.k, L.v};
-    if ((s = skinny(md, M, md->h, H, md->rs, L.in_norm, qkv, 3, EPI_QKV, nullptr, 0, st, l))) return s;
-    if ((s = attn_decode(md, M, max_ctx, md->qbuf, md->attn_o, l, st))) return s;
-    if ((s = skinny(md, M, md->attn_o, c.n_heads * c.head_dim, nullptr, nullptr, &L.o, 1, EPI_RESID, md->h, H, st)))
+    if ((s = skinny(md, K_GEMV_QKV, M, md->h, H, md->rs, L.in_norm, qkv, 3, EPI_QKV, nullptr, 0, st, l))) return s;
+    if ((s = attn_decode(md, M, max_ctx, md->qbuf, md->attn_o, l, st, kv_positions))) return s;
+    if ((s = skinny(md, K_GEMV_O, M, md->attn_o, c.n_heads * c.head_dim, nullptr, nullptr, &L.o, 1, EPI_RESID, md->h,
+                    H, st)))
       return s;
     LinearW gu[2] = {L.gate, L.up};
-    if ((s = skinny(md, M, md->h, H, md->rs, L.post_norm, gu, 2, EPI_SWIGLU, md->act, c.intermediate, st))) return s;
-    if ((s = skinny(md, M, md->act, c.intermediate, nullptr, nullptr, &L.down, 1, EPI_RESID, md->h, H, st)))
+    if ((s = skinny(md, K_GEMV_GATEUP, M, md->h, H, md->rs, L.post_norm, gu, 2, EPI_SWIGLU, md->act, c.intermediate,
+                    st)))
+      return s;
+    if ((s = skinny(md, K_GEMV_DOWN, M, md->act, c.intermediate, nullptr, nullptr, &L.down, 1, EPI_RESID, md->h, H,
+                    st)))
       return s;
   }
   if (head_n > 0) return head(md, head_n, md->h + (size_t)head_r0 * H, md->rs + head_r0, md->final_norm, logits, argmax, st);
@@ -375,40 +434,68 @@ dpk_status forward_gemm(dpk_model* md, int M, int start, int seq, bool want_head
                         hipStream_t st) {
   const dpk_config& c = md->cfg;
   const int H = c.hidden, I = c.intermediate, d = c.head_dim, Qd = c.n_heads * d;
-  HIP_TRY(launch_embed(M, H, md->fmt == DPK_FMT_Q4G64 ? W_Q4 : W_BF16, md->embed.w, md->embed.sc, md->embed.bi,
-                       md->rows_dev, nullptr, c.vocab, md->h, nullptr, c.rms_eps, md->err_flag, st));
+  auto gemm_prof = [&](int cls, const GemmArgs& g) -> dpk_status {
+    const double n = (g.epi == GEMM_SWIGLU_F16) ? 2.0 * g.N : g.N;
+    const double outb = (g.epi == GEMM_SWIGLU_F16) ? (double)g.M * g.N * 2 : (double)g.M * g.N * 4;
+    const double kb = g.Kb ? g.Kb : g.K;  // algorithmic K (the hi/lo split doubles the MFMA work)
+    ProfScope ps(md, st, cls, ((double)g.M * g.K + n * kb) * 2 + outb, 2.0 * g.M * n * kb);
+    HIP_TRY(launch_gemm(g, st));
+    return DPK_OK;
+  };
+  dpk_status s2;
+  {
+    ProfScope ps(md, st, K_EMBED, (double)M * H * 6, 0);
+    HIP_TRY(launch_embed(M, H, md->fmt == DPK_FMT_Q4G64 ? W_Q4 : W_BF16, md->embed.w, md->embed.sc, md->embed.bi,
+                         md->rows_dev, nullptr, c.vocab, md->h, nullptr, c.rms_eps, md->err_flag, st));
+  }
+  const double norm_bytes = (double)M * H * 6;
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& L = md->layers[l];
-    HIP_TRY(launch_rmsnorm_rows(M, H, md->h, H, L.in_norm, 0, c.rms_eps, md->y16, 1, H, st));
+    {
+      ProfScope ps(md, st, K_RMSNORM, norm_bytes, 0);
+      // fp16 hi + lo: the QKV projection gets near-fp32 activations
+      HIP_TRY(launch_rmsnorm_rows(M, H, md->h, H, L.in_norm, 0, c.rms_eps, md->y16, 2, 2 * H, st));
+    }
     GemmArgs g{};
-    g.M = M; g.N = md->Nqkv; g.K = H;
-    g.A = md->y16; g.lda = H; g.B = L.qkv16; g.ldb = H;
+    g.M = M; g.N = md->Nqkv; g.K = 2 * H; g.Kb = H;
+    g.A = md->y16; g.lda = 2 * H; g.B = L.qkv16; g.ldb = H;
     g.epi = GEMM_STORE_F32; g.C = md->qkv; g.ldc = md->Nqkv;
-    HIP_TRY(launch_gemm(g, st));
-    HIP_TRY(launch_qk_rope_kv(M, md->qkv, c.n_heads, c.n_kv_heads, d, c.qk_norm, L.q_norm, L.k_norm, 0, c.rms_eps,
-                              md->rope_cos, md->rope_sin, md->rows_dev, md->q16, 1, md->kvd, l, st));
+    if ((s2 = gemm_prof(K_GEMM_QKV, g))) return s2;
+    {
+      ProfScope ps(md, st, K_QK_ROPE_KV, (double)M * md->Nqkv * 6, 0);
+      HIP_TRY(launch_qk_rope_kv(M, md->qkv, c.n_heads, c.n_kv_heads, d, c.qk_norm, L.q_norm, L.k_norm, 0, c.rms_eps,
+                                md->rope_cos, md->rope_sin, md->rows_dev, md->q16, 1, md->kvd, l, st));
+    }
     AttnPrefillArgs at{};
     at.M = M; at.start = start; at.seq = seq;
     at.n_heads = c.n_heads; at.n_kv = c.n_kv_heads; at.d = d;
     at.q = md->q16; at.kv = md->kvd; at.layer = l; at.out = md->o16;
     at.scale = 1.0f / sqrtf((float)d);
-    HIP_TRY(launch_attn_prefill(at, st));
+    {
+      const double keys = (double)M * start + (double)M * (M + 1) / 2;  // causal (query, key) pairs
+      const double kvb = (double)(start + M) * 2 * c.n_kv_heads * d * 2;
+      ProfScope ps(md, st, K_ATTN_PREFILL, kvb + 2.0 * M * Qd * 2, 4.0 * c.n_heads * d * keys);
+      HIP_TRY(launch_attn_prefill(at, st));
+    }
     g = GemmArgs{};
     g.M = M; g.N = H; g.K = Qd;
     g.A = md->o16; g.lda = Qd; g.B = L.o16; g.ldb = Qd;
     g.epi = GEMM_ADD_F32; g.C = md->h; g.ldc = H;
-    HIP_TRY(launch_gemm(g, st));
-    HIP_TRY(launch_rmsnorm_rows(M, H, md->h, H, L.post_norm, 0, c.rms_eps, md->y16, 1, H, st));
+    if ((s2 = gemm_prof(K_GEMM_O, g))) return s2;
+    {
+      ProfScope ps(md, st, K_RMSNORM, norm_bytes, 0);
+      HIP_TRY(launch_rmsnorm_rows(M, H, md->h, H, L.post_norm, 0, c.rms_eps, md->y16, 1, H, st));
+    }
     g = GemmArgs{};
     g.M = M; g.N = I; g.K = H;
     g.A = md->y16; g.lda = H; g.B = L.gate16; g.B2 = L.up16; g.ldb = H;
     g.epi = GEMM_SWIGLU_F16; g.C16 = md->act16; g.ldc16 = I;
-    HIP_TRY(launch_gemm(g, st));
+    if ((s2 = gemm_prof(K_GEMM_GATEUP, g))) return s2;
     g = GemmArgs{};
     g.M = M; g.N = H; g.K = I;
     g.A = md->act16; g.lda = I; g.B = L.down16; g.ldb = I;
     g.epi = GEMM_ADD_F32; g.C = md->h; g.ldc = H;
-    HIP_TRY(launch_gemm(g, st));
+    if ((s2 = gemm_prof(K_GEMM_DOWN, g))) return s2;
   }
   if (!want_head) return DPK_OK;
   // final RMSNorm of the last row (fp32), then the weight-streaming head
@@ -418,7 +505,7 @@ dpk_status forward_gemm(dpk_model* md, int M, int start, int seq, bool want_head
 
 // fp32 weights (any M <= max_rows): plain kernels.
 dpk_status forward_f32(dpk_model* md, int M, int max_ctx, const int32_t* ids_dev, int head_r0, int head_n,
-                       float* logits, int32_t* argmax, hipStream_t st) {
+                       float* logits, int32_t* argmax, hipStream_t st, double kv_positions) {
   const dpk_config& c = md->cfg;
   const int H = c.hidden, d = c.head_dim, Qd = c.n_heads * d, KVd = c.n_kv_heads * d;
   const int Nqkv = Qd + 2 * KVd;
@@ -432,7 +519,7 @@ dpk_status forward_f32(dpk_model* md, int M, int max_ctx, const int32_t* ids_dev
     HIP_TRY(launch_gemv_f32(M, KVd, H, (const float*)L.v.w, nullptr, md->y32, H, md->qkv + Qd + KVd, Nqkv, 0, st));
     HIP_TRY(launch_qk_rope_kv(M, md->qkv, c.n_heads, c.n_kv_heads, d, c.qk_norm, L.q_norm, L.k_norm, 1, c.rms_eps,
                               md->rope_cos, md->rope_sin, md->rows_dev, md->qbuf, 0, md->kvd, l, st));
-    dpk_status s = attn_decode(md, M, max_ctx, md->qbuf, md->attn_o, l, st);
+    dpk_status s = attn_decode(md, M, max_ctx, md->qbuf, md->attn_o, l, st, kv_positions);
     if (s) return s;
     HIP_TRY(launch_gemv_f32(M, H, Qd, (const float*)L.o.w, nullptr, md->attn_o, Qd, md->h, H, 1, st));
     HIP_TRY(launch_rmsnorm_rows(M, H, md->h, H, L.post_norm, 1, c.rms_eps, md->y32, 0, H, st));
@@ -452,10 +539,13 @@ dpk_status forward_f32(dpk_model* md, int M, int max_ctx, const int32_t* ids_dev
 }
 
 // Rows already uploaded; pick the path by format and row count.
+// kv_positions: cached positions the attention must read (per distinct
+// sequence), for the profiler's byte count
 dpk_status forward_rows(dpk_model* md, int M, int max_ctx, const int32_t* ids_dev, int head_r0, int head_n,
-                        float* logits, int32_t* argmax, hipStream_t st) {
-  if (md->fmt == DPK_FMT_F32) return forward_f32(md, M, max_ctx, ids_dev, head_r0, head_n, logits, argmax, st);
-  return forward_skinny(md, M, max_ctx, ids_dev, head_r0, head_n, logits, argmax, st);
+                        float* logits, int32_t* argmax, hipStream_t st, double kv_positions) {
+  if (md->fmt == DPK_FMT_F32)
+    return forward_f32(md, M, max_ctx, ids_dev, head_r0, head_n, logits, argmax, st, kv_positions);
+  return forward_skinny(md, M, max_ctx, ids_dev, head_r0, head_n, logits, argmax, st, kv_positions);
 }
 
 int max_rows_for_path(const dpk_model* md) {
@@ -688,7 +778,7 @@ dpk_status dpk_prefill(dpk_model* md, int32_t seq, const int32_t* ids, int32_t n
     if (gemm_path && M > SKINNY_MAX)
       s = forward_gemm(md, M, r0, seq, last, logits, argmax, st);
     else
-      s = forward_rows(md, M, r0 + M, nullptr, M - 1, last ? 1 : 0, logits, argmax, st);
+      s = forward_rows(md, M, r0 + M, nullptr, M - 1, last ? 1 : 0, logits, argmax, st, r0 + M);
     if (s) return s;
   }
   md->seq_len[seq] = n;
@@ -717,7 +807,9 @@ dpk_status dpk_decode_step(dpk_model* md, int32_t batch, const int32_t* seqs, co
   }
   hipStream_t st = (hipStream_t)stream;
   if ((s = upload_rows(md, rows, batch, st))) return s;
-  if ((s = forward_rows(md, batch, max_ctx, ids_dev, 0, batch, logits, argmax, st))) return s;
+  double kvpos = 0;
+  for (int b = 0; b < batch; ++b) kvpos += pos[b] + 1;
+  if ((s = forward_rows(md, batch, max_ctx, ids_dev, 0, batch, logits, argmax, st, kvpos))) return s;
   for (int b = 0; b < batch; ++b) md->seq_len[seqs[b]] = pos[b] + 1;
   return DPK_OK;
 }
@@ -739,7 +831,7 @@ dpk_status dpk_verify(dpk_model* md, int32_t seq, const int32_t* ids, int32_t kp
   }
   hipStream_t st = (hipStream_t)stream;
   if ((s = upload_rows(md, rows, kp1, st))) return s;
-  if ((s = forward_rows(md, kp1, pos + kp1, nullptr, 0, kp1, logits, argmax, st))) return s;
+  if ((s = forward_rows(md, kp1, pos + kp1, nullptr, 0, kp1, logits, argmax, st, pos + kp1))) return s;
   HIP_TRY(hipMemcpyAsync(md->acc_host, argmax, sizeof(int32_t) * kp1, hipMemcpyDeviceToHost, st));
   HIP_TRY(hipStreamSynchronize(st));
   int m = 0;
@@ -770,8 +862,52 @@ dpk_status dpk_check_device_errors(dpk_model* md, void* stream) {
   return DPK_OK;
 }
 
+dpk_status dpk_profile_begin(dpk_model* md, int32_t max_launches) {
+  if (!md) return fail(DPK_EINVAL, "null model");
+  if (max_launches < 1) return fail(DPK_EINVAL, "max_launches must be >= 1");
+  if (md->prof) return fail(DPK_ESTATE, "profiling already active");
+  while ((int)md->prof_ev.size() < 2 * max_launches) {
+    hipEvent_t e;
+    HIP_TRY(hipEventCreate(&e));
+    md->prof_ev.push_back(e);
+  }
+  md->prof_max = max_launches;
+  md->prof_rec.clear();
+  md->prof_dropped = 0;
+  md->prof = true;
+  return DPK_OK;
+}
+
+dpk_status dpk_profile_end(dpk_model* md, dpk_kernel_stat* stats, int32_t max_stats, int32_t* n_stats) {
+  if (!md || !n_stats || (!stats && max_stats)) return fail(DPK_EINVAL, "null argument");
+  if (!md->prof) return fail(DPK_ESTATE, "profiling not active");
+  md->prof = false;
+  double ms[K_NCLASS] = {}, by[K_NCLASS] = {}, fl[K_NCLASS] = {};
+  long cnt[K_NCLASS] = {};
+  if (!md->prof_rec.empty()) HIP_TRY(hipEventSynchronize(md->prof_ev[2 * (md->prof_rec.size() - 1) + 1]));
+  for (size_t i = 0; i < md->prof_rec.size(); ++i) {
+    float t = 0.f;
+    HIP_TRY(hipEventElapsedTime(&t, md->prof_ev[2 * i], md->prof_ev[2 * i + 1]));
+    const int c = md->prof_rec[i].cls;
+    ms[c] += t;
+    by[c] += md->prof_rec[i].bytes;
+    fl[c] += md->prof_rec[i].flops;
+    ++cnt[c];
+  }
+  int n = 0;
+  for (int c = 0; c < K_NCLASS; ++c) {
+    if (!cnt[c]) continue;
+    if (n < max_stats) stats[n] = dpk_kernel_stat{kclass_name[c], cnt[c], ms[c], by[c], fl[c]};
+    ++n;
+  }
+  *n_stats = n;
+  if (md->prof_dropped) return fail(DPK_ERANGE, "%ld launches were not recorded (raise max_launches)", md->prof_dropped);
+  return DPK_OK;
+}
+
 void dpk_destroy(dpk_model* md) {
   if (!md) return;
+  for (hipEvent_t e : md->prof_ev) (void)hipEventDestroy(e);
   for (int i = 0; i < dpk_model::NSTAGE; ++i) {
     if (md->stage_ev[i]) {
       (void)hipEventSynchronize(md->stage_ev[i]);

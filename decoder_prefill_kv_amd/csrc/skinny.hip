@@ -263,12 +263,20 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(SkinnyArgs a) {
 #pragma unroll
       for (int v = 0; v < 4; ++v)
         if (col_on)
-          a.part[((size_t)ks * M + r16) * ldp + (size_t)block * rows + (wave * T + t) * 16 + 4 * j4 + v] = acc[t][v];
+          coh_store(a.part + ((size_t)ks * M + r16) * ldp + (size_t)block * rows + (wave * T + t) * 16 + 4 * j4 + v,
+                    acc[t][v]);
     if (!last_block_arrive(a.counters + 1 + block, a.ksplit, misc)) return;
     for (int i = tid; i < M * rows; i += THREADS) {
       const int m = i / rows, lr = i % rows;
+      const float* src = a.part + (size_t)m * ldp + (size_t)block * rows + lr;
+      const size_t kstride = (size_t)M * ldp;
+      // independent loads first (fixed summation order k2 = 0..ksplit-1)
+      float v[16];
+#pragma unroll
+      for (int k2 = 0; k2 < 16; ++k2) v[k2] = (k2 < a.ksplit) ? coh_load(src + k2 * kstride) : 0.f;
       float s = 0.f;
-      for (int k2 = 0; k2 < a.ksplit; ++k2) s += a.part[((size_t)k2 * M + m) * ldp + (size_t)block * rows + lr];
+#pragma unroll
+      for (int k2 = 0; k2 < 16; ++k2) s += v[k2];
       fin[m * rows + lr] = s;
     }
     __syncthreads();
@@ -295,13 +303,24 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(SkinnyArgs a) {
         sq += h * h;
       }
       sq = block_sum(sq, red + 16);
-      if (tid == 0) a.sq[m * nb + block] = sq;
+      if (tid == 0) coh_store(a.sq + m * nb + block, sq);
     }
     if (!last_block_arrive(a.counters, nb, misc)) return;
-    if (tid < M) {
+    // rs[m] = rsqrt(sum_b sq[m][b] / N + eps): one wave per row, lanes stride
+    // the blocks with independent loads, fixed-order wave reduction
+    for (int m = wave; m < M; m += WAVES) {
       float s = 0.f;
-      for (int b = 0; b < nb; ++b) s += a.sq[tid * nb + b];
-      a.rs_out[tid] = rsqrtf(s / (float)a.N + a.eps);
+      for (int b0 = 0; b0 < nb; b0 += 256) {
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int b = b0 + lane + 64 * u;
+          v[u] = b < nb ? coh_load(a.sq + m * nb + b) : 0.f;
+        }
+        s += (v[0] + v[1]) + (v[2] + v[3]);
+      }
+      s = wave_sum(s);
+      if (lane == 0) a.rs_out[m] = rsqrtf(s / (float)a.N + a.eps);
     }
     return;
   }
@@ -383,8 +402,8 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(SkinnyArgs a) {
         int bx = ri[0];
         for (int w = 1; w < WAVES; ++w)
           if (rv[w] > bv || (rv[w] == bv && ri[w] < bx)) { bv = rv[w]; bx = ri[w]; }
-        a.cand_val[m * nb + block] = bv;
-        a.cand_idx[m * nb + block] = bx;
+        coh_store(a.cand_val + m * nb + block, bv);
+        coh_store(a.cand_idx + m * nb + block, bx);
       }
       __syncthreads();
     }
@@ -392,10 +411,18 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(SkinnyArgs a) {
     for (int m = wave; m < M; m += WAVES) {
       float best = -INFINITY;
       int bi = 0x7fffffff;
-      for (int b = lane; b < nb; b += 64) {
-        const float v = a.cand_val[m * nb + b];
-        const int ix = a.cand_idx[m * nb + b];
-        if (v > best || (v == best && ix < bi)) { best = v; bi = ix; }
+      for (int b0 = 0; b0 < nb; b0 += 512) {
+        float v[8];
+        int ix[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int b = b0 + lane + 64 * u;
+          v[u] = b < nb ? coh_load(a.cand_val + m * nb + b) : -INFINITY;
+          ix[u] = b < nb ? coh_load(a.cand_idx + m * nb + b) : 0x7fffffff;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (v[u] > best || (v[u] == best && ix[u] < bi)) { best = v[u]; bi = ix[u]; }
       }
       wave_argmax(best, bi);
       if (lane == 0 && a.argmax_out) a.argmax_out[m] = bi;

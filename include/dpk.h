@@ -167,6 +167,24 @@ dpk_status dpk_seq_length(const dpk_model* m, int32_t seq, int32_t* length);
  * check (out-of-range device token ids): DPK_ERANGE if any, else DPK_OK. */
 dpk_status dpk_check_device_errors(dpk_model* m, void* stream);
 
+/* Per-kernel-class timing.  Between dpk_profile_begin and dpk_profile_end
+ * every launch of the library records a HIP event pair on its stream (at most
+ * max_launches launches; later ones are counted as dropped).  dpk_profile_end
+ * waits for the last event and returns, per kernel class, the number of
+ * launches, their summed duration in ms, and the summed algorithmic bytes and
+ * FLOPs of those launches (computed from the shapes: weights + activations
+ * read and written, causal attention pairs).  `name` points to a static
+ * string. */
+typedef struct {
+  const char* name;
+  int64_t launches;
+  double total_ms;
+  double bytes;
+  double flops;
+} dpk_kernel_stat;
+dpk_status dpk_profile_begin(dpk_model* m, int32_t max_launches);
+dpk_status dpk_profile_end(dpk_model* m, dpk_kernel_stat* stats, int32_t max_stats, int32_t* n_stats);
+
 /* Message of the last failure on the calling thread (valid until the next
  * call on this thread); "" if none. */
 const char* dpk_last_error(void);

@@ -22,6 +22,7 @@ def dpk():
 
 
 def test_library_exports_every_header_symbol(dpk):
+    dpk.lib()
     lib = ctypes.CDLL(dpk.library_path())
     names = header_functions()
     assert "dpk_prefill" in names and "dpk_verify" in names
