@@ -6,7 +6,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "_dpk.so")
-SOURCES = ["runtime.hip", "skinny.hip", "attn_decode.hip", "misc.hip", "gemm.hip", "attn_prefill.hip"]
+SOURCES = ["runtime.hip", "skinny.hip", "gemv.hip", "attn_decode.hip", "attn_decode_mfma.hip", "misc.hip", "gemm.hip", "attn_prefill.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-shared", "-std=c++17",
     # packed fp32 VALU ops are kept out of the generated code

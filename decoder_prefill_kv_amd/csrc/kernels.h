@@ -69,6 +69,32 @@ struct SkinnyArgs {
 };
 
 size_t skinny_lds_bytes(int M, int kchunk, int rows, int fmt);
+
+// ---- decode GEMV with the whole K in one workgroup (gemv.hip)
+struct GemvArgs {
+  int M, K, N;              // rows (<=16), input dim, output rows (per matrix for swiglu)
+  int fmt, tiles, swiglu, epi;
+  const void* w[3];
+  const uint16_t* sc[3];
+  const uint16_t* bi[3];
+  int seg_end[3];
+  int seg_rows[3];
+  const float* x;
+  int ldx;
+  const float* sq_in;       // [M][sq_nb] sums of squares of x's rows, or null (no norm)
+  int sq_nb;
+  const uint16_t* gain;     // bf16 [K] or null
+  float eps;
+  float* out;
+  int ldo;
+  float* sq_out;            // RESID: [M][n_blocks]
+  unsigned* counters;       // HEAD
+  float* cand_val;
+  int* cand_idx;
+  int* argmax_out;
+};
+size_t gemv_lds_bytes(int M, int K, int tiles, int fmt);
+hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream);
 hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t stream);
 
 // ---- decode attention (split-K over the context, merged in-kernel)
@@ -85,17 +111,32 @@ struct AttnDecodeArgs {
   unsigned* counters;         // [M * n_kv]
   float* out;                 // [M][n_heads*d] fp32
   float scale;                // 1/sqrt(d)
+  // raw mode (qkv_raw != null): q is taken from the raw projection
+  // [M][ld_raw] (q heads, k heads, v heads) and gets QK-norm + RoPE here; the
+  // workgroup whose chunk holds the row's position computes that position's
+  // k and v, stores them in the cache and uses them.  Each row's sequence
+  // must have exactly one new position (a decode step).
+  const float* qkv_raw;
+  int ld_raw;
+  const uint16_t* qn;         // bf16 gains or null
+  const uint16_t* kn;
+  const float* rope_cos;
+  const float* rope_sin;
+  float eps;
 };
 hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t stream);
 int attn_decode_chunk();  // positions per decode-attention workgroup
+// same contract on matrix cores, fp16 caches only (attn_decode_mfma.hip)
+hipError_t launch_attn_decode_mfma(const AttnDecodeArgs& a, hipStream_t stream);
 
 // ---- misc
 hipError_t launch_rope_table(float* cos_t, float* sin_t, int max_seq, int d, double theta,
                              hipStream_t stream);
-// h[m] = E[token_m] (fp32 / bf16 / q4 table); rs[m] = rsqrt(mean(h^2)+eps) if rs != null
+// h[m] = E[token_m] (fp32 / bf16 / q4 table); rs[m] = rsqrt(mean(h^2)+eps) if rs != null;
+// sq[m] = sum(h^2) if sq != null
 hipError_t launch_embed(int M, int H, int fmt, const void* table, const uint16_t* sc, const uint16_t* bi,
                         const RowParam* rp, const int32_t* ids_dev, int vocab, float* h, float* rs,
-                        float eps, int* err_flag, hipStream_t stream);
+                        float eps, int* err_flag, hipStream_t stream, float* sq = nullptr);
 // y[m] = x[m] * rsqrt(mean(x^2)+eps) * g; y_is_f16: 0 fp32, 1 fp16, 2 fp16 hi
 // in columns [0, H) and fp16 lo (= y - hi) in [H, 2H); g is fp32 or bf16
 hipError_t launch_rmsnorm_rows(int M, int H, const float* x, int ldx, const void* g, int g_is_f32,

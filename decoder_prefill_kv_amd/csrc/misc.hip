@@ -24,7 +24,7 @@ __global__ void rope_table_kernel(float* cos_t, float* sin_t, int max_seq, int d
 // one workgroup per row; token from RowParam (or ids_dev when given)
 __global__ void embed_kernel(int H, int fmt, const void* table, const uint16_t* sc, const uint16_t* bi,
                              const RowParam* rp, const int32_t* ids_dev, int vocab, float* h, float* rs,
-                             float eps, int* err_flag) {
+                             float eps, int* err_flag, float* sq) {
   __shared__ float red[32];
   const int m = blockIdx.x;
   int tok = ids_dev ? ids_dev[m] : rp[m].token;
@@ -48,9 +48,10 @@ __global__ void embed_kernel(int H, int fmt, const void* table, const uint16_t* 
     h[(size_t)m * H + k] = v;
     ss += v * v;
   }
-  if (rs) {
+  if (rs || sq) {
     ss = block_sum(ss, red);
-    if (threadIdx.x == 0) rs[m] = rsqrtf(ss / (float)H + eps);
+    if (threadIdx.x == 0 && rs) rs[m] = rsqrtf(ss / (float)H + eps);
+    if (threadIdx.x == 0 && sq) sq[m] = ss;
   }
 }
 
@@ -225,9 +226,9 @@ hipError_t launch_rope_table(float* cos_t, float* sin_t, int max_seq, int d, dou
 
 hipError_t launch_embed(int M, int H, int fmt, const void* table, const uint16_t* sc, const uint16_t* bi,
                         const RowParam* rp, const int32_t* ids_dev, int vocab, float* h, float* rs, float eps,
-                        int* err_flag, hipStream_t stream) {
+                        int* err_flag, hipStream_t stream, float* sq) {
   hipLaunchKernelGGL(embed_kernel, dim3(M), dim3(256), 0, stream, H, fmt, table, sc, bi, rp, ids_dev, vocab, h, rs,
-                     eps, err_flag);
+                     eps, err_flag, sq);
   return hipGetLastError();
 }
 

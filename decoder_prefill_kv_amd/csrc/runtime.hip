@@ -321,7 +321,7 @@ dpk_status skinny(dpk_model* md, int cls, int M, const float* x, int ldx, const 
 }
 
 dpk_status attn_decode(dpk_model* md, int M, int max_ctx, const float* q, float* out, int layer, hipStream_t st,
-                       double kv_positions) {
+                       double kv_positions, const float* qkv_raw = nullptr) {
   const dpk_config& c = md->cfg;
   AttnDecodeArgs a{};
   a.M = M;
@@ -339,14 +339,119 @@ dpk_status attn_decode(dpk_model* md, int M, int max_ctx, const float* q, float*
   a.counters = md->attn_counters;
   a.out = out;
   a.scale = 1.0f / sqrtf((float)c.head_dim);
+  if (qkv_raw) {
+    const LayerW& L = md->layers[layer];
+    a.qkv_raw = qkv_raw;
+    a.ld_raw = md->Nqkv;
+    a.qn = c.qk_norm ? (const uint16_t*)L.q_norm : nullptr;
+    a.kn = c.qk_norm ? (const uint16_t*)L.k_norm : nullptr;
+    a.rope_cos = md->rope_cos;
+    a.rope_sin = md->rope_sin;
+    a.eps = c.rms_eps;
+  }
   {
     const double elt = md->kvd.is_f32 ? 4 : 2;
     const double kvb = kv_positions * 2.0 * c.n_kv_heads * c.head_dim * elt;
     const double io = 2.0 * M * c.n_heads * c.head_dim * 4;
     ProfScope ps(md, st, K_ATTN_DECODE, kvb + io, 4.0 * kv_positions * c.n_heads * c.head_dim);
-    HIP_TRY(launch_attn_decode(a, st));
+    HIP_TRY(md->kvd.is_f32 ? launch_attn_decode(a, st) : launch_attn_decode_mfma(a, st));
   }
   return DPK_OK;
+}
+
+// One decode GEMV launch (whole K per workgroup, gemv.hip).
+dpk_status gemv(dpk_model* md, int cls, int M, const float* x, int ldx, const float* sq_in, int sq_nb,
+                const void* gain, const LinearW* segs, int nseg, int epi, bool swiglu, int tiles, float* out,
+                int ldo, float* sq_out, int32_t* argmax, hipStream_t st) {
+  const dpk_config& c = md->cfg;
+  GemvArgs a{};
+  a.M = M;
+  a.K = segs[0].cols;
+  a.fmt = md->fmt == DPK_FMT_Q4G64 ? W_Q4 : W_BF16;
+  a.tiles = tiles;
+  a.swiglu = swiglu;
+  a.epi = epi;
+  int n = 0;
+  for (int i = 0; i < 3; ++i) {
+    const LinearW& sg = segs[i < nseg ? i : nseg - 1];
+    a.w[i] = sg.w;
+    a.sc[i] = sg.sc;
+    a.bi[i] = sg.bi;
+    if (i < nseg) n += sg.rows;
+    a.seg_end[i] = n;
+    a.seg_rows[i] = sg.rows;
+  }
+  a.N = swiglu ? segs[0].rows : n;
+  a.x = x;
+  a.ldx = ldx;
+  a.sq_in = sq_in;
+  a.sq_nb = sq_nb;
+  a.gain = (const uint16_t*)gain;
+  a.eps = c.rms_eps;
+  a.out = out;
+  a.ldo = ldo;
+  a.sq_out = sq_out;
+  a.counters = md->counters;
+  a.cand_val = md->cand_val;
+  a.cand_idx = md->cand_idx;
+  a.argmax_out = argmax ? argmax : md->argmax_sink;
+  const double nrows = swiglu ? 2.0 * a.N : (double)a.N;
+  ProfScope ps(md, st, cls, nrows * a.K * wbytes_per_elem(md->fmt) + (double)M * a.K * 4 + (double)M * a.N * 4,
+               2.0 * M * nrows * a.K);
+  HIP_TRY(launch_gemv(a, st));
+  return DPK_OK;
+}
+
+// Can a decode step of M rows run on the whole-K GEMV kernels?
+bool decode_fits(const dpk_model* md, int M) {
+  if (md->fmt == DPK_FMT_F32) return false;
+  const dpk_config& c = md->cfg;
+  const int fmt = md->fmt == DPK_FMT_Q4G64 ? W_Q4 : W_BF16;
+  for (int K : {c.hidden, c.n_heads * c.head_dim, c.intermediate}) {
+    if (K % 1024) return false;
+    if (gemv_lds_bytes(M, K, 4, fmt) > 64 * 1024) return false;
+  }
+  return true;
+}
+
+// Decode step of M rows (distinct sequences, one new position each) whose
+// parameters are in md->rows_dev: every layer is QKV GEMV -> attention (with
+// QK-norm, RoPE and the KV write) -> O GEMV + residual -> gate/up GEMV +
+// SwiGLU -> down GEMV + residual; then the lm_head with the greedy argmax.
+dpk_status forward_decode(dpk_model* md, int M, int max_ctx, const int32_t* ids_dev, float* logits, int32_t* argmax,
+                          hipStream_t st, double kv_positions) {
+  const dpk_config& c = md->cfg;
+  const int H = c.hidden, Qd = c.n_heads * c.head_dim;
+  {
+    ProfScope ps(md, st, K_EMBED, (double)M * H * 6, 0);
+    HIP_TRY(launch_embed(M, H, md->fmt == DPK_FMT_Q4G64 ? W_Q4 : W_BF16, md->embed.w, md->embed.sc, md->embed.bi,
+                         md->rows_dev, ids_dev, c.vocab, md->h, nullptr, c.rms_eps, md->err_flag, st, md->sq));
+  }
+  int sq_nb = 1;
+  const int nb_resid = H / 16;
+  dpk_status s;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const LayerW& L = md->layers[l];
+    LinearW qkv[3] = {L.q, L.k, L.v};
+    if ((s = gemv(md, K_GEMV_QKV, M, md->h, H, md->sq, sq_nb, L.in_norm, qkv, 3, EPI_STORE, false, 1, md->qkv,
+                  md->Nqkv, nullptr, nullptr, st)))
+      return s;
+    if ((s = attn_decode(md, M, max_ctx, nullptr, md->attn_o, l, st, kv_positions, md->qkv))) return s;
+    if ((s = gemv(md, K_GEMV_O, M, md->attn_o, Qd, nullptr, 0, nullptr, &L.o, 1, EPI_RESID, false, 1, md->h, H, md->sq,
+                  nullptr, st)))
+      return s;
+    sq_nb = nb_resid;
+    LinearW gu[2] = {L.gate, L.up};
+    if ((s = gemv(md, K_GEMV_GATEUP, M, md->h, H, md->sq, sq_nb, L.post_norm, gu, 2, EPI_SWIGLU, true, 2, md->act,
+                  c.intermediate, nullptr, nullptr, st)))
+      return s;
+    if ((s = gemv(md, K_GEMV_DOWN, M, md->act, c.intermediate, nullptr, 0, nullptr, &L.down, 1, EPI_RESID, false, 1,
+                  md->h, H, md->sq, nullptr, st)))
+      return s;
+  }
+  float* dst = logits ? logits : md->sink;
+  return gemv(md, K_GEMV_HEAD, M, md->h, H, md->sq, sq_nb, md->final_norm, &md->head, 1, EPI_HEAD, false, 4, dst,
+              c.vocab, nullptr, argmax, st);
 }
 
 // Final norm + lm_head + greedy argmax for `rows` rows of x (weight-streaming
@@ -809,7 +914,11 @@ dpk_status dpk_decode_step(dpk_model* md, int32_t batch, const int32_t* seqs, co
   if ((s = upload_rows(md, rows, batch, st))) return s;
   double kvpos = 0;
   for (int b = 0; b < batch; ++b) kvpos += pos[b] + 1;
-  if ((s = forward_rows(md, batch, max_ctx, ids_dev, 0, batch, logits, argmax, st, kvpos))) return s;
+  if (decode_fits(md, batch))
+    s = forward_decode(md, batch, max_ctx, ids_dev, logits, argmax, st, kvpos);
+  else
+    s = forward_rows(md, batch, max_ctx, ids_dev, 0, batch, logits, argmax, st, kvpos);
+  if (s) return s;
   for (int b = 0; b < batch; ++b) md->seq_len[seqs[b]] = pos[b] + 1;
   return DPK_OK;
 }
