@@ -71,12 +71,15 @@ struct SkinnyArgs {
 size_t skinny_lds_bytes(int M, int kchunk, int rows, int fmt);
 
 // ---- decode GEMV with the whole K in one workgroup (gemv.hip)
+// Weights are given in the re-tiled fragment layout (launch_tile_bf16 /
+// launch_tile_q4): w = tiled bf16 or tiled 4-bit codes, sb = tiled 4-bit
+// (scale, bias) pairs.  Every segment has a multiple of 16 rows.
 struct GemvArgs {
   int M, K, N;              // rows (<=16), input dim, output rows (per matrix for swiglu)
   int fmt, tiles, swiglu, epi;
+  int grid;                 // workgroups (they loop over row tiles)
   const void* w[3];
-  const uint16_t* sc[3];
-  const uint16_t* bi[3];
+  const void* sb[3];
   int seg_end[3];
   int seg_rows[3];
   const float* x;
@@ -87,14 +90,18 @@ struct GemvArgs {
   float eps;
   float* out;
   int ldo;
-  float* sq_out;            // RESID: [M][n_blocks]
+  float* sq_out;            // RESID: [M][row tiles]
   unsigned* counters;       // HEAD
-  float* cand_val;
+  float* cand_val;          // HEAD: [M][grid]
   int* cand_idx;
   int* argmax_out;
 };
 size_t gemv_lds_bytes(int M, int K, int tiles, int fmt);
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream);
+// fragment-order copies of [N][K] weights for launch_gemv
+hipError_t launch_tile_bf16(const uint16_t* src, uint16_t* dst, int N, int K, hipStream_t stream);
+hipError_t launch_tile_q4(const uint32_t* codes, const uint16_t* sc, const uint16_t* bi, uint32_t* dst_c,
+                          uint32_t* dst_sb, int N, int K, hipStream_t stream);
 hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t stream);
 
 // ---- decode attention (split-K over the context, merged in-kernel)

@@ -37,6 +37,9 @@ struct LinearW {
   const uint16_t* sc = nullptr;   // q4
   const uint16_t* bi = nullptr;   // q4
   int rows = 0, cols = 0;
+  // decode copy in fragment order (prep buffer): bf16 or q4 codes, q4 (s, b)
+  const void* wt = nullptr;
+  const void* sbt = nullptr;
 };
 
 struct LayerW {
@@ -75,6 +78,7 @@ struct dpk_model {
   int* err_flag = nullptr;
   int* argmax_sink = nullptr;
   int rows_f32 = 0;       // rows of the fp32 activation buffers
+  int n_cu = 256;         // compute units of the bound device
   int attn_chunks_cap = 0;
   size_t part_floats = 0;
   // pinned staging for row parameters
@@ -163,12 +167,22 @@ ScratchLayout scratch_layout(const dpk_config& c) {
   return L;
 }
 
+// bytes of the fragment-order decode copy of one [rows][cols] linear layer
+size_t tiled_bytes(const dpk_config& c, size_t rows, size_t cols) {
+  if (c.weight_format == DPK_FMT_BF16) return up(rows * cols * 2);
+  return up(rows * cols / 2) + up(rows * (cols / 64) * 4);  // codes + (s, b) pairs
+}
+
 size_t prep_bytes(const dpk_config& c) {
   if (c.weight_format == DPK_FMT_F32) return 0;
   const size_t H = c.hidden, I = c.intermediate, d = c.head_dim;
-  const size_t Nqkv = (c.n_heads + 2 * c.n_kv_heads) * d, Qd = (size_t)c.n_heads * d;
+  const size_t Nqkv = (c.n_heads + 2 * c.n_kv_heads) * d, Qd = (size_t)c.n_heads * d, KVd = (size_t)c.n_kv_heads * d;
+  // fp16 prefill operands
   size_t per = up(Nqkv * H * 2) + up(H * Qd * 2) + 2 * up(I * H * 2) + up(H * I * 2);
-  return per * c.n_layers;
+  // decode copies
+  per += tiled_bytes(c, Qd, H) + 2 * tiled_bytes(c, KVd, H) + tiled_bytes(c, H, Qd) + 2 * tiled_bytes(c, I, H) +
+         tiled_bytes(c, H, I);
+  return per * c.n_layers + tiled_bytes(c, c.vocab, H);
 }
 
 // positions per KV slab row: max_seq rounded up to a multiple of 64 so that
@@ -374,14 +388,14 @@ dpk_status gemv(dpk_model* md, int cls, int M, const float* x, int ldx, const fl
   int n = 0;
   for (int i = 0; i < 3; ++i) {
     const LinearW& sg = segs[i < nseg ? i : nseg - 1];
-    a.w[i] = sg.w;
-    a.sc[i] = sg.sc;
-    a.bi[i] = sg.bi;
+    a.w[i] = sg.wt;
+    a.sb[i] = sg.sbt;
     if (i < nseg) n += sg.rows;
     a.seg_end[i] = n;
     a.seg_rows[i] = sg.rows;
   }
   a.N = swiglu ? segs[0].rows : n;
+  a.grid = md->n_cu;
   a.x = x;
   a.ldx = ldx;
   a.sq_in = sq_in;
@@ -450,7 +464,7 @@ dpk_status forward_decode(dpk_model* md, int M, int max_ctx, const int32_t* ids_
       return s;
   }
   float* dst = logits ? logits : md->sink;
-  return gemv(md, K_GEMV_HEAD, M, md->h, H, md->sq, sq_nb, md->final_norm, &md->head, 1, EPI_HEAD, false, 4, dst,
+  return gemv(md, K_GEMV_HEAD, M, md->h, H, md->sq, sq_nb, md->final_norm, &md->head, 1, EPI_HEAD, false, 1, dst,
               c.vocab, nullptr, argmax, st);
 }
 
@@ -752,6 +766,12 @@ dpk_status dpk_bind_workspace(dpk_model* md, void* kv, void* scratch, void* prep
     if (!md->stage_ev[i]) HIP_TRY(hipEventCreateWithFlags(&md->stage_ev[i], hipEventDisableTiming));
   }
   if (!md->acc_host) HIP_TRY(hipHostMalloc((void**)&md->acc_host, sizeof(int32_t) * 32, hipHostMallocDefault));
+  {
+    int dev = 0, ncu = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    HIP_TRY(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
+    if (ncu > 0) md->n_cu = ncu;
+  }
   HIP_TRY(hipMemsetAsync(md->counters, 0, (1 + nblocks_max(c)) * 4, st));
   HIP_TRY(hipMemsetAsync(md->attn_counters, 0, (size_t)(md->fmt == DPK_FMT_F32 ? c.max_rows : SKINNY_MAX) * c.n_kv_heads * 4, st));
   HIP_TRY(hipMemsetAsync(md->err_flag, 0, 4, st));
@@ -855,6 +875,24 @@ dpk_status dpk_load_weights(dpk_model* md, const dpk_tensor* t, int32_t n, void*
       HIP_TRY(conv(L.down, L.down16));
       p += up((size_t)H * I * 2);
     }
+    // fragment-order decode copies
+    auto tile = [&](LinearW& w) -> hipError_t {
+      w.wt = p;
+      if (fmt == DPK_FMT_BF16) {
+        p += up((size_t)w.rows * w.cols * 2);
+        return launch_tile_bf16((const uint16_t*)w.w, (uint16_t*)w.wt, w.rows, w.cols, st);
+      }
+      p += up((size_t)w.rows * w.cols / 2);
+      w.sbt = p;
+      p += up((size_t)w.rows * (w.cols / 64) * 4);
+      return launch_tile_q4((const uint32_t*)w.w, w.sc, w.bi, (uint32_t*)w.wt, (uint32_t*)w.sbt, w.rows, w.cols, st);
+    };
+    for (int l = 0; l < c.n_layers; ++l) {
+      LayerW& L = md->layers[l];
+      for (LinearW* w : {&L.q, &L.k, &L.v, &L.o, &L.gate, &L.up, &L.down}) HIP_TRY(tile(*w));
+    }
+    HIP_TRY(tile(md->head));
+    if ((size_t)(p - (char*)md->prep) > prep_bytes(c)) return fail(DPK_EINVAL, "internal: prep layout overflow");
   }
   md->loaded = true;
   return DPK_OK;

@@ -55,7 +55,9 @@ def test_workspace_sizes_and_call_order(dpk):
         kv, sc, pr = dpk.workspace_size(h)
         # 2 slots x 2 layers x {K,V} x 8 heads x 640 x 128 x fp16
         assert kv == 2 * 2 * 2 * 8 * 640 * 128 * 2
-        assert sc > 0 and pr == 2 * (4096 * 1024 + 1024 * 2048 + 2 * 3072 * 1024 + 1024 * 3072) * 2
+        per_layer = (4096 * 1024 + 1024 * 2048 + 2 * 3072 * 1024 + 1024 * 3072) * 2
+        # fp16 prefill operands + fragment-order bf16 decode copy, plus the tiled head
+        assert sc > 0 and pr == 2 * (2 * per_layer) + 151936 * 1024 * 2
         for call in (lambda: dpk.prefill(h, 0, [1, 2, 3], stream=0),
                      lambda: dpk.decode_step(h, [0], [1], [0], None, stream=0),
                      lambda: dpk.verify(h, 0, [1, 2], 0, None, stream=0)):

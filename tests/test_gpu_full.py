@@ -66,3 +66,100 @@ def test_full_size_greedy_run(dpk, name):
     dec.close()
     assert not bad, "decode steps over tolerance: %s" % bad[:5]
     assert not mism, "greedy ids differ at non-tie steps %s" % mism
+
+
+def _compare_row(row, g, i, tol, what):
+    """Sampled + top-16 logits of GPU row (device tensor) vs fixture row i."""
+    idx = torch.from_numpy(g["sample_idx"].astype(np.int64)).to(row.device)
+    samp = row[idx].cpu().double().numpy()
+    top = row[torch.from_numpy(g["top_idx"][i].astype(np.int64)).to(row.device)].cpu().double().numpy()
+    e = max(np.abs(samp - g["sample"][i]).max(), np.abs(top - g["top_val"][i]).max())
+    assert e <= tol, "%s: max-abs %.4g" % (what, e)
+    return e
+
+
+def test_full_size_speculative_verify(dpk):
+    """8B-shaped model: verify K=5 drafts (M=6 rows) against a KV cache of
+    8192 prompt tokens, 8 rounds along the greedy trajectory."""
+    g = np.load(os.path.join(GOLDEN, "q8b_verify.npz"))
+    cfg = synth.Q8B
+    P, K = int(g["prompt_len"]), int(g["K"])
+    rounds = g["rounds"]
+    print("\n[full] verify P=%d K=%d rounds=%d" % (P, K, len(rounds)), flush=True)
+    w = synth.make_weights(cfg, 0)
+    prompt = [int(t) for t in synth.prompt_ids(cfg, P, 0)]
+    dec = dpk.Decoder(cfg, w, max_batch=1, max_seq=P + (K + 1) * len(rounds) + 1, max_rows=P)
+    del w
+    tol = TOL["bf16"]
+    lg = dec.logits_buffer(K + 1)
+    am = dec.argmax_buffer(K + 1)
+    dec.prefill(0, prompt, lg[0:1], am[0:1])
+    d0 = np.abs(lg[0].cpu().double().numpy() - g["prefill_logits"].astype(np.float64)).max()
+    print("[full] verify prefill(8192) max-abs %.4g" % d0, flush=True)
+    assert d0 <= tol
+    worst = 0.0
+    for r, rec in enumerate(rounds):
+        pos, acc, bonus = int(rec[0]), int(rec[1]), int(rec[2])
+        ids = [int(x) for x in rec[3:3 + K + 1]]
+        acc_gpu = dec.verify(0, ids, pos, am, lg)
+        gam = am.cpu().tolist()
+        for i in range(K + 1):
+            j = r * (K + 1) + i
+            worst = max(worst, _compare_row(lg[i], g, j, tol, "round %d row %d" % (r, i)))
+            assert gam[i] == int(g["id"][j]) or bool(g["exempt"][j]), "round %d row %d argmax" % (r, i)
+        tie = any(bool(g["exempt"][r * (K + 1) + i]) for i in range(min(acc, acc_gpu) + 1))
+        print("[full] verify round %d pos %d accepted gpu %d oracle %d" % (r, pos, acc_gpu, acc), flush=True)
+        assert acc_gpu == acc or tie
+        if acc_gpu != acc:
+            break
+        assert dec.seq_length(0) == pos + acc + 1 and gam[acc] == bonus
+    print("[full] verify worst max-abs %.4g" % worst, flush=True)
+    dec.close()
+
+
+def test_full_size_batch16_decode(dpk):
+    """8B-shaped model: 16 independent 4096-token caches decoded at batch 16;
+    sequences 0 and 15 against the oracle (teacher-forced), sequence 7 against
+    a batch-1 decode of the same sequence on the GPU."""
+    g = np.load(os.path.join(GOLDEN, "q8b_batch16.npz"))
+    cfg = synth.Q8B
+    P, N, B = int(g["s0_prompt_len"]), int(g["s0_n_steps"]), 16
+    print("\n[full] batch16 P=%d N=%d" % (P, N), flush=True)
+    w = synth.make_weights(cfg, 0)
+    dec = dpk.Decoder(cfg, w, max_batch=B, max_seq=P + N, max_rows=P)
+    del w
+    tol = TOL["bf16"]
+    lg = dec.logits_buffer(B)
+    am = dec.argmax_buffer(B)
+    for b in range(B):
+        dec.prefill(b, [int(t) for t in synth.prompt_ids(cfg, P, 0, index=b)], lg[b:b + 1], am[b:b + 1])
+    for b in (0, 15):
+        d0 = np.abs(lg[b].cpu().double().numpy() - g["s%d_prefill_logits" % b].astype(np.float64)).max()
+        print("[full] batch16 seq %d prefill max-abs %.4g" % (b, d0), flush=True)
+        assert d0 <= tol
+    toks = am.cpu().tolist()
+    toks[0], toks[15] = int(g["s0_id"][0]), int(g["s15_id"][0])
+    fed7, logits7 = [], []
+    worst = 0.0
+    for s in range(N):
+        fed7.append(toks[7])
+        dec.decode_step(list(range(B)), toks, [P + s] * B, am, lg)
+        logits7.append(lg[7].cpu())
+        for b in (0, 15):
+            sub = {k[len("s%d_" % b):]: g[k] for k in g.files if k.startswith("s%d_" % b)}
+            worst = max(worst, _compare_row(lg[b], sub, s + 1, tol, "seq %d step %d" % (b, s)))
+            assert int(am[b].cpu()) == int(sub["id"][s + 1]) or bool(sub["exempt"][s + 1])
+        toks = am.cpu().tolist()
+        toks[0], toks[15] = int(g["s0_id"][s + 1]), int(g["s15_id"][s + 1])
+    print("[full] batch16 worst max-abs vs oracle %.4g" % worst, flush=True)
+    # batch invariance: sequence 7 alone (batch 1) with the same tokens
+    dec.prefill(7, [int(t) for t in synth.prompt_ids(cfg, P, 0, index=7)])
+    l1 = dec.logits_buffer(1)
+    a1 = dec.argmax_buffer(1)
+    inv = 0.0
+    for s in range(N):
+        dec.decode_step([7], [fed7[s]], [P + s], a1, l1)
+        inv = max(inv, float((l1[0].cpu() - logits7[s]).abs().max()))
+    print("[full] batch16 row 7 vs batch-1 decode max-abs %.3g" % inv, flush=True)
+    assert inv <= tol
+    dec.close()
