@@ -23,6 +23,29 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 matrix throughput
 
+# Measured HBM traffic per launch of the dominant decode kernel: two rocprofv3
+# --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),
+# each scaled by what the same counter reads for a plain 1 GiB device copy
+# (--copy-probe): FETCH_SIZE x 2.0, WRITE_SIZE x 1.0.  A figure is only
+# reported while the kernel's source is the one it was taken on.
+TRAFFIC = {
+    ("q8b", "gemv.gate_up"): {"fetch_kib": 98491.6, "write_kib": 48.0, "fetch_factor": 2.0, "write_factor": 1.0,
+                              "source": "decoder_prefill_kv_amd/csrc/gemv.hip",
+                              "sha256": "8cd541b00fbdfba0567029a64bfd74966844a74942b986bd8db1d13f8ca4f559"},
+}
+
+
+def measured_traffic(workload, kclass):
+    import hashlib
+    t = TRAFFIC.get((workload, kclass))
+    if not t:
+        return None
+    with open(os.path.join(ROOT, t["source"]), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != t["sha256"]:
+            return None
+    return 1024.0 * (t["fetch_kib"] * t["fetch_factor"] + t["write_kib"] * t["write_factor"])
+
+
 WORKLOADS = {
     # name: (config, prompt, decode steps, description)
     "q8b": ("q8b", 2048, 256, "Qwen3-8B-shaped bf16 decoder (36 layers, hidden 4096, 32/8 heads, d 128, MLP 12288, "
@@ -54,6 +77,20 @@ def cpu_baseline(cfg, w):
                       "at position 0; %.1f s" % dt}
 
 
+def copy_probe(nbytes):
+    """A plain copy kernel of known size: reads and writes nbytes once each.
+    Counter runs over it give the factor between what FETCH_SIZE / WRITE_SIZE
+    report and the bytes actually moved."""
+    import torch
+    n = (nbytes + 15) // 16 * 16
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -63,7 +100,14 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel profiled pass")
+    ap.add_argument("--decode-steps", type=int, default=None,
+                    help="override the workload's decode step count (for counter runs; not a bench figure)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes (calibrates HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
@@ -73,6 +117,8 @@ def main():
     import decoder_prefill_kv_amd as dpk
 
     cname, P, N, desc = WORKLOADS[args.workload]
+    if args.decode_steps is not None:
+        N = args.decode_steps
     cfg = synth.CONFIGS[cname]
     t0 = time.time()
     w = synth.make_weights(cfg, args.seed)
@@ -144,7 +190,7 @@ def main():
         avg_s = v["total_ms"] / 1e3 / v["launches"]
         ach = v["bytes"] / v["launches"] / avg_s / 1e9
         roof = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload, dom),
                 "bytes_per_launch": v["bytes"] / v["launches"], "avg_launch_us": round(avg_s * 1e6, 2)}
         gem = {k: v for k, v in stats.items() if k.startswith("gemm")}
         if gem:

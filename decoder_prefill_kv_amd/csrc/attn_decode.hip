@@ -275,10 +275,10 @@ int attn_decode_chunk() { return CHUNK; }
 template <typename KT, int D>
 hipError_t launch_g(const AttnDecodeArgs& a, dim3 grid, hipStream_t stream) {
   switch (a.n_heads / a.n_kv) {
-    case 1: hipLaunchKernelGGL((attn_decode_kernel<KT, D, 1>), grid, dim3(THREADS), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((attn_decode_kernel<KT, D, 2>), grid, dim3(THREADS), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((attn_decode_kernel<KT, D, 4>), grid, dim3(THREADS), 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((attn_decode_kernel<KT, D, 8>), grid, dim3(THREADS), 0, stream, a); break;
+    case 1: launch((attn_decode_kernel<KT, D, 1>), grid, dim3(THREADS), 0, stream, a); break;
+    case 2: launch((attn_decode_kernel<KT, D, 2>), grid, dim3(THREADS), 0, stream, a); break;
+    case 4: launch((attn_decode_kernel<KT, D, 4>), grid, dim3(THREADS), 0, stream, a); break;
+    case 8: launch((attn_decode_kernel<KT, D, 8>), grid, dim3(THREADS), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -324,9 +324,9 @@ hipError_t launch_attn_decode_mfma(const AttnDecodeArgs& a, hipStream_t stream) 
     return hipErrorInvalidValue;
   dim3 grid(a.max_chunks, a.n_kv, a.M);
   if (a.d == 128)
-    hipLaunchKernelGGL(attn_decode_mfma_kernel<128>, grid, dim3(THREADS), 0, stream, a);
+    launch(attn_decode_mfma_kernel<128>, grid, dim3(THREADS), 0, stream, a);
   else if (a.d == 64)
-    hipLaunchKernelGGL(attn_decode_mfma_kernel<64>, grid, dim3(THREADS), 0, stream, a);
+    launch(attn_decode_mfma_kernel<64>, grid, dim3(THREADS), 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

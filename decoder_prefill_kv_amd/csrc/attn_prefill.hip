@@ -174,7 +174,7 @@ hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t stream) {
   const int rbpw = 4 / hpw;
   const int n_rb = (a.M + 32 * rbpw - 1) / (32 * rbpw);
   dim3 grid(n_rb, a.n_heads / hpw);
-  hipLaunchKernelGGL(attn_prefill_kernel, grid, dim3(THREADS), 0, stream, a, hpw, rbpw, n_rb);
+  launch(attn_prefill_kernel, grid, dim3(THREADS), 0, stream, a, hpw, rbpw, n_rb);
   return hipGetLastError();
 }
 

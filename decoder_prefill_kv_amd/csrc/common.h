@@ -1,6 +1,7 @@
 // Shared device/host definitions for the dpk kernels (gfx950 / CDNA4).
 #pragma once
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 #define DPK_DEV __device__ __forceinline__
@@ -14,6 +15,22 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 namespace dpk {
+
+// Kernel-class timing.  While a profiling scope is open on this thread every
+// launch takes its timestamps from the dispatch itself (hipExtLaunchKernel's
+// start/stop events), so a class's duration excludes the gaps between
+// kernels.  The first launch of a scope records start and stop, later ones
+// only move stop.
+struct LaunchTiming {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+extern thread_local LaunchTiming g_timing;
+
+template <typename F, typename... Args>
+inline void launch(F kernel, dim3 grid, dim3 block, unsigned shmem, hipStream_t st, Args... args) {
+  hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, g_timing.start, g_timing.stop, 0u, args...);
+  g_timing.start = nullptr;
+}
 
 // One row of a forward call: the token it embeds, the position it occupies
 // and the KV-cache slot (sequence) it belongs to.  A row attends to every

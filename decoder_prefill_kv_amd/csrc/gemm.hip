@@ -153,9 +153,9 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.N % ntile) return hipErrorInvalidValue;
   dim3 grid(a.N / ntile, (a.M + BM - 1) / BM);
   switch (a.epi) {
-    case GEMM_STORE_F32: hipLaunchKernelGGL(gemm_kernel<GEMM_STORE_F32>, grid, dim3(THREADS), 0, stream, a); break;
-    case GEMM_ADD_F32: hipLaunchKernelGGL(gemm_kernel<GEMM_ADD_F32>, grid, dim3(THREADS), 0, stream, a); break;
-    case GEMM_SWIGLU_F16: hipLaunchKernelGGL(gemm_kernel<GEMM_SWIGLU_F16>, grid, dim3(THREADS), 0, stream, a); break;
+    case GEMM_STORE_F32: launch(gemm_kernel<GEMM_STORE_F32>, grid, dim3(THREADS), 0, stream, a); break;
+    case GEMM_ADD_F32: launch(gemm_kernel<GEMM_ADD_F32>, grid, dim3(THREADS), 0, stream, a); break;
+    case GEMM_SWIGLU_F16: launch(gemm_kernel<GEMM_SWIGLU_F16>, grid, dim3(THREADS), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -454,7 +454,7 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
   dim3 grid(a.grid < n_tiles ? a.grid : n_tiles);
 #define DPK_GEMV_CASE(F, T, WV)                                                            \
   if (a.fmt == F && a.tiles == T && W == WV) {                                            \
-    hipLaunchKernelGGL((gemv_kernel<F, T, WV>), grid, dim3(64 * WV), lds, stream, a);    \
+    launch((gemv_kernel<F, T, WV>), grid, dim3(64 * WV), lds, stream, a);    \
     return hipGetLastError();                                                             \
   }
   DPK_GEMV_CASE(W_BF16, 1, 4)
@@ -477,7 +477,7 @@ hipError_t launch_tile_bf16(const uint16_t* src, uint16_t* dst, int N, int K, hi
   if (N % 16 || K % 32) return hipErrorInvalidValue;
   const size_t n = (size_t)N / 16 * (K / 32) * 64;
   const int blocks = (int)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536);
-  hipLaunchKernelGGL(tile_bf16_kernel, dim3(blocks), dim3(256), 0, stream, src, dst, N, K);
+  launch(tile_bf16_kernel, dim3(blocks), dim3(256), 0, stream, src, dst, N, K);
   return hipGetLastError();
 }
 
@@ -486,7 +486,7 @@ hipError_t launch_tile_q4(const uint32_t* codes, const uint16_t* sc, const uint1
   if (N % 16 || K % 64) return hipErrorInvalidValue;
   const size_t n = (size_t)N / 16 * (K / 64) * 64;
   const int blocks = (int)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536);
-  hipLaunchKernelGGL(tile_q4_kernel, dim3(blocks), dim3(256), 0, stream, codes, sc, bi, dst_c, dst_sb, N, K);
+  launch(tile_q4_kernel, dim3(blocks), dim3(256), 0, stream, codes, sc, bi, dst_c, dst_sb, N, K);
   return hipGetLastError();
 }
 

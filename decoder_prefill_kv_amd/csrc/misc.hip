@@ -219,7 +219,7 @@ inline int grid_for(size_t n, int threads) {
 }  // namespace
 
 hipError_t launch_rope_table(float* cos_t, float* sin_t, int max_seq, int d, double theta, hipStream_t stream) {
-  hipLaunchKernelGGL(rope_table_kernel, dim3(grid_for((size_t)max_seq * d / 2, 256)), dim3(256), 0, stream, cos_t,
+  launch(rope_table_kernel, dim3(grid_for((size_t)max_seq * d / 2, 256)), dim3(256), 0, stream, cos_t,
                      sin_t, max_seq, d, theta);
   return hipGetLastError();
 }
@@ -227,14 +227,14 @@ hipError_t launch_rope_table(float* cos_t, float* sin_t, int max_seq, int d, dou
 hipError_t launch_embed(int M, int H, int fmt, const void* table, const uint16_t* sc, const uint16_t* bi,
                         const RowParam* rp, const int32_t* ids_dev, int vocab, float* h, float* rs, float eps,
                         int* err_flag, hipStream_t stream, float* sq) {
-  hipLaunchKernelGGL(embed_kernel, dim3(M), dim3(256), 0, stream, H, fmt, table, sc, bi, rp, ids_dev, vocab, h, rs,
+  launch(embed_kernel, dim3(M), dim3(256), 0, stream, H, fmt, table, sc, bi, rp, ids_dev, vocab, h, rs,
                      eps, err_flag, sq);
   return hipGetLastError();
 }
 
 hipError_t launch_rmsnorm_rows(int M, int H, const float* x, int ldx, const void* g, int g_is_f32, float eps,
                                void* y, int y_is_f16, int ldy, hipStream_t stream) {
-  hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(M), dim3(256), 0, stream, H, x, ldx, g, g_is_f32, eps, y, y_is_f16,
+  launch(rmsnorm_rows_kernel, dim3(M), dim3(256), 0, stream, H, x, ldx, g, g_is_f32, eps, y, y_is_f16,
                      ldy);
   return hipGetLastError();
 }
@@ -243,41 +243,41 @@ hipError_t launch_qk_rope_kv(int M, const float* qkv, int n_heads, int n_kv, int
                              const void* kn, int g_is_f32, float eps, const float* rope_cos, const float* rope_sin,
                              const RowParam* rp, void* q_out, int q_is_f16, KVDesc kv, int layer,
                              hipStream_t stream) {
-  hipLaunchKernelGGL(qk_rope_kv_kernel, dim3(M, n_heads + 2 * n_kv), dim3(64), 0, stream, qkv, n_heads, n_kv, d,
+  launch(qk_rope_kv_kernel, dim3(M, n_heads + 2 * n_kv), dim3(64), 0, stream, qkv, n_heads, n_kv, d,
                      qk_norm, qn, kn, g_is_f32, eps, rope_cos, rope_sin, rp, q_out, q_is_f16, kv, layer);
   return hipGetLastError();
 }
 
 hipError_t launch_gemv_f32(int M, int N, int K, const float* W, const float* W2, const float* x, int ldx,
                            float* out, int ldo, int mode, hipStream_t stream) {
-  hipLaunchKernelGGL(gemv_f32_kernel, dim3((N + 3) / 4), dim3(256), 0, stream, M, N, K, W, W2, x, ldx, out, ldo,
+  launch(gemv_f32_kernel, dim3((N + 3) / 4), dim3(256), 0, stream, M, N, K, W, W2, x, ldx, out, ldo,
                      mode);
   return hipGetLastError();
 }
 
 hipError_t launch_argmax_rows(int M, int N, const float* logits, int ld, int* out, hipStream_t stream) {
-  hipLaunchKernelGGL(argmax_rows_kernel, dim3(M), dim3(1024), 0, stream, N, logits, ld, out);
+  launch(argmax_rows_kernel, dim3(M), dim3(1024), 0, stream, N, logits, ld, out);
   return hipGetLastError();
 }
 
 hipError_t launch_add(int n, const float* in, float* out, hipStream_t stream) {
-  hipLaunchKernelGGL(add_kernel, dim3(grid_for(n, 256)), dim3(256), 0, stream, n, in, out);
+  launch(add_kernel, dim3(grid_for(n, 256)), dim3(256), 0, stream, n, in, out);
   return hipGetLastError();
 }
 
 hipError_t launch_bf16_to_f16(const uint16_t* src, _Float16* dst, size_t n, hipStream_t stream) {
-  hipLaunchKernelGGL(bf16_to_f16_kernel, dim3(grid_for(n, 256)), dim3(256), 0, stream, src, dst, n);
+  launch(bf16_to_f16_kernel, dim3(grid_for(n, 256)), dim3(256), 0, stream, src, dst, n);
   return hipGetLastError();
 }
 
 hipError_t launch_f32_to_f16(const float* src, _Float16* dst, size_t n, hipStream_t stream) {
-  hipLaunchKernelGGL(f32_to_f16_kernel, dim3(grid_for(n, 256)), dim3(256), 0, stream, src, dst, n);
+  launch(f32_to_f16_kernel, dim3(grid_for(n, 256)), dim3(256), 0, stream, src, dst, n);
   return hipGetLastError();
 }
 
 hipError_t launch_q4_to_f16(const uint32_t* codes, const uint16_t* sc, const uint16_t* bi, int rows, int K,
                             _Float16* dst, hipStream_t stream) {
-  hipLaunchKernelGGL(q4_to_f16_kernel, dim3(grid_for((size_t)rows * K, 256)), dim3(256), 0, stream, codes, sc, bi,
+  launch(q4_to_f16_kernel, dim3(grid_for((size_t)rows * K, 256)), dim3(256), 0, stream, codes, sc, bi,
                      rows, K, dst);
   return hipGetLastError();
 }

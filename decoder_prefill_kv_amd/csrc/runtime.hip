@@ -12,6 +12,10 @@
 #include "common.h"
 #include "kernels.h"
 
+namespace dpk {
+thread_local LaunchTiming g_timing;
+}
+
 using namespace dpk;
 
 namespace {
@@ -211,7 +215,7 @@ const char* const kclass_name[K_NCLASS] = {
     "gemv.qkv", "gemv.o", "gemv.gate_up", "gemv.down", "gemv.head", "attn.decode", "embed", "gemm.qkv", "gemm.o",
     "gemm.gate_up", "gemm.down", "attn.prefill", "qk_rope_kv", "rmsnorm", "gemv.f32", "other"};
 
-// Event pair around one launch when profiling is on.
+// Start/stop events of the launches of one kernel class when profiling is on.
 struct ProfScope {
   dpk_model* md;
   hipStream_t st;
@@ -224,11 +228,10 @@ struct ProfScope {
     }
     idx = (int)md->prof_rec.size();
     md->prof_rec.push_back({cls, bytes, flops});
-    (void)hipEventRecord(md->prof_ev[2 * idx], st);
+    g_timing.start = md->prof_ev[2 * idx];
+    g_timing.stop = md->prof_ev[2 * idx + 1];
   }
-  ~ProfScope() {
-    if (idx >= 0) (void)hipEventRecord(md->prof_ev[2 * idx + 1], st);
-  }
+  ~ProfScope() { g_timing = LaunchTiming{}; }
 };
 
 double wbytes_per_elem(int fmt) { return fmt == DPK_FMT_F32 ? 4.0 : fmt == DPK_FMT_BF16 ? 2.0 : 0.5 + 4.0 / 64.0; }
@@ -1015,7 +1018,8 @@ dpk_status dpk_profile_begin(dpk_model* md, int32_t max_launches) {
   if (md->prof) return fail(DPK_ESTATE, "profiling already active");
   while ((int)md->prof_ev.size() < 2 * max_launches) {
     hipEvent_t e;
-    HIP_TRY(hipEventCreate(&e));
+    // timing-only events: no system-scope fence (cache writeback) at record time
+    HIP_TRY(hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
     md->prof_ev.push_back(e);
   }
   md->prof_max = max_launches;
@@ -1031,7 +1035,7 @@ dpk_status dpk_profile_end(dpk_model* md, dpk_kernel_stat* stats, int32_t max_st
   md->prof = false;
   double ms[K_NCLASS] = {}, by[K_NCLASS] = {}, fl[K_NCLASS] = {};
   long cnt[K_NCLASS] = {};
-  if (!md->prof_rec.empty()) HIP_TRY(hipEventSynchronize(md->prof_ev[2 * (md->prof_rec.size() - 1) + 1]));
+  if (!md->prof_rec.empty()) HIP_TRY(hipDeviceSynchronize());
   for (size_t i = 0; i < md->prof_rec.size(); ++i) {
     float t = 0.f;
     HIP_TRY(hipEventElapsedTime(&t, md->prof_ev[2 * i], md->prof_ev[2 * i + 1]));

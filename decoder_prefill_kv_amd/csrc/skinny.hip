@@ -441,10 +441,10 @@ hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t stream) {
   const int tiles = a.rows_per_wg / (WAVES * 16);
   dim3 grid(a.n_blocks, a.ksplit), block(THREADS);
   const size_t lds = skinny_lds_bytes(a.M, a.kchunk, a.rows_per_wg, a.fmt);
-  if (a.fmt == W_BF16 && tiles == 1) hipLaunchKernelGGL((skinny_kernel<W_BF16, 1>), grid, block, lds, stream, a);
-  else if (a.fmt == W_BF16 && tiles == 2) hipLaunchKernelGGL((skinny_kernel<W_BF16, 2>), grid, block, lds, stream, a);
-  else if (a.fmt == W_Q4 && tiles == 1) hipLaunchKernelGGL((skinny_kernel<W_Q4, 1>), grid, block, lds, stream, a);
-  else if (a.fmt == W_Q4 && tiles == 2) hipLaunchKernelGGL((skinny_kernel<W_Q4, 2>), grid, block, lds, stream, a);
+  if (a.fmt == W_BF16 && tiles == 1) launch((skinny_kernel<W_BF16, 1>), grid, block, lds, stream, a);
+  else if (a.fmt == W_BF16 && tiles == 2) launch((skinny_kernel<W_BF16, 2>), grid, block, lds, stream, a);
+  else if (a.fmt == W_Q4 && tiles == 1) launch((skinny_kernel<W_Q4, 1>), grid, block, lds, stream, a);
+  else if (a.fmt == W_Q4 && tiles == 2) launch((skinny_kernel<W_Q4, 2>), grid, block, lds, stream, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
