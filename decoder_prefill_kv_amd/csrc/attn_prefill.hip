@@ -12,6 +12,10 @@
 // B operand of the second product by permuting the key order inside each
 // 16-key step; the V^T tile is read from LDS with the same permutation.
 //
+// Precision: q, P and the output are each carried as fp16 hi + lo parts
+// (two MFMAs per product), so the only 16-bit rounding left is that of the
+// cached K and V.
+//
 // Workgroup: 4 waves, each one query head x 32 query rows; the heads of a
 // workgroup share one KV head, so each K / V^T tile (64 keys) is staged in LDS
 // once for all of them.
@@ -49,12 +53,17 @@ __global__ __launch_bounds__(THREADS, 2) void attn_prefill_kernel(AttnPrefillArg
   const int qpos = a.start + (row_ok ? qrow : a.M - 1);
   const float c = a.scale * LOG2E;
 
-  // Q^T fragments: lane (query q32, k-group hh) holds q[16 s + 8 hh .. +7]
-  f16x8 qf[D / 16];
+  // Q^T fragments: lane (query q32, k-group hh) holds q[16 s + 8 hh .. +7],
+  // as fp16 hi and lo parts (q = hi + lo to ~22 bits)
+  f16x8 qf[D / 16], qlo[D / 16];
   {
     const _Float16* qp = a.q + ((size_t)(row_ok ? qrow : a.M - 1) * a.n_heads + head) * D;
+    const _Float16* qlp = qp + (size_t)a.M * a.n_heads * D;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) qf[s] = *(const f16x8*)(qp + 16 * s + 8 * hh);
+    for (int s = 0; s < D / 16; ++s) {
+      qf[s] = *(const f16x8*)(qp + 16 * s + 8 * hh);
+      qlo[s] = *(const f16x8*)(qlp + 16 * s + 8 * hh);
+    }
   }
   f32x16 o[D / 32];
 #pragma unroll
@@ -98,6 +107,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_prefill_kernel(AttnPrefillArg
       for (int st = 0; st < D / 16; ++st) {
         const f16x8 kf = *(const f16x8*)&Ks[b * 32 + q32][16 * st + 8 * hh];
         s[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[st], s[b], 0, 0, 0);
+        s[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qlo[st], s[b], 0, 0, 0);
       }
     }
     // mask + online softmax (log2 domain); lane key index = 8(v/4) + 4hh + v%4
@@ -116,14 +126,16 @@ __global__ __launch_bounds__(THREADS, 2) void attn_prefill_kernel(AttnPrefillArg
     const float mnew = fmaxf(mrun, tmax);
     const float alpha = (mrun == -INFINITY) ? 0.f : exp2f(mrun - mnew);
     float psum = 0.f;
-    f16x8 pf[2][2];
+    f16x8 pf[2][2], pl[2][2];  // P as fp16 hi + lo
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const float p = (s[b][v] == -INFINITY) ? 0.f : exp2f(s[b][v] - mnew);
         psum += p;
-        pf[b][v >> 3][v & 7] = (_Float16)p;
+        const _Float16 ph = (_Float16)p;
+        pf[b][v >> 3][v & 7] = ph;
+        pl[b][v >> 3][v & 7] = (_Float16)(p - (float)ph);
       }
     psum += __shfl_xor(psum, 32, 64);
     lrun = lrun * alpha + psum;
@@ -145,22 +157,31 @@ __global__ __launch_bounds__(THREADS, 2) void attn_prefill_kernel(AttnPrefillArg
           const u32x2 lo = *(const u32x2*)&Vs[dr][kb];
           const u32x2 hi = *(const u32x2*)&Vs[dr][kb + 8];
           const u32x4 vw = {lo.x, lo.y, hi.x, hi.y};
-          o[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vw), pf[b][t], o[i], 0, 0, 0);
+          const f16x8 vf = __builtin_bit_cast(f16x8, vw);
+          o[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[b][t], o[i], 0, 0, 0);
+          o[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pl[b][t], o[i], 0, 0, 0);
         }
       }
   }
   if (!row_ok) return;
   const float inv = 1.0f / lrun;
-  _Float16* op = a.out + (size_t)qrow * a.n_heads * D + (size_t)head * D;
+  // row layout [hi: n_heads * D][lo: n_heads * D]
+  _Float16* op = a.out + (size_t)qrow * 2 * a.n_heads * D + (size_t)head * D;
+  _Float16* olp = op + (size_t)a.n_heads * D;
   // O^T block i: channel = 32 i + 8 (v/4) + 4 hh + v%4 for query q32
 #pragma unroll
   for (int i = 0; i < D / 32; ++i)
 #pragma unroll
     for (int v4 = 0; v4 < 4; ++v4) {
-      f16x4 w;
+      f16x4 w, wl;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = (_Float16)(o[i][4 * v4 + e] * inv);
+      for (int e = 0; e < 4; ++e) {
+        const float x = o[i][4 * v4 + e] * inv;
+        w[e] = (_Float16)x;
+        wl[e] = (_Float16)(x - (float)w[e]);
+      }
       *(f16x4*)(op + 32 * i + 8 * v4 + 4 * hh) = w;
+      *(f16x4*)(olp + 32 * i + 8 * v4 + 4 * hh) = wl;
     }
 }
 

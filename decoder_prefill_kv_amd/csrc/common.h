@@ -113,6 +113,17 @@ DPK_DEV int coh_load(const int* p) {
   return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// 8-byte device-coherent accesses (two floats; same sc1 policy)
+DPK_DEV void coh_store2(float* p, float x, float y) {
+  const uint64_t v = (uint64_t)__float_as_uint(x) | ((uint64_t)__float_as_uint(y) << 32);
+  __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+DPK_DEV void coh_load2(const float* p, float& x, float& y) {
+  const uint64_t v = __hip_atomic_load((uint64_t*)const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  x = __uint_as_float((uint32_t)v);
+  y = __uint_as_float((uint32_t)(v >> 32));
+}
+
 // Last-arriving-workgroup election.  Every workgroup calls this once after
 // writing the data it hands over with coh_store; exactly one (the last) gets
 // true and may then read all of it with coh_load.  The counter is reset for

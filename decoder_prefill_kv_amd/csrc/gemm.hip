@@ -5,15 +5,31 @@
 // Prefill is compute bound (the whole prompt goes through every weight at
 // once, "LLMs on the ANE", opening section); this kernel is where its FLOPs go.
 // The operands are fp16 rather than bf16: every weight of the bf16 model is
-// exactly representable in fp16 (magnitudes >= 2^-17; smaller ones round with
+// exactly representable in fp16 (magnitudes >= 2^-24; smaller ones round with
 // an absolute error below 2^-25), and fp16 activations carry three more
 // mantissa bits, which the logits tolerance needs on deep models.  Where that
 // is still not enough (the QKV projection), A is given as [A_hi | A_lo] with
 // K = 2 Kb and B is read twice, which computes (A_hi + A_lo) B^T.
 //
 // Tile 256 x 256 x 64, 4 waves in a 2 x 2 layout, each wave 128 x 128 from
-// 4 x 4 v_mfma_f32_32x32x16_f16 blocks (256 fp32 accumulators per lane).
-// Global -> registers -> LDS double buffer, one barrier per k-tile.
+// 4 x 4 v_mfma_f32_32x32x16_f16 blocks (256 fp32 accumulators per lane, in
+// AGPRs).  One wave per SIMD, so latency is hidden inside the wave:
+//  * fragments are double-buffered in registers: the LDS reads of k-step
+//    s+1 are interleaved with the 16 MFMAs of step s;
+//  * the next k-tile's global loads are issued a whole k-tile ahead into
+//    staging registers and written to the other LDS stage between the MFMAs
+//    of the third k-step;
+//  * the one barrier per k-tile sits before the last k-step, whose operands
+//    are already in registers, so the first LDS reads of the next tile
+//    overlap its MFMAs.
+//
+// Split-K: when the (M, N) tiles cannot fill the chip (N = 4096 at M = 2048
+// gives 128 tiles for 256 CUs), blockIdx.z takes a contiguous 1/S of the
+// k-tiles.  Each split writes its partial tile to a workspace with device-
+// coherent stores; the last split to arrive adds the partials in split order
+// (so the result does not depend on arrival order) and runs the epilogue.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -24,35 +40,34 @@ namespace {
 constexpr int BM = 256, BN = 256, BK = 64, THREADS = 256;
 constexpr int LDS_STRIDE = BK + 8;  // halfs per LDS row (pad against bank conflicts)
 
-template <int EPI>
+// instruction classes for __builtin_amdgcn_sched_group_barrier
+constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100, SG_DS_WRITE = 0x200;
+
+template <int EPI, bool SPLIT>
 __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 As[2][BM][LDS_STRIDE];
   __shared__ __attribute__((aligned(16))) _Float16 Bs[2][BN][LDS_STRIDE];
+  __shared__ int s_last;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const int m0 = blockIdx.y * BM;
   // SWIGLU: the tile's B rows are 128 gate rows then the same 128 up rows
   const int n0 = (EPI == GEMM_SWIGLU_F16) ? blockIdx.x * (BN / 2) : blockIdx.x * BN;
+  const int nk_all = a.K / BK;
+  const int nks = SPLIT ? nk_all / a.splits : nk_all;
+  const int kt0 = SPLIT ? blockIdx.z * nks : 0;
 
-  // global load assignment: 8 threads per 64-half row, 32 rows per pass
+  // global load assignment: 8 threads per 64-half row, 32 rows per pass.
+  // Row block i of a pass is a uniform offset from the thread's first row,
+  // so each load is (uniform base, one per-thread 32-bit offset).  The A
+  // buffer holds whole 256-row tiles: rows past M are read but their results
+  // are never stored.
   const int lrow = tid >> 3, lk = (tid & 7) * 8;
-  const _Float16* Ag[BM / 32];
-  const _Float16* Bg[BN / 32];
-#pragma unroll
-  for (int i = 0; i < BM / 32; ++i) {
-    int r = m0 + lrow + 32 * i;
-    r = r < a.M ? r : a.M - 1;  // clamp the M tail (rows discarded at the store)
-    Ag[i] = a.A + (size_t)r * a.lda + lk;
-  }
-#pragma unroll
-  for (int i = 0; i < BN / 32; ++i) {
-    const int rr = lrow + 32 * i;
-    if (EPI == GEMM_SWIGLU_F16)
-      Bg[i] = (rr < BN / 2 ? a.B + (size_t)(n0 + rr) * a.ldb : a.B2 + (size_t)(n0 + rr - BN / 2) * a.ldb) + lk;
-    else
-      Bg[i] = a.B + (size_t)(n0 + rr) * a.ldb + lk;
-  }
+  const uint32_t a_off = (uint32_t)(lrow * a.lda + lk), b_off = (uint32_t)(lrow * a.ldb + lk);
+  const _Float16* A0 = a.A + (size_t)m0 * a.lda;
+  const _Float16* B0 = a.B + (size_t)n0 * a.ldb;
+  const _Float16* B20 = (EPI == GEMM_SWIGLU_F16) ? a.B2 + (size_t)n0 * a.ldb : nullptr;
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -62,22 +77,44 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  u32x4 ra[BM / 32], rb[BN / 32];
+  // two staging sets: tile t+1 waits in one while tile t+2 is in flight into
+  // the other (global loads are issued two k-tiles ahead of their LDS write).
+  // Staging register r < 8 holds A row block r, r >= 8 B row block r - 8.
+  u32x4 ra[2][BM / 32], rb[2][BN / 32];
   const int Kb = a.Kb ? a.Kb : a.K;
-  auto gload = [&](int kt) {
+  // global loads of staging registers [R0, R1) of set SET for k-tile kt
+  auto gload = [&](auto set_c, int kt, auto r0_c, auto r1_c) {
+    constexpr int SET = decltype(set_c)::value, R0 = decltype(r0_c)::value, R1 = decltype(r1_c)::value;
     const int ko = kt * BK;
     const int kob = ko < Kb ? ko : ko - Kb;  // B is read twice when A = [hi | lo]
+    const _Float16* Ak = A0 + ko;
 #pragma unroll
-    for (int i = 0; i < BM / 32; ++i) ra[i] = *(const u32x4*)(Ag[i] + ko);
-#pragma unroll
-    for (int i = 0; i < BN / 32; ++i) rb[i] = *(const u32x4*)(Bg[i] + kob);
+    for (int r = R0; r < R1; ++r) {
+      if (r < BM / 32) {
+        ra[SET][r] = *(const u32x4*)(Ak + (size_t)r * 32 * a.lda + a_off);
+      } else {
+        const int i = r - BM / 32;
+        // SWIGLU: B rows 0..127 of the tile are gate rows, 128..255 the same up rows
+        const _Float16* Bk = (EPI == GEMM_SWIGLU_F16 && i >= BN / 64) ? B20 + (size_t)(i - BN / 64) * 32 * a.ldb
+                                                                      : B0 + (size_t)i * 32 * a.ldb;
+        rb[SET][i] = *(const u32x4*)(Bk + kob + b_off);
+      }
+    }
   };
-  auto lstore = [&](int st) {
+  auto lstore = [&](auto set_c, int st, auto r0_c, auto r1_c) {
+    constexpr int SET = decltype(set_c)::value, R0 = decltype(r0_c)::value, R1 = decltype(r1_c)::value;
 #pragma unroll
-    for (int i = 0; i < BM / 32; ++i) *(u32x4*)&As[st][lrow + 32 * i][lk] = ra[i];
-#pragma unroll
-    for (int i = 0; i < BN / 32; ++i) *(u32x4*)&Bs[st][lrow + 32 * i][lk] = rb[i];
+    for (int r = R0; r < R1; ++r) {
+      if (r < BM / 32)
+        *(u32x4*)&As[st][lrow + 32 * r][lk] = ra[SET][r];
+      else
+        *(u32x4*)&Bs[st][lrow + 32 * (r - BM / 32)][lk] = rb[SET][r - BM / 32];
+    }
   };
+  using R0_ = std::integral_constant<int, 0>;
+  using R6_ = std::integral_constant<int, 6>;
+  using R11_ = std::integral_constant<int, 11>;
+  using R16_ = std::integral_constant<int, 16>;
 
   // B rows of this wave inside the LDS tile
   int brow[4];
@@ -89,28 +126,144 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs a) {
       brow[j] = wn * 128 + j * 32;
   }
 
-  const int nk = a.K / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
   const int r32 = lane & 31, k8 = (lane >> 5) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
+  f16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+  auto frag_load = [&](f16x8 (&fa)[4], f16x8 (&fb)[4], int st, int kk) {
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      f16x8 af[4], bfr[4];
+    for (int i = 0; i < 4; ++i) fa[i] = *(const f16x8*)&As[st][wm * 128 + i * 32 + r32][kk + k8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = *(const f16x8*)&As[st][wm * 128 + i * 32 + r32][kk + k8];
+    for (int j = 0; j < 4; ++j) fb[j] = *(const f16x8*)&Bs[st][brow[j] + r32][kk + k8];
+  };
+  auto mfma16 = [&](const f16x8 (&fa)[4], const f16x8 (&fb)[4]) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bfr[j] = *(const f16x8*)&Bs[st][brow[j] + r32][kk + k8];
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+  // 16 MFMAs with the 8 fragment reads of the next step spread between them
+  auto interleave_reads = [&]() {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    for (int x = 0; x < 8; ++x) {
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
     }
-    if (kt + 1 < nk) lstore(st ^ 1);
+  };
+
+  // One k-tile t of parity PAR (the staging set of tile t+1 is PAR ^ 1).
+  // Tile t+1 goes into the other LDS stage during k-steps 0-2 (that stage
+  // is free since the previous barrier), and each staging register is
+  // reloaded with tile t+3 right after it is written out, so LDS writes and
+  // global loads are spread over three k-steps.  Past the last tile the loads
+  // repeat the last tile (clamped index, results unused), so the body has no
+  // branches: it is one basic block, which the instruction-group
+  // interleaving needs.
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  const int kt_last = kt0 + nks - 1;
+  // 16 MFMAs with 8 fragment reads, up to 8 LDS writes and 8 global loads
+  auto interleave_all = [&]() {
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_DS_WRITE, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
+    }
+  };
+  auto ktile = [&](int t, auto par_c) {
+    constexpr int PAR = decltype(par_c)::value;
+    using NSET = std::integral_constant<int, PAR ^ 1>;
+    const int st = t & 1;
+    const int kt3 = min(kt0 + t + 3, kt_last);
+    // k-step 0 (operands fa0/fb0), reads for step 1
+    frag_load(fa1, fb1, st, 16);
+    mfma16(fa0, fb0);
+    lstore(NSET{}, st ^ 1, R0_{}, R6_{});
+    gload(NSET{}, kt3, R0_{}, R6_{});
+    interleave_all();
+    __builtin_amdgcn_sched_barrier(0);
+    // k-step 1, reads for step 2
+    frag_load(fa0, fb0, st, 32);
+    mfma16(fa1, fb1);
+    lstore(NSET{}, st ^ 1, R6_{}, R11_{});
+    gload(NSET{}, kt3, R6_{}, R11_{});
+    interleave_all();
+    __builtin_amdgcn_sched_barrier(0);
+    // k-step 2, reads for step 3
+    frag_load(fa1, fb1, st, 48);
+    mfma16(fa0, fb0);
+    lstore(NSET{}, st ^ 1, R11_{}, R16_{});
+    gload(NSET{}, kt3, R11_{}, R16_{});
+    interleave_all();
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
+    // k-step 3 (operands already in registers), first reads of the next tile
+    frag_load(fa0, fb0, st ^ 1, 0);
+    mfma16(fa1, fb1);
+    interleave_reads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  gload(P0{}, kt0, R0_{}, R16_{});
+  lstore(P0{}, 0, R0_{}, R16_{});
+  __syncthreads();
+  frag_load(fa0, fb0, 0, 0);
+  gload(P1{}, min(kt0 + 1, kt_last), R0_{}, R16_{});
+  gload(P0{}, min(kt0 + 2, kt_last), R0_{}, R16_{});
+  int t = 0;
+  for (; t + 1 < nks; t += 2) {
+    ktile(t, P0{});
+    ktile(t + 1, P1{});
+  }
+  if (t < nks) ktile(t, P0{});
+
+  if (SPLIT) {
+    // partial tile: value pair (v, v+1) of block (i, j) of thread tid sits at
+    // float offset ((((i * 4 + j) * 8 + v / 2) * THREADS + tid) * 2, so each
+    // 8-byte coherent store or load of a wave covers 512 contiguous bytes
+    const int tile = blockIdx.y * gridDim.x + blockIdx.x;
+    const int S = a.splits;
+    float* wsp = a.ws + (size_t)tile * S * (BM * BN);
+    float* own = wsp + (size_t)blockIdx.z * (BM * BN) + tid * 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; v += 2)
+          coh_store2(own + (((i * 4 + j) * 8 + v / 2) * THREADS) * 2, acc[i][j][v], acc[i][j][v + 1]);
+    if (!last_block_arrive(a.counters + tile, (unsigned)S, &s_last)) return;
+    // the last split re-reads every partial, its own included, and adds them
+    // in split order
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float* src = wsp + tid * 2;
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          float x, y;
+          coh_load2(src + (((i * 4 + j) * 8 + v / 2) * THREADS) * 2, x, y);
+          acc[i][j][v] = x;
+          acc[i][j][v + 1] = y;
+        }
+      }
+      for (int p = 1; p < S; ++p) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float* src = wsp + (size_t)p * (BM * BN) + tid * 2;
+#pragma unroll
+          for (int v = 0; v < 16; v += 2) {
+            float x, y;
+            coh_load2(src + (((i * 4 + j) * 8 + v / 2) * THREADS) * 2, x, y);
+            acc[i][j][v] += x;
+            acc[i][j][v + 1] += y;
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   // epilogue: lane holds C[row][col], col = lane % 32,
@@ -144,18 +297,53 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs a) {
   }
 }
 
+template <int EPI>
+void launch_epi(const GemmArgs& a, dim3 grid, hipStream_t stream) {
+  if (a.splits > 1)
+    launch(gemm_kernel<EPI, true>, grid, dim3(THREADS), 0, stream, a);
+  else
+    launch(gemm_kernel<EPI, false>, grid, dim3(THREADS), 0, stream, a);
+}
+
 }  // namespace
+
+int gemm_choose_splits(int M, int N, int K, int epi, int n_cu) {
+  if (K % BK) return 1;
+  const int ntile = (epi == GEMM_SWIGLU_F16) ? BN / 2 : BN;
+  const int tiles = (N / ntile) * ((M + BM - 1) / BM);
+  const int nk = K / BK;
+  int best = 1;
+  double best_t = 1e30;
+  // the partial exchange costs about a quarter of a round, so a split must
+  // save more than that
+  for (int S = 1; S <= GEMM_MAX_SPLITS; S *= 2) {
+    if (nk % S || nk / S < 4) break;
+    if (S > 1 && (size_t)tiles * S > GEMM_WS_TILES) break;
+    const int rounds = (tiles * S + n_cu - 1) / n_cu;
+    const double t = (double)rounds / S + (S > 1 ? 0.25 : 0.0);
+    if (t < best_t - 1e-9) {
+      best_t = t;
+      best = S;
+    }
+  }
+  return best;
+}
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.K % BK || a.M < 1) return hipErrorInvalidValue;
   if (a.Kb && (a.Kb % BK || (a.K != a.Kb && a.K != 2 * a.Kb))) return hipErrorInvalidValue;
   const int ntile = (a.epi == GEMM_SWIGLU_F16) ? BN / 2 : BN;
   if (a.N % ntile) return hipErrorInvalidValue;
-  dim3 grid(a.N / ntile, (a.M + BM - 1) / BM);
+  const int S = a.splits < 1 ? 1 : a.splits;
+  dim3 grid(a.N / ntile, (a.M + BM - 1) / BM, S);
+  if (S > 1) {
+    if (!a.ws || !a.counters || (a.K / BK) % S || (size_t)grid.x * grid.y * S > GEMM_WS_TILES)
+      return hipErrorInvalidValue;
+  }
   switch (a.epi) {
-    case GEMM_STORE_F32: launch(gemm_kernel<GEMM_STORE_F32>, grid, dim3(THREADS), 0, stream, a); break;
-    case GEMM_ADD_F32: launch(gemm_kernel<GEMM_ADD_F32>, grid, dim3(THREADS), 0, stream, a); break;
-    case GEMM_SWIGLU_F16: launch(gemm_kernel<GEMM_SWIGLU_F16>, grid, dim3(THREADS), 0, stream, a); break;
+    case GEMM_STORE_F32: launch_epi<GEMM_STORE_F32>(a, grid, stream); break;
+    case GEMM_ADD_F32: launch_epi<GEMM_ADD_F32>(a, grid, stream); break;
+    case GEMM_SWIGLU_F16: launch_epi<GEMM_SWIGLU_F16>(a, grid, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -148,7 +148,8 @@ hipError_t launch_embed(int M, int H, int fmt, const void* table, const uint16_t
 // in columns [0, H) and fp16 lo (= y - hi) in [H, 2H); g is fp32 or bf16
 hipError_t launch_rmsnorm_rows(int M, int H, const float* x, int ldx, const void* g, int g_is_f32,
                                float eps, void* y, int y_is_f16, int ldy, hipStream_t stream);
-// prefill: qkv fp32 [M][(Hq+2Hkv)d] -> q (fp16 or fp32 [M][Hq][d]), K/V into the cache
+// prefill: qkv fp32 [M][(Hq+2Hkv)d] -> q (q_is_f16 0: fp32 [M][Hq][d]; 1: fp16; 2: fp16 hi plane
+// then lo plane), K/V into the cache
 hipError_t launch_qk_rope_kv(int M, const float* qkv, int n_heads, int n_kv, int d, int qk_norm,
                              const void* qn, const void* kn, int g_is_f32, float eps,
                              const float* rope_cos, const float* rope_sin, const RowParam* rp,
@@ -178,7 +179,15 @@ struct GemmArgs {
   int epi;
   float* C; int ldc;              // STORE/ADD
   _Float16* C16; int ldc16;       // SWIGLU
+  int splits;                     // split-K factor (<= 1: none)
+  float* ws;                      // split-K partial tiles [tiles][splits][256 * 256]
+  unsigned* counters;             // split-K arrival counters [tiles], zero between launches
 };
+constexpr int GEMM_MAX_SPLITS = 2;
+constexpr size_t GEMM_WS_TILES = 768;             // partial tiles the workspace holds
+constexpr size_t GEMM_TILE_FLOATS = 256 * 256;
+// split-K factor that best fills n_cu CUs with (M, N) tiles
+int gemm_choose_splits(int M, int N, int K, int epi, int n_cu);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 
 // ---- prefill attention (fp16 MFMA, causal over the cache)
@@ -186,10 +195,10 @@ struct AttnPrefillArgs {
   int M;               // query rows, at positions start..start+M-1 of sequence seq
   int start, seq;
   int n_heads, n_kv, d;
-  const _Float16* q;   // [M][n_heads][d]
+  const _Float16* q;   // [2][M][n_heads][d]: fp16 hi plane, then the lo plane (q - hi)
   KVDesc kv;
   int layer;
-  _Float16* out;       // [M][n_heads*d]
+  _Float16* out;       // [M][2][n_heads*d]: per row the fp16 hi half, then the lo half (o - hi)
   float scale;
 };
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t stream);

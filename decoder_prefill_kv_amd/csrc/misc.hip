@@ -118,7 +118,16 @@ __global__ void qk_rope_kv_kernel(const float* qkv, int n_heads, int n_kv, int d
     const float y1 = x1 * c - x2 * s, y2 = x2 * c + x1 * s;
     if (is_q) {
       const size_t o = ((size_t)m * n_heads + hh) * d;
-      if (q_is_f16) {
+      if (q_is_f16 == 2) {
+        // fp16 hi plane, then the lo plane (y - hi) M * n_heads * d further
+        _Float16* qh = (_Float16*)q_out;
+        _Float16* ql = qh + (size_t)gridDim.x * n_heads * d;
+        const _Float16 h1 = (_Float16)y1, h2 = (_Float16)y2;
+        qh[o + e] = h1;
+        qh[o + e + hd2] = h2;
+        ql[o + e] = (_Float16)(y1 - (float)h1);
+        ql[o + e + hd2] = (_Float16)(y2 - (float)h2);
+      } else if (q_is_f16) {
         ((_Float16*)q_out)[o + e] = (_Float16)y1;
         ((_Float16*)q_out)[o + e + hd2] = (_Float16)y2;
       } else {

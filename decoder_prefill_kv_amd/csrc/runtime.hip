@@ -78,7 +78,8 @@ struct dpk_model {
         *act = nullptr, *part = nullptr, *sink = nullptr, *sq = nullptr, *cand_val = nullptr, *attn_part = nullptr;
   int* cand_idx = nullptr;
   _Float16 *y16 = nullptr, *q16 = nullptr, *o16 = nullptr, *act16 = nullptr;
-  unsigned *counters = nullptr, *attn_counters = nullptr;
+  unsigned *counters = nullptr, *attn_counters = nullptr, *gemm_counters = nullptr;
+  float* gemm_ws = nullptr;
   int* err_flag = nullptr;
   int* argmax_sink = nullptr;
   int rows_f32 = 0;       // rows of the fp32 activation buffers
@@ -111,7 +112,7 @@ size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct ScratchLayout {
   size_t rope_cos, rope_sin, rows, h, rs, qkv, y32, qbuf, attn_o, act, part, sink, sq, cand_val, cand_idx, attn_part,
-      y16, q16, o16, act16, counters, attn_counters, err, argmax_sink, total;
+      y16, q16, o16, act16, counters, attn_counters, err, argmax_sink, gemm_ws, gemm_counters, total;
   int rows_f32, attn_chunks_cap;
   size_t part_floats;
 };
@@ -159,14 +160,19 @@ ScratchLayout scratch_layout(const dpk_config& c) {
   L.cand_val = take(SKINNY_MAX * nbm * 4);
   L.cand_idx = take(SKINNY_MAX * nbm * 4);
   L.attn_part = take((size_t)(f32 ? R : SKINNY_MAX) * c.n_heads * L.attn_chunks_cap * (d + 2) * 4);
-  L.y16 = take(f32 ? 0 : R * H * 2 * 2);
-  L.q16 = take(f32 ? 0 : R * Qd * 2);
-  L.o16 = take(f32 ? 0 : R * Qd * 2);
-  L.act16 = take(f32 ? 0 : R * I * 2);
+  // GEMM A operands hold whole 256-row tiles (rows past M are read, never stored)
+  const size_t Rg = (R + 255) / 256 * 256;
+  L.y16 = take(f32 ? 0 : Rg * H * 2 * 2);
+  L.q16 = take(f32 ? 0 : R * Qd * 2 * 2);   // hi and lo planes
+  L.o16 = take(f32 ? 0 : Rg * Qd * 2 * 2);  // per row hi then lo
+  L.act16 = take(f32 ? 0 : Rg * I * 2);
   L.counters = take((1 + nbm) * 4);
   L.attn_counters = take((size_t)(f32 ? R : SKINNY_MAX) * c.n_kv_heads * 4);
   L.err = take(4);
   L.argmax_sink = take(SKINNY_MAX * 4);
+  const bool gemm_path = !f32 && R > SKINNY_MAX;
+  L.gemm_ws = take(gemm_path ? GEMM_WS_TILES * GEMM_TILE_FLOATS * 4 : 0);
+  L.gemm_counters = take(gemm_path ? GEMM_WS_TILES * 4 : 0);
   L.total = o;
   return L;
 }
@@ -561,7 +567,11 @@ dpk_status forward_gemm(dpk_model* md, int M, int start, int seq, bool want_head
     const double outb = (g.epi == GEMM_SWIGLU_F16) ? (double)g.M * g.N * 2 : (double)g.M * g.N * 4;
     const double kb = g.Kb ? g.Kb : g.K;  // algorithmic K (the hi/lo split doubles the MFMA work)
     ProfScope ps(md, st, cls, ((double)g.M * g.K + n * kb) * 2 + outb, 2.0 * g.M * n * kb);
-    HIP_TRY(launch_gemm(g, st));
+    GemmArgs gs = g;
+    gs.splits = md->gemm_ws ? gemm_choose_splits(g.M, g.N, g.K, g.epi, md->n_cu) : 1;
+    gs.ws = md->gemm_ws;
+    gs.counters = md->gemm_counters;
+    HIP_TRY(launch_gemm(gs, st));
     return DPK_OK;
   };
   dpk_status s2;
@@ -586,7 +596,7 @@ dpk_status forward_gemm(dpk_model* md, int M, int start, int seq, bool want_head
     {
       ProfScope ps(md, st, K_QK_ROPE_KV, (double)M * md->Nqkv * 6, 0);
       HIP_TRY(launch_qk_rope_kv(M, md->qkv, c.n_heads, c.n_kv_heads, d, c.qk_norm, L.q_norm, L.k_norm, 0, c.rms_eps,
-                                md->rope_cos, md->rope_sin, md->rows_dev, md->q16, 1, md->kvd, l, st));
+                                md->rope_cos, md->rope_sin, md->rows_dev, md->q16, 2, md->kvd, l, st));
     }
     AttnPrefillArgs at{};
     at.M = M; at.start = start; at.seq = seq;
@@ -600,8 +610,8 @@ dpk_status forward_gemm(dpk_model* md, int M, int start, int seq, bool want_head
       HIP_TRY(launch_attn_prefill(at, st));
     }
     g = GemmArgs{};
-    g.M = M; g.N = H; g.K = Qd;
-    g.A = md->o16; g.lda = Qd; g.B = L.o16; g.ldb = Qd;
+    g.M = M; g.N = H; g.K = 2 * Qd; g.Kb = Qd;
+    g.A = md->o16; g.lda = 2 * Qd; g.B = L.o16; g.ldb = Qd;
     g.epi = GEMM_ADD_F32; g.C = md->h; g.ldc = H;
     if ((s2 = gemm_prof(K_GEMM_O, g))) return s2;
     {
@@ -761,6 +771,8 @@ dpk_status dpk_bind_workspace(dpk_model* md, void* kv, void* scratch, void* prep
   md->attn_counters = (unsigned*)(s + L.attn_counters);
   md->err_flag = (int*)(s + L.err);
   md->argmax_sink = (int*)(s + L.argmax_sink);
+  md->gemm_ws = L.gemm_counters > L.gemm_ws ? (float*)(s + L.gemm_ws) : nullptr;
+  md->gemm_counters = L.total > L.gemm_counters ? (unsigned*)(s + L.gemm_counters) : nullptr;
   md->rows_f32 = L.rows_f32;
   md->attn_chunks_cap = L.attn_chunks_cap;
   md->part_floats = L.part_floats;
@@ -778,6 +790,7 @@ dpk_status dpk_bind_workspace(dpk_model* md, void* kv, void* scratch, void* prep
   HIP_TRY(hipMemsetAsync(md->counters, 0, (1 + nblocks_max(c)) * 4, st));
   HIP_TRY(hipMemsetAsync(md->attn_counters, 0, (size_t)(md->fmt == DPK_FMT_F32 ? c.max_rows : SKINNY_MAX) * c.n_kv_heads * 4, st));
   HIP_TRY(hipMemsetAsync(md->err_flag, 0, 4, st));
+  if (md->gemm_counters) HIP_TRY(hipMemsetAsync(md->gemm_counters, 0, GEMM_WS_TILES * 4, st));
   HIP_TRY(launch_rope_table(md->rope_cos, md->rope_sin, c.max_seq, c.head_dim, c.rope_theta, st));
   md->bound = true;
   return DPK_OK;
