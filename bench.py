@@ -100,6 +100,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel profiled pass")
+    ap.add_argument("--decode-path", choices=["auto", "multi"], default="auto",
+                    help="auto: one persistent launch per decode step where the shapes allow it; "
+                         "multi: one launch per kernel")
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="override the workload's decode step count (for counter runs; not a bench figure)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -127,7 +130,8 @@ def main():
     torch.cuda.init()
     stream = torch.cuda.current_stream()
     t0 = time.time()
-    dec = dpk.Decoder(cfg, w, max_batch=1, max_seq=P + N, max_rows=P)
+    dec = dpk.Decoder(cfg, w, max_batch=1, max_seq=P + N, max_rows=P,
+                      flags=2 if args.decode_path == "multi" else 0)  # DPK_FLAG_DECODE_MULTI
     torch.cuda.synchronize()
     log("[bench] weights on device in %.1f s (kv %.2f GB, scratch %.2f GB, prep %.2f GB)"
         % ((time.time() - t0,) + tuple(x / 1e9 for x in dec.sizes)))
@@ -184,7 +188,8 @@ def main():
         stats = dpk.profile_end(dec.handle)
         kernels = {k: {"launches": v["launches"], "avg_us": round(1e3 * v["total_ms"] / v["launches"], 2),
                        "total_ms": round(v["total_ms"], 3)} for k, v in stats.items()}
-        dec_cls = {k: v for k, v in stats.items() if k.startswith("gemv") or k.startswith("attn.decode")}
+        dec_cls = {k: v for k, v in stats.items()
+                   if k.startswith("gemv") or k.startswith("attn.decode") or k == "decode.step"}
         dom = max(dec_cls, key=lambda k: dec_cls[k]["total_ms"])
         v = stats[dom]
         avg_s = v["total_ms"] / 1e3 / v["launches"]
@@ -221,7 +226,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if cfg.weight_format == "bf16" else cfg.weight_format,
         "data": "synthetic (seeded N(0,0.02) weights, uniform random prompt ids)",
-        "config": {"workload": desc, "prompt_tokens": P, "decode_steps": N, "batch": 1},
+        "config": {"workload": desc, "prompt_tokens": P, "decode_steps": N, "batch": 1,
+                   "decode_path": args.decode_path},
         "decode_tok_s": round(decode_tps, 2),
         "prefill_tok_s": round(prefill_tps, 1),
         "prefill_ms": round(pre_ms, 3),

@@ -90,6 +90,27 @@ DPK_DEV void wave_argmax(float& v, int& i) {
 }
 
 // Block-wide sum over blockDim.x threads (multiple of 64); red has >= 16 floats.
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// accesses, not for its outstanding global loads (a __syncthreads() fence
+// would also drain every load in flight, e.g. a weight prefetch).  Global
+// data written before it is not made visible to the other waves.
+DPK_DEV void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+}
+
+// block_sum with lds_barrier(): the sum of v over the workgroup
+DPK_DEV float block_sum_lds(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, nw = blockDim.x >> 6;
+  lds_barrier();
+  if (l == 0) red[w] = v;
+  lds_barrier();
+  float t = 0.f;
+  for (int i = 0; i < nw; ++i) t += red[i];
+  return t;
+}
+
 DPK_DEV float block_sum(float v, float* red) {
   v = wave_sum(v);
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, nw = blockDim.x >> 6;
@@ -122,6 +143,28 @@ DPK_DEV void coh_load2(const float* p, float& x, float& y) {
   const uint64_t v = __hip_atomic_load((uint64_t*)const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   x = __uint_as_float((uint32_t)v);
   y = __uint_as_float((uint32_t)(v >> 32));
+}
+
+// Device-coherent loads / stores without atomic semantics: buffer accesses
+// with the same sc1 cache policy as the agent-scope atomics above, through a
+// descriptor whose base must be uniform over the wave.  Being plain loads,
+// the compiler batches them and waits only where a value is used (an atomic
+// load waits for itself before the next memory operation).
+constexpr int CPOL_SC1 = 16;
+typedef __amdgpu_buffer_rsrc_t coh_buf;
+DPK_DEV coh_buf coh_buffer(const void* base) {
+  // raw buffer: stride 0, 2^31-1 bytes, the gfx9 data-format word
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+// (the builtins move 32-bit integers: the values are bit-cast, never converted)
+DPK_DEV float cload(coh_buf r, uint32_t i) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, i * 4u, 0, CPOL_SC1));
+}
+DPK_DEV f32x4 cload4(coh_buf r, uint32_t i) {  // floats i .. i+3, i % 4 == 0
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, i * 4u, 0, CPOL_SC1));
+}
+DPK_DEV void cstore(coh_buf r, uint32_t i, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, i * 4u, 0, CPOL_SC1);
 }
 
 // Last-arriving-workgroup election.  Every workgroup calls this once after

@@ -1,0 +1,540 @@
+// A whole decode step in one persistent launch (gfx950, bf16 weights).
+//
+// The step is the single-token decode order of the Butter architecture notes
+// ("SINGLE-TOKEN DECODE": gather, then per layer norm / q,k,v / rope at the
+// cache length / cache append / attention / o / add / norm / gate, up /
+// silu-mul / down / add, then final norm, lm_head and the greedy token).
+// Every weight is read once per step, so the step is an HBM stream; what
+// keeps a stream of ~180 dependent kernels from reaching the bandwidth is the
+// gap at each kernel boundary, where the next weights only start to load
+// after the previous kernel has drained.
+//
+// Here one workgroup per CU runs all phases in order, separated by grid-wide
+// barriers, and each workgroup issues the first weight loads of its next
+// phase *before* it waits at the barrier (weights do not depend on the
+// activations), so the barrier's latency overlaps the weight stream.  Data
+// handed between phases (activations, norm sums, attention records) is
+// written and read with device-coherent accesses, which is what makes it
+// visible across the XCDs' separate L2 caches inside one launch.
+//
+// Phases: embedding (h and its per-tile sums of squares), then per layer the
+// QKV GEMV, attention (with QK-norm, RoPE and the KV write), the O GEMV with
+// the residual add, the gate/up GEMV with SwiGLU and the down GEMV with the
+// residual add; then the lm_head GEMV with the greedy argmax.  The GEMVs are
+// gemv_body.h's; attention splits the context into 256-position chunks, one
+// per workgroup item (32 positions per wave), merged by the last chunk to
+// finish.
+//
+// The launch is cooperative (all workgroups resident), and every barrier wait
+// is bounded: a workgroup that waits too long raises an abort flag, after
+// which every barrier passes at once and the host sees the error flag.
+#include "gemv_body.h"
+
+namespace dpk {
+
+namespace {
+
+constexpr int MT = 512;        // threads per workgroup (8 waves)
+constexpr int AW = MT / 64;    // attention: waves per workgroup
+constexpr int ACH = 32 * AW;   // attention: positions per workgroup item
+constexpr int D = 128;         // head dim
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr unsigned SPIN_LIMIT = 200000;
+
+// Grid barrier in two levels: workgroup wg counts in on the counter of group
+// wg % 8 (its own 256-byte line; with round-robin dispatch that is the
+// workgroups of one XCD), the last of a group counts the group in on the top
+// counter, and every workgroup polls the top counter.  Counters only grow
+// within a launch (phase p completes at p * group size, p * 8).
+struct Barrier {
+  unsigned* ctr;         // [0] top, [64 * (1 + g)] group g
+  unsigned* abort_flag;
+  unsigned nwg;
+  unsigned phase;
+};
+
+// All of the workgroup's stores are complete before it counts in; prefetch()
+// (loads of the next phase that do not depend on other workgroups) is issued
+// after counting in and before the wait, so those loads fly while the barrier
+// completes.  Only wave 0 waits on memory for the barrier itself, and its
+// waits also cover its own prefetch loads (vector memory returns in order).
+template <typename F>
+DPK_DEV void grid_sync(Barrier& b, F&& prefetch) {
+  ++b.phase;
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
+  __syncthreads();
+  const unsigned ngrp = b.nwg < 8u ? b.nwg : 8u;
+  if (threadIdx.x == 0) {
+    const unsigned grp = blockIdx.x & 7u;
+    const unsigned gsize = (b.nwg - grp + 7u) / 8u;
+    const unsigned prev =
+        __hip_atomic_fetch_add(b.ctr + 64 * (1 + grp), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == b.phase * gsize - 1u) __hip_atomic_fetch_add(b.ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  prefetch();
+  if (threadIdx.x == 0) {
+    const unsigned target = b.phase * ngrp;
+    for (unsigned spin = 0;; ++spin) {
+      if (__hip_atomic_load(b.ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) break;
+      if (__hip_atomic_load(b.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) break;
+      if (spin >= SPIN_LIMIT) {
+        __hip_atomic_store(b.abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
+}
+
+// After the last barrier: the last workgroup out resets the arrival counter
+// for the next launch (no workgroup waits on it any more) and turns an abort
+// into bit 1 of the error word the host reads.
+DPK_DEV void grid_exit(Barrier& b, unsigned* exit_ctr, int* err) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(exit_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == b.nwg - 1) {
+      if (__hip_atomic_load(b.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+        atomicOr(err, 2);
+        __hip_atomic_store(b.abort_flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      for (int g = 0; g <= 8; ++g) __hip_atomic_store(b.ctr + 64 * g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(exit_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// h[m] = E[token m] and its sums of squares per 16-column tile (the first
+// layer's norm input, in the same layout the residual epilogues write).
+DPK_DEV void embed_phase(const MegaArgs& a, int wg, int nwg) {
+  const int tid = threadIdx.x;
+  const int ntile = a.H / 16;
+  for (int n = wg; n < ntile; n += nwg) {
+    if (tid < 16) {
+      for (int m = 0; m < a.M; ++m) {
+        int tok = a.ids_dev ? a.ids_dev[m] : a.rp[m].token;
+        if (tok < 0 || tok >= a.vocab) {
+          if (tid == 0) atomicOr(a.err, 1);
+          tok = 0;
+        }
+        const int col = n * 16 + tid;
+        const float v = bf16_to_f32(((const uint16_t*)a.emb)[(size_t)tok * a.H + col]);
+        cstore(coh_buffer(a.h), (uint32_t)(m * a.H + col), v);
+        float ss = v * v;
+        ss += __shfl_xor(ss, 1, 64);
+        ss += __shfl_xor(ss, 2, 64);
+        ss += __shfl_xor(ss, 4, 64);
+        ss += __shfl_xor(ss, 8, 64);
+        if (tid == 0) cstore(coh_buffer(a.sq), (uint32_t)(m * ntile + n), ss);
+      }
+    }
+  }
+}
+
+DPK_DEV void split_f16(float x, _Float16& hi, _Float16& lo) {
+  hi = (_Float16)x;
+  lo = (_Float16)(x - (float)hi);
+}
+
+// Attention of one layer for all rows.  Item = (row m, KV head g, chunk of
+// ACH positions); wave w of the item takes positions c0 + 32 w .. + 31.
+//   S   = K Q^T   on v_mfma_f32_16x16x32_f16, A = K rows from the cache, B = q
+//                 (the G query heads of g are the MFMA columns), q as fp16
+//                 hi + lo;
+//   O^T = V^T P^T with P^T straight from the S accumulators (hi + lo).
+// The waves' softmax statistics are combined in LDS; with more than one chunk
+// each chunk writes a record (max, sum, O) and the last chunk of (m, g) to
+// finish merges them (log-sum-exp weights).  QK-norm, RoPE and the new
+// position's K/V come from the raw QKV projection of the previous phase.
+template <int G, typename Sync>
+DPK_DEV void attn_phase(const MegaArgs& a, int layer, const uint16_t* qn, const uint16_t* kn, unsigned char* lds,
+                        int wg, int nwg, Sync&& sync) {
+  float* qs = (float*)lds;              // [G][D], scaled to the log2 domain
+  float* knew = qs + G * D;             // [D]
+  float* vnew = knew + D;               // [D]
+  float* wst = vnew + D;                // [AW][2][G]
+  float* ow = wst + AW * 2 * G;         // [AW][D][G]
+  float* ml = ow + AW * D * G;          // [2][MEGA_ATTN_MAXCH][G]
+  float* mw = ml + 2 * MEGA_ATTN_MAXCH * G;  // [MEGA_ATTN_MAXCH][G]
+  int* flag = (int*)(mw + MEGA_ATTN_MAXCH * G);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r16 = lane & 15, j4 = lane >> 4;
+  const int n_items = a.M * a.n_kv * a.max_chunks;
+  const int rec = D + 2;
+
+  u32x4 kf[2][D / 32];
+  u32x2 vf[D / 16][2];
+  float cs = 0.f, sn = 0.f, g0 = 1.f, g1 = 1.f;  // this wave's RoPE and gain values
+
+  // K / V^T fragments of the item's positions for this wave, and the RoPE /
+  // QK-norm constants of the row (none of it depends on the previous phase)
+  auto prefetch = [&](int it) {
+    const int chunk = it % a.max_chunks, g = (it / a.max_chunks) % a.n_kv, m = it / (a.max_chunks * a.n_kv);
+    const RowParam rp = a.rp[m];
+    const int ctx = rp.pos + 1;
+    const int c0 = chunk * ACH, c1 = min(ctx, c0 + ACH);
+    const int wp0 = c0 + 32 * wave;
+    const _Float16* Kb = (const _Float16*)a.kv.base + kv_slab(a.kv, rp.seq, layer, 0, g);
+    const _Float16* Vb = (const _Float16*)a.kv.base + kv_slab(a.kv, rp.seq, layer, 1, g);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int p = wp0 + 16 * t + r16;
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) {
+        kf[t][s] = u32x4{0u, 0u, 0u, 0u};
+        if (p < c1) kf[t][s] = *(const u32x4*)(Kb + (size_t)p * D + 32 * s + 8 * j4);
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int p = wp0 + 16 * h + 4 * j4;
+        vf[dt][h] = u32x2{0u, 0u};
+        // the 4-position group stays inside the slab row (max_seq % 64 == 0)
+        if (p < c1) {
+          vf[dt][h] = *(const u32x2*)(Vb + (size_t)(dt * 16 + r16) * a.kv.max_seq + p);
+          if (p + 4 > c1) {  // positions past the context may hold any bits (0 * NaN)
+            f16x4 v4 = __builtin_bit_cast(f16x4, vf[dt][h]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (p + e >= c1) v4[e] = (_Float16)0.f;
+            vf[dt][h] = __builtin_bit_cast(u32x2, v4);
+          }
+        }
+      }
+    if (wave <= G) {
+      cs = a.rope_cos[(size_t)rp.pos * (D / 2) + lane];
+      sn = a.rope_sin[(size_t)rp.pos * (D / 2) + lane];
+      const uint16_t* gn = wave < G ? qn : kn;
+      if (gn) {
+        g0 = bf16_to_f32(gn[lane]);
+        g1 = bf16_to_f32(gn[lane + 64]);
+      }
+    }
+  };
+
+  int it = wg;
+  sync([&] {  // the QKV projection of every row is complete after this
+    if (it < n_items) prefetch(it);
+  });
+  for (; it < n_items; it += nwg) {
+    if (it != wg) prefetch(it);
+    const int chunk = it % a.max_chunks, g = (it / a.max_chunks) % a.n_kv, m = it / (a.max_chunks * a.n_kv);
+    const RowParam rp = a.rp[m];
+    const int ctx = rp.pos + 1;
+    const int nch = (ctx + ACH - 1) / ACH;
+    if (chunk >= nch) continue;  // uniform over the workgroup
+    const int c0 = chunk * ACH, c1 = min(ctx, c0 + ACH);
+    const int wp0 = c0 + 32 * wave;
+    const bool own = rp.pos >= c0 && rp.pos < c1;
+
+    // ---- q heads (waves < G), the new key (wave G) and value (wave G + 1)
+    // raw projection = the two K-half partial sums
+    const coh_buf q0 = coh_buffer(a.qkv), q1 = coh_buffer(a.qkv1);
+    const uint32_t row = (uint32_t)(m * a.ld_qkv);
+    if (wave <= G && (wave < G || own)) {
+      const uint32_t x = row + (uint32_t)((wave < G ? g * G + wave : a.n_heads + g) * D);
+      const float xa = cload(q0, x + lane) + cload(q1, x + lane);
+      const float xb = cload(q0, x + lane + 64) + cload(q1, x + lane + 64);
+      const bool norm = (wave < G ? qn : kn) != nullptr;
+      const float ss = wave_sum(xa * xa + xb * xb);
+      const float r = norm ? rsqrtf(ss / (float)D + a.eps) : 1.0f;
+      const float x1 = xa * r * g0, x2 = xb * r * g1;
+      const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
+      if (wave < G) {
+        qs[wave * D + lane] = y1 * a.scale * LOG2E;
+        qs[wave * D + lane + 64] = y2 * a.scale * LOG2E;
+      } else {
+        knew[lane] = y1;
+        knew[lane + 64] = y2;
+      }
+    } else if (wave == G + 1 && own) {
+      const uint32_t v = row + (uint32_t)((a.n_heads + a.n_kv + g) * D);
+      vnew[lane] = cload(q0, v + lane) + cload(q1, v + lane);
+      vnew[lane + 64] = cload(q0, v + lane + 64) + cload(q1, v + lane + 64);
+    }
+    __syncthreads();
+    if (own) {
+      for (int e = tid; e < D; e += MT) {
+        kv_store(a.kv, kv_offset(a.kv, rp.seq, layer, 0, g, e, rp.pos), knew[e]);
+        kv_store(a.kv, kv_offset(a.kv, rp.seq, layer, 1, g, e, rp.pos), vnew[e]);
+      }
+      // the new position inside this wave's fragments comes from knew / vnew
+      const int off = rp.pos - wp0;
+      if (off >= 0 && off < 32) {
+        // compile-time fragment indices only (runtime ones would spill the arrays)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          if (t == off / 16 && r16 == off % 16) {
+#pragma unroll
+            for (int s = 0; s < D / 32; ++s) {
+              f16x8 k8;
+#pragma unroll
+              for (int i = 0; i < 8; ++i) k8[i] = (_Float16)knew[32 * s + 8 * j4 + i];
+              kf[t][s] = __builtin_bit_cast(u32x4, k8);
+            }
+          }
+        const int e4 = off % 4;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          if (h == off / 16 && j4 == (off % 16) / 4) {
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) {
+              f16x4 v4 = __builtin_bit_cast(f16x4, vf[dt][h]);
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (e == e4) v4[e] = (_Float16)vnew[dt * 16 + r16];
+              vf[dt][h] = __builtin_bit_cast(u32x2, v4);
+            }
+          }
+      }
+    }
+
+    // ---- S = K Q^T (log2 domain), 2 tiles of 16 positions
+    f16x8 qh[D / 32], ql[D / 32];
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        _Float16 h = (_Float16)0.f, l = (_Float16)0.f;
+        if (r16 < G) split_f16(qs[r16 * D + 32 * s + 8 * j4 + i], h, l);
+        qh[s][i] = h;
+        ql[s][i] = l;
+      }
+    f32x4 sc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) {
+        const f16x8 A = __builtin_bit_cast(f16x8, kf[t][s]);
+        sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qh[s], sc[t], 0, 0, 0);
+        sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, ql[s], sc[t], 0, 0, 0);
+      }
+    }
+    // mask (positions 16 t + 4 j4 + v past the context), column max / sum
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        if (wp0 + 16 * t + 4 * j4 + v >= c1) sc[t][v] = -INFINITY;
+        mx = fmaxf(mx, sc[t][v]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float sum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float e = (sc[t][v] == -INFINITY) ? 0.f : exp2f(sc[t][v] - mx);
+        sc[t][v] = e;
+        sum += e;
+      }
+    sum += __shfl_xor(sum, 16, 64);
+    sum += __shfl_xor(sum, 32, 64);
+
+    // ---- O^T = V^T P^T over the 32 positions (k slots 0..3 from tile 0, 4..7 from tile 1)
+    f32x4 o[D / 16];
+    {
+      f16x8 ph, pl;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        _Float16 h0, l0, h1, l1;
+        split_f16(sc[0][v], h0, l0);
+        split_f16(sc[1][v], h1, l1);
+        ph[v] = h0;
+        pl[v] = l0;
+        ph[4 + v] = h1;
+        pl[4 + v] = l1;
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const u32x4 w = {vf[dt][0].x, vf[dt][0].y, vf[dt][1].x, vf[dt][1].y};
+        const f16x8 A = __builtin_bit_cast(f16x8, w);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, ph, o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pl, o[dt], 0, 0, 0);
+      }
+    }
+
+    // ---- combine the waves (per column = query head)
+    if (r16 < G) {
+      if (j4 == 0) {
+        wst[(wave * 2 + 0) * G + r16] = mx;
+        wst[(wave * 2 + 1) * G + r16] = sum;
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) ow[(wave * D + dt * 16 + 4 * j4 + v) * G + r16] = o[dt][v];
+    }
+    __syncthreads();
+    // chunk statistics per column c: Mc = max_w m_w, Lc = sum_w 2^(m_w - Mc) l_w,
+    // Oc = sum_w 2^(m_w - Mc) O_w
+    const coh_buf ob = coh_buffer(a.attn_out), pb = coh_buffer(a.part);
+    const uint32_t outp = (uint32_t)((m * a.n_heads + g * G) * D);
+    for (int i = tid; i < G * D; i += MT) {
+      const int c = i / D, e = i % D;
+      float Mc = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < AW; ++w) Mc = fmaxf(Mc, wst[(w * 2) * G + c]);
+      float L = 0.f, O = 0.f;
+#pragma unroll
+      for (int w = 0; w < AW; ++w) {
+        const float mwv = wst[(w * 2) * G + c];
+        const float f = (mwv == -INFINITY) ? 0.f : exp2f(mwv - Mc);
+        L += f * wst[(w * 2 + 1) * G + c];
+        O += f * ow[(w * D + e) * G + c];
+      }
+      if (nch == 1) {
+        cstore(ob, outp + c * D + e, O / L);
+      } else {
+        const uint32_t r = (uint32_t)(((m * a.n_heads + g * G + c) * a.max_chunks + chunk) * rec);
+        cstore(pb, r + 2 + e, O);
+        if (e == 0) {
+          cstore(pb, r, Mc);
+          cstore(pb, r + 1, L);
+        }
+      }
+    }
+    if (nch > 1 && last_block_arrive(a.attn_counters + m * a.n_kv + g, nch, flag)) {
+      for (int i = tid; i < G * nch; i += MT) {
+        const int c = i % G, ch = i / G;
+        const uint32_t base = (uint32_t)(((m * a.n_heads + g * G + c) * a.max_chunks + ch) * rec);
+        ml[ch * G + c] = cload(pb, base);
+        ml[(MEGA_ATTN_MAXCH + ch) * G + c] = cload(pb, base + 1);
+      }
+      __syncthreads();
+      if (tid < G) {
+        const int c = tid;
+        float Mx = -INFINITY;
+        for (int ch = 0; ch < nch; ++ch) Mx = fmaxf(Mx, ml[ch * G + c]);
+        float den = 0.f;
+        for (int ch = 0; ch < nch; ++ch) {
+          const float w = exp2f(ml[ch * G + c] - Mx);
+          mw[ch * G + c] = w;
+          den += w * ml[(MEGA_ATTN_MAXCH + ch) * G + c];
+        }
+        const float inv = 1.0f / den;
+        for (int ch = 0; ch < nch; ++ch) mw[ch * G + c] *= inv;
+      }
+      __syncthreads();
+      for (int i = tid; i < G * D; i += MT) {
+        const int c = i / D, e = i % D;
+        const uint32_t base = (uint32_t)(((m * a.n_heads + g * G + c) * a.max_chunks) * rec + 2 + e);
+        float O = 0.f;
+        int ch = 0;
+        for (; ch + 4 <= nch; ch += 4) {
+          const float o0 = cload(pb, base + ch * rec), o1 = cload(pb, base + (ch + 1) * rec);
+          const float o2 = cload(pb, base + (ch + 2) * rec), o3 = cload(pb, base + (ch + 3) * rec);
+          O += mw[ch * G + c] * o0 + mw[(ch + 1) * G + c] * o1 + mw[(ch + 2) * G + c] * o2 +
+               mw[(ch + 3) * G + c] * o3;
+        }
+        for (; ch < nch; ++ch) O += mw[ch * G + c] * cload(pb, base + ch * rec);
+        cstore(ob, outp + c * D + e, O);
+      }
+    }
+    __syncthreads();  // LDS is rewritten by the next item
+  }
+}
+
+template <int G>
+__global__ __launch_bounds__(MT, 1) void decode_step_kernel(MegaArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const int wg = blockIdx.x, nwg = gridDim.x;
+  Barrier bar{a.bar, a.bar + MEGA_BAR_ABORT, (unsigned)nwg, 0u};
+  // phase tracing (workgroup 0, thread 0): ticks from one barrier release to
+  // the next go to the phase the barrier closes
+  const bool tr = a.trace && wg == 0 && threadIdx.x == 0;
+  unsigned long long t_prev = tr ? wall_clock64() : 0ull;
+  int closing = MP_EMBED;
+  auto mark = [&](int phase) {
+    if (tr) {
+      const unsigned long long t = wall_clock64();
+      a.trace[phase] += t - t_prev;
+      t_prev = t;
+    }
+  };
+  auto sync = [&](auto&& prefetch) {
+    grid_sync(bar, prefetch);
+    mark(closing);
+  };
+  using gemv_detail::gemv_body;
+  embed_phase(a, wg, nwg);
+  for (int l = 0; l < a.n_layers; ++l) {
+    const MegaLayer& L = a.layers[l];
+    // QKV over the two halves of K; the second half rotates the workgroups so
+    // that the 1.5 row tiles per workgroup of each half add up evenly
+    gemv_body<W_BF16, 1, 8, true>(L.qkv[0], a.M, lds, wg, nwg, sync);
+    gemv_body<W_BF16, 1, 8, true>(L.qkv[1], a.M, lds, (wg + nwg / 2) % nwg, nwg, [](auto&& issue) { issue(); });
+    closing = MP_QKV;
+    attn_phase<G>(a, l, L.qn, L.kn, lds, wg, nwg, sync);
+    closing = MP_ATTN;
+    gemv_body<W_BF16, 1, 8, true>(L.o, a.M, lds, wg, nwg, sync);
+    closing = MP_O;
+    gemv_body<W_BF16, 2, 8, true>(L.gu, a.M, lds, wg, nwg, sync);
+    closing = MP_GATEUP;
+    gemv_body<W_BF16, 1, 8, true>(L.down, a.M, lds, wg, nwg, sync);
+    closing = MP_DOWN;
+  }
+  gemv_body<W_BF16, 1, 8, true>(a.head, a.M, lds, wg, nwg, sync);
+  grid_exit(bar, a.bar + MEGA_BAR_EXIT, a.err);
+  if (tr) {
+    mark(MP_HEAD);
+    a.trace[MP_STEPS] += 1;
+  }
+}
+
+template <int G>
+const void* mega_kernel_ptr() {
+  return (const void*)decode_step_kernel<G>;
+}
+
+const void* mega_kernel_for(int G) {
+  switch (G) {
+    case 1: return mega_kernel_ptr<1>();
+    case 2: return mega_kernel_ptr<2>();
+    case 4: return mega_kernel_ptr<4>();
+    default: return nullptr;
+  }
+}
+
+}  // namespace
+
+size_t mega_attn_lds_bytes(int G) {
+  return ((size_t)G * D + 2 * D + AW * 2 * G + AW * D * G + 3 * MEGA_ATTN_MAXCH * G + 4) * 4;
+}
+
+int mega_threads() { return MT; }
+int mega_attn_chunk() { return ACH; }
+
+// Workgroups per CU the kernel can keep resident with lds bytes of LDS (0 if
+// the kernel does not exist for G).
+int mega_occupancy(int G, size_t lds) {
+  const void* k = mega_kernel_for(G);
+  if (!k) return 0;
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k, MT, lds) != hipSuccess) return 0;
+  return nb;
+}
+
+hipError_t launch_decode_step(const MegaArgs& a, int G, int n_wg, size_t lds, hipStream_t stream) {
+  const void* k = mega_kernel_for(G);
+  if (!k || n_wg < 1 || a.M < 1 || a.M > 16) return hipErrorInvalidValue;
+  MegaArgs copy = a;
+  void* args[] = {&copy};
+  hipEvent_t start = g_timing.start, stop = g_timing.stop;
+  if (start) (void)hipEventRecord(start, stream);
+  const hipError_t e = hipLaunchCooperativeKernel(k, dim3(n_wg), dim3(MT), args, (unsigned)lds, stream);
+  if (stop) (void)hipEventRecord(stop, stream);
+  g_timing.start = nullptr;
+  return e != hipSuccess ? e : hipGetLastError();
+}
+
+}  // namespace dpk

@@ -78,6 +78,7 @@ struct GemvArgs {
   int M, K, N;              // rows (<=16), input dim, output rows (per matrix for swiglu)
   int fmt, tiles, swiglu, epi;
   int grid;                 // workgroups (they loop over row tiles)
+  int kofs, kfull;          // reduce over columns [kofs, kofs + K) of rows of kfull (0: K) columns
   const void* w[3];
   const void* sb[3];
   int seg_end[3];
@@ -97,6 +98,7 @@ struct GemvArgs {
   int* argmax_out;
 };
 size_t gemv_lds_bytes(int M, int K, int tiles, int fmt);
+int gemv_waves(int K, int tiles, int fmt);
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream);
 // fragment-order copies of [N][K] weights for launch_gemv
 hipError_t launch_tile_bf16(const uint16_t* src, uint16_t* dst, int N, int K, hipStream_t stream);
@@ -202,5 +204,48 @@ struct AttnPrefillArgs {
   float scale;
 };
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t stream);
+
+// ---- whole decode step in one persistent (cooperative) launch, bf16 weights
+constexpr int MEGA_ATTN_MAXCH = 64;  // attention chunks per row (256 positions each)
+struct MegaLayer {                   // device-resident, one per layer
+  GemvArgs qkv[2];                   // the QKV projection over the two halves of K (partial sums)
+  GemvArgs o, gu, down;              // M is set per launch
+  const uint16_t* qn;                // QK-norm gains (bf16) or null
+  const uint16_t* kn;
+};
+struct MegaArgs {
+  int M, n_layers, H, vocab;
+  const MegaLayer* layers;
+  GemvArgs head;
+  const void* emb;                   // bf16 [vocab][H]
+  const RowParam* rp;
+  const int32_t* ids_dev;            // token ids, or null: rp[m].token
+  float* h;                          // [M][H] residual
+  float* sq;                         // [M][H/16] per-tile sums of squares
+  int* err;                          // bit 0: token out of range
+  int n_heads, n_kv;
+  KVDesc kv;
+  const float* qkv;                  // [M][ld_qkv] raw projection, first half of K
+  const float* qkv1;                 // [M][ld_qkv] second half of K (q = qkv + qkv1)
+  int ld_qkv;
+  const float* rope_cos;
+  const float* rope_sin;
+  float eps, scale;
+  int max_chunks;
+  float* part;                       // [M][n_heads][max_chunks][d + 2]
+  unsigned* attn_counters;           // [M * n_kv]
+  float* attn_out;                   // [M][n_heads * d]
+  unsigned* bar;                     // MEGA_BAR_WORDS zeroed words: barrier counters, exit count, abort flag
+  unsigned long long* trace;         // null, or MEGA_TRACE_WORDS accumulators (see below)
+};
+// Phase tracing: workgroup 0 adds the wall-clock ticks from one barrier
+// release to the next to trace[phase] and counts steps in trace[0].
+enum MegaPhase : int { MP_STEPS = 0, MP_EMBED, MP_QKV, MP_ATTN, MP_O, MP_GATEUP, MP_DOWN, MP_HEAD, MEGA_TRACE_WORDS };
+constexpr int MEGA_BAR_EXIT = 64 * 9, MEGA_BAR_ABORT = 64 * 10, MEGA_BAR_WORDS = 64 * 11;
+size_t mega_attn_lds_bytes(int G);
+int mega_threads();
+int mega_attn_chunk();
+int mega_occupancy(int G, size_t lds);
+hipError_t launch_decode_step(const MegaArgs& a, int G, int n_wg, size_t lds, hipStream_t stream);
 
 }  // namespace dpk

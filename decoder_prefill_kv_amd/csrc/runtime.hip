@@ -80,6 +80,14 @@ struct dpk_model {
   _Float16 *y16 = nullptr, *q16 = nullptr, *o16 = nullptr, *act16 = nullptr;
   unsigned *counters = nullptr, *attn_counters = nullptr, *gemm_counters = nullptr;
   float* gemm_ws = nullptr;
+  // whole-step persistent decode kernel
+  MegaLayer* mega_layers = nullptr;  // device table (in scratch)
+  unsigned* mega_bar = nullptr;      // barrier words (in scratch)
+  unsigned long long* mega_trace = nullptr;  // phase-time accumulators (in scratch)
+  float* mega_qkv1 = nullptr;        // second K-half of the QKV projection [16][Nqkv]
+  int mega_G = 0;                    // query heads per KV head, 0: not available
+  size_t mega_lds = 0;
+  bool mega_table = false;           // table written for the loaded weights
   int* err_flag = nullptr;
   int* argmax_sink = nullptr;
   int rows_f32 = 0;       // rows of the fp32 activation buffers
@@ -112,7 +120,8 @@ size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct ScratchLayout {
   size_t rope_cos, rope_sin, rows, h, rs, qkv, y32, qbuf, attn_o, act, part, sink, sq, cand_val, cand_idx, attn_part,
-      y16, q16, o16, act16, counters, attn_counters, err, argmax_sink, gemm_ws, gemm_counters, total;
+      y16, q16, o16, act16, counters, attn_counters, err, argmax_sink, gemm_ws, gemm_counters, mega_layers, mega_bar,
+      mega_trace, mega_qkv1, total;
   int rows_f32, attn_chunks_cap;
   size_t part_floats;
 };
@@ -173,6 +182,10 @@ ScratchLayout scratch_layout(const dpk_config& c) {
   const bool gemm_path = !f32 && R > SKINNY_MAX;
   L.gemm_ws = take(gemm_path ? GEMM_WS_TILES * GEMM_TILE_FLOATS * 4 : 0);
   L.gemm_counters = take(gemm_path ? GEMM_WS_TILES * 4 : 0);
+  L.mega_layers = take(f32 ? 0 : (size_t)c.n_layers * sizeof(MegaLayer));
+  L.mega_bar = take(MEGA_BAR_WORDS * 4);
+  L.mega_trace = take(MEGA_TRACE_WORDS * 8);
+  L.mega_qkv1 = take(f32 ? 0 : SKINNY_MAX * Nqkv * 4);
   L.total = o;
   return L;
 }
@@ -215,11 +228,13 @@ size_t kv_bytes(const dpk_config& c) {
 
 enum KClass : int {
   K_GEMV_QKV, K_GEMV_O, K_GEMV_GATEUP, K_GEMV_DOWN, K_GEMV_HEAD, K_ATTN_DECODE, K_EMBED, K_GEMM_QKV, K_GEMM_O,
-  K_GEMM_GATEUP, K_GEMM_DOWN, K_ATTN_PREFILL, K_QK_ROPE_KV, K_RMSNORM, K_GEMV_F32, K_OTHER, K_NCLASS
+  K_GEMM_GATEUP, K_GEMM_DOWN, K_ATTN_PREFILL, K_QK_ROPE_KV, K_RMSNORM, K_GEMV_F32, K_DECODE_STEP, K_STEP_EMBED, K_STEP_QKV,
+  K_STEP_ATTN, K_STEP_O, K_STEP_GATEUP, K_STEP_DOWN, K_STEP_HEAD, K_OTHER, K_NCLASS
 };
 const char* const kclass_name[K_NCLASS] = {
     "gemv.qkv", "gemv.o", "gemv.gate_up", "gemv.down", "gemv.head", "attn.decode", "embed", "gemm.qkv", "gemm.o",
-    "gemm.gate_up", "gemm.down", "attn.prefill", "qk_rope_kv", "rmsnorm", "gemv.f32", "other"};
+    "gemm.gate_up", "gemm.down", "attn.prefill", "qk_rope_kv", "rmsnorm", "gemv.f32", "decode.step", "step.embed", "step.qkv",
+    "step.attn", "step.o", "step.gate_up", "step.down", "step.head", "other"};
 
 // Start/stop events of the launches of one kernel class when profiling is on.
 struct ProfScope {
@@ -383,9 +398,9 @@ dpk_status attn_decode(dpk_model* md, int M, int max_ctx, const float* q, float*
 }
 
 // One decode GEMV launch (whole K per workgroup, gemv.hip).
-dpk_status gemv(dpk_model* md, int cls, int M, const float* x, int ldx, const float* sq_in, int sq_nb,
-                const void* gain, const LinearW* segs, int nseg, int epi, bool swiglu, int tiles, float* out,
-                int ldo, float* sq_out, int32_t* argmax, hipStream_t st) {
+GemvArgs gemv_args(dpk_model* md, int M, const float* x, int ldx, const float* sq_in, int sq_nb, const void* gain,
+                   const LinearW* segs, int nseg, int epi, bool swiglu, int tiles, float* out, int ldo, float* sq_out,
+                   int32_t* argmax) {
   const dpk_config& c = md->cfg;
   GemvArgs a{};
   a.M = M;
@@ -418,6 +433,14 @@ dpk_status gemv(dpk_model* md, int cls, int M, const float* x, int ldx, const fl
   a.cand_val = md->cand_val;
   a.cand_idx = md->cand_idx;
   a.argmax_out = argmax ? argmax : md->argmax_sink;
+  return a;
+}
+
+dpk_status gemv(dpk_model* md, int cls, int M, const float* x, int ldx, const float* sq_in, int sq_nb,
+                const void* gain, const LinearW* segs, int nseg, int epi, bool swiglu, int tiles, float* out,
+                int ldo, float* sq_out, int32_t* argmax, hipStream_t st) {
+  const GemvArgs a = gemv_args(md, M, x, ldx, sq_in, sq_nb, gain, segs, nseg, epi, swiglu, tiles, out, ldo, sq_out,
+                               argmax);
   const double nrows = swiglu ? 2.0 * a.N : (double)a.N;
   ProfScope ps(md, st, cls, nrows * a.K * wbytes_per_elem(md->fmt) + (double)M * a.K * 4 + (double)M * a.N * 4,
                2.0 * M * nrows * a.K);
@@ -475,6 +498,111 @@ dpk_status forward_decode(dpk_model* md, int M, int max_ctx, const int32_t* ids_
   float* dst = logits ? logits : md->sink;
   return gemv(md, K_GEMV_HEAD, M, md->h, H, md->sq, sq_nb, md->final_norm, &md->head, 1, EPI_HEAD, false, 1, dst,
               c.vocab, nullptr, argmax, st);
+}
+
+// LDS bytes of the persistent decode kernel for M rows, or 0 if the model or
+// M does not fit it: bf16 weights, head_dim 128, 1, 2 or 4 query heads per KV
+// head, every GEMV on eight waves, at most 64 KB of LDS, one resident
+// workgroup per CU.
+size_t mega_lds_for(dpk_model* md, int M, int max_ctx) {
+  const dpk_config& c = md->cfg;
+  if ((c.flags & DPK_FLAG_DECODE_MULTI) || md->fmt != DPK_FMT_BF16 || !md->mega_layers) return 0;
+  if (c.head_dim != 128 || c.n_heads % c.n_kv_heads) return 0;
+  const int G = c.n_heads / c.n_kv_heads;
+  if (G != 1 && G != 2 && G != 4) return 0;
+  if (!decode_fits(md, M)) return 0;
+  const int H = c.hidden, Qd = c.n_heads * c.head_dim, I = c.intermediate;
+  if (H % 2048 || gemv_waves(H / 2, 1, W_BF16) != 8 || gemv_waves(H, 1, W_BF16) != 8 ||
+      gemv_waves(Qd, 1, W_BF16) != 8 || gemv_waves(H, 2, W_BF16) != 8 || gemv_waves(I, 1, W_BF16) != 8)
+    return 0;
+  if ((max_ctx + mega_attn_chunk() - 1) / mega_attn_chunk() > MEGA_ATTN_MAXCH) return 0;
+  size_t lds = mega_attn_lds_bytes(G);
+  for (size_t b : {gemv_lds_bytes(M, H, 1, W_BF16), gemv_lds_bytes(M, Qd, 1, W_BF16), gemv_lds_bytes(M, H, 2, W_BF16),
+                   gemv_lds_bytes(M, I, 1, W_BF16)})
+    lds = b > lds ? b : lds;
+  if (lds > 64 * 1024) return 0;
+  if (mega_occupancy(G, lds) < 1) return 0;
+  return lds;
+}
+
+// Device table of the per-layer GEMV arguments of the persistent kernel.
+dpk_status mega_table(dpk_model* md, hipStream_t st) {
+  const dpk_config& c = md->cfg;
+  const int H = c.hidden, Qd = c.n_heads * c.head_dim, I = c.intermediate;
+  std::vector<MegaLayer> t(c.n_layers);
+  for (int l = 0; l < c.n_layers; ++l) {
+    const LayerW& L = md->layers[l];
+    LinearW qkv[3] = {L.q, L.k, L.v};
+    LinearW gu[2] = {L.gate, L.up};
+    for (int hf = 0; hf < 2; ++hf) {
+      GemvArgs& q = t[l].qkv[hf];
+      q = gemv_args(md, 1, md->h, H, md->sq, H / 16, L.in_norm, qkv, 3, EPI_STORE, false, 1,
+                    hf ? md->mega_qkv1 : md->qkv, md->Nqkv, nullptr, nullptr);
+      q.K = H / 2;
+      q.kofs = hf * (H / 2);
+      q.kfull = H;
+    }
+    t[l].o = gemv_args(md, 1, md->attn_o, Qd, nullptr, 0, nullptr, &L.o, 1, EPI_RESID, false, 1, md->h, H, md->sq,
+                       nullptr);
+    t[l].gu = gemv_args(md, 1, md->h, H, md->sq, H / 16, L.post_norm, gu, 2, EPI_SWIGLU, true, 2, md->act, I, nullptr,
+                        nullptr);
+    t[l].down = gemv_args(md, 1, md->act, I, nullptr, 0, nullptr, &L.down, 1, EPI_RESID, false, 1, md->h, H, md->sq,
+                          nullptr);
+    t[l].qn = c.qk_norm ? (const uint16_t*)L.q_norm : nullptr;
+    t[l].kn = c.qk_norm ? (const uint16_t*)L.k_norm : nullptr;
+  }
+  HIP_TRY(hipMemcpyAsync(md->mega_layers, t.data(), sizeof(MegaLayer) * t.size(), hipMemcpyHostToDevice, st));
+  HIP_TRY(hipStreamSynchronize(st));  // t is a host temporary
+  md->mega_table = true;
+  return DPK_OK;
+}
+
+// Decode step of M rows (parameters in md->rows_dev) as one persistent launch.
+dpk_status forward_mega(dpk_model* md, int M, int max_ctx, size_t lds, const int32_t* ids_dev, float* logits,
+                        int32_t* argmax, hipStream_t st, double kv_positions) {
+  const dpk_config& c = md->cfg;
+  dpk_status s;
+  if (!md->mega_table && (s = mega_table(md, st))) return s;
+  const int H = c.hidden;
+  MegaArgs a{};
+  a.M = M;
+  a.n_layers = c.n_layers;
+  a.H = H;
+  a.vocab = c.vocab;
+  a.layers = md->mega_layers;
+  a.head = gemv_args(md, M, md->h, H, md->sq, H / 16, md->final_norm, &md->head, 1, EPI_HEAD, false, 1,
+                     logits ? logits : md->sink, c.vocab, nullptr, argmax);
+  a.emb = md->embed.w;
+  a.rp = md->rows_dev;
+  a.ids_dev = ids_dev;
+  a.h = md->h;
+  a.sq = md->sq;
+  a.err = md->err_flag;
+  a.n_heads = c.n_heads;
+  a.n_kv = c.n_kv_heads;
+  a.kv = md->kvd;
+  a.qkv = md->qkv;
+  a.qkv1 = md->mega_qkv1;
+  a.ld_qkv = md->Nqkv;
+  a.rope_cos = md->rope_cos;
+  a.rope_sin = md->rope_sin;
+  a.eps = c.rms_eps;
+  a.scale = 1.0f / sqrtf((float)c.head_dim);
+  a.max_chunks = (max_ctx + mega_attn_chunk() - 1) / mega_attn_chunk();
+  a.part = md->attn_part;
+  a.attn_counters = md->attn_counters;
+  a.attn_out = md->attn_o;
+  a.bar = md->mega_bar;
+  a.trace = md->prof ? md->mega_trace : nullptr;
+  // algorithmic work: every linear weight (lm_head included) once, the KV of
+  // every attended position, the new positions' K/V
+  const double Qd = (double)c.n_heads * c.head_dim;
+  const double params = (double)c.n_layers * ((double)md->Nqkv * H + H * Qd + 3.0 * c.intermediate * H) +
+                        (double)c.vocab * H;
+  const double kvb = (kv_positions + M) * 2.0 * c.n_kv_heads * c.head_dim * 2.0 * c.n_layers;
+  ProfScope ps(md, st, K_DECODE_STEP, params * 2.0 + kvb, 2.0 * M * params + 4.0 * kv_positions * Qd * c.n_layers);
+  HIP_TRY(launch_decode_step(a, c.n_heads / c.n_kv_heads, md->n_cu, lds, st));
+  return DPK_OK;
 }
 
 // Final norm + lm_head + greedy argmax for `rows` rows of x (weight-streaming
@@ -772,7 +900,12 @@ dpk_status dpk_bind_workspace(dpk_model* md, void* kv, void* scratch, void* prep
   md->err_flag = (int*)(s + L.err);
   md->argmax_sink = (int*)(s + L.argmax_sink);
   md->gemm_ws = L.gemm_counters > L.gemm_ws ? (float*)(s + L.gemm_ws) : nullptr;
-  md->gemm_counters = L.total > L.gemm_counters ? (unsigned*)(s + L.gemm_counters) : nullptr;
+  md->gemm_counters = L.mega_layers > L.gemm_counters ? (unsigned*)(s + L.gemm_counters) : nullptr;
+  md->mega_layers = L.mega_bar > L.mega_layers ? (MegaLayer*)(s + L.mega_layers) : nullptr;
+  md->mega_bar = (unsigned*)(s + L.mega_bar);
+  md->mega_trace = (unsigned long long*)(s + L.mega_trace);
+  md->mega_qkv1 = (float*)(s + L.mega_qkv1);
+  md->mega_table = false;
   md->rows_f32 = L.rows_f32;
   md->attn_chunks_cap = L.attn_chunks_cap;
   md->part_floats = L.part_floats;
@@ -791,6 +924,7 @@ dpk_status dpk_bind_workspace(dpk_model* md, void* kv, void* scratch, void* prep
   HIP_TRY(hipMemsetAsync(md->attn_counters, 0, (size_t)(md->fmt == DPK_FMT_F32 ? c.max_rows : SKINNY_MAX) * c.n_kv_heads * 4, st));
   HIP_TRY(hipMemsetAsync(md->err_flag, 0, 4, st));
   if (md->gemm_counters) HIP_TRY(hipMemsetAsync(md->gemm_counters, 0, GEMM_WS_TILES * 4, st));
+  HIP_TRY(hipMemsetAsync(md->mega_bar, 0, MEGA_BAR_WORDS * 4, st));
   HIP_TRY(launch_rope_table(md->rope_cos, md->rope_sin, c.max_seq, c.head_dim, c.rope_theta, st));
   md->bound = true;
   return DPK_OK;
@@ -800,6 +934,7 @@ dpk_status dpk_load_weights(dpk_model* md, const dpk_tensor* t, int32_t n, void*
   if (!md || (!t && n)) return fail(DPK_EINVAL, "null argument");
   if (md->failed) return fail(DPK_ESTATE, "model failed");
   if (!md->bound) return fail(DPK_ESTATE, "bind the workspace before loading weights");
+  md->mega_table = false;
   const dpk_config& c = md->cfg;
   const int fmt = md->fmt;
   const int gdt = fmt == DPK_FMT_F32 ? DPK_DT_F32 : DPK_DT_BF16;
@@ -968,7 +1103,10 @@ dpk_status dpk_decode_step(dpk_model* md, int32_t batch, const int32_t* seqs, co
   if ((s = upload_rows(md, rows, batch, st))) return s;
   double kvpos = 0;
   for (int b = 0; b < batch; ++b) kvpos += pos[b] + 1;
-  if (decode_fits(md, batch))
+  const size_t mega_lds = mega_lds_for(md, batch, max_ctx);
+  if (mega_lds)
+    s = forward_mega(md, batch, max_ctx, mega_lds, ids_dev, logits, argmax, st, kvpos);
+  else if (decode_fits(md, batch))
     s = forward_decode(md, batch, max_ctx, ids_dev, logits, argmax, st, kvpos);
   else
     s = forward_rows(md, batch, max_ctx, ids_dev, 0, batch, logits, argmax, st, kvpos);
@@ -1020,6 +1158,8 @@ dpk_status dpk_check_device_errors(dpk_model* md, void* stream) {
   HIP_TRY(hipStreamSynchronize(st));
   if (flag) {
     HIP_TRY(hipMemsetAsync(md->err_flag, 0, 4, st));
+    HIP_TRY(hipStreamSynchronize(st));
+    if (flag & 2) return fail(DPK_EHIP, "a decode step's grid barrier timed out (results of that step are invalid)");
     return fail(DPK_ERANGE, "a device-side token id was outside [0, vocab)");
   }
   return DPK_OK;
@@ -1038,6 +1178,7 @@ dpk_status dpk_profile_begin(dpk_model* md, int32_t max_launches) {
   md->prof_max = max_launches;
   md->prof_rec.clear();
   md->prof_dropped = 0;
+  if (md->mega_trace) HIP_TRY(hipMemset(md->mega_trace, 0, MEGA_TRACE_WORDS * 8));
   md->prof = true;
   return DPK_OK;
 }
@@ -1057,6 +1198,31 @@ dpk_status dpk_profile_end(dpk_model* md, dpk_kernel_stat* stats, int32_t max_st
     by[c] += md->prof_rec[i].bytes;
     fl[c] += md->prof_rec[i].flops;
     ++cnt[c];
+  }
+  // phases of the persistent decode kernel: wall-clock ticks of workgroup 0
+  // from one barrier release to the next (a phase and the barrier after it)
+  unsigned long long tr[MEGA_TRACE_WORDS] = {};
+  if (md->mega_trace) HIP_TRY(hipMemcpy(tr, md->mega_trace, sizeof tr, hipMemcpyDeviceToHost));
+  if (tr[MP_STEPS]) {
+    int dev = 0, khz = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    HIP_TRY(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev));
+    const dpk_config& c = md->cfg;
+    const double steps = (double)tr[MP_STEPS], L = c.n_layers, H = c.hidden, I = c.intermediate;
+    const double Qd = (double)c.n_heads * c.head_dim;
+    struct P { int phase, cls; double per_step, wbytes; };
+    const P ps[] = {{MP_EMBED, K_STEP_EMBED, 1, 0},
+                    {MP_QKV, K_STEP_QKV, L, md->Nqkv * H * 2},
+                    {MP_ATTN, K_STEP_ATTN, L, 0},
+                    {MP_O, K_STEP_O, L, H * Qd * 2},
+                    {MP_GATEUP, K_STEP_GATEUP, L, 2 * I * H * 2},
+                    {MP_DOWN, K_STEP_DOWN, L, H * I * 2},
+                    {MP_HEAD, K_STEP_HEAD, 1, (double)c.vocab * H * 2}};
+    for (const P& p : ps) {
+      ms[p.cls] += khz > 0 ? (double)tr[p.phase] / khz : 0.0;
+      cnt[p.cls] += (long)(steps * p.per_step);
+      by[p.cls] += steps * p.per_step * p.wbytes;
+    }
   }
   int n = 0;
   for (int c = 0; c < K_NCLASS; ++c) {

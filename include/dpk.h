@@ -80,6 +80,10 @@ typedef struct {
 /* Prefill through the weight-streaming (decode) kernels in chunks of 16 rows
  * instead of the MFMA GEMM path (bf16 / q4 formats). */
 #define DPK_FLAG_PREFILL_STREAM 1
+/* Decode steps as one kernel launch per GEMV / attention instead of one
+ * persistent launch for the whole step (bf16 models whose shapes the
+ * persistent kernel supports use it by default). */
+#define DPK_FLAG_DECODE_MULTI 2
 
 /*
  * One weight tensor.  Names (transformers-style):
@@ -163,8 +167,10 @@ dpk_status dpk_verify(dpk_model* m, int32_t seq, const int32_t* ids, int32_t k_p
 /* Current cursor (cached positions) of a slot. */
 dpk_status dpk_seq_length(const dpk_model* m, int32_t seq, int32_t* length);
 
-/* Synchronize `stream` and report device-side input errors seen since the last
- * check (out-of-range device token ids): DPK_ERANGE if any, else DPK_OK. */
+/* Synchronize `stream` and report device-side errors seen since the last
+ * check: DPK_EHIP if a persistent decode step's bounded grid-barrier wait
+ * timed out (that step's outputs are invalid), else DPK_ERANGE for
+ * out-of-range device token ids, else DPK_OK.  Clears the errors. */
 dpk_status dpk_check_device_errors(dpk_model* m, void* stream);
 
 /* Per-kernel-class timing.  Between dpk_profile_begin and dpk_profile_end
