@@ -91,6 +91,82 @@ def copy_probe(nbytes):
     print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
 
 
+def bench_verify(dpk, cfg, w, seed, flags, K=5, rounds=24, warm=4):
+    """Speculative verify of K drafts (M = K + 1 rows) against the KV cache of
+    an 8192-token prompt: passes/s, and the ratio to one decode step at the
+    same context.  Each verify call returns the accept count to the host (one
+    synchronisation per pass, as the speculative loop needs it)."""
+    import torch
+    import synth
+    P = 8192
+    dec = dpk.Decoder(cfg, w, max_batch=1, max_seq=P + (K + 1) * (rounds + warm) + 8, max_rows=P, flags=flags)
+    lg = dec.logits_buffer(K + 1)
+    am = dec.argmax_buffer(K + 1)
+    dec.prefill(0, [int(t) for t in synth.prompt_ids(cfg, P, seed)], lg[0:1], am[0:1])
+    drafts = [int(t) for t in synth.prompt_ids(cfg, (K + 1) * (rounds + warm), seed, index=99)]
+    torch.cuda.synchronize()
+    pos = P
+    times = []
+    for r in range(rounds + warm):
+        t0 = time.perf_counter()
+        acc = dec.verify(0, drafts[r * (K + 1):(r + 1) * (K + 1)], pos, am, lg)
+        dt = time.perf_counter() - t0
+        if r >= warm:
+            times.append(dt)
+        pos += acc + 1
+    vt = sum(times) / len(times)
+    # one decode step at the same context, for the verify / decode ratio
+    a1 = dec.argmax_buffer(1)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(3):
+        dec.decode_step([0], [drafts[i]], [pos + i], a1)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(8):
+        dec.decode_step([0], [drafts[i]], [pos + 3 + i], a1)
+    e1.record()
+    torch.cuda.synchronize()
+    dt_dec = e0.elapsed_time(e1) / 8 / 1e3
+    dec.close()
+    H, L, d = cfg.hidden, cfg.n_layers, cfg.head_dim
+    wbytes = (cfg.n_linear_params() + cfg.vocab * H) * 2.0
+    kv = (P + K + 1) * 2 * L * cfg.n_kv_heads * d * 2.0
+    return {"workload": "verify K=%d (M=%d rows) over the KV cache of an %d-token prompt" % (K, K + 1, P),
+            "passes_per_s": round(1.0 / vt, 2), "ms_per_pass": round(vt * 1e3, 3),
+            "hbm_frac": round((wbytes + kv) / vt / 1e9 / HBM_PEAK_GBS, 4),
+            "decode_ms_same_ctx": round(dt_dec * 1e3, 3), "verify_over_decode": round(vt / dt_dec, 3),
+            "note": "per-pass wall time includes the host read of the accept count"}
+
+
+def bench_batch16(dpk, cfg, w, seed, flags, B=16, P=4096, N=32):
+    """Decode of 16 independent sequences, each with its own 4096-token KV
+    cache, one token per sequence per step: aggregate tok/s."""
+    import torch
+    import synth
+    dec = dpk.Decoder(cfg, w, max_batch=B, max_seq=P + N + 8, max_rows=P, flags=flags)
+    lg = dec.logits_buffer(B)
+    am = dec.argmax_buffer(B)
+    for b in range(B):
+        dec.prefill(b, [int(t) for t in synth.prompt_ids(cfg, P, seed, index=b)], lg[b:b + 1], am[b:b + 1])
+    seqs = list(range(B))
+    dec.decode_step(seqs, None, [P] * B, am, lg, ids_dev=am)  # warm-up
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s in range(N):
+        dec.decode_step(seqs, None, [P + 1 + s] * B, am, lg, ids_dev=am)
+    e1.record()
+    torch.cuda.synchronize()
+    dt = e0.elapsed_time(e1) / N / 1e3
+    dec.close()
+    H, L, d = cfg.hidden, cfg.n_layers, cfg.head_dim
+    wbytes = (cfg.n_linear_params() + cfg.vocab * H) * 2.0
+    kv = B * (P + 1 + N / 2.0) * 2 * L * cfg.n_kv_heads * d * 2.0
+    return {"workload": "batched decode: %d sequences x %d-token KV caches, %d steps" % (B, P, N),
+            "tok_s": round(B / dt, 1), "ms_per_step": round(dt * 1e3, 3),
+            "hbm_frac": round((wbytes + kv) / dt / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,6 +176,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel profiled pass")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the verify (K=5 over 8192 tokens) and batch-16 decode measurements")
     ap.add_argument("--decode-path", choices=["auto", "multi"], default="auto",
                     help="auto: one persistent launch per decode step where the shapes allow it; "
                          "multi: one launch per kernel")
@@ -207,6 +285,19 @@ def main():
                             "unit": "TFLOP/s", "frac": round(achg / MFMA_PEAK_TFLOPS, 4), "traffic": None,
                             "flops_per_launch": g["flops"] / g["launches"], "avg_launch_us": round(avg_g * 1e6, 2)}
 
+    dec.close()
+    extra = {}
+    if not args.no_extra and args.workload == "q8b" and args.decode_steps is None:
+        flags = 2 if args.decode_path == "multi" else 0
+        torch.cuda.empty_cache()
+        log("[bench] verify K=5 over an 8192-token cache ...")
+        extra["verify"] = bench_verify(dpk, cfg, w, args.seed, flags)
+        log("[bench] verify: %s" % extra["verify"])
+        torch.cuda.empty_cache()
+        log("[bench] batch-16 decode over 4096-token caches ...")
+        extra["batch16"] = bench_batch16(dpk, cfg, w, args.seed, flags)
+        log("[bench] batch16: %s" % extra["batch16"])
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
@@ -242,7 +333,7 @@ def main():
         "kernels": kernels,
         "cpu_baseline": cpu,
     }
-    dec.close()
+    out.update(extra)
     print(json.dumps(out), flush=True)
 
 

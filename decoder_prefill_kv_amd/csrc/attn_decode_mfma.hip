@@ -31,19 +31,36 @@ DPK_DEV void split_f16(float x, _Float16& hi, _Float16& lo) {
   lo = (_Float16)(x - (float)hi);
 }
 
-template <int D>
+// the fp16 of positions p + e >= c1 zeroed (a group of 4 from position p)
+DPK_DEV u32x2 vmask(u32x2 v, int p, int c1) {
+  const int n = c1 - p;
+  const uint32_t m0 = n >= 2 ? 0xffffffffu : (n == 1 ? 0x0000ffffu : 0u);
+  const uint32_t m1 = n >= 4 ? 0xffffffffu : (n == 3 ? 0x0000ffffu : 0u);
+  return u32x2{v.x & m0, v.y & m1};
+}
+
+template <int D, bool RAW>
 __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArgs a) {
-  const int chunk_id = blockIdx.x, g = blockIdx.y, m = blockIdx.z;
-  const RowParam rp = a.rows_param[m];
-  const int ctx = rp.pos + 1;
+  const int chunk_id = blockIdx.x, g = blockIdx.y;
+  // rows m .. m + R - 1 (one sequence when R > 1); column c = r G + head
+  const int SH = a.share > 1 ? a.share : 1;
+  const int m = blockIdx.z * SH;
+  const int R = min(SH, a.M - m);
+  const int G = a.n_heads / a.n_kv;
+  const int RG = R * G;
+  RowParam rp = a.rows_param[m];
+  for (int r = 1; r < R; ++r) rp.pos = max(rp.pos, a.rows_param[m + r].pos);
+  const int ctx = rp.pos + 1;  // the group's longest context
   const int nch = (ctx + CHUNK - 1) / CHUNK;
   if (chunk_id >= nch) return;
-  const int G = a.n_heads / a.n_kv;
   const int c0 = chunk_id * CHUNK;
   const int c1 = min(ctx, c0 + CHUNK);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform over the wave
   const int r16 = lane & 15, j4 = lane >> 4;
   const int wp0 = c0 + 64 * wave;  // this wave's first position
+  // end of this lane's column (its row's context) inside the chunk
+  const int c1_col = (r16 < RG) ? min(a.rows_param[m + r16 / G].pos + 1, c1) : c1;
 
   __shared__ float qs[16][D];
   __shared__ float knew[D], vnew[D];
@@ -55,85 +72,111 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
 
   const _Float16* Kb = (const _Float16*)a.kv.base + kv_slab(a.kv, rp.seq, a.layer, 0, g);
   const _Float16* Vb = (const _Float16*)a.kv.base + kv_slab(a.kv, rp.seq, a.layer, 1, g);
-  const bool raw = a.qkv_raw != nullptr;
+  constexpr bool raw = RAW;  // a.qkv_raw != nullptr
   const bool own = raw && rp.pos >= c0 && rp.pos < c1;
 
-  // ---- cache loads first (independent of q): K fragments of 4 tiles x D/32
-  // k-steps, V^T fragments of D/16 channel tiles x 2 position steps
+  // ---- this workgroup's inputs other than the cache are loaded before it,
+  // so that waiting for them leaves the cache loads in flight (loads complete
+  // in issue order).  Not raw: q of the RG columns.  Raw: the row's projected
+  // heads that this wave normalises and rotates (query heads wave, wave + 4,
+  // ..., then the KV head's key when own), their gains, the rotation of the
+  // position and the new value; clamped indices, no branches.
+  constexpr int QPT = 16 * D / THREADS;
+  constexpr int HD = D / 2;
+  constexpr int NIT = (16 + 1 + 3) / 4;  // G + 1 <= 17 heads over 4 waves
+  const int nh = own ? G + 1 : G;
+  const int li = lane % HD;
+  float qv[QPT];
+  float xr[NIT][2], rc = 0.f, rsn = 0.f, vv = 0.f;
+  uint16_t gr[NIT][2];
+  if constexpr (!raw) {
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+      const int i = tid + j * THREADS, c = i / D, e = i % D, cc = min(c, RG - 1);
+      qv[j] = a.q[((size_t)(m + cc / G) * a.n_heads + g * G + cc % G) * D + e];  // columns >= RG: zeroed later
+    }
+  } else {
+    const float* src = a.qkv_raw + (size_t)m * a.ld_raw;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int h = min(wave + 4 * it, nh - 1);
+      const float* x = (h < G) ? src + (size_t)(g * G + h) * D : src + (size_t)(a.n_heads + g) * D;
+      xr[it][0] = x[li];
+      xr[it][1] = x[li + HD];
+      const uint16_t* gn = (h < G) ? a.qn : a.kn;
+      // no gain: read a valid dummy address (no branch), use 1
+      const uint16_t* gp = gn ? gn : (const uint16_t*)a.rope_cos;
+      gr[it][0] = gp[li];  // converted where used
+      gr[it][1] = gp[li + HD];
+    }
+    rc = a.rope_cos[(size_t)rp.pos * HD + li];
+    rsn = a.rope_sin[(size_t)rp.pos * HD + li];
+    vv = src[(size_t)(a.n_heads + a.n_kv + g) * D + tid % D];
+  }
+
+  // ---- cache loads (independent of q), unconditional: positions past the
+  // context read the last one's address (K rows are masked in S, V groups at
+  // the product).  K fragments of 4 tiles x D/32 k-steps, V^T fragments of
+  // D/16 channel tiles x 2 position steps.
   u32x4 kf[4][D / 32];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int p = wp0 + 16 * t + r16;
+    const int p = min(wp0 + 16 * t + r16, c1 - 1);
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-      kf[t][s] = u32x4{0u, 0u, 0u, 0u};
-      if (p < c1) kf[t][s] = *(const u32x4*)(Kb + (size_t)p * D + 32 * s + 8 * j4);
-    }
+    for (int s = 0; s < D / 32; ++s) kf[t][s] = *(const u32x4*)(Kb + (size_t)p * D + 32 * s + 8 * j4);
   }
-  // position slots of k-group j4 in step ps: 32 ps + {4 j4..+3, 16 + 4 j4..+3}
+  // position slots of k-group j4 in step ps: 32 ps + {4 j4..+3, 16 + 4 j4..+3};
+  // a 4-position group stays inside the slab row (max_seq % 64 == 0)
   u32x2 vf[D / 16][2][2];
+  const int vlast = (c1 - 1) & ~3;
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
     for (int ps = 0; ps < 2; ++ps)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int p = wp0 + 32 * ps + 16 * h + 4 * j4;
-        vf[dt][ps][h] = u32x2{0u, 0u};
-        // the 4-position group stays inside the slab row (max_seq % 64 == 0)
-        if (p < c1) {
-          vf[dt][ps][h] = *(const u32x2*)(Vb + (size_t)(dt * 16 + r16) * a.kv.max_seq + p);
-          if (p + 4 > c1) {  // positions past the context may hold any bits (0 * NaN)
-            f16x4 v4 = __builtin_bit_cast(f16x4, vf[dt][ps][h]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (p + e >= c1) v4[e] = (_Float16)0.f;
-            vf[dt][ps][h] = __builtin_bit_cast(u32x2, v4);
-          }
-        }
+        const int p = min(wp0 + 32 * ps + 16 * h + 4 * j4, vlast);
+        vf[dt][ps][h] = *(const u32x2*)(Vb + (size_t)(dt * 16 + r16) * a.kv.max_seq + p);
       }
+  const bool vfull = wp0 + 64 <= c1;  // no V group of this wave reaches past the context
 
   // ---- q (and in raw mode the new key/value) -> LDS
-  for (int i = tid; i < 16 * D; i += THREADS) (&qs[0][0])[i] = 0.f;
-  __syncthreads();
-  if (!raw) {
-    for (int i = tid; i < G * D; i += THREADS) {
-      const int h = i / D, e = i % D;
-      qs[h][e] = a.q[((size_t)m * a.n_heads + g * G + h) * D + e] * a.scale * LOG2E;
+  if constexpr (!raw) {
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+      const int i = tid + j * THREADS;
+      // (a multiply, not a select: a load used on one side of a select gets
+      // sunk past the cache loads and then waits for them)
+      (&qs[0][0])[i] = qv[j] * ((i / D < RG) ? a.scale * LOG2E : 0.f);
     }
   } else {
-    const float* src = a.qkv_raw + (size_t)m * a.ld_raw;
-    const int nh = own ? G + 1 : G;
-    for (int h = wave; h < nh; h += 4) {
-      const float* x = (h < G) ? src + (size_t)(g * G + h) * D : src + (size_t)(a.n_heads + g) * D;
-      const uint16_t* gn = (h < G) ? a.qn : a.kn;
-      float ss = 0.f;
-      for (int e = lane; e < D; e += 64) ss += x[e] * x[e];
+    for (int i = G * D + tid; i < 16 * D; i += THREADS) (&qs[0][0])[i] = 0.f;  // unused columns
+    const bool qk = a.qn != nullptr;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int h = wave + 4 * it;
+      if (h >= nh) break;
+      const bool on = lane < HD;
+      float ss = on ? xr[it][0] * xr[it][0] + xr[it][1] * xr[it][1] : 0.f;
       ss = wave_sum(ss);
-      const float r = gn ? rsqrtf(ss / (float)D + a.eps) : 1.0f;
-      for (int i = lane; i < D / 2; i += 64) {
-        float x1 = x[i] * r, x2 = x[i + D / 2] * r;
-        if (gn) {
-          x1 *= bf16_to_f32(gn[i]);
-          x2 *= bf16_to_f32(gn[i + D / 2]);
-        }
-        const float cs = a.rope_cos[(size_t)rp.pos * (D / 2) + i], sn = a.rope_sin[(size_t)rp.pos * (D / 2) + i];
-        const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
+      const bool normed = (h < G) ? qk : (a.kn != nullptr);
+      const float r = normed ? rsqrtf(ss / (float)D + a.eps) : 1.0f;
+      if (on) {
+        const float g0 = normed ? bf16_to_f32(gr[it][0]) : 1.0f, g1 = normed ? bf16_to_f32(gr[it][1]) : 1.0f;
+        const float x1 = xr[it][0] * r * g0, x2 = xr[it][1] * r * g1;
+        const float y1 = x1 * rc - x2 * rsn, y2 = x2 * rc + x1 * rsn;
         if (h < G) {
-          qs[h][i] = y1 * a.scale * LOG2E;
-          qs[h][i + D / 2] = y2 * a.scale * LOG2E;
+          qs[h][lane] = y1 * a.scale * LOG2E;
+          qs[h][lane + HD] = y2 * a.scale * LOG2E;
         } else {
-          knew[i] = y1;
-          knew[i + D / 2] = y2;
+          knew[lane] = y1;
+          knew[lane + HD] = y2;
         }
       }
     }
-    if (own) {
-      const float* vsrc = src + (size_t)(a.n_heads + a.n_kv + g) * D;
-      for (int e = tid; e < D; e += THREADS) vnew[e] = vsrc[e];
-    }
+    if (own && tid < D) vnew[tid] = vv;
   }
-  __syncthreads();
+  lds_barrier();  // an LDS-only barrier: the cache loads stay in flight
   if (own) {
     for (int e = tid; e < D; e += THREADS) {
       kv_store(a.kv, kv_offset(a.kv, rp.seq, a.layer, 0, g, e, rp.pos), knew[e]);
@@ -200,7 +243,7 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      if (wp0 + 16 * t + 4 * j4 + v >= c1) sc[t][v] = -INFINITY;
+      if (wp0 + 16 * t + 4 * j4 + v >= c1_col) sc[t][v] = -INFINITY;
       mx = fmaxf(mx, sc[t][v]);
     }
   mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
@@ -236,7 +279,12 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
     }
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      const u32x4 w = {vf[dt][ps][0].x, vf[dt][ps][0].y, vf[dt][ps][1].x, vf[dt][ps][1].y};
+      u32x2 v0 = vf[dt][ps][0], v1 = vf[dt][ps][1];
+      if (!vfull) {  // positions past the context may hold any bits (0 * NaN)
+        v0 = vmask(v0, wp0 + 32 * ps + 4 * j4, c1);
+        v1 = vmask(v1, wp0 + 32 * ps + 16 + 4 * j4, c1);
+      }
+      const u32x4 w = {v0.x, v0.y, v1.x, v1.y};
       const f16x8 A = __builtin_bit_cast(f16x8, w);
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, ph, o[dt], 0, 0, 0);
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pl, o[dt], 0, 0, 0);
@@ -256,8 +304,9 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
   // chunk statistics per column c: M = max_w m_w, L = sum_w 2^(m_w - M) l_w,
   // O = sum_w 2^(m_w - M) O_w
   const int rec = D + 2;
-  for (int i = tid; i < G * D; i += THREADS) {
+  for (int i = tid; i < RG * D; i += THREADS) {
     const int c = i / D, e = i % D;
+    const size_t mh = (size_t)(m + c / G) * a.n_heads + g * G + c % G;  // (row, head)
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < 4; ++w) M = fmaxf(M, wst[w][0][c]);
@@ -268,10 +317,10 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
       L += f * wst[w][1][c];
       O += f * ow[w][e][c];
     }
-    if (nch == 1) {
-      a.out[(size_t)m * a.n_heads * D + (size_t)(g * G + c) * D + e] = O / L;
+    if (nch == 1 && !a.merge) {
+      a.out[mh * D + e] = O / L;
     } else {
-      float* r = a.part + (((size_t)m * a.n_heads + g * G + c) * a.max_chunks + chunk_id) * rec;
+      float* r = a.part + (mh * a.max_chunks + chunk_id) * rec;
       coh_store(r + 2 + e, O);
       if (e == 0) {
         coh_store(r, M);
@@ -279,16 +328,20 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
       }
     }
   }
-  if (nch == 1) return;
-  if (!last_block_arrive(a.counters + m * a.n_kv + g, nch, &flag)) return;
-  for (int i = tid; i < G * nch; i += THREADS) {
-    const int h = i % G, c = i / G;
-    const float* base = a.part + ((((size_t)m * a.n_heads + g * G + h) * a.max_chunks) + c) * rec;
-    ml[0][c][h] = coh_load(base);
-    ml[1][c][h] = coh_load(base + 1);
+  if (nch == 1 || a.merge) return;
+  if (!last_block_arrive(a.counters + blockIdx.z * a.n_kv + g, nch, &flag)) return;
+  // the other workgroups' partials: device-coherent plain loads (batched,
+  // unlike atomic loads, which wait for themselves one by one)
+  const coh_buf pb = coh_buffer(a.part);
+  for (int i = tid; i < RG * nch; i += THREADS) {
+    const int h = i % RG, c = i / RG;  // h: column
+    const size_t mh = (size_t)(m + h / G) * a.n_heads + g * G + h % G;
+    const uint32_t base = (uint32_t)((mh * a.max_chunks + c) * rec);
+    ml[0][c][h] = cload(pb, base);
+    ml[1][c][h] = cload(pb, base + 1);
   }
   __syncthreads();
-  if (tid < G) {
+  if (tid < RG) {
     const int h = tid;
     float M = -INFINITY;
     for (int c = 0; c < nch; ++c) M = fmaxf(M, ml[0][c][h]);
@@ -302,18 +355,69 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
     for (int c = 0; c < nch; ++c) mw[c][h] *= inv;
   }
   __syncthreads();
-  for (int i = tid; i < G * D; i += THREADS) {
+  for (int i = tid; i < RG * D; i += THREADS) {
     const int h = i / D, e = i % D;
-    const float* base = a.part + (((size_t)m * a.n_heads + g * G + h) * a.max_chunks) * rec + 2 + e;
+    const size_t mh = (size_t)(m + h / G) * a.n_heads + g * G + h % G;
+    const uint32_t base = (uint32_t)((mh * a.max_chunks) * rec + 2 + e);
     float O = 0.f;
     int c = 0;
-    for (; c + 4 <= nch; c += 4) {
-      const float o0 = coh_load(base + (size_t)c * rec), o1 = coh_load(base + (size_t)(c + 1) * rec);
-      const float o2 = coh_load(base + (size_t)(c + 2) * rec), o3 = coh_load(base + (size_t)(c + 3) * rec);
-      O += mw[c][h] * o0 + mw[c + 1][h] * o1 + mw[c + 2][h] * o2 + mw[c + 3][h] * o3;
+    for (; c + 8 <= nch; c += 8) {
+      float o[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) o[u] = cload(pb, base + (uint32_t)((c + u) * rec));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) O += mw[c + u][h] * o[u];
     }
-    for (; c < nch; ++c) O += mw[c][h] * coh_load(base + (size_t)c * rec);
-    a.out[(size_t)m * a.n_heads * D + (size_t)(g * G + h) * D + e] = O;
+    for (; c < nch; ++c) O += mw[c][h] * cload(pb, base + (uint32_t)(c * rec));
+    a.out[mh * D + e] = O;
+  }
+}
+
+// Log-sum-exp merge of the chunk partials [M][n_heads][max_chunks][D + 2]
+// (max, sum, O[D]); grid (n_heads, M), one thread per channel, the chunks
+// taken 16 at a time with a running maximum.  A row uses the chunks that hold
+// its own positions (later chunks of its row group hold nothing of it).
+template <int D>
+__global__ __launch_bounds__(D) void attn_merge_kernel(AttnDecodeArgs a) {
+  constexpr int B = 16;
+  const int head = blockIdx.x, m = blockIdx.y, e = threadIdx.x;
+  const int nch = (a.rows_param[m].pos + 1 + CHUNK - 1) / CHUNK;
+  const int rec = D + 2;
+  const float* base = a.part + ((size_t)m * a.n_heads + head) * a.max_chunks * rec;
+  float mx = -INFINITY, den = 0.f, O = 0.f;
+  for (int c0 = 0; c0 < nch; c0 += B) {
+    float w[B], l[B], o[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {  // clamped, all issued before any use
+      const int c = min(c0 + u, nch - 1);
+      w[u] = base[(size_t)c * rec];
+      l[u] = base[(size_t)c * rec + 1];
+      o[u] = base[(size_t)c * rec + 2 + e];
+    }
+    float bm = mx;
+#pragma unroll
+    for (int u = 0; u < B; ++u)
+      if (c0 + u < nch) bm = fmaxf(bm, w[u]);
+    const float f0 = (mx == -INFINITY) ? 0.f : exp2f(mx - bm);
+    den *= f0;
+    O *= f0;
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const float f = (c0 + u >= nch || w[u] == -INFINITY) ? 0.f : exp2f(w[u] - bm);
+      den += f * l[u];
+      O += f * o[u];
+    }
+    mx = bm;
+  }
+  const float y = O / den;
+  const size_t oi = ((size_t)m * a.n_heads + head) * D + e;
+  if (a.out_hi) {
+    uint32_t h16, l16;
+    split_bf16(y, h16, l16);
+    a.out_hi[oi] = (uint16_t)h16;
+    a.out_lo[oi] = (uint16_t)l16;
+  } else {
+    a.out[oi] = y;
   }
 }
 
@@ -322,13 +426,25 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
 hipError_t launch_attn_decode_mfma(const AttnDecodeArgs& a, hipStream_t stream) {
   if (a.kv.is_f32 || a.n_heads % a.n_kv || a.n_heads / a.n_kv > 16 || a.max_chunks > MAXCH || a.kv.max_seq % 64)
     return hipErrorInvalidValue;
-  dim3 grid(a.max_chunks, a.n_kv, a.M);
-  if (a.d == 128)
-    launch(attn_decode_mfma_kernel<128>, grid, dim3(THREADS), 0, stream, a);
-  else if (a.d == 64)
-    launch(attn_decode_mfma_kernel<64>, grid, dim3(THREADS), 0, stream, a);
-  else
+  const int sh = a.share > 1 ? a.share : 1;
+  if (sh > 1 && (a.qkv_raw || sh * (a.n_heads / a.n_kv) > 16)) return hipErrorInvalidValue;
+  dim3 grid(a.max_chunks, a.n_kv, (a.M + sh - 1) / sh);
+  const bool raw = a.qkv_raw != nullptr;
+  if (a.d == 128) {
+    if (raw)
+      launch(attn_decode_mfma_kernel<128, true>, grid, dim3(THREADS), 0, stream, a);
+    else
+      launch(attn_decode_mfma_kernel<128, false>, grid, dim3(THREADS), 0, stream, a);
+    if (a.merge) launch(attn_merge_kernel<128>, dim3(a.n_heads, a.M), dim3(128), 0, stream, a);
+  } else if (a.d == 64) {
+    if (raw)
+      launch(attn_decode_mfma_kernel<64, true>, grid, dim3(THREADS), 0, stream, a);
+    else
+      launch(attn_decode_mfma_kernel<64, false>, grid, dim3(THREADS), 0, stream, a);
+    if (a.merge) launch(attn_merge_kernel<64>, dim3(a.n_heads, a.M), dim3(64), 0, stream, a);
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

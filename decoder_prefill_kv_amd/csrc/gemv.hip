@@ -14,6 +14,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(GemvArgs a) {
   gemv_detail::gemv_body<FMT, T, WAVES, false>(a, a.M, lds, blockIdx.x, gridDim.x, [](auto&& issue) { issue(); });
 }
 
+// bf16 weights with ready-made bf16 hi / lo activation rows (any M <= 16)
+template <int T, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemv_xg_kernel(GemvArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  gemv_detail::gemv_body<W_BF16, T, WAVES, false, true>(a, a.M, lds, blockIdx.x, gridDim.x,
+                                                        [](auto&& issue) { issue(); });
+}
+
 // ---- load-time re-tiling into fragment order
 __global__ void tile_bf16_kernel(const uint16_t* src, uint16_t* dst, int N, int K) {
   // dst block (rt, s) = 64 lanes x 8 elements: lane l -> row 16 rt + l%16,
@@ -70,11 +78,30 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
   if (rows % RB || (a.swiglu && a.tiles < 2)) return hipErrorInvalidValue;
   for (int i = 0; i < 3; ++i)
     if (a.seg_rows[i] % 16) return hipErrorInvalidValue;
-  const size_t lds = gemv_lds_bytes(a.M, a.K, a.tiles, a.fmt);
-  if (lds > 64 * 1024) return hipErrorInvalidValue;
-  const int W = gemv_waves(a.K, a.tiles, a.fmt);
   const int n_tiles = rows / RB;
   dim3 grid(a.grid < n_tiles ? a.grid : n_tiles);
+  if (a.xb_hi) {
+    // 4 waves by default (measured a little faster than 8 at every layer
+    // shape); each wave's K part must hold whole 128-column iterations
+    const int W = a.waves ? a.waves : 4;
+    if ((W != 4 && W != 8) || a.K % (W * 128)) return hipErrorInvalidValue;
+    if (a.fmt != W_BF16 || !a.xb_lo || a.ldxb < a.K) return hipErrorInvalidValue;
+    const size_t lds_xg = (size_t)W * a.M * RB * 4 + (64 + 16 * W) * 4;
+#define DPK_GEMV_XG_CASE(T, WV)                                                  \
+  if (a.tiles == T && W == WV) {                                               \
+    launch((gemv_xg_kernel<T, WV>), grid, dim3(64 * WV), lds_xg, stream, a);   \
+    return hipGetLastError();                                                  \
+  }
+    DPK_GEMV_XG_CASE(1, 4)
+    DPK_GEMV_XG_CASE(2, 4)
+    DPK_GEMV_XG_CASE(1, 8)
+    DPK_GEMV_XG_CASE(2, 8)
+#undef DPK_GEMV_XG_CASE
+    return hipErrorInvalidValue;
+  }
+  const int W = gemv_waves(a.K, a.tiles, a.fmt);
+  const size_t lds = gemv_lds_bytes(a.M, a.K, a.tiles, a.fmt);
+  if (lds > 64 * 1024) return hipErrorInvalidValue;
 #define DPK_GEMV_CASE(F, T, WV)                                                            \
   if (a.fmt == F && a.tiles == T && W == WV) {                                            \
     launch((gemv_kernel<F, T, WV>), grid, dim3(64 * WV), lds, stream, a);    \

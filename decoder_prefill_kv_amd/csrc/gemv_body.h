@@ -56,8 +56,13 @@ __host__ __device__ inline int gemv_lds_layout(int M, int K, int RB, int fmt, in
 // accessed with device-coherent loads / stores, for a producer or consumer in
 // the same launch.  Barriers inside are LDS-only (lds_barrier), so weight
 // loads in flight are never drained by them.
-template <int FMT, int T, int WAVES, bool COH, typename Pre>
+//
+// XG: the activations come ready-made from global memory as bf16 hi / lo
+// rows (a.xb_hi / a.xb_lo, row stride a.ldxb, norm and gain already applied)
+// instead of being staged in LDS, so M is not limited by LDS (bf16 weights).
+template <int FMT, int T, int WAVES, bool COH, bool XG = false, typename Pre>
 DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const int wg, const int nwg, Pre&& pre) {
+  static_assert(!XG || FMT == W_BF16, "ready-made activations are for bf16 weights");
   constexpr int RB = 16 * T;
   constexpr int THREADS = 64 * WAVES;
   const int K = a.K;                      // columns this call reduces over
@@ -65,7 +70,12 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
   const int KO = a.kofs;                  // first column of this call
   const int kq = K / WAVES, xstride = kq + 8, ng = K / 64;
   int xs_off, xsum_off, red_off, misc_off;
-  gemv_lds_layout(M, K, RB, FMT, WAVES, &xs_off, &xsum_off, &red_off, &misc_off);
+  if constexpr (XG) {  // no staged x: red and misc only
+    xs_off = xsum_off = red_off = 0;
+    misc_off = WAVES * M * RB * 4;
+  } else {
+    gemv_lds_layout(M, K, RB, FMT, WAVES, &xs_off, &xsum_off, &red_off, &misc_off);
+  }
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   uint16_t* xs_hi = (uint16_t*)(lds + xs_off) + (size_t)wave * 2 * M * xstride;
   uint16_t* xs_lo = xs_hi + M * xstride;
@@ -94,7 +104,9 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
     return (size_t)rt;
   };
 
-  constexpr int U = 8 / T;                   // bf16: k-steps of 32 per iteration
+  // bf16: k-steps of 32 per iteration (XG holds its activations in registers
+  // as well, so a one-tile XG wave loads half as much per iteration)
+  constexpr int U = (XG && T == 1) ? 4 : 8 / T;
   constexpr int GU = 4 / T > 0 ? 4 / T : 1;  // 4-bit: groups of 64 per iteration
   const int nit = (FMT == W_BF16) ? kq / (32 * U) : kq / (64 * GU);
   const unsigned char* wp[T];   // this wave's stream inside each 16-row tile
@@ -117,12 +129,26 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
   u32x4 b0[T][U], b1[T][U];
   u32x2 c0[T][GU], c1[T][GU];
   u32x4 s0[T][GU], s1[T][GU];
-  auto load_bf = [&](u32x4 (&b)[T][U], int it) {
+  // XG: each iteration's activation fragments are loaded with its weights, so
+  // one wait covers both and the next iteration's loads stay in flight.  Rows
+  // past M read row M - 1 (their results are never stored).
+  constexpr int UX = XG ? U : 1;
+  u32x4 xh0[UX], xl0[UX], xh1[UX], xl1[UX];
+  size_t xrow = 0;
+  if constexpr (XG) xrow = (size_t)(r16 < M ? r16 : M - 1) * a.ldxb + KO + k0 + 8 * j4;
+  auto load_bf = [&](u32x4 (&b)[T][U], u32x4 (&xh)[UX], u32x4 (&xl)[UX], int it) {
 #pragma unroll
     for (int t = 0; t < T; ++t)
 #pragma unroll
       for (int u = 0; u < U; ++u)
         b[t][u] = __builtin_nontemporal_load((const u32x4*)(wp[t] + (size_t)(it * U + u) * 1024));
+    if constexpr (XG) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        xh[u] = *(const u32x4*)(a.xb_hi + xrow + (it * U + u) * 32);
+        xl[u] = *(const u32x4*)(a.xb_lo + xrow + (it * U + u) * 32);
+      }
+    }
   };
   auto load_q4 = [&](u32x2 (&c)[T][GU], u32x4 (&sv)[T][GU], int it) {
 #pragma unroll
@@ -139,8 +165,8 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
   bool two = false;  // iterations 0 and 1 of the current tile are already loading
   auto first_loads = [&]() {
     if constexpr (FMT == W_BF16) {
-      load_bf(b0, 0);
-      if (nit > 1) load_bf(b1, 1);
+      load_bf(b0, xh0, xl0, 0);
+      if (nit > 1) load_bf(b1, xh1, xl1, 1);
     } else {
       load_q4(c0, s0, 0);
       if (nit > 1) load_q4(c1, s1, 1);
@@ -155,9 +181,17 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
   });
 
   // ---- row norm scales from the producer's per-tile sums of squares (each
-  // wave computes them itself, so no barrier separates them from x's loads)
+  // wave computes them itself, so no barrier separates them from x's loads;
+  // XG applies wave 0's copy to the reduced outputs)
   float* rsw = misc + 64 + 16 * wave;
-  if (a.sq_in) {
+  if (XG && a.sq_in) {  // rows spread over the waves, one shared copy
+    for (int m = wave; m < M; m += WAVES) {
+      float s = 0.f;
+      for (int b = lane; b < a.sq_nb; b += 64) s += a.sq_in[m * a.sq_nb + b];
+      s = wave_sum(s);
+      if (lane == 0) misc[64 + m] = rsqrtf(s / (float)KF + a.eps);
+    }
+  } else if (a.sq_in) {
     for (int m = 0; m < M; ++m) {
       float s = 0.f;
       for (int b = lane; b < a.sq_nb; b += 64)
@@ -166,6 +200,7 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
       if (lane == 0) rsw[m] = rsqrtf(s / (float)KF + a.eps);
     }
   }
+  if constexpr (!XG) {
   // ---- prologue: this wave's K part of x' -> bf16 hi/lo (once per workgroup)
   for (int i = lane; i < M * (kq / 8); i += 64) {
     const int m = i / (kq / 8);
@@ -218,13 +253,18 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
     }
   }
   lds_barrier();
+  }
 
-  auto compute_bf = [&](f32x4 (&acc)[T], const u32x4 (&b)[T][U], int it) {
+  auto compute_bf = [&](f32x4 (&acc)[T], const u32x4 (&b)[T][U], const u32x4 (&xh)[UX], const u32x4 (&xl)[UX],
+                        int it) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       u32x4 bh = {0u, 0u, 0u, 0u}, bl = {0u, 0u, 0u, 0u};
-      const int kl = (it * U + u) * 32 + 8 * j4;
-      if (col_on) {
+      if constexpr (XG) {
+        bh = xh[u];
+        bl = xl[u];
+      } else if (col_on) {
+        const int kl = (it * U + u) * 32 + 8 * j4;
         bh = *(const u32x4*)(xs_hi + r16 * xstride + kl);
         bl = *(const u32x4*)(xs_lo + r16 * xstride + kl);
       }
@@ -299,6 +339,8 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
       float v = red[i];
 #pragma unroll
       for (int w = 1; w < WAVES; ++w) v += red[w * M * RB + i];
+      if constexpr (XG)
+        if (a.sq_in) v *= misc[64 + i / RB];  // the row's norm scale
       red[i] = v;  // wave 0's slice holds the result (each i touched by one thread)
     }
     lds_barrier();
@@ -317,32 +359,44 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
       for (int i = tid; i < M * HR; i += THREADS) {
         const int m = i / HR, r = i % HR;
         const float y = silu(red[m * RB + r]) * red[m * RB + HR + r];
-        if constexpr (COH)
+        if (a.xo_hi) {  // the next GEMV's activations, bf16 hi / lo
+          uint32_t h16, l16;
+          split_bf16(y, h16, l16);
+          const size_t o = (size_t)m * a.ldxo + tile * HR + r;
+          a.xo_hi[o] = (uint16_t)h16;
+          a.xo_lo[o] = (uint16_t)l16;
+        } else if constexpr (COH)
           cstore(coh_buffer(a.out), (uint32_t)(m * a.ldo + tile * HR + r), y);
         else
           a.out[(size_t)m * a.ldo + tile * HR + r] = y;
       }
     } else if (a.epi == EPI_RESID) {
-      // h += y; per-tile sum of squares of the new h (the next kernel's norm)
-      for (int m = 0; m < M; ++m) {
+      // h += y over all rows at once; per-row sums of squares of the new h
+      // over the tile (the next kernel's norm) from the squares left in red
+      for (int i = tid; i < M * RB; i += THREADS) {
+        const int m = i / RB, n = tile * RB + i % RB;
+        const uint32_t hi = (uint32_t)(m * a.ldo + n);
+        const float h = (COH ? cload(coh_buffer(a.out), hi) : a.out[hi]) + red[i];
+        if constexpr (COH)
+          cstore(coh_buffer(a.out), hi, h);
+        else
+          a.out[hi] = h;
+        red[i] = h * h;
+        if (a.xo_hi) {  // h * gain as the next GEMV's bf16 hi / lo activations
+          uint32_t h16, l16;
+          split_bf16(a.xo_gain ? h * bf16_to_f32(a.xo_gain[n]) : h, h16, l16);
+          a.xo_hi[(size_t)m * a.ldxo + n] = (uint16_t)h16;
+          a.xo_lo[(size_t)m * a.ldxo + n] = (uint16_t)l16;
+        }
+      }
+      lds_barrier();
+      if (tid < M) {
         float sq = 0.f;
-        for (int r = tid; r < RB; r += THREADS) {
-          float* hp = a.out + (size_t)m * a.ldo + tile * RB + r;
-          const uint32_t hi = (uint32_t)(m * a.ldo + tile * RB + r);
-          const float h = (COH ? cload(coh_buffer(a.out), hi) : *hp) + red[m * RB + r];
-          if constexpr (COH)
-            cstore(coh_buffer(a.out), hi, h);
-          else
-            *hp = h;
-          sq += h * h;
-        }
-        sq = block_sum_lds(sq, misc + 16);
-        if (tid == 0) {
-          if constexpr (COH)
-            cstore(coh_buffer(a.sq_out), (uint32_t)(m * n_tiles + tile), sq);
-          else
-            a.sq_out[m * n_tiles + tile] = sq;
-        }
+        for (int r = 0; r < RB; ++r) sq += red[tid * RB + r];
+        if constexpr (COH)
+          cstore(coh_buffer(a.sq_out), (uint32_t)(tid * n_tiles + tile), sq);
+        else
+          a.sq_out[tid * n_tiles + tile] = sq;
       }
     } else if (a.epi == EPI_HEAD) {
       // logits; running (max, lowest index) per row for this workgroup
@@ -367,10 +421,10 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
     for (int t = 0; t < T; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (FMT == W_BF16) {
       for (int it = 0; it < nit; it += 2) {
-        if (it + 1 < nit && !(two && it == 0)) load_bf(b1, it + 1);
-        compute_bf(acc, b0, it);
-        if (it + 2 < nit) load_bf(b0, it + 2);
-        if (it + 1 < nit) compute_bf(acc, b1, it + 1);
+        if (it + 1 < nit && !(two && it == 0)) load_bf(b1, xh1, xl1, it + 1);
+        compute_bf(acc, b0, xh0, xl0, it);
+        if (it + 2 < nit) load_bf(b0, xh0, xl0, it + 2);
+        if (it + 1 < nit) compute_bf(acc, b1, xh1, xl1, it + 1);
       }
     } else {
       for (int it = 0; it < nit; it += 2) {

@@ -78,7 +78,15 @@ struct GemvArgs {
   int M, K, N;              // rows (<=16), input dim, output rows (per matrix for swiglu)
   int fmt, tiles, swiglu, epi;
   int grid;                 // workgroups (they loop over row tiles)
+  int waves;                // ready-made-activation mode: 4 or 8 waves per workgroup, 0: by K
   int kofs, kfull;          // reduce over columns [kofs, kofs + K) of rows of kfull (0: K) columns
+  const uint16_t* xb_hi;    // non-null: activations as bf16 hi / lo rows [M][ldxb] (bf16
+  const uint16_t* xb_lo;    //   weights; x is not read).  Any gain is already applied; with
+  int ldxb;                 //   sq_in the outputs are scaled by each row's rsqrt(mean + eps)
+  uint16_t* xo_hi;          // non-null (EPI_RESID / EPI_SWIGLU): also write the result as the
+  uint16_t* xo_lo;          //   next GEMV's bf16 hi / lo activations [M][ldxo], times
+  int ldxo;                 //   xo_gain[n] if given (RESID); SWIGLU then skips out
+  const uint16_t* xo_gain;
   const void* w[3];
   const void* sb[3];
   int seg_end[3];
@@ -120,6 +128,17 @@ struct AttnDecodeArgs {
   unsigned* counters;         // [M * n_kv]
   float* out;                 // [M][n_heads*d] fp32
   float scale;                // 1/sqrt(d)
+  // share (mfma kernel, 0 or 1: off): consecutive groups of `share` rows of one
+  // sequence (each its own position) run in one workgroup per chunk and KV
+  // head, their share * G query heads as the MFMA columns (share * G <= 16),
+  // so each chunk of the cache is read once per group; not with raw mode
+  int share;
+  // merge (mfma kernel): 1 = the chunks' partials are always written and a
+  // second launch (attn_merge_kernel) combines them, one thread per output
+  // element, instead of the last-arriving workgroup of each row and KV head
+  int merge;
+  uint16_t* out_hi;           // with merge: if non-null, the output goes here as bf16 hi / lo
+  uint16_t* out_lo;           //   rows [M][n_heads*d] (a GEMV's activations) instead of to out
   // raw mode (qkv_raw != null): q is taken from the raw projection
   // [M][ld_raw] (q heads, k heads, v heads) and gets QK-norm + RoPE here; the
   // workgroup whose chunk holds the row's position computes that position's
@@ -162,6 +181,10 @@ hipError_t launch_gemv_f32(int M, int N, int K, const float* W, const float* W2,
                            float* out, int ldo, int mode, hipStream_t stream);
 // argmax per row over [M][N] logits (lowest index on ties)
 hipError_t launch_argmax_rows(int M, int N, const float* logits, int ld, int* out, hipStream_t stream);
+// x'[m][k] = x[m][k] * rs[m] * g[k] as bf16 hi + lo rows [M][K]; rs[m] from the
+// sums of squares sq_in[m][0..nb) over K (null: 1), g bf16 [K] or null
+hipError_t launch_xprep(int M, int K, const float* x, int ldx, const float* sq_in, int nb, const uint16_t* g,
+                        float eps, uint16_t* hi, uint16_t* lo, hipStream_t stream);
 // residual add out += in
 hipError_t launch_add(int n, const float* in, float* out, hipStream_t stream);
 // bf16 -> fp16 / q4 -> fp16 weight conversion for the prefill GEMM operands

@@ -55,6 +55,39 @@ __global__ void embed_kernel(int H, int fmt, const void* table, const uint16_t* 
   }
 }
 
+// grid (M, ceil(K / 2048)), 256 threads x 8 elements
+__global__ void xprep_kernel(int K, const float* x, int ldx, const float* sq_in, int nb, const uint16_t* g, float eps,
+                             uint16_t* hi, uint16_t* lo) {
+  __shared__ float red[8];
+  const int m = blockIdx.x;
+  float rs = 1.0f;
+  if (sq_in) {
+    float s = 0.f;
+    for (int b = threadIdx.x; b < nb; b += blockDim.x) s += sq_in[(size_t)m * nb + b];
+    s = block_sum(s, red);
+    rs = rsqrtf(s / (float)K + eps);
+  }
+  const int k = (blockIdx.y * blockDim.x + threadIdx.x) * 8;
+  if (k >= K) return;
+  const float* xp = x + (size_t)m * ldx + k;
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    float v0 = xp[e] * rs, v1 = xp[e + 1] * rs;
+    if (g) {
+      v0 *= bf16_to_f32(g[k + e]);
+      v1 *= bf16_to_f32(g[k + e + 1]);
+    }
+    uint32_t h0, l0, h1, l1;
+    split_bf16(v0, h0, l0);
+    split_bf16(v1, h1, l1);
+    h[e / 2] = h0 | (h1 << 16);
+    l[e / 2] = l0 | (l1 << 16);
+  }
+  *(uint4*)(hi + (size_t)m * K + k) = make_uint4(h[0], h[1], h[2], h[3]);
+  *(uint4*)(lo + (size_t)m * K + k) = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
 __global__ void rmsnorm_rows_kernel(int H, const float* x, int ldx, const void* g, int g_is_f32, float eps,
                                     void* y, int y_is_f16, int ldy) {
   __shared__ float red[32];
@@ -266,6 +299,13 @@ hipError_t launch_gemv_f32(int M, int N, int K, const float* W, const float* W2,
 
 hipError_t launch_argmax_rows(int M, int N, const float* logits, int ld, int* out, hipStream_t stream) {
   launch(argmax_rows_kernel, dim3(M), dim3(1024), 0, stream, N, logits, ld, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_xprep(int M, int K, const float* x, int ldx, const float* sq_in, int nb, const uint16_t* g,
+                        float eps, uint16_t* hi, uint16_t* lo, hipStream_t stream) {
+  if (M < 1 || K % 8) return hipErrorInvalidValue;
+  launch(xprep_kernel, dim3(M, (K + 2047) / 2048), dim3(256), 0, stream, K, x, ldx, sq_in, nb, g, eps, hi, lo);
   return hipGetLastError();
 }
 

@@ -85,6 +85,9 @@ struct dpk_model {
   unsigned* mega_bar = nullptr;      // barrier words (in scratch)
   unsigned long long* mega_trace = nullptr;  // phase-time accumulators (in scratch)
   float* mega_qkv1 = nullptr;        // second K-half of the QKV projection [16][Nqkv]
+  // batch GEMV activations: two sets of bf16 (hi, lo) rows [16][xb_w]
+  uint16_t* xb[2][2] = {};
+  int xb_w = 0;
   int mega_G = 0;                    // query heads per KV head, 0: not available
   size_t mega_lds = 0;
   bool mega_table = false;           // table written for the loaded weights
@@ -121,7 +124,8 @@ size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 struct ScratchLayout {
   size_t rope_cos, rope_sin, rows, h, rs, qkv, y32, qbuf, attn_o, act, part, sink, sq, cand_val, cand_idx, attn_part,
       y16, q16, o16, act16, counters, attn_counters, err, argmax_sink, gemm_ws, gemm_counters, mega_layers, mega_bar,
-      mega_trace, mega_qkv1, total;
+      mega_trace, mega_qkv1, xb, total;
+  size_t xb_w;
   int rows_f32, attn_chunks_cap;
   size_t part_floats;
 };
@@ -186,6 +190,9 @@ ScratchLayout scratch_layout(const dpk_config& c) {
   L.mega_bar = take(MEGA_BAR_WORDS * 4);
   L.mega_trace = take(MEGA_TRACE_WORDS * 8);
   L.mega_qkv1 = take(f32 ? 0 : SKINNY_MAX * Nqkv * 4);
+  L.xb_w = H > Qd ? H : Qd;
+  if (I > L.xb_w) L.xb_w = I;
+  L.xb = take(f32 ? 0 : 4 * SKINNY_MAX * L.xb_w * 2);
   L.total = o;
   return L;
 }
@@ -229,12 +236,12 @@ size_t kv_bytes(const dpk_config& c) {
 enum KClass : int {
   K_GEMV_QKV, K_GEMV_O, K_GEMV_GATEUP, K_GEMV_DOWN, K_GEMV_HEAD, K_ATTN_DECODE, K_EMBED, K_GEMM_QKV, K_GEMM_O,
   K_GEMM_GATEUP, K_GEMM_DOWN, K_ATTN_PREFILL, K_QK_ROPE_KV, K_RMSNORM, K_GEMV_F32, K_DECODE_STEP, K_STEP_EMBED, K_STEP_QKV,
-  K_STEP_ATTN, K_STEP_O, K_STEP_GATEUP, K_STEP_DOWN, K_STEP_HEAD, K_OTHER, K_NCLASS
+  K_STEP_ATTN, K_STEP_O, K_STEP_GATEUP, K_STEP_DOWN, K_STEP_HEAD, K_XPREP, K_OTHER, K_NCLASS
 };
 const char* const kclass_name[K_NCLASS] = {
     "gemv.qkv", "gemv.o", "gemv.gate_up", "gemv.down", "gemv.head", "attn.decode", "embed", "gemm.qkv", "gemm.o",
     "gemm.gate_up", "gemm.down", "attn.prefill", "qk_rope_kv", "rmsnorm", "gemv.f32", "decode.step", "step.embed", "step.qkv",
-    "step.attn", "step.o", "step.gate_up", "step.down", "step.head", "other"};
+    "step.attn", "step.o", "step.gate_up", "step.down", "step.head", "xprep", "other"};
 
 // Start/stop events of the launches of one kernel class when profiling is on.
 struct ProfScope {
@@ -358,8 +365,13 @@ dpk_status skinny(dpk_model* md, int cls, int M, const float* x, int ldx, const 
   return DPK_OK;
 }
 
+// one_seq: the rows are positions of one sequence (not with qkv_raw); on the
+// fp16-cache kernel their query heads then share each chunk's cache reads.
+// out16: if non-null (fp16-cache kernel only), the output goes there as bf16
+// hi / lo rows instead of to out.
 dpk_status attn_decode(dpk_model* md, int M, int max_ctx, const float* q, float* out, int layer, hipStream_t st,
-                       double kv_positions, const float* qkv_raw = nullptr) {
+                       double kv_positions, const float* qkv_raw = nullptr, bool one_seq = false,
+                       uint16_t* const* out16 = nullptr) {
   const dpk_config& c = md->cfg;
   AttnDecodeArgs a{};
   a.M = M;
@@ -377,6 +389,14 @@ dpk_status attn_decode(dpk_model* md, int M, int max_ctx, const float* q, float*
   a.counters = md->attn_counters;
   a.out = out;
   a.scale = 1.0f / sqrtf((float)c.head_dim);
+  a.share = (one_seq && !qkv_raw && !md->kvd.is_f32) ? 16 / (c.n_heads / c.n_kv_heads) : 1;
+  if (a.share > M) a.share = M;
+  a.merge = a.max_chunks > 1 || out16;  // a second launch merges the chunks
+  if (out16) {
+    if (md->kvd.is_f32) return fail(DPK_EINVAL, "internal: split attention output needs the fp16 cache");
+    a.out_hi = out16[0];
+    a.out_lo = out16[1];
+  }
   if (qkv_raw) {
     const LayerW& L = md->layers[layer];
     a.qkv_raw = qkv_raw;
@@ -446,6 +466,108 @@ dpk_status gemv(dpk_model* md, int cls, int M, const float* x, int ldx, const fl
                2.0 * M * nrows * a.K);
   HIP_TRY(launch_gemv(a, st));
   return DPK_OK;
+}
+
+// One GEMV launch on ready-made bf16 hi / lo activations xin (row stride
+// ldxin; sq_in: per-row sums of squares whose norm scale the outputs take).
+// xout: where a RESID / SWIGLU epilogue also writes the next GEMV's
+// activations (times xo_gain for RESID).
+dpk_status gemv_xg(dpk_model* md, int cls, int M, uint16_t* const* xin, int ldxin, const float* sq_in, int sq_nb,
+                   const LinearW* segs, int nseg, int epi, bool swiglu, int tiles, float* out, int ldo,
+                   float* sq_out, int32_t* argmax, uint16_t* const* xout, int ldxout, const void* xo_gain,
+                   hipStream_t st) {
+  GemvArgs a = gemv_args(md, M, nullptr, 0, sq_in, sq_nb, nullptr, segs, nseg, epi, swiglu, tiles, out, ldo, sq_out,
+                         argmax);
+  a.xb_hi = xin[0];
+  a.xb_lo = xin[1];
+  a.ldxb = ldxin;
+  // up to two row tiles per compute unit all at once (the 4-wave workgroups
+  // fit two to a unit), else a persistent grid
+  const int n_tiles = (swiglu ? 2 * a.N : a.N) / (16 * tiles);
+  if (epi != EPI_HEAD && n_tiles > a.grid && n_tiles <= 2 * a.grid) a.grid = n_tiles;
+  if (xout) {
+    a.xo_hi = xout[0];
+    a.xo_lo = xout[1];
+    a.ldxo = ldxout;
+    a.xo_gain = (const uint16_t*)xo_gain;
+  }
+  const double nrows = swiglu ? 2.0 * a.N : (double)a.N;
+  const double outb = (xout ? 4.0 : 0.0) * M * a.N + (epi == EPI_SWIGLU && xout ? 0.0 : 4.0 * M * a.N);
+  ProfScope ps(md, st, cls, nrows * a.K * 2.0 + (double)M * a.K * 4 + outb, 2.0 * M * nrows * a.K);
+  HIP_TRY(launch_gemv(a, st));
+  return DPK_OK;
+}
+
+// Can M rows of this model run on the ready-made-activation GEMVs?
+bool batch_fits(const dpk_model* md, int M) {
+  const dpk_config& c = md->cfg;
+  if (md->fmt != DPK_FMT_BF16 || !md->xb[0][0] || M < 1 || M > SKINNY_MAX) return false;
+  for (int K : {c.hidden, c.n_heads * c.head_dim, c.intermediate})
+    if (K % 1024) return false;
+  return true;
+}
+
+// M rows (parameters in md->rows_dev; one_seq: consecutive positions of one
+// sequence, as in a verify pass, else distinct sequences with one new position
+// each) on the ready-made-activation GEMVs.  Each layer: QKV GEMV -> [QK-norm,
+// RoPE, KV write] -> attention (its chunk merge writing the O GEMV's bf16
+// hi / lo activations) -> O GEMV + residual
+// (writing norm-gained bf16 activations of the new h) -> gate/up GEMV + SwiGLU
+// (writing the down GEMV's activations) -> down GEMV + residual (writing the
+// next layer's QKV activations); the row norm scales are applied to the GEMV
+// outputs.  Then the lm_head on rows [head_r0, head_r0 + head_n).
+dpk_status forward_batch(dpk_model* md, int M, int max_ctx, const int32_t* ids_dev, int head_r0, int head_n,
+                         float* logits, int32_t* argmax, hipStream_t st, double kv_positions, bool one_seq) {
+  const dpk_config& c = md->cfg;
+  const int H = c.hidden, Qd = c.n_heads * c.head_dim, I = c.intermediate;
+  uint16_t* const* X0 = md->xb[0];
+  uint16_t* const* X1 = md->xb[1];
+  {
+    ProfScope ps(md, st, K_EMBED, (double)M * H * 6, 0);
+    HIP_TRY(launch_embed(M, H, W_BF16, md->embed.w, md->embed.sc, md->embed.bi, md->rows_dev, ids_dev, c.vocab,
+                         md->h, nullptr, c.rms_eps, md->err_flag, st, md->sq));
+  }
+  {
+    ProfScope ps(md, st, K_XPREP, (double)M * H * 8, 0);
+    HIP_TRY(launch_xprep(M, H, md->h, H, nullptr, 0, (const uint16_t*)md->layers[0].in_norm, c.rms_eps, X0[0], X0[1],
+                         st));
+  }
+  int sq_nb = 1;
+  dpk_status s;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const LayerW& L = md->layers[l];
+    LinearW qkv[3] = {L.q, L.k, L.v};
+    if ((s = gemv_xg(md, K_GEMV_QKV, M, X0, H, md->sq, sq_nb, qkv, 3, EPI_STORE, false, 1, md->qkv, md->Nqkv,
+                     nullptr, nullptr, nullptr, 0, nullptr, st)))
+      return s;
+    if (one_seq) {
+      {
+        ProfScope ps(md, st, K_QK_ROPE_KV, (double)M * md->Nqkv * 6, 0);
+        HIP_TRY(launch_qk_rope_kv(M, md->qkv, c.n_heads, c.n_kv_heads, c.head_dim, c.qk_norm, L.q_norm, L.k_norm, 0,
+                                  c.rms_eps, md->rope_cos, md->rope_sin, md->rows_dev, md->qbuf, 0, md->kvd, l, st));
+      }
+      if ((s = attn_decode(md, M, max_ctx, md->qbuf, md->attn_o, l, st, kv_positions, nullptr, true, X1))) return s;
+    } else if ((s = attn_decode(md, M, max_ctx, nullptr, md->attn_o, l, st, kv_positions, md->qkv, false, X1))) {
+      return s;
+    }
+    if ((s = gemv_xg(md, K_GEMV_O, M, X1, Qd, nullptr, 0, &L.o, 1, EPI_RESID, false, 1, md->h, H, md->sq, nullptr,
+                     X0, H, L.post_norm, st)))
+      return s;
+    sq_nb = H / 16;
+    LinearW gu[2] = {L.gate, L.up};
+    if ((s = gemv_xg(md, K_GEMV_GATEUP, M, X0, H, md->sq, sq_nb, gu, 2, EPI_SWIGLU, true, 2, md->act, I, nullptr,
+                     nullptr, X1, I, nullptr, st)))
+      return s;
+    const void* next_gain = l + 1 < c.n_layers ? md->layers[l + 1].in_norm : md->final_norm;
+    if ((s = gemv_xg(md, K_GEMV_DOWN, M, X1, I, nullptr, 0, &L.down, 1, EPI_RESID, false, 1, md->h, H, md->sq,
+                     nullptr, X0, H, next_gain, st)))
+      return s;
+  }
+  if (head_n <= 0) return DPK_OK;
+  uint16_t* xh[2] = {X0[0] + (size_t)head_r0 * H, X0[1] + (size_t)head_r0 * H};
+  float* dst = logits ? logits : md->sink;
+  return gemv_xg(md, K_GEMV_HEAD, head_n, xh, H, md->sq + (size_t)head_r0 * sq_nb, sq_nb, &md->head, 1, EPI_HEAD,
+                 false, 1, dst, c.vocab, nullptr, argmax, nullptr, 0, nullptr, st);
 }
 
 // Can a decode step of M rows run on the whole-K GEMV kernels?
@@ -654,7 +776,7 @@ dpk_status head(dpk_model* md, int rows, const float* x, const float* rs, const 
 // Rows whose parameters are already in md->rows_dev.  M <= 16, bf16 / q4
 // weights.  Writes logits/argmax for rows [head_r0, head_r0 + head_n).
 dpk_status forward_skinny(dpk_model* md, int M, int max_ctx, const int32_t* ids_dev, int head_r0, int head_n,
-                          float* logits, int32_t* argmax, hipStream_t st, double kv_positions) {
+                          float* logits, int32_t* argmax, hipStream_t st, double kv_positions, bool one_seq) {
   const dpk_config& c = md->cfg;
   const int H = c.hidden;
   {
@@ -667,7 +789,7 @@ dpk_status forward_skinny(dpk_model* md, int M, int max_ctx, const int32_t* ids_
     const LayerW& L = md->layers[l];
     LinearW qkv[3] = {L.q, L.k, L.v};
     if ((s = skinny(md, K_GEMV_QKV, M, md->h, H, md->rs, L.in_norm, qkv, 3, EPI_QKV, nullptr, 0, st, l))) return s;
-    if ((s = attn_decode(md, M, max_ctx, md->qbuf, md->attn_o, l, st, kv_positions))) return s;
+    if ((s = attn_decode(md, M, max_ctx, md->qbuf, md->attn_o, l, st, kv_positions, nullptr, one_seq))) return s;
     if ((s = skinny(md, K_GEMV_O, M, md->attn_o, c.n_heads * c.head_dim, nullptr, nullptr, &L.o, 1, EPI_RESID, md->h,
                     H, st)))
       return s;
@@ -801,11 +923,15 @@ dpk_status forward_f32(dpk_model* md, int M, int max_ctx, const int32_t* ids_dev
 // Rows already uploaded; pick the path by format and row count.
 // kv_positions: cached positions the attention must read (per distinct
 // sequence), for the profiler's byte count
+// one_seq: the rows are consecutive positions of one sequence, else distinct
+// sequences with one new position each.
 dpk_status forward_rows(dpk_model* md, int M, int max_ctx, const int32_t* ids_dev, int head_r0, int head_n,
-                        float* logits, int32_t* argmax, hipStream_t st, double kv_positions) {
+                        float* logits, int32_t* argmax, hipStream_t st, double kv_positions, bool one_seq) {
   if (md->fmt == DPK_FMT_F32)
     return forward_f32(md, M, max_ctx, ids_dev, head_r0, head_n, logits, argmax, st, kv_positions);
-  return forward_skinny(md, M, max_ctx, ids_dev, head_r0, head_n, logits, argmax, st, kv_positions);
+  if (batch_fits(md, M))
+    return forward_batch(md, M, max_ctx, ids_dev, head_r0, head_n, logits, argmax, st, kv_positions, one_seq);
+  return forward_skinny(md, M, max_ctx, ids_dev, head_r0, head_n, logits, argmax, st, kv_positions, one_seq);
 }
 
 int max_rows_for_path(const dpk_model* md) {
@@ -905,6 +1031,9 @@ dpk_status dpk_bind_workspace(dpk_model* md, void* kv, void* scratch, void* prep
   md->mega_bar = (unsigned*)(s + L.mega_bar);
   md->mega_trace = (unsigned long long*)(s + L.mega_trace);
   md->mega_qkv1 = (float*)(s + L.mega_qkv1);
+  md->xb_w = (int)L.xb_w;
+  for (int i = 0; i < 4; ++i)
+    md->xb[i / 2][i % 2] = L.total > L.xb ? (uint16_t*)(s + L.xb) + (size_t)i * SKINNY_MAX * L.xb_w : nullptr;
   md->mega_table = false;
   md->rows_f32 = L.rows_f32;
   md->attn_chunks_cap = L.attn_chunks_cap;
@@ -1072,7 +1201,7 @@ dpk_status dpk_prefill(dpk_model* md, int32_t seq, const int32_t* ids, int32_t n
     if (gemm_path && M > SKINNY_MAX)
       s = forward_gemm(md, M, r0, seq, last, logits, argmax, st);
     else
-      s = forward_rows(md, M, r0 + M, nullptr, M - 1, last ? 1 : 0, logits, argmax, st, r0 + M);
+      s = forward_rows(md, M, r0 + M, nullptr, M - 1, last ? 1 : 0, logits, argmax, st, r0 + M, true);
     if (s) return s;
   }
   md->seq_len[seq] = n;
@@ -1109,7 +1238,7 @@ dpk_status dpk_decode_step(dpk_model* md, int32_t batch, const int32_t* seqs, co
   else if (decode_fits(md, batch))
     s = forward_decode(md, batch, max_ctx, ids_dev, logits, argmax, st, kvpos);
   else
-    s = forward_rows(md, batch, max_ctx, ids_dev, 0, batch, logits, argmax, st, kvpos);
+    s = forward_rows(md, batch, max_ctx, ids_dev, 0, batch, logits, argmax, st, kvpos, false);
   if (s) return s;
   for (int b = 0; b < batch; ++b) md->seq_len[seqs[b]] = pos[b] + 1;
   return DPK_OK;
@@ -1132,7 +1261,7 @@ dpk_status dpk_verify(dpk_model* md, int32_t seq, const int32_t* ids, int32_t kp
   }
   hipStream_t st = (hipStream_t)stream;
   if ((s = upload_rows(md, rows, kp1, st))) return s;
-  if ((s = forward_rows(md, kp1, pos + kp1, nullptr, 0, kp1, logits, argmax, st, pos + kp1))) return s;
+  if ((s = forward_rows(md, kp1, pos + kp1, nullptr, 0, kp1, logits, argmax, st, pos + kp1, true))) return s;
   HIP_TRY(hipMemcpyAsync(md->acc_host, argmax, sizeof(int32_t) * kp1, hipMemcpyDeviceToHost, st));
   HIP_TRY(hipStreamSynchronize(st));
   int m = 0;

@@ -106,10 +106,21 @@ def test_prefill_without_outputs_then_decode(dpk):
     dec.close()
 
 
-def test_verify_matches_oracle(dpk):
-    cfg = synth.Q06B.with_(n_layers=2)
+VERIFY_CASES = [
+    # (id, config, prompt length, drafts K): one group of rows per KV head;
+    # 4-bit weights with two row groups; ready-made-activation GEMVs with two
+    # row groups across the 256-position chunk edge; 16 rows across 512
+    ("q06b-L2-k5", synth.Q06B.with_(n_layers=2), 33, 5),
+    ("q06b_q4-L2-k11", synth.Q06B_Q4.with_(n_layers=2), 300, 11),
+    ("q8b-L1-v4096-k5", synth.Q8B.with_(n_layers=1, vocab=4096), 254, 5),
+    ("q8b-L1-v4096-k15", synth.Q8B.with_(n_layers=1, vocab=4096), 500, 15),
+]
+
+
+@pytest.mark.parametrize("case", VERIFY_CASES, ids=[c[0] for c in VERIFY_CASES])
+def test_verify_matches_oracle(dpk, case):
+    _, cfg, P, K = case
     w = synth.make_weights(cfg, 0)
-    P, K = 33, 5
     prompt = synth.prompt_ids(cfg, P, 0)
     m, run = oracle_greedy(cfg, w, prompt, K + 1)
     g = run["ids"]
@@ -119,7 +130,7 @@ def test_verify_matches_oracle(dpk):
     c = m.new_cache(P + K + 1)
     m.forward_block(c, prompt, 0)
     ref = oracle.verify(m, c, ids_in, P)
-    dec = dpk.Decoder(cfg, w, max_batch=1, max_seq=P + K + 1, max_rows=64)
+    dec = dpk.Decoder(cfg, w, max_batch=1, max_seq=(P + K + 64) // 64 * 64, max_rows=512)
     lg = dec.logits_buffer(K + 1)
     am = dec.argmax_buffer(K + 1)
     dec.prefill(0, [int(t) for t in prompt])
@@ -127,6 +138,7 @@ def test_verify_matches_oracle(dpk):
     for i in range(K + 1):
         compare_logits(lg[i].cpu(), ref["logits"][i], TOL["bf16"], "verify row %d" % i)
     check_ids(am.cpu().tolist(), list(ref["logits"]), ref["argmax"], "verify")
+    dpk.check_device_errors(dec.handle)
     assert acc == ref["accepted"]
     assert dec.seq_length(0) == P + acc + 1
     dec.close()
