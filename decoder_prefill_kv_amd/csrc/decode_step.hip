@@ -233,13 +233,13 @@ DPK_DEV void attn_phase(const MegaArgs& a, int layer, const uint16_t* qn, const 
     const bool own = rp.pos >= c0 && rp.pos < c1;
 
     // ---- q heads (waves < G), the new key (wave G) and value (wave G + 1)
-    // raw projection = the two K-half partial sums
-    const coh_buf q0 = coh_buffer(a.qkv), q1 = coh_buffer(a.qkv1);
+    // from the raw projection
+    const coh_buf q0 = coh_buffer(a.qkv);
     const uint32_t row = (uint32_t)(m * a.ld_qkv);
     if (wave <= G && (wave < G || own)) {
       const uint32_t x = row + (uint32_t)((wave < G ? g * G + wave : a.n_heads + g) * D);
-      const float xa = cload(q0, x + lane) + cload(q1, x + lane);
-      const float xb = cload(q0, x + lane + 64) + cload(q1, x + lane + 64);
+      const float xa = cload(q0, x + lane);
+      const float xb = cload(q0, x + lane + 64);
       const bool norm = (wave < G ? qn : kn) != nullptr;
       const float ss = wave_sum(xa * xa + xb * xb);
       const float r = norm ? rsqrtf(ss / (float)D + a.eps) : 1.0f;
@@ -254,8 +254,8 @@ DPK_DEV void attn_phase(const MegaArgs& a, int layer, const uint16_t* qn, const 
       }
     } else if (wave == G + 1 && own) {
       const uint32_t v = row + (uint32_t)((a.n_heads + a.n_kv + g) * D);
-      vnew[lane] = cload(q0, v + lane) + cload(q1, v + lane);
-      vnew[lane + 64] = cload(q0, v + lane + 64) + cload(q1, v + lane + 64);
+      vnew[lane] = cload(q0, v + lane);
+      vnew[lane + 64] = cload(q0, v + lane + 64);
     }
     __syncthreads();
     if (own) {
@@ -469,10 +469,7 @@ __global__ __launch_bounds__(MT, 1) void decode_step_kernel(MegaArgs a) {
   embed_phase(a, wg, nwg);
   for (int l = 0; l < a.n_layers; ++l) {
     const MegaLayer& L = a.layers[l];
-    // QKV over the two halves of K; the second half rotates the workgroups so
-    // that the 1.5 row tiles per workgroup of each half add up evenly
-    gemv_body<W_BF16, 1, 8, true>(L.qkv[0], a.M, lds, wg, nwg, sync);
-    gemv_body<W_BF16, 1, 8, true>(L.qkv[1], a.M, lds, (wg + nwg / 2) % nwg, nwg, [](auto&& issue) { issue(); });
+    gemv_body<W_BF16, 1, 8, true>(L.qkv, a.M, lds, wg, nwg, sync);
     closing = MP_QKV;
     attn_phase<G>(a, l, L.qn, L.kn, lds, wg, nwg, sync);
     closing = MP_ATTN;

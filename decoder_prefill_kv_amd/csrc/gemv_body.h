@@ -179,6 +179,9 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
       first_loads();
     }
   });
+  // no row tile here: nothing to stage or finish (the head's argmax needs
+  // every workgroup's candidates, and it has more tiles than workgroups)
+  if (tile >= n_tiles && a.epi != EPI_HEAD) return;
 
   // ---- row norm scales from the producer's per-tile sums of squares (each
   // wave computes them itself, so no barrier separates them from x's loads;

@@ -231,7 +231,8 @@ hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t stream);
 // ---- whole decode step in one persistent (cooperative) launch, bf16 weights
 constexpr int MEGA_ATTN_MAXCH = 64;  // attention chunks per row (256 positions each)
 struct MegaLayer {                   // device-resident, one per layer
-  GemvArgs qkv[2];                   // the QKV projection over the two halves of K (partial sums)
+  GemvArgs qkv;                      // the QKV projection, whole K (1.5 row tiles per workgroup
+                                     //   measured faster than splits of K that balance the tiles)
   GemvArgs o, gu, down;              // M is set per launch
   const uint16_t* qn;                // QK-norm gains (bf16) or null
   const uint16_t* kn;
@@ -248,8 +249,7 @@ struct MegaArgs {
   int* err;                          // bit 0: token out of range
   int n_heads, n_kv;
   KVDesc kv;
-  const float* qkv;                  // [M][ld_qkv] raw projection, first half of K
-  const float* qkv1;                 // [M][ld_qkv] second half of K (q = qkv + qkv1)
+  const float* qkv;                  // [M][ld_qkv] raw projection
   int ld_qkv;
   const float* rope_cos;
   const float* rope_sin;

@@ -84,7 +84,6 @@ struct dpk_model {
   MegaLayer* mega_layers = nullptr;  // device table (in scratch)
   unsigned* mega_bar = nullptr;      // barrier words (in scratch)
   unsigned long long* mega_trace = nullptr;  // phase-time accumulators (in scratch)
-  float* mega_qkv1 = nullptr;        // second K-half of the QKV projection [16][Nqkv]
   // batch GEMV activations: two sets of bf16 (hi, lo) rows [16][xb_w]
   uint16_t* xb[2][2] = {};
   int xb_w = 0;
@@ -124,7 +123,7 @@ size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 struct ScratchLayout {
   size_t rope_cos, rope_sin, rows, h, rs, qkv, y32, qbuf, attn_o, act, part, sink, sq, cand_val, cand_idx, attn_part,
       y16, q16, o16, act16, counters, attn_counters, err, argmax_sink, gemm_ws, gemm_counters, mega_layers, mega_bar,
-      mega_trace, mega_qkv1, xb, total;
+      mega_trace, xb, total;
   size_t xb_w;
   int rows_f32, attn_chunks_cap;
   size_t part_floats;
@@ -189,7 +188,6 @@ ScratchLayout scratch_layout(const dpk_config& c) {
   L.mega_layers = take(f32 ? 0 : (size_t)c.n_layers * sizeof(MegaLayer));
   L.mega_bar = take(MEGA_BAR_WORDS * 4);
   L.mega_trace = take(MEGA_TRACE_WORDS * 8);
-  L.mega_qkv1 = take(f32 ? 0 : SKINNY_MAX * Nqkv * 4);
   L.xb_w = H > Qd ? H : Qd;
   if (I > L.xb_w) L.xb_w = I;
   L.xb = take(f32 ? 0 : 4 * SKINNY_MAX * L.xb_w * 2);
@@ -634,7 +632,7 @@ size_t mega_lds_for(dpk_model* md, int M, int max_ctx) {
   if (G != 1 && G != 2 && G != 4) return 0;
   if (!decode_fits(md, M)) return 0;
   const int H = c.hidden, Qd = c.n_heads * c.head_dim, I = c.intermediate;
-  if (H % 2048 || gemv_waves(H / 2, 1, W_BF16) != 8 || gemv_waves(H, 1, W_BF16) != 8 ||
+  if (gemv_waves(H, 1, W_BF16) != 8 ||
       gemv_waves(Qd, 1, W_BF16) != 8 || gemv_waves(H, 2, W_BF16) != 8 || gemv_waves(I, 1, W_BF16) != 8)
     return 0;
   if ((max_ctx + mega_attn_chunk() - 1) / mega_attn_chunk() > MEGA_ATTN_MAXCH) return 0;
@@ -656,14 +654,8 @@ dpk_status mega_table(dpk_model* md, hipStream_t st) {
     const LayerW& L = md->layers[l];
     LinearW qkv[3] = {L.q, L.k, L.v};
     LinearW gu[2] = {L.gate, L.up};
-    for (int hf = 0; hf < 2; ++hf) {
-      GemvArgs& q = t[l].qkv[hf];
-      q = gemv_args(md, 1, md->h, H, md->sq, H / 16, L.in_norm, qkv, 3, EPI_STORE, false, 1,
-                    hf ? md->mega_qkv1 : md->qkv, md->Nqkv, nullptr, nullptr);
-      q.K = H / 2;
-      q.kofs = hf * (H / 2);
-      q.kfull = H;
-    }
+    t[l].qkv = gemv_args(md, 1, md->h, H, md->sq, H / 16, L.in_norm, qkv, 3, EPI_STORE, false, 1, md->qkv, md->Nqkv,
+                         nullptr, nullptr);
     t[l].o = gemv_args(md, 1, md->attn_o, Qd, nullptr, 0, nullptr, &L.o, 1, EPI_RESID, false, 1, md->h, H, md->sq,
                        nullptr);
     t[l].gu = gemv_args(md, 1, md->h, H, md->sq, H / 16, L.post_norm, gu, 2, EPI_SWIGLU, true, 2, md->act, I, nullptr,
@@ -704,7 +696,6 @@ dpk_status forward_mega(dpk_model* md, int M, int max_ctx, size_t lds, const int
   a.n_kv = c.n_kv_heads;
   a.kv = md->kvd;
   a.qkv = md->qkv;
-  a.qkv1 = md->mega_qkv1;
   a.ld_qkv = md->Nqkv;
   a.rope_cos = md->rope_cos;
   a.rope_sin = md->rope_sin;
@@ -1030,7 +1021,6 @@ dpk_status dpk_bind_workspace(dpk_model* md, void* kv, void* scratch, void* prep
   md->mega_layers = L.mega_bar > L.mega_layers ? (MegaLayer*)(s + L.mega_layers) : nullptr;
   md->mega_bar = (unsigned*)(s + L.mega_bar);
   md->mega_trace = (unsigned long long*)(s + L.mega_trace);
-  md->mega_qkv1 = (float*)(s + L.mega_qkv1);
   md->xb_w = (int)L.xb_w;
   for (int i = 0; i < 4; ++i)
     md->xb[i / 2][i % 2] = L.total > L.xb ? (uint16_t*)(s + L.xb) + (size_t)i * SKINNY_MAX * L.xb_w : nullptr;
