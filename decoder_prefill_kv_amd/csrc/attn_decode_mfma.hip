@@ -31,12 +31,11 @@ DPK_DEV void split_f16(float x, _Float16& hi, _Float16& lo) {
   lo = (_Float16)(x - (float)hi);
 }
 
-// the fp16 of positions p + e >= c1 zeroed (a group of 4 from position p)
-DPK_DEV u32x2 vmask(u32x2 v, int p, int c1) {
+// the fp16 of positions p + e >= c1 zeroed (a group of 8 from position p)
+DPK_DEV u32x4 vmask(u32x4 v, int p, int c1) {
   const int n = c1 - p;
-  const uint32_t m0 = n >= 2 ? 0xffffffffu : (n == 1 ? 0x0000ffffu : 0u);
-  const uint32_t m1 = n >= 4 ? 0xffffffffu : (n == 3 ? 0x0000ffffu : 0u);
-  return u32x2{v.x & m0, v.y & m1};
+  auto m = [n](int e) { return n >= e + 2 ? 0xffffffffu : (n == e + 1 ? 0x0000ffffu : 0u); };
+  return u32x4{v.x & m(0), v.y & m(2), v.z & m(4), v.w & m(6)};
 }
 
 template <int D, bool RAW>
@@ -118,26 +117,29 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
   // context read the last one's address (K rows are masked in S, V groups at
   // the product).  K fragments of 4 tiles x D/32 k-steps, V^T fragments of
   // D/16 channel tiles x 2 position steps.
+  // Row r of K tile t is position kpos(t, r) = 32 (t / 2) + 8 (r / 4) + 4 (t % 2)
+  // + r % 4 of the wave's 64: the S accumulators of tiles 2 ps and 2 ps + 1 then
+  // give lane group j4 the positions 32 ps + 8 j4 .. + 7, which is the k range
+  // of P^T that lane group takes in the P V product, so V^T is read as one
+  // contiguous 8-position (16-byte) group per lane.
   u32x4 kf[4][D / 32];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int p = min(wp0 + 16 * t + r16, c1 - 1);
+    const int p = min(wp0 + 32 * (t >> 1) + 8 * (r16 >> 2) + 4 * (t & 1) + (r16 & 3), c1 - 1);
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) kf[t][s] = *(const u32x4*)(Kb + (size_t)p * D + 32 * s + 8 * j4);
   }
-  // position slots of k-group j4 in step ps: 32 ps + {4 j4..+3, 16 + 4 j4..+3};
-  // a 4-position group stays inside the slab row (max_seq % 64 == 0)
-  u32x2 vf[D / 16][2][2];
-  const int vlast = (c1 - 1) & ~3;
+  // V^T: channel row dt * 16 + r16, positions 32 ps + 8 j4 .. + 7 (an 8-position
+  // group stays inside the slab row: max_seq % 64 == 0)
+  u32x4 vf[D / 16][2];
+  const int vlast = (c1 - 1) & ~7;
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
-    for (int ps = 0; ps < 2; ++ps)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int p = min(wp0 + 32 * ps + 16 * h + 4 * j4, vlast);
-        vf[dt][ps][h] = *(const u32x2*)(Vb + (size_t)(dt * 16 + r16) * a.kv.max_seq + p);
-      }
+    for (int ps = 0; ps < 2; ++ps) {
+      const int p = min(wp0 + 32 * ps + 8 * j4, vlast);
+      vf[dt][ps] = *(const u32x4*)(Vb + (size_t)(dt * 16 + r16) * a.kv.max_seq + p);
+    }
   const bool vfull = wp0 + 64 <= c1;  // no V group of this wave reaches past the context
 
   // ---- q (and in raw mode the new key/value) -> LDS
@@ -186,9 +188,10 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
     const int off = rp.pos - wp0;
     if (off >= 0 && off < 64) {
       // compile-time fragment indices only (runtime ones would spill the arrays)
+      const int kt = 2 * (off / 32) + (off % 8) / 4, kr = 4 * ((off % 32) / 8) + off % 4;  // kpos^-1
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        if (t == off / 16 && r16 == off % 16) {
+        if (t == kt && r16 == kr) {
 #pragma unroll
           for (int s = 0; s < D / 32; ++s) {
             f16x8 k8;
@@ -197,21 +200,19 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
             kf[t][s] = __builtin_bit_cast(u32x4, k8);
           }
         }
-      const int e4 = off % 4;
+      const int e8 = off % 8;
 #pragma unroll
       for (int ps = 0; ps < 2; ++ps)
+        if (ps == off / 32 && j4 == (off % 32) / 8) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-          if (ps == off / 32 && h == (off % 32) / 16 && j4 == (off % 16) / 4) {
+          for (int dt = 0; dt < D / 16; ++dt) {
+            f16x8 v8 = __builtin_bit_cast(f16x8, vf[dt][ps]);
 #pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt) {
-              f16x4 v4 = __builtin_bit_cast(f16x4, vf[dt][ps][h]);
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (e == e4) v4[e] = (_Float16)vnew[dt * 16 + r16];
-              vf[dt][ps][h] = __builtin_bit_cast(u32x2, v4);
-            }
+            for (int e = 0; e < 8; ++e)
+              if (e == e8) v8[e] = (_Float16)vnew[dt * 16 + r16];
+            vf[dt][ps] = __builtin_bit_cast(u32x4, v8);
           }
+        }
     }
   }
 
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      if (wp0 + 16 * t + 4 * j4 + v >= c1_col) sc[t][v] = -INFINITY;
+      if (wp0 + 32 * (t >> 1) + 8 * j4 + 4 * (t & 1) + v >= c1_col) sc[t][v] = -INFINITY;
       mx = fmaxf(mx, sc[t][v]);
     }
   mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
@@ -279,12 +280,8 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
     }
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      u32x2 v0 = vf[dt][ps][0], v1 = vf[dt][ps][1];
-      if (!vfull) {  // positions past the context may hold any bits (0 * NaN)
-        v0 = vmask(v0, wp0 + 32 * ps + 4 * j4, c1);
-        v1 = vmask(v1, wp0 + 32 * ps + 16 + 4 * j4, c1);
-      }
-      const u32x4 w = {v0.x, v0.y, v1.x, v1.y};
+      u32x4 w = vf[dt][ps];
+      if (!vfull) w = vmask(w, wp0 + 32 * ps + 8 * j4, c1);  // past the context: any bits (0 * NaN)
       const f16x8 A = __builtin_bit_cast(f16x8, w);
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, ph, o[dt], 0, 0, 0);
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pl, o[dt], 0, 0, 0);
