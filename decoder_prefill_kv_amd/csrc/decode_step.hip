@@ -165,8 +165,11 @@ DPK_DEV void attn_phase(const MegaArgs& a, int layer, const uint16_t* qn, const 
   const int n_items = a.M * a.n_kv * a.max_chunks;
   const int rec = D + 2;
 
+  // K tile t row r is position 8 (r / 4) + 4 t + r % 4 of the wave's 32, so the
+  // S accumulators give lane group j4 positions 8 j4 .. + 7 (its k range of P^T
+  // in the P V product) and V^T is read as one 8-position group per lane
   u32x4 kf[2][D / 32];
-  u32x2 vf[D / 16][2];
+  u32x4 vf[D / 16];
   float cs = 0.f, sn = 0.f, g0 = 1.f, g1 = 1.f;  // this wave's RoPE and gain values
 
   // K / V^T fragments of the item's positions for this wave, and the RoPE /
@@ -179,33 +182,19 @@ DPK_DEV void attn_phase(const MegaArgs& a, int layer, const uint16_t* qn, const 
     const int wp0 = c0 + 32 * wave;
     const _Float16* Kb = (const _Float16*)a.kv.base + kv_slab(a.kv, rp.seq, layer, 0, g);
     const _Float16* Vb = (const _Float16*)a.kv.base + kv_slab(a.kv, rp.seq, layer, 1, g);
+    // unconditional loads: positions past the context read the last one's
+    // address (K rows are masked in S, V groups where they are used); an
+    // 8-position group stays inside the slab row (max_seq % 64 == 0)
+    const int plast = max(c1 - 1, 0);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int p = wp0 + 16 * t + r16;
+      const int p = min(wp0 + 8 * (r16 >> 2) + 4 * t + (r16 & 3), plast);
 #pragma unroll
-      for (int s = 0; s < D / 32; ++s) {
-        kf[t][s] = u32x4{0u, 0u, 0u, 0u};
-        if (p < c1) kf[t][s] = *(const u32x4*)(Kb + (size_t)p * D + 32 * s + 8 * j4);
-      }
+      for (int s = 0; s < D / 32; ++s) kf[t][s] = *(const u32x4*)(Kb + (size_t)p * D + 32 * s + 8 * j4);
     }
+    const int p8 = min(wp0 + 8 * j4, plast & ~7);
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int p = wp0 + 16 * h + 4 * j4;
-        vf[dt][h] = u32x2{0u, 0u};
-        // the 4-position group stays inside the slab row (max_seq % 64 == 0)
-        if (p < c1) {
-          vf[dt][h] = *(const u32x2*)(Vb + (size_t)(dt * 16 + r16) * a.kv.max_seq + p);
-          if (p + 4 > c1) {  // positions past the context may hold any bits (0 * NaN)
-            f16x4 v4 = __builtin_bit_cast(f16x4, vf[dt][h]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (p + e >= c1) v4[e] = (_Float16)0.f;
-            vf[dt][h] = __builtin_bit_cast(u32x2, v4);
-          }
-        }
-      }
+    for (int dt = 0; dt < D / 16; ++dt) vf[dt] = *(const u32x4*)(Vb + (size_t)(dt * 16 + r16) * a.kv.max_seq + p8);
     if (wave <= G) {
       cs = a.rope_cos[(size_t)rp.pos * (D / 2) + lane];
       sn = a.rope_sin[(size_t)rp.pos * (D / 2) + lane];
@@ -267,9 +256,10 @@ DPK_DEV void attn_phase(const MegaArgs& a, int layer, const uint16_t* qn, const 
       const int off = rp.pos - wp0;
       if (off >= 0 && off < 32) {
         // compile-time fragment indices only (runtime ones would spill the arrays)
+        const int kt = (off % 8) / 4, kr = 4 * (off / 8) + off % 4;  // the row holding position off
 #pragma unroll
         for (int t = 0; t < 2; ++t)
-          if (t == off / 16 && r16 == off % 16) {
+          if (t == kt && r16 == kr) {
 #pragma unroll
             for (int s = 0; s < D / 32; ++s) {
               f16x8 k8;
@@ -278,19 +268,17 @@ DPK_DEV void attn_phase(const MegaArgs& a, int layer, const uint16_t* qn, const 
               kf[t][s] = __builtin_bit_cast(u32x4, k8);
             }
           }
-        const int e4 = off % 4;
+        const int e8 = off % 8;
+        if (j4 == off / 8) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-          if (h == off / 16 && j4 == (off % 16) / 4) {
+          for (int dt = 0; dt < D / 16; ++dt) {
+            f16x8 v8 = __builtin_bit_cast(f16x8, vf[dt]);
 #pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt) {
-              f16x4 v4 = __builtin_bit_cast(f16x4, vf[dt][h]);
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (e == e4) v4[e] = (_Float16)vnew[dt * 16 + r16];
-              vf[dt][h] = __builtin_bit_cast(u32x2, v4);
-            }
+            for (int e = 0; e < 8; ++e)
+              if (e == e8) v8[e] = (_Float16)vnew[dt * 16 + r16];
+            vf[dt] = __builtin_bit_cast(u32x4, v8);
           }
+        }
       }
     }
 
@@ -316,13 +304,13 @@ DPK_DEV void attn_phase(const MegaArgs& a, int layer, const uint16_t* qn, const 
         sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, ql[s], sc[t], 0, 0, 0);
       }
     }
-    // mask (positions 16 t + 4 j4 + v past the context), column max / sum
+    // mask (positions 8 j4 + 4 t + v past the context), column max / sum
     float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        if (wp0 + 16 * t + 4 * j4 + v >= c1) sc[t][v] = -INFINITY;
+        if (wp0 + 8 * j4 + 4 * t + v >= c1) sc[t][v] = -INFINITY;
         mx = fmaxf(mx, sc[t][v]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
@@ -356,7 +344,12 @@ DPK_DEV void attn_phase(const MegaArgs& a, int layer, const uint16_t* qn, const 
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
         o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const u32x4 w = {vf[dt][0].x, vf[dt][0].y, vf[dt][1].x, vf[dt][1].y};
+        u32x4 w = vf[dt];
+        if (wp0 + 32 > c1) {  // positions past the context may hold any bits (0 * NaN)
+          const int n = c1 - wp0 - 8 * j4;
+          auto mk = [n](int e) { return n >= e + 2 ? 0xffffffffu : (n == e + 1 ? 0x0000ffffu : 0u); };
+          w = u32x4{w.x & mk(0), w.y & mk(2), w.z & mk(4), w.w & mk(6)};
+        }
         const f16x8 A = __builtin_bit_cast(f16x8, w);
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, ph, o[dt], 0, 0, 0);
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pl, o[dt], 0, 0, 0);
