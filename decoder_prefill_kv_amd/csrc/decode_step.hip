@@ -160,7 +160,8 @@ DPK_DEV void attn_phase(const MegaArgs& a, int layer, const uint16_t* qn, const 
   float* mw = ml + 2 * MEGA_ATTN_MAXCH * G;  // [MEGA_ATTN_MAXCH][G]
   int* flag = (int*)(mw + MEGA_ATTN_MAXCH * G);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform over the wave
   const int r16 = lane & 15, j4 = lane >> 4;
   const int n_items = a.M * a.n_kv * a.max_chunks;
   const int rec = D + 2;
@@ -170,7 +171,8 @@ DPK_DEV void attn_phase(const MegaArgs& a, int layer, const uint16_t* qn, const 
   // in the P V product) and V^T is read as one 8-position group per lane
   u32x4 kf[2][D / 32];
   u32x4 vf[D / 16];
-  float cs = 0.f, sn = 0.f, g0 = 1.f, g1 = 1.f;  // this wave's RoPE and gain values
+  float cs = 0.f, sn = 0.f;  // this wave's RoPE values
+  uint16_t gr0 = 0, gr1 = 0;  // and its QK-norm gains (bf16)
 
   // K / V^T fragments of the item's positions for this wave, and the RoPE /
   // QK-norm constants of the row (none of it depends on the previous phase)
@@ -195,15 +197,14 @@ DPK_DEV void attn_phase(const MegaArgs& a, int layer, const uint16_t* qn, const 
     const int p8 = min(wp0 + 8 * j4, plast & ~7);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) vf[dt] = *(const u32x4*)(Vb + (size_t)(dt * 16 + r16) * a.kv.max_seq + p8);
-    if (wave <= G) {
-      cs = a.rope_cos[(size_t)rp.pos * (D / 2) + lane];
-      sn = a.rope_sin[(size_t)rp.pos * (D / 2) + lane];
-      const uint16_t* gn = wave < G ? qn : kn;
-      if (gn) {
-        g0 = bf16_to_f32(gn[lane]);
-        g1 = bf16_to_f32(gn[lane + 64]);
-      }
-    }
+    // (unconditional too: a gain that does not exist reads a dummy address,
+    // and the values are converted where they are used)
+    cs = a.rope_cos[(size_t)rp.pos * (D / 2) + lane];
+    sn = a.rope_sin[(size_t)rp.pos * (D / 2) + lane];
+    const uint16_t* gn = wave < G ? qn : kn;
+    const uint16_t* gp = gn ? gn : (const uint16_t*)a.rope_cos;
+    gr0 = gp[lane];
+    gr1 = gp[lane + 64];
   };
 
   int it = wg;
@@ -232,6 +233,7 @@ DPK_DEV void attn_phase(const MegaArgs& a, int layer, const uint16_t* qn, const 
       const bool norm = (wave < G ? qn : kn) != nullptr;
       const float ss = wave_sum(xa * xa + xb * xb);
       const float r = norm ? rsqrtf(ss / (float)D + a.eps) : 1.0f;
+      const float g0 = norm ? bf16_to_f32(gr0) : 1.0f, g1 = norm ? bf16_to_f32(gr1) : 1.0f;
       const float x1 = xa * r * g0, x2 = xb * r * g1;
       const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
       if (wave < G) {
