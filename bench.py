@@ -27,11 +27,14 @@ MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 matrix throughput
 # --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),
 # each scaled by what the same counter reads for a plain 1 GiB device copy
 # (--copy-probe): FETCH_SIZE x 2.0, WRITE_SIZE x 1.0.  A figure is only
-# reported while the kernel's source is the one it was taken on.
+# reported while the kernel's sources are the ones it was taken on.
 TRAFFIC = {
-    ("q8b", "gemv.gate_up"): {"fetch_kib": 98491.6, "write_kib": 48.0, "fetch_factor": 2.0, "write_factor": 1.0,
-                              "source": "decoder_prefill_kv_amd/csrc/gemv.hip",
-                              "sha256": "8cd541b00fbdfba0567029a64bfd74966844a74942b986bd8db1d13f8ca4f559"},
+    ("q8b", "decode.step"): {"fetch_kib": 7576837.0, "write_kib": 18955.1, "fetch_factor": 2.0, "write_factor": 1.0,
+                             "sources": ["decoder_prefill_kv_amd/csrc/decode_step.hip",
+                                         "decoder_prefill_kv_amd/csrc/gemv_body.h",
+                                         "decoder_prefill_kv_amd/csrc/common.h",
+                                         "decoder_prefill_kv_amd/csrc/kernels.h"],
+                             "sha256": "82872222d8611de8e39aa7b3dcf209db107223d93b1f2a9e2e677ded5ab1792d"},
 }
 
 
@@ -40,9 +43,12 @@ def measured_traffic(workload, kclass):
     t = TRAFFIC.get((workload, kclass))
     if not t:
         return None
-    with open(os.path.join(ROOT, t["source"]), "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != t["sha256"]:
-            return None
+    h = hashlib.sha256()
+    for src in t["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != t["sha256"]:
+        return None
     return 1024.0 * (t["fetch_kib"] * t["fetch_factor"] + t["write_kib"] * t["write_factor"])
 
 
