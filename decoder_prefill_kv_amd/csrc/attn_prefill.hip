@@ -76,26 +76,44 @@ __global__ __launch_bounds__(THREADS, 2) void attn_prefill_kernel(AttnPrefillArg
   const _Float16* Vg = (const _Float16*)a.kv.base + kv_slab(a.kv, a.seq, a.layer, 1, g);
   const int kend = a.start + wg_r1;  // keys [0, kend) are visible to some row here
   const int wave_kend = a.start + min(a.M, r0 + 32);
-  for (int k0 = 0; k0 < kend; k0 += BKV) {
-    __syncthreads();
-    // stage K [64 keys][128] and V^T [128][64 keys]
+  // K [64 keys][128] and V^T [128][64 keys] of a tile: global -> registers
+  // one tile ahead (the loads fly while the current tile is computed), then
+  // registers -> LDS.  The V^T row stride (kv.max_seq) is a multiple of 64, so
+  // an 8-key load stays inside the row.
+  u32x4 kreg[4];
+  f16x8 vreg[4];
+  auto gload = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int idx = tid + THREADS * i;  // 0..1023
       const int kr = idx >> 4, kc = (idx & 15) * 8;
-      const int key = min(k0 + kr, kend - 1);
-      *(u32x4*)&Ks[kr][kc] = *(const u32x4*)(Kg + (size_t)key * D + kc);
+      kreg[i] = *(const u32x4*)(Kg + (size_t)min(k0 + kr, kend - 1) * D + kc);
       const int vr = idx >> 3, vc = (idx & 7) * 8;
-      // the V^T row stride (kv.max_seq) is a multiple of 64, so the 8-key
-      // load stays inside the row; keys at or past kend are zeroed (the
-      // cache there may hold any bit pattern, and 0 * NaN would poison O)
-      f16x8 vv = *(const f16x8*)(Vg + (size_t)vr * a.kv.max_seq + k0 + vc);
+      vreg[i] = *(const f16x8*)(Vg + (size_t)vr * a.kv.max_seq + k0 + vc);
+    }
+  };
+  auto lstore = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + THREADS * i;
+      const int kr = idx >> 4, kc = (idx & 15) * 8;
+      *(u32x4*)&Ks[kr][kc] = kreg[i];
+      const int vr = idx >> 3, vc = (idx & 7) * 8;
+      // keys at or past kend are zeroed (the cache there may hold any bit
+      // pattern, and 0 * NaN would poison O)
+      f16x8 vv = vreg[i];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (k0 + vc + e >= kend) vv[e] = (_Float16)0.f;
       *(f16x8*)&Vs[vr][vc] = vv;
     }
+  };
+  gload(0);
+  for (int k0 = 0; k0 < kend; k0 += BKV) {
+    __syncthreads();  // the previous tile's LDS reads are done (and this tile's loads have landed)
+    lstore(k0);
     __syncthreads();
+    if (k0 + BKV < kend) gload(k0 + BKV);
     if (k0 >= wave_kend) continue;  // every key of this tile is after this wave's rows
     // S^T for two blocks of 32 keys
     f32x16 s[2];
