@@ -483,6 +483,7 @@ dpk_status gemv_xg(dpk_model* md, int cls, int M, uint16_t* const* xin, int ldxi
   // fit two to a unit), else a persistent grid
   const int n_tiles = (swiglu ? 2 * a.N : a.N) / (16 * tiles);
   if (epi != EPI_HEAD && n_tiles > a.grid && n_tiles <= 2 * a.grid) a.grid = n_tiles;
+  if (epi == EPI_HEAD && M > 8) a.grid = 2 * md->n_cu;  // measured: more rows want more workgroups in flight
   if (xout) {
     a.xo_hi = xout[0];
     a.xo_lo = xout[1];
@@ -502,6 +503,8 @@ bool batch_fits(const dpk_model* md, int M) {
   if (md->fmt != DPK_FMT_BF16 || !md->xb[0][0] || M < 1 || M > SKINNY_MAX) return false;
   for (int K : {c.hidden, c.n_heads * c.head_dim, c.intermediate})
     if (K % 1024) return false;
+  // 32-row tiles for QKV and the head, 16-row segments
+  if (md->Nqkv % 32 || c.vocab % 32 || (c.n_kv_heads * c.head_dim) % 16) return false;
   return true;
 }
 
@@ -535,7 +538,9 @@ dpk_status forward_batch(dpk_model* md, int M, int max_ctx, const int32_t* ids_d
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& L = md->layers[l];
     LinearW qkv[3] = {L.q, L.k, L.v};
-    if ((s = gemv_xg(md, K_GEMV_QKV, M, X0, H, md->sq, sq_nb, qkv, 3, EPI_STORE, false, 1, md->qkv, md->Nqkv,
+    // 32-row tiles for QKV and the head (each activation fragment serves two
+    // weight tiles; measured faster there), 16-row tiles for O and down
+    if ((s = gemv_xg(md, K_GEMV_QKV, M, X0, H, md->sq, sq_nb, qkv, 3, EPI_STORE, false, 2, md->qkv, md->Nqkv,
                      nullptr, nullptr, nullptr, 0, nullptr, st)))
       return s;
     if (one_seq) {
@@ -565,7 +570,7 @@ dpk_status forward_batch(dpk_model* md, int M, int max_ctx, const int32_t* ids_d
   uint16_t* xh[2] = {X0[0] + (size_t)head_r0 * H, X0[1] + (size_t)head_r0 * H};
   float* dst = logits ? logits : md->sink;
   return gemv_xg(md, K_GEMV_HEAD, head_n, xh, H, md->sq + (size_t)head_r0 * sq_nb, sq_nb, &md->head, 1, EPI_HEAD,
-                 false, 1, dst, c.vocab, nullptr, argmax, nullptr, 0, nullptr, st);
+                 false, 2, dst, c.vocab, nullptr, argmax, nullptr, 0, nullptr, st);
 }
 
 // Can a decode step of M rows run on the whole-K GEMV kernels?
