@@ -160,8 +160,16 @@ DPK_DEV coh_buf coh_buffer(const void* base) {
 DPK_DEV float cload(coh_buf r, uint32_t i) {
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, i * 4u, 0, CPOL_SC1));
 }
+DPK_DEV void cload2(coh_buf r, uint32_t i, float& x, float& y) {  // floats i, i+1, i % 2 == 0
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, i * 4u, 0, CPOL_SC1);
+  x = __uint_as_float(v[0]);
+  y = __uint_as_float(v[1]);
+}
 DPK_DEV f32x4 cload4(coh_buf r, uint32_t i) {  // floats i .. i+3, i % 4 == 0
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, i * 4u, 0, CPOL_SC1));
+}
+DPK_DEV void cstore2(coh_buf r, uint32_t i, float x, float y) {  // floats i, i+1, i % 2 == 0
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(x), __float_as_uint(y)}, r, i * 4u, 0, CPOL_SC1);
 }
 DPK_DEV void cstore(coh_buf r, uint32_t i, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, i * 4u, 0, CPOL_SC1);

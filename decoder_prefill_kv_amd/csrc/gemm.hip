@@ -225,26 +225,27 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs a) {
     const int tile = blockIdx.y * gridDim.x + blockIdx.x;
     const int S = a.splits;
     float* wsp = a.ws + (size_t)tile * S * (BM * BN);
-    float* own = wsp + (size_t)blockIdx.z * (BM * BN) + tid * 2;
+    const coh_buf wsb = coh_buffer(wsp);
+    const uint32_t own = (uint32_t)(blockIdx.z * (BM * BN) + tid * 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int v = 0; v < 16; v += 2)
-          coh_store2(own + (((i * 4 + j) * 8 + v / 2) * THREADS) * 2, acc[i][j][v], acc[i][j][v + 1]);
+          cstore2(wsb, own + (uint32_t)((((i * 4 + j) * 8 + v / 2) * THREADS) * 2), acc[i][j][v], acc[i][j][v + 1]);
     if (!last_block_arrive(a.counters + tile, (unsigned)S, &s_last)) return;
     // the last split re-reads every partial, its own included, and adds them
-    // in split order
+    // in split order (device-coherent buffer loads: batched, unlike atomic
+    // loads, which wait for themselves one by one)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float* src = wsp + tid * 2;
 #pragma unroll
         for (int v = 0; v < 16; v += 2) {
           float x, y;
-          coh_load2(src + (((i * 4 + j) * 8 + v / 2) * THREADS) * 2, x, y);
+          cload2(wsb, (uint32_t)((((i * 4 + j) * 8 + v / 2) * THREADS + tid) * 2), x, y);
           acc[i][j][v] = x;
           acc[i][j][v + 1] = y;
         }
@@ -252,11 +253,10 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs a) {
       for (int p = 1; p < S; ++p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float* src = wsp + (size_t)p * (BM * BN) + tid * 2;
 #pragma unroll
           for (int v = 0; v < 16; v += 2) {
             float x, y;
-            coh_load2(src + (((i * 4 + j) * 8 + v / 2) * THREADS) * 2, x, y);
+            cload2(wsb, (uint32_t)(p * (BM * BN) + (((i * 4 + j) * 8 + v / 2) * THREADS + tid) * 2), x, y);
             acc[i][j][v] += x;
             acc[i][j][v + 1] += y;
           }
