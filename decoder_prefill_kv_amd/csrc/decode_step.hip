@@ -464,7 +464,7 @@ __global__ __launch_bounds__(MT, 1) void decode_step_kernel(MegaArgs a) {
   embed_phase(a, wg, nwg);
   for (int l = 0; l < a.n_layers; ++l) {
     const MegaLayer& L = a.layers[l];
-    gemv_body<W_BF16, 1, 8, true>(L.qkv, a.M, lds, wg, nwg, sync);
+    gemv_body<W_BF16, 2, 8, true>(L.qkv, a.M, lds, wg, nwg, sync);
     closing = MP_QKV;
     attn_phase<G>(a, l, L.qn, L.kn, lds, wg, nwg, sync);
     closing = MP_ATTN;

@@ -231,8 +231,8 @@ hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t stream);
 // ---- whole decode step in one persistent (cooperative) launch, bf16 weights
 constexpr int MEGA_ATTN_MAXCH = 64;  // attention chunks per row (256 positions each)
 struct MegaLayer {                   // device-resident, one per layer
-  GemvArgs qkv;                      // the QKV projection, whole K (1.5 row tiles per workgroup
-                                     //   measured faster than splits of K that balance the tiles)
+  GemvArgs qkv;                      // the QKV projection, whole K, 32-row tiles (measured faster
+                                     //   than 16-row tiles and than K splits that balance the tiles)
   GemvArgs o, gu, down;              // M is set per launch
   const uint16_t* qn;                // QK-norm gains (bf16) or null
   const uint16_t* kn;

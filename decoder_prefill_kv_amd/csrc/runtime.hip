@@ -659,7 +659,7 @@ dpk_status mega_table(dpk_model* md, hipStream_t st) {
     const LayerW& L = md->layers[l];
     LinearW qkv[3] = {L.q, L.k, L.v};
     LinearW gu[2] = {L.gate, L.up};
-    t[l].qkv = gemv_args(md, 1, md->h, H, md->sq, H / 16, L.in_norm, qkv, 3, EPI_STORE, false, 1, md->qkv, md->Nqkv,
+    t[l].qkv = gemv_args(md, 1, md->h, H, md->sq, H / 16, L.in_norm, qkv, 3, EPI_STORE, false, 2, md->qkv, md->Nqkv,
                          nullptr, nullptr);
     t[l].o = gemv_args(md, 1, md->attn_o, Qd, nullptr, 0, nullptr, &L.o, 1, EPI_RESID, false, 1, md->h, H, md->sq,
                        nullptr);
