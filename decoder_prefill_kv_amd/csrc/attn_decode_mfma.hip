@@ -411,8 +411,9 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(AttnDecodeArgs a) {
   if (a.out_hi) {
     uint32_t h16, l16;
     split_bf16(y, h16, l16);
-    a.out_hi[oi] = (uint16_t)h16;
-    a.out_lo[oi] = (uint16_t)l16;
+    const size_t xi = xg_index(m, head * D + e);
+    a.out_hi[xi] = (uint16_t)h16;
+    a.out_lo[xi] = (uint16_t)l16;
   } else {
     a.out[oi] = y;
   }

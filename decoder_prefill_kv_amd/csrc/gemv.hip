@@ -85,7 +85,8 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
     // shape); each wave's K part must hold whole 128-column iterations
     const int W = a.waves ? a.waves : 4;
     if ((W != 4 && W != 8) || a.K % (W * 128)) return hipErrorInvalidValue;
-    if (a.fmt != W_BF16 || !a.xb_lo || a.ldxb < a.K) return hipErrorInvalidValue;
+    if (a.fmt != W_BF16 || !a.xb_lo || a.xrow0 < 0 || a.xrow0 + a.M > 16 || (a.kofs + a.K) % 32)
+      return hipErrorInvalidValue;
     const size_t lds_xg = (size_t)W * a.M * RB * 4 + (64 + 16 * W) * 4;
 #define DPK_GEMV_XG_CASE(T, WV)                                                  \
   if (a.tiles == T && W == WV) {                                               \

@@ -58,7 +58,7 @@ __host__ __device__ inline int gemv_lds_layout(int M, int K, int RB, int fmt, in
 // loads in flight are never drained by them.
 //
 // XG: the activations come ready-made from global memory as bf16 hi / lo
-// rows (a.xb_hi / a.xb_lo, row stride a.ldxb, norm and gain already applied)
+// rows (a.xb_hi / a.xb_lo in the xg_index layout, norm gain already applied)
 // instead of being staged in LDS, so M is not limited by LDS (bf16 weights).
 template <int FMT, int T, int WAVES, bool COH, bool XG = false, typename Pre>
 DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const int wg, const int nwg, Pre&& pre) {
@@ -135,7 +135,7 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
   constexpr int UX = XG ? U : 1;
   u32x4 xh0[UX], xl0[UX], xh1[UX], xl1[UX];
   size_t xrow = 0;
-  if constexpr (XG) xrow = (size_t)(r16 < M ? r16 : M - 1) * a.ldxb + KO + k0 + 8 * j4;
+  if constexpr (XG) xrow = xg_index(a.xrow0 + (r16 < M ? r16 : M - 1), KO + k0 + 8 * j4);
   auto load_bf = [&](u32x4 (&b)[T][U], u32x4 (&xh)[UX], u32x4 (&xl)[UX], int it) {
 #pragma unroll
     for (int t = 0; t < T; ++t)
@@ -145,8 +145,8 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
     if constexpr (XG) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        xh[u] = *(const u32x4*)(a.xb_hi + xrow + (it * U + u) * 32);
-        xl[u] = *(const u32x4*)(a.xb_lo + xrow + (it * U + u) * 32);
+        xh[u] = *(const u32x4*)(a.xb_hi + xrow + ((size_t)(it * U + u) << 9));  // next 32-column block
+        xl[u] = *(const u32x4*)(a.xb_lo + xrow + ((size_t)(it * U + u) << 9));
       }
     }
   };
@@ -365,7 +365,7 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
         if (a.xo_hi) {  // the next GEMV's activations, bf16 hi / lo
           uint32_t h16, l16;
           split_bf16(y, h16, l16);
-          const size_t o = (size_t)m * a.ldxo + tile * HR + r;
+          const size_t o = xg_index(m, tile * HR + r);
           a.xo_hi[o] = (uint16_t)h16;
           a.xo_lo[o] = (uint16_t)l16;
         } else if constexpr (COH)
@@ -388,8 +388,8 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
         if (a.xo_hi) {  // h * gain as the next GEMV's bf16 hi / lo activations
           uint32_t h16, l16;
           split_bf16(a.xo_gain ? h * bf16_to_f32(a.xo_gain[n]) : h, h16, l16);
-          a.xo_hi[(size_t)m * a.ldxo + n] = (uint16_t)h16;
-          a.xo_lo[(size_t)m * a.ldxo + n] = (uint16_t)l16;
+          a.xo_hi[xg_index(m, n)] = (uint16_t)h16;
+          a.xo_lo[xg_index(m, n)] = (uint16_t)l16;
         }
       }
       lds_barrier();

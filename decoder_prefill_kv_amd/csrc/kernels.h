@@ -74,19 +74,27 @@ size_t skinny_lds_bytes(int M, int kchunk, int rows, int fmt);
 // Weights are given in the re-tiled fragment layout (launch_tile_bf16 /
 // launch_tile_q4): w = tiled bf16 or tiled 4-bit codes, sb = tiled 4-bit
 // (scale, bias) pairs.  Every segment has a multiple of 16 rows.
+// Layout of ready-made GEMV activations: blocks of 32 columns, each holding
+// 16 rows x 32 columns (1 KB of bf16), so that one wave's MFMA B fragment
+// (row = lane % 16, columns 8 (lane / 16) .. + 7 of a 32-column step) is one
+// contiguous 1 KB read.  Holds 16 rows; column counts are multiples of 32.
+__host__ __device__ inline size_t xg_index(int m, int k) {
+  return ((size_t)(k >> 5) << 9) + ((size_t)m << 5) + (k & 31);
+}
+
 struct GemvArgs {
   int M, K, N;              // rows (<=16), input dim, output rows (per matrix for swiglu)
   int fmt, tiles, swiglu, epi;
   int grid;                 // workgroups (they loop over row tiles)
   int waves;                // ready-made-activation mode: 4 or 8 waves per workgroup, 0: by K
   int kofs, kfull;          // reduce over columns [kofs, kofs + K) of rows of kfull (0: K) columns
-  const uint16_t* xb_hi;    // non-null: activations as bf16 hi / lo rows [M][ldxb] (bf16
-  const uint16_t* xb_lo;    //   weights; x is not read).  Any gain is already applied; with
-  int ldxb;                 //   sq_in the outputs are scaled by each row's rsqrt(mean + eps)
+  const uint16_t* xb_hi;    // non-null: activations as bf16 hi / lo in the xg_index layout (bf16
+  const uint16_t* xb_lo;    //   weights; x is not read), rows xrow0 .. xrow0 + M - 1.  Any gain
+  int xrow0;                //   is already applied; with sq_in the outputs are scaled by each
+                            //   row's rsqrt(mean + eps)
   uint16_t* xo_hi;          // non-null (EPI_RESID / EPI_SWIGLU): also write the result as the
-  uint16_t* xo_lo;          //   next GEMV's bf16 hi / lo activations [M][ldxo], times
-  int ldxo;                 //   xo_gain[n] if given (RESID); SWIGLU then skips out
-  const uint16_t* xo_gain;
+  uint16_t* xo_lo;          //   next GEMV's bf16 hi / lo activations (xg_index layout), times
+  const uint16_t* xo_gain;  //   xo_gain[n] if given (RESID); SWIGLU then skips out
   const void* w[3];
   const void* sb[3];
   int seg_end[3];
@@ -138,7 +146,7 @@ struct AttnDecodeArgs {
   // element, instead of the last-arriving workgroup of each row and KV head
   int merge;
   uint16_t* out_hi;           // with merge: if non-null, the output goes here as bf16 hi / lo
-  uint16_t* out_lo;           //   rows [M][n_heads*d] (a GEMV's activations) instead of to out
+  uint16_t* out_lo;           //   (a GEMV's activations, xg_index layout) instead of to out
   // raw mode (qkv_raw != null): q is taken from the raw projection
   // [M][ld_raw] (q heads, k heads, v heads) and gets QK-norm + RoPE here; the
   // workgroup whose chunk holds the row's position computes that position's
@@ -181,8 +189,9 @@ hipError_t launch_gemv_f32(int M, int N, int K, const float* W, const float* W2,
                            float* out, int ldo, int mode, hipStream_t stream);
 // argmax per row over [M][N] logits (lowest index on ties)
 hipError_t launch_argmax_rows(int M, int N, const float* logits, int ld, int* out, hipStream_t stream);
-// x'[m][k] = x[m][k] * rs[m] * g[k] as bf16 hi + lo rows [M][K]; rs[m] from the
-// sums of squares sq_in[m][0..nb) over K (null: 1), g bf16 [K] or null
+// x'[m][k] = x[m][k] * rs[m] * g[k] as bf16 hi + lo in the xg_index layout
+// (M <= 16, K % 32 == 0); rs[m] from the sums of squares sq_in[m][0..nb)
+// over K (null: 1), g bf16 [K] or null
 hipError_t launch_xprep(int M, int K, const float* x, int ldx, const float* sq_in, int nb, const uint16_t* g,
                         float eps, uint16_t* hi, uint16_t* lo, hipStream_t stream);
 // residual add out += in

@@ -84,8 +84,9 @@ __global__ void xprep_kernel(int K, const float* x, int ldx, const float* sq_in,
     h[e / 2] = h0 | (h1 << 16);
     l[e / 2] = l0 | (l1 << 16);
   }
-  *(uint4*)(hi + (size_t)m * K + k) = make_uint4(h[0], h[1], h[2], h[3]);
-  *(uint4*)(lo + (size_t)m * K + k) = make_uint4(l[0], l[1], l[2], l[3]);
+  // 8 consecutive columns stay inside one 32-column block of the layout
+  *(uint4*)(hi + xg_index(m, k)) = make_uint4(h[0], h[1], h[2], h[3]);
+  *(uint4*)(lo + xg_index(m, k)) = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
 __global__ void rmsnorm_rows_kernel(int H, const float* x, int ldx, const void* g, int g_is_f32, float eps,
@@ -304,7 +305,7 @@ hipError_t launch_argmax_rows(int M, int N, const float* logits, int ld, int* ou
 
 hipError_t launch_xprep(int M, int K, const float* x, int ldx, const float* sq_in, int nb, const uint16_t* g,
                         float eps, uint16_t* hi, uint16_t* lo, hipStream_t stream) {
-  if (M < 1 || K % 8) return hipErrorInvalidValue;
+  if (M < 1 || M > 16 || K % 32) return hipErrorInvalidValue;
   launch(xprep_kernel, dim3(M, (K + 2047) / 2048), dim3(256), 0, stream, K, x, ldx, sq_in, nb, g, eps, hi, lo);
   return hipGetLastError();
 }

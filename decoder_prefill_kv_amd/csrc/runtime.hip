@@ -466,19 +466,18 @@ dpk_status gemv(dpk_model* md, int cls, int M, const float* x, int ldx, const fl
   return DPK_OK;
 }
 
-// One GEMV launch on ready-made bf16 hi / lo activations xin (row stride
-// ldxin; sq_in: per-row sums of squares whose norm scale the outputs take).
-// xout: where a RESID / SWIGLU epilogue also writes the next GEMV's
-// activations (times xo_gain for RESID).
-dpk_status gemv_xg(dpk_model* md, int cls, int M, uint16_t* const* xin, int ldxin, const float* sq_in, int sq_nb,
+// One GEMV launch on ready-made bf16 hi / lo activations xin (xg_index
+// layout, rows xrow0 .. xrow0 + M - 1; sq_in: per-row sums of squares whose
+// norm scale the outputs take).  xout: where a RESID / SWIGLU epilogue also
+// writes the next GEMV's activations (times xo_gain for RESID).
+dpk_status gemv_xg(dpk_model* md, int cls, int M, uint16_t* const* xin, int xrow0, const float* sq_in, int sq_nb,
                    const LinearW* segs, int nseg, int epi, bool swiglu, int tiles, float* out, int ldo,
-                   float* sq_out, int32_t* argmax, uint16_t* const* xout, int ldxout, const void* xo_gain,
-                   hipStream_t st) {
+                   float* sq_out, int32_t* argmax, uint16_t* const* xout, const void* xo_gain, hipStream_t st) {
   GemvArgs a = gemv_args(md, M, nullptr, 0, sq_in, sq_nb, nullptr, segs, nseg, epi, swiglu, tiles, out, ldo, sq_out,
                          argmax);
   a.xb_hi = xin[0];
   a.xb_lo = xin[1];
-  a.ldxb = ldxin;
+  a.xrow0 = xrow0;
   // up to two row tiles per compute unit all at once (the 4-wave workgroups
   // fit two to a unit), else a persistent grid
   const int n_tiles = (swiglu ? 2 * a.N : a.N) / (16 * tiles);
@@ -487,7 +486,6 @@ dpk_status gemv_xg(dpk_model* md, int cls, int M, uint16_t* const* xin, int ldxi
   if (xout) {
     a.xo_hi = xout[0];
     a.xo_lo = xout[1];
-    a.ldxo = ldxout;
     a.xo_gain = (const uint16_t*)xo_gain;
   }
   const double nrows = swiglu ? 2.0 * a.N : (double)a.N;
@@ -540,8 +538,8 @@ dpk_status forward_batch(dpk_model* md, int M, int max_ctx, const int32_t* ids_d
     LinearW qkv[3] = {L.q, L.k, L.v};
     // 32-row tiles for QKV and the head (each activation fragment serves two
     // weight tiles; measured faster there), 16-row tiles for O and down
-    if ((s = gemv_xg(md, K_GEMV_QKV, M, X0, H, md->sq, sq_nb, qkv, 3, EPI_STORE, false, 2, md->qkv, md->Nqkv,
-                     nullptr, nullptr, nullptr, 0, nullptr, st)))
+    if ((s = gemv_xg(md, K_GEMV_QKV, M, X0, 0, md->sq, sq_nb, qkv, 3, EPI_STORE, false, 2, md->qkv, md->Nqkv,
+                     nullptr, nullptr, nullptr, nullptr, st)))
       return s;
     if (one_seq) {
       {
@@ -553,24 +551,23 @@ dpk_status forward_batch(dpk_model* md, int M, int max_ctx, const int32_t* ids_d
     } else if ((s = attn_decode(md, M, max_ctx, nullptr, md->attn_o, l, st, kv_positions, md->qkv, false, X1))) {
       return s;
     }
-    if ((s = gemv_xg(md, K_GEMV_O, M, X1, Qd, nullptr, 0, &L.o, 1, EPI_RESID, false, 1, md->h, H, md->sq, nullptr,
-                     X0, H, L.post_norm, st)))
+    if ((s = gemv_xg(md, K_GEMV_O, M, X1, 0, nullptr, 0, &L.o, 1, EPI_RESID, false, 1, md->h, H, md->sq, nullptr,
+                     X0, L.post_norm, st)))
       return s;
     sq_nb = H / 16;
     LinearW gu[2] = {L.gate, L.up};
-    if ((s = gemv_xg(md, K_GEMV_GATEUP, M, X0, H, md->sq, sq_nb, gu, 2, EPI_SWIGLU, true, 2, md->act, I, nullptr,
-                     nullptr, X1, I, nullptr, st)))
+    if ((s = gemv_xg(md, K_GEMV_GATEUP, M, X0, 0, md->sq, sq_nb, gu, 2, EPI_SWIGLU, true, 2, md->act, I, nullptr,
+                     nullptr, X1, nullptr, st)))
       return s;
     const void* next_gain = l + 1 < c.n_layers ? md->layers[l + 1].in_norm : md->final_norm;
-    if ((s = gemv_xg(md, K_GEMV_DOWN, M, X1, I, nullptr, 0, &L.down, 1, EPI_RESID, false, 1, md->h, H, md->sq,
-                     nullptr, X0, H, next_gain, st)))
+    if ((s = gemv_xg(md, K_GEMV_DOWN, M, X1, 0, nullptr, 0, &L.down, 1, EPI_RESID, false, 1, md->h, H, md->sq,
+                     nullptr, X0, next_gain, st)))
       return s;
   }
   if (head_n <= 0) return DPK_OK;
-  uint16_t* xh[2] = {X0[0] + (size_t)head_r0 * H, X0[1] + (size_t)head_r0 * H};
   float* dst = logits ? logits : md->sink;
-  return gemv_xg(md, K_GEMV_HEAD, head_n, xh, H, md->sq + (size_t)head_r0 * sq_nb, sq_nb, &md->head, 1, EPI_HEAD,
-                 false, 2, dst, c.vocab, nullptr, argmax, nullptr, 0, nullptr, st);
+  return gemv_xg(md, K_GEMV_HEAD, head_n, X0, head_r0, md->sq + (size_t)head_r0 * sq_nb, sq_nb, &md->head, 1,
+                 EPI_HEAD, false, 2, dst, c.vocab, nullptr, argmax, nullptr, nullptr, st);
 }
 
 // Can a decode step of M rows run on the whole-K GEMV kernels?
