@@ -1,16 +1,22 @@
 // Decode attention on gfx950 matrix cores (fp16 KV cache).
 //
 // Same contract as attn_decode.hip (rows with their own slot and position,
-// grouped-query heads, context split in chunks of 256 positions merged by
-// log-sum-exp), but both products run on v_mfma_f32_16x16x32_f16 with the G
-// query heads of a KV head as the MFMA columns:
+// grouped-query heads, context split in chunks merged by log-sum-exp), with
+// both products on v_mfma_f32_16x16x32_f16 and the G query heads of a KV head
+// as the MFMA columns:
 //   S   = K Q^T     A = K rows (16 positions x 32 channels, straight from the
 //                   cache), B = q (32 channels x 16 columns, G used)
 //   O^T = V^T P^T   A = V^T rows (16 channels x 32 positions), B = P^T taken
 //                   directly from the S accumulators
 // q and p are split into fp16 hi + lo (two MFMAs each), so the only rounding
-// is the fp16 cache itself.  Each wave owns 64 positions of the chunk; the
-// four waves' softmax statistics are combined through LDS.
+// is the fp16 cache itself.
+//
+// Streaming: a workgroup (8 waves) walks a chunk of a.chunk positions in
+// steps of 256 (32 per wave) with an online softmax, the next step's cache
+// loads in flight while the current one is computed, so the memory system
+// stays busy instead of every workgroup loading, then computing, then exiting
+// at once.  The host sizes the chunk to give about one workgroup per CU.  The
+// chunks' (max, sum, O) records are merged by attn_merge_kernel.
 //
 // MFMA 16x16x32 lane layout: A lane l holds row l%16, k = 8(l/16)..+7; B lane l
 // holds column l%16, the same k; D lane l holds rows 4(l/16)+v, column l%16.
@@ -21,21 +27,15 @@ namespace dpk {
 
 namespace {
 
-constexpr int THREADS = 256;
-constexpr int CHUNK = 256;   // positions per workgroup, 64 per wave
+constexpr int NW = 8;              // waves per workgroup
+constexpr int THREADS = 64 * NW;
+constexpr int STEP = 32 * NW;      // positions per step (32 per wave)
 constexpr int MAXCH = 64;
 constexpr float LOG2E = 1.4426950408889634f;
 
 DPK_DEV void split_f16(float x, _Float16& hi, _Float16& lo) {
   hi = (_Float16)x;
   lo = (_Float16)(x - (float)hi);
-}
-
-// the fp16 of positions p + e >= c1 zeroed (a group of 8 from position p)
-DPK_DEV u32x4 vmask(u32x4 v, int p, int c1) {
-  const int n = c1 - p;
-  auto m = [n](int e) { return n >= e + 2 ? 0xffffffffu : (n == e + 1 ? 0x0000ffffu : 0u); };
-  return u32x4{v.x & m(0), v.y & m(2), v.z & m(4), v.w & m(6)};
 }
 
 template <int D, bool RAW>
@@ -50,24 +50,23 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
   RowParam rp = a.rows_param[m];
   for (int r = 1; r < R; ++r) rp.pos = max(rp.pos, a.rows_param[m + r].pos);
   const int ctx = rp.pos + 1;  // the group's longest context
-  const int nch = (ctx + CHUNK - 1) / CHUNK;
+  const int CH = a.chunk;
+  const int nch = (ctx + CH - 1) / CH;
   if (chunk_id >= nch) return;
-  const int c0 = chunk_id * CHUNK;
-  const int c1 = min(ctx, c0 + CHUNK);
+  const int c0 = chunk_id * CH;
+  const int c1 = min(ctx, c0 + CH);
+  const int nsteps = (c1 - c0 + STEP - 1) / STEP;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform over the wave
   const int r16 = lane & 15, j4 = lane >> 4;
-  const int wp0 = c0 + 64 * wave;  // this wave's first position
   // end of this lane's column (its row's context) inside the chunk
   const int c1_col = (r16 < RG) ? min(a.rows_param[m + r16 / G].pos + 1, c1) : c1;
 
   __shared__ float qs[16][D];
+  __shared__ __attribute__((aligned(16))) _Float16 qh16[16][D], ql16[16][D];
   __shared__ float knew[D], vnew[D];
-  __shared__ float wst[4][2][16];     // per wave: max, sum per column
-  __shared__ float ow[4][D][16];      // per wave: O^T partial
-  __shared__ float ml[2][MAXCH][16];
-  __shared__ float mw[MAXCH][16];
-  __shared__ int flag;
+  __shared__ float wst[NW][2][16];     // per wave: max, sum per column
+  __shared__ float ow[NW][D][16];      // per wave: O^T partial
 
   const _Float16* Kb = (const _Float16*)a.kv.base + kv_slab(a.kv, rp.seq, a.layer, 0, g);
   const _Float16* Vb = (const _Float16*)a.kv.base + kv_slab(a.kv, rp.seq, a.layer, 1, g);
@@ -77,12 +76,12 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
   // ---- this workgroup's inputs other than the cache are loaded before it,
   // so that waiting for them leaves the cache loads in flight (loads complete
   // in issue order).  Not raw: q of the RG columns.  Raw: the row's projected
-  // heads that this wave normalises and rotates (query heads wave, wave + 4,
+  // heads that this wave normalises and rotates (query heads wave, wave + NW,
   // ..., then the KV head's key when own), their gains, the rotation of the
   // position and the new value; clamped indices, no branches.
   constexpr int QPT = 16 * D / THREADS;
   constexpr int HD = D / 2;
-  constexpr int NIT = (16 + 1 + 3) / 4;  // G + 1 <= 17 heads over 4 waves
+  constexpr int NIT = (16 + 1 + NW - 1) / NW;  // G + 1 <= 17 heads over NW waves
   const int nh = own ? G + 1 : G;
   const int li = lane % HD;
   float qv[QPT];
@@ -98,7 +97,7 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
     const float* src = a.qkv_raw + (size_t)m * a.ld_raw;
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      const int h = min(wave + 4 * it, nh - 1);
+      const int h = min(wave + NW * it, nh - 1);
       const float* x = (h < G) ? src + (size_t)(g * G + h) * D : src + (size_t)(a.n_heads + g) * D;
       xr[it][0] = x[li];
       xr[it][1] = x[li + HD];
@@ -113,34 +112,28 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
     vv = src[(size_t)(a.n_heads + a.n_kv + g) * D + tid % D];
   }
 
-  // ---- cache loads (independent of q), unconditional: positions past the
-  // context read the last one's address (K rows are masked in S, V groups at
-  // the product).  K fragments of 4 tiles x D/32 k-steps, V^T fragments of
-  // D/16 channel tiles x 2 position steps.
-  // Row r of K tile t is position kpos(t, r) = 32 (t / 2) + 8 (r / 4) + 4 (t % 2)
-  // + r % 4 of the wave's 64: the S accumulators of tiles 2 ps and 2 ps + 1 then
-  // give lane group j4 the positions 32 ps + 8 j4 .. + 7, which is the k range
-  // of P^T that lane group takes in the P V product, so V^T is read as one
-  // contiguous 8-position (16-byte) group per lane.
-  u32x4 kf[4][D / 32];
+  // ---- cache fragments of one step for this wave, unconditional loads:
+  // positions past the context read the last one's address (K rows are masked
+  // in S, V groups where they are used).  K tile t row r is position
+  // 8 (r / 4) + 4 t + r % 4 of the wave's 32, so the S accumulators give lane
+  // group j4 positions 8 j4 .. + 7 (its k range of P^T in the P V product)
+  // and V^T is read as one 8-position (16-byte) group per lane; an 8-position
+  // group stays inside the slab row (max_seq % 64 == 0).
+  auto load = [&](u32x4 (&kf)[2][D / 32], u32x4 (&vf)[D / 16], int s) {
+    const int sp = c0 + s * STEP + 32 * wave;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int p = min(wp0 + 32 * (t >> 1) + 8 * (r16 >> 2) + 4 * (t & 1) + (r16 & 3), c1 - 1);
+    for (int t = 0; t < 2; ++t) {
+      const int p = min(sp + 8 * (r16 >> 2) + 4 * t + (r16 & 3), c1 - 1);
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) kf[t][s] = *(const u32x4*)(Kb + (size_t)p * D + 32 * s + 8 * j4);
-  }
-  // V^T: channel row dt * 16 + r16, positions 32 ps + 8 j4 .. + 7 (an 8-position
-  // group stays inside the slab row: max_seq % 64 == 0)
-  u32x4 vf[D / 16][2];
-  const int vlast = (c1 - 1) & ~7;
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-    for (int ps = 0; ps < 2; ++ps) {
-      const int p = min(wp0 + 32 * ps + 8 * j4, vlast);
-      vf[dt][ps] = *(const u32x4*)(Vb + (size_t)(dt * 16 + r16) * a.kv.max_seq + p);
+      for (int ks = 0; ks < D / 32; ++ks) kf[t][ks] = *(const u32x4*)(Kb + (size_t)p * D + 32 * ks + 8 * j4);
     }
-  const bool vfull = wp0 + 64 <= c1;  // no V group of this wave reaches past the context
+    const int p8 = min(sp + 8 * j4, (c1 - 1) & ~7);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) vf[dt] = *(const u32x4*)(Vb + (size_t)(dt * 16 + r16) * a.kv.max_seq + p8);
+  };
+  u32x4 kA[2][D / 32], vA[D / 16], kB[2][D / 32], vB[D / 16];
+  load(kA, vA, 0);
+  if (nsteps > 1) load(kB, vB, 1);
 
   // ---- q (and in raw mode the new key/value) -> LDS
   if constexpr (!raw) {
@@ -156,7 +149,7 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
     const bool qk = a.qn != nullptr;
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      const int h = wave + 4 * it;
+      const int h = wave + NW * it;
       if (h >= nh) break;
       const bool on = lane < HD;
       float ss = on ? xr[it][0] * xr[it][0] + xr[it][1] * xr[it][1] : 0.f;
@@ -179,119 +172,137 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
     if (own && tid < D) vnew[tid] = vv;
   }
   lds_barrier();  // an LDS-only barrier: the cache loads stay in flight
-  if (own) {
+  if (own)
     for (int e = tid; e < D; e += THREADS) {
       kv_store(a.kv, kv_offset(a.kv, rp.seq, a.layer, 0, g, e, rp.pos), knew[e]);
       kv_store(a.kv, kv_offset(a.kv, rp.seq, a.layer, 1, g, e, rp.pos), vnew[e]);
     }
-    // the new position inside this wave's fragments comes from knew / vnew
-    const int off = rp.pos - wp0;
-    if (off >= 0 && off < 64) {
-      // compile-time fragment indices only (runtime ones would spill the arrays)
-      const int kt = 2 * (off / 32) + (off % 8) / 4, kr = 4 * ((off % 32) / 8) + off % 4;  // kpos^-1
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        if (t == kt && r16 == kr) {
-#pragma unroll
-          for (int s = 0; s < D / 32; ++s) {
-            f16x8 k8;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) k8[i] = (_Float16)knew[32 * s + 8 * j4 + i];
-            kf[t][s] = __builtin_bit_cast(u32x4, k8);
-          }
-        }
-      const int e8 = off % 8;
-#pragma unroll
-      for (int ps = 0; ps < 2; ++ps)
-        if (ps == off / 32 && j4 == (off % 32) / 8) {
-#pragma unroll
-          for (int dt = 0; dt < D / 16; ++dt) {
-            f16x8 v8 = __builtin_bit_cast(f16x8, vf[dt][ps]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (e == e8) v8[e] = (_Float16)vnew[dt * 16 + r16];
-            vf[dt][ps] = __builtin_bit_cast(u32x4, v8);
-          }
-        }
-    }
-  }
 
-  // ---- S = K Q^T (log2 domain), 4 tiles of 16 positions
-  f16x8 qh[D / 32], ql[D / 32];
-#pragma unroll
-  for (int s = 0; s < D / 32; ++s)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      _Float16 h, l;
-      split_f16(qs[r16][32 * s + 8 * j4 + i], h, l);
-      qh[s][i] = h;
-      ql[s][i] = l;
-    }
-  f32x4 sc[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-      const f16x8 A = __builtin_bit_cast(f16x8, kf[t][s]);
-      sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qh[s], sc[t], 0, 0, 0);
-      sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, ql[s], sc[t], 0, 0, 0);
-    }
+  // q as fp16 hi + lo, kept in LDS (the B fragments are re-read every step:
+  // registers are what the two steps of cache fragments in flight need)
+  for (int i = tid; i < 16 * D; i += THREADS) {
+    _Float16 h, l;
+    split_f16((&qs[0][0])[i], h, l);
+    (&qh16[0][0])[i] = h;
+    (&ql16[0][0])[i] = l;
   }
-  // mask (positions 16 t + 4 j4 + v past the context), column max / sum
-  float mx = -INFINITY;
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      if (wp0 + 32 * (t >> 1) + 8 * j4 + 4 * (t & 1) + v >= c1_col) sc[t][v] = -INFINITY;
-      mx = fmaxf(mx, sc[t][v]);
-    }
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  float sum = 0.f;
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float e = (sc[t][v] == -INFINITY) ? 0.f : exp2f(sc[t][v] - mx);
-      sc[t][v] = e;
-      sum += e;
-    }
-  sum += __shfl_xor(sum, 16, 64);
-  sum += __shfl_xor(sum, 32, 64);
+  lds_barrier();
 
-  // ---- O^T = V^T P^T: step ps uses tiles 2 ps (slots 0..3) and 2 ps + 1 (4..7)
+  // ---- the steps, online softmax per column (log2 domain)
+  float mrun = -INFINITY, lrun = 0.f;
   f32x4 o[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto step = [&](u32x4 (&kf)[2][D / 32], u32x4 (&vf)[D / 16], int s) {
+    const int sp = c0 + s * STEP + 32 * wave;
+    if (own) {  // the new position inside this wave's fragments comes from knew / vnew
+      const int off = rp.pos - sp;
+      if (off >= 0 && off < 32) {
+        // compile-time fragment indices only (runtime ones would spill the arrays)
+        const int kt = (off % 8) / 4, kr = 4 * (off / 8) + off % 4;
 #pragma unroll
-  for (int ps = 0; ps < 2; ++ps) {
+        for (int t = 0; t < 2; ++t)
+          if (t == kt && r16 == kr) {
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks) {
+              f16x8 k8;
+#pragma unroll
+              for (int i = 0; i < 8; ++i) k8[i] = (_Float16)knew[32 * ks + 8 * j4 + i];
+              kf[t][ks] = __builtin_bit_cast(u32x4, k8);
+            }
+          }
+        const int e8 = off % 8;
+        if (j4 == off / 8) {
+#pragma unroll
+          for (int dt = 0; dt < D / 16; ++dt) {
+            f16x8 v8 = __builtin_bit_cast(f16x8, vf[dt]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (e == e8) v8[e] = (_Float16)vnew[dt * 16 + r16];
+            vf[dt] = __builtin_bit_cast(u32x4, v8);
+          }
+        }
+      }
+    }
+    f32x4 sc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        const f16x8 A = __builtin_bit_cast(f16x8, kf[t][ks]);
+        const f16x8 qh = *(const f16x8*)&qh16[r16][32 * ks + 8 * j4];
+        const f16x8 ql = *(const f16x8*)&ql16[r16][32 * ks + 8 * j4];
+        sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qh, sc[t], 0, 0, 0);
+        sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, ql, sc[t], 0, 0, 0);
+      }
+    }
+    // mask (positions sp + 8 j4 + 4 t + v past the column's context), step max
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        if (sp + 8 * j4 + 4 * t + v >= c1_col) sc[t][v] = -INFINITY;
+        mx = fmaxf(mx, sc[t][v]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mnew = fmaxf(mrun, mx);
+    const float alpha = (mrun == -INFINITY) ? 0.f : exp2f(mrun - mnew);
+    float sum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float e = (sc[t][v] == -INFINITY) ? 0.f : exp2f(sc[t][v] - mnew);
+        sc[t][v] = e;
+        sum += e;
+      }
+    sum += __shfl_xor(sum, 16, 64);
+    sum += __shfl_xor(sum, 32, 64);
+    lrun = lrun * alpha + sum;
+    mrun = mnew;
+    // O^T = alpha O^T + V^T P^T (k slots 0..3 from tile 0, 4..7 from tile 1)
     f16x8 ph, pl;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       _Float16 h0, l0, h1, l1;
-      split_f16(sc[2 * ps][v], h0, l0);
-      split_f16(sc[2 * ps + 1][v], h1, l1);
+      split_f16(sc[0][v], h0, l0);
+      split_f16(sc[1][v], h1, l1);
       ph[v] = h0;
       pl[v] = l0;
       ph[4 + v] = h1;
       pl[4 + v] = l1;
     }
+    // V positions past the context may hold any bits (0 * NaN): masked with
+    // ANDs (no branch, so the wait counts stay exact)
+    const int nv = c1 - sp - 8 * j4;
+    auto mk = [nv](int e) { return nv >= e + 2 ? 0xffffffffu : (nv == e + 1 ? 0x0000ffffu : 0u); };
+    const u32x4 vm = {mk(0), mk(2), mk(4), mk(6)};
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      u32x4 w = vf[dt][ps];
-      if (!vfull) w = vmask(w, wp0 + 32 * ps + 8 * j4, c1);  // past the context: any bits (0 * NaN)
+      const u32x4 w = vf[dt] & vm;
       const f16x8 A = __builtin_bit_cast(f16x8, w);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) o[dt][v] *= alpha;
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, ph, o[dt], 0, 0, 0);
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pl, o[dt], 0, 0, 0);
     }
+  };
+  for (int s = 0; s < nsteps; s += 2) {
+    step(kA, vA, s);
+    if (s + 2 < nsteps) load(kA, vA, s + 2);
+    if (s + 1 < nsteps) {
+      step(kB, vB, s + 1);
+      if (s + 3 < nsteps) load(kB, vB, s + 3);
+    }
   }
 
-  // ---- combine the four waves (per column = query head)
+  // ---- combine the waves (per column = query head)
   if (j4 == 0) {
-    wst[wave][0][r16] = mx;
-    wst[wave][1][r16] = sum;
+    wst[wave][0][r16] = mrun;
+    wst[wave][1][r16] = lrun;
   }
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt)
@@ -306,67 +317,24 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
     const size_t mh = (size_t)(m + c / G) * a.n_heads + g * G + c % G;  // (row, head)
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, wst[w][0][c]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, wst[w][0][c]);
     float L = 0.f, O = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float f = (wst[w][0][c] == -INFINITY) ? 0.f : exp2f(wst[w][0][c] - M);
       L += f * wst[w][1][c];
       O += f * ow[w][e][c];
     }
-    if (nch == 1 && !a.merge) {
+    if (!a.merge) {  // one chunk: the result
       a.out[mh * D + e] = O / L;
     } else {
       float* r = a.part + (mh * a.max_chunks + chunk_id) * rec;
-      coh_store(r + 2 + e, O);
+      r[2 + e] = O;
       if (e == 0) {
-        coh_store(r, M);
-        coh_store(r + 1, L);
+        r[0] = M;
+        r[1] = L;
       }
     }
-  }
-  if (nch == 1 || a.merge) return;
-  if (!last_block_arrive(a.counters + blockIdx.z * a.n_kv + g, nch, &flag)) return;
-  // the other workgroups' partials: device-coherent plain loads (batched,
-  // unlike atomic loads, which wait for themselves one by one)
-  const coh_buf pb = coh_buffer(a.part);
-  for (int i = tid; i < RG * nch; i += THREADS) {
-    const int h = i % RG, c = i / RG;  // h: column
-    const size_t mh = (size_t)(m + h / G) * a.n_heads + g * G + h % G;
-    const uint32_t base = (uint32_t)((mh * a.max_chunks + c) * rec);
-    ml[0][c][h] = cload(pb, base);
-    ml[1][c][h] = cload(pb, base + 1);
-  }
-  __syncthreads();
-  if (tid < RG) {
-    const int h = tid;
-    float M = -INFINITY;
-    for (int c = 0; c < nch; ++c) M = fmaxf(M, ml[0][c][h]);
-    float den = 0.f;
-    for (int c = 0; c < nch; ++c) {
-      const float w = exp2f(ml[0][c][h] - M);
-      mw[c][h] = w;
-      den += w * ml[1][c][h];
-    }
-    const float inv = 1.0f / den;
-    for (int c = 0; c < nch; ++c) mw[c][h] *= inv;
-  }
-  __syncthreads();
-  for (int i = tid; i < RG * D; i += THREADS) {
-    const int h = i / D, e = i % D;
-    const size_t mh = (size_t)(m + h / G) * a.n_heads + g * G + h % G;
-    const uint32_t base = (uint32_t)((mh * a.max_chunks) * rec + 2 + e);
-    float O = 0.f;
-    int c = 0;
-    for (; c + 8 <= nch; c += 8) {
-      float o[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) o[u] = cload(pb, base + (uint32_t)((c + u) * rec));
-#pragma unroll
-      for (int u = 0; u < 8; ++u) O += mw[c + u][h] * o[u];
-    }
-    for (; c < nch; ++c) O += mw[c][h] * cload(pb, base + (uint32_t)(c * rec));
-    a.out[mh * D + e] = O;
   }
 }
 
@@ -378,7 +346,7 @@ template <int D>
 __global__ __launch_bounds__(D) void attn_merge_kernel(AttnDecodeArgs a) {
   constexpr int B = 16;
   const int head = blockIdx.x, m = blockIdx.y, e = threadIdx.x;
-  const int nch = (a.rows_param[m].pos + 1 + CHUNK - 1) / CHUNK;
+  const int nch = (a.rows_param[m].pos + 1 + a.chunk - 1) / a.chunk;
   const int rec = D + 2;
   const float* base = a.part + ((size_t)m * a.n_heads + head) * a.max_chunks * rec;
   float mx = -INFINITY, den = 0.f, O = 0.f;
@@ -421,8 +389,18 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(AttnDecodeArgs a) {
 
 }  // namespace
 
+int attn_decode_mfma_chunk(int max_ctx, int units, int n_cu) {
+  // about one workgroup per CU: chunks per (row group, KV head) unit
+  const int per = units >= n_cu ? 1 : n_cu / units;
+  int ch = (max_ctx + per - 1) / per;
+  ch = (ch + STEP - 1) / STEP * STEP;
+  while ((max_ctx + ch - 1) / ch > MAXCH) ch += STEP;
+  return ch;
+}
+
 hipError_t launch_attn_decode_mfma(const AttnDecodeArgs& a, hipStream_t stream) {
-  if (a.kv.is_f32 || a.n_heads % a.n_kv || a.n_heads / a.n_kv > 16 || a.max_chunks > MAXCH || a.kv.max_seq % 64)
+  if (a.kv.is_f32 || a.n_heads % a.n_kv || a.n_heads / a.n_kv > 16 || a.max_chunks > MAXCH || a.kv.max_seq % 64 ||
+      a.chunk < STEP || a.chunk % STEP || (a.max_chunks > 1 && !a.merge))
     return hipErrorInvalidValue;
   const int sh = a.share > 1 ? a.share : 1;
   if (sh > 1 && (a.qkv_raw || sh * (a.n_heads / a.n_kv) > 16)) return hipErrorInvalidValue;

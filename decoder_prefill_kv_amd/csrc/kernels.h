@@ -130,7 +130,7 @@ struct AttnDecodeArgs {
   const float* q;             // [M][n_heads][d] (normed, roped)
   KVDesc kv;
   int layer;
-  int chunk;                  // positions per workgroup (attn_decode_chunk())
+  int chunk;                  // positions per workgroup (attn_decode_chunk() / attn_decode_mfma_chunk())
   int max_chunks;             // grid.x
   float* part;                // [M][n_heads][max_chunks][d + 2]
   unsigned* counters;         // [M * n_kv]
@@ -162,8 +162,12 @@ struct AttnDecodeArgs {
 };
 hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t stream);
 int attn_decode_chunk();  // positions per decode-attention workgroup
-// same contract on matrix cores, fp16 caches only (attn_decode_mfma.hip)
+// same contract on matrix cores, fp16 caches only (attn_decode_mfma.hip):
+// a.chunk from attn_decode_mfma_chunk (a multiple of 256), a.merge set
+// whenever a.max_chunks > 1
 hipError_t launch_attn_decode_mfma(const AttnDecodeArgs& a, hipStream_t stream);
+// positions per workgroup for max_ctx over `units` (row group, KV head) pairs
+int attn_decode_mfma_chunk(int max_ctx, int units, int n_cu);
 
 // ---- misc
 hipError_t launch_rope_table(float* cos_t, float* sin_t, int max_seq, int d, double theta,

@@ -380,15 +380,16 @@ dpk_status attn_decode(dpk_model* md, int M, int max_ctx, const float* q, float*
   a.q = q;
   a.kv = md->kvd;
   a.layer = layer;
-  a.chunk = attn_decode_chunk();
+  a.share = (one_seq && !qkv_raw && !md->kvd.is_f32) ? 16 / (c.n_heads / c.n_kv_heads) : 1;
+  if (a.share > M) a.share = M;
+  a.chunk = md->kvd.is_f32 ? attn_decode_chunk()
+                           : attn_decode_mfma_chunk(max_ctx, (M + a.share - 1) / a.share * c.n_kv_heads, md->n_cu);
   a.max_chunks = (max_ctx + a.chunk - 1) / a.chunk;
   if (a.max_chunks > md->attn_chunks_cap) return fail(DPK_EINVAL, "attention chunk cap");
   a.part = md->attn_part;
   a.counters = md->attn_counters;
   a.out = out;
   a.scale = 1.0f / sqrtf((float)c.head_dim);
-  a.share = (one_seq && !qkv_raw && !md->kvd.is_f32) ? 16 / (c.n_heads / c.n_kv_heads) : 1;
-  if (a.share > M) a.share = M;
   a.merge = a.max_chunks > 1 || out16;  // a second launch merges the chunks
   if (out16) {
     if (md->kvd.is_f32) return fail(DPK_EINVAL, "internal: split attention output needs the fp16 cache");
