@@ -64,6 +64,16 @@ __global__ __launch_bounds__(THREADS, 2) void attn_prefill_kernel(AttnPrefillArg
       qf[s] = *(const f16x8*)(qp + 16 * s + 8 * hh);
       qlo[s] = *(const f16x8*)(qlp + 16 * s + 8 * hh);
     }
+    // fold the softmax scale (and log2 e) into q once: q c split again
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = ((float)qf[s][e] + (float)qlo[s][e]) * c;
+        const _Float16 h = (_Float16)x;
+        qf[s][e] = h;
+        qlo[s][e] = (_Float16)(x - (float)h);
+      }
   }
   f32x16 o[D / 32];
 #pragma unroll
@@ -128,18 +138,25 @@ __global__ __launch_bounds__(THREADS, 2) void attn_prefill_kernel(AttnPrefillArg
         s[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qlo[st], s[b], 0, 0, 0);
       }
     }
-    // mask + online softmax (log2 domain); lane key index = 8(v/4) + 4hh + v%4
+    // mask + online softmax (log2 domain; q carries the scale); lane key
+    // index = 8(v/4) + 4hh + v%4.  Only tiles that reach past this wave's
+    // first row (the diagonal) or past kend need the mask.
     float tmax = -INFINITY;
+    if (k0 + BKV - 1 > a.start + r0 || k0 + BKV > kend) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = k0 + b * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-        float x = s[b][v] * c;
-        if (key > qpos || key >= kend) x = -INFINITY;
-        s[b][v] = x;
-        tmax = fmaxf(tmax, x);
-      }
+        for (int v = 0; v < 16; ++v) {
+          const int key = k0 + b * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
+          if (key > qpos || key >= kend) s[b][v] = -INFINITY;
+          tmax = fmaxf(tmax, s[b][v]);
+        }
+    } else {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, s[b][v]);
+    }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const float mnew = fmaxf(mrun, tmax);
     const float alpha = (mrun == -INFINITY) ? 0.f : exp2f(mrun - mnew);
