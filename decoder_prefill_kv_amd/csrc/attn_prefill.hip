@@ -166,7 +166,10 @@ __global__ __launch_bounds__(THREADS, 2) void attn_prefill_kernel(AttnPrefillArg
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float p = (s[b][v] == -INFINITY) ? 0.f : exp2f(s[b][v] - mnew);
+        // mnew is finite (key 0 is visible to every row, and the first tile
+        // a wave computes is k0 = 0), so a masked -inf gives exactly 0; the
+        // hardware exp2 (results below 2^-126 flush to 0, immaterial here)
+        const float p = __builtin_amdgcn_exp2f(s[b][v] - mnew);
         psum += p;
         const _Float16 ph = (_Float16)p;
         pf[b][v >> 3][v & 7] = ph;
