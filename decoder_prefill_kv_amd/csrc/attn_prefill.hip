@@ -165,15 +165,20 @@ __global__ __launch_bounds__(THREADS, 2) void attn_prefill_kernel(AttnPrefillArg
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
+      for (int v = 0; v < 16; v += 2) {
         // mnew is finite (key 0 is visible to every row, and the first tile
         // a wave computes is k0 = 0), so a masked -inf gives exactly 0; the
         // hardware exp2 (results below 2^-126 flush to 0, immaterial here)
-        const float p = __builtin_amdgcn_exp2f(s[b][v] - mnew);
-        psum += p;
-        const _Float16 ph = (_Float16)p;
-        pf[b][v >> 3][v & 7] = ph;
-        pl[b][v >> 3][v & 7] = (_Float16)(p - (float)ph);
+        const float p0 = __builtin_amdgcn_exp2f(s[b][v] - mnew), p1 = __builtin_amdgcn_exp2f(s[b][v + 1] - mnew);
+        psum += p0 + p1;
+        // hi: two at once, rounded toward zero (lo = p - hi takes the rest, so
+        // hi + lo keeps ~22 bits either way)
+        const auto h2 = __builtin_amdgcn_cvt_pkrtz(p0, p1);
+        const auto l2 = __builtin_amdgcn_cvt_pkrtz(p0 - (float)h2[0], p1 - (float)h2[1]);
+        pf[b][v >> 3][v & 7] = h2[0];
+        pf[b][v >> 3][(v & 7) + 1] = h2[1];
+        pl[b][v >> 3][v & 7] = l2[0];
+        pl[b][v >> 3][(v & 7) + 1] = l2[1];
       }
     psum += __shfl_xor(psum, 32, 64);
     lrun = lrun * alpha + psum;
