@@ -113,6 +113,111 @@ __global__ void rmsnorm_rows_kernel(int H, const float* x, int ldx, const void* 
   }
 }
 
+// Prefill variant of rmsnorm_rows (bf16 gain, fp16 output, H = NV * 2048):
+// each thread holds 8 consecutive columns per 2048 in registers (one read of
+// the row), 16-byte loads and stores.  mode 1: fp16; 2: fp16 hi in [0, H),
+// lo = v - hi in [H, 2H).
+template <int NV>
+__global__ __launch_bounds__(256) void rmsnorm_vec_kernel(int H, const float* x, int ldx, const uint16_t* g,
+                                                         float eps, _Float16* y, int mode, int ldy) {
+  __shared__ float red[8];
+  const int m = blockIdx.x, tid = threadIdx.x;
+  const float* xr = x + (size_t)m * ldx;
+  float v[NV][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int k = (j * 256 + tid) * 8;
+    const float4 a = *(const float4*)(xr + k), b = *(const float4*)(xr + k + 4);
+    v[j][0] = a.x; v[j][1] = a.y; v[j][2] = a.z; v[j][3] = a.w;
+    v[j][4] = b.x; v[j][5] = b.y; v[j][6] = b.z; v[j][7] = b.w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += v[j][e] * v[j][e];
+  }
+  ss = block_sum(ss, red);
+  const float r = rsqrtf(ss / (float)H + eps);
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int k = (j * 256 + tid) * 8;
+    const uint4 gw = *(const uint4*)(g + k);
+    const uint32_t gg[4] = {gw.x, gw.y, gw.z, gw.w};
+    f16x8 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float gk = (e & 1) ? bf16hi_to_f32(gg[e / 2]) : bf16lo_to_f32(gg[e / 2]);
+      const float t = v[j][e] * r * gk;
+      hi[e] = (_Float16)t;
+      lo[e] = (_Float16)(t - (float)hi[e]);
+    }
+    _Float16* yr = y + (size_t)m * ldy;
+    *(f16x8*)(yr + k) = hi;
+    if (mode == 2) *(f16x8*)(yr + H + k) = lo;
+  }
+}
+
+// Prefill variant of qk_rope_kv (fp16 hi / lo q planes, bf16 gains, d = 128,
+// rows at consecutive positions of one sequence): grid (ceil(M / 64), n_heads
+// + 2 n_kv), 4 waves of 16 rows each.  A value head goes through LDS so that
+// its transposed slab rows are written 64 positions at a time.
+__global__ __launch_bounds__(256) void qk_rope_kv_rows_kernel(const float* qkv, int M, int n_heads, int n_kv,
+                                                            const uint16_t* qn, const uint16_t* kn, float eps,
+                                                            const float* rope_cos, const float* rope_sin,
+                                                            const RowParam* rp, _Float16* q_out, KVDesc kv,
+                                                            int layer) {
+  constexpr int D = 128, HD = 64;
+  __shared__ _Float16 vt[D][64 + 2];
+  const int blk = blockIdx.x, hh = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int ld = (n_heads + 2 * n_kv) * D;
+  const int m0 = blk * 64;
+  const int rows = min(64, M - m0);
+  const RowParam r0 = rp[m0];
+  if (hh >= n_heads + n_kv) {  // v head -> V^T slab
+    const int vh = hh - n_heads - n_kv;
+    for (int i = tid; i < rows * D; i += 256) {
+      const int rr = i / D, e = i % D;
+      vt[e][rr] = (_Float16)qkv[(size_t)(m0 + rr) * ld + (size_t)hh * D + e];
+    }
+    __syncthreads();
+    _Float16* vb = (_Float16*)kv.base + kv_slab(kv, r0.seq, layer, 1, vh);
+    for (int i = tid; i < D * 64; i += 256) {
+      const int e = i / 64, rr = i % 64;
+      if (rr < rows) vb[(size_t)e * kv.max_seq + r0.pos + rr] = vt[e][rr];
+    }
+    return;
+  }
+  const bool is_q = hh < n_heads;
+  const uint16_t* g = is_q ? qn : kn;
+  for (int rr = wave; rr < rows; rr += 4) {
+    const int m = m0 + rr;
+    const float* src = qkv + (size_t)m * ld + (size_t)hh * D;
+    const float a = src[lane], b = src[lane + HD];
+    float scale = 1.f;
+    if (g) scale = rsqrtf(wave_sum(a * a + b * b) / (float)D + eps);
+    float x1 = a * scale, x2 = b * scale;
+    if (g) {
+      x1 *= bf16_to_f32(g[lane]);
+      x2 *= bf16_to_f32(g[lane + HD]);
+    }
+    const int pos = r0.pos + rr;
+    const float c = rope_cos[(size_t)pos * HD + lane], sn = rope_sin[(size_t)pos * HD + lane];
+    const float y1 = x1 * c - x2 * sn, y2 = x2 * c + x1 * sn;
+    if (is_q) {
+      const size_t o = ((size_t)m * n_heads + hh) * D;
+      _Float16* qh = q_out;
+      _Float16* ql = q_out + (size_t)M * n_heads * D;
+      const _Float16 h1 = (_Float16)y1, h2 = (_Float16)y2;
+      qh[o + lane] = h1;
+      qh[o + lane + HD] = h2;
+      ql[o + lane] = (_Float16)(y1 - (float)h1);
+      ql[o + lane + HD] = (_Float16)(y2 - (float)h2);
+    } else {
+      _Float16* kb = (_Float16*)kv.base + kv_slab(kv, r0.seq, layer, 0, hh - n_heads) + (size_t)pos * D;
+      kb[lane] = (_Float16)y1;
+      kb[lane + HD] = (_Float16)y2;
+    }
+  }
+}
+
 // grid (M, n_heads + 2*n_kv); one workgroup of 64 threads per (row, head)
 __global__ void qk_rope_kv_kernel(const float* qkv, int n_heads, int n_kv, int d, int qk_norm, const void* qn,
                                   const void* kn, int g_is_f32, float eps, const float* rope_cos,
@@ -277,6 +382,17 @@ hipError_t launch_embed(int M, int H, int fmt, const void* table, const uint16_t
 
 hipError_t launch_rmsnorm_rows(int M, int H, const float* x, int ldx, const void* g, int g_is_f32, float eps,
                                void* y, int y_is_f16, int ldy, hipStream_t stream) {
+  if (!g_is_f32 && g && y_is_f16 && H % 2048 == 0 && H <= 4 * 2048 && ldx % 4 == 0 && ldy % 8 == 0) {
+    const uint16_t* gb = (const uint16_t*)g;
+    _Float16* yb = (_Float16*)y;
+    switch (H / 2048) {
+      case 1: launch(rmsnorm_vec_kernel<1>, dim3(M), dim3(256), 0, stream, H, x, ldx, gb, eps, yb, y_is_f16, ldy); break;
+      case 2: launch(rmsnorm_vec_kernel<2>, dim3(M), dim3(256), 0, stream, H, x, ldx, gb, eps, yb, y_is_f16, ldy); break;
+      case 3: launch(rmsnorm_vec_kernel<3>, dim3(M), dim3(256), 0, stream, H, x, ldx, gb, eps, yb, y_is_f16, ldy); break;
+      default: launch(rmsnorm_vec_kernel<4>, dim3(M), dim3(256), 0, stream, H, x, ldx, gb, eps, yb, y_is_f16, ldy); break;
+    }
+    return hipGetLastError();
+  }
   launch(rmsnorm_rows_kernel, dim3(M), dim3(256), 0, stream, H, x, ldx, g, g_is_f32, eps, y, y_is_f16,
                      ldy);
   return hipGetLastError();
@@ -286,6 +402,13 @@ hipError_t launch_qk_rope_kv(int M, const float* qkv, int n_heads, int n_kv, int
                              const void* kn, int g_is_f32, float eps, const float* rope_cos, const float* rope_sin,
                              const RowParam* rp, void* q_out, int q_is_f16, KVDesc kv, int layer,
                              hipStream_t stream) {
+  if (q_is_f16 == 2 && d == 128 && !g_is_f32 && !kv.is_f32 && (qk_norm ? (qn && kn) : true)) {
+    // (rows at consecutive positions of one sequence: the prefill block)
+    launch(qk_rope_kv_rows_kernel, dim3((M + 63) / 64, n_heads + 2 * n_kv), dim3(256), 0, stream, qkv, M, n_heads,
+           n_kv, qk_norm ? (const uint16_t*)qn : nullptr, qk_norm ? (const uint16_t*)kn : nullptr, eps, rope_cos,
+           rope_sin, rp, (_Float16*)q_out, kv, layer);
+    return hipGetLastError();
+  }
   launch(qk_rope_kv_kernel, dim3(M, n_heads + 2 * n_kv), dim3(64), 0, stream, qkv, n_heads, n_kv, d,
                      qk_norm, qn, kn, g_is_f32, eps, rope_cos, rope_sin, rp, q_out, q_is_f16, kv, layer);
   return hipGetLastError();
