@@ -187,10 +187,20 @@ __global__ __launch_bounds__(256) void qk_rope_kv_rows_kernel(const float* qkv, 
   }
   const bool is_q = hh < n_heads;
   const uint16_t* g = is_q ? qn : kn;
-  for (int rr = wave; rr < rows; rr += 4) {
+  // this wave's 16 rows loaded first (clamped: rows past M repeat the last)
+  float av[16], bv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float* src = qkv + (size_t)(m0 + min(wave + 4 * i, rows - 1)) * ld + (size_t)hh * D;
+    av[i] = src[lane];
+    bv[i] = src[lane + HD];
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int rr = wave + 4 * i;
+    if (rr >= rows) break;
     const int m = m0 + rr;
-    const float* src = qkv + (size_t)m * ld + (size_t)hh * D;
-    const float a = src[lane], b = src[lane + HD];
+    const float a = av[i], b = bv[i];
     float scale = 1.f;
     if (g) scale = rsqrtf(wave_sum(a * a + b * b) / (float)D + eps);
     float x1 = a * scale, x2 = b * scale;
