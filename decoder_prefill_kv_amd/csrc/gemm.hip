@@ -51,12 +51,24 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs a) {
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * BM;
+  // tile (bx, by) and split bz of this workgroup.  xcd_blocks: consecutive
+  // workgroups go to the 8 XCDs in turn, so workgroup L runs on XCD L % 8;
+  // XCD k then takes the 4 x 4 tile block k with all its splits, which its
+  // L2 shares (A rows across the block's columns, B rows across its rows).
+  int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
+  if (a.xcd_blocks) {
+    const int L = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int k = L & 7, s = L >> 3, gx = gridDim.x / 4;
+    bz = s % gridDim.z;
+    bx = 4 * (k % gx) + (s / gridDim.z) % 4;
+    by = 4 * (k / gx) + s / (gridDim.z * 4);
+  }
+  const int m0 = by * BM;
   // SWIGLU: the tile's B rows are 128 gate rows then the same 128 up rows
-  const int n0 = (EPI == GEMM_SWIGLU_F16) ? blockIdx.x * (BN / 2) : blockIdx.x * BN;
+  const int n0 = (EPI == GEMM_SWIGLU_F16) ? bx * (BN / 2) : bx * BN;
   const int nk_all = a.K / BK;
   const int nks = SPLIT ? nk_all / a.splits : nk_all;
-  const int kt0 = SPLIT ? blockIdx.z * nks : 0;
+  const int kt0 = SPLIT ? bz * nks : 0;
 
   // global load assignment: 8 threads per 64-half row, 32 rows per pass.
   // Row block i of a pass is a uniform offset from the thread's first row,
@@ -222,11 +234,11 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs a) {
     // partial tile: value pair (v, v+1) of block (i, j) of thread tid sits at
     // float offset ((((i * 4 + j) * 8 + v / 2) * THREADS + tid) * 2, so each
     // 8-byte coherent store or load of a wave covers 512 contiguous bytes
-    const int tile = blockIdx.y * gridDim.x + blockIdx.x;
+    const int tile = by * gridDim.x + bx;
     const int S = a.splits;
     float* wsp = a.ws + (size_t)tile * S * (BM * BN);
     const coh_buf wsb = coh_buffer(wsp);
-    const uint32_t own = (uint32_t)(blockIdx.z * (BM * BN) + tid * 2);
+    const uint32_t own = (uint32_t)(bz * (BM * BN) + tid * 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -340,10 +352,13 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
     if (!a.ws || !a.counters || (a.K / BK) % S || (size_t)grid.x * grid.y * S > GEMM_WS_TILES)
       return hipErrorInvalidValue;
   }
+  GemmArgs b = a;
+  // one round of exactly 8 blocks of 4 x 4 tiles (with all their splits)
+  b.xcd_blocks = (grid.x % 4 == 0 && grid.y % 4 == 0 && (grid.x / 4) * (grid.y / 4) == 8) ? 1 : 0;
   switch (a.epi) {
-    case GEMM_STORE_F32: launch_epi<GEMM_STORE_F32>(a, grid, stream); break;
-    case GEMM_ADD_F32: launch_epi<GEMM_ADD_F32>(a, grid, stream); break;
-    case GEMM_SWIGLU_F16: launch_epi<GEMM_SWIGLU_F16>(a, grid, stream); break;
+    case GEMM_STORE_F32: launch_epi<GEMM_STORE_F32>(b, grid, stream); break;
+    case GEMM_ADD_F32: launch_epi<GEMM_ADD_F32>(b, grid, stream); break;
+    case GEMM_SWIGLU_F16: launch_epi<GEMM_SWIGLU_F16>(b, grid, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -218,6 +218,8 @@ struct GemmArgs {
   float* C; int ldc;              // STORE/ADD
   _Float16* C16; int ldc16;       // SWIGLU
   int splits;                     // split-K factor (<= 1: none)
+  int xcd_blocks;                 // set by launch_gemm: workgroups remapped so each of the 8 XCDs
+                                  //   (workgroup i runs on XCD i % 8) takes a 4 x 4 tile block
   float* ws;                      // split-K partial tiles [tiles][splits][256 * 256]
   unsigned* counters;             // split-K arrival counters [tiles], zero between launches
 };
