@@ -97,6 +97,27 @@ def copy_probe(nbytes):
     print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
 
 
+def membench(nbytes=2 << 30, reps=5):
+    """Achievable HBM rate on this GPU for context: a plain device-to-device
+    copy of nbytes (read + write counted), best of reps."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = 1e30
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) / 1e3)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"kind": "device copy (read + write)", "bytes": 2 * nbytes, "GBps": round(2 * nbytes / best / 1e9, 1),
+            "frac_of_peak": round(2 * nbytes / best / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def bench_verify(dpk, cfg, w, seed, flags, K=5, rounds=24, warm=4):
     """Speculative verify of K drafts (M = K + 1 rows) against the KV cache of
     an 8192-token prompt: passes/s, and the ratio to one decode step at the
@@ -304,6 +325,9 @@ def main():
         extra["batch16"] = bench_batch16(dpk, cfg, w, args.seed, flags)
         log("[bench] batch16: %s" % extra["batch16"])
 
+    mem = membench()
+    log("[bench] membench: %s" % mem)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
@@ -338,6 +362,7 @@ def main():
         "roofline_prefill": roof_prefill,
         "kernels": kernels,
         "cpu_baseline": cpu,
+        "membench": mem,
     }
     out.update(extra)
     print(json.dumps(out), flush=True)
