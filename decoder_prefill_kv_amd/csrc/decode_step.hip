@@ -1,4 +1,5 @@
-// A whole decode step in one persistent launch (gfx950, bf16 weights).
+// A whole decode step in one persistent launch (gfx950, bf16 or MLX 4-bit
+// weights).
 //
 // The step is the single-token decode order of the Butter architecture notes
 // ("SINGLE-TOKEN DECODE": gather, then per layer norm / q,k,v / rope at the
@@ -120,7 +121,14 @@ DPK_DEV void embed_phase(const MegaArgs& a, int wg, int nwg) {
           tok = 0;
         }
         const int col = n * 16 + tid;
-        const float v = bf16_to_f32(((const uint16_t*)a.emb)[(size_t)tok * a.H + col]);
+        float v;
+        if (a.fmt == W_Q4) {  // MLX 4-bit: w = s * c + b per 64 columns
+          const uint32_t word = ((const uint32_t*)a.emb)[(size_t)tok * (a.H / 8) + col / 8];
+          const size_t gi = (size_t)tok * (a.H / 64) + col / 64;
+          v = bf16_to_f32(a.emb_sc[gi]) * (float)((word >> (4 * (col & 7))) & 0xFu) + bf16_to_f32(a.emb_bi[gi]);
+        } else {
+          v = bf16_to_f32(((const uint16_t*)a.emb)[(size_t)tok * a.H + col]);
+        }
         cstore(coh_buffer(a.h), (uint32_t)(m * a.H + col), v);
         float ss = v * v;
         ss += __shfl_xor(ss, 1, 64);
@@ -176,9 +184,11 @@ DPK_DEV void attn_phase(const MegaArgs& a, int layer, const uint16_t* qn, const 
 
   // K / V^T fragments of the item's positions for this wave, and the RoPE /
   // QK-norm constants of the row (none of it depends on the previous phase)
+  RowParam rp_it{};  // the row parameters of the prefetched item
   auto prefetch = [&](int it) {
     const int chunk = it % a.max_chunks, g = (it / a.max_chunks) % a.n_kv, m = it / (a.max_chunks * a.n_kv);
-    const RowParam rp = a.rp[m];
+    rp_it = a.rp[m];
+    const RowParam rp = rp_it;
     const int ctx = rp.pos + 1;
     const int c0 = chunk * ACH, c1 = min(ctx, c0 + ACH);
     const int wp0 = c0 + 32 * wave;
@@ -203,8 +213,8 @@ DPK_DEV void attn_phase(const MegaArgs& a, int layer, const uint16_t* qn, const 
     sn = a.rope_sin[(size_t)rp.pos * (D / 2) + lane];
     const uint16_t* gn = wave < G ? qn : kn;
     const uint16_t* gp = gn ? gn : (const uint16_t*)a.rope_cos;
-    gr0 = gp[lane];
-    gr1 = gp[lane + 64];
+    gr0 = gemv_detail::gmem(gp)[lane];
+    gr1 = gemv_detail::gmem(gp)[lane + 64];
   };
 
   int it = wg;
@@ -214,7 +224,7 @@ DPK_DEV void attn_phase(const MegaArgs& a, int layer, const uint16_t* qn, const 
   for (; it < n_items; it += nwg) {
     if (it != wg) prefetch(it);
     const int chunk = it % a.max_chunks, g = (it / a.max_chunks) % a.n_kv, m = it / (a.max_chunks * a.n_kv);
-    const RowParam rp = a.rp[m];
+    const RowParam rp = rp_it;
     const int ctx = rp.pos + 1;
     const int nch = (ctx + ACH - 1) / ACH;
     if (chunk >= nch) continue;  // uniform over the workgroup
@@ -439,8 +449,13 @@ DPK_DEV void attn_phase(const MegaArgs& a, int layer, const uint16_t* qn, const 
   }
 }
 
-template <int G>
+// FMT: weight format of every GEMV.  SMALL: each wave reduces 128 columns per
+// iteration (so rows of 1024, 2048, 3072 ... columns split over eight waves)
+// and the QKV projection goes in 16-row tiles, which gives a narrow model's
+// QKV about one tile per workgroup.
+template <int G, int FMT, bool SMALL>
 __global__ __launch_bounds__(MT, 1) void decode_step_kernel(MegaArgs a) {
+  constexpr int KI = SMALL ? 128 : 0, TQ = SMALL ? 1 : 2;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int wg = blockIdx.x, nwg = gridDim.x;
   Barrier bar{a.bar, a.bar + MEGA_BAR_ABORT, (unsigned)nwg, 0u};
@@ -461,21 +476,36 @@ __global__ __launch_bounds__(MT, 1) void decode_step_kernel(MegaArgs a) {
     mark(closing);
   };
   using gemv_detail::gemv_body;
+  // The layer's table entry (and at the end the lm_head's arguments) is
+  // copied into LDS before its first phase: the phases then read their
+  // arguments from LDS, where a read never waits for the weight loads in
+  // flight (a reload from device memory would wait for every vector load
+  // issued before it).  The copy overwrites the previous layer's entry only
+  // after every wave has finished that layer (the barrier below).
+  MegaLayer* const Ls = (MegaLayer*)(lds + a.lds_args);
+  GemvArgs* const Hs = (GemvArgs*)(Ls + 1);
+  auto stage = [&](void* dst, const void* src, int bytes) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < bytes / 4; i += MT) ((uint32_t*)dst)[i] = ((const uint32_t*)src)[i];
+    __syncthreads();
+  };
   embed_phase(a, wg, nwg);
   for (int l = 0; l < a.n_layers; ++l) {
-    const MegaLayer& L = a.layers[l];
-    gemv_body<W_BF16, 2, 8, true>(L.qkv, a.M, lds, wg, nwg, sync);
+    stage(Ls, a.layers + l, (int)sizeof(MegaLayer));
+    const MegaLayer& L = *Ls;
+    gemv_body<FMT, TQ, 8, true, false, KI>(L.qkv, a.M, lds, wg, nwg, sync);
     closing = MP_QKV;
     attn_phase<G>(a, l, L.qn, L.kn, lds, wg, nwg, sync);
     closing = MP_ATTN;
-    gemv_body<W_BF16, 1, 8, true>(L.o, a.M, lds, wg, nwg, sync);
+    gemv_body<FMT, 1, 8, true, false, KI>(L.o, a.M, lds, wg, nwg, sync);
     closing = MP_O;
-    gemv_body<W_BF16, 2, 8, true>(L.gu, a.M, lds, wg, nwg, sync);
+    gemv_body<FMT, 2, 8, true, false, KI>(L.gu, a.M, lds, wg, nwg, sync);
     closing = MP_GATEUP;
-    gemv_body<W_BF16, 1, 8, true>(L.down, a.M, lds, wg, nwg, sync);
+    gemv_body<FMT, 1, 8, true, false, KI>(L.down, a.M, lds, wg, nwg, sync);
     closing = MP_DOWN;
   }
-  gemv_body<W_BF16, 1, 8, true>(a.head, a.M, lds, wg, nwg, sync);
+  stage(Hs, &a.head, (int)sizeof(GemvArgs));
+  gemv_body<FMT, 1, 8, true, false, KI>(*Hs, a.M, lds, wg, nwg, sync);
   grid_exit(bar, a.bar + MEGA_BAR_EXIT, a.err);
   if (tr) {
     mark(MP_HEAD);
@@ -483,18 +513,26 @@ __global__ __launch_bounds__(MT, 1) void decode_step_kernel(MegaArgs a) {
   }
 }
 
-template <int G>
-const void* mega_kernel_ptr() {
-  return (const void*)decode_step_kernel<G>;
-}
-
-const void* mega_kernel_for(int G) {
-  switch (G) {
-    case 1: return mega_kernel_ptr<1>();
-    case 2: return mega_kernel_ptr<2>();
-    case 4: return mega_kernel_ptr<4>();
-    default: return nullptr;
+// Built variants: bf16 at 256 columns per iteration for G = 1, 2, 4; bf16
+// and 4-bit at 128 columns for G = 2, 4.
+const void* mega_kernel_for(int G, int fmt, bool small) {
+  if (fmt == W_BF16 && !small) {
+    switch (G) {
+      case 1: return (const void*)decode_step_kernel<1, W_BF16, false>;
+      case 2: return (const void*)decode_step_kernel<2, W_BF16, false>;
+      case 4: return (const void*)decode_step_kernel<4, W_BF16, false>;
+      default: return nullptr;
+    }
   }
+  if (!small) return nullptr;
+  if (fmt == W_BF16) {
+    if (G == 2) return (const void*)decode_step_kernel<2, W_BF16, true>;
+    if (G == 4) return (const void*)decode_step_kernel<4, W_BF16, true>;
+  } else if (fmt == W_Q4) {
+    if (G == 2) return (const void*)decode_step_kernel<2, W_Q4, true>;
+    if (G == 4) return (const void*)decode_step_kernel<4, W_Q4, true>;
+  }
+  return nullptr;
 }
 
 }  // namespace
@@ -507,9 +545,9 @@ int mega_threads() { return MT; }
 int mega_attn_chunk() { return ACH; }
 
 // Workgroups per CU the kernel can keep resident with lds bytes of LDS (0 if
-// the kernel does not exist for G).
-int mega_occupancy(int G, size_t lds) {
-  const void* k = mega_kernel_for(G);
+// the kernel does not exist for G, fmt, small).
+int mega_occupancy(int G, int fmt, bool small, size_t lds) {
+  const void* k = mega_kernel_for(G, fmt, small);
   if (!k) return 0;
   int nb = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k, MT, lds) != hipSuccess) return 0;
@@ -517,7 +555,7 @@ int mega_occupancy(int G, size_t lds) {
 }
 
 hipError_t launch_decode_step(const MegaArgs& a, int G, int n_wg, size_t lds, hipStream_t stream) {
-  const void* k = mega_kernel_for(G);
+  const void* k = mega_kernel_for(G, a.fmt, a.small != 0);
   if (!k || n_wg < 1 || a.M < 1 || a.M > 16) return hipErrorInvalidValue;
   MegaArgs copy = a;
   void* args[] = {&copy};

@@ -66,9 +66,13 @@ int gemv_waves(int K, int tiles, int fmt) {
   return (K % (8 * per_iter) == 0 && K / 8 >= per_iter) ? 8 : 4;
 }
 
-size_t gemv_lds_bytes(int M, int K, int tiles, int fmt) {
+size_t gemv_lds_bytes_waves(int M, int K, int tiles, int fmt, int waves) {
   int a, b, c, d;
-  return (size_t)gemv_lds_layout(M, K, 16 * tiles, fmt, gemv_waves(K, tiles, fmt), &a, &b, &c, &d);
+  return (size_t)gemv_lds_layout(M, K, 16 * tiles, fmt, waves, &a, &b, &c, &d);
+}
+
+size_t gemv_lds_bytes(int M, int K, int tiles, int fmt) {
+  return gemv_lds_bytes_waves(M, K, tiles, fmt, gemv_waves(K, tiles, fmt));
 }
 
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {

@@ -30,6 +30,15 @@
 namespace dpk {
 namespace gemv_detail {
 
+// p as a global-memory pointer.  Arguments that a persistent caller stages in
+// LDS hold their pointers as plain values the compiler cannot trace to global
+// memory; without this it would use flat accesses, which also count against
+// the LDS wait counter.
+template <typename T>
+DPK_DEV __attribute__((address_space(1))) T* gmem(T* p) {
+  return (__attribute__((address_space(1))) T*)p;
+}
+
 __host__ __device__ inline int gemv_lds_layout(int M, int K, int RB, int fmt, int WAVES, int* xs_off,
                                                 int* xsum_off, int* red_off, int* misc_off) {
   const int kq = K / WAVES, xstride = kq + 8;
@@ -60,7 +69,9 @@ __host__ __device__ inline int gemv_lds_layout(int M, int K, int RB, int fmt, in
 // XG: the activations come ready-made from global memory as bf16 hi / lo
 // rows (a.xb_hi / a.xb_lo in the xg_index layout, norm gain already applied)
 // instead of being staged in LDS, so M is not limited by LDS (bf16 weights).
-template <int FMT, int T, int WAVES, bool COH, bool XG = false, typename Pre>
+// KI: columns a wave reduces per iteration (0: the default for T; 128 lets
+// eight waves split rows of 1024, 2048, 3072 ... columns).
+template <int FMT, int T, int WAVES, bool COH, bool XG = false, int KI = 0, typename Pre>
 DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const int wg, const int nwg, Pre&& pre) {
   static_assert(!XG || FMT == W_BF16, "ready-made activations are for bf16 weights");
   constexpr int RB = 16 * T;
@@ -106,8 +117,9 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
 
   // bf16: k-steps of 32 per iteration (XG holds its activations in registers
   // as well, so a one-tile XG wave loads half as much per iteration)
-  constexpr int U = (XG && T == 1) ? 4 : 8 / T;
-  constexpr int GU = 4 / T > 0 ? 4 / T : 1;  // 4-bit: groups of 64 per iteration
+  constexpr int U = KI ? KI / 32 : (XG && T == 1) ? 4 : 8 / T;
+  constexpr int GU = KI ? KI / 64 : 4 / T > 0 ? 4 / T : 1;  // 4-bit: groups of 64 per iteration
+  static_assert(KI % 64 == 0, "whole 4-bit groups per iteration");
   const int nit = (FMT == W_BF16) ? kq / (32 * U) : kq / (64 * GU);
   const unsigned char* wp[T];   // this wave's stream inside each 16-row tile
   const unsigned char* sbp[T];  // 4-bit: scale/bias stream
@@ -141,7 +153,7 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
     for (int t = 0; t < T; ++t)
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        b[t][u] = __builtin_nontemporal_load((const u32x4*)(wp[t] + (size_t)(it * U + u) * 1024));
+        b[t][u] = __builtin_nontemporal_load(gmem((const u32x4*)(wp[t] + (size_t)(it * U + u) * 1024)));
     if constexpr (XG) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -155,14 +167,25 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
     for (int t = 0; t < T; ++t)
 #pragma unroll
       for (int u = 0; u < GU; ++u) {
-        c[t][u] = __builtin_nontemporal_load((const u32x2*)(wp[t] + (size_t)(it * GU + u) * 512));
-        sv[t][u] = __builtin_nontemporal_load((const u32x4*)(sbp[t] + (size_t)(it * GU + u) * 64));
+        c[t][u] = __builtin_nontemporal_load(gmem((const u32x2*)(wp[t] + (size_t)(it * GU + u) * 512)));
+        sv[t][u] = __builtin_nontemporal_load(gmem((const u32x4*)(sbp[t] + (size_t)(it * GU + u) * 64)));
       }
   };
 
   // ---- first tile's first two iterations of weights, before x is read
   int tile = wg;
   bool two = false;  // iterations 0 and 1 of the current tile are already loading
+  // residual epilogue: element tid of the tile's h (final before this GEMV
+  // starts: only the workgroup that owns a tile writes it) is loaded with the
+  // tile's first weights, so the epilogue does not wait for it
+  const bool h_early = a.epi == EPI_RESID && M * RB <= THREADS;
+  float h_tile = 0.f;
+  auto load_h = [&](int t) {
+    if (h_early && tid < M * RB) {
+      const uint32_t hi = (uint32_t)((tid / RB) * a.ldo + t * RB + tid % RB);
+      h_tile = COH ? cload(coh_buffer(a.out), hi) : gmem(a.out)[hi];
+    }
+  };
   auto first_loads = [&]() {
     if constexpr (FMT == W_BF16) {
       load_bf(b0, xh0, xl0, 0);
@@ -177,6 +200,7 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
     if (tile < n_tiles) {
       set_tile(tile);
       first_loads();
+      load_h(tile);
     }
   });
   // no row tile here: nothing to stage or finish (the head's argmax needs
@@ -185,9 +209,14 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
 
   // ---- row norm scales from the producer's per-tile sums of squares (each
   // wave computes them itself, so no barrier separates them from x's loads;
-  // XG applies wave 0's copy to the reduced outputs)
+  // XG applies wave 0's copy to the reduced outputs).  own_rs (persistent
+  // step, whole rows here): the scale comes from x itself instead -- each
+  // wave's part of every row's sum of squares goes to misc and the reduced
+  // outputs are scaled -- so x is the only thing this GEMV waits for.
   float* rsw = misc + 64 + 16 * wave;
-  if (XG && a.sq_in) {  // rows spread over the waves, one shared copy
+  const bool own_rs = COH && !XG && a.sq_in && KO == 0 && KF == K;
+  if (own_rs) {
+  } else if (XG && a.sq_in) {  // rows spread over the waves, one shared copy
     for (int m = wave; m < M; m += WAVES) {
       float s = 0.f;
       for (int b = lane; b < a.sq_nb; b += 64) s += a.sq_in[m * a.sq_nb + b];
@@ -204,10 +233,10 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
     }
   }
   if constexpr (!XG) {
-  // ---- prologue: this wave's K part of x' -> bf16 hi/lo (once per workgroup)
-  for (int i = lane; i < M * (kq / 8); i += 64) {
-    const int m = i / (kq / 8);
-    const int kl = (i % (kq / 8)) * 8;
+  // ---- prologue: this wave's K part of x' -> bf16 hi/lo (once per workgroup);
+  // stage(m, kl) does columns kl .. kl + 7 of row m and returns their sum of
+  // squares (before the gain)
+  auto stage = [&](const int m, const int kl) -> float {
     const float* xp = a.x + (size_t)m * a.ldx + KO + k0 + kl;
     float v[8];
     if constexpr (COH) {
@@ -220,16 +249,19 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
       v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
       v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
     }
-    const float r = a.sq_in ? rsw[m] : 1.0f;
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+    const float r = (a.sq_in && !own_rs) ? rsw[m] : 1.0f;
     if (a.gain) {
-      const uint4 g = *(const uint4*)(a.gain + KO + k0 + kl);
-      const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
+      const u32x4 g = *gmem((const u32x4*)(a.gain + KO + k0 + kl));
+      const uint32_t gw[4] = {g[0], g[1], g[2], g[3]};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         v[2 * e] *= r * bf16lo_to_f32(gw[e]);
         v[2 * e + 1] *= r * bf16hi_to_f32(gw[e]);
       }
-    } else if (a.sq_in) {
+    } else if (a.sq_in && !own_rs) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] *= r;
     }
@@ -254,6 +286,17 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
       s += __shfl_xor(s, 4, 64);
       if ((kl & 63) == 0) xsum[m * ng + (k0 + kl) / 64] = s;
     }
+    return ss;
+  };
+  if (own_rs) {  // this wave's part of row m's sum of squares -> misc[64 + m * WAVES + wave]
+    for (int m = 0; m < M; ++m) {
+      float ss = 0.f;
+      for (int j = lane; j < kq / 8; j += 64) ss += stage(m, 8 * j);
+      ss = wave_sum(ss);
+      if (lane == 0) misc[64 + m * WAVES + wave] = ss;
+    }
+  } else {
+    for (int i = lane; i < M * (kq / 8); i += 64) (void)stage(i / (kq / 8), (i % (kq / 8)) * 8);
   }
   lds_barrier();
   }
@@ -330,83 +373,99 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
     best_v[m] = -INFINITY;
     best_i[m] = 0x7fffffff;
   }
-  auto finish_tile = [&](const int tile, const f32x4 (&acc)[T]) {
-    // ---- sum the waves' K parts: D[n][m] lane layout rows 4 j4 + v, column r16
+  // sum of WAVES consecutive floats of LDS (16-byte aligned)
+  auto lds_sum = [&](const float* p) -> float {
+    if constexpr (WAVES % 4 == 0) {
+      f32x4 s4 = *(const f32x4*)p;
+#pragma unroll
+      for (int w = 4; w < WAVES; w += 4) s4 += *(const f32x4*)(p + w);
+      return (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    } else {
+      float s1 = 0.f;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) s1 += p[w];
+      return s1;
+    }
+  };
+  auto finish_tile = [&](const int tile, const f32x4 (&acc)[T], const float h_pre) {
+    // ---- the waves' K parts go to red[(m * RB + r) * WAVES + wave] (D[n][m]
+    // lane layout: rows 4 j4 + v, column r16), so one output's parts are
+    // adjacent and the thread that sums them finishes that output itself
 #pragma unroll
     for (int t = 0; t < T; ++t)
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        if (col_on) red[(wave * M + r16) * RB + t * 16 + 4 * j4 + v] = acc[t][v];
+        if (col_on) red[(r16 * RB + t * 16 + 4 * j4 + v) * WAVES + wave] = acc[t][v];
     lds_barrier();
-    for (int i = tid; i < M * RB; i += THREADS) {
-      float v = red[i];
-#pragma unroll
-      for (int w = 1; w < WAVES; ++w) v += red[w * M * RB + i];
-      if constexpr (XG)
+    auto result = [&](const int i) -> float {
+      float v = lds_sum(red + i * WAVES);
+      if constexpr (XG) {
         if (a.sq_in) v *= misc[64 + i / RB];  // the row's norm scale
-      red[i] = v;  // wave 0's slice holds the result (each i touched by one thread)
-    }
-    lds_barrier();
+      } else if (own_rs) {
+        v *= rsqrtf(lds_sum(misc + 64 + (i / RB) * WAVES) / (float)KF + a.eps);
+      }
+      return v;
+    };
 
-    // ---- epilogues on red[m * RB + r]
     if (a.epi == EPI_STORE) {
       for (int i = tid; i < M * RB; i += THREADS) {
         const int m = i / RB, n = tile * RB + i % RB;
+        const float y = result(i);
         if constexpr (COH)
-          cstore(coh_buffer(a.out), (uint32_t)(m * a.ldo + n), red[i]);
+          cstore(coh_buffer(a.out), (uint32_t)(m * a.ldo + n), y);
         else
-          a.out[(size_t)m * a.ldo + n] = red[i];
+          gmem(a.out)[(size_t)m * a.ldo + n] = y;
       }
     } else if (a.epi == EPI_SWIGLU) {
       constexpr int HR = RB / 2;
       for (int i = tid; i < M * HR; i += THREADS) {
         const int m = i / HR, r = i % HR;
-        const float y = silu(red[m * RB + r]) * red[m * RB + HR + r];
+        const float y = silu(result(m * RB + r)) * result(m * RB + HR + r);
         if (a.xo_hi) {  // the next GEMV's activations, bf16 hi / lo
           uint32_t h16, l16;
           split_bf16(y, h16, l16);
           const size_t o = xg_index(m, tile * HR + r);
-          a.xo_hi[o] = (uint16_t)h16;
-          a.xo_lo[o] = (uint16_t)l16;
+          gmem(a.xo_hi)[o] = (uint16_t)h16;
+          gmem(a.xo_lo)[o] = (uint16_t)l16;
         } else if constexpr (COH)
           cstore(coh_buffer(a.out), (uint32_t)(m * a.ldo + tile * HR + r), y);
         else
-          a.out[(size_t)m * a.ldo + tile * HR + r] = y;
+          gmem(a.out)[(size_t)m * a.ldo + tile * HR + r] = y;
       }
     } else if (a.epi == EPI_RESID) {
-      // h += y over all rows at once; per-row sums of squares of the new h
-      // over the tile (the next kernel's norm) from the squares left in red
+      // h += y; the per-row sum of squares of the new h over the tile (the
+      // next GEMV's norm) by shuffles: a row's RB outputs are RB adjacent
+      // lanes of one wave
       for (int i = tid; i < M * RB; i += THREADS) {
         const int m = i / RB, n = tile * RB + i % RB;
         const uint32_t hi = (uint32_t)(m * a.ldo + n);
-        const float h = (COH ? cload(coh_buffer(a.out), hi) : a.out[hi]) + red[i];
+        const float h = (h_early ? h_pre : COH ? cload(coh_buffer(a.out), hi) : gmem(a.out)[hi]) + result(i);
         if constexpr (COH)
           cstore(coh_buffer(a.out), hi, h);
         else
-          a.out[hi] = h;
-        red[i] = h * h;
+          gmem(a.out)[hi] = h;
         if (a.xo_hi) {  // h * gain as the next GEMV's bf16 hi / lo activations
           uint32_t h16, l16;
-          split_bf16(a.xo_gain ? h * bf16_to_f32(a.xo_gain[n]) : h, h16, l16);
-          a.xo_hi[xg_index(m, n)] = (uint16_t)h16;
-          a.xo_lo[xg_index(m, n)] = (uint16_t)l16;
+          split_bf16(a.xo_gain ? h * bf16_to_f32(gmem(a.xo_gain)[n]) : h, h16, l16);
+          gmem(a.xo_hi)[xg_index(m, n)] = (uint16_t)h16;
+          gmem(a.xo_lo)[xg_index(m, n)] = (uint16_t)l16;
         }
-      }
-      lds_barrier();
-      if (tid < M) {
-        float sq = 0.f;
-        for (int r = 0; r < RB; ++r) sq += red[tid * RB + r];
-        if constexpr (COH)
-          cstore(coh_buffer(a.sq_out), (uint32_t)(tid * n_tiles + tile), sq);
-        else
-          a.sq_out[tid * n_tiles + tile] = sq;
+        float sq = h * h;
+#pragma unroll
+        for (int o = 1; o < RB; o <<= 1) sq += __shfl_xor(sq, o, 64);
+        if (i % RB == 0) {
+          if constexpr (COH)
+            cstore(coh_buffer(a.sq_out), (uint32_t)(m * n_tiles + tile), sq);
+          else
+            a.sq_out[m * n_tiles + tile] = sq;
+        }
       }
     } else if (a.epi == EPI_HEAD) {
       // logits; running (max, lowest index) per row for this workgroup
       for (int i = tid; i < M * RB; i += THREADS) {
         const int m = i / RB, n = tile * RB + i % RB;
-        const float v = red[i];
-        a.out[(size_t)m * a.ldo + n] = v;
+        const float v = result(i);
+        gmem(a.out)[(size_t)m * a.ldo + n] = v;
 #pragma unroll
         for (int mm = 0; mm < 16; ++mm)
           if (mm == m && (v > best_v[mm] || (v == best_v[mm] && n < best_i[mm]))) {
@@ -415,7 +474,7 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
           }
       }
     }
-    lds_barrier();  // red is rewritten by the next tile
+    if (tile + nwg < n_tiles) lds_barrier();  // red is rewritten by the next tile
   };
 
   for (; tile < n_tiles; tile += nwg) {
@@ -440,11 +499,13 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
     two = false;
     // the next tile's first weights load while this tile is finished
     const int next = tile + nwg;
+    const float h_cur = h_tile;
     if (next < n_tiles) {
       set_tile(next);
       first_loads();
+      load_h(next);
     }
-    finish_tile(tile, acc);
+    finish_tile(tile, acc, h_cur);
   }
 
   if (a.epi != EPI_HEAD) return;

@@ -114,6 +114,7 @@ struct GemvArgs {
   int* argmax_out;
 };
 size_t gemv_lds_bytes(int M, int K, int tiles, int fmt);
+size_t gemv_lds_bytes_waves(int M, int K, int tiles, int fmt, int waves);
 int gemv_waves(int K, int tiles, int fmt);
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream);
 // fragment-order copies of [N][K] weights for launch_gemv
@@ -246,8 +247,9 @@ hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t stream);
 // ---- whole decode step in one persistent (cooperative) launch, bf16 weights
 constexpr int MEGA_ATTN_MAXCH = 64;  // attention chunks per row (256 positions each)
 struct MegaLayer {                   // device-resident, one per layer
-  GemvArgs qkv;                      // the QKV projection, whole K, 32-row tiles (measured faster
-                                     //   than 16-row tiles and than K splits that balance the tiles)
+  GemvArgs qkv;                      // the QKV projection, whole K: 32-row tiles (measured faster
+                                     //   than 16-row tiles and than K splits that balance the tiles),
+                                     //   16-row tiles in the 128-column variant
   GemvArgs o, gu, down;              // M is set per launch
   const uint16_t* qn;                // QK-norm gains (bf16) or null
   const uint16_t* kn;
@@ -256,7 +258,11 @@ struct MegaArgs {
   int M, n_layers, H, vocab;
   const MegaLayer* layers;
   GemvArgs head;
-  const void* emb;                   // bf16 [vocab][H]
+  int fmt;                           // W_BF16 or W_Q4 (every linear, the embedding included)
+  int small;                         // GEMVs reduce 128 columns per wave and iteration (rows of 1024 k)
+  const void* emb;                   // bf16 [vocab][H], or 4-bit codes [vocab][H / 8] words
+  const uint16_t* emb_sc;            // 4-bit: per-64 scales / biases [vocab][H / 64]
+  const uint16_t* emb_bi;
   const RowParam* rp;
   const int32_t* ids_dev;            // token ids, or null: rp[m].token
   float* h;                          // [M][H] residual
@@ -275,6 +281,7 @@ struct MegaArgs {
   float* attn_out;                   // [M][n_heads * d]
   unsigned* bar;                     // MEGA_BAR_WORDS zeroed words: barrier counters, exit count, abort flag
   unsigned long long* trace;         // null, or MEGA_TRACE_WORDS accumulators (see below)
+  int lds_args;                      // byte offset of a MegaLayer and a GemvArgs at the end of the dynamic LDS
 };
 // Phase tracing: workgroup 0 adds the wall-clock ticks from one barrier
 // release to the next to trace[phase] and counts steps in trace[0].
@@ -283,7 +290,7 @@ constexpr int MEGA_BAR_EXIT = 64 * 9, MEGA_BAR_ABORT = 64 * 10, MEGA_BAR_WORDS =
 size_t mega_attn_lds_bytes(int G);
 int mega_threads();
 int mega_attn_chunk();
-int mega_occupancy(int G, size_t lds);
+int mega_occupancy(int G, int fmt, bool small, size_t lds);
 hipError_t launch_decode_step(const MegaArgs& a, int G, int n_wg, size_t lds, hipStream_t stream);
 
 }  // namespace dpk

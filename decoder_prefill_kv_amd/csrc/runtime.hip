@@ -623,28 +623,45 @@ dpk_status forward_decode(dpk_model* md, int M, int max_ctx, const int32_t* ids_
               c.vocab, nullptr, argmax, st);
 }
 
+// GEMV tiling of the persistent decode kernel for the loaded model: 0 when
+// every GEMV row splits over eight waves at 256 columns per iteration (bf16),
+// 1 at 128 columns (every row length a multiple of 1024; bf16 or 4-bit), -1
+// when neither fits.
+int mega_variant(const dpk_model* md) {
+  const dpk_config& c = md->cfg;
+  const int H = c.hidden, Qd = c.n_heads * c.head_dim, I = c.intermediate;
+  if (md->fmt == DPK_FMT_BF16 && gemv_waves(H, 1, W_BF16) == 8 && gemv_waves(Qd, 1, W_BF16) == 8 &&
+      gemv_waves(H, 2, W_BF16) == 8 && gemv_waves(I, 1, W_BF16) == 8)
+    return 0;
+  if ((md->fmt == DPK_FMT_BF16 || md->fmt == DPK_FMT_Q4G64) && H % 1024 == 0 && Qd % 1024 == 0 && I % 1024 == 0)
+    return 1;
+  return -1;
+}
+
 // LDS bytes of the persistent decode kernel for M rows, or 0 if the model or
-// M does not fit it: bf16 weights, head_dim 128, 1, 2 or 4 query heads per KV
-// head, every GEMV on eight waves, at most 64 KB of LDS, one resident
-// workgroup per CU.
+// M does not fit it: bf16 or 4-bit weights, head_dim 128, 1, 2 or 4 query
+// heads per KV head (2 or 4 for the 128-column tiling), every GEMV on eight
+// waves, at most 64 KB of LDS, one resident workgroup per CU.
 size_t mega_lds_for(dpk_model* md, int M, int max_ctx) {
   const dpk_config& c = md->cfg;
-  if ((c.flags & DPK_FLAG_DECODE_MULTI) || md->fmt != DPK_FMT_BF16 || !md->mega_layers) return 0;
+  if ((c.flags & DPK_FLAG_DECODE_MULTI) || !md->mega_layers) return 0;
   if (c.head_dim != 128 || c.n_heads % c.n_kv_heads) return 0;
   const int G = c.n_heads / c.n_kv_heads;
   if (G != 1 && G != 2 && G != 4) return 0;
   if (!decode_fits(md, M)) return 0;
+  const int var = mega_variant(md);
+  if (var < 0) return 0;
+  const int fmt = md->fmt == DPK_FMT_Q4G64 ? W_Q4 : W_BF16;
   const int H = c.hidden, Qd = c.n_heads * c.head_dim, I = c.intermediate;
-  if (gemv_waves(H, 1, W_BF16) != 8 ||
-      gemv_waves(Qd, 1, W_BF16) != 8 || gemv_waves(H, 2, W_BF16) != 8 || gemv_waves(I, 1, W_BF16) != 8)
-    return 0;
   if ((max_ctx + mega_attn_chunk() - 1) / mega_attn_chunk() > MEGA_ATTN_MAXCH) return 0;
   size_t lds = mega_attn_lds_bytes(G);
-  for (size_t b : {gemv_lds_bytes(M, H, 1, W_BF16), gemv_lds_bytes(M, Qd, 1, W_BF16), gemv_lds_bytes(M, H, 2, W_BF16),
-                   gemv_lds_bytes(M, I, 1, W_BF16)})
+  for (size_t b : {gemv_lds_bytes_waves(M, H, var ? 1 : 2, fmt, 8), gemv_lds_bytes_waves(M, Qd, 1, fmt, 8),
+                   gemv_lds_bytes_waves(M, H, 2, fmt, 8), gemv_lds_bytes_waves(M, I, 1, fmt, 8),
+                   gemv_lds_bytes_waves(M, H, 1, fmt, 8)})
     lds = b > lds ? b : lds;
+  lds = (lds + 15) / 16 * 16 + sizeof(MegaLayer) + sizeof(GemvArgs);  // + the staged layer / head arguments
   if (lds > 64 * 1024) return 0;
-  if (mega_occupancy(G, lds) < 1) return 0;
+  if (mega_occupancy(G, fmt, var == 1, lds) < 1) return 0;
   return lds;
 }
 
@@ -657,8 +674,8 @@ dpk_status mega_table(dpk_model* md, hipStream_t st) {
     const LayerW& L = md->layers[l];
     LinearW qkv[3] = {L.q, L.k, L.v};
     LinearW gu[2] = {L.gate, L.up};
-    t[l].qkv = gemv_args(md, 1, md->h, H, md->sq, H / 16, L.in_norm, qkv, 3, EPI_STORE, false, 2, md->qkv, md->Nqkv,
-                         nullptr, nullptr);
+    t[l].qkv = gemv_args(md, 1, md->h, H, md->sq, H / 16, L.in_norm, qkv, 3, EPI_STORE, false,
+                         mega_variant(md) == 1 ? 1 : 2, md->qkv, md->Nqkv, nullptr, nullptr);
     t[l].o = gemv_args(md, 1, md->attn_o, Qd, nullptr, 0, nullptr, &L.o, 1, EPI_RESID, false, 1, md->h, H, md->sq,
                        nullptr);
     t[l].gu = gemv_args(md, 1, md->h, H, md->sq, H / 16, L.post_norm, gu, 2, EPI_SWIGLU, true, 2, md->act, I, nullptr,
@@ -689,7 +706,11 @@ dpk_status forward_mega(dpk_model* md, int M, int max_ctx, size_t lds, const int
   a.layers = md->mega_layers;
   a.head = gemv_args(md, M, md->h, H, md->sq, H / 16, md->final_norm, &md->head, 1, EPI_HEAD, false, 1,
                      logits ? logits : md->sink, c.vocab, nullptr, argmax);
+  a.fmt = md->fmt == DPK_FMT_Q4G64 ? W_Q4 : W_BF16;
+  a.small = mega_variant(md) == 1;
   a.emb = md->embed.w;
+  a.emb_sc = md->embed.sc;
+  a.emb_bi = md->embed.bi;
   a.rp = md->rows_dev;
   a.ids_dev = ids_dev;
   a.h = md->h;
@@ -710,13 +731,14 @@ dpk_status forward_mega(dpk_model* md, int M, int max_ctx, size_t lds, const int
   a.attn_out = md->attn_o;
   a.bar = md->mega_bar;
   a.trace = md->prof ? md->mega_trace : nullptr;
+  a.lds_args = (int)(lds - sizeof(MegaLayer) - sizeof(GemvArgs));
   // algorithmic work: every linear weight (lm_head included) once, the KV of
   // every attended position, the new positions' K/V
   const double Qd = (double)c.n_heads * c.head_dim;
   const double params = (double)c.n_layers * ((double)md->Nqkv * H + H * Qd + 3.0 * c.intermediate * H) +
                         (double)c.vocab * H;
   const double kvb = (kv_positions + M) * 2.0 * c.n_kv_heads * c.head_dim * 2.0 * c.n_layers;
-  ProfScope ps(md, st, K_DECODE_STEP, params * 2.0 + kvb, 2.0 * M * params + 4.0 * kv_positions * Qd * c.n_layers);
+  ProfScope ps(md, st, K_DECODE_STEP, params * wbytes_per_elem(md->fmt) + kvb, 2.0 * M * params + 4.0 * kv_positions * Qd * c.n_layers);
   HIP_TRY(launch_decode_step(a, c.n_heads / c.n_kv_heads, md->n_cu, lds, st));
   return DPK_OK;
 }
@@ -1331,15 +1353,15 @@ dpk_status dpk_profile_end(dpk_model* md, dpk_kernel_stat* stats, int32_t max_st
     HIP_TRY(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev));
     const dpk_config& c = md->cfg;
     const double steps = (double)tr[MP_STEPS], L = c.n_layers, H = c.hidden, I = c.intermediate;
-    const double Qd = (double)c.n_heads * c.head_dim;
+    const double Qd = (double)c.n_heads * c.head_dim, wb = wbytes_per_elem(md->fmt);
     struct P { int phase, cls; double per_step, wbytes; };
     const P ps[] = {{MP_EMBED, K_STEP_EMBED, 1, 0},
-                    {MP_QKV, K_STEP_QKV, L, md->Nqkv * H * 2},
+                    {MP_QKV, K_STEP_QKV, L, md->Nqkv * H * wb},
                     {MP_ATTN, K_STEP_ATTN, L, 0},
-                    {MP_O, K_STEP_O, L, H * Qd * 2},
-                    {MP_GATEUP, K_STEP_GATEUP, L, 2 * I * H * 2},
-                    {MP_DOWN, K_STEP_DOWN, L, H * I * 2},
-                    {MP_HEAD, K_STEP_HEAD, 1, (double)c.vocab * H * 2}};
+                    {MP_O, K_STEP_O, L, H * Qd * wb},
+                    {MP_GATEUP, K_STEP_GATEUP, L, 2 * I * H * wb},
+                    {MP_DOWN, K_STEP_DOWN, L, H * I * wb},
+                    {MP_HEAD, K_STEP_HEAD, 1, (double)c.vocab * H * wb}};
     for (const P& p : ps) {
       ms[p.cls] += khz > 0 ? (double)tr[p.phase] / khz : 0.0;
       cnt[p.cls] += (long)(steps * p.per_step);

@@ -22,8 +22,8 @@ def dpk():
 
 
 STREAM = 1  # DPK_FLAG_PREFILL_STREAM: prefill through the decode kernels
-MULTI = 2   # DPK_FLAG_DECODE_MULTI: decode as one launch per kernel (8B shapes
-            # otherwise decode in one persistent launch)
+MULTI = 2   # DPK_FLAG_DECODE_MULTI: decode as one launch per kernel (these
+            # shapes otherwise decode in one persistent launch)
 CASES = [
     # (name, config, prompt length, decode steps, Decoder kwargs); weight-
     # streaming prefill first, then the MFMA GEMM prefill path
@@ -35,6 +35,9 @@ CASES = [
     ("q06b_q4-L2-gemm", synth.Q06B_Q4.with_(n_layers=2), 37, 6, {}),
     ("q8b-L1-v4096-gemm", synth.Q8B.with_(n_layers=1, vocab=4096), 21, 5, {}),
     ("q06b-L2-chunked", synth.Q06B.with_(n_layers=2), 300, 4, dict(max_rows=128)),
+    ("q06b-L2-multi", synth.Q06B.with_(n_layers=2), 40, 8, dict(flags=MULTI)),
+    ("q06b_q4-L2-multi", synth.Q06B_Q4.with_(n_layers=2), 37, 6, dict(flags=MULTI)),
+    ("q06b_q4-L2-persistent-ctx300", synth.Q06B_Q4.with_(n_layers=2), 290, 12, dict(max_rows=128)),
     ("q8b-L2-v4096-chunked", synth.Q8B.with_(n_layers=2, vocab=4096), 600, 4, dict(max_rows=256)),
     ("q8b-L2-v4096-multi", synth.Q8B.with_(n_layers=2, vocab=4096), 250, 12, dict(flags=MULTI, max_rows=256)),
     ("q8b-L2-v4096-persistent", synth.Q8B.with_(n_layers=2, vocab=4096), 250, 12, dict(max_rows=256)),
@@ -62,18 +65,25 @@ def test_prefill_and_decode_match_oracle(dpk, name, cfg, P, N, kw):
     dec.close()
 
 
-def test_persistent_decode_matches_multi_launch(dpk):
+PERSISTENT_CFGS = [
+    ("q8b-L2-v4096", synth.Q8B.with_(n_layers=2, vocab=4096)),          # 256 columns per wave step
+    ("q06b-L2-v4096", synth.Q06B.with_(n_layers=2, vocab=4096)),        # 128 columns, bf16
+    ("q06b_q4-L2-v4096", synth.Q06B_Q4.with_(n_layers=2, vocab=4096)),  # 128 columns, 4-bit
+]
+
+
+@pytest.mark.parametrize("name,cfg", PERSISTENT_CFGS, ids=[c[0] for c in PERSISTENT_CFGS])
+def test_persistent_decode_matches_multi_launch(dpk, name, cfg):
     """The one-launch decode step against the one-launch-per-kernel path on
     the same model and tokens, across attention chunk boundaries (contexts
     250..282 cross 256) and with several chunks merged."""
-    cfg = synth.Q8B.with_(n_layers=2, vocab=4096)
     w = synth.make_weights(cfg, 0)
     P, N = 250, 32
     prompt = [int(t) for t in synth.prompt_ids(cfg, P, 0)]
     feed = [int(t) for t in synth.prompt_ids(cfg, N, 1)]  # the same tokens for both paths
     outs = []
     for flags in (0, MULTI):
-        print("\n[parity] persistent-vs-multi flags=%d" % flags, flush=True)
+        print("\n[parity] persistent-vs-multi %s flags=%d" % (name, flags), flush=True)
         dec = dpk.Decoder(cfg, w, max_batch=1, max_seq=P + N, max_rows=256, flags=flags)
         lg = dec.logits_buffer(1)
         am = dec.argmax_buffer(1)
@@ -87,7 +97,7 @@ def test_persistent_decode_matches_multi_launch(dpk):
         outs.append(torch.stack(rows).cpu())
         dec.close()
     d = (outs[0] - outs[1]).abs().max().item()
-    print("[parity] persistent vs multi-launch decode max-abs %.3g" % d, flush=True)
+    print("[parity] %s persistent vs multi-launch decode max-abs %.3g" % (name, d), flush=True)
     assert d <= 1e-3
 
 
