@@ -159,14 +159,15 @@ DPK_DEV void split_f16(float x, _Float16& hi, _Float16& lo) {
 template <int G, typename Sync>
 DPK_DEV void attn_phase(const MegaArgs& a, int layer, const uint16_t* qn, const uint16_t* kn, unsigned char* lds,
                         int wg, int nwg, Sync&& sync) {
-  float* qs = (float*)lds;              // [G][D], scaled to the log2 domain
-  float* knew = qs + G * D;             // [D]
-  float* vnew = knew + D;               // [D]
-  float* wst = vnew + D;                // [AW][2][G]
+  // q (log2 domain) as fp16 hi + lo and the new position's K / V in cache
+  // precision, all in MFMA fragment order (8 consecutive d per 16 bytes)
+  _Float16* qh16 = (_Float16*)lds;      // [G][D]
+  _Float16* ql16 = qh16 + G * D;        // [G][D]
+  _Float16* kn16 = ql16 + G * D;        // [D]
+  _Float16* vn16 = kn16 + D;            // [D]
+  float* wst = (float*)lds + G * D + 2 * D;  // [AW][2][G]
   float* ow = wst + AW * 2 * G;         // [AW][D][G]
-  float* ml = ow + AW * D * G;          // [2][MEGA_ATTN_MAXCH][G]
-  float* mw = ml + 2 * MEGA_ATTN_MAXCH * G;  // [MEGA_ATTN_MAXCH][G]
-  int* flag = (int*)(mw + MEGA_ATTN_MAXCH * G);
+  int* flag = (int*)(ow + AW * D * G);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform over the wave
@@ -247,64 +248,73 @@ DPK_DEV void attn_phase(const MegaArgs& a, int layer, const uint16_t* qn, const 
       const float x1 = xa * r * g0, x2 = xb * r * g1;
       const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
       if (wave < G) {
-        qs[wave * D + lane] = y1 * a.scale * LOG2E;
-        qs[wave * D + lane + 64] = y2 * a.scale * LOG2E;
+        _Float16 h, l;
+        split_f16(y1 * a.scale * LOG2E, h, l);
+        qh16[wave * D + lane] = h;
+        ql16[wave * D + lane] = l;
+        split_f16(y2 * a.scale * LOG2E, h, l);
+        qh16[wave * D + lane + 64] = h;
+        ql16[wave * D + lane + 64] = l;
       } else {
-        knew[lane] = y1;
-        knew[lane + 64] = y2;
+        kn16[lane] = (_Float16)y1;
+        kn16[lane + 64] = (_Float16)y2;
       }
     } else if (wave == G + 1 && own) {
       const uint32_t v = row + (uint32_t)((a.n_heads + a.n_kv + g) * D);
-      vnew[lane] = cload(q0, v + lane);
-      vnew[lane + 64] = cload(q0, v + lane + 64);
+      vn16[lane] = (_Float16)cload(q0, v + lane);
+      vn16[lane + 64] = (_Float16)cload(q0, v + lane + 64);
     }
     __syncthreads();
     if (own) {
       for (int e = tid; e < D; e += MT) {
-        kv_store(a.kv, kv_offset(a.kv, rp.seq, layer, 0, g, e, rp.pos), knew[e]);
-        kv_store(a.kv, kv_offset(a.kv, rp.seq, layer, 1, g, e, rp.pos), vnew[e]);
+        kv_store(a.kv, kv_offset(a.kv, rp.seq, layer, 0, g, e, rp.pos), (float)kn16[e]);
+        kv_store(a.kv, kv_offset(a.kv, rp.seq, layer, 1, g, e, rp.pos), (float)vn16[e]);
       }
-      // the new position inside this wave's fragments comes from knew / vnew
+      // the new position inside this wave's fragments comes from kn16 / vn16
       const int off = rp.pos - wp0;
       if (off >= 0 && off < 32) {
         // compile-time fragment indices only (runtime ones would spill the arrays)
         const int kt = (off % 8) / 4, kr = 4 * (off / 8) + off % 4;  // the row holding position off
+        if (r16 == kr) {
+          u32x4 k4[D / 32];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-          if (t == kt && r16 == kr) {
+          for (int s = 0; s < D / 32; ++s) k4[s] = *(const u32x4*)(kn16 + 32 * s + 8 * j4);
 #pragma unroll
-            for (int s = 0; s < D / 32; ++s) {
-              f16x8 k8;
+          for (int t = 0; t < 2; ++t)
+            if (t == kt) {
 #pragma unroll
-              for (int i = 0; i < 8; ++i) k8[i] = (_Float16)knew[32 * s + 8 * j4 + i];
-              kf[t][s] = __builtin_bit_cast(u32x4, k8);
+              for (int s = 0; s < D / 32; ++s) kf[t][s] = k4[s];
             }
-          }
+        }
         const int e8 = off % 8;
         if (j4 == off / 8) {
+          _Float16 vv[D / 16];
+#pragma unroll
+          for (int dt = 0; dt < D / 16; ++dt) vv[dt] = vn16[dt * 16 + r16];
 #pragma unroll
           for (int dt = 0; dt < D / 16; ++dt) {
             f16x8 v8 = __builtin_bit_cast(f16x8, vf[dt]);
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-              if (e == e8) v8[e] = (_Float16)vnew[dt * 16 + r16];
+              if (e == e8) v8[e] = vv[dt];
             vf[dt] = __builtin_bit_cast(u32x4, v8);
           }
         }
       }
     }
 
-    // ---- S = K Q^T (log2 domain), 2 tiles of 16 positions
+    // ---- S = K Q^T (log2 domain), 2 tiles of 16 positions.  Columns past G
+    // read head G - 1: they are never used, and an MFMA column depends on its
+    // own B column only.
     f16x8 qh[D / 32], ql[D / 32];
+    {
+      const int qc = r16 < G ? r16 : G - 1;
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        _Float16 h = (_Float16)0.f, l = (_Float16)0.f;
-        if (r16 < G) split_f16(qs[r16 * D + 32 * s + 8 * j4 + i], h, l);
-        qh[s][i] = h;
-        ql[s][i] = l;
+      for (int s = 0; s < D / 32; ++s) {
+        qh[s] = *(const f16x8*)(qh16 + qc * D + 32 * s + 8 * j4);
+        ql[s] = *(const f16x8*)(ql16 + qc * D + 32 * s + 8 * j4);
       }
+    }
     f32x4 sc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -332,7 +342,7 @@ DPK_DEV void attn_phase(const MegaArgs& a, int layer, const uint16_t* qn, const 
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float e = (sc[t][v] == -INFINITY) ? 0.f : exp2f(sc[t][v] - mx);
+        const float e = (sc[t][v] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sc[t][v] - mx);
         sc[t][v] = e;
         sum += e;
       }
@@ -393,7 +403,7 @@ DPK_DEV void attn_phase(const MegaArgs& a, int layer, const uint16_t* qn, const 
 #pragma unroll
       for (int w = 0; w < AW; ++w) {
         const float mwv = wst[(w * 2) * G + c];
-        const float f = (mwv == -INFINITY) ? 0.f : exp2f(mwv - Mc);
+        const float f = (mwv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mwv - Mc);
         L += f * wst[(w * 2 + 1) * G + c];
         O += f * ow[(w * D + e) * G + c];
       }
@@ -409,40 +419,33 @@ DPK_DEV void attn_phase(const MegaArgs& a, int layer, const uint16_t* qn, const 
       }
     }
     if (nch > 1 && last_block_arrive(a.attn_counters + m * a.n_kv + g, nch, flag)) {
-      for (int i = tid; i < G * nch; i += MT) {
-        const int c = i % G, ch = i / G;
-        const uint32_t base = (uint32_t)(((m * a.n_heads + g * G + c) * a.max_chunks + ch) * rec);
-        ml[ch * G + c] = cload(pb, base);
-        ml[(MEGA_ATTN_MAXCH + ch) * G + c] = cload(pb, base + 1);
-      }
-      __syncthreads();
-      if (tid < G) {
-        const int c = tid;
-        float Mx = -INFINITY;
-        for (int ch = 0; ch < nch; ++ch) Mx = fmaxf(Mx, ml[ch * G + c]);
-        float den = 0.f;
-        for (int ch = 0; ch < nch; ++ch) {
-          const float w = exp2f(ml[ch * G + c] - Mx);
-          mw[ch * G + c] = w;
-          den += w * ml[(MEGA_ATTN_MAXCH + ch) * G + c];
-        }
-        const float inv = 1.0f / den;
-        for (int ch = 0; ch < nch; ++ch) mw[ch * G + c] *= inv;
-      }
-      __syncthreads();
+      // output (c, e) of every query head of g: the (max, sum, O[e]) records
+      // of up to 16 chunks are loaded at once and folded in with a running
+      // maximum (log-sum-exp weights)
       for (int i = tid; i < G * D; i += MT) {
         const int c = i / D, e = i % D;
-        const uint32_t base = (uint32_t)(((m * a.n_heads + g * G + c) * a.max_chunks) * rec + 2 + e);
-        float O = 0.f;
-        int ch = 0;
-        for (; ch + 4 <= nch; ch += 4) {
-          const float o0 = cload(pb, base + ch * rec), o1 = cload(pb, base + (ch + 1) * rec);
-          const float o2 = cload(pb, base + (ch + 2) * rec), o3 = cload(pb, base + (ch + 3) * rec);
-          O += mw[ch * G + c] * o0 + mw[(ch + 1) * G + c] * o1 + mw[(ch + 2) * G + c] * o2 +
-               mw[(ch + 3) * G + c] * o3;
+        const uint32_t base = (uint32_t)(((m * a.n_heads + g * G + c) * a.max_chunks) * rec);
+        float Mx = -INFINITY, den = 0.f, O = 0.f;
+        for (int ch0 = 0; ch0 < nch; ch0 += 16) {
+          float mv[16], lv[16], ov[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            const uint32_t r = base + (uint32_t)min(ch0 + u, nch - 1) * rec;
+            mv[u] = cload(pb, r);
+            lv[u] = cload(pb, r + 1);
+            ov[u] = cload(pb, r + 2 + e);
+          }
+#pragma unroll
+          for (int u = 0; u < 16; ++u)
+            if (ch0 + u < nch) {
+              const float mn = fmaxf(Mx, mv[u]);
+              const float fa = __builtin_amdgcn_exp2f(Mx - mn), fb = __builtin_amdgcn_exp2f(mv[u] - mn);
+              den = den * fa + lv[u] * fb;
+              O = O * fa + ov[u] * fb;
+              Mx = mn;
+            }
         }
-        for (; ch < nch; ++ch) O += mw[ch * G + c] * cload(pb, base + ch * rec);
-        cstore(ob, outp + c * D + e, O);
+        cstore(ob, outp + c * D + e, O / den);
       }
     }
     __syncthreads();  // LDS is rewritten by the next item
@@ -538,7 +541,7 @@ const void* mega_kernel_for(int G, int fmt, bool small) {
 }  // namespace
 
 size_t mega_attn_lds_bytes(int G) {
-  return ((size_t)G * D + 2 * D + AW * 2 * G + AW * D * G + 3 * MEGA_ATTN_MAXCH * G + 4) * 4;
+  return ((size_t)G * D + 2 * D + AW * 2 * G + AW * D * G + 4) * 4;
 }
 
 int mega_threads() { return MT; }
