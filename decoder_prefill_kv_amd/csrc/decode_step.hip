@@ -157,8 +157,8 @@ DPK_DEV void split_f16(float x, _Float16& hi, _Float16& lo) {
 // finish merges them (log-sum-exp weights).  QK-norm, RoPE and the new
 // position's K/V come from the raw QKV projection of the previous phase.
 template <int G, typename Sync>
-DPK_DEV void attn_phase(const MegaArgs& a, int layer, const uint16_t* qn, const uint16_t* kn, unsigned char* lds,
-                        int wg, int nwg, Sync&& sync) {
+DPK_DEV void attn_phase(const MegaArgs& a, const RowParam* rows, int layer, const uint16_t* qn, const uint16_t* kn,
+                        unsigned char* lds, int wg, int nwg, Sync&& sync) {
   // q (log2 domain) as fp16 hi + lo and the new position's K / V in cache
   // precision, all in MFMA fragment order (8 consecutive d per 16 bytes)
   _Float16* qh16 = (_Float16*)lds;      // [G][D]
@@ -188,7 +188,7 @@ DPK_DEV void attn_phase(const MegaArgs& a, int layer, const uint16_t* qn, const 
   RowParam rp_it{};  // the row parameters of the prefetched item
   auto prefetch = [&](int it) {
     const int chunk = it % a.max_chunks, g = (it / a.max_chunks) % a.n_kv, m = it / (a.max_chunks * a.n_kv);
-    rp_it = a.rp[m];
+    rp_it = rows[m];
     const RowParam rp = rp_it;
     const int ctx = rp.pos + 1;
     const int c0 = chunk * ACH, c1 = min(ctx, c0 + ACH);
@@ -458,7 +458,9 @@ DPK_DEV void attn_phase(const MegaArgs& a, int layer, const uint16_t* qn, const 
 // QKV about one tile per workgroup.
 template <int G, int FMT, bool SMALL>
 __global__ __launch_bounds__(MT, 1) void decode_step_kernel(MegaArgs a) {
-  constexpr int KI = SMALL ? 128 : 0, TQ = SMALL ? 1 : 2;
+  // (the lm_head of a narrow model goes in 32-row tiles: one 128-column
+  // iteration per 16 rows would leave a wave a single 4 KB load in flight)
+  constexpr int KI = SMALL ? 128 : 0, TQ = SMALL ? 1 : 2, TH = SMALL ? 2 : 1;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int wg = blockIdx.x, nwg = gridDim.x;
   Barrier bar{a.bar, a.bar + MEGA_BAR_ABORT, (unsigned)nwg, 0u};
@@ -485,20 +487,24 @@ __global__ __launch_bounds__(MT, 1) void decode_step_kernel(MegaArgs a) {
   // flight (a reload from device memory would wait for every vector load
   // issued before it).  The copy overwrites the previous layer's entry only
   // after every wave has finished that layer (the barrier below).
+  // The rows' parameters (constant over the step) are staged there too, so
+  // the attention prefetch computes its cache addresses without a round trip.
   MegaLayer* const Ls = (MegaLayer*)(lds + a.lds_args);
   GemvArgs* const Hs = (GemvArgs*)(Ls + 1);
+  RowParam* const Rs = (RowParam*)(Hs + 1);
   auto stage = [&](void* dst, const void* src, int bytes) {
     __syncthreads();
     for (int i = threadIdx.x; i < bytes / 4; i += MT) ((uint32_t*)dst)[i] = ((const uint32_t*)src)[i];
     __syncthreads();
   };
+  stage(Rs, a.rp, a.M * (int)sizeof(RowParam));
   embed_phase(a, wg, nwg);
   for (int l = 0; l < a.n_layers; ++l) {
     stage(Ls, a.layers + l, (int)sizeof(MegaLayer));
     const MegaLayer& L = *Ls;
     gemv_body<FMT, TQ, 8, true, false, KI>(L.qkv, a.M, lds, wg, nwg, sync);
     closing = MP_QKV;
-    attn_phase<G>(a, l, L.qn, L.kn, lds, wg, nwg, sync);
+    attn_phase<G>(a, Rs, l, L.qn, L.kn, lds, wg, nwg, sync);
     closing = MP_ATTN;
     gemv_body<FMT, 1, 8, true, false, KI>(L.o, a.M, lds, wg, nwg, sync);
     closing = MP_O;
@@ -508,7 +514,7 @@ __global__ __launch_bounds__(MT, 1) void decode_step_kernel(MegaArgs a) {
     closing = MP_DOWN;
   }
   stage(Hs, &a.head, (int)sizeof(GemvArgs));
-  gemv_body<FMT, 1, 8, true, false, KI>(*Hs, a.M, lds, wg, nwg, sync);
+  gemv_body<FMT, TH, 8, true, false, KI>(*Hs, a.M, lds, wg, nwg, sync);
   grid_exit(bar, a.bar + MEGA_BAR_EXIT, a.err);
   if (tr) {
     mark(MP_HEAD);

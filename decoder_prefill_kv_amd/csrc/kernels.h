@@ -281,7 +281,8 @@ struct MegaArgs {
   float* attn_out;                   // [M][n_heads * d]
   unsigned* bar;                     // MEGA_BAR_WORDS zeroed words: barrier counters, exit count, abort flag
   unsigned long long* trace;         // null, or MEGA_TRACE_WORDS accumulators (see below)
-  int lds_args;                      // byte offset of a MegaLayer and a GemvArgs at the end of the dynamic LDS
+  int lds_args;                      // byte offset of a MegaLayer, a GemvArgs and 16 RowParams at the
+                                     //   end of the dynamic LDS
 };
 // Phase tracing: workgroup 0 adds the wall-clock ticks from one barrier
 // release to the next to trace[phase] and counts steps in trace[0].

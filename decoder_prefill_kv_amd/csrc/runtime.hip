@@ -659,7 +659,8 @@ size_t mega_lds_for(dpk_model* md, int M, int max_ctx) {
                    gemv_lds_bytes_waves(M, H, 2, fmt, 8), gemv_lds_bytes_waves(M, I, 1, fmt, 8),
                    gemv_lds_bytes_waves(M, H, 1, fmt, 8)})
     lds = b > lds ? b : lds;
-  lds = (lds + 15) / 16 * 16 + sizeof(MegaLayer) + sizeof(GemvArgs);  // + the staged layer / head arguments
+  // + the staged layer / head arguments and row parameters
+  lds = (lds + 15) / 16 * 16 + sizeof(MegaLayer) + sizeof(GemvArgs) + 16 * sizeof(RowParam);
   if (lds > 64 * 1024) return 0;
   if (mega_occupancy(G, fmt, var == 1, lds) < 1) return 0;
   return lds;
@@ -731,7 +732,7 @@ dpk_status forward_mega(dpk_model* md, int M, int max_ctx, size_t lds, const int
   a.attn_out = md->attn_o;
   a.bar = md->mega_bar;
   a.trace = md->prof ? md->mega_trace : nullptr;
-  a.lds_args = (int)(lds - sizeof(MegaLayer) - sizeof(GemvArgs));
+  a.lds_args = (int)(lds - sizeof(MegaLayer) - sizeof(GemvArgs) - 16 * sizeof(RowParam));
   // algorithmic work: every linear weight (lm_head included) once, the KV of
   // every attended position, the new positions' K/V
   const double Qd = (double)c.n_heads * c.head_dim;
