@@ -38,6 +38,9 @@ CASES = [
     ("q06b-L2-multi", synth.Q06B.with_(n_layers=2), 40, 8, dict(flags=MULTI)),
     ("q06b_q4-L2-multi", synth.Q06B_Q4.with_(n_layers=2), 37, 6, dict(flags=MULTI)),
     ("q06b_q4-L2-persistent-ctx300", synth.Q06B_Q4.with_(n_layers=2), 290, 12, dict(max_rows=128)),
+    # hidden 1024 with 4 query heads per KV head: the 128-column persistent step for G = 4
+    ("h1024-g4-L2-v4096", synth.Q06B.with_(n_layers=2, n_kv_heads=4, vocab=4096), 260, 6, dict(max_rows=128)),
+    ("h1024-g4-q4-L2-v4096", synth.Q06B_Q4.with_(n_layers=2, n_kv_heads=4, vocab=4096), 260, 6, dict(max_rows=128)),
     ("q8b-L2-v4096-chunked", synth.Q8B.with_(n_layers=2, vocab=4096), 600, 4, dict(max_rows=256)),
     ("q8b-L2-v4096-multi", synth.Q8B.with_(n_layers=2, vocab=4096), 250, 12, dict(flags=MULTI, max_rows=256)),
     ("q8b-L2-v4096-persistent", synth.Q8B.with_(n_layers=2, vocab=4096), 250, 12, dict(max_rows=256)),
@@ -99,6 +102,35 @@ def test_persistent_decode_matches_multi_launch(dpk, name, cfg):
     d = (outs[0] - outs[1]).abs().max().item()
     print("[parity] %s persistent vs multi-launch decode max-abs %.3g" % (name, d), flush=True)
     assert d <= 1e-3
+
+
+PATH_CASES = [
+    ("q8b-L1-v4096", synth.Q8B.with_(n_layers=1, vocab=4096), True),
+    ("q06b-L1", synth.Q06B.with_(n_layers=1), True),
+    ("q06b_q4-L1", synth.Q06B_Q4.with_(n_layers=1), True),
+    ("tiny-f32", synth.TINY, False),
+]
+
+
+@pytest.mark.parametrize("name,cfg,persistent", PATH_CASES, ids=[c[0] for c in PATH_CASES])
+def test_decode_path_taken(dpk, name, cfg, persistent):
+    """Which decode path a batch-1 step takes: one persistent launch
+    ('decode.step' in the profile) for bf16 / 4-bit models whose shapes it
+    supports, one launch per kernel otherwise."""
+    w = synth.make_weights(cfg, 0)
+    P = 24
+    dec = dpk.Decoder(cfg, w, max_batch=1, max_seq=P + 8, max_rows=64)
+    lg, am = dec.logits_buffer(1), dec.argmax_buffer(1)
+    dec.prefill(0, [int(t) for t in synth.prompt_ids(cfg, P, 0)], lg, am)
+    dpk.profile_begin(dec.handle, 10000)
+    dec.decode_step([0], None, [P], am, lg, ids_dev=am)
+    stats = dpk.profile_end(dec.handle)
+    dpk.check_device_errors(dec.handle)
+    dec.close()
+    print("\n[parity] %s decode classes %s" % (name, sorted(stats)), flush=True)
+    assert ("decode.step" in stats) == persistent, sorted(stats)
+    if persistent:
+        assert not any(k.startswith("gemv.") or k.startswith("attn.") for k in stats), sorted(stats)
 
 
 def test_prefill_without_outputs_then_decode(dpk):
