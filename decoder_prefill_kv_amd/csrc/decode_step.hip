@@ -492,6 +492,10 @@ __global__ __launch_bounds__(MT, 1) void decode_step_kernel(MegaArgs a) {
   MegaLayer* const Ls = (MegaLayer*)(lds + a.lds_args);
   GemvArgs* const Hs = (GemvArgs*)(Ls + 1);
   RowParam* const Rs = (RowParam*)(Hs + 1);
+  // bf16: the GEMVs' LDS prefetch slots (8 waves x 8 KB), after the staged
+  // arguments, used by nothing else
+  constexpr bool PF = FMT == W_BF16;
+  unsigned char* const pf = lds + a.lds_args + MEGA_ARGS_LDS;
   auto stage = [&](void* dst, const void* src, int bytes) {
     __syncthreads();
     for (int i = threadIdx.x; i < bytes / 4; i += MT) ((uint32_t*)dst)[i] = ((const uint32_t*)src)[i];
@@ -502,15 +506,15 @@ __global__ __launch_bounds__(MT, 1) void decode_step_kernel(MegaArgs a) {
   for (int l = 0; l < a.n_layers; ++l) {
     stage(Ls, a.layers + l, (int)sizeof(MegaLayer));
     const MegaLayer& L = *Ls;
-    gemv_body<FMT, TQ, 8, true, false, KI>(L.qkv, a.M, lds, wg, nwg, sync);
+    gemv_body<FMT, TQ, 8, true, false, KI, PF>(L.qkv, a.M, lds, wg, nwg, sync, pf);
     closing = MP_QKV;
     attn_phase<G>(a, Rs, l, L.qn, L.kn, lds, wg, nwg, sync);
     closing = MP_ATTN;
-    gemv_body<FMT, 1, 8, true, false, KI>(L.o, a.M, lds, wg, nwg, sync);
+    gemv_body<FMT, 1, 8, true, false, KI, PF>(L.o, a.M, lds, wg, nwg, sync, pf);
     closing = MP_O;
-    gemv_body<FMT, 2, 8, true, false, KI>(L.gu, a.M, lds, wg, nwg, sync);
+    gemv_body<FMT, 2, 8, true, false, KI, PF>(L.gu, a.M, lds, wg, nwg, sync, pf);
     closing = MP_GATEUP;
-    gemv_body<FMT, 1, 8, true, false, KI>(L.down, a.M, lds, wg, nwg, sync);
+    gemv_body<FMT, 1, 8, true, false, KI, PF>(L.down, a.M, lds, wg, nwg, sync, pf);
     closing = MP_DOWN;
   }
   stage(Hs, &a.head, (int)sizeof(GemvArgs));

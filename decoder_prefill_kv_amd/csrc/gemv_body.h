@@ -71,8 +71,15 @@ __host__ __device__ inline int gemv_lds_layout(int M, int K, int RB, int fmt, in
 // instead of being staged in LDS, so M is not limited by LDS (bf16 weights).
 // KI: columns a wave reduces per iteration (0: the default for T; 128 lets
 // eight waves split rows of 1024, 2048, 3072 ... columns).
-template <int FMT, int T, int WAVES, bool COH, bool XG = false, int KI = 0, typename Pre>
-DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const int wg, const int nwg, Pre&& pre) {
+//
+// PF (bf16): the first tile's third iteration of weights is loaded straight
+// into LDS (pf + wave * T * U KB, this wave's slot) together with its first
+// two, so three iterations are in flight while the caller waits at its
+// barrier; the loop reads that iteration from LDS.
+template <int FMT, int T, int WAVES, bool COH, bool XG = false, int KI = 0, bool PF = false, typename Pre>
+DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const int wg, const int nwg, Pre&& pre,
+                       unsigned char* pf = nullptr) {
+  static_assert(!PF || (FMT == W_BF16 && !XG), "LDS prefetch is for staged-x bf16 GEMVs");
   static_assert(!XG || FMT == W_BF16, "ready-made activations are for bf16 weights");
   constexpr int RB = 16 * T;
   constexpr int THREADS = 64 * WAVES;
@@ -175,6 +182,22 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
   // ---- first tile's first two iterations of weights, before x is read
   int tile = wg;
   bool two = false;  // iterations 0 and 1 of the current tile are already loading
+  bool in_pf = false;  // iteration 2 of the current tile is in this wave's LDS slot
+  unsigned char* const pf_slot = PF ? pf + (size_t)__builtin_amdgcn_readfirstlane(wave) * (T * U * 1024) : nullptr;
+  auto pf_issue = [&]() {
+    if constexpr (PF) {
+      if (nit > 2) {
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+            __builtin_amdgcn_global_load_lds(gmem((const void*)(wp[t] + (size_t)(2 * U + u) * 1024)),
+                                             (__attribute__((address_space(3))) void*)(pf_slot + (t * U + u) * 1024),
+                                             16, 0, 2 /* nt */);
+        in_pf = true;
+      }
+    }
+  };
   // residual epilogue: element tid of the tile's h (final before this GEMV
   // starts: only the workgroup that owns a tile writes it) is loaded with the
   // tile's first weights, so the epilogue does not wait for it
@@ -200,6 +223,7 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
     if (tile < n_tiles) {
       set_tile(tile);
       first_loads();
+      pf_issue();
       load_h(tile);
     }
   });
@@ -485,9 +509,19 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
       for (int it = 0; it < nit; it += 2) {
         if (it + 1 < nit && !(two && it == 0)) load_bf(b1, xh1, xl1, it + 1);
         compute_bf(acc, b0, xh0, xl0, it);
-        if (it + 2 < nit) load_bf(b0, xh0, xl0, it + 2);
+        if (it + 2 < nit) {
+          if (PF && in_pf && it == 0) {
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+              for (int u = 0; u < U; ++u) b0[t][u] = *(const u32x4*)(pf_slot + (t * U + u) * 1024 + lane * 16);
+          } else {
+            load_bf(b0, xh0, xl0, it + 2);
+          }
+        }
         if (it + 1 < nit) compute_bf(acc, b1, xh1, xl1, it + 1);
       }
+      in_pf = false;
     } else {
       for (int it = 0; it < nit; it += 2) {
         if (it + 1 < nit && !(two && it == 0)) load_q4(c1, s1, it + 1);

@@ -281,13 +281,17 @@ struct MegaArgs {
   float* attn_out;                   // [M][n_heads * d]
   unsigned* bar;                     // MEGA_BAR_WORDS zeroed words: barrier counters, exit count, abort flag
   unsigned long long* trace;         // null, or MEGA_TRACE_WORDS accumulators (see below)
-  int lds_args;                      // byte offset of a MegaLayer, a GemvArgs and 16 RowParams at the
-                                     //   end of the dynamic LDS
+  int lds_args;                      // byte offset of the staged arguments (MEGA_ARGS_LDS bytes) and,
+                                     //   for bf16, the GEMVs' prefetch slots (MEGA_PF_LDS bytes)
 };
 // Phase tracing: workgroup 0 adds the wall-clock ticks from one barrier
 // release to the next to trace[phase] and counts steps in trace[0].
 enum MegaPhase : int { MP_STEPS = 0, MP_EMBED, MP_QKV, MP_ATTN, MP_O, MP_GATEUP, MP_DOWN, MP_HEAD, MEGA_TRACE_WORDS };
 constexpr int MEGA_BAR_EXIT = 64 * 9, MEGA_BAR_ABORT = 64 * 10, MEGA_BAR_WORDS = 64 * 11;
+// LDS after the phases' own use: the staged layer / head arguments and row
+// parameters (MEGA_ARGS_LDS bytes), then (bf16) the GEMVs' prefetch slots
+constexpr int MEGA_ARGS_LDS = (int)((sizeof(MegaLayer) + sizeof(GemvArgs) + 16 * sizeof(RowParam) + 15) / 16 * 16);
+constexpr int MEGA_PF_LDS = 8 * 8 * 1024;
 size_t mega_attn_lds_bytes(int G);
 int mega_threads();
 int mega_attn_chunk();

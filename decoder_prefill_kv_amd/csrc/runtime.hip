@@ -94,6 +94,7 @@ struct dpk_model {
   int* argmax_sink = nullptr;
   int rows_f32 = 0;       // rows of the fp32 activation buffers
   int n_cu = 256;         // compute units of the bound device
+  int lds_max = 64 * 1024;  // LDS bytes one workgroup may allocate on it
   int attn_chunks_cap = 0;
   size_t part_floats = 0;
   // pinned staging for row parameters
@@ -659,9 +660,10 @@ size_t mega_lds_for(dpk_model* md, int M, int max_ctx) {
                    gemv_lds_bytes_waves(M, H, 2, fmt, 8), gemv_lds_bytes_waves(M, I, 1, fmt, 8),
                    gemv_lds_bytes_waves(M, H, 1, fmt, 8)})
     lds = b > lds ? b : lds;
-  // + the staged layer / head arguments and row parameters
-  lds = (lds + 15) / 16 * 16 + sizeof(MegaLayer) + sizeof(GemvArgs) + 16 * sizeof(RowParam);
-  if (lds > 64 * 1024) return 0;
+  // + the staged layer / head arguments and row parameters, + (bf16) the
+  // GEMVs' prefetch slots
+  lds = (lds + 15) / 16 * 16 + MEGA_ARGS_LDS + (fmt == W_BF16 ? MEGA_PF_LDS : 0);
+  if (lds > (size_t)md->lds_max) return 0;
   if (mega_occupancy(G, fmt, var == 1, lds) < 1) return 0;
   return lds;
 }
@@ -732,7 +734,7 @@ dpk_status forward_mega(dpk_model* md, int M, int max_ctx, size_t lds, const int
   a.attn_out = md->attn_o;
   a.bar = md->mega_bar;
   a.trace = md->prof ? md->mega_trace : nullptr;
-  a.lds_args = (int)(lds - sizeof(MegaLayer) - sizeof(GemvArgs) - 16 * sizeof(RowParam));
+  a.lds_args = (int)(lds - MEGA_ARGS_LDS - (md->fmt == DPK_FMT_BF16 ? MEGA_PF_LDS : 0));
   // algorithmic work: every linear weight (lm_head included) once, the KV of
   // every attended position, the new positions' K/V
   const double Qd = (double)c.n_heads * c.head_dim;
@@ -1064,6 +1066,9 @@ dpk_status dpk_bind_workspace(dpk_model* md, void* kv, void* scratch, void* prep
     HIP_TRY(hipGetDevice(&dev));
     HIP_TRY(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
     if (ncu > 0) md->n_cu = ncu;
+    int lmax = 0;
+    HIP_TRY(hipDeviceGetAttribute(&lmax, hipDeviceAttributeMaxSharedMemoryPerBlock, dev));
+    if (lmax > 0) md->lds_max = lmax;
   }
   HIP_TRY(hipMemsetAsync(md->counters, 0, (1 + nblocks_max(c)) * 4, st));
   HIP_TRY(hipMemsetAsync(md->attn_counters, 0, (size_t)(md->fmt == DPK_FMT_F32 ? c.max_rows : SKINNY_MAX) * c.n_kv_heads * 4, st));
