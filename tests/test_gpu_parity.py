@@ -69,25 +69,29 @@ def test_prefill_and_decode_match_oracle(dpk, name, cfg, P, N, kw):
 
 
 PERSISTENT_CFGS = [
-    ("q8b-L2-v4096", synth.Q8B.with_(n_layers=2, vocab=4096)),          # 256 columns per wave step
-    ("q06b-L2-v4096", synth.Q06B.with_(n_layers=2, vocab=4096)),        # 128 columns, bf16
-    ("q06b_q4-L2-v4096", synth.Q06B_Q4.with_(n_layers=2, vocab=4096)),  # 128 columns, 4-bit
+    # (name, config, prompt length): contexts P .. P + 31 cross a 256-position
+    # attention chunk boundary; the long ones merge 17 chunks
+    ("q8b-L2-v4096", synth.Q8B.with_(n_layers=2, vocab=4096), 250),          # 256 columns per wave step
+    ("q06b-L2-v4096", synth.Q06B.with_(n_layers=2, vocab=4096), 250),        # 128 columns, bf16
+    ("q06b_q4-L2-v4096", synth.Q06B_Q4.with_(n_layers=2, vocab=4096), 250),  # 128 columns, 4-bit
+    ("q8b-L1-v4096-ctx4100", synth.Q8B.with_(n_layers=1, vocab=4096), 4080),
+    ("q06b_q4-L1-v4096-ctx4100", synth.Q06B_Q4.with_(n_layers=1, vocab=4096), 4080),
 ]
 
 
-@pytest.mark.parametrize("name,cfg", PERSISTENT_CFGS, ids=[c[0] for c in PERSISTENT_CFGS])
-def test_persistent_decode_matches_multi_launch(dpk, name, cfg):
+@pytest.mark.parametrize("name,cfg,P", PERSISTENT_CFGS, ids=[c[0] for c in PERSISTENT_CFGS])
+def test_persistent_decode_matches_multi_launch(dpk, name, cfg, P):
     """The one-launch decode step against the one-launch-per-kernel path on
-    the same model and tokens, across attention chunk boundaries (contexts
-    250..282 cross 256) and with several chunks merged."""
+    the same model and tokens, across attention chunk boundaries and with
+    several chunks merged."""
     w = synth.make_weights(cfg, 0)
-    P, N = 250, 32
+    N = 32
     prompt = [int(t) for t in synth.prompt_ids(cfg, P, 0)]
     feed = [int(t) for t in synth.prompt_ids(cfg, N, 1)]  # the same tokens for both paths
     outs = []
     for flags in (0, MULTI):
         print("\n[parity] persistent-vs-multi %s flags=%d" % (name, flags), flush=True)
-        dec = dpk.Decoder(cfg, w, max_batch=1, max_seq=P + N, max_rows=256, flags=flags)
+        dec = dpk.Decoder(cfg, w, max_batch=1, max_seq=(P + N + 63) // 64 * 64, max_rows=256, flags=flags)
         lg = dec.logits_buffer(1)
         am = dec.argmax_buffer(1)
         dec.prefill(0, prompt, lg, am)
@@ -204,4 +208,38 @@ def test_batched_decode_matches_oracle(dpk):
         dec.decode_step([b + 1 for b in range(B)], toks, [lens[b] + s for b in range(B)], am, lg)
         for b in range(B):
             compare_logits(lg[b].cpu(), runs[b]["logits"][s + 1], TOL["bf16"], "batch row %d step %d" % (b, s))
+    dec.close()
+
+
+@pytest.mark.parametrize("name,cfg", [("q06b-L2", synth.Q06B.with_(n_layers=2)),
+                                      ("q06b_q4-L2", synth.Q06B_Q4.with_(n_layers=2))], ids=["q06b-L2", "q06b_q4-L2"])
+def test_batched_persistent_decode_long_contexts(dpk, name, cfg):
+    """Three sequences decoded together through the persistent step (M = 3
+    rows, each with its own position and cache), with contexts of one, two
+    and three attention chunks."""
+    w = synth.make_weights(cfg, 0)
+    lens = [200, 300, 530]
+    N = 3
+    prompts = [synth.prompt_ids(cfg, L, 0, index=b) for b, L in enumerate(lens)]
+    runs = [oracle_greedy(cfg, w, p, N)[1] for p in prompts]
+    dec = dpk.Decoder(cfg, w, max_batch=3, max_seq=576, max_rows=256)
+    B = len(lens)
+    for b in range(B):
+        dec.prefill(b, [int(t) for t in prompts[b]])
+    lg = dec.logits_buffer(B)
+    am = dec.argmax_buffer(B)
+    worst = 0.0
+    for s in range(N):
+        toks = [runs[b]["ids"][s] for b in range(B)]
+        if s == 0:
+            dpk.profile_begin(dec.handle, 10000)
+        dec.decode_step(list(range(B)), toks, [lens[b] + s for b in range(B)], am, lg)
+        if s == 0:
+            stats = dpk.profile_end(dec.handle)
+            assert "decode.step" in stats, sorted(stats)  # the persistent kernel took all three rows
+        for b in range(B):
+            worst = max(worst, compare_logits(lg[b].cpu(), runs[b]["logits"][s + 1], TOL[cfg.weight_format],
+                                              "%s row %d step %d" % (name, b, s)))
+    dpk.check_device_errors(dec.handle)
+    print("\n[parity] %s batched persistent worst max-abs %.3g" % (name, worst), flush=True)
     dec.close()
