@@ -34,7 +34,7 @@ TRAFFIC = {
                                          "decoder_prefill_kv_amd/csrc/gemv_body.h",
                                          "decoder_prefill_kv_amd/csrc/common.h",
                                          "decoder_prefill_kv_amd/csrc/kernels.h"],
-                             "sha256": "ed09ff57055d2ba2dcfb5a66c82df77458fbf757af4cc6d2f61192edbe884578"},
+                             "sha256": "294e3e07602b229c60b15a12c15922ff7616f32b2092a8624766d1bd533820cc"},
 }
 
 

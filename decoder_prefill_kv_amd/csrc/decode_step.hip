@@ -18,13 +18,19 @@
 // written and read with device-coherent accesses, which is what makes it
 // visible across the XCDs' separate L2 caches inside one launch.
 //
-// Phases: embedding (h and its per-tile sums of squares), then per layer the
-// QKV GEMV, attention (with QK-norm, RoPE and the KV write), the O GEMV with
-// the residual add, the gate/up GEMV with SwiGLU and the down GEMV with the
-// residual add; then the lm_head GEMV with the greedy argmax.  The GEMVs are
-// gemv_body.h's; attention splits the context into 256-position chunks, one
-// per workgroup item (32 positions per wave), merged by the last chunk to
-// finish.
+// Phases: embedding (h), then per layer the QKV GEMV, attention (with
+// QK-norm, RoPE and the KV write), the O GEMV with the residual add, the
+// gate/up GEMV with SwiGLU and the down GEMV with the residual add; then the
+// lm_head GEMV with the greedy argmax.  The GEMVs are gemv_body.h's (each
+// takes its input row's norm scale from the row it stages); attention splits
+// the context into 256-position chunks, one per workgroup item (32 positions
+// per wave), merged by the last chunk to finish.
+//
+// LDS: the phases' own scratch from offset 0; after the largest of those, the
+// current layer's argument table entry, the lm_head's arguments and the rows'
+// parameters (copied in once, so no phase re-reads them from device memory
+// while its weight loads are in flight); then, for bf16, each wave's slot for
+// the LDS-prefetched weight iteration of the next GEMV.
 //
 // The launch is cooperative (all workgroups resident), and every barrier wait
 // is bounded: a workgroup that waits too long raises an abort flag, after
