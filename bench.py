@@ -118,6 +118,16 @@ def membench(nbytes=2 << 30, reps=5):
             "frac_of_peak": round(2 * nbytes / best / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def class_times(stats, passes):
+    """{kernel class: [launches per pass, total us per pass, GB/s]} from a
+    profile_end() result covering `passes` passes."""
+    out = {}
+    for k, v in sorted(stats.items(), key=lambda kv: -kv[1]["total_ms"]):
+        gbs = v["bytes"] / (v["total_ms"] / 1e3) / 1e9 if v["total_ms"] else 0.0
+        out[k] = [v["launches"] // passes, round(1e3 * v["total_ms"] / passes, 1), round(gbs, 1)]
+    return out
+
+
 def bench_verify(dpk, cfg, w, seed, flags, K=5, rounds=24, warm=4):
     """Speculative verify of K drafts (M = K + 1 rows) against the KV cache of
     an 8192-token prompt: passes/s, and the ratio to one decode step at the
@@ -126,7 +136,8 @@ def bench_verify(dpk, cfg, w, seed, flags, K=5, rounds=24, warm=4):
     import torch
     import synth
     P = 8192
-    dec = dpk.Decoder(cfg, w, max_batch=1, max_seq=P + (K + 1) * (rounds + warm) + 8, max_rows=P, flags=flags)
+    # room for the timed passes, the profiled pass and the decode steps after them
+    dec = dpk.Decoder(cfg, w, max_batch=1, max_seq=P + (K + 1) * (rounds + warm + 1) + 32, max_rows=P, flags=flags)
     lg = dec.logits_buffer(K + 1)
     am = dec.argmax_buffer(K + 1)
     dec.prefill(0, [int(t) for t in synth.prompt_ids(cfg, P, seed)], lg[0:1], am[0:1])
@@ -142,6 +153,11 @@ def bench_verify(dpk, cfg, w, seed, flags, K=5, rounds=24, warm=4):
             times.append(dt)
         pos += acc + 1
     vt = sum(times) / len(times)
+    # one more pass with per-launch timing: where a verify pass spends its time
+    dpk.profile_begin(dec.handle, 100000)
+    acc = dec.verify(0, drafts[0:K + 1], pos, am, lg)
+    pos += acc + 1
+    classes = class_times(dpk.profile_end(dec.handle), 1)
     # one decode step at the same context, for the verify / decode ratio
     a1 = dec.argmax_buffer(1)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -162,7 +178,8 @@ def bench_verify(dpk, cfg, w, seed, flags, K=5, rounds=24, warm=4):
             "passes_per_s": round(1.0 / vt, 2), "ms_per_pass": round(vt * 1e3, 3),
             "hbm_frac": round((wbytes + kv) / vt / 1e9 / HBM_PEAK_GBS, 4),
             "decode_ms_same_ctx": round(dt_dec * 1e3, 3), "verify_over_decode": round(vt / dt_dec, 3),
-            "note": "per-pass wall time includes the host read of the accept count"}
+            "note": "per-pass wall time includes the host read of the accept count",
+            "kernel_classes_us_per_pass": classes}
 
 
 def bench_batch16(dpk, cfg, w, seed, flags, B=16, P=4096, N=32):
@@ -185,13 +202,18 @@ def bench_batch16(dpk, cfg, w, seed, flags, B=16, P=4096, N=32):
     e1.record()
     torch.cuda.synchronize()
     dt = e0.elapsed_time(e1) / N / 1e3
+    # one more step with per-launch timing: where a batch step spends its time
+    dpk.profile_begin(dec.handle, 100000)
+    dec.decode_step(seqs, None, [P + 1 + N] * B, am, lg, ids_dev=am)
+    classes = class_times(dpk.profile_end(dec.handle), 1)
     dec.close()
     H, L, d = cfg.hidden, cfg.n_layers, cfg.head_dim
     wbytes = (cfg.n_linear_params() + cfg.vocab * H) * 2.0
     kv = B * (P + 1 + N / 2.0) * 2 * L * cfg.n_kv_heads * d * 2.0
     return {"workload": "batched decode: %d sequences x %d-token KV caches, %d steps" % (B, P, N),
             "tok_s": round(B / dt, 1), "ms_per_step": round(dt * 1e3, 3),
-            "hbm_frac": round((wbytes + kv) / dt / 1e9 / HBM_PEAK_GBS, 4)}
+            "hbm_frac": round((wbytes + kv) / dt / 1e9 / HBM_PEAK_GBS, 4),
+            "kernel_classes_us_per_step": classes}
 
 
 def main():
