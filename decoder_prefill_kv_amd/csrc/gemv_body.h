@@ -239,15 +239,14 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
   // outputs are scaled -- so x is the only thing this GEMV waits for.
   float* rsw = misc + 64 + 16 * wave;
   const bool own_rs = COH && !XG && a.sq_in && KO == 0 && KF == K;
-  if (own_rs) {
-  } else if (XG && a.sq_in) {  // rows spread over the waves, one shared copy
+  if (XG && a.sq_in) {  // rows spread over the waves, one shared copy
     for (int m = wave; m < M; m += WAVES) {
       float s = 0.f;
       for (int b = lane; b < a.sq_nb; b += 64) s += a.sq_in[m * a.sq_nb + b];
       s = wave_sum(s);
       if (lane == 0) misc[64 + m] = rsqrtf(s / (float)KF + a.eps);
     }
-  } else if (a.sq_in) {
+  } else if (a.sq_in && !own_rs) {
     for (int m = 0; m < M; ++m) {
       float s = 0.f;
       for (int b = lane; b < a.sq_nb; b += 64)

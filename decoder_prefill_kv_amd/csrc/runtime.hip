@@ -642,7 +642,8 @@ int mega_variant(const dpk_model* md) {
 // LDS bytes of the persistent decode kernel for M rows, or 0 if the model or
 // M does not fit it: bf16 or 4-bit weights, head_dim 128, 1, 2 or 4 query
 // heads per KV head (2 or 4 for the 128-column tiling), every GEMV on eight
-// waves, at most 64 KB of LDS, one resident workgroup per CU.
+// waves, LDS within the device's per-workgroup limit, one resident workgroup
+// per CU.
 size_t mega_lds_for(dpk_model* md, int M, int max_ctx) {
   const dpk_config& c = md->cfg;
   if ((c.flags & DPK_FLAG_DECODE_MULTI) || !md->mega_layers) return 0;
@@ -741,7 +742,8 @@ dpk_status forward_mega(dpk_model* md, int M, int max_ctx, size_t lds, const int
   const double params = (double)c.n_layers * ((double)md->Nqkv * H + H * Qd + 3.0 * c.intermediate * H) +
                         (double)c.vocab * H;
   const double kvb = (kv_positions + M) * 2.0 * c.n_kv_heads * c.head_dim * 2.0 * c.n_layers;
-  ProfScope ps(md, st, K_DECODE_STEP, params * wbytes_per_elem(md->fmt) + kvb, 2.0 * M * params + 4.0 * kv_positions * Qd * c.n_layers);
+  ProfScope ps(md, st, K_DECODE_STEP, params * wbytes_per_elem(md->fmt) + kvb,
+               2.0 * M * params + 4.0 * kv_positions * Qd * c.n_layers);
   HIP_TRY(launch_decode_step(a, c.n_heads / c.n_kv_heads, md->n_cu, lds, st));
   return DPK_OK;
 }
