@@ -35,6 +35,12 @@ TRAFFIC = {
                                          "decoder_prefill_kv_amd/csrc/common.h",
                                          "decoder_prefill_kv_amd/csrc/kernels.h"],
                              "sha256": "a6bfe09d7b8fa7e34e3ea9049b4253b324436df2a326a1fb3bc57de08483e010"},
+    # the prefill gate+up GEMM (M = 2048): operands re-read from HBM ~3.5x
+    ("q8b", "gemm.gate_up"): {"fetch_kib": 381357.6, "write_kib": 49152.3, "fetch_factor": 2.0, "write_factor": 1.0,
+                              "sources": ["decoder_prefill_kv_amd/csrc/gemm.hip",
+                                          "decoder_prefill_kv_amd/csrc/common.h",
+                                          "decoder_prefill_kv_amd/csrc/kernels.h"],
+                              "sha256": "9ec9faa0045360a9570d8e0915563c92db2d8c20b379c84809f5433ff3525303"},
 }
 
 
@@ -331,7 +337,8 @@ def main():
             avg_g = g["total_ms"] / 1e3 / g["launches"]
             achg = g["flops"] / g["launches"] / avg_g / 1e12
             roof_prefill = {"bound": "mfma", "kernel": domg, "achieved": round(achg, 1), "peak": MFMA_PEAK_TFLOPS,
-                            "unit": "TFLOP/s", "frac": round(achg / MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                            "unit": "TFLOP/s", "frac": round(achg / MFMA_PEAK_TFLOPS, 4),
+                            "traffic": measured_traffic(args.workload, domg),
                             "flops_per_launch": g["flops"] / g["launches"], "avg_launch_us": round(avg_g * 1e6, 2)}
 
     dec.close()

@@ -115,6 +115,7 @@ struct dpk_model {
   std::vector<hipEvent_t> prof_ev;
   std::vector<ProfRec> prof_rec;
   long prof_dropped = 0;
+  double prof_step_kv = 0;  // persistent steps while profiling: cached positions their attention read
 };
 
 namespace {
@@ -744,6 +745,7 @@ dpk_status forward_mega(dpk_model* md, int M, int max_ctx, size_t lds, const int
   const double kvb = (kv_positions + M) * 2.0 * c.n_kv_heads * c.head_dim * 2.0 * c.n_layers;
   ProfScope ps(md, st, K_DECODE_STEP, params * wbytes_per_elem(md->fmt) + kvb,
                2.0 * M * params + 4.0 * kv_positions * Qd * c.n_layers);
+  if (md->prof) md->prof_step_kv += kv_positions + M;
   HIP_TRY(launch_decode_step(a, c.n_heads / c.n_kv_heads, md->n_cu, lds, st));
   return DPK_OK;
 }
@@ -1330,6 +1332,7 @@ dpk_status dpk_profile_begin(dpk_model* md, int32_t max_launches) {
   md->prof_max = max_launches;
   md->prof_rec.clear();
   md->prof_dropped = 0;
+  md->prof_step_kv = 0;
   if (md->mega_trace) HIP_TRY(hipMemset(md->mega_trace, 0, MEGA_TRACE_WORDS * 8));
   md->prof = true;
   return DPK_OK;
@@ -1365,7 +1368,8 @@ dpk_status dpk_profile_end(dpk_model* md, dpk_kernel_stat* stats, int32_t max_st
     struct P { int phase, cls; double per_step, wbytes; };
     const P ps[] = {{MP_EMBED, K_STEP_EMBED, 1, 0},
                     {MP_QKV, K_STEP_QKV, L, md->Nqkv * H * wb},
-                    {MP_ATTN, K_STEP_ATTN, L, 0},
+                    // the attention phase reads every cached position's K and V (fp16)
+                    {MP_ATTN, K_STEP_ATTN, L, md->prof_step_kv / steps * 2.0 * c.n_kv_heads * c.head_dim * 2.0},
                     {MP_O, K_STEP_O, L, H * Qd * wb},
                     {MP_GATEUP, K_STEP_GATEUP, L, 2 * I * H * wb},
                     {MP_DOWN, K_STEP_DOWN, L, H * I * wb},
