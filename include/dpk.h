@@ -81,8 +81,13 @@ typedef struct {
  * instead of the MFMA GEMM path (bf16 / q4 formats). */
 #define DPK_FLAG_PREFILL_STREAM 1
 /* Decode steps as one kernel launch per GEMV / attention instead of one
- * persistent launch for the whole step (bf16 models whose shapes the
- * persistent kernel supports use it by default). */
+ * persistent launch for the whole step.  bf16 and 4-bit models whose shapes
+ * the persistent kernel supports use it by default for a step of up to a few
+ * rows.  That launch is cooperative (one workgroup on every compute unit,
+ * grid-wide barriers inside); its barrier waits are bounded, so if other work
+ * on the device keeps its workgroups from running together the step ends with
+ * a device error (dpk_check_device_errors) instead of hanging.  Callers that
+ * share the GPU with other kernels may prefer this flag. */
 #define DPK_FLAG_DECODE_MULTI 2
 
 /*
