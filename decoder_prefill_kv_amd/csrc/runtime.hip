@@ -131,9 +131,14 @@ struct ScratchLayout {
   size_t part_floats;
 };
 
+// Most workgroups (row blocks) any one GEMV reports per-row argmax
+// candidates or per-tile sums for: every row-block count, and at least the
+// lm_head's grid on ready-made activations (up to two workgroups per compute
+// unit; MAX_HEAD_WG covers 512 units).
+constexpr int MAX_HEAD_WG = 1024;
 int nblocks_max(const dpk_config& c) {
   const int Nqkv = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
-  int nb = 0;
+  int nb = MAX_HEAD_WG;
   for (int n : {Nqkv / 64, c.hidden / 64, c.intermediate / 32, (c.vocab + 63) / 64}) nb = n > nb ? n : nb;
   return nb;
 }
@@ -486,6 +491,7 @@ dpk_status gemv_xg(dpk_model* md, int cls, int M, uint16_t* const* xin, int xrow
   const int n_tiles = (swiglu ? 2 * a.N : a.N) / (16 * tiles);
   if (epi != EPI_HEAD && n_tiles > a.grid && n_tiles <= 2 * a.grid) a.grid = n_tiles;
   if (epi == EPI_HEAD && M > 8) a.grid = 2 * md->n_cu;  // measured: more rows want more workgroups in flight
+  if (epi == EPI_HEAD && a.grid > MAX_HEAD_WG) return fail(DPK_EINVAL, "lm_head grid beyond the candidate buffer");
   if (xout) {
     a.xo_hi = xout[0];
     a.xo_lo = xout[1];
@@ -746,6 +752,7 @@ dpk_status forward_mega(dpk_model* md, int M, int max_ctx, size_t lds, const int
   ProfScope ps(md, st, K_DECODE_STEP, params * wbytes_per_elem(md->fmt) + kvb,
                2.0 * M * params + 4.0 * kv_positions * Qd * c.n_layers);
   if (md->prof) md->prof_step_kv += kv_positions + M;
+  if (md->n_cu > MAX_HEAD_WG) return fail(DPK_EINVAL, "more compute units than the candidate buffer holds");
   HIP_TRY(launch_decode_step(a, c.n_heads / c.n_kv_heads, md->n_cu, lds, st));
   return DPK_OK;
 }

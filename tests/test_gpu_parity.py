@@ -243,3 +243,50 @@ def test_batched_persistent_decode_long_contexts(dpk, name, cfg):
     dpk.check_device_errors(dec.handle)
     print("\n[parity] %s batched persistent worst max-abs %.3g" % (name, worst), flush=True)
     dec.close()
+
+
+
+BATCH16_CASES = [
+    # (name, config, prompt lengths): independent sequences decoded together on
+    # the ready-made-activation GEMVs (more rows than the persistent step
+    # stages); contexts of one and two attention chunks.  With more than 8 rows
+    # the lm_head runs on two workgroups per compute unit, more than a small
+    # vocabulary has row blocks: its argmax candidates must still fit.
+    ("q8b-L1-v4096-M16", synth.Q8B.with_(n_layers=1, vocab=4096), [5 + 17 * b for b in range(16)]),
+    ("q06b-L2-v4096-M16", synth.Q06B.with_(n_layers=2, vocab=4096), [300 - 19 * b for b in range(16)]),
+    ("q8b-L1-v4096-M2", synth.Q8B.with_(n_layers=1, vocab=4096), [270, 31]),
+]
+
+
+@pytest.mark.parametrize("name,cfg,lens", BATCH16_CASES, ids=[c[0] for c in BATCH16_CASES])
+def test_batched_decode_many_rows_match_oracle(dpk, name, cfg, lens):
+    """Every row of a batched decode step against the oracle, teacher-forced
+    on each sequence's own greedy ids."""
+    w = synth.make_weights(cfg, 0)
+    N = 3
+    B = len(lens)
+    prompts = [synth.prompt_ids(cfg, L, 0, index=b) for b, L in enumerate(lens)]
+    runs = [oracle_greedy(cfg, w, p, N)[1] for p in prompts]
+    print("\n[parity] %s rows=%d" % (name, B), flush=True)
+    dec = dpk.Decoder(cfg, w, max_batch=B, max_seq=(max(lens) + N + 63) // 64 * 64, max_rows=256)
+    for b in range(B):
+        dec.prefill(b, [int(t) for t in prompts[b]])
+    lg = dec.logits_buffer(B)
+    am = dec.argmax_buffer(B)
+    worst = 0.0
+    for s in range(N):
+        toks = [runs[b]["ids"][s] for b in range(B)]
+        if s == 0:
+            dpk.profile_begin(dec.handle, 10000)
+        dec.decode_step(list(range(B)), toks, [lens[b] + s for b in range(B)], am, lg)
+        if s == 0:
+            stats = dpk.profile_end(dec.handle)
+            assert "gemv.head" in stats, sorted(stats)
+        ids = am.cpu().tolist()
+        for b in range(B):
+            worst = max(worst, compare_logits(lg[b].cpu(), runs[b]["logits"][s + 1], TOL[cfg.weight_format],
+                                              "%s row %d step %d" % (name, b, s)))
+            check_ids([ids[b]], [runs[b]["logits"][s + 1]], [runs[b]["ids"][s + 1]], "%s row %d" % (name, b))
+    dpk.check_device_errors(dec.handle)
+    print("[parity] %s worst max-abs %.3g" % (name, worst), flush=True)
+    dec.close()
