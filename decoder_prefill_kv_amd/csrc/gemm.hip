@@ -43,10 +43,14 @@ constexpr int LDS_STRIDE = BK + 8;  // halfs per LDS row (pad against bank confl
 // instruction classes for __builtin_amdgcn_sched_group_barrier
 constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100, SG_DS_WRITE = 0x200;
 
-template <int EPI, bool SPLIT>
+// BNT: tile columns, 256, or 128 (whole-K STORE / ADD GEMMs whose 256-wide
+// tiles would leave CUs idle: each wave then holds 128 x 64 of C).
+template <int EPI, bool SPLIT, int BNT = BN>
 __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs a) {
+  static_assert(BNT == BN || (BNT == BN / 2 && EPI != GEMM_SWIGLU_F16 && !SPLIT), "narrow tiles: whole K, no SwiGLU");
+  constexpr int JB = BNT / 64;  // 32-column blocks per wave
   __shared__ __attribute__((aligned(16))) _Float16 As[2][BM][LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][BN][LDS_STRIDE];
+  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][BNT][LDS_STRIDE];
   __shared__ int s_last;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -57,15 +61,18 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs a) {
   // L2 shares (A rows across the block's columns, B rows across its rows).
   int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
   if (a.xcd_blocks) {
+    // blocks of 4 tile rows x BW tile columns (4 x 4 wide tiles, 4 x 8 narrow
+    // ones: 1024 A rows and 1024 B rows per XCD either way)
+    constexpr int BW = (BNT == BN) ? 4 : 8;
     const int L = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-    const int k = L & 7, s = L >> 3, gx = gridDim.x / 4;
+    const int k = L & 7, s = L >> 3, gx = gridDim.x / BW;
     bz = s % gridDim.z;
-    bx = 4 * (k % gx) + (s / gridDim.z) % 4;
-    by = 4 * (k / gx) + s / (gridDim.z * 4);
+    bx = BW * (k % gx) + (s / gridDim.z) % BW;
+    by = 4 * (k / gx) + s / (gridDim.z * BW);
   }
   const int m0 = by * BM;
   // SWIGLU: the tile's B rows are 128 gate rows then the same 128 up rows
-  const int n0 = (EPI == GEMM_SWIGLU_F16) ? bx * (BN / 2) : bx * BN;
+  const int n0 = (EPI == GEMM_SWIGLU_F16) ? bx * (BN / 2) : bx * BNT;
   const int nk_all = a.K / BK;
   const int nks = SPLIT ? nk_all / a.splits : nk_all;
   const int kt0 = SPLIT ? bz * nks : 0;
@@ -81,18 +88,18 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs a) {
   const _Float16* B0 = a.B + (size_t)n0 * a.ldb;
   const _Float16* B20 = (EPI == GEMM_SWIGLU_F16) ? a.B2 + (size_t)n0 * a.ldb : nullptr;
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][JB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < JB; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   // two staging sets: tile t+1 waits in one while tile t+2 is in flight into
   // the other (global loads are issued two k-tiles ahead of their LDS write).
   // Staging register r < 8 holds A row block r, r >= 8 B row block r - 8.
-  u32x4 ra[2][BM / 32], rb[2][BN / 32];
+  u32x4 ra[2][BM / 32], rb[2][BNT / 32];
   const int Kb = a.Kb ? a.Kb : a.K;
   // global loads of staging registers [R0, R1) of set SET for k-tile kt
   auto gload = [&](auto set_c, int kt, auto r0_c, auto r1_c) {
@@ -123,41 +130,52 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs a) {
         *(u32x4*)&Bs[st][lrow + 32 * (r - BM / 32)][lk] = rb[SET][r - BM / 32];
     }
   };
+  // the staging registers written out / reloaded in k-steps 0, 1, 2
+  constexpr int NR = BM / 32 + BNT / 32;
   using R0_ = std::integral_constant<int, 0>;
-  using R6_ = std::integral_constant<int, 6>;
-  using R11_ = std::integral_constant<int, 11>;
-  using R16_ = std::integral_constant<int, 16>;
+  using R6_ = std::integral_constant<int, NR == 16 ? 6 : 4>;
+  using R11_ = std::integral_constant<int, NR == 16 ? 11 : 8>;
+  using R16_ = std::integral_constant<int, NR>;
 
   // B rows of this wave inside the LDS tile
-  int brow[4];
+  int brow[JB];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < JB; ++j) {
     if (EPI == GEMM_SWIGLU_F16)
       brow[j] = (j < 2 ? 0 : BN / 2) + wn * 64 + (j & 1) * 32;
     else
-      brow[j] = wn * 128 + j * 32;
+      brow[j] = wn * (BNT / 2) + j * 32;
   }
 
   const int r32 = lane & 31, k8 = (lane >> 5) * 8;
-  f16x8 fa0[4], fb0[4], fa1[4], fb1[4];
-  auto frag_load = [&](f16x8 (&fa)[4], f16x8 (&fb)[4], int st, int kk) {
+  f16x8 fa0[4], fb0[JB], fa1[4], fb1[JB];
+  auto frag_load = [&](f16x8 (&fa)[4], f16x8 (&fb)[JB], int st, int kk) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) fa[i] = *(const f16x8*)&As[st][wm * 128 + i * 32 + r32][kk + k8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) fb[j] = *(const f16x8*)&Bs[st][brow[j] + r32][kk + k8];
+    for (int j = 0; j < JB; ++j) fb[j] = *(const f16x8*)&Bs[st][brow[j] + r32][kk + k8];
   };
-  auto mfma16 = [&](const f16x8 (&fa)[4], const f16x8 (&fb)[4]) {
+  auto mfma16 = [&](const f16x8 (&fa)[4], const f16x8 (&fb)[JB]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < JB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
   };
-  // 16 MFMAs with the 8 fragment reads of the next step spread between them
+  // 4 JB MFMAs with the 4 + JB fragment reads of the next step spread between them
   auto interleave_reads = [&]() {
+    if constexpr (JB == 4) {
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
+      for (int x = 0; x < 8; ++x) {
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+      }
+    } else {
+#pragma unroll
+      for (int x = 0; x < 6; ++x) {
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+      }
       __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
     }
   };
 
@@ -172,16 +190,18 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs a) {
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
   const int kt_last = kt0 + nks - 1;
-  // 16 MFMAs with 8 fragment reads, up to 8 LDS writes and 8 global loads
+  // 4 JB MFMAs with 4 + JB fragment reads, up to 2 JB LDS writes and 2 JB
+  // global loads
   auto interleave_all = [&]() {
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
+    for (int x = 0; x < 2 * JB; ++x) {
       __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
       __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
       __builtin_amdgcn_sched_group_barrier(SG_DS_WRITE, 1, 0);
       __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
       __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
     }
+    if constexpr (JB == 2) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
   };
   auto ktile = [&](int t, auto par_c) {
     constexpr int PAR = decltype(par_c)::value;
@@ -230,7 +250,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs a) {
   }
   if (t < nks) ktile(t, P0{});
 
-  if (SPLIT) {
+  if constexpr (SPLIT) {
     // partial tile: value pair (v, v+1) of block (i, j) of thread tid sits at
     // float offset ((((i * 4 + j) * 8 + v / 2) * THREADS + tid) * 2, so each
     // 8-byte coherent store or load of a wave covers 512 contiguous bytes
@@ -287,7 +307,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs a) {
     for (int v = 0; v < 16; ++v) {
       const int m = m0 + wm * 128 + i * 32 + 8 * (v / 4) + hi4 + (v % 4);
       if (m >= a.M) continue;
-      if (EPI == GEMM_SWIGLU_F16) {
+      if constexpr (EPI == GEMM_SWIGLU_F16) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int n = n0 + wn * 64 + j * 32 + r32;
@@ -296,8 +316,8 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs a) {
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int n = n0 + wn * 128 + j * 32 + r32;
+        for (int j = 0; j < JB; ++j) {
+          const int n = n0 + wn * (BNT / 2) + j * 32 + r32;
           float* c = a.C + (size_t)m * a.ldc + n;
           if (EPI == GEMM_ADD_F32)
             *c += acc[i][j][v];
@@ -310,17 +330,44 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs a) {
 }
 
 template <int EPI>
-void launch_epi(const GemmArgs& a, dim3 grid, hipStream_t stream) {
-  if (a.splits > 1)
+void launch_epi(const GemmArgs& a, dim3 grid, bool narrow, hipStream_t stream) {
+  if (a.splits > 1) {
     launch(gemm_kernel<EPI, true>, grid, dim3(THREADS), 0, stream, a);
-  else
+  } else if constexpr (EPI != GEMM_SWIGLU_F16) {
+    if (narrow)
+      launch(gemm_kernel<EPI, false, BN / 2>, grid, dim3(THREADS), 0, stream, a);
+    else
+      launch(gemm_kernel<EPI, false>, grid, dim3(THREADS), 0, stream, a);
+  } else {
     launch(gemm_kernel<EPI, false>, grid, dim3(THREADS), 0, stream, a);
+  }
+}
+
+// 256 x 128 tiles (no split) when 256 x 256 tiles leave CUs idle and the
+// narrow ones still fit one round: the N = 4096 projections of a 2048-row
+// prefill get 256 tiles instead of 128 split in two along K.
+bool gemm_narrow(int M, int N, int epi, int n_cu) {
+  if (epi == GEMM_SWIGLU_F16 || N % (BN / 2)) return false;
+  const int mt = (M + BM - 1) / BM;
+  return (N / BN) * mt < n_cu && (N / (BN / 2)) * mt <= n_cu;
+}
+
+int device_cus() {  // compute units of the current device (cached per device)
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) cus[dev] = n;
+  }
+  return cus[dev];
 }
 
 }  // namespace
 
 int gemm_choose_splits(int M, int N, int K, int epi, int n_cu) {
   if (K % BK) return 1;
+  if (gemm_narrow(M, N, epi, n_cu)) return 1;
   const int ntile = (epi == GEMM_SWIGLU_F16) ? BN / 2 : BN;
   const int tiles = (N / ntile) * ((M + BM - 1) / BM);
   const int nk = K / BK;
@@ -344,21 +391,24 @@ int gemm_choose_splits(int M, int N, int K, int epi, int n_cu) {
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.K % BK || a.M < 1) return hipErrorInvalidValue;
   if (a.Kb && (a.Kb % BK || (a.K != a.Kb && a.K != 2 * a.Kb))) return hipErrorInvalidValue;
-  const int ntile = (a.epi == GEMM_SWIGLU_F16) ? BN / 2 : BN;
-  if (a.N % ntile) return hipErrorInvalidValue;
   const int S = a.splits < 1 ? 1 : a.splits;
+  const bool narrow = S == 1 && gemm_narrow(a.M, a.N, a.epi, device_cus());
+  const int ntile = (a.epi == GEMM_SWIGLU_F16 || narrow) ? BN / 2 : BN;
+  if (a.N % ntile) return hipErrorInvalidValue;
   dim3 grid(a.N / ntile, (a.M + BM - 1) / BM, S);
   if (S > 1) {
     if (!a.ws || !a.counters || (a.K / BK) % S || (size_t)grid.x * grid.y * S > GEMM_WS_TILES)
       return hipErrorInvalidValue;
   }
   GemmArgs b = a;
-  // one round of exactly 8 blocks of 4 x 4 tiles (with all their splits)
-  b.xcd_blocks = (grid.x % 4 == 0 && grid.y % 4 == 0 && (grid.x / 4) * (grid.y / 4) == 8) ? 1 : 0;
+  // one round of exactly 8 blocks of 4 x 4 tiles (with all their splits), or
+  // of 4 x 8 narrow tiles
+  const int bw = narrow ? 8 : 4;
+  b.xcd_blocks = (grid.x % bw == 0 && grid.y % 4 == 0 && (grid.x / bw) * (grid.y / 4) == 8) ? 1 : 0;
   switch (a.epi) {
-    case GEMM_STORE_F32: launch_epi<GEMM_STORE_F32>(b, grid, stream); break;
-    case GEMM_ADD_F32: launch_epi<GEMM_ADD_F32>(b, grid, stream); break;
-    case GEMM_SWIGLU_F16: launch_epi<GEMM_SWIGLU_F16>(b, grid, stream); break;
+    case GEMM_STORE_F32: launch_epi<GEMM_STORE_F32>(b, grid, narrow, stream); break;
+    case GEMM_ADD_F32: launch_epi<GEMM_ADD_F32>(b, grid, narrow, stream); break;
+    case GEMM_SWIGLU_F16: launch_epi<GEMM_SWIGLU_F16>(b, grid, false, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
