@@ -115,13 +115,13 @@ DPK_DEV void grid_exit(Barrier& b, unsigned* exit_ctr, int* err) {
 
 // h[m] = E[token m] and its sums of squares per 16-column tile (the first
 // layer's norm input, in the same layout the residual epilogues write).
-DPK_DEV void embed_phase(const MegaArgs& a, int wg, int nwg) {
+DPK_DEV void embed_phase(const MegaArgs& a, const RowParam* rows, int wg, int nwg) {
   const int tid = threadIdx.x;
   const int ntile = a.H / 16;
   for (int n = wg; n < ntile; n += nwg) {
     if (tid < 16) {
       for (int m = 0; m < a.M; ++m) {
-        int tok = a.ids_dev ? a.ids_dev[m] : a.rp[m].token;
+        int tok = a.ids_dev ? a.ids_dev[m] : rows[m].token;
         if (tok < 0 || tok >= a.vocab) {
           if (tid == 0) atomicOr(a.err, 1);
           tok = 0;
@@ -507,8 +507,14 @@ __global__ __launch_bounds__(MT, 1) void decode_step_kernel(MegaArgs a) {
     for (int i = threadIdx.x; i < bytes / 4; i += MT) ((uint32_t*)dst)[i] = ((const uint32_t*)src)[i];
     __syncthreads();
   };
-  stage(Rs, a.rp, a.M * (int)sizeof(RowParam));
-  embed_phase(a, wg, nwg);
+  __syncthreads();
+  if (threadIdx.x == 0) {  // from the kernel arguments (compile-time indices)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (i < a.M) Rs[i] = a.rows[i];
+  }
+  __syncthreads();
+  embed_phase(a, Rs, wg, nwg);
   for (int l = 0; l < a.n_layers; ++l) {
     stage(Ls, a.layers + l, (int)sizeof(MegaLayer));
     const MegaLayer& L = *Ls;

@@ -263,7 +263,7 @@ struct MegaArgs {
   const void* emb;                   // bf16 [vocab][H], or 4-bit codes [vocab][H / 8] words
   const uint16_t* emb_sc;            // 4-bit: per-64 scales / biases [vocab][H / 64]
   const uint16_t* emb_bi;
-  const RowParam* rp;
+  RowParam rows[16];                 // the rows' token / position / slot (by value: no upload per step)
   const int32_t* ids_dev;            // token ids, or null: rp[m].token
   float* h;                          // [M][H] residual
   float* sq;                         // [M][H/16] per-tile sums of squares

@@ -703,8 +703,9 @@ dpk_status mega_table(dpk_model* md, hipStream_t st) {
 }
 
 // Decode step of M rows (parameters in md->rows_dev) as one persistent launch.
-dpk_status forward_mega(dpk_model* md, int M, int max_ctx, size_t lds, const int32_t* ids_dev, float* logits,
-                        int32_t* argmax, hipStream_t st, double kv_positions) {
+// rows: the M rows' parameters (host), passed in the launch arguments.
+dpk_status forward_mega(dpk_model* md, int M, int max_ctx, size_t lds, const RowParam* rows, const int32_t* ids_dev,
+                        float* logits, int32_t* argmax, hipStream_t st, double kv_positions) {
   const dpk_config& c = md->cfg;
   dpk_status s;
   if (!md->mega_table && (s = mega_table(md, st))) return s;
@@ -722,7 +723,8 @@ dpk_status forward_mega(dpk_model* md, int M, int max_ctx, size_t lds, const int
   a.emb = md->embed.w;
   a.emb_sc = md->embed.sc;
   a.emb_bi = md->embed.bi;
-  a.rp = md->rows_dev;
+  if (M > 16) return fail(DPK_EINVAL, "internal: persistent step of more than 16 rows");
+  for (int m = 0; m < M; ++m) a.rows[m] = rows[m];
   a.ids_dev = ids_dev;
   a.h = md->h;
   a.sq = md->sq;
@@ -1261,12 +1263,14 @@ dpk_status dpk_decode_step(dpk_model* md, int32_t batch, const int32_t* seqs, co
     if (pos[b] + 1 > max_ctx) max_ctx = pos[b] + 1;
   }
   hipStream_t st = (hipStream_t)stream;
-  if ((s = upload_rows(md, rows, batch, st))) return s;
   double kvpos = 0;
   for (int b = 0; b < batch; ++b) kvpos += pos[b] + 1;
+  // the persistent step takes the rows in its launch arguments; the other
+  // paths read them from device memory
   const size_t mega_lds = mega_lds_for(md, batch, max_ctx);
+  if (!mega_lds && (s = upload_rows(md, rows, batch, st))) return s;
   if (mega_lds)
-    s = forward_mega(md, batch, max_ctx, mega_lds, ids_dev, logits, argmax, st, kvpos);
+    s = forward_mega(md, batch, max_ctx, mega_lds, rows, ids_dev, logits, argmax, st, kvpos);
   else if (decode_fits(md, batch))
     s = forward_decode(md, batch, max_ctx, ids_dev, logits, argmax, st, kvpos);
   else
