@@ -29,18 +29,18 @@ MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 matrix throughput
 # (--copy-probe): FETCH_SIZE x 2.0, WRITE_SIZE x 1.0.  A figure is only
 # reported while the kernel's sources are the ones it was taken on.
 TRAFFIC = {
-    ("q8b", "decode.step"): {"fetch_kib": 7570387.6, "write_kib": 19979.1, "fetch_factor": 2.0, "write_factor": 1.0,
+    ("q8b", "decode.step"): {"fetch_kib": 7570861.4, "write_kib": 19979.1, "fetch_factor": 2.0, "write_factor": 1.0,
                              "sources": ["decoder_prefill_kv_amd/csrc/decode_step.hip",
                                          "decoder_prefill_kv_amd/csrc/gemv_body.h",
                                          "decoder_prefill_kv_amd/csrc/common.h",
                                          "decoder_prefill_kv_amd/csrc/kernels.h"],
-                             "sha256": "a6bfe09d7b8fa7e34e3ea9049b4253b324436df2a326a1fb3bc57de08483e010"},
+                             "sha256": "945376821cd2cb1074918187bc9a614e8fa805561cbdeb06faf9f031d7e87e43"},
     # the prefill gate+up GEMM (M = 2048): operands re-read from HBM ~3.5x
-    ("q8b", "gemm.gate_up"): {"fetch_kib": 383388.0, "write_kib": 49152.5, "fetch_factor": 2.0, "write_factor": 1.0,
+    ("q8b", "gemm.gate_up"): {"fetch_kib": 382914.6, "write_kib": 49152.5, "fetch_factor": 2.0, "write_factor": 1.0,
                               "sources": ["decoder_prefill_kv_amd/csrc/gemm.hip",
                                           "decoder_prefill_kv_amd/csrc/common.h",
                                           "decoder_prefill_kv_amd/csrc/kernels.h"],
-                              "sha256": "5619616f88fc592c93f8be93d1e606523731768364c17082d62503e9bfd8e41f"},
+                              "sha256": "e3c25bbfb9fd88e832a29f70dde3fdf4041e3f182e4089f8a8cc1ae37877b7ad"},
 }
 
 
