@@ -34,15 +34,20 @@ constexpr int VSTR = BKV + 8;   // halfs per V^T row in LDS
 constexpr float LOG2E = 1.4426950408889634f;
 
 __global__ __launch_bounds__(THREADS, 2) void attn_prefill_kernel(AttnPrefillArgs a, int heads_per_wg, int rb_per_wg,
-                                                                    int n_rb) {
+                                                                    int n_rb, int n_hg) {
   __shared__ __attribute__((aligned(16))) _Float16 Ks[BKV][KSTR];
   __shared__ __attribute__((aligned(16))) _Float16 Vs[D][VSTR];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int G = a.n_heads / a.n_kv;
-  // longest (latest) row blocks first
-  const int rbw = (n_rb - 1 - (int)blockIdx.x);
-  const int head0 = blockIdx.y * heads_per_wg;
+  // (row block, head group) items in order of causal length, longest first:
+  // the first half of the grid takes them from the longest end, the second
+  // half from the shortest end, so a compute unit holding workgroups L and
+  // L + half pairs a long item with a short one instead of two of equal length
+  const int total = n_rb * n_hg, half = (total + 1) / 2, L = (int)blockIdx.x;
+  const int k = L < half ? L : total - 1 - (L - half);
+  const int rbw = n_rb - 1 - k / n_hg;
+  const int head0 = (k % n_hg) * heads_per_wg;
   const int g = head0 / G;
   const int head = head0 + wave % heads_per_wg;
   const int r0 = (rbw * rb_per_wg + wave / heads_per_wg) * 32;  // this wave's first query row
@@ -237,8 +242,8 @@ hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t stream) {
   if (G % hpw || 4 % hpw) return hipErrorInvalidValue;
   const int rbpw = 4 / hpw;
   const int n_rb = (a.M + 32 * rbpw - 1) / (32 * rbpw);
-  dim3 grid(n_rb, a.n_heads / hpw);
-  launch(attn_prefill_kernel, grid, dim3(THREADS), 0, stream, a, hpw, rbpw, n_rb);
+  const int n_hg = a.n_heads / hpw;
+  launch(attn_prefill_kernel, dim3(n_rb * n_hg), dim3(THREADS), 0, stream, a, hpw, rbpw, n_rb, n_hg);
   return hipGetLastError();
 }
 
