@@ -160,3 +160,29 @@ def test_rollback_replays_a_step(dpk, weights):
     assert d <= 1e-5
     dpk.check_device_errors(dec.handle)
     dec.close()
+
+
+def test_verify_at_the_maximum_block(dpk, weights, model):
+    """k_plus_1 = 16 (the largest verify block): drafts are the oracle's own
+    greedy continuation with one wrong token planted at draft 10, so exactly 9
+    drafts are accepted (unless a step is a near tie); every row's logits
+    against the oracle's block pass."""
+    dec = dpk.Decoder(CFG, weights, max_batch=1, max_seq=MAX_SEQ, max_rows=64)
+    lg, am = dec.logits_buffer(16), dec.argmax_buffer(16)
+    prompt = [int(t) for t in synth.prompt_ids(CFG, 20, 5)]
+    run = oracle.greedy_run(model, prompt, 16)
+    g = run["ids"]
+    ids_in = [g[0]] + [g[i] for i in range(1, 16)]
+    ids_in[10] = (ids_in[10] + 1) % CFG.vocab  # draft 10 (index 10) is wrong
+    dec.prefill(0, prompt)
+    cache = model.new_cache(MAX_SEQ)
+    model.forward_block(cache, prompt, 0)
+    ref = oracle.verify(model, cache, ids_in, 20)
+    acc = dec.verify(0, ids_in, 20, am, lg)
+    for i in range(16):
+        compare_logits(lg[i].cpu(), ref["logits"][i], TOL["bf16"], "verify-16 row %d" % i)
+    assert acc == ref["accepted"]
+    assert dec.seq_length(0) == 20 + acc + 1
+    print("\n[edges] verify k+1=16 accepted %d" % acc, flush=True)
+    dpk.check_device_errors(dec.handle)
+    dec.close()
