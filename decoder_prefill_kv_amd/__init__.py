@@ -25,8 +25,8 @@ FMT_F32, FMT_BF16, FMT_Q4G64 = 0, 1, 2
 FLAG_PREFILL_STREAM = 1
 DT_F32, DT_BF16, DT_U32 = 0, 1, 2
 SYMBOLS = ["dpk_create", "dpk_workspace_size", "dpk_bind_workspace", "dpk_load_weights", "dpk_prefill",
-           "dpk_decode_step", "dpk_verify", "dpk_seq_length", "dpk_check_device_errors", "dpk_profile_begin",
-           "dpk_profile_end", "dpk_last_error", "dpk_destroy"]
+           "dpk_prefill_at", "dpk_decode_step", "dpk_verify", "dpk_seq_length", "dpk_check_device_errors",
+           "dpk_test_set_barrier_abort", "dpk_profile_begin", "dpk_profile_end", "dpk_last_error", "dpk_destroy"]
 
 
 class DpkError(RuntimeError):
@@ -70,10 +70,12 @@ def _load():
         "dpk_bind_workspace": [vp, vp, vp, vp, vp],
         "dpk_load_weights": [vp, ctypes.POINTER(Tensor), i32, vp],
         "dpk_prefill": [vp, i32, p32, i32, vp, vp, vp],
+        "dpk_prefill_at": [vp, i32, i32, p32, i32, vp, vp, vp],
         "dpk_decode_step": [vp, i32, p32, p32, vp, p32, vp, vp, vp],
         "dpk_verify": [vp, i32, p32, i32, i32, vp, vp, p32, vp],
         "dpk_seq_length": [vp, i32, p32],
         "dpk_check_device_errors": [vp, vp],
+        "dpk_test_set_barrier_abort": [vp, vp],
         "dpk_profile_begin": [vp, i32],
         "dpk_profile_end": [vp, ctypes.POINTER(KernelStat), i32, p32],
     }
@@ -151,6 +153,13 @@ def prefill(model: int, seq: int, ids: Sequence[int], logits_dev=None, argmax_de
     _check(lib().dpk_prefill(model, seq, p, len(a), _ptr(logits_dev), _ptr(argmax_dev), _stream(stream)))
 
 
+def prefill_at(model: int, seq: int, start: int, ids: Sequence[int], logits_dev=None, argmax_dev=None,
+               stream=None):
+    a, p = _i32(ids)
+    _check(lib().dpk_prefill_at(model, seq, start, p, len(a), _ptr(logits_dev), _ptr(argmax_dev),
+                                _stream(stream)))
+
+
 def decode_step(model: int, seqs: Sequence[int], ids: Optional[Sequence[int]], pos: Sequence[int], argmax_dev,
                 logits_dev=None, ids_dev=None, stream=None):
     s, sp = _i32(seqs)
@@ -179,6 +188,10 @@ def seq_length(model: int, seq: int) -> int:
 
 def check_device_errors(model: int, stream=None):
     _check(lib().dpk_check_device_errors(model, _stream(stream)))
+
+
+def test_set_barrier_abort(model: int, stream=None):
+    _check(lib().dpk_test_set_barrier_abort(model, _stream(stream)))
 
 
 def profile_begin(model: int, max_launches: int = 100000):
@@ -265,6 +278,9 @@ class Decoder:
 
     def prefill(self, seq: int, ids, logits=None, argmax=None):
         prefill(self.handle, seq, ids, logits, argmax, self.stream)
+
+    def prefill_at(self, seq: int, start: int, ids, logits=None, argmax=None):
+        prefill_at(self.handle, seq, start, ids, logits, argmax, self.stream)
 
     def decode_step(self, seqs, ids, pos, argmax, logits=None, ids_dev=None):
         decode_step(self.handle, seqs, ids, pos, argmax, logits, ids_dev, self.stream)

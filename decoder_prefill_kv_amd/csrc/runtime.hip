@@ -1212,15 +1212,18 @@ dpk_status dpk_load_weights(dpk_model* md, const dpk_tensor* t, int32_t n, void*
   return DPK_OK;
 }
 
-dpk_status dpk_prefill(dpk_model* md, int32_t seq, const int32_t* ids, int32_t n, float* logits, int32_t* argmax,
-                       void* stream) {
+dpk_status dpk_prefill_at(dpk_model* md, int32_t seq, int32_t start, const int32_t* ids, int32_t n, float* logits,
+                          int32_t* argmax, void* stream) {
   dpk_status s = check_ready(md);
   if (s) return s;
   const dpk_config& c = md->cfg;
   if (!ids) return fail(DPK_EINVAL, "null ids");
   if (n < 1) return fail(DPK_EINVAL, "n must be >= 1");
   if (seq < 0 || seq >= c.max_batch) return fail(DPK_ERANGE, "seq %d outside [0, %d)", seq, c.max_batch);
-  if (n > c.max_seq) return fail(DPK_ERANGE, "prompt of %d tokens exceeds max_seq %d", n, c.max_seq);
+  if (start < 0 || start > md->seq_len[seq])
+    return fail(DPK_ERANGE, "start %d beyond the cursor %d of slot %d", start, md->seq_len[seq], seq);
+  if ((int64_t)start + n > c.max_seq)
+    return fail(DPK_ERANGE, "start %d + %d tokens exceeds max_seq %d", start, n, c.max_seq);
   for (int i = 0; i < n; ++i)
     if (ids[i] < 0 || ids[i] >= c.vocab) return fail(DPK_ERANGE, "id %d at %d outside [0, %d)", ids[i], i, c.vocab);
   hipStream_t st = (hipStream_t)stream;
@@ -1229,17 +1232,23 @@ dpk_status dpk_prefill(dpk_model* md, int32_t seq, const int32_t* ids, int32_t n
   std::vector<RowParam> rows(chunk);
   for (int r0 = 0; r0 < n; r0 += chunk) {
     const int M = (n - r0 < chunk) ? n - r0 : chunk;
-    for (int i = 0; i < M; ++i) rows[i] = RowParam{ids[r0 + i], r0 + i, seq, 0};
+    const int p0 = start + r0;  // position of the chunk's first row
+    for (int i = 0; i < M; ++i) rows[i] = RowParam{ids[r0 + i], p0 + i, seq, 0};
     if ((s = upload_rows(md, rows.data(), M, st))) return s;
     const bool last = r0 + M == n;
     if (gemm_path && M > SKINNY_MAX)
-      s = forward_gemm(md, M, r0, seq, last, logits, argmax, st);
+      s = forward_gemm(md, M, p0, seq, last, logits, argmax, st);
     else
-      s = forward_rows(md, M, r0 + M, nullptr, M - 1, last ? 1 : 0, logits, argmax, st, r0 + M, true);
+      s = forward_rows(md, M, p0 + M, nullptr, M - 1, last ? 1 : 0, logits, argmax, st, p0 + M, true);
     if (s) return s;
   }
-  md->seq_len[seq] = n;
+  md->seq_len[seq] = start + n;
   return DPK_OK;
+}
+
+dpk_status dpk_prefill(dpk_model* md, int32_t seq, const int32_t* ids, int32_t n, float* logits, int32_t* argmax,
+                       void* stream) {
+  return dpk_prefill_at(md, seq, 0, ids, n, logits, argmax, stream);
 }
 
 dpk_status dpk_decode_step(dpk_model* md, int32_t batch, const int32_t* seqs, const int32_t* ids,
@@ -1314,6 +1323,22 @@ dpk_status dpk_seq_length(const dpk_model* md, int32_t seq, int32_t* length) {
   return DPK_OK;
 }
 
+// Zero every cross-workgroup counter of the library.  After a persistent
+// step whose barrier wait gave up, its workgroups ran the phases out of step:
+// arrivals of different layers may have met on one attention-merge counter,
+// and an arrival that lands between the last arriver's increment and its
+// reset is lost, which would leave the counter off by one for every later
+// step.
+dpk_status reset_counters(dpk_model* md, hipStream_t st) {
+  const dpk_config& c = md->cfg;
+  HIP_TRY(hipMemsetAsync(md->counters, 0, (1 + nblocks_max(c)) * 4, st));
+  HIP_TRY(hipMemsetAsync(md->attn_counters, 0,
+                         (size_t)(md->fmt == DPK_FMT_F32 ? c.max_rows : SKINNY_MAX) * c.n_kv_heads * 4, st));
+  if (md->gemm_counters) HIP_TRY(hipMemsetAsync(md->gemm_counters, 0, GEMM_WS_TILES * 4, st));
+  HIP_TRY(hipMemsetAsync(md->mega_bar, 0, MEGA_BAR_WORDS * 4, st));
+  return DPK_OK;
+}
+
 dpk_status dpk_check_device_errors(dpk_model* md, void* stream) {
   if (!md) return fail(DPK_EINVAL, "null model");
   if (!md->bound) return fail(DPK_ESTATE, "workspace not bound");
@@ -1323,10 +1348,27 @@ dpk_status dpk_check_device_errors(dpk_model* md, void* stream) {
   HIP_TRY(hipStreamSynchronize(st));
   if (flag) {
     HIP_TRY(hipMemsetAsync(md->err_flag, 0, 4, st));
+    if (flag & 2) {
+      dpk_status s = reset_counters(md, st);
+      if (s) return s;
+    }
     HIP_TRY(hipStreamSynchronize(st));
-    if (flag & 2) return fail(DPK_EHIP, "a decode step's grid barrier timed out (results of that step are invalid)");
-    return fail(DPK_ERANGE, "a device-side token id was outside [0, vocab)");
+    if (flag & 2)
+      return fail(DPK_EHIP,
+                  "a persistent decode step's grid barrier wait gave up: the logits, argmax and KV entries written "
+                  "by steps since the last check are invalid (the counters have been reset; decode again from the "
+                  "last position known good)");
+    return fail(DPK_ERANGE, "a device-side token id was outside [0, vocab) (replaced by 0)");
   }
+  return DPK_OK;
+}
+
+dpk_status dpk_test_set_barrier_abort(dpk_model* md, void* stream) {
+  dpk_status s = check_ready(md);
+  if (s) return s;
+  const unsigned one = 1u;
+  HIP_TRY(hipMemcpyAsync(md->mega_bar + MEGA_BAR_ABORT, &one, 4, hipMemcpyHostToDevice, (hipStream_t)stream));
+  HIP_TRY(hipStreamSynchronize((hipStream_t)stream));
   return DPK_OK;
 }
 

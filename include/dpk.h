@@ -146,6 +146,20 @@ dpk_status dpk_load_weights(dpk_model* m, const dpk_tensor* tensors, int32_t n, 
 dpk_status dpk_prefill(dpk_model* m, int32_t seq, const int32_t* ids, int32_t n, float* logits_dev,
                        int32_t* argmax_dev, void* stream);
 
+/* Prefill onto an existing cache (multi-turn, or a prompt fed in pieces):
+ * write the n ids (host array) at positions start..start+n-1 of slot `seq`,
+ * attending causally within the block and to the cached positions
+ * 0..start-1, set the cursor to start + n and return the last token's logits
+ * / greedy id as dpk_prefill does.  Requires start <= cursor (an earlier
+ * start drops the positions after it, as a rollback) and start + n <=
+ * max_seq (DPK_ERANGE otherwise, nothing enqueued).  dpk_prefill is this call
+ * with start = 0.  The block is the same computation as a verify pass of n
+ * rows (Butter notes, speculative decoding loop: a batch of positions put
+ * through attention over the cache together); oxinfer 0.0.5 docs, "Build and
+ * run", chunked prefill. */
+dpk_status dpk_prefill_at(dpk_model* m, int32_t seq, int32_t start, const int32_t* ids, int32_t n,
+                          float* logits_dev, int32_t* argmax_dev, void* stream);
+
 /* Decode one token for each of `batch` rows (batch <= 16).  Row b feeds token
  * ids[b] at position pos[b] of slot seqs[b] (host arrays; slots distinct).
  * Requires pos[b] <= cursor and pos[b] < max_seq; writes K/V at pos[b],
@@ -173,10 +187,24 @@ dpk_status dpk_verify(dpk_model* m, int32_t seq, const int32_t* ids, int32_t k_p
 dpk_status dpk_seq_length(const dpk_model* m, int32_t seq, int32_t* length);
 
 /* Synchronize `stream` and report device-side errors seen since the last
- * check: DPK_EHIP if a persistent decode step's bounded grid-barrier wait
- * timed out (that step's outputs are invalid), else DPK_ERANGE for
- * out-of-range device token ids, else DPK_OK.  Clears the errors. */
+ * check, then clear them:
+ *  - DPK_EHIP if a persistent decode step's bounded grid-barrier wait gave
+ *    up (the device was shared with other work, or a test forced it): the
+ *    logits, argmax and KV entries written by the steps since the last check
+ *    are invalid.  The library's cross-workgroup counters are reset, so the
+ *    caller may decode again from the last position known good (an earlier
+ *    pos rolls the slot back);
+ *  - else DPK_ERANGE for device-side token ids outside [0, vocab) (each
+ *    replaced by 0);
+ *  - else DPK_OK. */
 dpk_status dpk_check_device_errors(dpk_model* m, void* stream);
+
+/* Failure-path test support: set the persistent decode step's abort word, as
+ * a barrier wait that gives up does.  The next persistent step then passes
+ * every grid barrier without waiting (its outputs are invalid, every
+ * workgroup still finishes) and dpk_check_device_errors reports DPK_EHIP.
+ * Synchronizes `stream`. */
+dpk_status dpk_test_set_barrier_abort(dpk_model* m, void* stream);
 
 /* Per-kernel-class timing.  Between dpk_profile_begin and dpk_profile_end
  * every launch of the library records a HIP event pair on its stream (at most

@@ -186,3 +186,38 @@ def test_verify_at_the_maximum_block(dpk, weights, model):
     print("\n[edges] verify k+1=16 accepted %d" % acc, flush=True)
     dpk.check_device_errors(dec.handle)
     dec.close()
+
+
+@pytest.mark.parametrize("name,cfg", [
+    ("q8b-L2-v4096", synth.Q8B.with_(n_layers=2, vocab=4096)),      # 256-column persistent step
+    ("q06b-L2-v4096", synth.Q06B.with_(n_layers=2, vocab=4096)),    # 128-column persistent step
+])
+def test_barrier_abort_is_reported_and_recovered(dpk, name, cfg):
+    """A persistent step run with the abort word set (as after a barrier wait
+    that gave up) passes every barrier at once and finishes; the error is
+    reported, the counters are reset, and decoding again from the same
+    position reproduces the undisturbed steps exactly.  The 600-token context
+    spans three attention chunks, so the chunk-merge counters are exercised."""
+    P, N = 600, 4
+    w = synth.make_weights(cfg, 0)
+    prompt = [int(t) for t in synth.prompt_ids(cfg, P, 0)]
+    dec = dpk.Decoder(cfg, w, max_batch=1, max_seq=P + N, max_rows=256)
+    lg, am = dec.logits_buffer(1), dec.argmax_buffer(1)
+    feed = [int(t) for t in synth.prompt_ids(cfg, N, 0, index=5)]
+    dec.prefill(0, prompt, lg, am)
+    ref = []
+    for s in range(N):
+        dec.decode_step([0], [feed[s]], [P + s], am, lg)
+        ref.append(lg[0].cpu().clone())
+    dpk.check_device_errors(dec.handle)
+    print("\n[abort] %s: forcing the abort word before a step at pos %d" % (name, P), flush=True)
+    dpk.test_set_barrier_abort(dec.handle)
+    dec.decode_step([0], [feed[0]], [P], am, lg)
+    assert status_of(dpk, lambda: dpk.check_device_errors(dec.handle)) == dpk.DPK_EHIP
+    assert "barrier" in dpk.last_error()
+    dpk.check_device_errors(dec.handle)  # cleared
+    for s in range(N):
+        dec.decode_step([0], [feed[s]], [P + s], am, lg)
+        assert torch.equal(lg[0].cpu(), ref[s]), "%s step %d after recovery" % (name, s)
+    dpk.check_device_errors(dec.handle)
+    dec.close()
