@@ -26,7 +26,8 @@ FLAG_PREFILL_STREAM = 1
 DT_F32, DT_BF16, DT_U32 = 0, 1, 2
 SYMBOLS = ["dpk_create", "dpk_workspace_size", "dpk_bind_workspace", "dpk_load_weights", "dpk_prefill",
            "dpk_prefill_at", "dpk_decode_step", "dpk_verify", "dpk_seq_length", "dpk_check_device_errors",
-           "dpk_test_set_barrier_abort", "dpk_profile_begin", "dpk_profile_end", "dpk_last_error", "dpk_destroy"]
+           "dpk_test_set_barrier_abort", "dpk_profile_begin", "dpk_profile_end", "dpk_spec_generate", "dpk_sample",
+           "dpk_spec_accept_workspace_size", "dpk_spec_accept", "dpk_last_error", "dpk_destroy"]
 
 
 class DpkError(RuntimeError):
@@ -47,6 +48,19 @@ class Config(ctypes.Structure):
 class Tensor(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char_p), ("data", ctypes.c_void_p), ("dtype", ctypes.c_int32),
                 ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+class SpecConfig(ctypes.Structure):
+    _fields_ = [("k_init", ctypes.c_int32), ("k_min", ctypes.c_int32), ("k_max", ctypes.c_int32)]
+
+
+class SpecStats(ctypes.Structure):
+    _fields_ = [("rounds", ctypes.c_int32), ("drafted", ctypes.c_int32), ("accepted", ctypes.c_int32),
+                ("draft_steps", ctypes.c_int32)]
+
+
+class Sampler(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("top_k", ctypes.c_int32), ("top_p", ctypes.c_float)]
 
 
 class KernelStat(ctypes.Structure):
@@ -78,6 +92,12 @@ def _load():
         "dpk_test_set_barrier_abort": [vp, vp],
         "dpk_profile_begin": [vp, i32],
         "dpk_profile_end": [vp, ctypes.POINTER(KernelStat), i32, p32],
+        "dpk_spec_generate": [vp, vp, i32, i32, i32, i32, ctypes.POINTER(SpecConfig), p32,
+                              ctypes.POINTER(SpecStats), vp],
+        "dpk_sample": [vp, i32, i32, ctypes.c_int64, ctypes.POINTER(Sampler), vp, vp, vp],
+        "dpk_spec_accept_workspace_size": [i32, sz],
+        "dpk_spec_accept": [vp, vp, ctypes.c_int64, i32, i32, vp, ctypes.POINTER(Sampler), vp, vp, vp, vp,
+                            ctypes.c_size_t, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -209,6 +229,48 @@ def profile_end(model: int):
         out[k.name.decode()] = dict(launches=k.launches, total_ms=k.total_ms, bytes=k.bytes, flops=k.flops)
     _check(st)
     return out
+
+
+def spec_generate(target: int, draft: int, seq: int, pos: int, token: int, n_new: int, k_init: int = 4,
+                  k_min: int = 2, k_max: int = 6, stream=None):
+    """-> (list of n_new token ids, stats dict)"""
+    out = np.zeros(n_new, dtype=np.int32)
+    sc = SpecConfig(k_init, k_min, k_max)
+    st = SpecStats()
+    _check(lib().dpk_spec_generate(target, draft, seq, pos, token, n_new, ctypes.byref(sc),
+                                   out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ctypes.byref(st),
+                                   _stream(stream)))
+    return [int(t) for t in out], dict(rounds=st.rounds, drafted=st.drafted, accepted=st.accepted,
+                                        draft_steps=st.draft_steps)
+
+
+def sample(logits_dev, u_dev, out_dev, temperature: float, top_k: int = 0, top_p: float = 1.0, stream=None):
+    """One token per row of logits_dev (fp32 [rows, V] device tensor) with the
+    rows' uniforms u_dev (fp32 [rows]) into out_dev (int32 [rows])."""
+    rows, V = logits_dev.shape
+    sp = Sampler(temperature, top_k, top_p)
+    _check(lib().dpk_sample(_ptr(logits_dev), rows, V, logits_dev.stride(0), ctypes.byref(sp), _ptr(u_dev),
+                            _ptr(out_dev), _stream(stream)))
+
+
+def spec_accept_workspace_size(k: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().dpk_spec_accept_workspace_size(k, ctypes.byref(n)))
+    return n.value
+
+
+def spec_accept(target_logits, draft_logits, drafts_dev, r_dev, u_dev, out_dev, workspace, temperature: float,
+                top_k: int = 0, top_p: float = 1.0, stream=None):
+    """target_logits [k+1, V], draft_logits [k, V] (same row stride), drafts
+    int32 [k], r fp32 [k], u fp32 [k+1], out int32 [2] (all device tensors);
+    workspace: a device tensor of spec_accept_workspace_size(k) bytes."""
+    k = draft_logits.shape[0]
+    assert target_logits.stride(0) == draft_logits.stride(0)
+    sp = Sampler(temperature, top_k, top_p)
+    _check(lib().dpk_spec_accept(_ptr(target_logits), _ptr(draft_logits), target_logits.stride(0),
+                                 target_logits.shape[1], k, _ptr(drafts_dev), ctypes.byref(sp), _ptr(r_dev),
+                                 _ptr(u_dev), _ptr(out_dev), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def destroy(model: int):

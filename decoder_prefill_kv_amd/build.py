@@ -8,7 +8,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "_dpk.so")
-SOURCES = ["runtime.hip", "skinny.hip", "gemv.hip", "attn_decode.hip", "attn_decode_mfma.hip", "misc.hip", "gemm.hip", "attn_prefill.hip", "decode_step.hip"]
+SOURCES = ["runtime.hip", "skinny.hip", "gemv.hip", "attn_decode.hip", "attn_decode_mfma.hip", "misc.hip", "gemm.hip", "attn_prefill.hip", "decode_step.hip", "sample.hip"]
 BUILD = os.path.join(HERE, "_build")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",

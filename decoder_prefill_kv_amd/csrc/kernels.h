@@ -298,4 +298,18 @@ int mega_attn_chunk();
 int mega_occupancy(int G, int fmt, bool small, size_t lds);
 hipError_t launch_decode_step(const MegaArgs& a, int G, int n_wg, size_t lds, hipStream_t stream);
 
+// ---------------------------------------------------------------- sampling (sample.hip)
+// Temperature / top-k / top-p sampling of `rows` logit rows, one token each
+// drawn with the row's uniform u[r]; T == 0 is greedy.
+hipError_t launch_sample(const float* logits, long long ld, int rows, int V, float T, int top_k, float top_p,
+                         const float* u, int* out, hipStream_t stream);
+// Bytes of the per-row distribution records speculative acceptance of K
+// drafts keeps in its workspace.
+size_t spec_dist_bytes(int K);
+// Speculative-sampling acceptance of K drafts: out[0] = accepted count,
+// out[1] = next token (residual or bonus draw).
+hipError_t launch_spec_accept(const float* target, const float* draft, long long ld, int V, int K, float T,
+                              int top_k, float top_p, const int* drafts, const float* r, const float* u, void* ws,
+                              int* out, hipStream_t stream);
+
 }  // namespace dpk

@@ -92,6 +92,7 @@ struct dpk_model {
   bool mega_table = false;           // table written for the loaded weights
   int* err_flag = nullptr;
   int* argmax_sink = nullptr;
+  int* spec_ids = nullptr;  // 64 device ints: tokens of the speculative loop
   int rows_f32 = 0;       // rows of the fp32 activation buffers
   int n_cu = 256;         // compute units of the bound device
   int lds_max = 64 * 1024;  // LDS bytes one workgroup may allocate on it
@@ -124,8 +125,8 @@ size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct ScratchLayout {
   size_t rope_cos, rope_sin, rows, h, rs, qkv, y32, qbuf, attn_o, act, part, sink, sq, cand_val, cand_idx, attn_part,
-      y16, q16, o16, act16, counters, attn_counters, err, argmax_sink, gemm_ws, gemm_counters, mega_layers, mega_bar,
-      mega_trace, xb, total;
+      y16, q16, o16, act16, counters, attn_counters, err, argmax_sink, spec_ids, gemm_ws, gemm_counters, mega_layers,
+      mega_bar, mega_trace, xb, total;
   size_t xb_w;
   int rows_f32, attn_chunks_cap;
   size_t part_floats;
@@ -189,6 +190,7 @@ ScratchLayout scratch_layout(const dpk_config& c) {
   L.attn_counters = take((size_t)(f32 ? R : SKINNY_MAX) * c.n_kv_heads * 4);
   L.err = take(4);
   L.argmax_sink = take(SKINNY_MAX * 4);
+  L.spec_ids = take(64 * 4);
   const bool gemm_path = !f32 && R > SKINNY_MAX;
   L.gemm_ws = take(gemm_path ? GEMM_WS_TILES * GEMM_TILE_FLOATS * 4 : 0);
   L.gemm_counters = take(gemm_path ? GEMM_WS_TILES * 4 : 0);
@@ -234,6 +236,15 @@ size_t kv_bytes(const dpk_config& c) {
     hipError_t _e = (expr);                                                            \
     if (_e != hipSuccess) {                                                            \
       md->failed = true;                                                               \
+      return fail(DPK_EHIP, "%s failed: %s (%s:%d)", #expr, hipGetErrorString(_e), __FILE__, __LINE__); \
+    }                                                                                  \
+  } while (0)
+
+#define HIP_TRY_M(model, expr)                                                         \
+  do {                                                                                 \
+    hipError_t _e = (expr);                                                            \
+    if (_e != hipSuccess) {                                                            \
+      (model)->failed = true;                                                          \
       return fail(DPK_EHIP, "%s failed: %s (%s:%d)", #expr, hipGetErrorString(_e), __FILE__, __LINE__); \
     }                                                                                  \
   } while (0)
@@ -1057,6 +1068,7 @@ dpk_status dpk_bind_workspace(dpk_model* md, void* kv, void* scratch, void* prep
   md->attn_counters = (unsigned*)(s + L.attn_counters);
   md->err_flag = (int*)(s + L.err);
   md->argmax_sink = (int*)(s + L.argmax_sink);
+  md->spec_ids = (int*)(s + L.spec_ids);
   md->gemm_ws = L.gemm_counters > L.gemm_ws ? (float*)(s + L.gemm_ws) : nullptr;
   md->gemm_counters = L.mega_layers > L.gemm_counters ? (unsigned*)(s + L.gemm_counters) : nullptr;
   md->mega_layers = L.mega_bar > L.mega_layers ? (MegaLayer*)(s + L.mega_layers) : nullptr;
@@ -1441,6 +1453,143 @@ dpk_status dpk_profile_end(dpk_model* md, dpk_kernel_stat* stats, int32_t max_st
   }
   *n_stats = n;
   if (md->prof_dropped) return fail(DPK_ERANGE, "%ld launches were not recorded (raise max_launches)", md->prof_dropped);
+  return DPK_OK;
+}
+
+// ---------------------------------------------------------------- speculative loop
+
+dpk_status dpk_spec_generate(dpk_model* target, dpk_model* draft, int32_t seq, int32_t pos, int32_t token,
+                             int32_t n_new, const dpk_spec_config* sc, int32_t* out_ids, dpk_spec_stats* stats,
+                             void* stream) {
+  dpk_status s = check_ready(target);
+  if (s) return s;
+  if ((s = check_ready(draft))) return s;
+  if (target == draft) return fail(DPK_EINVAL, "the draft must be a separate model handle");
+  if (!sc || !out_ids) return fail(DPK_EINVAL, "null argument");
+  const dpk_config &tc = target->cfg, &dc = draft->cfg;
+  if (tc.vocab != dc.vocab) return fail(DPK_EINVAL, "draft vocab %d differs from target vocab %d", dc.vocab, tc.vocab);
+  if (sc->k_min < 1 || sc->k_min > sc->k_init || sc->k_init > sc->k_max || sc->k_max > SKINNY_MAX - 1)
+    return fail(DPK_EINVAL, "need 1 <= k_min <= k_init <= k_max <= %d", SKINNY_MAX - 1);
+  if (n_new < 1) return fail(DPK_EINVAL, "n_new must be >= 1");
+  if (seq < 0 || seq >= tc.max_batch || seq >= dc.max_batch) return fail(DPK_ERANGE, "seq %d outside both models", seq);
+  if (pos < 0 || pos > target->seq_len[seq] || pos > draft->seq_len[seq])
+    return fail(DPK_ERANGE, "pos %d beyond a cursor (target %d, draft %d)", pos, target->seq_len[seq],
+                draft->seq_len[seq]);
+  if ((int64_t)pos + n_new + sc->k_max > tc.max_seq || (int64_t)pos + n_new + sc->k_max > dc.max_seq)
+    return fail(DPK_ERANGE, "pos + n_new + k_max exceeds max_seq");
+  if (token < 0 || token >= tc.vocab) return fail(DPK_ERANGE, "token %d outside [0, %d)", token, tc.vocab);
+  hipStream_t st = (hipStream_t)stream;
+  dpk_spec_stats stt{};
+  int k = sc->k_init, emitted = 0, cur = pos, t_last = token;
+  int pending = -1;  // a committed token the draft cache lacks (at cur - 1), or -1
+  int* dd = draft->spec_ids;  // draft tokens d_1..d_K (device)
+  while (emitted < n_new) {
+    const int K = k;
+    // the draft catches up on the last draft token of a fully accepted round
+    if (pending >= 0) {
+      const int p = cur - 1;
+      if ((s = dpk_decode_step(draft, 1, &seq, &pending, nullptr, &p, nullptr, dd + 32, stream))) return s;
+      ++stt.draft_steps;
+      pending = -1;
+    }
+    // K greedy draft steps chained on the device: d_{i+1} = argmax(draft(d_i at cur + i))
+    for (int i = 0; i < K; ++i) {
+      const int p = cur + i;
+      if ((s = dpk_decode_step(draft, 1, &seq, i == 0 ? &t_last : nullptr, i == 0 ? nullptr : dd + i - 1, &p,
+                               nullptr, dd + i, stream)))
+        return s;
+    }
+    stt.draft_steps += K;
+    HIP_TRY_M(draft, hipMemcpyAsync(draft->acc_host, dd, sizeof(int32_t) * K, hipMemcpyDeviceToHost, st));
+    HIP_TRY_M(draft, hipStreamSynchronize(st));
+    int32_t ids[SKINNY_MAX];
+    ids[0] = t_last;
+    for (int i = 0; i < K; ++i) ids[1 + i] = draft->acc_host[i];
+    int32_t m = 0;
+    if ((s = dpk_verify(target, seq, ids, K + 1, cur, nullptr, target->spec_ids, &m, stream))) return s;
+    ++stt.rounds;
+    stt.drafted += K;
+    stt.accepted += m;
+    const int bonus = target->acc_host[m];
+    // emit d_1..d_m and the bonus, up to n_new
+    int e = 0;
+    for (; e < m && emitted < n_new; ++e) out_ids[emitted++] = ids[1 + e];
+    if (emitted < n_new) {
+      out_ids[emitted++] = bonus;
+      e = m + 1;
+    }
+    // positions cur..cur+e-1 now hold committed tokens (t_last, d_1..d_{e-1});
+    // the next pending token is the last emitted one
+    const int next = cur + e;
+    target->seq_len[seq] = next;
+    // the draft holds t_last, d_1..d_{K-1} at cur..cur+K-1
+    const int draft_valid = cur + (e < K ? e : K);
+    draft->seq_len[seq] = draft_valid;
+    if (e == K + 1) pending = ids[K];  // d_K at cur + K is missing from the draft
+    t_last = out_ids[emitted - 1];
+    cur = next;
+    // adaptive draft length: longer after a fully accepted round, shorter
+    // after one that accepted fewer than half
+    if (m == K && k < sc->k_max) ++k;
+    else if (2 * m < K && k > sc->k_min) --k;
+  }
+  if (pending >= 0) {
+    // leave the draft consistent with the target's committed prefix
+    const int p = cur - 1;
+    if ((s = dpk_decode_step(draft, 1, &seq, &pending, nullptr, &p, nullptr, dd + 32, stream))) return s;
+    ++stt.draft_steps;
+  }
+  if (stats) *stats = stt;
+  return DPK_OK;
+}
+
+// ---------------------------------------------------------------- sampling
+
+namespace {
+dpk_status check_sampler(const dpk_sampler* sp) {
+  if (!sp) return fail(DPK_EINVAL, "null sampler");
+  if (!(sp->temperature >= 0.0f) || !(sp->temperature < INFINITY))
+    return fail(DPK_EINVAL, "temperature must be finite and >= 0");
+  if (sp->top_k < 0) return fail(DPK_EINVAL, "top_k must be >= 0");
+  if (!(sp->top_p > 0.0f && sp->top_p <= 1.0f)) return fail(DPK_EINVAL, "top_p must be in (0, 1]");
+  return DPK_OK;
+}
+}  // namespace
+
+dpk_status dpk_sample(const float* logits, int32_t rows, int32_t vocab, int64_t ld, const dpk_sampler* sp,
+                      const float* u, int32_t* out, void* stream) {
+  if (!logits || !u || !out) return fail(DPK_EINVAL, "null argument");
+  if (rows < 1 || vocab < 1 || ld < vocab) return fail(DPK_EINVAL, "rows, vocab >= 1 and ld >= vocab required");
+  dpk_status s = check_sampler(sp);
+  if (s) return s;
+  const hipError_t e = launch_sample(logits, ld, rows, vocab, sp->temperature, sp->top_k, sp->top_p, u, out,
+                                     (hipStream_t)stream);
+  if (e != hipSuccess) return fail(DPK_EHIP, "sampling launch failed: %s", hipGetErrorString(e));
+  return DPK_OK;
+}
+
+dpk_status dpk_spec_accept_workspace_size(int32_t k, size_t* bytes) {
+  if (!bytes) return fail(DPK_EINVAL, "null argument");
+  if (k < 1 || k > DPK_SPEC_MAX_K) return fail(DPK_EINVAL, "k must be in [1, %d]", DPK_SPEC_MAX_K);
+  *bytes = spec_dist_bytes(k);
+  return DPK_OK;
+}
+
+dpk_status dpk_spec_accept(const float* target_logits, const float* draft_logits, int64_t ld, int32_t vocab,
+                           int32_t k, const int32_t* drafts, const dpk_sampler* sp, const float* r, const float* u,
+                           int32_t* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!target_logits || !draft_logits || !drafts || !r || !u || !out || !workspace)
+    return fail(DPK_EINVAL, "null argument");
+  if (k < 1 || k > DPK_SPEC_MAX_K) return fail(DPK_EINVAL, "k must be in [1, %d]", DPK_SPEC_MAX_K);
+  if (vocab < 1 || ld < vocab) return fail(DPK_EINVAL, "vocab >= 1 and ld >= vocab required");
+  if (workspace_bytes < spec_dist_bytes(k) || (uintptr_t)workspace % 16)
+    return fail(DPK_EINVAL, "workspace: %zu bytes (16-byte aligned) needed, %zu given", spec_dist_bytes(k),
+                workspace_bytes);
+  dpk_status s = check_sampler(sp);
+  if (s) return s;
+  const hipError_t e = launch_spec_accept(target_logits, draft_logits, ld, vocab, k, sp->temperature, sp->top_k,
+                                          sp->top_p, drafts, r, u, workspace, out, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(DPK_EHIP, "speculative acceptance launch failed: %s", hipGetErrorString(e));
   return DPK_OK;
 }
 

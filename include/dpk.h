@@ -224,6 +224,94 @@ typedef struct {
 dpk_status dpk_profile_begin(dpk_model* m, int32_t max_launches);
 dpk_status dpk_profile_end(dpk_model* m, dpk_kernel_stat* stats, int32_t max_stats, int32_t* n_stats);
 
+/* ------------------------------------------------------------ speculative loop
+ * Greedy speculative decoding with a draft model (LLMs on the ANE, section
+ * "Speculative decoding": a small model of the same family drafts, the large
+ * one verifies K drafts in one pass; Butter notes, speculative decoding loop:
+ * draft K, verify, accept the leading matches plus one bonus token, roll the
+ * caches back by moving their cursors; oxinfer 0.0.5 docs, "Speculative
+ * decoding": the number of drafts adapts, 2 to 6 by default).
+ *
+ * Both models hold slot `seq` with the same committed tokens cached at
+ * positions 0..pos-1 (pos <= both cursors; positions past pos are dropped)
+ * and share the vocabulary; `token` is the last committed token, not yet
+ * cached, which goes at `pos`.  Each round the draft decodes K tokens
+ * greedily (its steps chained on the device), the target verifies
+ * [last, d_1..d_K] with dpk_verify, and the accepted drafts plus the bonus
+ * token are emitted.  The emitted tokens are the target's greedy
+ * continuation: out_ids[0..n_new) (host) receives the tokens that follow
+ * `token`.  K starts at k_init, grows by one after a round that accepted
+ * all K drafts and shrinks by one after a round that accepted fewer than
+ * half, within [k_min, k_max].  On return the target's cursor is pos plus
+ * the tokens consumed (the last emitted token is not cached, as `token` was
+ * not), and the draft's cursor equals it.  Requires
+ * 1 <= k_min <= k_init <= k_max <= 15 and pos + n_new + k_max <= max_seq of
+ * both models.  Synchronizes `stream` once per round (the drafts and the
+ * accepted count are read back). */
+typedef struct {
+  int32_t k_init, k_min, k_max;
+} dpk_spec_config;
+typedef struct {
+  int32_t rounds;       /* verify passes of the target */
+  int32_t drafted;      /* draft tokens proposed */
+  int32_t accepted;     /* of which accepted */
+  int32_t draft_steps;  /* draft decode steps run (drafts plus catch-up steps) */
+} dpk_spec_stats;
+dpk_status dpk_spec_generate(dpk_model* target, dpk_model* draft, int32_t seq, int32_t pos, int32_t token,
+                             int32_t n_new, const dpk_spec_config* sc, int32_t* out_ids, dpk_spec_stats* stats,
+                             void* stream);
+
+/* ------------------------------------------------------------ sampling
+ * Sampling as a final kernel on the logits (Butter architecture notes, GPU
+ * sampling diagram: only the 4-byte token leaves the GPU).  Per logit row x:
+ *  - z = x / temperature; temperature 0 is greedy (lowest index of the max);
+ *  - top_k > 0: keep the tokens whose z is at least the k-th largest z (ties
+ *    with it kept); 0 keeps all;
+ *  - the kept tokens' weights are exp(z - max z);
+ *  - top_p < 1: the cut is the weight at which the mass of the heaviest
+ *    kept tokens first reaches top_p of their total; every token at or
+ *    above the cut stays (ties kept); 1 keeps all;
+ *  - the token is the smallest index (index order) whose cumulative kept
+ *    weight exceeds u times the kept total, for the row's uniform u in
+ *    [0, 1) (the caller supplies the random numbers).
+ * Weights are summed in 64-bit fixed point (2^-40 resolution), so a call is
+ * deterministic.  Logits must be finite. */
+typedef struct {
+  float temperature; /* >= 0 */
+  int32_t top_k;     /* >= 0; 0 = no top-k */
+  float top_p;       /* (0, 1]; 1 = no top-p */
+} dpk_sampler;
+
+/* One token per row: logits fp32 [rows, ld] (device, the first vocab
+ * entries of each row used), u fp32 [rows] (device), out int32 [rows]
+ * (device).  Enqueued on `stream`; no workspace.  DPK_EINVAL for bad sizes
+ * or sampler fields (nothing enqueued). */
+dpk_status dpk_sample(const float* logits_dev, int32_t rows, int32_t vocab, int64_t ld, const dpk_sampler* sp,
+                      const float* u_dev, int32_t* out_dev, void* stream);
+
+/* Speculative-sampling acceptance (oxinfer 0.0.5 docs, "Speculative
+ * decoding": the standard speculative-sampling rule; Butter notes,
+ * speculative decoding loop).  k drafts d_1..d_k (device int32 [k]) were
+ * drawn from the draft model's rows draft_logits [k, ld] (row i-1 drew d_i);
+ * target_logits [k+1, ld] are the target's rows for the same positions (one
+ * verify pass).  Both are turned into distributions p (target) and q
+ * (draft) by the sampler above.  Draft d_i is accepted while
+ * r[i-1] < p_{i-1}(d_i) / q_{i-1}(d_i); at the first rejection the next token
+ * is drawn with u[i-1] from max(0, p - q) renormalised (from p if that is
+ * zero everywhere); if all k are accepted it is drawn from target row k
+ * with u[k].  r fp32 [k], u fp32 [k+1] (device uniforms in [0, 1)).  out
+ * int32 [2] (device): accepted count m, next token.  With temperature 0 the
+ * rule is the greedy one (accept while d_i equals the argmax).  A draft id
+ * outside [0, vocab) counts as rejected.  workspace:
+ * device, 16-byte aligned, dpk_spec_accept_workspace_size(k) bytes, owned
+ * by the caller; calls that share one workspace must not overlap. */
+#define DPK_SPEC_MAX_K 16
+dpk_status dpk_spec_accept_workspace_size(int32_t k, size_t* bytes);
+dpk_status dpk_spec_accept(const float* target_logits_dev, const float* draft_logits_dev, int64_t ld, int32_t vocab,
+                           int32_t k, const int32_t* drafts_dev, const dpk_sampler* sp, const float* r_dev,
+                           const float* u_dev, int32_t* out_dev, void* workspace_dev, size_t workspace_bytes,
+                           void* stream);
+
 /* Message of the last failure on the calling thread (valid until the next
  * call on this thread); "" if none. */
 const char* dpk_last_error(void);
