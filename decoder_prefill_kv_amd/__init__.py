@@ -21,9 +21,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "_dpk.so")
 
 DPK_OK, DPK_EINVAL, DPK_ERANGE, DPK_ESTATE, DPK_ENOMEM, DPK_EHIP = 0, -1, -2, -3, -4, -5
-FMT_F32, FMT_BF16, FMT_Q4G64 = 0, 1, 2
+FMT_F32, FMT_BF16, FMT_Q4G64, FMT_I8 = 0, 1, 2, 3
 FLAG_PREFILL_STREAM = 1
-DT_F32, DT_BF16, DT_U32 = 0, 1, 2
+DT_F32, DT_BF16, DT_U32, DT_I8 = 0, 1, 2, 3
 SYMBOLS = ["dpk_create", "dpk_workspace_size", "dpk_bind_workspace", "dpk_load_weights", "dpk_prefill",
            "dpk_prefill_at", "dpk_decode_step", "dpk_verify", "dpk_seq_length", "dpk_check_device_errors",
            "dpk_test_set_barrier_abort", "dpk_profile_begin", "dpk_profile_end", "dpk_spec_generate", "dpk_sample",
@@ -278,7 +278,7 @@ def destroy(model: int):
 
 
 # ------------------------------------------------------------------ convenience
-_FMT = {"f32": FMT_F32, "bf16": FMT_BF16, "q4": FMT_Q4G64}
+_FMT = {"f32": FMT_F32, "bf16": FMT_BF16, "q4": FMT_Q4G64, "i8": FMT_I8}
 
 
 def make_config(mc, max_batch: int, max_seq: int, max_rows: int = 512, flags: int = 0) -> Config:
@@ -295,6 +295,8 @@ def _dtype_code(a: np.ndarray) -> int:
         return DT_BF16
     if a.dtype == np.uint32:
         return DT_U32
+    if a.dtype == np.int8:
+        return DT_I8
     raise TypeError(a.dtype)
 
 

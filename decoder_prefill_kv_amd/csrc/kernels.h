@@ -34,9 +34,9 @@ enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_
 
 struct SkinnyArgs {
   int M, K, N;  // activation rows (<=16), input dim, output rows
-  int fmt;      // W_BF16 | W_Q4
-  const void* w[3];         // bf16 [rows][K] or q4 codes uint32 [rows][K/8]
-  const uint16_t* sc[3];    // q4 scales bf16 [rows][K/64]
+  int fmt;      // W_BF16 | W_Q4 | W_I8
+  const void* w[3];         // bf16 [rows][K], q4 codes uint32 [rows][K/8] or int8 [rows][K]
+  const uint16_t* sc[3];    // q4 scales bf16 [rows][K/64]; int8: row scales bf16 [rows]
   const uint16_t* bi[3];    // q4 biases bf16 [rows][K/64]
   int seg_end[3];           // cumulative row ends of the stacked segments
   int seg_rows[3];          // rows of each segment (load clamp)
@@ -203,6 +203,8 @@ hipError_t launch_xprep(int M, int K, const float* x, int ldx, const float* sq_i
 hipError_t launch_add(int n, const float* in, float* out, hipStream_t stream);
 // bf16 -> fp16 / q4 -> fp16 weight conversion for the prefill GEMM operands
 hipError_t launch_bf16_to_f16(const uint16_t* src, _Float16* dst, size_t n, hipStream_t stream);
+hipError_t launch_i8_to_f16(const int8_t* q, const uint16_t* sc, int rows, int K, _Float16* dst,
+                            hipStream_t stream);
 hipError_t launch_q4_to_f16(const uint32_t* codes, const uint16_t* sc, const uint16_t* bi, int rows, int K,
                             _Float16* dst, hipStream_t stream);
 hipError_t launch_f32_to_f16(const float* src, _Float16* dst, size_t n, hipStream_t stream);

@@ -39,6 +39,8 @@ __global__ void embed_kernel(int H, int fmt, const void* table, const uint16_t* 
       v = ((const float*)table)[(size_t)tok * H + k];
     } else if (fmt == W_BF16) {
       v = bf16_to_f32(((const uint16_t*)table)[(size_t)tok * H + k]);
+    } else if (fmt == W_I8) {  // int8 per output row: w = s * q
+      v = bf16_to_f32(sc[tok]) * (float)((const int8_t*)table)[(size_t)tok * H + k];
     } else {  // MLX 4-bit: w = s * c + b, group 64 along the row
       const uint32_t word = ((const uint32_t*)table)[(size_t)tok * (H / 8) + k / 8];
       const float c = (float)((word >> (4 * (k & 7))) & 0xF);
@@ -356,6 +358,12 @@ __global__ void f32_to_f16_kernel(const float* src, _Float16* dst, size_t n) {
     dst[i] = (_Float16)src[i];
 }
 
+__global__ void i8_to_f16_kernel(const int8_t* q, const uint16_t* sc, int rows, int K, _Float16* dst) {
+  const size_t n = (size_t)rows * K;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = (_Float16)(bf16_to_f32(sc[i / K]) * (float)q[i]);
+}
+
 __global__ void q4_to_f16_kernel(const uint32_t* codes, const uint16_t* sc, const uint16_t* bi, int rows, int K,
                                  _Float16* dst) {
   const size_t n = (size_t)rows * K;
@@ -455,6 +463,12 @@ hipError_t launch_bf16_to_f16(const uint16_t* src, _Float16* dst, size_t n, hipS
 
 hipError_t launch_f32_to_f16(const float* src, _Float16* dst, size_t n, hipStream_t stream) {
   launch(f32_to_f16_kernel, dim3(grid_for(n, 256)), dim3(256), 0, stream, src, dst, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_i8_to_f16(const int8_t* q, const uint16_t* sc, int rows, int K, _Float16* dst,
+                            hipStream_t stream) {
+  launch(i8_to_f16_kernel, dim3(grid_for((size_t)rows * K, 256)), dim3(256), 0, stream, q, sc, rows, K, dst);
   return hipGetLastError();
 }
 

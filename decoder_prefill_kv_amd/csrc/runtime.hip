@@ -206,6 +206,7 @@ ScratchLayout scratch_layout(const dpk_config& c) {
 
 // bytes of the fragment-order decode copy of one [rows][cols] linear layer
 size_t tiled_bytes(const dpk_config& c, size_t rows, size_t cols) {
+  if (c.weight_format == DPK_FMT_I8) return 0;  // decoded straight from the row-major codes
   if (c.weight_format == DPK_FMT_BF16) return up(rows * cols * 2);
   return up(rows * cols / 2) + up(rows * (cols / 64) * 4);  // codes + (s, b) pairs
 }
@@ -278,7 +279,14 @@ struct ProfScope {
   ~ProfScope() { g_timing = LaunchTiming{}; }
 };
 
-double wbytes_per_elem(int fmt) { return fmt == DPK_FMT_F32 ? 4.0 : fmt == DPK_FMT_BF16 ? 2.0 : 0.5 + 4.0 / 64.0; }
+double wbytes_per_elem(int fmt) {
+  return fmt == DPK_FMT_F32 ? 4.0 : fmt == DPK_FMT_BF16 ? 2.0 : fmt == DPK_FMT_I8 ? 1.0 : 0.5 + 4.0 / 64.0;
+}
+
+// Kernel weight format of the model's linear layers (bf16 / q4 / i8 models).
+int wfmt(const dpk_model* md) {
+  return md->fmt == DPK_FMT_Q4G64 ? W_Q4 : md->fmt == DPK_FMT_I8 ? W_I8 : W_BF16;
+}
 
 dpk_status check_ready(const dpk_model* md) {
   if (!md) return fail(DPK_EINVAL, "null model");
@@ -322,7 +330,7 @@ dpk_status skinny(dpk_model* md, int cls, int M, const float* x, int ldx, const 
   SkinnyArgs a{};
   a.M = M;
   a.K = segs[0].cols;
-  a.fmt = md->fmt == DPK_FMT_Q4G64 ? W_Q4 : W_BF16;
+  a.fmt = wfmt(md);
   int n = 0;
   for (int i = 0; i < 3; ++i) {
     const LinearW& s = segs[i < nseg ? i : nseg - 1];
@@ -442,7 +450,7 @@ GemvArgs gemv_args(dpk_model* md, int M, const float* x, int ldx, const float* s
   GemvArgs a{};
   a.M = M;
   a.K = segs[0].cols;
-  a.fmt = md->fmt == DPK_FMT_Q4G64 ? W_Q4 : W_BF16;
+  a.fmt = wfmt(md);
   a.tiles = tiles;
   a.swiglu = swiglu;
   a.epi = epi;
@@ -592,9 +600,9 @@ dpk_status forward_batch(dpk_model* md, int M, int max_ctx, const int32_t* ids_d
 
 // Can a decode step of M rows run on the whole-K GEMV kernels?
 bool decode_fits(const dpk_model* md, int M) {
-  if (md->fmt == DPK_FMT_F32) return false;
+  if (md->fmt != DPK_FMT_BF16 && md->fmt != DPK_FMT_Q4G64) return false;
   const dpk_config& c = md->cfg;
-  const int fmt = md->fmt == DPK_FMT_Q4G64 ? W_Q4 : W_BF16;
+  const int fmt = wfmt(md);
   for (int K : {c.hidden, c.n_heads * c.head_dim, c.intermediate}) {
     if (K % 1024) return false;
     if (gemv_lds_bytes(M, K, 4, fmt) > 64 * 1024) return false;
@@ -612,7 +620,7 @@ dpk_status forward_decode(dpk_model* md, int M, int max_ctx, const int32_t* ids_
   const int H = c.hidden, Qd = c.n_heads * c.head_dim;
   {
     ProfScope ps(md, st, K_EMBED, (double)M * H * 6, 0);
-    HIP_TRY(launch_embed(M, H, md->fmt == DPK_FMT_Q4G64 ? W_Q4 : W_BF16, md->embed.w, md->embed.sc, md->embed.bi,
+    HIP_TRY(launch_embed(M, H, wfmt(md), md->embed.w, md->embed.sc, md->embed.bi,
                          md->rows_dev, ids_dev, c.vocab, md->h, nullptr, c.rms_eps, md->err_flag, st, md->sq));
   }
   int sq_nb = 1;
@@ -671,7 +679,7 @@ size_t mega_lds_for(dpk_model* md, int M, int max_ctx) {
   if (!decode_fits(md, M)) return 0;
   const int var = mega_variant(md);
   if (var < 0) return 0;
-  const int fmt = md->fmt == DPK_FMT_Q4G64 ? W_Q4 : W_BF16;
+  const int fmt = wfmt(md);
   const int H = c.hidden, Qd = c.n_heads * c.head_dim, I = c.intermediate;
   if ((max_ctx + mega_attn_chunk() - 1) / mega_attn_chunk() > MEGA_ATTN_MAXCH) return 0;
   size_t lds = mega_attn_lds_bytes(G);
@@ -729,7 +737,7 @@ dpk_status forward_mega(dpk_model* md, int M, int max_ctx, size_t lds, const Row
   a.layers = md->mega_layers;
   a.head = gemv_args(md, M, md->h, H, md->sq, H / 16, md->final_norm, &md->head, 1, EPI_HEAD, false, 1,
                      logits ? logits : md->sink, c.vocab, nullptr, argmax);
-  a.fmt = md->fmt == DPK_FMT_Q4G64 ? W_Q4 : W_BF16;
+  a.fmt = wfmt(md);
   a.small = mega_variant(md) == 1;
   a.emb = md->embed.w;
   a.emb_sc = md->embed.sc;
@@ -780,7 +788,7 @@ dpk_status head(dpk_model* md, int rows, const float* x, const float* rs, const 
   SkinnyArgs h{};
   h.M = rows;
   h.K = H;
-  h.fmt = md->fmt == DPK_FMT_Q4G64 ? W_Q4 : W_BF16;
+  h.fmt = wfmt(md);
   for (int i = 0; i < 3; ++i) {
     h.w[i] = hw.w;
     h.sc[i] = hw.sc;
@@ -824,7 +832,7 @@ dpk_status forward_skinny(dpk_model* md, int M, int max_ctx, const int32_t* ids_
   const int H = c.hidden;
   {
     ProfScope ps(md, st, K_EMBED, (double)M * H * 6, 0);
-    HIP_TRY(launch_embed(M, H, md->fmt == DPK_FMT_Q4G64 ? W_Q4 : W_BF16, md->embed.w, md->embed.sc, md->embed.bi,
+    HIP_TRY(launch_embed(M, H, wfmt(md), md->embed.w, md->embed.sc, md->embed.bi,
                          md->rows_dev, ids_dev, c.vocab, md->h, md->rs, c.rms_eps, md->err_flag, st));
   }
   dpk_status s;
@@ -870,7 +878,7 @@ dpk_status forward_gemm(dpk_model* md, int M, int start, int seq, bool want_head
   dpk_status s2;
   {
     ProfScope ps(md, st, K_EMBED, (double)M * H * 6, 0);
-    HIP_TRY(launch_embed(M, H, md->fmt == DPK_FMT_Q4G64 ? W_Q4 : W_BF16, md->embed.w, md->embed.sc, md->embed.bi,
+    HIP_TRY(launch_embed(M, H, wfmt(md), md->embed.w, md->embed.sc, md->embed.bi,
                          md->rows_dev, nullptr, c.vocab, md->h, nullptr, c.rms_eps, md->err_flag, st));
   }
   const double norm_bytes = (double)M * H * 6;
@@ -999,10 +1007,10 @@ dpk_status dpk_create(const dpk_config* cfg, dpk_model** out) {
   if (c.n_heads / c.n_kv_heads > 8) return fail(DPK_EINVAL, "at most 8 query heads per KV head");
   if (c.hidden % 256 || c.intermediate % 256 || (c.n_heads * c.head_dim) % 256)
     return fail(DPK_EINVAL, "hidden, intermediate and n_heads*head_dim must be multiples of 256");
-  if (c.weight_format < 0 || c.weight_format > 2) return fail(DPK_EINVAL, "unknown weight_format");
-  if (c.weight_format != DPK_FMT_F32 && c.head_dim != 128) return fail(DPK_EINVAL, "bf16/q4 need head_dim 128");
-  if (c.weight_format != DPK_FMT_F32 && !c.qk_norm) return fail(DPK_EINVAL, "bf16/q4 path needs qk_norm");
-  if (c.weight_format != DPK_FMT_F32 && c.vocab % 64) return fail(DPK_EINVAL, "bf16/q4 need vocab % 64 == 0");
+  if (c.weight_format < 0 || c.weight_format > 3) return fail(DPK_EINVAL, "unknown weight_format");
+  if (c.weight_format != DPK_FMT_F32 && c.head_dim != 128) return fail(DPK_EINVAL, "bf16/q4/i8 need head_dim 128");
+  if (c.weight_format != DPK_FMT_F32 && !c.qk_norm) return fail(DPK_EINVAL, "bf16/q4/i8 path needs qk_norm");
+  if (c.weight_format != DPK_FMT_F32 && c.vocab % 64) return fail(DPK_EINVAL, "bf16/q4/i8 need vocab % 64 == 0");
   if (c.max_batch < 1 || c.max_seq < 1 || c.max_rows < SKINNY_MAX)
     return fail(DPK_EINVAL, "max_batch, max_seq >= 1 and max_rows >= 16 required");
   if (!(c.rms_eps >= 0.0f) || !(c.rope_theta > 0.0)) return fail(DPK_EINVAL, "bad eps / theta");
@@ -1126,7 +1134,10 @@ dpk_status dpk_load_weights(dpk_model* md, const dpk_tensor* t, int32_t n, void*
   auto add_linear = [&](const std::string& name, LinearW* lw, int rows, int cols) {
     lw->rows = rows;
     lw->cols = cols;
-    if (fmt == DPK_FMT_Q4G64) {
+    if (fmt == DPK_FMT_I8) {
+      want[name + ".q"] = {DPK_DT_I8, rows, cols, &lw->w, false};
+      want[name + ".scales"] = {DPK_DT_BF16, rows, 1, (const void**)&lw->sc, false};
+    } else if (fmt == DPK_FMT_Q4G64) {
       want[name + ".codes"] = {DPK_DT_U32, rows, cols / 8, &lw->w, false};
       want[name + ".scales"] = {DPK_DT_BF16, rows, cols / 64, (const void**)&lw->sc, false};
       want[name + ".biases"] = {DPK_DT_BF16, rows, cols / 64, (const void**)&lw->bi, false};
@@ -1179,6 +1190,7 @@ dpk_status dpk_load_weights(dpk_model* md, const dpk_tensor* t, int32_t n, void*
     char* p = (char*)md->prep;
     auto conv = [&](const LinearW& w, _Float16* dst) -> hipError_t {
       if (fmt == DPK_FMT_BF16) return launch_bf16_to_f16((const uint16_t*)w.w, dst, (size_t)w.rows * w.cols, st);
+      if (fmt == DPK_FMT_I8) return launch_i8_to_f16((const int8_t*)w.w, w.sc, w.rows, w.cols, dst, st);
       return launch_q4_to_f16((const uint32_t*)w.w, w.sc, w.bi, w.rows, w.cols, dst, st);
     };
     for (int l = 0; l < c.n_layers; ++l) {
@@ -1203,6 +1215,7 @@ dpk_status dpk_load_weights(dpk_model* md, const dpk_tensor* t, int32_t n, void*
     }
     // fragment-order decode copies
     auto tile = [&](LinearW& w) -> hipError_t {
+      if (fmt == DPK_FMT_I8) return hipSuccess;  // no fragment-order copy
       w.wt = p;
       if (fmt == DPK_FMT_BF16) {
         p += up((size_t)w.rows * w.cols * 2);

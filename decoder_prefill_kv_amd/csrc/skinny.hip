@@ -16,6 +16,9 @@
 // (bit pattern 0x4300 | c) and accumulated per group:
 //   sum_k w x = s * sum (128+c) x + (b - 128 s) * sum x.
 //
+// int8 weights with one scale per output row (w = s * q) become the exact
+// bf16 value q in registers; the row scale multiplies the accumulated sum.
+//
 // Grid: x = row blocks, y = K splits.  The workgroup that finishes a row block
 // last sums the K-split partials in a fixed order (deterministic) and runs the
 // fused epilogue; the last row block to finish runs the grid-wide tail
@@ -47,7 +50,7 @@ __host__ __device__ inline SkinnyLds skinny_lds_layout(int M, int kchunk, int ro
   off = (off + 15) & ~15;
   int ng = kchunk / 64;
   L.xsum = off; off += (fmt == W_Q4 ? M * ng * 4 : 0);
-  L.qsc = off; off += (fmt == W_Q4 ? rows * ng * 4 : 0);  // fp32 s
+  L.qsc = off; off += (fmt == W_Q4 ? rows * ng * 4 : fmt == W_I8 ? rows * 4 : 0);  // fp32 s
   L.qbi = off; off += (fmt == W_Q4 ? rows * ng * 4 : 0);  // fp32 b - 128 s
   off = (off + 15) & ~15;
   L.fin = off; off += M * rows * 4;
@@ -154,6 +157,13 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(SkinnyArgs a) {
       qbi[lr * ng + g] = b - 128.0f * s;
     }
   }
+  if (FMT == W_I8) {  // the workgroup's row scales
+    for (int i = tid; i < rows; i += THREADS) {
+      int seg, srow;
+      map_row(a, block, i, seg, srow);
+      qsc[i] = bf16_to_f32(a.sc[seg][srow]);
+    }
+  }
   __syncthreads();
 
   // ---- main loop: each wave owns T row tiles of 16 rows
@@ -171,6 +181,8 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(SkinnyArgs a) {
     map_row(a, block, (wave * T + t) * 16 + r16, seg, srow);
     if (FMT == W_Q4)
       wrow[t] = (const unsigned char*)a.w[seg] + (size_t)srow * (a.K / 2) + k0 / 2;
+    else if (FMT == W_I8)
+      wrow[t] = (const unsigned char*)a.w[seg] + (size_t)srow * a.K + k0;
     else
       wrow[t] = (const unsigned char*)a.w[seg] + (size_t)srow * a.K * 2 + (size_t)k0 * 2;
   }
@@ -198,6 +210,44 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(SkinnyArgs a) {
         }
       }
     }
+  } else if (FMT == W_I8) {
+    for (int kk = 0; kk < kchunk; kk += KSTEP) {
+      u32x2 wq[T][8];
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          wq[t][s] = __builtin_nontemporal_load((const u32x2*)(wrow[t] + kk + 32 * s + 8 * j4));
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        u32x4 bh = {0u, 0u, 0u, 0u}, bl = {0u, 0u, 0u, 0u};
+        if (col_on) {
+          bh = *(const u32x4*)(xs_hi + r16 * L.xstride + kk + 32 * s + 8 * j4);
+          bl = *(const u32x4*)(xs_lo + r16 * L.xstride + kk + 32 * s + 8 * j4);
+        }
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          // 8 int8 codes -> 8 exact bf16 values (an integer of at most 8 bits)
+          uint32_t b16[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t word = e < 4 ? wq[t][s].x : wq[t][s].y;
+            const int q = (int)(int8_t)((word >> (8 * (e & 3))) & 0xFFu);
+            b16[e] = __float_as_uint((float)q) >> 16;
+          }
+          const u32x4 av = {b16[0] | (b16[1] << 16), b16[2] | (b16[3] << 16), b16[4] | (b16[5] << 16),
+                            b16[6] | (b16[7] << 16)};
+          const bf16x8 A = __builtin_bit_cast(bf16x8, av);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, bh), acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, bl), acc[t], 0, 0, 0);
+        }
+      }
+    }
+    // row scales: lane holds rows 4 j4 + v of each tile
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[t][v] *= qsc[(wave * T + t) * 16 + 4 * j4 + v];
   } else {  // W_Q4: per group of 64: lane k range 64g + 16 j4 + 8 t2 + e, t2 in {0,1}
     for (int kk = 0; kk < kchunk; kk += KSTEP) {
       u32x2 wc[T][4];
@@ -445,6 +495,8 @@ hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t stream) {
   else if (a.fmt == W_BF16 && tiles == 2) launch((skinny_kernel<W_BF16, 2>), grid, block, lds, stream, a);
   else if (a.fmt == W_Q4 && tiles == 1) launch((skinny_kernel<W_Q4, 1>), grid, block, lds, stream, a);
   else if (a.fmt == W_Q4 && tiles == 2) launch((skinny_kernel<W_Q4, 2>), grid, block, lds, stream, a);
+  else if (a.fmt == W_I8 && tiles == 1) launch((skinny_kernel<W_I8, 1>), grid, block, lds, stream, a);
+  else if (a.fmt == W_I8 && tiles == 2) launch((skinny_kernel<W_I8, 2>), grid, block, lds, stream, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

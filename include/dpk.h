@@ -58,11 +58,15 @@ typedef enum {
 typedef enum {
   DPK_FMT_F32 = 0,  /* fp32 weights, fp32 KV cache */
   DPK_FMT_BF16 = 1, /* bf16 weights, fp16 KV cache */
-  DPK_FMT_Q4G64 = 2 /* MLX 4-bit affine, group 64 along the input dim; fp16 KV cache */
+  DPK_FMT_Q4G64 = 2, /* MLX 4-bit affine, group 64 along the input dim; fp16 KV cache */
+  DPK_FMT_I8 = 3     /* int8 with one bf16 scale per output row (w = scale * q); fp16 KV cache.
+                        Decoded by the weight-streaming GEMV (one launch per kernel), prefilled
+                        through the fp16 GEMMs ("LLMs on the ANE", section "Quantized weights":
+                        int8 weights) */
 } dpk_format;
 
 /* Element types of dpk_tensor entries. */
-typedef enum { DPK_DT_F32 = 0, DPK_DT_BF16 = 1, DPK_DT_U32 = 2 } dpk_dtype;
+typedef enum { DPK_DT_F32 = 0, DPK_DT_BF16 = 1, DPK_DT_U32 = 2, DPK_DT_I8 = 3 } dpk_dtype;
 
 typedef struct {
   int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, intermediate, vocab;
@@ -101,7 +105,9 @@ typedef struct {
  * BF16 otherwise).  In DPK_FMT_Q4G64 each linear tensor (including
  * embed_tokens / lm_head) is three entries: "<name>.codes" U32 [out, in/8]
  * (element 8w+j in bits 4j..4j+3 of word w), "<name>.scales" and
- * "<name>.biases" BF16 [out, in/64].
+ * "<name>.biases" BF16 [out, in/64].  In DPK_FMT_I8 each linear tensor
+ * (including embed_tokens / lm_head) is two entries: "<name>.q" I8 [out, in]
+ * and "<name>.scales" BF16 [out, 1].
  */
 typedef struct {
   const char* name;
@@ -114,8 +120,8 @@ typedef struct dpk_model dpk_model;
 
 /* Validate the configuration and create a handle.  Supported shapes:
  * head_dim 64 or 128, n_heads a multiple of n_kv_heads with at most 8 query
- * heads per KV head, hidden and intermediate multiples of 256; bf16 / q4
- * models need head_dim 128.  Does not touch the GPU. */
+ * heads per KV head, hidden and intermediate multiples of 256; bf16 / q4 /
+ * i8 models need head_dim 128, per-head QK-norm and vocab % 64 == 0.  Does not touch the GPU. */
 dpk_status dpk_create(const dpk_config* cfg, dpk_model** out);
 
 /* Bytes of the three caller-provided device buffers:

@@ -19,7 +19,8 @@ What it computes (plain, slow, obviously correct; float64 by default):
 * The KV cache is resident state; a step writes one slot ("LLMs on the ANE",
   "Prefill and decode"; Butter notes, decode diagram).
 * MLX 4-bit affine weights: w = scale * code + bias per group of 64 inputs
-  (oxinfer 0.0.5 docs, "MLX checkpoints").
+  (oxinfer 0.0.5 docs, "MLX checkpoints"); int8 weights with one scale per
+  output row, w = scale * q ("LLMs on the ANE", "Quantized weights").
 * Greedy speculative verify: accept while draft[i] equals the argmax of row i,
   then one bonus token; a KV cache rolls back by moving its length cursor
   (Butter notes, speculative decoding loop; oxinfer docs, "Speculative
@@ -124,6 +125,13 @@ def dequant_q4(codes: np.ndarray, scales_bf16: np.ndarray, biases_bf16: np.ndarr
     return (c * s + b).to(dtype)
 
 
+def dequant_i8(q: np.ndarray, scales_bf16: np.ndarray, dtype=torch.float64) -> torch.Tensor:
+    """w[n, k] = scale[n] * q[n, k] (int8 with one scale per output row, the
+    int8 weights of "LLMs on the ANE", "Quantized weights"), in float64."""
+    s = torch.from_numpy(synth.bf16_bits_to_f32(scales_bf16)).to(torch.float64)
+    return (torch.from_numpy(q.astype(np.float64)) * s).to(dtype)
+
+
 class OracleModel:
     """The decoder with weights taken exactly as stored (bf16 widen exactly)."""
 
@@ -140,6 +148,8 @@ class OracleModel:
         if cfg.weight_format == "q4" and name + ".codes" in self.w:
             return dequant_q4(self.w[name + ".codes"], self.w[name + ".scales"],
                               self.w[name + ".biases"], self.dtype)
+        if cfg.weight_format == "i8" and name + ".q" in self.w:
+            return dequant_i8(self.w[name + ".q"], self.w[name + ".scales"], self.dtype)
         a = self.w[name]
         if a.dtype == np.uint16:
             return torch.from_numpy(synth.bf16_bits_to_f32(a)).to(self.dtype)
@@ -167,6 +177,9 @@ class OracleModel:
                                self.w["embed_tokens.biases"][i:i + 1], self.dtype)[0]
                     for i in ids]
             return torch.stack(rows)
+        if cfg.weight_format == "i8":
+            sel = np.array(ids, dtype=np.int64)
+            return dequant_i8(self.w["embed_tokens.q"][sel], self.w["embed_tokens.scales"][sel], self.dtype)
         E = self.w["embed_tokens"]
         rows = E[np.array(ids, dtype=np.int64)]
         if rows.dtype == np.uint16:

@@ -16,6 +16,10 @@ checkpoint.  Storage formats:
   becomes three arrays: ``name.codes`` uint32 ``[out, in/8]`` (element 8w+j in
   bits 4j..4j+3 of word w), ``name.scales`` and ``name.biases`` uint16 (bf16)
   ``[out, in/64]``.
+* ``i8``   - int8 with one scale per output row (symmetric per-channel
+  quantisation of the N(0, std) weights: scale = bf16(max |w| / 127),
+  q = round(w / scale) clipped to [-127, 127]).  A tensor ``name`` becomes
+  ``name.q`` int8 ``[out, in]`` and ``name.scales`` uint16 (bf16) ``[out, 1]``.
 """
 from __future__ import annotations
 
@@ -128,7 +132,7 @@ class ModelConfig:
     head_dim: int
     intermediate: int
     vocab: int
-    weight_format: str     # "f32" | "bf16" | "q4"
+    weight_format: str     # "f32" | "bf16" | "q4" | "i8"
     qk_norm: bool
     tied: bool
     rms_eps: float = 1e-6
@@ -188,7 +192,12 @@ Q06B = ModelConfig("q06b", 28, 1024, 16, 8, 128, 3072, 151936, "bf16", qk_norm=T
 Q06B_Q4 = ModelConfig("q06b_q4", 28, 1024, 16, 8, 128, 3072, 151936, "q4", qk_norm=True, tied=True)
 Q8B = ModelConfig("q8b", 36, 4096, 32, 8, 128, 12288, 151936, "bf16", qk_norm=True, tied=False)
 
-CONFIGS = {"tiny": TINY, "q06b": Q06B, "q06b_q4": Q06B_Q4, "q8b": Q8B}
+# int8 per-channel variants of the same shapes (other weight formats on the
+# same decode path)
+Q06B_I8 = Q06B.with_(family="q06b_i8", weight_format="i8")
+Q8B_I8 = Q8B.with_(family="q8b_i8", weight_format="i8")
+
+CONFIGS = {"tiny": TINY, "q06b": Q06B, "q06b_q4": Q06B_Q4, "q8b": Q8B, "q06b_i8": Q06B_I8, "q8b_i8": Q8B_I8}
 
 
 def _gain(cfg: ModelConfig, seed: int, name: str, shape) -> np.ndarray:
@@ -219,6 +228,11 @@ def _linear(cfg: ModelConfig, seed: int, name: str, shape) -> Dict[str, np.ndarr
         return {name: normal_f32(key_of(seed, tag), shape, cfg.init_std)}
     if cfg.weight_format == "bf16":
         return {name: normal_bf16(key_of(seed, tag), shape, cfg.init_std)}
+    if cfg.weight_format == "i8":
+        w = normal_f32(key_of(seed, tag), shape, cfg.init_std)
+        sc = f32_to_bf16_bits((np.abs(w).max(axis=1, keepdims=True) / 127.0).astype(np.float32))
+        q = np.clip(np.rint(w / bf16_bits_to_f32(sc)), -127, 127).astype(np.int8)
+        return {name + ".q": q, name + ".scales": sc}
     if cfg.weight_format == "q4":
         assert cols % 64 == 0
         return {

@@ -44,6 +44,11 @@ CASES = [
     ("q8b-L2-v4096-chunked", synth.Q8B.with_(n_layers=2, vocab=4096), 600, 4, dict(max_rows=256)),
     ("q8b-L2-v4096-multi", synth.Q8B.with_(n_layers=2, vocab=4096), 250, 12, dict(flags=MULTI, max_rows=256)),
     ("q8b-L2-v4096-persistent", synth.Q8B.with_(n_layers=2, vocab=4096), 250, 12, dict(max_rows=256)),
+    # int8 per-channel weights: GEMM prefill from the fp16 copy, weight-streaming decode
+    ("q06b_i8-L2-gemm", synth.Q06B_I8.with_(n_layers=2), 40, 8, {}),
+    ("q06b_i8-L2-stream", synth.Q06B_I8.with_(n_layers=2), 37, 6, dict(flags=STREAM)),
+    ("q8b_i8-L1-v4096-gemm", synth.Q8B_I8.with_(n_layers=1, vocab=4096), 21, 5, {}),
+    ("q8b_i8-L2-v4096-chunked", synth.Q8B_I8.with_(n_layers=2, vocab=4096), 300, 4, dict(max_rows=128)),
 ]
 
 
@@ -113,6 +118,7 @@ PATH_CASES = [
     ("q06b-L1", synth.Q06B.with_(n_layers=1), True),
     ("q06b_q4-L1", synth.Q06B_Q4.with_(n_layers=1), True),
     ("tiny-f32", synth.TINY, False),
+    ("q06b_i8-L1", synth.Q06B_I8.with_(n_layers=1), False),
 ]
 
 
@@ -160,6 +166,7 @@ VERIFY_CASES = [
     ("q06b_q4-L2-k11", synth.Q06B_Q4.with_(n_layers=2), 300, 11),
     ("q8b-L1-v4096-k5", synth.Q8B.with_(n_layers=1, vocab=4096), 254, 5),
     ("q8b-L1-v4096-k15", synth.Q8B.with_(n_layers=1, vocab=4096), 500, 15),
+    ("q06b_i8-L2-k5", synth.Q06B_I8.with_(n_layers=2), 70, 5),
 ]
 
 
@@ -182,7 +189,7 @@ def test_verify_matches_oracle(dpk, case):
     dec.prefill(0, [int(t) for t in prompt])
     acc = dec.verify(0, ids_in, P, am, lg)
     for i in range(K + 1):
-        compare_logits(lg[i].cpu(), ref["logits"][i], TOL["bf16"], "verify row %d" % i)
+        compare_logits(lg[i].cpu(), ref["logits"][i], TOL[cfg.weight_format], "verify row %d" % i)
     check_ids(am.cpu().tolist(), list(ref["logits"]), ref["argmax"], "verify")
     dpk.check_device_errors(dec.handle)
     assert acc == ref["accepted"]
@@ -257,6 +264,7 @@ BATCH16_CASES = [
     ("q8b-L1-v4096-M2", synth.Q8B.with_(n_layers=1, vocab=4096), [270, 31]),
     # 4-bit weights: the rows go through the 4-bit skinny GEMVs
     ("q06b_q4-L2-v4096-M16", synth.Q06B_Q4.with_(n_layers=2, vocab=4096), [40 + 13 * b for b in range(16)]),
+    ("q06b_i8-L2-v4096-M16", synth.Q06B_I8.with_(n_layers=2, vocab=4096), [40 + 13 * b for b in range(16)]),
 ]
 
 

@@ -1,6 +1,7 @@
 """Pins of the CPU oracle to facts other than itself (closed forms, library
 routines, brute force on tiny inputs, structural invariants).  CPU only."""
 import math
+import os
 
 import numpy as np
 import pytest
@@ -429,3 +430,120 @@ def test_fp32_path_agrees_with_fp64(synth_built):
     la = a.forward_block(a.new_cache(64), prompt, 0)[0]
     lb = b.forward_block(b.new_cache(64), prompt, 0)[0].double()
     assert float((la - lb).abs().max()) < 2e-3
+
+
+# ---------------------------------------------------------------------------
+# The float32 path at depth.  The 8B-shaped fixtures are written by the
+# oracle's float32 path (the float64 definition is too slow for their sizes),
+# so that path is pinned against float64 where the error could grow: the full
+# 28-layer 0.6B-shaped run, a 4-layer 8B-shaped model, and the full 36-layer
+# 8B-shaped prefill and first decode steps.  Bound: 2e-3 max-abs, ten times
+# inside the GPU tolerance.
+# ---------------------------------------------------------------------------
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+FP32_BOUND = 2e-3
+
+
+def _fp32_gap_report(name, gaps):
+    print("\n[fp32 vs fp64] %s: %s" % (name, ", ".join("%s %.3g" % kv for kv in gaps.items())))
+
+
+def test_fp32_path_full_qwen06b_against_stored_fp64(synth_built):
+    """28 layers, 512-token prefill and decode steps 0 and 1 (teacher-forced on
+    the stored greedy ids) against the float64 fixture's whole logit rows."""
+    with np.load(os.path.join(GOLDEN, "q06b.npz")) as z:
+        g = {k: z[k] for k in z.files}
+    cfg = synth.Q06B
+    P = int(g["prompt_len"])
+    w = synth.make_weights(cfg, 0)
+    m = oracle.OracleModel(cfg, w, torch.float32)
+    cache = m.new_cache(P + 2)
+    gaps = {"prefill": float(np.abs(m.forward_block(cache, synth.prompt_ids(cfg, P, 0), 0)[0].double().numpy()
+                                    - g["prefill_logits"].astype(np.float64)).max())}
+    full_rows = [int(r) for r in g["full_rows"]]
+    for s in range(2):
+        lg = m.forward_step(cache, int(g["id"][s]), P + s).double().numpy()
+        gaps["step %d" % s] = float(np.abs(lg - g["full_logits"][full_rows.index(s + 1)]).max())
+    _fp32_gap_report("q06b full", gaps)
+    assert max(gaps.values()) < FP32_BOUND, gaps
+
+
+def test_fp32_path_4layer_qwen8b_against_fp64(synth_built):
+    """The 8B shape (hidden 4096, 32/8 heads, MLP 12288, vocab 151936) with 4
+    layers: 256-token prefill and two decode steps, float32 against float64."""
+    cfg = synth.Q8B.with_(n_layers=4)
+    w = synth.make_weights(cfg, 0)
+    prompt = synth.prompt_ids(cfg, 256, 0)
+    runs = {}
+    for dt in (torch.float64, torch.float32):
+        m = oracle.OracleModel(cfg, w, dt, cache_weights=False)
+        cache = m.new_cache(258)
+        rows = [m.forward_block(cache, prompt, 0)[0].double()]
+        toks = runs[torch.float64][1] if dt == torch.float32 else None
+        fed = []
+        for s in range(2):
+            t = toks[s] if toks else oracle.argmax_lowest(rows[-1])
+            fed.append(t)
+            rows.append(m.forward_step(cache, t, 256 + s).double())
+        runs[dt] = (rows, fed)
+    gaps = {k: float((a - b).abs().max()) for k, a, b in
+            zip(("prefill", "step 0", "step 1"), runs[torch.float64][0], runs[torch.float32][0])}
+    _fp32_gap_report("q8b 4 layers", gaps)
+    assert max(gaps.values()) < FP32_BOUND, gaps
+
+
+def test_fp32_fixture_full_qwen8b_against_fp64_fixture():
+    """The 36-layer 8B-shaped fixture (float32 path: prefill of 2048 ids and
+    decode steps 0 and 1) against the float64 re-run of the same records."""
+    with np.load(os.path.join(GOLDEN, "q8b.npz")) as z:
+        g = {k: z[k] for k in z.files}
+    with np.load(os.path.join(GOLDEN, "q8b_f64.npz")) as z:
+        h = {k: z[k] for k in z.files}
+    assert list(h["fed_ids"]) == [int(x) for x in g["id"][:2]]
+    full_rows = [int(r) for r in g["full_rows"]]
+    refs = [g["prefill_logits"], g["full_logits"][full_rows.index(1)], g["full_logits"][full_rows.index(2)]]
+    gaps = {k: float(np.abs(a.astype(np.float64) - b).max())
+            for k, a, b in zip(("prefill", "step 0", "step 1"), refs, h["logits"])}
+    _fp32_gap_report("q8b full (fixtures)", gaps)
+    assert max(gaps.values()) < FP32_BOUND, gaps
+
+
+# ---------------------------------------------------------------- int8 weights
+def test_i8_dequant_hand_values_and_requant(synth_built):
+    from oracle.decoder import dequant_i8
+    q = np.array([[3, -5, 127], [0, -127, 1]], dtype=np.int8)
+    sc = synth.f32_to_bf16_bits(np.array([[0.5], [0.015625]], dtype=np.float32))
+    W = dequant_i8(q, sc)
+    assert W.tolist() == [[1.5, -2.5, 63.5], [0.0, -1.984375, 0.015625]]
+    cfg = synth.Q06B.with_(family="i8pin", weight_format="i8", n_layers=1, vocab=512)
+    w = synth.make_weights(cfg, 3)
+    for name in ("layers.0.mlp.down_proj", "embed_tokens"):
+        q, sc = w[name + ".q"], w[name + ".scales"]
+        s = torch.from_numpy(synth.bf16_bits_to_f32(sc)).double()
+        Wd = dequant_i8(q, sc)
+        assert torch.equal(torch.round(Wd / s).to(torch.int64), torch.from_numpy(q.astype(np.int64)))
+        assert int(np.abs(q.astype(np.int32)).max(axis=1).min()) >= 126  # per-row absmax scaling
+        # within half a step of the N(0, std) draw it was quantised from
+        ref = synth.normal_f32(synth.key_of(3, cfg.family + "/" + name), q.shape, cfg.init_std)
+        assert float((Wd - torch.from_numpy(ref).double()).abs().div(s).max()) <= 0.5 + 1e-3
+
+
+def test_i8_model_equals_f32_model_with_the_dequantized_weights(synth_built):
+    """scale (bf16, 8 significant bits) times q (int8) is exact in fp32, so
+    the int8 model must equal an fp32-format model holding those products."""
+    from oracle.decoder import dequant_i8
+    cfg = synth.Q06B.with_(family="i8pin2", weight_format="i8", n_layers=2, vocab=512, hidden=256, n_heads=4,
+                           n_kv_heads=2, intermediate=512)
+    w = synth.make_weights(cfg, 1)
+    f = {}
+    for k, v in w.items():
+        if k.endswith(".q"):
+            f[k[:-2]] = dequant_i8(v, w[k[:-2] + ".scales"], torch.float32).numpy()
+        elif not k.endswith(".scales"):
+            f[k] = synth.bf16_bits_to_f32(v)
+    cf = cfg.with_(weight_format="f32")
+    prompt = synth.prompt_ids(cfg, 12, 0)
+    a = oracle.OracleModel(cfg, w).forward_block(oracle.OracleModel(cfg, w).new_cache(12), prompt, 0)
+    mb = oracle.OracleModel(cf, f)
+    b = mb.forward_block(mb.new_cache(12), prompt, 0)
+    assert float((a - b).abs().max()) == 0.0
