@@ -27,7 +27,8 @@ DT_F32, DT_BF16, DT_U32, DT_I8 = 0, 1, 2, 3
 SYMBOLS = ["dpk_create", "dpk_workspace_size", "dpk_bind_workspace", "dpk_load_weights", "dpk_prefill",
            "dpk_prefill_at", "dpk_decode_step", "dpk_verify", "dpk_seq_length", "dpk_check_device_errors",
            "dpk_test_set_barrier_abort", "dpk_profile_begin", "dpk_profile_end", "dpk_spec_generate", "dpk_sample",
-           "dpk_spec_accept_workspace_size", "dpk_spec_accept", "dpk_last_error", "dpk_destroy"]
+           "dpk_spec_accept_workspace_size", "dpk_spec_accept", "dpk_spec_accept_noalloc", "dpk_last_error",
+           "dpk_destroy"]
 
 
 class DpkError(RuntimeError):
@@ -98,6 +99,7 @@ def _load():
         "dpk_spec_accept_workspace_size": [i32, sz],
         "dpk_spec_accept": [vp, vp, ctypes.c_int64, i32, i32, vp, ctypes.POINTER(Sampler), vp, vp, vp, vp,
                             ctypes.c_size_t, vp],
+        "dpk_spec_accept_noalloc": [vp, vp, ctypes.c_int64, i32, i32, vp, ctypes.POINTER(Sampler), vp, vp, vp, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -271,6 +273,17 @@ def spec_accept(target_logits, draft_logits, drafts_dev, r_dev, u_dev, out_dev, 
                                  target_logits.shape[1], k, _ptr(drafts_dev), ctypes.byref(sp), _ptr(r_dev),
                                  _ptr(u_dev), _ptr(out_dev), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def spec_accept_noalloc(target_logits, draft_logits, drafts_dev, r_dev, u_dev, out_dev, temperature: float,
+                        top_k: int = 0, top_p: float = 1.0, stream=None):
+    """spec_accept with the library's built-in workspace (no allocation)."""
+    k = draft_logits.shape[0]
+    assert target_logits.stride(0) == draft_logits.stride(0)
+    sp = Sampler(temperature, top_k, top_p)
+    _check(lib().dpk_spec_accept_noalloc(_ptr(target_logits), _ptr(draft_logits), target_logits.stride(0),
+                                         target_logits.shape[1], k, _ptr(drafts_dev), ctypes.byref(sp),
+                                         _ptr(r_dev), _ptr(u_dev), _ptr(out_dev), _stream(stream)))
 
 
 def destroy(model: int):

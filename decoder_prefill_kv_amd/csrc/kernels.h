@@ -308,6 +308,11 @@ hipError_t launch_sample(const float* logits, long long ld, int rows, int V, flo
 // Bytes of the per-row distribution records speculative acceptance of K
 // drafts keeps in its workspace.
 size_t spec_dist_bytes(int K);
+// The allocation-free acceptance's workspace: the device address of a
+// file-scope array on the current device (looked up once per device), and
+// the most drafts one call may have.
+hipError_t spec_noalloc_scratch(void** ptr);
+int spec_noalloc_max_k();
 // Speculative-sampling acceptance of K drafts: out[0] = accepted count,
 // out[1] = next token (residual or bonus draw).
 hipError_t launch_spec_accept(const float* target, const float* draft, long long ld, int V, int K, float T,

@@ -1606,6 +1606,25 @@ dpk_status dpk_spec_accept(const float* target_logits, const float* draft_logits
   return DPK_OK;
 }
 
+dpk_status dpk_spec_accept_noalloc(const float* target_logits, const float* draft_logits, int64_t ld, int32_t vocab,
+                                   int32_t k, const int32_t* drafts, const dpk_sampler* sp, const float* r,
+                                   const float* u, int32_t* out, void* stream) {
+  if (!target_logits || !draft_logits || !drafts || !r || !u || !out) return fail(DPK_EINVAL, "null argument");
+  if (k < 1 || k > spec_noalloc_max_k())
+    return fail(DPK_EINVAL, "k = %d outside [1, %d], the most drafts the built-in workspace holds", k,
+                spec_noalloc_max_k());
+  if (vocab < 1 || ld < vocab) return fail(DPK_EINVAL, "vocab >= 1 and ld >= vocab required");
+  dpk_status s = check_sampler(sp);
+  if (s) return s;
+  void* ws = nullptr;
+  hipError_t e = spec_noalloc_scratch(&ws);
+  if (e != hipSuccess) return fail(DPK_EHIP, "built-in workspace lookup failed: %s", hipGetErrorString(e));
+  e = launch_spec_accept(target_logits, draft_logits, ld, vocab, k, sp->temperature, sp->top_k, sp->top_p, drafts, r,
+                         u, ws, out, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(DPK_EHIP, "speculative acceptance launch failed: %s", hipGetErrorString(e));
+  return DPK_OK;
+}
+
 void dpk_destroy(dpk_model* md) {
   if (!md) return;
   for (hipEvent_t e : md->prof_ev) (void)hipEventDestroy(e);

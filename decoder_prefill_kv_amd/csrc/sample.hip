@@ -21,6 +21,8 @@
 // the target extends the prefix.  Weights are summed as 64-bit fixed point
 // (2^40 per unit), so every sum and every decision is independent of the
 // order the threads add in: the same logits give the same token on every run.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -361,9 +363,43 @@ __global__ __launch_bounds__(ST) void spec_accept_kernel(const float* target, co
   }
 }
 
+// Workspace of the allocation-free acceptance entry point: the per-row
+// distribution records of one call with up to SPEC_NOALLOC_MAX_K drafts.  One
+// copy per GPU, shared by every call on that GPU (calls that overlap on one
+// GPU race on it); each call writes every record it reads, so nothing needs
+// clearing between calls.
+constexpr int SPEC_NOALLOC_MAX_K = 16;
+constexpr size_t SPEC_NOALLOC_BYTES = 4096;
+static_assert((2 * SPEC_NOALLOC_MAX_K + 1) * sizeof(Dist) <= SPEC_NOALLOC_BYTES, "records fit the scratch array");
+static __device__ __align__(256) unsigned char scratch[SPEC_NOALLOC_BYTES];
+
 }  // namespace
 
 size_t spec_dist_bytes(int K) { return (size_t)(2 * K + 1) * sizeof(Dist); }
+
+int spec_noalloc_max_k() { return SPEC_NOALLOC_MAX_K; }
+
+// Device address of `scratch` on the current device.  The array's name is a
+// host-side stand-in in host code; its device address comes from the runtime,
+// looked up once per device (with that device current) and kept.
+hipError_t spec_noalloc_scratch(void** ptr) {
+  constexpr int MAX_DEV = 64;
+  static std::mutex mu;
+  static void* addr[MAX_DEV] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEV) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_sample(const float* logits, long long ld, int rows, int V, float T, int top_k, float top_p,
                          const float* u, int* out, hipStream_t stream) {

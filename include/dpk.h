@@ -318,6 +318,18 @@ dpk_status dpk_spec_accept(const float* target_logits_dev, const float* draft_lo
                            const float* u_dev, int32_t* out_dev, void* workspace_dev, size_t workspace_bytes,
                            void* stream);
 
+/* dpk_spec_accept without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The distribution records live in a
+ * 4 KB array built into the library, one per GPU, held until the process
+ * ends; k may be at most 16.  Every call on one GPU shares that array, so
+ * calls that overlap on one GPU (concurrent streams or threads) race and
+ * must be serialized by the caller.  Allocates nothing (no hipMalloc, no
+ * allocating library call); arguments and results as dpk_spec_accept. */
+dpk_status dpk_spec_accept_noalloc(const float* target_logits_dev, const float* draft_logits_dev, int64_t ld,
+                                   int32_t vocab, int32_t k, const int32_t* drafts_dev, const dpk_sampler* sp,
+                                   const float* r_dev, const float* u_dev, int32_t* out_dev, void* stream);
+
 /* Message of the last failure on the calling thread (valid until the next
  * call on this thread); "" if none. */
 const char* dpk_last_error(void);
