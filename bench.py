@@ -74,19 +74,46 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(cfg, w):
-    """The oracle (float64, weights widened per use) on a bounded sample: one
-    decode step of the full model at an empty cache."""
+def host_info():
+    """CPUs this process may run on and the host's CPU model."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncpu = os.cpu_count() or 0
+    return {"nproc": ncpu, "cpu_model": model}
+
+
+def cpu_baseline(cfg, w, prompt, n_prefix=32):
+    """The oracle as it stands (float64, weights widened from bf16 per use) on a
+    bounded sample of the workload: the block path over the first n_prefix
+    prompt ids (prompt tok/s), then one step-path decode step at position
+    n_prefix (decode tok/s)."""
     import torch
     import oracle
     m = oracle.OracleModel(cfg, w, torch.float64, cache_weights=False)
-    cache = m.new_cache(4)
+    cache = m.new_cache(n_prefix + 1)
     t0 = time.perf_counter()
-    m.forward_step(cache, 1, 0)
-    dt = time.perf_counter() - t0
-    return {"value": 1.0 / dt, "unit": "tok/s", "cores": torch.get_num_threads(), "kind": "oracle",
-            "sample": "1 decode step (step path, fp64, weights widened from bf16 per use) of the full model "
-                      "at position 0; %.1f s" % dt}
+    lg = m.forward_block(cache, prompt[:n_prefix], 0)[0]
+    t_pre = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    m.forward_step(cache, oracle.argmax_lowest(lg), n_prefix)
+    t_dec = time.perf_counter() - t0
+    out = {"value": round(1.0 / t_dec, 5), "unit": "tok/s", "cores": torch.get_num_threads(), "kind": "oracle",
+           "prefill_tok_s": round(n_prefix / t_pre, 4),
+           "sample": "float64 oracle, weights widened from bf16 per use: block-path prefill of the workload "
+                     "prompt's first %d ids (%.1f s), then one step-path decode step at position %d (%.1f s); "
+                     "value is that decode rate, prefill_tok_s the prompt rate" % (n_prefix, t_pre, n_prefix, t_dec)}
+    out.update(host_info())
+    return out
 
 
 def copy_probe(nbytes):
@@ -134,6 +161,20 @@ def class_times(stats, passes):
     return out
 
 
+class DeviceError(RuntimeError):
+    pass
+
+
+def check_device(dpk, dec, what):
+    """Raise if the library saw a device-side error (a persistent step's
+    bounded barrier wait that gave up, or an out-of-range device token id)
+    since the last check: the timed work would not be valid."""
+    try:
+        dpk.check_device_errors(dec.handle)
+    except dpk.DpkError as e:
+        raise DeviceError("%s: %s" % (what, e))
+
+
 def bench_verify(dpk, cfg, w, seed, flags, K=5, rounds=24, warm=4):
     """Speculative verify of K drafts (M = K + 1 rows) against the KV cache of
     an 8192-token prompt: passes/s, and the ratio to one decode step at the
@@ -159,6 +200,7 @@ def bench_verify(dpk, cfg, w, seed, flags, K=5, rounds=24, warm=4):
             times.append(dt)
         pos += acc + 1
     vt = sum(times) / len(times)
+    check_device(dpk, dec, "verify passes")
     # one more pass with per-launch timing: where a verify pass spends its time
     dpk.profile_begin(dec.handle, 100000)
     acc = dec.verify(0, drafts[0:K + 1], pos, am, lg)
@@ -176,6 +218,7 @@ def bench_verify(dpk, cfg, w, seed, flags, K=5, rounds=24, warm=4):
     e1.record()
     torch.cuda.synchronize()
     dt_dec = e0.elapsed_time(e1) / 8 / 1e3
+    check_device(dpk, dec, "verify profiled pass and decode steps")
     dec.close()
     H, L, d = cfg.hidden, cfg.n_layers, cfg.head_dim
     wbytes = (cfg.n_linear_params() + cfg.vocab * H) * 2.0
@@ -208,10 +251,12 @@ def bench_batch16(dpk, cfg, w, seed, flags, B=16, P=4096, N=32):
     e1.record()
     torch.cuda.synchronize()
     dt = e0.elapsed_time(e1) / N / 1e3
+    check_device(dpk, dec, "batch-16 steps")
     # one more step with per-launch timing: where a batch step spends its time
     dpk.profile_begin(dec.handle, 100000)
     dec.decode_step(seqs, None, [P + 1 + N] * B, am, lg, ids_dev=am)
     classes = class_times(dpk.profile_end(dec.handle), 1)
+    check_device(dpk, dec, "batch-16 profiled step")
     dec.close()
     H, L, d = cfg.hidden, cfg.n_layers, cfg.head_dim
     wbytes = (cfg.n_linear_params() + cfg.vocab * H) * 2.0
@@ -220,6 +265,121 @@ def bench_batch16(dpk, cfg, w, seed, flags, B=16, P=4096, N=32):
             "tok_s": round(B / dt, 1), "ms_per_step": round(dt * 1e3, 3),
             "hbm_frac": round((wbytes + kv) / dt / 1e9 / HBM_PEAK_GBS, 4),
             "kernel_classes_us_per_step": classes}
+
+
+def run_workload(dpk, name, steps, warmup, seed, flags, decode_steps=None, profile=True, w=None):
+    """Prefill + greedy batch-1 decode of one workload: steps timed passes after
+    warmup untimed ones.  Returns (result dict, host weights)."""
+    import torch
+    import synth
+    cname, P, N, desc = WORKLOADS[name]
+    if decode_steps is not None:
+        N = decode_steps
+    cfg = synth.CONFIGS[cname]
+    t0 = time.time()
+    if w is None:
+        w = synth.make_weights(cfg, seed)
+    log("[bench] %s: weights generated in %.1f s" % (name, time.time() - t0))
+    prompt = [int(t) for t in synth.prompt_ids(cfg, P, seed)]
+    stream = torch.cuda.current_stream()
+    t0 = time.time()
+    dec = dpk.Decoder(cfg, w, max_batch=1, max_seq=P + N, max_rows=P, flags=flags)
+    torch.cuda.synchronize()
+    log("[bench] %s: weights on device in %.1f s (kv %.2f GB, scratch %.2f GB, prep %.2f GB)"
+        % ((name, time.time() - t0) + tuple(x / 1e9 for x in dec.sizes)))
+    lg = dec.logits_buffer(1)
+    am = dec.argmax_buffer(1)
+
+    def one_step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        dec.prefill(0, prompt, lg, am)
+        if ev:
+            ev[1].record(stream)
+        for s in range(N):
+            dec.decode_step([0], None, [P + s], am, lg, ids_dev=am)
+        if ev:
+            ev[2].record(stream)
+
+    for i in range(warmup):
+        one_step()
+        torch.cuda.synchronize()
+        log("[bench] %s: warmup %d done" % (name, i))
+    check_device(dpk, dec, name + " warmup")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        one_step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    check_device(dpk, dec, name + " timed steps")
+    pre_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    log("[bench] %s: timed %d steps: %.1f ms/step (prefill %.2f ms, decode %.1f ms)"
+        % (name, steps, wall * 1e3 / steps, pre_ms, dec_ms))
+    decode_tps = N / (dec_ms / 1e3)
+    prefill_tps = P / (pre_ms / 1e3)
+
+    # algorithmic work of the workload
+    H, L, d = cfg.hidden, cfg.n_layers, cfg.head_dim
+    n_lin = cfg.n_linear_params()
+    head_params = cfg.vocab * H
+    wbytes = {"bf16": 2.0, "f32": 4.0, "q4": 0.5 + 4.0 / 64}[cfg.weight_format]
+    kv_elt = 4 if cfg.weight_format == "f32" else 2
+    kv_per_pos = 2 * L * cfg.n_kv_heads * d * kv_elt
+    mean_ctx = P + (N + 1) / 2.0
+    decode_bytes_tok = (n_lin + head_params) * wbytes + kv_per_pos * mean_ctx
+    prefill_flops = 2.0 * n_lin * P + 4.0 * L * cfg.n_heads * d * P * (P + 1) / 2 + 2.0 * head_params
+
+    roof = roof_prefill = kernels = None
+    if profile:
+        dpk.profile_begin(dec.handle, 200000)
+        one_step()
+        stats = dpk.profile_end(dec.handle)
+        check_device(dpk, dec, name + " profiled step")
+        kernels = {k: {"launches": v["launches"], "avg_us": round(1e3 * v["total_ms"] / v["launches"], 2),
+                       "total_ms": round(v["total_ms"], 3)} for k, v in stats.items()}
+        dec_cls = {k: v for k, v in stats.items()
+                   if k.startswith("gemv") or k.startswith("attn.decode") or k == "decode.step"}
+        dom = max(dec_cls, key=lambda k: dec_cls[k]["total_ms"])
+        v = stats[dom]
+        avg_s = v["total_ms"] / 1e3 / v["launches"]
+        ach = v["bytes"] / v["launches"] / avg_s / 1e9
+        roof = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name, dom),
+                "bytes_per_launch": v["bytes"] / v["launches"], "avg_launch_us": round(avg_s * 1e6, 2)}
+        gem = {k: v for k, v in stats.items() if k.startswith("gemm")}
+        if gem:
+            domg = max(gem, key=lambda k: gem[k]["total_ms"])
+            g = gem[domg]
+            avg_g = g["total_ms"] / 1e3 / g["launches"]
+            achg = g["flops"] / g["launches"] / avg_g / 1e12
+            roof_prefill = {"bound": "mfma", "kernel": domg, "achieved": round(achg, 1), "peak": MFMA_PEAK_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(achg / MFMA_PEAK_TFLOPS, 4),
+                            "traffic": measured_traffic(name, domg),
+                            "flops_per_launch": g["flops"] / g["launches"], "avg_launch_us": round(avg_g * 1e6, 2)}
+    dec.close()
+    del dec
+    torch.cuda.empty_cache()
+    res = {"workload": desc, "prompt_tokens": P, "decode_steps": N,
+           "decode_tok_s": round(decode_tps, 2), "prefill_tok_s": round(prefill_tps, 1),
+           "prefill_ms": round(pre_ms, 3), "decode_ms_per_token": round(dec_ms / N, 4),
+           "ms_per_step": round(wall * 1e3 / steps, 3),
+           "decode_hbm_frac": round(decode_bytes_tok * decode_tps / 1e9 / HBM_PEAK_GBS, 4),
+           "decode_bytes_per_token": decode_bytes_tok,
+           "prefill_mfma_frac": round(prefill_flops / (pre_ms / 1e3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+           "prefill_flops": prefill_flops,
+           "roofline": roof, "roofline_prefill": roof_prefill, "kernels": kernels}
+    return res, w, cfg, prompt
+
+
+# The pages' own figures for this path (Apple M2 Pro Neural Engine, fp16;
+# "LLMs on the ANE", ANEForge docs): context, not the target.
+PAGES_CONTEXT = {"hardware": "Apple M2 Pro Neural Engine, fp16 weights",
+                 "source": "LLMs on the ANE (ANEForge docs), prefill / decode figures",
+                 "qwen3_0.6b_prefill_tok_s": 8600, "qwen3_0.6b_decode_tok_s": 75, "qwen3_8b_decode_tok_s": 7.5}
 
 
 def main():
@@ -232,7 +392,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel profiled pass")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the verify (K=5 over 8192 tokens) and batch-16 decode measurements")
+                    help="skip the verify (K=5 over 8192 tokens), batch-16 decode and 0.6B-shaped measurements")
     ap.add_argument("--decode-path", choices=["auto", "multi"], default="auto",
                     help="auto: one persistent launch per decode step where the shapes allow it; "
                          "multi: one launch per kernel")
@@ -249,110 +409,32 @@ def main():
         sys.exit(2)
 
     import torch
-    import synth
     import decoder_prefill_kv_amd as dpk
 
-    cname, P, N, desc = WORKLOADS[args.workload]
-    if args.decode_steps is not None:
-        N = args.decode_steps
-    cfg = synth.CONFIGS[cname]
-    t0 = time.time()
-    w = synth.make_weights(cfg, args.seed)
-    log("[bench] weights generated in %.1f s" % (time.time() - t0))
-    prompt = [int(t) for t in synth.prompt_ids(cfg, P, args.seed)]
     torch.cuda.init()
-    stream = torch.cuda.current_stream()
-    t0 = time.time()
-    dec = dpk.Decoder(cfg, w, max_batch=1, max_seq=P + N, max_rows=P,
-                      flags=2 if args.decode_path == "multi" else 0)  # DPK_FLAG_DECODE_MULTI
-    torch.cuda.synchronize()
-    log("[bench] weights on device in %.1f s (kv %.2f GB, scratch %.2f GB, prep %.2f GB)"
-        % ((time.time() - t0,) + tuple(x / 1e9 for x in dec.sizes)))
-    lg = dec.logits_buffer(1)
-    am = dec.argmax_buffer(1)
-
-    def one_step(ev=None):
-        if ev:
-            ev[0].record(stream)
-        dec.prefill(0, prompt, lg, am)
-        if ev:
-            ev[1].record(stream)
-        for s in range(N):
-            dec.decode_step([0], None, [P + s], am, lg, ids_dev=am)
-        if ev:
-            ev[2].record(stream)
-
-    for i in range(args.warmup):
-        one_step()
-        torch.cuda.synchronize()
-        log("[bench] warmup %d done" % i)
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        one_step(evs[k])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    pre_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    log("[bench] timed %d steps: %.1f ms/step (prefill %.2f ms, decode %.1f ms)"
-        % (args.steps, wall * 1e3 / args.steps, pre_ms, dec_ms))
-    decode_tps = N / (dec_ms / 1e3)
-    prefill_tps = P / (pre_ms / 1e3)
-
-    # algorithmic work of the workload
-    H, L, d = cfg.hidden, cfg.n_layers, cfg.head_dim
-    n_lin = cfg.n_linear_params()
-    head_params = cfg.vocab * H
-    wbytes = {"bf16": 2.0, "f32": 4.0, "q4": 0.5 + 4.0 / 64}[cfg.weight_format]
-    kv_elt = 4 if cfg.weight_format == "f32" else 2
-    kv_per_pos = 2 * L * cfg.n_kv_heads * d * kv_elt
-    mean_ctx = P + (N + 1) / 2.0
-    decode_bytes_tok = (n_lin + head_params) * wbytes + kv_per_pos * mean_ctx
-    prefill_flops = 2.0 * n_lin * P + 4.0 * L * cfg.n_heads * d * P * (P + 1) / 2 + 2.0 * head_params
-
-    roof = None
-    roof_prefill = None
-    kernels = None
-    if not args.no_profile:
-        dpk.profile_begin(dec.handle, 200000)
-        one_step()
-        stats = dpk.profile_end(dec.handle)
-        kernels = {k: {"launches": v["launches"], "avg_us": round(1e3 * v["total_ms"] / v["launches"], 2),
-                       "total_ms": round(v["total_ms"], 3)} for k, v in stats.items()}
-        dec_cls = {k: v for k, v in stats.items()
-                   if k.startswith("gemv") or k.startswith("attn.decode") or k == "decode.step"}
-        dom = max(dec_cls, key=lambda k: dec_cls[k]["total_ms"])
-        v = stats[dom]
-        avg_s = v["total_ms"] / 1e3 / v["launches"]
-        ach = v["bytes"] / v["launches"] / avg_s / 1e9
-        roof = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload, dom),
-                "bytes_per_launch": v["bytes"] / v["launches"], "avg_launch_us": round(avg_s * 1e6, 2)}
-        gem = {k: v for k, v in stats.items() if k.startswith("gemm")}
-        if gem:
-            domg = max(gem, key=lambda k: gem[k]["total_ms"])
-            g = gem[domg]
-            avg_g = g["total_ms"] / 1e3 / g["launches"]
-            achg = g["flops"] / g["launches"] / avg_g / 1e12
-            roof_prefill = {"bound": "mfma", "kernel": domg, "achieved": round(achg, 1), "peak": MFMA_PEAK_TFLOPS,
-                            "unit": "TFLOP/s", "frac": round(achg / MFMA_PEAK_TFLOPS, 4),
-                            "traffic": measured_traffic(args.workload, domg),
-                            "flops_per_launch": g["flops"] / g["launches"], "avg_launch_us": round(avg_g * 1e6, 2)}
-
-    dec.close()
-    extra = {}
-    if not args.no_extra and args.workload == "q8b" and args.decode_steps is None:
-        flags = 2 if args.decode_path == "multi" else 0
-        torch.cuda.empty_cache()
-        log("[bench] verify K=5 over an 8192-token cache ...")
-        extra["verify"] = bench_verify(dpk, cfg, w, args.seed, flags)
-        log("[bench] verify: %s" % extra["verify"])
-        torch.cuda.empty_cache()
-        log("[bench] batch-16 decode over 4096-token caches ...")
-        extra["batch16"] = bench_batch16(dpk, cfg, w, args.seed, flags)
-        log("[bench] batch16: %s" % extra["batch16"])
+    flags = 2 if args.decode_path == "multi" else 0  # DPK_FLAG_DECODE_MULTI
+    try:
+        head, w, cfg, prompt = run_workload(dpk, args.workload, args.steps, args.warmup, args.seed, flags,
+                                            args.decode_steps, not args.no_profile)
+        extra = {}
+        if not args.no_extra and args.workload == "q8b" and args.decode_steps is None:
+            log("[bench] verify K=5 over an 8192-token cache ...")
+            extra["verify"] = bench_verify(dpk, cfg, w, args.seed, flags)
+            log("[bench] verify: %s" % extra["verify"])
+            torch.cuda.empty_cache()
+            log("[bench] batch-16 decode over 4096-token caches ...")
+            extra["batch16"] = bench_batch16(dpk, cfg, w, args.seed, flags)
+            log("[bench] batch16: %s" % extra["batch16"])
+            torch.cuda.empty_cache()
+            # the 0.6B-shaped workloads (bf16 and 4-bit), same measurement
+            for name in ("q06b", "q06b_q4"):
+                r, _, _, _ = run_workload(dpk, name, 2, 1, args.seed, flags)
+                extra[name] = r
+                log("[bench] %s: decode %.1f tok/s, prefill %.0f tok/s"
+                    % (name, r["decode_tok_s"], r["prefill_tok_s"]))
+    except DeviceError as e:
+        print("bench.py: device-side error, no result reported: %s" % e, file=sys.stderr, flush=True)
+        sys.exit(3)
 
     mem = membench()
     log("[bench] membench: %s" % mem)
@@ -360,39 +442,33 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
-        cpu = cpu_baseline(cfg, w)
-        log("[bench] cpu oracle: %.4f tok/s" % cpu["value"])
+        cpu = cpu_baseline(cfg, w, prompt)
+        log("[bench] cpu oracle: %s" % cpu)
 
     out = {
         "metric": "decode tok/s & prefill tok/s, 8B-shaped bf16, 1 MI355X; % HBM / MFMA peak",
-        "value": round(decode_tps, 2),
+        "value": head["decode_tok_s"],
         "unit": "tok/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall * 1e3 / args.steps, 3),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if cfg.weight_format == "bf16" else cfg.weight_format,
         "data": "synthetic (seeded N(0,0.02) weights, uniform random prompt ids)",
-        "config": {"workload": desc, "prompt_tokens": P, "decode_steps": N, "batch": 1,
-                   "decode_path": args.decode_path},
-        "decode_tok_s": round(decode_tps, 2),
-        "prefill_tok_s": round(prefill_tps, 1),
-        "prefill_ms": round(pre_ms, 3),
-        "decode_ms_per_token": round(dec_ms / N, 4),
-        "decode_hbm_frac": round(decode_bytes_tok * decode_tps / 1e9 / HBM_PEAK_GBS, 4),
-        "decode_bytes_per_token": decode_bytes_tok,
-        "prefill_mfma_frac": round(prefill_flops / (pre_ms / 1e3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
-        "prefill_flops": prefill_flops,
+        "config": {"workload": head["workload"], "prompt_tokens": head["prompt_tokens"],
+                   "decode_steps": head["decode_steps"], "batch": 1, "decode_path": args.decode_path},
         "prefill_dtype": "fp16 operands, fp32 accumulation",
-        "roofline": roof,
-        "roofline_prefill": roof_prefill,
-        "kernels": kernels,
-        "cpu_baseline": cpu,
-        "membench": mem,
     }
+    for k in ("decode_tok_s", "prefill_tok_s", "prefill_ms", "decode_ms_per_token", "decode_hbm_frac",
+              "decode_bytes_per_token", "prefill_mfma_frac", "prefill_flops", "roofline", "roofline_prefill",
+              "kernels"):
+        out[k] = head[k]
+    out["cpu_baseline"] = cpu
+    out["membench"] = mem
+    out["pages_context"] = PAGES_CONTEXT
     out.update(extra)
     print(json.dumps(out), flush=True)
 
