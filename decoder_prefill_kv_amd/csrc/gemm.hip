@@ -23,6 +23,15 @@
 //    are already in registers, so the first LDS reads of the next tile
 //    overlap its MFMAs.
 //
+// QKV epilogue: a wave's 128 columns are exactly one head (tiles start at
+// multiples of 256, heads at multiples of 128), and each of its rows is held
+// by 32 lanes of one half-wave, four columns per lane with column c and
+// c + 64 in the same lane.  So the per-head QK-norm ("LLMs on the ANE",
+// "Correctness": RMSNorm of q and k per head before RoPE) is a 32-lane sum of
+// squares and the RoPE rotation of the pair (c, c + 64) is lane-local; q goes
+// out as fp16 hi / lo, k and v straight into the fp16 KV cache, so the fp32
+// projection never reaches memory.
+//
 // Split-K: when the (M, N) tiles cannot fill the chip (N = 4096 at M = 2048
 // gives 128 tiles for 256 CUs), blockIdx.z takes a contiguous 1/S of the
 // k-tiles.  Each split writes its partial tile to a workspace with device-
@@ -47,7 +56,8 @@ constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100, SG_DS_W
 // tiles would leave CUs idle: each wave then holds 128 x 64 of C).
 template <int EPI, bool SPLIT, int BNT = BN>
 __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs a) {
-  static_assert(BNT == BN || (BNT == BN / 2 && EPI != GEMM_SWIGLU_F16 && !SPLIT), "narrow tiles: whole K, no SwiGLU");
+  static_assert(BNT == BN || (BNT == BN / 2 && EPI != GEMM_SWIGLU_F16 && EPI != GEMM_QKV_F16 && !SPLIT),
+                "narrow tiles: whole K, no SwiGLU, no QKV epilogue");
   constexpr int JB = BNT / 64;  // 32-column blocks per wave
   __shared__ __attribute__((aligned(16))) _Float16 As[2][BM][LDS_STRIDE];
   __shared__ __attribute__((aligned(16))) _Float16 Bs[2][BNT][LDS_STRIDE];
@@ -301,6 +311,123 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs a) {
   // epilogue: lane holds C[row][col], col = lane % 32,
   // row = 8 * (v / 4) + 4 * (lane / 32) + v % 4 inside each 32 x 32 block
   const int hi4 = (lane >> 5) * 4;
+  if constexpr (EPI == GEMM_QKV_F16) {
+    constexpr int D = 128, HD = 64, VT = 132;  // VT: halfs per transposed row in LDS (8-byte aligned rows)
+    const int hh = (n0 + wn * 128) / D;  // this wave's head
+    const bool is_q = hh < a.n_heads, is_v = hh >= a.n_heads + a.n_kv;
+    __syncthreads();  // every wave is done with the tiles in LDS
+    if (is_v) {
+      // V^T rows (a channel's positions are contiguous in the cache): the
+      // wave's 128 x 128 block goes through LDS transposed (waves 0, 1 in As,
+      // 2, 3 in Bs), then each store covers consecutive positions
+      _Float16* vt = (wave < 2 ? &As[0][0][0] : &Bs[0][0][0]) + (wave & 1) * (D * VT);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            vt[(j * 32 + r32) * VT + i * 32 + 8 * (v / 4) + hi4 + (v % 4)] = (_Float16)acc[i][j][v];
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done (lgkmcnt(0))
+      _Float16* const vb = (_Float16*)a.kv.base + kv_slab(a.kv, a.seq, a.layer, 1, hh - a.n_heads - a.n_kv);
+      if ((a.start & 3) == 0) {
+        // 4 positions per lane, two channels per store round (8-byte stores)
+        const int r = 4 * (lane & 31), mr = m0 + wm * 128 + r;
+        _Float16* const col = vb + (size_t)(lane >> 5) * a.kv.max_seq + a.start + mr;
+        for (int c = 0; c < D; c += 2) {
+          const u32x2 four = *(const u32x2*)&vt[(c + (lane >> 5)) * VT + r];
+          _Float16* dst = col + (size_t)c * a.kv.max_seq;
+          if (mr + 3 < a.M) {
+            *(u32x2*)dst = four;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (mr + e < a.M) dst[e] = __builtin_bit_cast(_Float16, (uint16_t)((e < 2 ? four.x : four.y) >> (16 * (e & 1))));
+          }
+        }
+      } else {
+        const int r = 2 * lane, mr = m0 + wm * 128 + r;  // rows r, r + 1 of the block
+        for (int c = 0; c < D; ++c) {
+          const uint32_t two = *(const uint32_t*)&vt[c * VT + r];
+          _Float16* dst = vb + (size_t)c * a.kv.max_seq + a.start + mr;
+          if (mr < a.M) dst[0] = __builtin_bit_cast(_Float16, (uint16_t)(two & 0xFFFFu));
+          if (mr + 1 < a.M) dst[1] = __builtin_bit_cast(_Float16, (uint16_t)(two >> 16));
+        }
+      }
+      return;
+    }
+    const uint16_t* g = is_q ? a.qn : a.kn;
+    float gj[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) gj[j] = (g && !is_v) ? bf16_to_f32(g[j * 32 + r32]) : 1.f;
+    _Float16* const qh = a.q16;
+    _Float16* const ql = a.q16 + (size_t)a.M * a.n_heads * D;
+    _Float16* const kb = is_q ? nullptr : (_Float16*)a.kv.base + kv_slab(a.kv, a.seq, a.layer, 0, hh - a.n_heads);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // the RoPE values of this block's 16 rows first, all loads in flight together
+      float c0[16], s0[16], c1[16], s1[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + wm * 128 + i * 32 + 8 * (v / 4) + hi4 + (v % 4);
+        const size_t t = (size_t)(a.start + (m < a.M ? m : a.M - 1)) * HD;
+        c0[v] = a.rope_cos[t + r32];
+        s0[v] = a.rope_sin[t + r32];
+        c1[v] = a.rope_cos[t + 32 + r32];
+        s1[v] = a.rope_sin[t + 32 + r32];
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + wm * 128 + i * 32 + 8 * (v / 4) + hi4 + (v % 4);
+        const bool ok = m < a.M;
+        float x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = acc[i][j][v];
+        // every lane of the half-wave holding this row takes part (rows past M included)
+        float ss = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+        const float r = g ? rsqrtf(ss / (float)D + a.eps) : 1.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] *= r * gj[j];
+        // rotate (c, c + 64) for c = r32 and c = 32 + r32 by pos * theta^(-2c/d)
+        float y[4];
+        y[0] = x[0] * c0[v] - x[2] * s0[v];
+        y[2] = x[2] * c0[v] + x[0] * s0[v];
+        y[1] = x[1] * c1[v] - x[3] * s1[v];
+        y[3] = x[3] * c1[v] + x[1] * s1[v];
+        // neighbour lanes swap so that each lane owns two adjacent columns:
+        // an even lane (columns 2k of each block j) takes blocks 0 and 2, an odd
+        // lane blocks 1 and 3; each lane then stores 4-byte pairs
+        const bool even = (r32 & 1) == 0;
+        const float t0 = __shfl_xor(even ? y[1] : y[0], 1, 64);
+        const float t1 = __shfl_xor(even ? y[3] : y[2], 1, 64);
+        float p[4];  // (first, second) of the two pairs
+        p[0] = even ? y[0] : t0;
+        p[1] = even ? t0 : y[1];
+        p[2] = even ? y[2] : t1;
+        p[3] = even ? t1 : y[3];
+        const int cb = (r32 & ~1) + (even ? 0 : 32);  // first column of this lane's first pair
+        if (!ok) continue;
+        if (is_q) {
+          const size_t o = ((size_t)m * a.n_heads + hh) * D + cb;
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const _Float16 h0 = (_Float16)p[2 * u], h1 = (_Float16)p[2 * u + 1];
+            const f16x2 hv = {h0, h1};
+            const f16x2 lv = {(_Float16)(p[2 * u] - (float)h0), (_Float16)(p[2 * u + 1] - (float)h1)};
+            *(f16x2*)(qh + o + 64 * u) = hv;
+            *(f16x2*)(ql + o + 64 * u) = lv;
+          }
+        } else {
+          _Float16* kr = kb + (size_t)(a.start + m) * D + cb;
+#pragma unroll
+          for (int u = 0; u < 2; ++u) *(f16x2*)(kr + 64 * u) = f16x2{(_Float16)p[2 * u], (_Float16)p[2 * u + 1]};
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -333,7 +460,7 @@ template <int EPI>
 void launch_epi(const GemmArgs& a, dim3 grid, bool narrow, hipStream_t stream) {
   if (a.splits > 1) {
     launch(gemm_kernel<EPI, true>, grid, dim3(THREADS), 0, stream, a);
-  } else if constexpr (EPI != GEMM_SWIGLU_F16) {
+  } else if constexpr (EPI != GEMM_SWIGLU_F16 && EPI != GEMM_QKV_F16) {
     if (narrow)
       launch(gemm_kernel<EPI, false, BN / 2>, grid, dim3(THREADS), 0, stream, a);
     else
@@ -347,7 +474,7 @@ void launch_epi(const GemmArgs& a, dim3 grid, bool narrow, hipStream_t stream) {
 // narrow ones still fit one round: the N = 4096 projections of a 2048-row
 // prefill get 256 tiles instead of 128 split in two along K.
 bool gemm_narrow(int M, int N, int epi, int n_cu) {
-  if (epi == GEMM_SWIGLU_F16 || N % (BN / 2)) return false;
+  if (epi == GEMM_SWIGLU_F16 || epi == GEMM_QKV_F16 || N % (BN / 2)) return false;
   const int mt = (M + BM - 1) / BM;
   return (N / BN) * mt < n_cu && (N / (BN / 2)) * mt <= n_cu;
 }
@@ -364,6 +491,8 @@ int device_cus() {  // compute units of the current device (cached per device)
 }
 
 }  // namespace
+
+bool gemm_prefers_narrow(int M, int N, int n_cu) { return gemm_narrow(M, N, GEMM_STORE_F32, n_cu); }
 
 int gemm_choose_splits(int M, int N, int K, int epi, int n_cu) {
   if (K % BK) return 1;
@@ -409,6 +538,10 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
     case GEMM_STORE_F32: launch_epi<GEMM_STORE_F32>(b, grid, narrow, stream); break;
     case GEMM_ADD_F32: launch_epi<GEMM_ADD_F32>(b, grid, narrow, stream); break;
     case GEMM_SWIGLU_F16: launch_epi<GEMM_SWIGLU_F16>(b, grid, false, stream); break;
+    case GEMM_QKV_F16:
+      if (a.kv.is_f32 || a.kv.d != 128 || !a.q16 || !a.rope_cos || !a.rope_sin) return hipErrorInvalidValue;
+      launch_epi<GEMM_QKV_F16>(b, grid, false, stream);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

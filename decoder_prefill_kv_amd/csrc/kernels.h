@@ -210,7 +210,10 @@ hipError_t launch_q4_to_f16(const uint32_t* codes, const uint16_t* sc, const uin
 hipError_t launch_f32_to_f16(const float* src, _Float16* dst, size_t n, hipStream_t stream);
 
 // ---- prefill GEMM (fp16 MFMA): C[m][n] = sum_k A[m][k] B[n][k]
-enum GemmEpi : int { GEMM_STORE_F32 = 0, GEMM_ADD_F32 = 1, GEMM_SWIGLU_F16 = 2 };
+// GEMM_QKV_F16: the QKV projection's epilogue (head_dim 128): per-head
+// QK-norm and RoPE of the q and k heads, q written as fp16 hi / lo planes for
+// the prefill attention, k and v written into the KV cache (v transposed).
+enum GemmEpi : int { GEMM_STORE_F32 = 0, GEMM_ADD_F32 = 1, GEMM_SWIGLU_F16 = 2, GEMM_QKV_F16 = 3 };
 struct GemmArgs {
   int M, N, K;
   int Kb;                         // K of B (0: = K); K = 2 Kb multiplies [A_hi | A_lo] by [B | B]
@@ -225,6 +228,16 @@ struct GemmArgs {
                                   //   (workgroup i runs on XCD i % 8) takes a 4 x 4 tile block
   float* ws;                      // split-K partial tiles [tiles][splits][256 * 256]
   unsigned* counters;             // split-K arrival counters [tiles], zero between launches
+  // QKV epilogue: rows are positions start.. of sequence seq; columns are the
+  // n_heads q heads, then the n_kv k heads, then the n_kv v heads (128 each)
+  int n_heads, n_kv, start, seq, layer;
+  const uint16_t* qn;             // q / k RMSNorm gains (bf16 [128]) or null
+  const uint16_t* kn;
+  float eps;
+  const float* rope_cos;          // [max_seq][64]
+  const float* rope_sin;
+  _Float16* q16;                  // hi plane [M][n_heads][128], then the lo plane
+  KVDesc kv;
 };
 constexpr int GEMM_MAX_SPLITS = 2;
 constexpr size_t GEMM_WS_TILES = 768;             // partial tiles the workspace holds
@@ -232,6 +245,8 @@ constexpr size_t GEMM_TILE_FLOATS = 256 * 256;
 // split-K factor that best fills n_cu CUs with (M, N) tiles
 int gemm_choose_splits(int M, int N, int K, int epi, int n_cu);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+// Whether a plain store GEMM of this shape runs on 256 x 128 tiles.
+bool gemm_prefers_narrow(int M, int N, int n_cu);
 
 // ---- prefill attention (fp16 MFMA, causal over the cache)
 struct AttnPrefillArgs {

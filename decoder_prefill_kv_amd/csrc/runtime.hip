@@ -882,6 +882,10 @@ dpk_status forward_gemm(dpk_model* md, int M, int start, int seq, bool want_head
                          md->rows_dev, nullptr, c.vocab, md->h, nullptr, c.rms_eps, md->err_flag, st));
   }
   const double norm_bytes = (double)M * H * 6;
+  // the QKV epilogue takes QK-norm / RoPE / the cache write when the
+  // projection runs on full 256 x 256 tiles (a narrow-tile grid splits a head
+  // over two waves)
+  const bool qkv_fused = d == 128 && !gemm_prefers_narrow(M, md->Nqkv, md->n_cu);
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& L = md->layers[l];
     {
@@ -892,9 +896,18 @@ dpk_status forward_gemm(dpk_model* md, int M, int start, int seq, bool want_head
     GemmArgs g{};
     g.M = M; g.N = md->Nqkv; g.K = 2 * H; g.Kb = H;
     g.A = md->y16; g.lda = 2 * H; g.B = L.qkv16; g.ldb = H;
-    g.epi = GEMM_STORE_F32; g.C = md->qkv; g.ldc = md->Nqkv;
-    if ((s2 = gemm_prof(K_GEMM_QKV, g))) return s2;
-    {
+    if (qkv_fused) {
+      // QK-norm, RoPE, the q hi / lo split and the KV-cache write in the epilogue
+      g.epi = GEMM_QKV_F16;
+      g.n_heads = c.n_heads; g.n_kv = c.n_kv_heads; g.start = start; g.seq = seq; g.layer = l;
+      g.qn = c.qk_norm ? (const uint16_t*)L.q_norm : nullptr;
+      g.kn = c.qk_norm ? (const uint16_t*)L.k_norm : nullptr;
+      g.eps = c.rms_eps; g.rope_cos = md->rope_cos; g.rope_sin = md->rope_sin;
+      g.q16 = md->q16; g.kv = md->kvd;
+      if ((s2 = gemm_prof(K_GEMM_QKV, g))) return s2;
+    } else {
+      g.epi = GEMM_STORE_F32; g.C = md->qkv; g.ldc = md->Nqkv;
+      if ((s2 = gemm_prof(K_GEMM_QKV, g))) return s2;
       ProfScope ps(md, st, K_QK_ROPE_KV, (double)M * md->Nqkv * 6, 0);
       HIP_TRY(launch_qk_rope_kv(M, md->qkv, c.n_heads, c.n_kv_heads, d, c.qk_norm, L.q_norm, L.k_norm, 0, c.rms_eps,
                                 md->rope_cos, md->rope_sin, md->rows_dev, md->q16, 2, md->kvd, l, st));

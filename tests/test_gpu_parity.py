@@ -44,6 +44,11 @@ CASES = [
     ("q8b-L2-v4096-chunked", synth.Q8B.with_(n_layers=2, vocab=4096), 600, 4, dict(max_rows=256)),
     ("q8b-L2-v4096-multi", synth.Q8B.with_(n_layers=2, vocab=4096), 250, 12, dict(flags=MULTI, max_rows=256)),
     ("q8b-L2-v4096-persistent", synth.Q8B.with_(n_layers=2, vocab=4096), 250, 12, dict(max_rows=256)),
+    # prompts long enough for the QKV projection to run on 256 x 256 tiles, whose
+    # epilogue applies QK-norm / RoPE and writes the cache (one chunk; chunks
+    # at offsets 0 and 1400 plus a short tail)
+    ("q8b-L1-v4096-qkv-epilogue", synth.Q8B.with_(n_layers=1, vocab=4096), 1400, 3, dict(max_rows=1400)),
+    ("q8b-L1-v4096-qkv-epilogue-chunked", synth.Q8B.with_(n_layers=1, vocab=4096), 2900, 3, dict(max_rows=1400)),
     # int8 per-channel weights: GEMM prefill from the fp16 copy, weight-streaming decode
     ("q06b_i8-L2-gemm", synth.Q06B_I8.with_(n_layers=2), 40, 8, {}),
     ("q06b_i8-L2-stream", synth.Q06B_I8.with_(n_layers=2), 37, 6, dict(flags=STREAM)),

@@ -36,6 +36,9 @@ CASES = [
     ("q8b-L2-v4096", synth.Q8B.with_(n_layers=2, vocab=4096), [(0, 300), (300, 257), (557, 16)], 4,
      dict(max_rows=256)),
     ("tiny", synth.TINY, [(0, 7), (7, 12), (19, 1), (20, 9)], 4, {}),
+    # a piece long enough for the QKV epilogue path, at an odd offset
+    ("q8b-L1-v4096-qkv-epilogue", synth.Q8B.with_(n_layers=1, vocab=4096), [(0, 37), (37, 1400), (1437, 3)], 2,
+     dict(max_rows=1400)),
 ]
 
 
