@@ -98,16 +98,18 @@ __global__ __launch_bounds__(THREADS, 2) void attn_prefill_kernel(AttnPrefillArg
   u32x4 kreg[4];
   f16x8 vreg[4];
   auto gload = [&](int k0) {
+    const bool tail = k0 + BKV > kend;  // uniform: only the last tile has keys past kend
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int idx = tid + THREADS * i;  // 0..1023
       const int kr = idx >> 4, kc = (idx & 15) * 8;
-      kreg[i] = *(const u32x4*)(Kg + (size_t)min(k0 + kr, kend - 1) * D + kc);
+      kreg[i] = *(const u32x4*)(Kg + (size_t)(tail ? min(k0 + kr, kend - 1) : k0 + kr) * D + kc);
       const int vr = idx >> 3, vc = (idx & 7) * 8;
       vreg[i] = *(const f16x8*)(Vg + (size_t)vr * a.kv.max_seq + k0 + vc);
     }
   };
   auto lstore = [&](int k0) {
+    const bool tail = k0 + BKV > kend;  // uniform over the workgroup
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int idx = tid + THREADS * i;
@@ -115,11 +117,13 @@ __global__ __launch_bounds__(THREADS, 2) void attn_prefill_kernel(AttnPrefillArg
       *(u32x4*)&Ks[kr][kc] = kreg[i];
       const int vr = idx >> 3, vc = (idx & 7) * 8;
       // keys at or past kend are zeroed (the cache there may hold any bit
-      // pattern, and 0 * NaN would poison O)
+      // pattern, and 0 * NaN would poison O); only the last tile has any
       f16x8 vv = vreg[i];
+      if (tail) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (k0 + vc + e >= kend) vv[e] = (_Float16)0.f;
+        for (int e = 0; e < 8; ++e)
+          if (k0 + vc + e >= kend) vv[e] = (_Float16)0.f;
+      }
       *(f16x8*)&Vs[vr][vc] = vv;
     }
   };
@@ -187,11 +191,16 @@ __global__ __launch_bounds__(THREADS, 2) void attn_prefill_kernel(AttnPrefillArg
       }
     psum += __shfl_xor(psum, 32, 64);
     lrun = lrun * alpha + psum;
+    // O only needs rescaling when some query's running maximum moved (alpha
+    // is exactly 1 otherwise); past the first tiles that is rare
+    const bool moved = __builtin_amdgcn_ballot_w64(mnew != mrun) != 0;
     mrun = mnew;
+    if (moved) {
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i)
+      for (int i = 0; i < D / 32; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
+        for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
+    }
     // O^T += V^T P^T; key slots of k-group hh in step (b, t):
     //   b*32 + 16t + {4hh..4hh+3, 8+4hh..8+4hh+3}
 #pragma unroll
