@@ -96,8 +96,10 @@ DPK_DEV void wave_argmax(float& v, int& i) {
 // would also drain every load in flight, e.g. a weight prefetch).  Global
 // data written before it is not made visible to the other waves.
 DPK_DEV void lds_barrier() {
+  asm volatile("" ::: "memory");       // no memory access moves across it in the compiler
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt unconstrained
   __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // block_sum with lds_barrier(): the sum of v over the workgroup
@@ -120,6 +122,16 @@ DPK_DEV float block_sum(float v, float* red) {
   __syncthreads();
   float t = 0.f;
   for (int i = 0; i < nw; ++i) t += red[i];
+  return t;
+}
+
+// threadIdx.x as a value the compiler cannot see through.  In a long
+// persistent kernel, per-lane address terms derived from the thread index
+// would otherwise be computed once, kept live across every phase and spilled
+// to scratch; a phase that takes its index from here computes them itself.
+DPK_DEV int opaque_tid() {
+  int t = (int)threadIdx.x;
+  asm volatile("" : "+v"(t));
   return t;
 }
 
@@ -175,6 +187,32 @@ DPK_DEV void cstore2(coh_buf r, uint32_t i, float x, float y) {  // floats i, i+
 DPK_DEV void cstore(coh_buf r, uint32_t i, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, i * 4u, 0, CPOL_SC1);
 }
+
+// 16 bytes at byte offset 16 i (i.e. two 64-bit words 2 i, 2 i + 1), device-coherent
+DPK_DEV u32x4 cload16(coh_buf r, uint32_t i) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, i * 16u, 0, CPOL_SC1));
+}
+DPK_DEV void cstore8z(coh_buf r, uint32_t i) {  // zero the 64-bit word i
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, r, i * 8u, 0, CPOL_SC1);
+}
+
+// Partial sums added by several workgroups with 64-bit integer atomics, in
+// fixed point (value * 2^FX_BITS): integer adds are exact, so the sum does not
+// depend on the order the workgroups arrive in.  A value that is not finite
+// or not below 2^26 in magnitude is entered as FX_BAD; with at most 16 terms a
+// total at or beyond FX_NAN in magnitude can only come from such a term and
+// reads back as NaN.
+constexpr int FX_BITS = 28;
+constexpr long long FX_BAD = 1ll << 59, FX_NAN = 1ll << 58;
+DPK_DEV long long to_fixed(float v) {
+  if (!(fabsf(v) < 67108864.0f)) return FX_BAD;  // NaN included
+  return __float2ll_rn(v * (float)(1 << FX_BITS));
+}
+DPK_DEV float from_fixed(long long x) {
+  if (x >= FX_NAN || x <= -FX_NAN) return __builtin_nanf("");
+  return __ll2float_rn(x) * (1.0f / (float)(1 << FX_BITS));
+}
+DPK_DEV long long fixed_word(uint32_t lo, uint32_t hi) { return (long long)(((uint64_t)hi << 32) | lo); }
 
 // Last-arriving-workgroup election.  Every workgroup calls this once after
 // writing the data it hands over with coh_store; exactly one (the last) gets

@@ -64,7 +64,8 @@ struct Barrier {
 // (loads of the next phase that do not depend on other workgroups) is issued
 // after counting in and before the wait, so those loads fly while the barrier
 // completes.  Only wave 0 waits on memory for the barrier itself, and its
-// waits also cover its own prefetch loads (vector memory returns in order).
+// waits also cover its own prefetch loads (vector memory returns in order);
+// the other waves leave theirs in flight.
 template <typename F>
 DPK_DEV void grid_sync(Barrier& b, F&& prefetch) {
   ++b.phase;
@@ -91,13 +92,18 @@ DPK_DEV void grid_sync(Barrier& b, F&& prefetch) {
       __builtin_amdgcn_s_sleep(1);
     }
   }
-  __syncthreads();
+  // execution order only: what other workgroups handed over is read with
+  // device-coherent loads issued after this, and a __syncthreads here would
+  // make every wave wait for its whole prefetch before it could even issue
+  // the loads of its input
+  lds_barrier();
 }
 
-// After the last barrier: the last workgroup out resets the arrival counter
-// for the next launch (no workgroup waits on it any more) and turns an abort
-// into bit 1 of the error word the host reads.
-DPK_DEV void grid_exit(Barrier& b, unsigned* exit_ctr, int* err) {
+// After the last barrier: the last workgroup out resets the arrival counters
+// (and the attention chunk counters) for the next launch (no workgroup waits
+// on them any more) and turns an abort into bit 1 of the error word the host
+// reads.
+DPK_DEV void grid_exit(Barrier& b, unsigned* exit_ctr, int* err, unsigned* attn_ctr, int n_attn_ctr) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -108,6 +114,9 @@ DPK_DEV void grid_exit(Barrier& b, unsigned* exit_ctr, int* err) {
         __hip_atomic_store(b.abort_flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       for (int g = 0; g <= 8; ++g) __hip_atomic_store(b.ctr + 64 * g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // (the fused attention's chunk counters grow over the step)
+      for (int i = 0; i < n_attn_ctr; ++i)
+        __hip_atomic_store(attn_ctr + i * MEGA_CTR_STRIDE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(exit_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -162,9 +171,259 @@ DPK_DEV void split_f16(float x, _Float16& hi, _Float16& lo) {
 // each chunk writes a record (max, sum, O) and the last chunk of (m, g) to
 // finish merges them (log-sum-exp weights).  QK-norm, RoPE and the new
 // position's K/V come from the raw QKV projection of the previous phase.
+//
+// FO (bf16, a.oacc set): the O projection runs in the same phase, split by
+// KV head, on the workgroups attention does not use (o_phase).  Every chunk
+// writes its record and counts in on the (m, g) counter: there is no merge
+// step and no grid barrier after attention.
+// The O projection of the fused phase.  Item j = (block j / n_kv of 16 * o_rt
+// output rows, KV head g = j % n_kv) multiplies those rows of W_o,
+// restricted to g's G * d columns, by g's attention outputs and adds the
+// product to a.oacc in fixed point (the n_kv items of a row block are summed
+// there, exactly and in any order).  Wave w takes 16-row tile w / WPT of the
+// block over k-steps (32 columns) (w % WPT) * KW .. + KW, its weight blocks
+// in registers.
+//
+// The items run on the workgroups that attention does not use: workgroup ow
+// of n_ow (a multiple of n_kv) takes items ow, ow + n_ow, ... -- all of KV
+// head g = ow % n_kv, so one wait on g's chunk counters and one merge of g's
+// records (running maximum, log-sum-exp weights) serve them.  The weights
+// of its first two items load when the QKV barrier is passed, while
+// attention runs; a further item (a grid of fewer than half as many
+// workgroups as items) loads after the two.
+struct OItem {
+  int RT, WPT, KW, n_o;
+};
+template <int G>
+DPK_DEV OItem o_shape(const MegaArgs& a) {
+  OItem o;
+  o.RT = a.o_rt;
+  o.WPT = 8 / o.RT;
+  o.KW = (G * D / 32) / o.WPT;
+  o.n_o = (a.H / (16 * o.RT)) * a.n_kv;
+  return o;
+}
+constexpr int O_KWMAX = 16;  // k-steps per wave: G * D / 32 with G <= 4
+template <int G>
+DPK_DEV void o_load(const MegaArgs& a, const GemvArgs* Lo, const OItem& o, int j, u32x4 (&wr)[O_KWMAX]) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int g = j % a.n_kv;
+  const size_t rt = (size_t)(j / a.n_kv) * o.RT + wave / o.WPT;
+  const unsigned char* src = (const unsigned char*)Lo->w[0] +
+                             (rt * (Lo->K / 32) + g * (G * D / 32) + (wave % o.WPT) * o.KW) * 1024 + lane * 16;
+#pragma unroll
+  for (int k = 0; k < O_KWMAX; ++k)
+    if (k < o.KW) wr[k] = __builtin_nontemporal_load(gemv_detail::gmem((const u32x4*)(src + (size_t)k * 1024)));
+}
+
+// This wave's products of up to two items over KW k-steps, x' from LDS (row
+// stride xst bf16): with PACK (at most 8 rows) one MFMA takes hi and lo
+// together -- B column m is row m's hi part, column m + 8 its lo part, added
+// with a lane shuffle; otherwise hi and lo are two MFMAs.  Columns past the
+// rows read row M - 1: they are never used (an MFMA column depends on its
+// own B column only).
+template <int KW, bool PACK, bool TWO>
+DPK_DEV void o_products(const u32x4 (&w0)[O_KWMAX], const u32x4 (&w1)[O_KWMAX], const uint16_t* xs_hi,
+                        const uint16_t* xs_lo, int xst, int M, int ksw, f32x4& y0, f32x4& y1) {
+  const int lane = threadIdx.x & 63, r16 = lane & 15, j4 = lane >> 4;
+  const int mrow = min(PACK ? (r16 & 7) : r16, M - 1);
+  const uint16_t* xa = ((PACK && r16 >= 8) ? xs_lo : xs_hi) + mrow * xst + ksw * 32 + 8 * j4;
+  const uint16_t* xb = xs_lo + mrow * xst + ksw * 32 + 8 * j4;
+  f32x4 a0[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}}, a1[2] = {a0[0], a0[0]};
+  constexpr int KB = KW < 4 ? KW : 4;  // x fragments read in batches of KB k-steps
+#pragma unroll
+  for (int k0 = 0; k0 < KW; k0 += KB) {
+    u32x4 xh[KB], xl[KB];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      xh[u] = *(const u32x4*)(xa + 32 * (k0 + u));
+      if (!PACK) xl[u] = *(const u32x4*)(xb + 32 * (k0 + u));
+    }
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int k = k0 + u;
+      const bf16x8 H = __builtin_bit_cast(bf16x8, xh[u]);
+      a0[k & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w0[k]), H, a0[k & 1], 0, 0, 0);
+      if (TWO)
+        a1[k & 1] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w1[k]), H, a1[k & 1], 0, 0, 0);
+      if (!PACK) {
+        const bf16x8 L = __builtin_bit_cast(bf16x8, xl[u]);
+        a0[k & 1] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w0[k]), L, a0[k & 1], 0, 0, 0);
+        if (TWO)
+          a1[k & 1] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w1[k]), L, a1[k & 1], 0, 0, 0);
+      }
+    }
+  }
+  y0 = a0[0] + a0[1];
+  y1 = a1[0] + a1[1];
+  if (PACK) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      y0[v] += __shfl_down(y0[v], 8, 16);
+      if (TWO) y1[v] += __shfl_down(y1[v], 8, 16);
+    }
+  }
+}
+template <int KW>
+DPK_DEV void o_products_kw(bool pack, bool two, const u32x4 (&w0)[O_KWMAX], const u32x4 (&w1)[O_KWMAX],
+                           const uint16_t* xs_hi, const uint16_t* xs_lo, int xst, int M, int ksw, f32x4& y0,
+                           f32x4& y1) {
+  if (pack) {
+    if (two) o_products<KW, true, true>(w0, w1, xs_hi, xs_lo, xst, M, ksw, y0, y1);
+    else o_products<KW, true, false>(w0, w1, xs_hi, xs_lo, xst, M, ksw, y0, y1);
+  } else {
+    if (two) o_products<KW, false, true>(w0, w1, xs_hi, xs_lo, xst, M, ksw, y0, y1);
+    else o_products<KW, false, false>(w0, w1, xs_hi, xs_lo, xst, M, ksw, y0, y1);
+  }
+}
+
 template <int G, typename Sync>
+DPK_DEV void o_phase(const MegaArgs& a, const RowParam* rows, int layer, const GemvArgs* Lo, unsigned char* lds,
+                     const Barrier& bar, int ow, int n_ow, Sync&& sync) {
+  const int tid = opaque_tid(), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, j4 = lane >> 4;
+  const OItem o = o_shape<G>(a);
+  const int g = ow % a.n_kv, rtw = wave / o.WPT, ksw = (wave % o.WPT) * o.KW;
+  const int rec = D + 2;
+  constexpr int GD = G * D, XST = GD + 8;  // x' row stride (bf16)
+  uint16_t* xs_hi = (uint16_t*)lds;        // [M][XST] attention outputs of g, bf16 hi
+  uint16_t* xs_lo = xs_hi + a.M * XST;     //   and lo
+  float* red = (float*)(lds + ((4 * a.M * XST + 15) & ~15));  // [8 waves][64 lanes][4]
+
+  u32x4 w0[O_KWMAX], w1[O_KWMAX];  // this wave's blocks of items ow and ow + n_ow
+  const int j0 = ow, j1 = ow + n_ow;
+  sync([&] {  // the QKV projection of every row is complete after this
+    if (j0 < o.n_o) o_load<G>(a, Lo, o, j0, w0);
+    if (j1 < o.n_o) o_load<G>(a, Lo, o, j1, w1);
+  });
+  if (j0 >= o.n_o) return;  // uniform over the workgroup
+
+  // every row's chunks of g have stored their records
+  if (tid == 0) {
+    for (int m = 0; m < a.M; ++m) {
+      const unsigned target = (unsigned)(layer + 1) * (unsigned)((rows[m].pos + ACH) / ACH);
+      for (unsigned spin = 0;; ++spin) {
+        if (__hip_atomic_load(a.attn_counters + (m * a.n_kv + g) * MEGA_CTR_STRIDE, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT) >= target)
+          break;
+        if (__hip_atomic_load(bar.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) break;
+        if (spin >= SPIN_LIMIT) {
+          __hip_atomic_store(bar.abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+  }
+  lds_barrier();
+  // x'[m][c * D + e] = query head g * G + c of row m, as bf16 hi + lo.  Waves
+  // 0 .. 3 take blocks of 64 outputs (one (m, c), half of e) two at a time;
+  // lane u loads chunk u's (max, sum), broadcast with readlane, and every
+  // load of both blocks is issued before the first is used.
+  const coh_buf pb = coh_buffer(a.part);
+  if (wave < 4) {
+    const int nblk = a.M * G * 2;
+    for (int b0 = wave; b0 < nblk; b0 += 8) {
+      float mvl[2], lvl[2], ov[2][16];
+      int nchb[2];
+      uint32_t bse[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int b = min(b0 + 4 * h, nblk - 1);
+        const int m = b / (2 * G), c = (b / 2) % G, e = (b % 2) * 64 + lane;
+        nchb[h] = (rows[m].pos + ACH) / ACH;
+        bse[h] = (uint32_t)(((m * a.n_heads + g * G + c) * a.max_chunks) * rec);
+        const uint32_t rl = bse[h] + (uint32_t)min(lane, nchb[h] - 1) * rec;
+        mvl[h] = cload(pb, rl);
+        lvl[h] = cload(pb, rl + 1);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) ov[h][u] = cload(pb, bse[h] + (uint32_t)min(u, nchb[h] - 1) * rec + 2 + e);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int b = b0 + 4 * h;
+        if (b >= nblk) break;
+        const int m = b / (2 * G), c = (b / 2) % G, e = (b % 2) * 64 + lane;
+        float Mx = -INFINITY, den = 0.f, O = 0.f;
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          if (u < nchb[h]) {
+            const float mu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mvl[h]), u));
+            const float lu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lvl[h]), u));
+            const float mn = fmaxf(Mx, mu);
+            const float fa = __builtin_amdgcn_exp2f(Mx - mn), fb = __builtin_amdgcn_exp2f(mu - mn);
+            den = den * fa + lu * fb;
+            O = O * fa + ov[h][u] * fb;
+            Mx = mn;
+          }
+        // chunks past 16 (contexts beyond 16 * 256 positions), one at a time
+        for (int u = 16; u < nchb[h]; ++u) {
+          const uint32_t r = bse[h] + (uint32_t)u * rec;
+          const float mu = cload(pb, r), lu = cload(pb, r + 1), ou = cload(pb, r + 2 + e);
+          const float mn = fmaxf(Mx, mu);
+          const float fa = __builtin_amdgcn_exp2f(Mx - mn), fb = __builtin_amdgcn_exp2f(mu - mn);
+          den = den * fa + lu * fb;
+          O = O * fa + ou * fb;
+          Mx = mn;
+        }
+        uint32_t h16, l16;
+        split_bf16(O / den, h16, l16);
+        xs_hi[m * XST + c * D + e] = (uint16_t)h16;
+        xs_lo[m * XST + c * D + e] = (uint16_t)l16;
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's weight blocks are in registers
+  __syncthreads();
+
+  // the WPT waves of a row tile are summed in wave order, then the first adds
+  // rows 4 j4 .. + 3 of column r16 (= row m) to oacc
+  const bool pack = a.M <= 8;
+  auto finish = [&](int j, f32x4 acc) {
+    if (o.WPT > 1) {
+      *(f32x4*)(red + (wave * 64 + lane) * 4) = acc;
+      lds_barrier();
+      if (wave % o.WPT == 0)
+        for (int q = 1; q < o.WPT; ++q) acc += *(const f32x4*)(red + ((wave + q) * 64 + lane) * 4);
+      lds_barrier();  // red is rewritten next
+    }
+    if (wave % o.WPT == 0 && r16 < a.M && (!pack || r16 < 8)) {
+      const size_t n0 = (size_t)r16 * a.H + (size_t)((j / a.n_kv) * o.RT + rtw) * 16 + 4 * j4;
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        __hip_atomic_fetch_add(a.oacc + n0 + v, to_fixed(acc[v]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+  for (int j = j0; j < o.n_o; j += 2 * n_ow) {
+    const int jb = j + n_ow;
+    const bool two = jb < o.n_o;
+    if (j != j0) {  // items past the first two, loaded now
+      o_load<G>(a, Lo, o, j, w0);
+      if (two) o_load<G>(a, Lo, o, jb, w1);
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+    f32x4 y0, y1;
+    switch (o.KW) {
+      case 1: o_products_kw<1>(pack, two, w0, w1, xs_hi, xs_lo, XST, a.M, ksw, y0, y1); break;
+      case 2: o_products_kw<2>(pack, two, w0, w1, xs_hi, xs_lo, XST, a.M, ksw, y0, y1); break;
+      case 4: o_products_kw<4>(pack, two, w0, w1, xs_hi, xs_lo, XST, a.M, ksw, y0, y1); break;
+      case 8: o_products_kw<8>(pack, two, w0, w1, xs_hi, xs_lo, XST, a.M, ksw, y0, y1); break;
+      default: o_products_kw<16>(pack, two, w0, w1, xs_hi, xs_lo, XST, a.M, ksw, y0, y1); break;
+    }
+    finish(j, y0);
+    if (two) finish(jb, y1);
+  }
+  lds_barrier();  // x' and red are rewritten by the next phase
+}
+
+template <int G, bool FO, typename Sync>
 DPK_DEV void attn_phase(const MegaArgs& a, const RowParam* rows, int layer, const uint16_t* qn, const uint16_t* kn,
-                        unsigned char* lds, int wg, int nwg, Sync&& sync) {
+                        const GemvArgs* Lo, unsigned char* lds, const Barrier& bar, int wg,
+                        int nwg, Sync&& sync) {
   // q (log2 domain) as fp16 hi + lo and the new position's K / V in cache
   // precision, all in MFMA fragment order (8 consecutive d per 16 bytes)
   _Float16* qh16 = (_Float16*)lds;      // [G][D]
@@ -175,7 +434,7 @@ DPK_DEV void attn_phase(const MegaArgs& a, const RowParam* rows, int layer, cons
   float* ow = wst + AW * 2 * G;         // [AW][D][G]
   int* flag = (int*)(ow + AW * D * G);
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = opaque_tid(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform over the wave
   const int r16 = lane & 15, j4 = lane >> 4;
   const int n_items = a.M * a.n_kv * a.max_chunks;
@@ -224,11 +483,22 @@ DPK_DEV void attn_phase(const MegaArgs& a, const RowParam* rows, int layer, cons
     gr1 = gemv_detail::gmem(gp)[lane + 64];
   };
 
+  // FO: workgroups [0, n_aw) run the attention items and the other n_ow (a
+  // multiple of n_kv, at least half the grid) the O projection (o_phase)
+  int n_aw = nwg;
+  if constexpr (FO) {
+    const int n_ow = ((nwg - min(n_items, nwg / 2)) / a.n_kv) * a.n_kv;
+    n_aw = nwg - n_ow;
+    if (wg >= n_aw) {
+      o_phase<G>(a, rows, layer, Lo, lds, bar, wg - n_aw, n_ow, sync);
+      return;
+    }
+  }
   int it = wg;
   sync([&] {  // the QKV projection of every row is complete after this
     if (it < n_items) prefetch(it);
   });
-  for (; it < n_items; it += nwg) {
+  for (; it < n_items; it += n_aw) {
     if (it != wg) prefetch(it);
     const int chunk = it % a.max_chunks, g = (it / a.max_chunks) % a.n_kv, m = it / (a.max_chunks * a.n_kv);
     const RowParam rp = rp_it;
@@ -384,6 +654,7 @@ DPK_DEV void attn_phase(const MegaArgs& a, const RowParam* rows, int layer, cons
       }
     }
 
+
     // ---- combine the waves (per column = query head)
     if (r16 < G) {
       if (j4 == 0) {
@@ -413,7 +684,7 @@ DPK_DEV void attn_phase(const MegaArgs& a, const RowParam* rows, int layer, cons
         L += f * wst[(w * 2 + 1) * G + c];
         O += f * ow[(w * D + e) * G + c];
       }
-      if (nch == 1) {
+      if (nch == 1 && !FO) {
         cstore(ob, outp + c * D + e, O / L);
       } else {
         const uint32_t r = (uint32_t)(((m * a.n_heads + g * G + c) * a.max_chunks + chunk) * rec);
@@ -424,7 +695,15 @@ DPK_DEV void attn_phase(const MegaArgs& a, const RowParam* rows, int layer, cons
         }
       }
     }
-    if (nch > 1 && last_block_arrive(a.attn_counters + m * a.n_kv + g, nch, flag)) {
+    if (FO) {
+      // count in once the records are stored; the counter grows over the
+      // step's layers
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0)
+        __hip_atomic_fetch_add(a.attn_counters + (m * a.n_kv + g) * MEGA_CTR_STRIDE, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    } else if (nch > 1 && last_block_arrive(a.attn_counters + m * a.n_kv + g, nch, flag)) {
       // output (c, e) of every query head of g: the (max, sum, O[e]) records
       // of up to 16 chunks are loaded at once and folded in with a running
       // maximum (log-sum-exp weights)
@@ -462,7 +741,10 @@ DPK_DEV void attn_phase(const MegaArgs& a, const RowParam* rows, int layer, cons
 // iteration (so rows of 1024, 2048, 3072 ... columns split over eight waves)
 // and the QKV projection goes in 16-row tiles, which gives a narrow model's
 // QKV about one tile per workgroup.
-template <int G, int FMT, bool SMALL>
+//
+// FO (bf16, a.oacc set): attention and the O projection are one phase (see
+// attn_phase), and gate/up and down fold the fixed-point O sums into h.
+template <int G, int FMT, bool SMALL, bool FO>
 __global__ __launch_bounds__(MT, 1) void decode_step_kernel(MegaArgs a) {
   // (the lm_head of a narrow model goes in 32-row tiles: one 128-column
   // iteration per 16 rows would leave a wave a single 4 KB load in flight)
@@ -520,18 +802,20 @@ __global__ __launch_bounds__(MT, 1) void decode_step_kernel(MegaArgs a) {
     const MegaLayer& L = *Ls;
     gemv_body<FMT, TQ, 8, true, false, KI, PF>(L.qkv, a.M, lds, wg, nwg, sync, pf);
     closing = MP_QKV;
-    attn_phase<G>(a, Rs, l, L.qn, L.kn, lds, wg, nwg, sync);
+    attn_phase<G, FO>(a, Rs, l, L.qn, L.kn, &L.o, lds, bar, wg, nwg, sync);
     closing = MP_ATTN;
-    gemv_body<FMT, 1, 8, true, false, KI, PF>(L.o, a.M, lds, wg, nwg, sync, pf);
-    closing = MP_O;
-    gemv_body<FMT, 2, 8, true, false, KI, PF>(L.gu, a.M, lds, wg, nwg, sync, pf);
+    if constexpr (!FO) {
+      gemv_body<FMT, 1, 8, true, false, KI, PF>(L.o, a.M, lds, wg, nwg, sync, pf);
+      closing = MP_O;
+    }
+    gemv_body<FMT, 2, 8, true, false, KI, PF, FO>(L.gu, a.M, lds, wg, nwg, sync, pf);
     closing = MP_GATEUP;
-    gemv_body<FMT, 1, 8, true, false, KI, PF>(L.down, a.M, lds, wg, nwg, sync, pf);
+    gemv_body<FMT, 1, 8, true, false, KI, PF, FO>(L.down, a.M, lds, wg, nwg, sync, pf);
     closing = MP_DOWN;
   }
   stage(Hs, &a.head, (int)sizeof(GemvArgs));
   gemv_body<FMT, TH, 8, true, false, KI>(*Hs, a.M, lds, wg, nwg, sync);
-  grid_exit(bar, a.bar + MEGA_BAR_EXIT, a.err);
+  grid_exit(bar, a.bar + MEGA_BAR_EXIT, a.err, a.attn_counters, FO ? a.M * a.n_kv : 0);
   if (tr) {
     mark(MP_HEAD);
     a.trace[MP_STEPS] += 1;
@@ -539,28 +823,40 @@ __global__ __launch_bounds__(MT, 1) void decode_step_kernel(MegaArgs a) {
 }
 
 // Built variants: bf16 at 256 columns per iteration for G = 1, 2, 4; bf16
-// and 4-bit at 128 columns for G = 2, 4.
-const void* mega_kernel_for(int G, int fmt, bool small) {
+// and 4-bit at 128 columns for G = 2, 4; bf16 with and without the fused O
+// projection.
+template <bool FO>
+const void* mega_kernel_fo(int G, int fmt, bool small) {
   if (fmt == W_BF16 && !small) {
     switch (G) {
-      case 1: return (const void*)decode_step_kernel<1, W_BF16, false>;
-      case 2: return (const void*)decode_step_kernel<2, W_BF16, false>;
-      case 4: return (const void*)decode_step_kernel<4, W_BF16, false>;
+      case 1: return (const void*)decode_step_kernel<1, W_BF16, false, FO>;
+      case 2: return (const void*)decode_step_kernel<2, W_BF16, false, FO>;
+      case 4: return (const void*)decode_step_kernel<4, W_BF16, false, FO>;
       default: return nullptr;
     }
   }
   if (!small) return nullptr;
   if (fmt == W_BF16) {
-    if (G == 2) return (const void*)decode_step_kernel<2, W_BF16, true>;
-    if (G == 4) return (const void*)decode_step_kernel<4, W_BF16, true>;
-  } else if (fmt == W_Q4) {
-    if (G == 2) return (const void*)decode_step_kernel<2, W_Q4, true>;
-    if (G == 4) return (const void*)decode_step_kernel<4, W_Q4, true>;
+    if (G == 2) return (const void*)decode_step_kernel<2, W_BF16, true, FO>;
+    if (G == 4) return (const void*)decode_step_kernel<4, W_BF16, true, FO>;
+  } else if (fmt == W_Q4 && !FO) {
+    if (G == 2) return (const void*)decode_step_kernel<2, W_Q4, true, false>;
+    if (G == 4) return (const void*)decode_step_kernel<4, W_Q4, true, false>;
   }
   return nullptr;
 }
+const void* mega_kernel_for(int G, int fmt, bool small, bool fo) {
+  return fo ? mega_kernel_fo<true>(G, fmt, small) : mega_kernel_fo<false>(G, fmt, small);
+}
 
 }  // namespace
+
+size_t mega_o_lds_bytes(int M, int G, int rt) {
+  if (rt != 1 && rt != 2 && rt != 4 && rt != 8) return 0;
+  const int KS = G * D / 32, WPT = 8 / rt;
+  if (KS % WPT || KS / WPT > O_KWMAX) return 0;
+  return ((4 * (size_t)M * (G * D + 8) + 15) & ~(size_t)15) + 8 * 64 * 4 * 4;
+}
 
 size_t mega_attn_lds_bytes(int G) {
   return ((size_t)G * D + 2 * D + AW * 2 * G + AW * D * G + 4) * 4;
@@ -571,8 +867,8 @@ int mega_attn_chunk() { return ACH; }
 
 // Workgroups per CU the kernel can keep resident with lds bytes of LDS (0 if
 // the kernel does not exist for G, fmt, small).
-int mega_occupancy(int G, int fmt, bool small, size_t lds) {
-  const void* k = mega_kernel_for(G, fmt, small);
+int mega_occupancy(int G, int fmt, bool small, bool fo, size_t lds) {
+  const void* k = mega_kernel_for(G, fmt, small, fo);
   if (!k) return 0;
   int nb = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k, MT, lds) != hipSuccess) return 0;
@@ -580,7 +876,7 @@ int mega_occupancy(int G, int fmt, bool small, size_t lds) {
 }
 
 hipError_t launch_decode_step(const MegaArgs& a, int G, int n_wg, size_t lds, hipStream_t stream) {
-  const void* k = mega_kernel_for(G, a.fmt, a.small != 0);
+  const void* k = mega_kernel_for(G, a.fmt, a.small != 0, a.oacc != nullptr);
   if (!k || n_wg < 1 || a.M < 1 || a.M > 16) return hipErrorInvalidValue;
   MegaArgs copy = a;
   void* args[] = {&copy};

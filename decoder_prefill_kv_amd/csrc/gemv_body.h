@@ -76,7 +76,10 @@ __host__ __device__ inline int gemv_lds_layout(int M, int K, int RB, int fmt, in
 // into LDS (pf + wave * T * U KB, this wave's slot) together with its first
 // two, so three iterations are in flight while the caller waits at its
 // barrier; the loop reads that iteration from LDS.
-template <int FMT, int T, int WAVES, bool COH, bool XG = false, int KI = 0, bool PF = false, typename Pre>
+// ACC (COH): a.xacc / a.racc may be set (the persistent step's fixed-point O
+// sums); without it they are ignored.
+template <int FMT, int T, int WAVES, bool COH, bool XG = false, int KI = 0, bool PF = false, bool ACC = false,
+          typename Pre>
 DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const int wg, const int nwg, Pre&& pre,
                        unsigned char* pf = nullptr) {
   static_assert(!PF || (FMT == W_BF16 && !XG), "LDS prefetch is for staged-x bf16 GEMVs");
@@ -94,7 +97,7 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
   } else {
     gemv_lds_layout(M, K, RB, FMT, WAVES, &xs_off, &xsum_off, &red_off, &misc_off);
   }
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = COH ? opaque_tid() : (int)threadIdx.x, wave = tid >> 6, lane = tid & 63;
   uint16_t* xs_hi = (uint16_t*)(lds + xs_off) + (size_t)wave * 2 * M * xstride;
   uint16_t* xs_lo = xs_hi + M * xstride;
   float* xsum = (float*)(lds + xsum_off);
@@ -203,10 +206,16 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
   // tile's first weights, so the epilogue does not wait for it
   const bool h_early = a.epi == EPI_RESID && M * RB <= THREADS;
   float h_tile = 0.f;
+  uint32_t r_lo = 0, r_hi = 0;  // racc word of the same element (COH)
   auto load_h = [&](int t) {
     if (h_early && tid < M * RB) {
       const uint32_t hi = (uint32_t)((tid / RB) * a.ldo + t * RB + tid % RB);
       h_tile = COH ? cload(coh_buffer(a.out), hi) : gmem(a.out)[hi];
+      if (COH && ACC && a.racc) {
+        const auto w = __builtin_amdgcn_raw_buffer_load_b64(coh_buffer(a.racc), hi * 8u, 0, CPOL_SC1);
+        r_lo = w[0];
+        r_hi = w[1];
+      }
     }
   };
   auto first_loads = [&]() {
@@ -267,6 +276,15 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
       const f32x4 v0 = cload4(coh_buffer(a.x), xi), v1 = cload4(coh_buffer(a.x), xi + 4);
       v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
       v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+      if (ACC && a.xacc) {  // x + the fixed-point sums (8 words = 4 x 16 bytes)
+        const coh_buf ab = coh_buffer(a.xacc);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x4 w = cload16(ab, xi / 2 + q);
+          v[2 * q] = v[2 * q] + from_fixed(fixed_word(w[0], w[1]));
+          v[2 * q + 1] = v[2 * q + 1] + from_fixed(fixed_word(w[2], w[3]));
+        }
+      }
     } else {
       const float4 v0 = *(const float4*)xp, v1 = *(const float4*)(xp + 4);
       v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
@@ -410,7 +428,7 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
       return s1;
     }
   };
-  auto finish_tile = [&](const int tile, const f32x4 (&acc)[T], const float h_pre) {
+  auto finish_tile = [&](const int tile, const f32x4 (&acc)[T], const float h_pre, const long long r_pre) {
     // ---- the waves' K parts go to red[(m * RB + r) * WAVES + wave] (D[n][m]
     // lane layout: rows 4 j4 + v, column r16), so one output's parts are
     // adjacent and the thread that sums them finishes that output itself
@@ -462,7 +480,17 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
       for (int i = tid; i < M * RB; i += THREADS) {
         const int m = i / RB, n = tile * RB + i % RB;
         const uint32_t hi = (uint32_t)(m * a.ldo + n);
-        const float h = (h_early ? h_pre : COH ? cload(coh_buffer(a.out), hi) : gmem(a.out)[hi]) + result(i);
+        float h0 = h_early ? h_pre : COH ? cload(coh_buffer(a.out), hi) : gmem(a.out)[hi];
+        if (COH && ACC && a.racc) {  // h after the O projection, exactly as the gate/up GEMV staged it
+          long long r = r_pre;
+          if (!h_early) {
+            const auto w = __builtin_amdgcn_raw_buffer_load_b64(coh_buffer(a.racc), hi * 8u, 0, CPOL_SC1);
+            r = fixed_word(w[0], w[1]);
+          }
+          h0 = h0 + from_fixed(r);
+          cstore8z(coh_buffer(a.racc), hi);
+        }
+        const float h = h0 + result(i);
         if constexpr (COH)
           cstore(coh_buffer(a.out), hi, h);
         else
@@ -533,12 +561,13 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
     // the next tile's first weights load while this tile is finished
     const int next = tile + nwg;
     const float h_cur = h_tile;
+    const long long r_cur = fixed_word(r_lo, r_hi);
     if (next < n_tiles) {
       set_tile(next);
       first_loads();
       load_h(next);
     }
-    finish_tile(tile, acc, h_cur);
+    finish_tile(tile, acc, h_cur, r_cur);
   }
 
   if (a.epi != EPI_HEAD) return;

@@ -112,6 +112,11 @@ struct GemvArgs {
   float* cand_val;          // HEAD: [M][grid]
   int* cand_idx;
   int* argmax_out;
+  // persistent step, O projection by KV head (fixed-point partial sums, see
+  // to_fixed): xacc [M][ldx] is added to x as it is staged; RESID with racc
+  // [M][ldo]: h = (h + racc) + y, and racc is cleared
+  const long long* xacc;
+  long long* racc;
 };
 size_t gemv_lds_bytes(int M, int K, int tiles, int fmt);
 size_t gemv_lds_bytes_waves(int M, int K, int tiles, int fmt, int waves);
@@ -263,6 +268,7 @@ hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t stream);
 
 // ---- whole decode step in one persistent (cooperative) launch, bf16 weights
 constexpr int MEGA_ATTN_MAXCH = 64;  // attention chunks per row (256 positions each)
+constexpr int MEGA_CTR_STRIDE = 64;  // words between the fused step's attention counters (own 256-byte line)
 struct MegaLayer {                   // device-resident, one per layer
   GemvArgs qkv;                      // the QKV projection, whole K: 32-row tiles (measured faster
                                      //   than 16-row tiles and than K splits that balance the tiles),
@@ -294,8 +300,11 @@ struct MegaArgs {
   float eps, scale;
   int max_chunks;
   float* part;                       // [M][n_heads][max_chunks][d + 2]
-  unsigned* attn_counters;           // [M * n_kv]
+  unsigned* attn_counters;           // [M * n_kv] (fused O: one per MEGA_CTR_STRIDE words)
   float* attn_out;                   // [M][n_heads * d]
+  long long* oacc;                   // [M][H] fixed-point O-projection sums, or null: the O projection is a
+                                     //   GEMV after attention (see attn_phase)
+  int o_rt;                          // 16-row tiles per O item (1, 2, 4 or 8) when oacc is set
   unsigned* bar;                     // MEGA_BAR_WORDS zeroed words: barrier counters, exit count, abort flag
   unsigned long long* trace;         // null, or MEGA_TRACE_WORDS accumulators (see below)
   int lds_args;                      // byte offset of the staged arguments (MEGA_ARGS_LDS bytes) and,
@@ -310,9 +319,13 @@ constexpr int MEGA_BAR_EXIT = 64 * 9, MEGA_BAR_ABORT = 64 * 10, MEGA_BAR_WORDS =
 constexpr int MEGA_ARGS_LDS = (int)((sizeof(MegaLayer) + sizeof(GemvArgs) + 16 * sizeof(RowParam) + 15) / 16 * 16);
 constexpr int MEGA_PF_LDS = 8 * 8 * 1024;
 size_t mega_attn_lds_bytes(int G);
+// LDS of the fused attention + O phase below the staged arguments (the
+// weights not held in the prefetch slots, x, reduction), 0 if the shape does
+// not fit it
+size_t mega_o_lds_bytes(int M, int G, int rt);
 int mega_threads();
 int mega_attn_chunk();
-int mega_occupancy(int G, int fmt, bool small, size_t lds);
+int mega_occupancy(int G, int fmt, bool small, bool fo, size_t lds);
 hipError_t launch_decode_step(const MegaArgs& a, int G, int n_wg, size_t lds, hipStream_t stream);
 
 // ---------------------------------------------------------------- sampling (sample.hip)

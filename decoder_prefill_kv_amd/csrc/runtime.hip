@@ -79,6 +79,7 @@ struct dpk_model {
   int* cand_idx = nullptr;
   _Float16 *y16 = nullptr, *q16 = nullptr, *o16 = nullptr, *act16 = nullptr;
   unsigned *counters = nullptr, *attn_counters = nullptr, *gemm_counters = nullptr;
+  long long* oacc = nullptr;  // [SKINNY_MAX][hidden] fixed-point O-projection sums of the persistent step
   float* gemm_ws = nullptr;
   // whole-step persistent decode kernel
   MegaLayer* mega_layers = nullptr;  // device table (in scratch)
@@ -123,10 +124,17 @@ namespace {
 
 size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
+// the attention chunk counters (the persistent step's fused O projection
+// keeps each on its own line)
+size_t attn_counter_bytes(const dpk_model* md) {
+  const bool f32 = md->fmt == DPK_FMT_F32;
+  return (size_t)(f32 ? md->cfg.max_rows : SKINNY_MAX) * md->cfg.n_kv_heads * 4 * (f32 ? 1 : MEGA_CTR_STRIDE);
+}
+
 struct ScratchLayout {
   size_t rope_cos, rope_sin, rows, h, rs, qkv, y32, qbuf, attn_o, act, part, sink, sq, cand_val, cand_idx, attn_part,
       y16, q16, o16, act16, counters, attn_counters, err, argmax_sink, spec_ids, gemm_ws, gemm_counters, mega_layers,
-      mega_bar, mega_trace, xb, total;
+      mega_bar, mega_trace, xb, oacc, total;
   size_t xb_w;
   int rows_f32, attn_chunks_cap;
   size_t part_floats;
@@ -187,7 +195,7 @@ ScratchLayout scratch_layout(const dpk_config& c) {
   L.o16 = take(f32 ? 0 : Rg * Qd * 2 * 2);  // per row hi then lo
   L.act16 = take(f32 ? 0 : Rg * I * 2);
   L.counters = take((1 + nbm) * 4);
-  L.attn_counters = take((size_t)(f32 ? R : SKINNY_MAX) * c.n_kv_heads * 4);
+  L.attn_counters = take((size_t)(f32 ? R : SKINNY_MAX) * c.n_kv_heads * 4 * (f32 ? 1 : MEGA_CTR_STRIDE));
   L.err = take(4);
   L.argmax_sink = take(SKINNY_MAX * 4);
   L.spec_ids = take(64 * 4);
@@ -200,6 +208,7 @@ ScratchLayout scratch_layout(const dpk_config& c) {
   L.xb_w = H > Qd ? H : Qd;
   if (I > L.xb_w) L.xb_w = I;
   L.xb = take(f32 ? 0 : 4 * SKINNY_MAX * L.xb_w * 2);
+  L.oacc = take(f32 ? 0 : SKINNY_MAX * H * 8);
   L.total = o;
   return L;
 }
@@ -665,6 +674,27 @@ int mega_variant(const dpk_model* md) {
   return -1;
 }
 
+// 16-row tiles per O-projection item when the persistent step runs the O
+// projection inside the attention phase (bf16 weights, hidden size 2048 or
+// more; the largest of 8, 4, 2, 1 that still gives every compute unit an
+// item), 0 when it runs as a GEMV after attention.  Measured on the 1024-wide
+// 0.6B shapes the fused phase saves ~1.9 us per layer but the O sums cost
+// gate/up and down ~2 us, so narrow models keep the GEMV.
+int mega_o_rt(const dpk_model* md, int M) {
+  const dpk_config& c = md->cfg;
+  // (attention keeps at most half the grid: the rest, at least n_kv
+  // workgroups, runs the O projection)
+  if (md->fmt != DPK_FMT_BF16 || !md->oacc || c.hidden < 2048 || c.n_kv_heads > 16 || c.hidden % 16 ||
+      md->n_cu < 2 * c.n_kv_heads)
+    return 0;
+  const int G = c.n_heads / c.n_kv_heads, tiles = c.hidden / 16;
+  for (int rt = 8; rt >= 1; rt /= 2) {
+    if (tiles % rt || (rt > 1 && (tiles / rt) * c.n_kv_heads < md->n_cu)) continue;
+    if (mega_o_lds_bytes(M, G, rt)) return rt;
+  }
+  return 0;
+}
+
 // LDS bytes of the persistent decode kernel for M rows, or 0 if the model or
 // M does not fit it: bf16 or 4-bit weights, head_dim 128, 1, 2 or 4 query
 // heads per KV head (2 or 4 for the 128-column tiling), every GEMV on eight
@@ -683,6 +713,10 @@ size_t mega_lds_for(dpk_model* md, int M, int max_ctx) {
   const int H = c.hidden, Qd = c.n_heads * c.head_dim, I = c.intermediate;
   if ((max_ctx + mega_attn_chunk() - 1) / mega_attn_chunk() > MEGA_ATTN_MAXCH) return 0;
   size_t lds = mega_attn_lds_bytes(G);
+  if (const int ort = mega_o_rt(md, M)) {
+    const size_t ob = mega_o_lds_bytes(M, G, ort);
+    if (ob > lds) lds = ob;
+  }
   for (size_t b : {gemv_lds_bytes_waves(M, H, var ? 1 : 2, fmt, 8), gemv_lds_bytes_waves(M, Qd, 1, fmt, 8),
                    gemv_lds_bytes_waves(M, H, 2, fmt, 8), gemv_lds_bytes_waves(M, I, 1, fmt, 8),
                    gemv_lds_bytes_waves(M, H, 1, fmt, 8)})
@@ -691,7 +725,7 @@ size_t mega_lds_for(dpk_model* md, int M, int max_ctx) {
   // GEMVs' prefetch slots
   lds = (lds + 15) / 16 * 16 + MEGA_ARGS_LDS + (fmt == W_BF16 ? MEGA_PF_LDS : 0);
   if (lds > (size_t)md->lds_max) return 0;
-  if (mega_occupancy(G, fmt, var == 1, lds) < 1) return 0;
+  if (mega_occupancy(G, fmt, var == 1, mega_o_rt(md, M) > 0, lds) < 1) return 0;
   return lds;
 }
 
@@ -712,6 +746,12 @@ dpk_status mega_table(dpk_model* md, hipStream_t st) {
                         nullptr);
     t[l].down = gemv_args(md, 1, md->act, I, nullptr, 0, nullptr, &L.down, 1, EPI_RESID, false, 1, md->h, H, md->sq,
                           nullptr);
+    // the fixed-point O sums (zero when the O projection runs as a GEMV)
+    // join h where gate/up stages it and where down adds to it
+    if (md->fmt == DPK_FMT_BF16) {
+      t[l].gu.xacc = md->oacc;
+      t[l].down.racc = md->oacc;
+    }
     t[l].qn = c.qk_norm ? (const uint16_t*)L.q_norm : nullptr;
     t[l].kn = c.qk_norm ? (const uint16_t*)L.k_norm : nullptr;
   }
@@ -761,6 +801,8 @@ dpk_status forward_mega(dpk_model* md, int M, int max_ctx, size_t lds, const Row
   a.part = md->attn_part;
   a.attn_counters = md->attn_counters;
   a.attn_out = md->attn_o;
+  a.o_rt = mega_o_rt(md, M);
+  a.oacc = a.o_rt ? md->oacc : nullptr;
   a.bar = md->mega_bar;
   a.trace = md->prof ? md->mega_trace : nullptr;
   a.lds_args = (int)(lds - MEGA_ARGS_LDS - (md->fmt == DPK_FMT_BF16 ? MEGA_PF_LDS : 0));
@@ -1095,6 +1137,7 @@ dpk_status dpk_bind_workspace(dpk_model* md, void* kv, void* scratch, void* prep
   md->mega_layers = L.mega_bar > L.mega_layers ? (MegaLayer*)(s + L.mega_layers) : nullptr;
   md->mega_bar = (unsigned*)(s + L.mega_bar);
   md->mega_trace = (unsigned long long*)(s + L.mega_trace);
+  md->oacc = L.total > L.oacc ? (long long*)(s + L.oacc) : nullptr;
   md->xb_w = (int)L.xb_w;
   for (int i = 0; i < 4; ++i)
     md->xb[i / 2][i % 2] = L.total > L.xb ? (uint16_t*)(s + L.xb) + (size_t)i * SKINNY_MAX * L.xb_w : nullptr;
@@ -1117,10 +1160,11 @@ dpk_status dpk_bind_workspace(dpk_model* md, void* kv, void* scratch, void* prep
     if (lmax > 0) md->lds_max = lmax;
   }
   HIP_TRY(hipMemsetAsync(md->counters, 0, (1 + nblocks_max(c)) * 4, st));
-  HIP_TRY(hipMemsetAsync(md->attn_counters, 0, (size_t)(md->fmt == DPK_FMT_F32 ? c.max_rows : SKINNY_MAX) * c.n_kv_heads * 4, st));
+  HIP_TRY(hipMemsetAsync(md->attn_counters, 0, attn_counter_bytes(md), st));
   HIP_TRY(hipMemsetAsync(md->err_flag, 0, 4, st));
   if (md->gemm_counters) HIP_TRY(hipMemsetAsync(md->gemm_counters, 0, GEMM_WS_TILES * 4, st));
   HIP_TRY(hipMemsetAsync(md->mega_bar, 0, MEGA_BAR_WORDS * 4, st));
+  if (md->oacc) HIP_TRY(hipMemsetAsync(md->oacc, 0, (size_t)SKINNY_MAX * c.hidden * 8, st));
   HIP_TRY(launch_rope_table(md->rope_cos, md->rope_sin, c.max_seq, c.head_dim, c.rope_theta, st));
   md->bound = true;
   return DPK_OK;
@@ -1370,10 +1414,10 @@ dpk_status dpk_seq_length(const dpk_model* md, int32_t seq, int32_t* length) {
 dpk_status reset_counters(dpk_model* md, hipStream_t st) {
   const dpk_config& c = md->cfg;
   HIP_TRY(hipMemsetAsync(md->counters, 0, (1 + nblocks_max(c)) * 4, st));
-  HIP_TRY(hipMemsetAsync(md->attn_counters, 0,
-                         (size_t)(md->fmt == DPK_FMT_F32 ? c.max_rows : SKINNY_MAX) * c.n_kv_heads * 4, st));
+  HIP_TRY(hipMemsetAsync(md->attn_counters, 0, attn_counter_bytes(md), st));
   if (md->gemm_counters) HIP_TRY(hipMemsetAsync(md->gemm_counters, 0, GEMM_WS_TILES * 4, st));
   HIP_TRY(hipMemsetAsync(md->mega_bar, 0, MEGA_BAR_WORDS * 4, st));
+  if (md->oacc) HIP_TRY(hipMemsetAsync(md->oacc, 0, (size_t)SKINNY_MAX * c.hidden * 8, st));
   return DPK_OK;
 }
 

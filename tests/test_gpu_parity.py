@@ -78,12 +78,21 @@ def test_prefill_and_decode_match_oracle(dpk, name, cfg, P, N, kw):
     dec.close()
 
 
+# hidden size 2048, bf16: the persistent step runs the O projection inside
+# the attention phase (split by KV head, fixed-point sums); with 4 and 8 KV
+# heads its items are 32- and 64-row blocks shared by 4 and 2 waves per row
+# tile
+H2048_G4 = synth.Q8B.with_(n_layers=2, hidden=2048, n_heads=16, n_kv_heads=4, intermediate=4096, vocab=4096)
+H2048_G2 = synth.Q8B.with_(n_layers=2, hidden=2048, n_heads=16, n_kv_heads=8, intermediate=4096, vocab=4096)
+
 PERSISTENT_CFGS = [
     # (name, config, prompt length): contexts P .. P + 31 cross a 256-position
     # attention chunk boundary; the long ones merge 17 chunks
     ("q8b-L2-v4096", synth.Q8B.with_(n_layers=2, vocab=4096), 250),          # 256 columns per wave step
     ("q06b-L2-v4096", synth.Q06B.with_(n_layers=2, vocab=4096), 250),        # 128 columns, bf16
     ("q06b_q4-L2-v4096", synth.Q06B_Q4.with_(n_layers=2, vocab=4096), 250),  # 128 columns, 4-bit
+    ("h2048-g4-L2-v4096", H2048_G4, 250),                                   # O projection in the attention phase
+    ("h2048-g2-L2-v4096", H2048_G2, 250),
     ("q8b-L1-v4096-ctx4100", synth.Q8B.with_(n_layers=1, vocab=4096), 4080),
     ("q06b_q4-L1-v4096-ctx4100", synth.Q06B_Q4.with_(n_layers=1, vocab=4096), 4080),
 ]
@@ -223,8 +232,11 @@ def test_batched_decode_matches_oracle(dpk):
     dec.close()
 
 
-@pytest.mark.parametrize("name,cfg", [("q06b-L2", synth.Q06B.with_(n_layers=2)),
-                                      ("q06b_q4-L2", synth.Q06B_Q4.with_(n_layers=2))], ids=["q06b-L2", "q06b_q4-L2"])
+BATCHED_PERSISTENT = [("q06b-L2", synth.Q06B.with_(n_layers=2)), ("q06b_q4-L2", synth.Q06B_Q4.with_(n_layers=2)),
+                      ("h2048-g4-L2-v4096", H2048_G4), ("h2048-g2-L2-v4096", H2048_G2)]
+
+
+@pytest.mark.parametrize("name,cfg", BATCHED_PERSISTENT, ids=[c[0] for c in BATCHED_PERSISTENT])
 def test_batched_persistent_decode_long_contexts(dpk, name, cfg):
     """Three sequences decoded together through the persistent step (M = 3
     rows, each with its own position and cache), with contexts of one, two
