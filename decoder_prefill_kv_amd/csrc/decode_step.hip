@@ -280,9 +280,14 @@ DPK_DEV void o_products_kw(bool pack, bool two, const u32x4 (&w0)[O_KWMAX], cons
   }
 }
 
-template <int G, typename Sync>
-DPK_DEV void o_phase(const MegaArgs& a, const RowParam* rows, int layer, const GemvArgs* Lo, unsigned char* lds,
-                     const Barrier& bar, int ow, int n_ow, Sync&& sync) {
+//
+// Its prefetch slots are free during this phase, so it also loads the
+// gate/up GEMV's LDS-prefetched iteration (gemv_pf_first) when the QKV
+// barrier is passed; returns whether it did.
+template <int G, int KI, typename Sync>
+DPK_DEV bool o_phase(const MegaArgs& a, const RowParam* rows, int layer, const GemvArgs* Lo, const GemvArgs* Lgu,
+                     unsigned char* lds, unsigned char* pf, const Barrier& bar, int wg, int ow, int n_ow,
+                     Sync&& sync) {
   const int tid = opaque_tid(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, j4 = lane >> 4;
@@ -296,11 +301,13 @@ DPK_DEV void o_phase(const MegaArgs& a, const RowParam* rows, int layer, const G
 
   u32x4 w0[O_KWMAX], w1[O_KWMAX];  // this wave's blocks of items ow and ow + n_ow
   const int j0 = ow, j1 = ow + n_ow;
+  bool gu_pf = false;
   sync([&] {  // the QKV projection of every row is complete after this
     if (j0 < o.n_o) o_load<G>(a, Lo, o, j0, w0);
     if (j1 < o.n_o) o_load<G>(a, Lo, o, j1, w1);
+    gu_pf = gemv_detail::gemv_pf_first<2, 8, KI>(*Lgu, wg, pf);
   });
-  if (j0 >= o.n_o) return;  // uniform over the workgroup
+  if (j0 >= o.n_o) return gu_pf;  // uniform over the workgroup
 
   // every row's chunks of g have stored their records
   if (tid == 0) {
@@ -418,12 +425,15 @@ DPK_DEV void o_phase(const MegaArgs& a, const RowParam* rows, int layer, const G
     if (two) finish(jb, y1);
   }
   lds_barrier();  // x' and red are rewritten by the next phase
+  return gu_pf;
 }
 
-template <int G, bool FO, typename Sync>
-DPK_DEV void attn_phase(const MegaArgs& a, const RowParam* rows, int layer, const uint16_t* qn, const uint16_t* kn,
-                        const GemvArgs* Lo, unsigned char* lds, const Barrier& bar, int wg,
-                        int nwg, Sync&& sync) {
+// Returns whether the gate/up GEMV's LDS-prefetched iteration was loaded
+// here (FO: o_phase).
+template <int G, bool FO, int KI, typename Sync>
+DPK_DEV bool attn_phase(const MegaArgs& a, const RowParam* rows, int layer, const uint16_t* qn, const uint16_t* kn,
+                        const GemvArgs* Lo, const GemvArgs* Lgu, unsigned char* lds, unsigned char* pf,
+                        const Barrier& bar, int wg, int nwg, Sync&& sync) {
   // q (log2 domain) as fp16 hi + lo and the new position's K / V in cache
   // precision, all in MFMA fragment order (8 consecutive d per 16 bytes)
   _Float16* qh16 = (_Float16*)lds;      // [G][D]
@@ -489,10 +499,7 @@ DPK_DEV void attn_phase(const MegaArgs& a, const RowParam* rows, int layer, cons
   if constexpr (FO) {
     const int n_ow = ((nwg - min(n_items, nwg / 2)) / a.n_kv) * a.n_kv;
     n_aw = nwg - n_ow;
-    if (wg >= n_aw) {
-      o_phase<G>(a, rows, layer, Lo, lds, bar, wg - n_aw, n_ow, sync);
-      return;
-    }
+    if (wg >= n_aw) return o_phase<G, KI>(a, rows, layer, Lo, Lgu, lds, pf, bar, wg, wg - n_aw, n_ow, sync);
   }
   int it = wg;
   sync([&] {  // the QKV projection of every row is complete after this
@@ -735,6 +742,7 @@ DPK_DEV void attn_phase(const MegaArgs& a, const RowParam* rows, int layer, cons
     }
     __syncthreads();  // LDS is rewritten by the next item
   }
+  return false;
 }
 
 // FMT: weight format of every GEMV.  SMALL: each wave reduces 128 columns per
@@ -802,13 +810,13 @@ __global__ __launch_bounds__(MT, 1) void decode_step_kernel(MegaArgs a) {
     const MegaLayer& L = *Ls;
     gemv_body<FMT, TQ, 8, true, false, KI, PF>(L.qkv, a.M, lds, wg, nwg, sync, pf);
     closing = MP_QKV;
-    attn_phase<G, FO>(a, Rs, l, L.qn, L.kn, &L.o, lds, bar, wg, nwg, sync);
+    const bool gu_pf = attn_phase<G, FO, KI>(a, Rs, l, L.qn, L.kn, &L.o, &L.gu, lds, pf, bar, wg, nwg, sync);
     closing = MP_ATTN;
     if constexpr (!FO) {
       gemv_body<FMT, 1, 8, true, false, KI, PF>(L.o, a.M, lds, wg, nwg, sync, pf);
       closing = MP_O;
     }
-    gemv_body<FMT, 2, 8, true, false, KI, PF, FO>(L.gu, a.M, lds, wg, nwg, sync, pf);
+    gemv_body<FMT, 2, 8, true, false, KI, PF, FO>(L.gu, a.M, lds, wg, nwg, sync, pf, gu_pf);
     closing = MP_GATEUP;
     gemv_body<FMT, 1, 8, true, false, KI, PF, FO>(L.down, a.M, lds, wg, nwg, sync, pf);
     closing = MP_DOWN;

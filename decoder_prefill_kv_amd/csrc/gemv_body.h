@@ -75,13 +75,67 @@ __host__ __device__ inline int gemv_lds_layout(int M, int K, int RB, int fmt, in
 // PF (bf16): the first tile's third iteration of weights is loaded straight
 // into LDS (pf + wave * T * U KB, this wave's slot) together with its first
 // two, so three iterations are in flight while the caller waits at its
-// barrier; the loop reads that iteration from LDS.
+// barrier; the loop reads that iteration from LDS.  pf_ready: the caller has
+// already loaded it (gemv_pf_first).
 // ACC (COH): a.xacc / a.racc may be set (the persistent step's fixed-point O
 // sums); without it they are ignored.
+// 16-row tile index (inside its segment, seg) of 16-row tile t of row tile
+// `tile` (RB = 16 T rows)
+template <int T>
+DPK_DEV size_t gemv_tile_rt(const GemvArgs& a, int tile, int t, int& seg) {
+  constexpr int RB = 16 * T;
+  int rt;
+  if (a.swiglu) {  // RB/2 gate rows then RB/2 up rows, both at rows tile * RB/2
+    seg = t / (T / 2 > 0 ? T / 2 : 1);
+    rt = tile * (T / 2) + t % (T / 2 > 0 ? T / 2 : 1);
+  } else {
+    const int n = tile * RB + t * 16;
+    seg = 0;
+    int base = 0;
+    while (seg < 2 && n >= a.seg_end[seg]) { base = a.seg_end[seg]; ++seg; }
+    rt = (n - base) / 16;
+  }
+  return (size_t)rt;
+}
+
+// (bf16, staged x) k-steps of 32 columns a wave reduces per iteration
+template <int T, int KI>
+constexpr int gemv_bf16_u() {
+  return KI ? KI / 32 : 8 / T;
+}
+
+// The LDS-prefetched iteration of workgroup wg's first row tile -- what
+// gemv_body (PF) loads when its barrier is passed -- issued earlier by a
+// persistent caller whose prefetch slots are free sooner; gemv_body is then
+// called with pf_ready.  Returns whether anything was issued.
+template <int T, int WAVES, int KI>
+DPK_DEV bool gemv_pf_first(const GemvArgs& a, int wg, unsigned char* pf) {
+  constexpr int U = gemv_bf16_u<T, KI>();
+  const int K = a.K, KF = a.kfull ? a.kfull : K, KO = a.kofs;
+  const int kq = K / WAVES, nit = kq / (32 * U);
+  const int rows = a.swiglu ? 2 * a.N : a.N;
+  if (wg >= rows / (16 * T) || nit <= 2) return false;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  unsigned char* const slot = pf + (size_t)wave * (T * U * 1024);
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    int seg;
+    const size_t rt = gemv_tile_rt<T>(a, wg, t, seg);
+    const unsigned char* wp =
+        (const unsigned char*)a.w[seg] + (rt * (KF / 32) + (KO + wave * kq) / 32) * 1024 + lane * 16;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      __builtin_amdgcn_global_load_lds(gmem((const void*)(wp + (size_t)(2 * U + u) * 1024)),
+                                       (__attribute__((address_space(3))) void*)(slot + (t * U + u) * 1024), 16, 0,
+                                       2 /* nt */);
+  }
+  return true;
+}
+
 template <int FMT, int T, int WAVES, bool COH, bool XG = false, int KI = 0, bool PF = false, bool ACC = false,
           typename Pre>
 DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const int wg, const int nwg, Pre&& pre,
-                       unsigned char* pf = nullptr) {
+                       unsigned char* pf = nullptr, bool pf_ready = false) {
   static_assert(!PF || (FMT == W_BF16 && !XG), "LDS prefetch is for staged-x bf16 GEMVs");
   static_assert(!XG || FMT == W_BF16, "ready-made activations are for bf16 weights");
   constexpr int RB = 16 * T;
@@ -109,25 +163,11 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
   const int rows = a.swiglu ? 2 * a.N : a.N;
   const int n_tiles = rows / RB;
 
-  // 16-row tile index (inside its segment) of tile t of row tile `tile`
-  auto tile_rt = [&](int tile, int t, int& seg) -> size_t {
-    int rt;
-    if (a.swiglu) {  // RB/2 gate rows then RB/2 up rows, both at rows tile * RB/2
-      seg = t / (T / 2 > 0 ? T / 2 : 1);
-      rt = tile * (T / 2) + t % (T / 2 > 0 ? T / 2 : 1);
-    } else {
-      const int n = tile * RB + t * 16;
-      seg = 0;
-      int base = 0;
-      while (seg < 2 && n >= a.seg_end[seg]) { base = a.seg_end[seg]; ++seg; }
-      rt = (n - base) / 16;
-    }
-    return (size_t)rt;
-  };
+  auto tile_rt = [&](int tile, int t, int& seg) -> size_t { return gemv_tile_rt<T>(a, tile, t, seg); };
 
   // bf16: k-steps of 32 per iteration (XG holds its activations in registers
   // as well, so a one-tile XG wave loads half as much per iteration)
-  constexpr int U = KI ? KI / 32 : (XG && T == 1) ? 4 : 8 / T;
+  constexpr int U = (XG && T == 1 && !KI) ? 4 : gemv_bf16_u<T, KI>();
   constexpr int GU = KI ? KI / 64 : 4 / T > 0 ? 4 / T : 1;  // 4-bit: groups of 64 per iteration
   static_assert(KI % 64 == 0, "whole 4-bit groups per iteration");
   const int nit = (FMT == W_BF16) ? kq / (32 * U) : kq / (64 * GU);
@@ -232,7 +272,10 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
     if (tile < n_tiles) {
       set_tile(tile);
       first_loads();
-      pf_issue();
+      if (pf_ready)  // (gemv_pf_first issued it)
+        in_pf = PF && nit > 2;
+      else
+        pf_issue();
       load_h(tile);
     }
   });
