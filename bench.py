@@ -29,18 +29,18 @@ MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 matrix throughput
 # (--copy-probe): FETCH_SIZE x 2.0, WRITE_SIZE x 1.0.  A figure is only
 # reported while the kernel's sources are the ones it was taken on.
 TRAFFIC = {
-    ("q8b", "decode.step"): {"fetch_kib": 7570861.4, "write_kib": 19979.1, "fetch_factor": 2.0, "write_factor": 1.0,
+    ("q8b", "decode.step"): {"fetch_kib": 7563906.8, "write_kib": 50617.4, "fetch_factor": 2.0, "write_factor": 1.0,
                              "sources": ["decoder_prefill_kv_amd/csrc/decode_step.hip",
                                          "decoder_prefill_kv_amd/csrc/gemv_body.h",
                                          "decoder_prefill_kv_amd/csrc/common.h",
                                          "decoder_prefill_kv_amd/csrc/kernels.h"],
-                             "sha256": "945376821cd2cb1074918187bc9a614e8fa805561cbdeb06faf9f031d7e87e43"},
+                             "sha256": "157760266d420c7c7374075e7c0ee3c58c7dba1757dc133fb7beb87837ecfcfb"},
     # the prefill gate+up GEMM (M = 2048): operands re-read from HBM ~3.5x
-    ("q8b", "gemm.gate_up"): {"fetch_kib": 382914.6, "write_kib": 49152.5, "fetch_factor": 2.0, "write_factor": 1.0,
+    ("q8b", "gemm.gate_up"): {"fetch_kib": 381042.8, "write_kib": 49152.6, "fetch_factor": 2.0, "write_factor": 1.0,
                               "sources": ["decoder_prefill_kv_amd/csrc/gemm.hip",
                                           "decoder_prefill_kv_amd/csrc/common.h",
                                           "decoder_prefill_kv_amd/csrc/kernels.h"],
-                              "sha256": "e3c25bbfb9fd88e832a29f70dde3fdf4041e3f182e4089f8a8cc1ae37877b7ad"},
+                              "sha256": "e7d0729d0db0be76ccec5f401e5066106645a1cdd6f77d00b59482dcd9fc2814"},
 }
 
 
