@@ -132,6 +132,14 @@ def dequant_i8(q: np.ndarray, scales_bf16: np.ndarray, dtype=torch.float64) -> t
     return (torch.from_numpy(q.astype(np.float64)) * s).to(dtype)
 
 
+def dequant_q8(q: np.ndarray, scales_f32: np.ndarray, dtype=torch.float64) -> torch.Tensor:
+    """w[n, k] = scale[n, k // 32] * q[n, k], in float64: int8 codes in blocks of
+    32 weights along the input dimension, one float32 scale per block (oxinfer
+    docs page, "Build and run", the q8 quantization flag)."""
+    s = torch.from_numpy(np.ascontiguousarray(scales_f32, dtype=np.float32).astype(np.float64))
+    return (torch.from_numpy(q.astype(np.float64)) * torch.repeat_interleave(s, 32, dim=1)).to(dtype)
+
+
 class OracleModel:
     """The decoder with weights taken exactly as stored (bf16 widen exactly)."""
 
@@ -150,6 +158,8 @@ class OracleModel:
                               self.w[name + ".biases"], self.dtype)
         if cfg.weight_format == "i8" and name + ".q" in self.w:
             return dequant_i8(self.w[name + ".q"], self.w[name + ".scales"], self.dtype)
+        if cfg.weight_format == "q8" and name + ".q" in self.w:
+            return dequant_q8(self.w[name + ".q"], self.w[name + ".scales"], self.dtype)
         a = self.w[name]
         if a.dtype == np.uint16:
             return torch.from_numpy(synth.bf16_bits_to_f32(a)).to(self.dtype)
@@ -180,6 +190,9 @@ class OracleModel:
         if cfg.weight_format == "i8":
             sel = np.array(ids, dtype=np.int64)
             return dequant_i8(self.w["embed_tokens.q"][sel], self.w["embed_tokens.scales"][sel], self.dtype)
+        if cfg.weight_format == "q8":
+            sel = np.array(ids, dtype=np.int64)
+            return dequant_q8(self.w["embed_tokens.q"][sel], self.w["embed_tokens.scales"][sel], self.dtype)
         E = self.w["embed_tokens"]
         rows = E[np.array(ids, dtype=np.int64)]
         if rows.dtype == np.uint16:

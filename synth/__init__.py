@@ -20,6 +20,12 @@ checkpoint.  Storage formats:
   quantisation of the N(0, std) weights: scale = bf16(max |w| / 127),
   q = round(w / scale) clipped to [-127, 127]).  A tensor ``name`` becomes
   ``name.q`` int8 ``[out, in]`` and ``name.scales`` uint16 (bf16) ``[out, 1]``.
+* ``q8``   - int8 in blocks of 32 along the input dimension with one float32
+  scale per block (oxinfer docs page, "Build and run", the q8 quantization
+  flag; its pre-quantized files store the same blocks as int8 codes plus
+  float32 scales): scale = max |w| / 127 over the block (float32),
+  q = round(w / scale) clipped to [-127, 127].  A tensor ``name`` becomes
+  ``name.q`` int8 ``[out, in]`` and ``name.scales`` float32 ``[out, in/32]``.
 """
 from __future__ import annotations
 
@@ -132,7 +138,7 @@ class ModelConfig:
     head_dim: int
     intermediate: int
     vocab: int
-    weight_format: str     # "f32" | "bf16" | "q4" | "i8"
+    weight_format: str     # "f32" | "bf16" | "q4" | "i8" | "q8"
     qk_norm: bool
     tied: bool
     rms_eps: float = 1e-6
@@ -196,8 +202,12 @@ Q8B = ModelConfig("q8b", 36, 4096, 32, 8, 128, 12288, 151936, "bf16", qk_norm=Tr
 # same decode path)
 Q06B_I8 = Q06B.with_(family="q06b_i8", weight_format="i8")
 Q8B_I8 = Q8B.with_(family="q8b_i8", weight_format="i8")
+# Q8 block variants (32 weights per float32 scale)
+Q06B_Q8 = Q06B.with_(family="q06b_q8", weight_format="q8")
+Q8B_Q8 = Q8B.with_(family="q8b_q8", weight_format="q8")
 
-CONFIGS = {"tiny": TINY, "q06b": Q06B, "q06b_q4": Q06B_Q4, "q8b": Q8B, "q06b_i8": Q06B_I8, "q8b_i8": Q8B_I8}
+CONFIGS = {"tiny": TINY, "q06b": Q06B, "q06b_q4": Q06B_Q4, "q8b": Q8B, "q06b_i8": Q06B_I8, "q8b_i8": Q8B_I8,
+           "q06b_q8": Q06B_Q8, "q8b_q8": Q8B_Q8}
 
 
 def _gain(cfg: ModelConfig, seed: int, name: str, shape) -> np.ndarray:
@@ -233,6 +243,12 @@ def _linear(cfg: ModelConfig, seed: int, name: str, shape) -> Dict[str, np.ndarr
         sc = f32_to_bf16_bits((np.abs(w).max(axis=1, keepdims=True) / 127.0).astype(np.float32))
         q = np.clip(np.rint(w / bf16_bits_to_f32(sc)), -127, 127).astype(np.int8)
         return {name + ".q": q, name + ".scales": sc}
+    if cfg.weight_format == "q8":
+        assert cols % 32 == 0
+        w = normal_f32(key_of(seed, tag), shape, cfg.init_std).reshape(rows, cols // 32, 32)
+        sc = (np.abs(w).max(axis=2) / np.float32(127.0)).astype(np.float32)
+        q = np.clip(np.rint(w / np.where(sc > 0, sc, np.float32(1.0))[..., None]), -127, 127)
+        return {name + ".q": q.astype(np.int8).reshape(rows, cols), name + ".scales": sc}
     if cfg.weight_format == "q4":
         assert cols % 64 == 0
         return {

@@ -528,6 +528,55 @@ def test_i8_dequant_hand_values_and_requant(synth_built):
         assert float((Wd - torch.from_numpy(ref).double()).abs().div(s).max()) <= 0.5 + 1e-3
 
 
+def test_q8_dequant_hand_values_blocks_and_requant(synth_built):
+    """Each run of 32 weights along a row takes its own float32 scale: column
+    k uses scale[n, k // 32] (a scale indexed k % 32, or per row, fails)."""
+    from oracle.decoder import dequant_q8
+    q = np.zeros((2, 64), dtype=np.int8)
+    q[0, 0], q[0, 31], q[0, 32], q[0, 63] = 3, -5, 127, 1
+    q[1, 1], q[1, 33] = -127, 2
+    sc = np.array([[0.5, 0.25], [0.1, 3.0]], dtype=np.float32)
+    W = dequant_q8(q, sc)
+    assert W[0, 0] == 1.5 and W[0, 31] == -2.5 and W[0, 32] == 31.75 and W[0, 63] == 0.25
+    assert W[1, 1] == -127 * float(np.float32(0.1)) and W[1, 33] == 6.0
+    assert int((W != 0).sum()) == 6
+    cfg = synth.Q06B.with_(family="q8pin", weight_format="q8", n_layers=1, vocab=512)
+    w = synth.make_weights(cfg, 3)
+    for name in ("layers.0.mlp.down_proj", "embed_tokens"):
+        q, sc = w[name + ".q"], w[name + ".scales"]
+        assert sc.dtype == np.float32 and sc.shape == (q.shape[0], q.shape[1] // 32)
+        s = torch.repeat_interleave(torch.from_numpy(sc).double(), 32, dim=1)
+        Wd = dequant_q8(q, sc)
+        assert torch.equal(torch.round(Wd / s).to(torch.int64), torch.from_numpy(q.astype(np.int64)))
+        # per-block absmax scaling: every block holds a code of magnitude 127
+        assert int(np.abs(q.astype(np.int32)).reshape(q.shape[0], -1, 32).max(axis=2).min()) == 127
+        # within half a step of the N(0, std) draw it was quantised from
+        ref = synth.normal_f32(synth.key_of(3, cfg.family + "/" + name), q.shape, cfg.init_std)
+        assert float((Wd - torch.from_numpy(ref).double()).abs().div(s).max()) <= 0.5 + 1e-3
+
+
+def test_q8_model_equals_f64_weight_model_with_the_dequantized_weights(synth_built):
+    """The block-scaled model must equal a plain-format model that holds the
+    products scale * q in float64 (exact: 24-bit scale times 8-bit code)."""
+    from oracle.decoder import dequant_q8
+    cfg = synth.Q06B.with_(family="q8pin2", weight_format="q8", n_layers=2, vocab=512, hidden=256, n_heads=4,
+                           n_kv_heads=2, intermediate=512)
+    w = synth.make_weights(cfg, 1)
+    f = {}
+    for k, v in w.items():
+        if k.endswith(".q"):
+            f[k[:-2]] = dequant_q8(v, w[k[:-2] + ".scales"]).numpy()
+        elif not k.endswith(".scales"):
+            f[k] = synth.bf16_bits_to_f32(v)
+    cf = cfg.with_(weight_format="f32")
+    prompt = synth.prompt_ids(cfg, 12, 0)
+    ma = oracle.OracleModel(cfg, w)
+    a = ma.forward_block(ma.new_cache(12), prompt, 0)
+    mb = oracle.OracleModel(cf, f)
+    b = mb.forward_block(mb.new_cache(12), prompt, 0)
+    assert float((a - b).abs().max()) == 0.0
+
+
 def test_i8_model_equals_f32_model_with_the_dequantized_weights(synth_built):
     """scale (bf16, 8 significant bits) times q (int8) is exact in fp32, so
     the int8 model must equal an fp32-format model holding those products."""
