@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "_dpk.so")
 
 DPK_OK, DPK_EINVAL, DPK_ERANGE, DPK_ESTATE, DPK_ENOMEM, DPK_EHIP = 0, -1, -2, -3, -4, -5
-FMT_F32, FMT_BF16, FMT_Q4G64, FMT_I8 = 0, 1, 2, 3
+FMT_F32, FMT_BF16, FMT_Q4G64, FMT_I8, FMT_Q8 = 0, 1, 2, 3, 4
 FLAG_PREFILL_STREAM = 1
 DT_F32, DT_BF16, DT_U32, DT_I8 = 0, 1, 2, 3
 SYMBOLS = ["dpk_create", "dpk_workspace_size", "dpk_bind_workspace", "dpk_load_weights", "dpk_prefill",
@@ -291,7 +291,7 @@ def destroy(model: int):
 
 
 # ------------------------------------------------------------------ convenience
-_FMT = {"f32": FMT_F32, "bf16": FMT_BF16, "q4": FMT_Q4G64, "i8": FMT_I8}
+_FMT = {"f32": FMT_F32, "bf16": FMT_BF16, "q4": FMT_Q4G64, "i8": FMT_I8, "q8": FMT_Q8}
 
 
 def make_config(mc, max_batch: int, max_seq: int, max_rows: int = 512, flags: int = 0) -> Config:

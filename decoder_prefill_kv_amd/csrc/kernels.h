@@ -34,10 +34,11 @@ enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_
 
 struct SkinnyArgs {
   int M, K, N;  // activation rows (<=16), input dim, output rows
-  int fmt;      // W_BF16 | W_Q4 | W_I8
+  int fmt;      // W_BF16 | W_Q4 | W_I8 | W_Q8
   const void* w[3];         // bf16 [rows][K], q4 codes uint32 [rows][K/8] or int8 [rows][K]
   const uint16_t* sc[3];    // q4 scales bf16 [rows][K/64]; int8: row scales bf16 [rows]
   const uint16_t* bi[3];    // q4 biases bf16 [rows][K/64]
+  const float* sf[3];       // q8: block scales fp32 [rows][K/32]
   int seg_end[3];           // cumulative row ends of the stacked segments
   int seg_rows[3];          // rows of each segment (load clamp)
   const float* x;
@@ -180,7 +181,8 @@ hipError_t launch_rope_table(float* cos_t, float* sin_t, int max_seq, int d, dou
                              hipStream_t stream);
 // h[m] = E[token_m] (fp32 / bf16 / q4 table); rs[m] = rsqrt(mean(h^2)+eps) if rs != null;
 // sq[m] = sum(h^2) if sq != null
-hipError_t launch_embed(int M, int H, int fmt, const void* table, const uint16_t* sc, const uint16_t* bi,
+// sc: bf16 scales (q4 groups, i8 rows) or fp32 block scales (q8)
+hipError_t launch_embed(int M, int H, int fmt, const void* table, const void* sc, const uint16_t* bi,
                         const RowParam* rp, const int32_t* ids_dev, int vocab, float* h, float* rs,
                         float eps, int* err_flag, hipStream_t stream, float* sq = nullptr);
 // y[m] = x[m] * rsqrt(mean(x^2)+eps) * g; y_is_f16: 0 fp32, 1 fp16, 2 fp16 hi
@@ -210,6 +212,7 @@ hipError_t launch_add(int n, const float* in, float* out, hipStream_t stream);
 hipError_t launch_bf16_to_f16(const uint16_t* src, _Float16* dst, size_t n, hipStream_t stream);
 hipError_t launch_i8_to_f16(const int8_t* q, const uint16_t* sc, int rows, int K, _Float16* dst,
                             hipStream_t stream);
+hipError_t launch_q8_to_f16(const int8_t* q, const float* sf, int rows, int K, _Float16* dst, hipStream_t stream);
 hipError_t launch_q4_to_f16(const uint32_t* codes, const uint16_t* sc, const uint16_t* bi, int rows, int K,
                             _Float16* dst, hipStream_t stream);
 hipError_t launch_f32_to_f16(const float* src, _Float16* dst, size_t n, hipStream_t stream);

@@ -22,7 +22,7 @@ __global__ void rope_table_kernel(float* cos_t, float* sin_t, int max_seq, int d
 }
 
 // one workgroup per row; token from RowParam (or ids_dev when given)
-__global__ void embed_kernel(int H, int fmt, const void* table, const uint16_t* sc, const uint16_t* bi,
+__global__ void embed_kernel(int H, int fmt, const void* table, const void* scp, const uint16_t* bi,
                              const RowParam* rp, const int32_t* ids_dev, int vocab, float* h, float* rs,
                              float eps, int* err_flag, float* sq) {
   __shared__ float red[32];
@@ -32,6 +32,7 @@ __global__ void embed_kernel(int H, int fmt, const void* table, const uint16_t* 
     if (threadIdx.x == 0 && err_flag) atomicOr(err_flag, 1);
     tok = 0;
   }
+  const uint16_t* sc = (const uint16_t*)scp;
   float ss = 0.f;
   for (int k = threadIdx.x; k < H; k += blockDim.x) {
     float v;
@@ -41,6 +42,8 @@ __global__ void embed_kernel(int H, int fmt, const void* table, const uint16_t* 
       v = bf16_to_f32(((const uint16_t*)table)[(size_t)tok * H + k]);
     } else if (fmt == W_I8) {  // int8 per output row: w = s * q
       v = bf16_to_f32(sc[tok]) * (float)((const int8_t*)table)[(size_t)tok * H + k];
+    } else if (fmt == W_Q8) {  // int8 in blocks of 32 with an fp32 scale each
+      v = ((const float*)scp)[(size_t)tok * (H / 32) + k / 32] * (float)((const int8_t*)table)[(size_t)tok * H + k];
     } else {  // MLX 4-bit: w = s * c + b, group 64 along the row
       const uint32_t word = ((const uint32_t*)table)[(size_t)tok * (H / 8) + k / 8];
       const float c = (float)((word >> (4 * (k & 7))) & 0xF);
@@ -364,6 +367,12 @@ __global__ void i8_to_f16_kernel(const int8_t* q, const uint16_t* sc, int rows, 
     dst[i] = (_Float16)(bf16_to_f32(sc[i / K]) * (float)q[i]);
 }
 
+__global__ void q8_to_f16_kernel(const int8_t* q, const float* sf, int rows, int K, _Float16* dst) {
+  const size_t n = (size_t)rows * K;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = (_Float16)(sf[i / 32] * (float)q[i]);  // K % 32 == 0: block i / 32 of the flat array
+}
+
 __global__ void q4_to_f16_kernel(const uint32_t* codes, const uint16_t* sc, const uint16_t* bi, int rows, int K,
                                  _Float16* dst) {
   const size_t n = (size_t)rows * K;
@@ -390,7 +399,7 @@ hipError_t launch_rope_table(float* cos_t, float* sin_t, int max_seq, int d, dou
   return hipGetLastError();
 }
 
-hipError_t launch_embed(int M, int H, int fmt, const void* table, const uint16_t* sc, const uint16_t* bi,
+hipError_t launch_embed(int M, int H, int fmt, const void* table, const void* sc, const uint16_t* bi,
                         const RowParam* rp, const int32_t* ids_dev, int vocab, float* h, float* rs, float eps,
                         int* err_flag, hipStream_t stream, float* sq) {
   launch(embed_kernel, dim3(M), dim3(256), 0, stream, H, fmt, table, sc, bi, rp, ids_dev, vocab, h, rs,
@@ -469,6 +478,11 @@ hipError_t launch_f32_to_f16(const float* src, _Float16* dst, size_t n, hipStrea
 hipError_t launch_i8_to_f16(const int8_t* q, const uint16_t* sc, int rows, int K, _Float16* dst,
                             hipStream_t stream) {
   launch(i8_to_f16_kernel, dim3(grid_for((size_t)rows * K, 256)), dim3(256), 0, stream, q, sc, rows, K, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_q8_to_f16(const int8_t* q, const float* sf, int rows, int K, _Float16* dst, hipStream_t stream) {
+  launch(q8_to_f16_kernel, dim3(grid_for((size_t)rows * K, 256)), dim3(256), 0, stream, q, sf, rows, K, dst);
   return hipGetLastError();
 }
 

@@ -40,6 +40,7 @@ struct LinearW {
   const void* w = nullptr;        // bf16 / f32 data or q4 codes
   const uint16_t* sc = nullptr;   // q4
   const uint16_t* bi = nullptr;   // q4
+  const float* sf = nullptr;      // q8 block scales [rows][cols/32]
   int rows = 0, cols = 0;
   // decode copy in fragment order (prep buffer): bf16 or q4 codes, q4 (s, b)
   const void* wt = nullptr;
@@ -215,7 +216,7 @@ ScratchLayout scratch_layout(const dpk_config& c) {
 
 // bytes of the fragment-order decode copy of one [rows][cols] linear layer
 size_t tiled_bytes(const dpk_config& c, size_t rows, size_t cols) {
-  if (c.weight_format == DPK_FMT_I8) return 0;  // decoded straight from the row-major codes
+  if (c.weight_format == DPK_FMT_I8 || c.weight_format == DPK_FMT_Q8) return 0;  // decoded from the row-major codes
   if (c.weight_format == DPK_FMT_BF16) return up(rows * cols * 2);
   return up(rows * cols / 2) + up(rows * (cols / 64) * 4);  // codes + (s, b) pairs
 }
@@ -289,12 +290,18 @@ struct ProfScope {
 };
 
 double wbytes_per_elem(int fmt) {
-  return fmt == DPK_FMT_F32 ? 4.0 : fmt == DPK_FMT_BF16 ? 2.0 : fmt == DPK_FMT_I8 ? 1.0 : 0.5 + 4.0 / 64.0;
+  return fmt == DPK_FMT_F32 ? 4.0 : fmt == DPK_FMT_BF16 ? 2.0 : fmt == DPK_FMT_I8 ? 1.0 :
+         fmt == DPK_FMT_Q8 ? 1.0 + 4.0 / 32.0 : 0.5 + 4.0 / 64.0;
 }
 
-// Kernel weight format of the model's linear layers (bf16 / q4 / i8 models).
+// Kernel weight format of the model's linear layers (bf16 / q4 / i8 / q8 models).
 int wfmt(const dpk_model* md) {
-  return md->fmt == DPK_FMT_Q4G64 ? W_Q4 : md->fmt == DPK_FMT_I8 ? W_I8 : W_BF16;
+  return md->fmt == DPK_FMT_Q4G64 ? W_Q4 : md->fmt == DPK_FMT_I8 ? W_I8 : md->fmt == DPK_FMT_Q8 ? W_Q8 : W_BF16;
+}
+
+// Scales the embedding gather takes: fp32 block scales (q8) or bf16 ones.
+const void* embed_scales(const dpk_model* md) {
+  return md->fmt == DPK_FMT_Q8 ? (const void*)md->embed.sf : (const void*)md->embed.sc;
 }
 
 dpk_status check_ready(const dpk_model* md) {
@@ -346,6 +353,7 @@ dpk_status skinny(dpk_model* md, int cls, int M, const float* x, int ldx, const 
     a.w[i] = s.w;
     a.sc[i] = s.sc;
     a.bi[i] = s.bi;
+    a.sf[i] = s.sf;
     if (i < nseg) n += s.rows;
     a.seg_end[i] = n;
     a.seg_rows[i] = s.rows;
@@ -629,7 +637,7 @@ dpk_status forward_decode(dpk_model* md, int M, int max_ctx, const int32_t* ids_
   const int H = c.hidden, Qd = c.n_heads * c.head_dim;
   {
     ProfScope ps(md, st, K_EMBED, (double)M * H * 6, 0);
-    HIP_TRY(launch_embed(M, H, wfmt(md), md->embed.w, md->embed.sc, md->embed.bi,
+    HIP_TRY(launch_embed(M, H, wfmt(md), md->embed.w, embed_scales(md), md->embed.bi,
                          md->rows_dev, ids_dev, c.vocab, md->h, nullptr, c.rms_eps, md->err_flag, st, md->sq));
   }
   int sq_nb = 1;
@@ -835,6 +843,7 @@ dpk_status head(dpk_model* md, int rows, const float* x, const float* rs, const 
     h.w[i] = hw.w;
     h.sc[i] = hw.sc;
     h.bi[i] = hw.bi;
+    h.sf[i] = hw.sf;
     h.seg_end[i] = hw.rows;
     h.seg_rows[i] = hw.rows;
   }
@@ -874,7 +883,7 @@ dpk_status forward_skinny(dpk_model* md, int M, int max_ctx, const int32_t* ids_
   const int H = c.hidden;
   {
     ProfScope ps(md, st, K_EMBED, (double)M * H * 6, 0);
-    HIP_TRY(launch_embed(M, H, wfmt(md), md->embed.w, md->embed.sc, md->embed.bi,
+    HIP_TRY(launch_embed(M, H, wfmt(md), md->embed.w, embed_scales(md), md->embed.bi,
                          md->rows_dev, ids_dev, c.vocab, md->h, md->rs, c.rms_eps, md->err_flag, st));
   }
   dpk_status s;
@@ -920,7 +929,7 @@ dpk_status forward_gemm(dpk_model* md, int M, int start, int seq, bool want_head
   dpk_status s2;
   {
     ProfScope ps(md, st, K_EMBED, (double)M * H * 6, 0);
-    HIP_TRY(launch_embed(M, H, wfmt(md), md->embed.w, md->embed.sc, md->embed.bi,
+    HIP_TRY(launch_embed(M, H, wfmt(md), md->embed.w, embed_scales(md), md->embed.bi,
                          md->rows_dev, nullptr, c.vocab, md->h, nullptr, c.rms_eps, md->err_flag, st));
   }
   const double norm_bytes = (double)M * H * 6;
@@ -1062,10 +1071,10 @@ dpk_status dpk_create(const dpk_config* cfg, dpk_model** out) {
   if (c.n_heads / c.n_kv_heads > 8) return fail(DPK_EINVAL, "at most 8 query heads per KV head");
   if (c.hidden % 256 || c.intermediate % 256 || (c.n_heads * c.head_dim) % 256)
     return fail(DPK_EINVAL, "hidden, intermediate and n_heads*head_dim must be multiples of 256");
-  if (c.weight_format < 0 || c.weight_format > 3) return fail(DPK_EINVAL, "unknown weight_format");
-  if (c.weight_format != DPK_FMT_F32 && c.head_dim != 128) return fail(DPK_EINVAL, "bf16/q4/i8 need head_dim 128");
-  if (c.weight_format != DPK_FMT_F32 && !c.qk_norm) return fail(DPK_EINVAL, "bf16/q4/i8 path needs qk_norm");
-  if (c.weight_format != DPK_FMT_F32 && c.vocab % 64) return fail(DPK_EINVAL, "bf16/q4/i8 need vocab % 64 == 0");
+  if (c.weight_format < 0 || c.weight_format > 4) return fail(DPK_EINVAL, "unknown weight_format");
+  if (c.weight_format != DPK_FMT_F32 && c.head_dim != 128) return fail(DPK_EINVAL, "bf16/q4/i8/q8 need head_dim 128");
+  if (c.weight_format != DPK_FMT_F32 && !c.qk_norm) return fail(DPK_EINVAL, "bf16/q4/i8/q8 path needs qk_norm");
+  if (c.weight_format != DPK_FMT_F32 && c.vocab % 64) return fail(DPK_EINVAL, "bf16/q4/i8/q8 need vocab % 64 == 0");
   if (c.max_batch < 1 || c.max_seq < 1 || c.max_rows < SKINNY_MAX)
     return fail(DPK_EINVAL, "max_batch, max_seq >= 1 and max_rows >= 16 required");
   if (!(c.rms_eps >= 0.0f) || !(c.rope_theta > 0.0)) return fail(DPK_EINVAL, "bad eps / theta");
@@ -1194,6 +1203,9 @@ dpk_status dpk_load_weights(dpk_model* md, const dpk_tensor* t, int32_t n, void*
     if (fmt == DPK_FMT_I8) {
       want[name + ".q"] = {DPK_DT_I8, rows, cols, &lw->w, false};
       want[name + ".scales"] = {DPK_DT_BF16, rows, 1, (const void**)&lw->sc, false};
+    } else if (fmt == DPK_FMT_Q8) {
+      want[name + ".q"] = {DPK_DT_I8, rows, cols, &lw->w, false};
+      want[name + ".scales"] = {DPK_DT_F32, rows, cols / 32, (const void**)&lw->sf, false};
     } else if (fmt == DPK_FMT_Q4G64) {
       want[name + ".codes"] = {DPK_DT_U32, rows, cols / 8, &lw->w, false};
       want[name + ".scales"] = {DPK_DT_BF16, rows, cols / 64, (const void**)&lw->sc, false};
@@ -1248,6 +1260,7 @@ dpk_status dpk_load_weights(dpk_model* md, const dpk_tensor* t, int32_t n, void*
     auto conv = [&](const LinearW& w, _Float16* dst) -> hipError_t {
       if (fmt == DPK_FMT_BF16) return launch_bf16_to_f16((const uint16_t*)w.w, dst, (size_t)w.rows * w.cols, st);
       if (fmt == DPK_FMT_I8) return launch_i8_to_f16((const int8_t*)w.w, w.sc, w.rows, w.cols, dst, st);
+      if (fmt == DPK_FMT_Q8) return launch_q8_to_f16((const int8_t*)w.w, w.sf, w.rows, w.cols, dst, st);
       return launch_q4_to_f16((const uint32_t*)w.w, w.sc, w.bi, w.rows, w.cols, dst, st);
     };
     for (int l = 0; l < c.n_layers; ++l) {
@@ -1272,7 +1285,7 @@ dpk_status dpk_load_weights(dpk_model* md, const dpk_tensor* t, int32_t n, void*
     }
     // fragment-order decode copies
     auto tile = [&](LinearW& w) -> hipError_t {
-      if (fmt == DPK_FMT_I8) return hipSuccess;  // no fragment-order copy
+      if (fmt == DPK_FMT_I8 || fmt == DPK_FMT_Q8) return hipSuccess;  // no fragment-order copy
       w.wt = p;
       if (fmt == DPK_FMT_BF16) {
         p += up((size_t)w.rows * w.cols * 2);

@@ -18,6 +18,10 @@
 //
 // int8 weights with one scale per output row (w = s * q) become the exact
 // bf16 value q in registers; the row scale multiplies the accumulated sum.
+// int8 weights in blocks of 32 with an fp32 scale per block (oxinfer docs,
+// "Build and run": the q8 format) take the same registers; one MFMA k-step
+// is one block, so each block's sum is scaled as it is added:
+//   acc += s_b * sum_{k in b} q x.
 //
 // Grid: x = row blocks, y = K splits.  The workgroup that finishes a row block
 // last sums the K-split partials in a fixed order (deterministic) and runs the
@@ -38,6 +42,7 @@ struct SkinnyLds {
   // offsets in bytes inside dynamic LDS
   int xs_hi, xs_lo, xsum, qsc, qbi, fin, misc;
   int xstride;  // elements per activation row in LDS (kchunk + 8)
+  int sstride;  // q8: floats per block of the transposed scale table (rows + 4)
   int total;
 };
 
@@ -50,7 +55,11 @@ __host__ __device__ inline SkinnyLds skinny_lds_layout(int M, int kchunk, int ro
   off = (off + 15) & ~15;
   int ng = kchunk / 64;
   L.xsum = off; off += (fmt == W_Q4 ? M * ng * 4 : 0);
-  L.qsc = off; off += (fmt == W_Q4 ? rows * ng * 4 : fmt == W_I8 ? rows * 4 : 0);  // fp32 s
+  // q8: scales [kchunk/32][rows + 4], so that a lane's four rows are one
+  // 16-byte read and the staging writes spread over the banks
+  L.sstride = rows + 4;
+  L.qsc = off;  // fp32 s
+  off += (fmt == W_Q4 ? rows * ng * 4 : fmt == W_I8 ? rows * 4 : fmt == W_Q8 ? (kchunk / 32) * L.sstride * 4 : 0);
   L.qbi = off; off += (fmt == W_Q4 ? rows * ng * 4 : 0);  // fp32 b - 128 s
   off = (off + 15) & ~15;
   L.fin = off; off += M * rows * 4;
@@ -164,6 +173,15 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(SkinnyArgs a) {
       qsc[i] = bf16_to_f32(a.sc[seg][srow]);
     }
   }
+  if (FMT == W_Q8) {  // the block scales of this K chunk, transposed
+    const int nbk = kchunk / 32;
+    for (int i = tid; i < rows * nbk; i += THREADS) {
+      const int lr = i / nbk, b = i % nbk;
+      int seg, srow;
+      map_row(a, block, lr, seg, srow);
+      qsc[b * L.sstride + lr] = a.sf[seg][(size_t)srow * (a.K / 32) + k0 / 32 + b];
+    }
+  }
   __syncthreads();
 
   // ---- main loop: each wave owns T row tiles of 16 rows
@@ -181,7 +199,7 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(SkinnyArgs a) {
     map_row(a, block, (wave * T + t) * 16 + r16, seg, srow);
     if (FMT == W_Q4)
       wrow[t] = (const unsigned char*)a.w[seg] + (size_t)srow * (a.K / 2) + k0 / 2;
-    else if (FMT == W_I8)
+    else if (FMT == W_I8 || FMT == W_Q8)
       wrow[t] = (const unsigned char*)a.w[seg] + (size_t)srow * a.K + k0;
     else
       wrow[t] = (const unsigned char*)a.w[seg] + (size_t)srow * a.K * 2 + (size_t)k0 * 2;
@@ -210,44 +228,82 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(SkinnyArgs a) {
         }
       }
     }
-  } else if (FMT == W_I8) {
-    for (int kk = 0; kk < kchunk; kk += KSTEP) {
-      u32x2 wq[T][8];
+  } else if (FMT == W_I8 || FMT == W_Q8) {
+    // Activation column r16 of the MFMA B operand: rows past M read row 0
+    // (their outputs are never stored), so the reads need no branch.
+    const int xrow = col_on ? r16 : 0;
+    // Two register buffers: the weights of the next 256 k are loaded while
+    // this 256 k is multiplied.
+    u32x2 wqa[T][8], wqb[T][8];
+    auto load = [&](u32x2 (&wq)[T][8], int kk) {
 #pragma unroll
       for (int t = 0; t < T; ++t)
 #pragma unroll
         for (int s = 0; s < 8; ++s)
           wq[t][s] = __builtin_nontemporal_load((const u32x2*)(wrow[t] + kk + 32 * s + 8 * j4));
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the multiplies
+    };
+    auto mul = [&](const u32x2 (&wq)[T][8], int kk) {
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        u32x4 bh = {0u, 0u, 0u, 0u}, bl = {0u, 0u, 0u, 0u};
-        if (col_on) {
-          bh = *(const u32x4*)(xs_hi + r16 * L.xstride + kk + 32 * s + 8 * j4);
-          bl = *(const u32x4*)(xs_lo + r16 * L.xstride + kk + 32 * s + 8 * j4);
-        }
+        const u32x4 bh = *(const u32x4*)(xs_hi + xrow * L.xstride + kk + 32 * s + 8 * j4);
+        const u32x4 bl = *(const u32x4*)(xs_lo + xrow * L.xstride + kk + 32 * s + 8 * j4);
+        f32x4 ag[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t) ag[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-          // 8 int8 codes -> 8 exact bf16 values (an integer of at most 8 bits)
-          uint32_t b16[8];
+          // 8 int8 codes -> 8 exact bf16 values: an integer of at most 8 bits
+          // is exact in fp32 and in the upper half of its fp32 bit pattern;
+          // v_perm packs the upper halves of two values into one dword.
+          uint32_t f[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const uint32_t word = e < 4 ? wq[t][s].x : wq[t][s].y;
-            const int q = (int)(int8_t)((word >> (8 * (e & 3))) & 0xFFu);
-            b16[e] = __float_as_uint((float)q) >> 16;
+            f[e] = __float_as_uint((float)(int)(int8_t)((word >> (8 * (e & 3))) & 0xFFu));
           }
-          const u32x4 av = {b16[0] | (b16[1] << 16), b16[2] | (b16[3] << 16), b16[4] | (b16[5] << 16),
-                            b16[6] | (b16[7] << 16)};
+          const u32x4 av = {__builtin_amdgcn_perm(f[1], f[0], 0x07060302u), __builtin_amdgcn_perm(f[3], f[2], 0x07060302u),
+                            __builtin_amdgcn_perm(f[5], f[4], 0x07060302u), __builtin_amdgcn_perm(f[7], f[6], 0x07060302u)};
           const bf16x8 A = __builtin_bit_cast(bf16x8, av);
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, bh), acc[t], 0, 0, 0);
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, bl), acc[t], 0, 0, 0);
+          f32x4& d = (FMT == W_Q8) ? ag[t] : acc[t];
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, bh), d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, bl), d, 0, 0, 0);
+        }
+        if (FMT == W_Q8) {  // k-step s is block (kk / 32 + s): lane holds rows 4 j4 + v
+#pragma unroll
+          for (int t = 0; t < T; ++t) {
+            const float4 sb = *(const float4*)(qsc + (kk / 32 + s) * L.sstride + (wave * T + t) * 16 + 4 * j4);
+            acc[t][0] += sb.x * ag[t][0];
+            acc[t][1] += sb.y * ag[t][1];
+            acc[t][2] += sb.z * ag[t][2];
+            acc[t][3] += sb.w * ag[t][3];
+          }
         }
       }
+    };
+    // (loads stay outside branches inside the loop, so that each wait
+    // counts only the loads of the buffer it needs)
+    load(wqa, 0);
+    int kk = 0;
+    for (; kk + 2 * KSTEP < kchunk; kk += 2 * KSTEP) {
+      load(wqb, kk + KSTEP);
+      mul(wqa, kk);
+      load(wqa, kk + 2 * KSTEP);
+      mul(wqb, kk + KSTEP);
     }
-    // row scales: lane holds rows 4 j4 + v of each tile
+    if (kk + KSTEP < kchunk) {  // two passes left (kchunk is a multiple of 256)
+      load(wqb, kk + KSTEP);
+      mul(wqa, kk);
+      mul(wqb, kk + KSTEP);
+    } else {
+      mul(wqa, kk);
+    }
+    if (FMT == W_I8) {  // row scales: lane holds rows 4 j4 + v of each tile
 #pragma unroll
-    for (int t = 0; t < T; ++t)
+      for (int t = 0; t < T; ++t)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[t][v] *= qsc[(wave * T + t) * 16 + 4 * j4 + v];
+        for (int v = 0; v < 4; ++v) acc[t][v] *= qsc[(wave * T + t) * 16 + 4 * j4 + v];
+    }
   } else {  // W_Q4: per group of 64: lane k range 64g + 16 j4 + 8 t2 + e, t2 in {0,1}
     for (int kk = 0; kk < kchunk; kk += KSTEP) {
       u32x2 wc[T][4];
@@ -497,6 +553,8 @@ hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t stream) {
   else if (a.fmt == W_Q4 && tiles == 2) launch((skinny_kernel<W_Q4, 2>), grid, block, lds, stream, a);
   else if (a.fmt == W_I8 && tiles == 1) launch((skinny_kernel<W_I8, 1>), grid, block, lds, stream, a);
   else if (a.fmt == W_I8 && tiles == 2) launch((skinny_kernel<W_I8, 2>), grid, block, lds, stream, a);
+  else if (a.fmt == W_Q8 && tiles == 1) launch((skinny_kernel<W_Q8, 1>), grid, block, lds, stream, a);
+  else if (a.fmt == W_Q8 && tiles == 2) launch((skinny_kernel<W_Q8, 2>), grid, block, lds, stream, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -59,10 +59,14 @@ typedef enum {
   DPK_FMT_F32 = 0,  /* fp32 weights, fp32 KV cache */
   DPK_FMT_BF16 = 1, /* bf16 weights, fp16 KV cache */
   DPK_FMT_Q4G64 = 2, /* MLX 4-bit affine, group 64 along the input dim; fp16 KV cache */
-  DPK_FMT_I8 = 3     /* int8 with one bf16 scale per output row (w = scale * q); fp16 KV cache.
+  DPK_FMT_I8 = 3,    /* int8 with one bf16 scale per output row (w = scale * q); fp16 KV cache.
                         Decoded by the weight-streaming GEMV (one launch per kernel), prefilled
                         through the fp16 GEMMs ("LLMs on the ANE", section "Quantized weights":
                         int8 weights) */
+  DPK_FMT_Q8 = 4     /* int8 in blocks of 32 weights along the input dim, one fp32 scale per
+                        block (w = scale[n][k / 32] * q[n][k]); fp16 KV cache.  Decoded by the
+                        weight-streaming GEMV, prefilled through the fp16 GEMMs (oxinfer docs,
+                        "Build and run": the q8 quantization of streamed weights) */
 } dpk_format;
 
 /* Element types of dpk_tensor entries. */
@@ -107,7 +111,9 @@ typedef struct {
  * (element 8w+j in bits 4j..4j+3 of word w), "<name>.scales" and
  * "<name>.biases" BF16 [out, in/64].  In DPK_FMT_I8 each linear tensor
  * (including embed_tokens / lm_head) is two entries: "<name>.q" I8 [out, in]
- * and "<name>.scales" BF16 [out, 1].
+ * and "<name>.scales" BF16 [out, 1].  In DPK_FMT_Q8 each linear tensor
+ * (including embed_tokens / lm_head) is "<name>.q" I8 [out, in] and
+ * "<name>.scales" F32 [out, in/32] (the scale of codes 32j .. 32j+31 of a row).
  */
 typedef struct {
   const char* name;
@@ -121,7 +127,7 @@ typedef struct dpk_model dpk_model;
 /* Validate the configuration and create a handle.  Supported shapes:
  * head_dim 64 or 128, n_heads a multiple of n_kv_heads with at most 8 query
  * heads per KV head, hidden and intermediate multiples of 256; bf16 / q4 /
- * i8 models need head_dim 128, per-head QK-norm and vocab % 64 == 0.  Does not touch the GPU. */
+ * i8 / q8 models need head_dim 128, per-head QK-norm and vocab % 64 == 0.  Does not touch the GPU. */
 dpk_status dpk_create(const dpk_config* cfg, dpk_model** out);
 
 /* Bytes of the three caller-provided device buffers:

@@ -40,7 +40,7 @@ def cfg_ok(dpk, **kw):
 
 
 @pytest.mark.parametrize("bad", [dict(head_dim=96), dict(n_kv_heads=3), dict(hidden=1000),
-                                 dict(max_rows=8), dict(weight_format=7), dict(vocab=0),
+                                 dict(max_rows=8), dict(weight_format=7), dict(weight_format=5), dict(vocab=0),
                                  dict(n_heads=32, n_kv_heads=2), dict(vocab=151937)])
 def test_create_rejects_bad_config(dpk, bad):
     with pytest.raises(dpk.DpkError) as e:
@@ -70,6 +70,19 @@ def test_workspace_sizes_and_call_order(dpk):
         with pytest.raises(dpk.DpkError) as e:
             dpk.load_weights(h, [], stream=0)
         assert e.value.status == dpk.DPK_ESTATE
+    finally:
+        dpk.destroy(h)
+
+
+@pytest.mark.parametrize("fmt", ["FMT_I8", "FMT_Q8"])
+def test_int8_code_formats_keep_only_the_fp16_prefill_copy(dpk, fmt):
+    """int8 codes are streamed as stored: the prep buffer holds the fp16
+    prefill operands and no fragment-order decode copy (nor a tiled head)."""
+    h = dpk.create(cfg_ok(dpk, weight_format=getattr(dpk, fmt)))
+    try:
+        kv, sc, pr = dpk.workspace_size(h)
+        per_layer = (4096 * 1024 + 1024 * 2048 + 2 * 3072 * 1024 + 1024 * 3072) * 2
+        assert pr == 2 * per_layer and kv == 2 * 2 * 2 * 8 * 640 * 128 * 2
     finally:
         dpk.destroy(h)
 

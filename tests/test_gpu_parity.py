@@ -54,6 +54,11 @@ CASES = [
     ("q06b_i8-L2-stream", synth.Q06B_I8.with_(n_layers=2), 37, 6, dict(flags=STREAM)),
     ("q8b_i8-L1-v4096-gemm", synth.Q8B_I8.with_(n_layers=1, vocab=4096), 21, 5, {}),
     ("q8b_i8-L2-v4096-chunked", synth.Q8B_I8.with_(n_layers=2, vocab=4096), 300, 4, dict(max_rows=128)),
+    # int8 in blocks of 32 with fp32 scales: the same paths, a scale per MFMA k-step
+    ("q06b_q8-L2-gemm", synth.Q06B_Q8.with_(n_layers=2), 40, 8, {}),
+    ("q06b_q8-L2-stream", synth.Q06B_Q8.with_(n_layers=2), 37, 6, dict(flags=STREAM)),
+    ("q8b_q8-L1-v4096-gemm", synth.Q8B_Q8.with_(n_layers=1, vocab=4096), 21, 5, {}),
+    ("q8b_q8-L2-v4096-chunked", synth.Q8B_Q8.with_(n_layers=2, vocab=4096), 300, 4, dict(max_rows=128)),
 ]
 
 
@@ -133,6 +138,7 @@ PATH_CASES = [
     ("q06b_q4-L1", synth.Q06B_Q4.with_(n_layers=1), True),
     ("tiny-f32", synth.TINY, False),
     ("q06b_i8-L1", synth.Q06B_I8.with_(n_layers=1), False),
+    ("q06b_q8-L1", synth.Q06B_Q8.with_(n_layers=1), False),
 ]
 
 
@@ -181,6 +187,7 @@ VERIFY_CASES = [
     ("q8b-L1-v4096-k5", synth.Q8B.with_(n_layers=1, vocab=4096), 254, 5),
     ("q8b-L1-v4096-k15", synth.Q8B.with_(n_layers=1, vocab=4096), 500, 15),
     ("q06b_i8-L2-k5", synth.Q06B_I8.with_(n_layers=2), 70, 5),
+    ("q06b_q8-L2-k5", synth.Q06B_Q8.with_(n_layers=2), 70, 5),
 ]
 
 
@@ -282,6 +289,7 @@ BATCH16_CASES = [
     # 4-bit weights: the rows go through the 4-bit skinny GEMVs
     ("q06b_q4-L2-v4096-M16", synth.Q06B_Q4.with_(n_layers=2, vocab=4096), [40 + 13 * b for b in range(16)]),
     ("q06b_i8-L2-v4096-M16", synth.Q06B_I8.with_(n_layers=2, vocab=4096), [40 + 13 * b for b in range(16)]),
+    ("q06b_q8-L2-v4096-M16", synth.Q06B_Q8.with_(n_layers=2, vocab=4096), [40 + 13 * b for b in range(16)]),
 ]
 
 
