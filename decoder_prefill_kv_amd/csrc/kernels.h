@@ -35,10 +35,10 @@ enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_
 struct SkinnyArgs {
   int M, K, N;  // activation rows (<=16), input dim, output rows
   int fmt;      // W_BF16 | W_Q4 | W_I8 | W_Q8
-  const void* w[3];         // bf16 [rows][K], q4 codes uint32 [rows][K/8] or int8 [rows][K]
+  const void* w[3];         // bf16 [rows][K], q4 codes uint32 [rows][K/8], int8: launch_tile_i8 order
   const uint16_t* sc[3];    // q4 scales bf16 [rows][K/64]; int8: row scales bf16 [rows]
   const uint16_t* bi[3];    // q4 biases bf16 [rows][K/64]
-  const float* sf[3];       // q8: block scales fp32 [rows][K/32]
+  const float* sf[3];       // q8: block scales fp32 in launch_tile_q8s order
   int seg_end[3];           // cumulative row ends of the stacked segments
   int seg_rows[3];          // rows of each segment (load clamp)
   const float* x;
@@ -128,6 +128,13 @@ hipError_t launch_tile_bf16(const uint16_t* src, uint16_t* dst, int N, int K, hi
 hipError_t launch_tile_q4(const uint32_t* codes, const uint16_t* sc, const uint16_t* bi, uint32_t* dst_c,
                           uint32_t* dst_sb, int N, int K, hipStream_t stream);
 hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t stream);
+// fragment-order copy of int8 codes [N][K] for the int8 skinny GEMV: per 16-row
+// tile and 256 columns, 4 KB in which lane l of a wave finds its 16 bytes of
+// MFMA k-steps 2p and 2p+1 at p * 1024 + l * 16 (N % 16 == 0, K % 256 == 0)
+hipError_t launch_tile_i8(const int8_t* src, int8_t* dst, int N, int K, hipStream_t stream);
+// fragment-order copy of q8 block scales [N][K/32]: per 16-row tile and 256
+// columns, 512 bytes holding row r's 8 scales at r * 32
+hipError_t launch_tile_q8s(const float* src, float* dst, int N, int K, hipStream_t stream);
 
 // ---- decode attention (split-K over the context, merged in-kernel)
 struct AttnDecodeArgs {

@@ -367,6 +367,32 @@ __global__ void i8_to_f16_kernel(const int8_t* q, const uint16_t* sc, int rows, 
     dst[i] = (_Float16)(bf16_to_f32(sc[i / K]) * (float)q[i]);
 }
 
+// dst[((rt * (K / 256) + kt) * 4 + p) * 1024 + l * 16 + 8 h + e] =
+//   src[16 rt + l % 16][256 kt + 32 (2 p + h) + 8 (l / 16) + e]
+__global__ void tile_i8_kernel(const int8_t* src, int8_t* dst, int N, int K) {
+  const size_t n8 = (size_t)N * K / 8;  // 8-byte pieces
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n8; i += (size_t)gridDim.x * blockDim.x) {
+    const int h = (int)(i & 1), l = (int)((i >> 1) & 63);
+    const size_t q = i >> 7;  // (rt, kt, p)
+    const int p = (int)(q & 3);
+    const size_t tk = q >> 2;
+    const size_t kt = tk % (K / 256), rt = tk / (K / 256);
+    const size_t row = 16 * rt + (l & 15);
+    const size_t col = 256 * kt + 32 * (2 * p + h) + 8 * (l >> 4);
+    *(uint2*)(dst + i * 8) = *(const uint2*)(src + row * K + col);
+  }
+}
+
+// dst[((rt * (K / 256) + kt) * 16 + r) * 8 + s] = src[16 rt + r][8 kt + s]
+__global__ void tile_q8s_kernel(const float* src, float* dst, int N, int K) {
+  const size_t n = (size_t)N * (K / 32);
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    const int s = (int)(i & 7), r = (int)((i >> 3) & 15);
+    const size_t tk = i >> 7, kt = tk % (K / 256), rt = tk / (K / 256);
+    dst[i] = src[(16 * rt + r) * (size_t)(K / 32) + 8 * kt + s];
+  }
+}
+
 __global__ void q8_to_f16_kernel(const int8_t* q, const float* sf, int rows, int K, _Float16* dst) {
   const size_t n = (size_t)rows * K;
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
@@ -478,6 +504,18 @@ hipError_t launch_f32_to_f16(const float* src, _Float16* dst, size_t n, hipStrea
 hipError_t launch_i8_to_f16(const int8_t* q, const uint16_t* sc, int rows, int K, _Float16* dst,
                             hipStream_t stream) {
   launch(i8_to_f16_kernel, dim3(grid_for((size_t)rows * K, 256)), dim3(256), 0, stream, q, sc, rows, K, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_i8(const int8_t* src, int8_t* dst, int N, int K, hipStream_t stream) {
+  if (N % 16 || K % 256) return hipErrorInvalidValue;
+  launch(tile_i8_kernel, dim3(grid_for((size_t)N * K / 8, 256)), dim3(256), 0, stream, src, dst, N, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_q8s(const float* src, float* dst, int N, int K, hipStream_t stream) {
+  if (N % 16 || K % 256) return hipErrorInvalidValue;
+  launch(tile_q8s_kernel, dim3(grid_for((size_t)N * (K / 32), 256)), dim3(256), 0, stream, src, dst, N, K);
   return hipGetLastError();
 }
 

@@ -44,7 +44,7 @@ struct LinearW {
   int rows = 0, cols = 0;
   // decode copy in fragment order (prep buffer): bf16 or q4 codes, q4 (s, b)
   const void* wt = nullptr;
-  const void* sbt = nullptr;
+  const void* sbt = nullptr;       // q4: tiled (s, b); q8: tiled block scales
 };
 
 struct LayerW {
@@ -216,7 +216,8 @@ ScratchLayout scratch_layout(const dpk_config& c) {
 
 // bytes of the fragment-order decode copy of one [rows][cols] linear layer
 size_t tiled_bytes(const dpk_config& c, size_t rows, size_t cols) {
-  if (c.weight_format == DPK_FMT_I8 || c.weight_format == DPK_FMT_Q8) return 0;  // decoded from the row-major codes
+  if (c.weight_format == DPK_FMT_I8) return up(rows * cols);  // int8 codes
+  if (c.weight_format == DPK_FMT_Q8) return up(rows * cols) + up(rows * (cols / 32) * 4);  // codes + block scales
   if (c.weight_format == DPK_FMT_BF16) return up(rows * cols * 2);
   return up(rows * cols / 2) + up(rows * (cols / 64) * 4);  // codes + (s, b) pairs
 }
@@ -324,16 +325,23 @@ dpk_status upload_rows(dpk_model* md, const RowParam* rows, int n, hipStream_t s
   return DPK_OK;
 }
 
+#ifndef SKINNY_I8_WG_TARGET
+#define SKINNY_I8_WG_TARGET 256
+#endif
 // Smallest K split that fits the activation chunk in 64 KB of LDS, grown until
-// the launch has ~1024 workgroups (4 per compute unit).
+// the launch has ~1024 workgroups (4 per compute unit).  The int8-code GEMV
+// stops at ~256: its workgroups pay a longer prologue (two passes over x),
+// and fewer, longer ones measured faster (8B shapes, 256 / 512 / 1024 / 2048 /
+// 4096 workgroups: gate/up 21.8 / 21.8 / 23.0 / 25.5 / 37.2 us).
 int choose_ksplit(int K, int nblocks, int M, int rows, int fmt) {
+  const long target = (fmt == W_I8 || fmt == W_Q8) ? SKINNY_I8_WG_TARGET : 1024;
   int best = 0;
   for (int ks = 1; ks <= KSPLIT_MAX; ks *= 2) {
     if (K % (ks * 256) != 0) break;
     const int kchunk = K / ks;
     if (skinny_lds_bytes(M, kchunk, rows, fmt) > 64 * 1024) continue;
     best = ks;
-    if ((long)nblocks * ks >= 1024) break;
+    if ((long)nblocks * ks >= target) break;
   }
   return best;
 }
@@ -350,10 +358,10 @@ dpk_status skinny(dpk_model* md, int cls, int M, const float* x, int ldx, const 
   int n = 0;
   for (int i = 0; i < 3; ++i) {
     const LinearW& s = segs[i < nseg ? i : nseg - 1];
-    a.w[i] = s.w;
+    a.w[i] = (a.fmt == W_I8 || a.fmt == W_Q8) ? s.wt : s.w;
     a.sc[i] = s.sc;
     a.bi[i] = s.bi;
-    a.sf[i] = s.sf;
+    a.sf[i] = (const float*)s.sbt;
     if (i < nseg) n += s.rows;
     a.seg_end[i] = n;
     a.seg_rows[i] = s.rows;
@@ -840,10 +848,10 @@ dpk_status head(dpk_model* md, int rows, const float* x, const float* rs, const 
   h.K = H;
   h.fmt = wfmt(md);
   for (int i = 0; i < 3; ++i) {
-    h.w[i] = hw.w;
+    h.w[i] = (h.fmt == W_I8 || h.fmt == W_Q8) ? hw.wt : hw.w;
     h.sc[i] = hw.sc;
     h.bi[i] = hw.bi;
-    h.sf[i] = hw.sf;
+    h.sf[i] = (const float*)hw.sbt;
     h.seg_end[i] = hw.rows;
     h.seg_rows[i] = hw.rows;
   }
@@ -1285,8 +1293,15 @@ dpk_status dpk_load_weights(dpk_model* md, const dpk_tensor* t, int32_t n, void*
     }
     // fragment-order decode copies
     auto tile = [&](LinearW& w) -> hipError_t {
-      if (fmt == DPK_FMT_I8 || fmt == DPK_FMT_Q8) return hipSuccess;  // no fragment-order copy
       w.wt = p;
+      if (fmt == DPK_FMT_I8 || fmt == DPK_FMT_Q8) {  // codes (+ q8 block scales); i8 row scales are read as given
+        p += up((size_t)w.rows * w.cols);
+        const hipError_t e = launch_tile_i8((const int8_t*)w.w, (int8_t*)w.wt, w.rows, w.cols, st);
+        if (e != hipSuccess || fmt == DPK_FMT_I8) return e;
+        w.sbt = p;
+        p += up((size_t)w.rows * (w.cols / 32) * 4);
+        return launch_tile_q8s(w.sf, (float*)w.sbt, w.rows, w.cols, st);
+      }
       if (fmt == DPK_FMT_BF16) {
         p += up((size_t)w.rows * w.cols * 2);
         return launch_tile_bf16((const uint16_t*)w.w, (uint16_t*)w.wt, w.rows, w.cols, st);

@@ -16,12 +16,16 @@
 // (bit pattern 0x4300 | c) and accumulated per group:
 //   sum_k w x = s * sum (128+c) x + (b - 128 s) * sum x.
 //
-// int8 weights with one scale per output row (w = s * q) become the exact
-// bf16 value q in registers; the row scale multiplies the accumulated sum.
-// int8 weights in blocks of 32 with an fp32 scale per block (oxinfer docs,
-// "Build and run": the q8 format) take the same registers; one MFMA k-step
-// is one block, so each block's sum is scaled as it is added:
-//   acc += s_b * sum_{k in b} q x.
+// int8 codes (one scale per output row, w = s * q; or blocks of 32 with an
+// fp32 scale per block, oxinfer docs, "Build and run": the q8 format) go into
+// fp16 MFMAs without a conversion: the byte q + 128 under the high byte 0x64
+// is the fp16 integer 1152 + q.  The activations are fp16 hi + lo of x' times
+// a power of two per row (its largest magnitude in the chunk brought to
+// [2^14, 2^15), undone on the sums), and sum (1152 + q) x - 1152 sum x gives
+// sum q x.  The row scale multiplies the finished sum; a block scale
+// multiplies each MFMA k-step's sum (one k-step is one block):
+//   acc += s_b * (sum_{k in b} (1152 + q) x + sum_{k in b} (-1152) x),
+// the second sum from two more MFMAs with a constant operand.
 //
 // Grid: x = row blocks, y = K splits.  The workgroup that finishes a row block
 // last sums the K-split partials in a fixed order (deterministic) and runs the
@@ -40,9 +44,8 @@ constexpr int KSTEP = 256;  // k per main-loop iteration (8 MFMA k-steps)
 
 struct SkinnyLds {
   // offsets in bytes inside dynamic LDS
-  int xs_hi, xs_lo, xsum, qsc, qbi, fin, misc;
+  int xs_hi, xs_lo, xsum, xsc, qsc, qbi, fin, misc;
   int xstride;  // elements per activation row in LDS (kchunk + 8)
-  int sstride;  // q8: floats per block of the transposed scale table (rows + 4)
   int total;
 };
 
@@ -54,12 +57,13 @@ __host__ __device__ inline SkinnyLds skinny_lds_layout(int M, int kchunk, int ro
   L.xs_lo = off; off += M * L.xstride * 2;
   off = (off + 15) & ~15;
   int ng = kchunk / 64;
-  L.xsum = off; off += (fmt == W_Q4 ? M * ng * 4 : 0);
-  // q8: scales [kchunk/32][rows + 4], so that a lane's four rows are one
-  // 16-byte read and the staging writes spread over the banks
-  L.sstride = rows + 4;
+  const bool i8f = fmt == W_I8 || fmt == W_Q8;
+  // q4: [M][kchunk/64] sums of x'; int8 codes: [kchunk/32][16] sums of the
+  // scaled x' per block of 32, then 16 row maxima and 16 row unscales
+  L.xsum = off; off += (fmt == W_Q4 ? M * ng * 4 : i8f ? (kchunk / 32) * 16 * 4 : 0);
+  L.xsc = off; off += (i8f ? 32 * 4 : 0);
   L.qsc = off;  // fp32 s
-  off += (fmt == W_Q4 ? rows * ng * 4 : fmt == W_I8 ? rows * 4 : fmt == W_Q8 ? (kchunk / 32) * L.sstride * 4 : 0);
+  off += (fmt == W_Q4 ? rows * ng * 4 : fmt == W_I8 ? rows * 4 : 0);
   L.qbi = off; off += (fmt == W_Q4 ? rows * ng * 4 : 0);  // fp32 b - 128 s
   off = (off + 15) & ~15;
   L.fin = off; off += M * rows * 4;
@@ -107,13 +111,55 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(SkinnyArgs a) {
   const int wave = tid >> 6, lane = tid & 63;
   const int ng = kchunk / 64;
 
-  // ---- prologue: x'[m][k0 .. k0+kchunk) -> bf16 hi/lo in LDS
-  for (int i = tid; i < M * (kchunk / 8); i += THREADS) {
-    const int m = i / (kchunk / 8);
-    const int k8 = (i % (kchunk / 8)) * 8;
+  constexpr bool I8F = FMT == W_I8 || FMT == W_Q8;
+  const int nbk = kchunk / 32;  // int8 formats: blocks of 32 columns in the chunk
+  const int r16 = lane & 15;    // A row / B column / D column
+  const int j4 = lane >> 4;     // k group of 8
+  const bool col_on = r16 < M;
+  // Activation column r16 of the MFMA B operand: rows past M read row 0
+  // (their outputs are never stored), so the reads need no branch.
+  const int xrow = col_on ? r16 : 0;
+
+  const unsigned char* wrow[T];
+  const unsigned char* srow_sf[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    int seg, srow;
+    map_row(a, block, (wave * T + t) * 16 + r16, seg, srow);
+    if (FMT == W_Q4)
+      wrow[t] = (const unsigned char*)a.w[seg] + (size_t)srow * (a.K / 2) + k0 / 2;
+    else if (I8F) {  // fragment-order codes: this tile's 4 KB per 256 columns, this lane's 16 bytes
+      wrow[t] = (const unsigned char*)a.w[seg] + ((size_t)(srow >> 4) * (a.K / 256) + k0 / 256) * 4096 + lane * 16;
+      if (FMT == W_Q8)  // fragment-order block scales: 512 bytes per tile and 256 columns, row r16's 8 at r16 * 32
+        srow_sf[t] = (const unsigned char*)a.sf[seg] + ((size_t)(srow >> 4) * (a.K / 256) + k0 / 256) * 512 + r16 * 32;
+    } else
+      wrow[t] = (const unsigned char*)a.w[seg] + (size_t)srow * a.K * 2 + (size_t)k0 * 2;
+  }
+  // int8 codes: two register buffers of 256 columns (a wave reads 1 KB in
+  // one 16-byte-per-lane load); the first is requested before the prologue,
+  // the next while the current one is multiplied
+  // (q8: with the 8 block scales of the lane's weight row)
+  u32x4 wqa[T][4], wqb[T][4], sqa[T][2], sqb[T][2];
+  auto load = [&](u32x4 (&wq)[T][4], u32x4 (&sq)[T][2], int kk) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) wq[t][p] = __builtin_nontemporal_load((const u32x4*)(wrow[t] + kk * 16 + p * 1024));
+      if constexpr (FMT == W_Q8) {
+        sq[t][0] = __builtin_nontemporal_load((const u32x4*)(srow_sf[t] + kk * 2));
+        sq[t][1] = __builtin_nontemporal_load((const u32x4*)(srow_sf[t] + kk * 2 + 16));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of what follows
+  };
+  if constexpr (I8F) load(wqa, sqa, 0);
+
+  // x'[m][k8 .. k8 + 8) of this chunk (x * rs * g in fp32)
+  auto xprime = [&](int m, int k8, float (&v)[8]) {
     const float* xp = a.x + (size_t)m * a.ldx + k0 + k8;
-    float4 v0 = *(const float4*)xp, v1 = *(const float4*)(xp + 4);
-    float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    const float4 v0 = *(const float4*)xp, v1 = *(const float4*)(xp + 4);
+    v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+    v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
     const float r = a.rs ? a.rs[m] : 1.0f;
     if (a.gain) {
       const uint4 g = *(const uint4*)(a.gain + k0 + k8);
@@ -127,30 +173,93 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(SkinnyArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] *= r;
     }
-    // q4 codes pair nibble p with nibble p+4 inside a packed dword, so the
-    // activation slots are permuted the same way: (0,4,1,5,2,6,3,7)
-    uint32_t hi[8], lo[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int src = (FMT == W_Q4) ? ((e & 1) ? (e >> 1) + 4 : (e >> 1)) : e;
-      split_bf16(v[src], hi[e], lo[e]);
+  };
+
+  if constexpr (I8F) {
+    // ---- prologue (int8 codes): x' scaled by a power of two per row so that
+    // its largest magnitude in the chunk lies in [2^14, 2^15), then split
+    // into fp16 hi + lo; per block of 32 columns the sum of hi + lo, which
+    // the code offset needs (the codes enter the MFMA as fp16 1152 + q).
+    unsigned* rmax = (unsigned*)(lds + L.xsc);
+    float* xunscale = (float*)(lds + L.xsc) + 16;
+    if (tid < 16) {
+      rmax[tid] = 0u;
+      xunscale[tid] = 1.0f;
     }
-    uint4 H, Lo;
-    H.x = hi[0] | (hi[1] << 16); H.y = hi[2] | (hi[3] << 16);
-    H.z = hi[4] | (hi[5] << 16); H.w = hi[6] | (hi[7] << 16);
-    Lo.x = lo[0] | (lo[1] << 16); Lo.y = lo[2] | (lo[3] << 16);
-    Lo.z = lo[4] | (lo[5] << 16); Lo.w = lo[6] | (lo[7] << 16);
-    *(uint4*)(xs_hi + m * L.xstride + k8) = H;
-    *(uint4*)(xs_lo + m * L.xstride + k8) = Lo;
-    if (FMT == W_Q4) {
-      float s = 0.f;
+    __syncthreads();
+    for (int i = tid; i < M * (kchunk / 8); i += THREADS) {
+      const int m = i / (kchunk / 8), k8 = (i % (kchunk / 8)) * 8;
+      float v[8];
+      xprime(m, k8, v);
+      float mx = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s += v[e];
-      // 8 consecutive threads cover one group of 64: reduce over them
-      s += __shfl_xor(s, 1, 64);
-      s += __shfl_xor(s, 2, 64);
-      s += __shfl_xor(s, 4, 64);
-      if ((k8 & 63) == 0) xsum[m * ng + k8 / 64] = s;
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(v[e]));
+      if (mx != mx) mx = __uint_as_float(0x7fc00000u);  // a NaN wins the maximum
+      atomicMax(&rmax[m], __float_as_uint(mx));  // non-negative floats order as their bits
+    }
+    __syncthreads();
+    for (int i = tid; i < M * (kchunk / 8); i += THREADS) {
+      const int m = i / (kchunk / 8), k8 = (i % (kchunk / 8)) * 8;
+      float v[8];
+      xprime(m, k8, v);
+      const float mx = __uint_as_float(rmax[m]);
+      int ex = 0;
+      if (mx > 0.f && mx <= 3.0e38f) frexpf(mx, &ex);  // mx = f 2^ex, f in [0.5, 1)
+      const int sh = min(max(15 - ex, -100), 100);
+      const float sc = ldexpf(1.0f, sh);
+      uint32_t hl[8], ll[8];
+      float bs = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = v[e] * sc;
+        const _Float16 h = (_Float16)x;
+        const _Float16 l = (_Float16)(x - (float)h);
+        bs += (float)h + (float)l;
+        hl[e] = __builtin_bit_cast(uint16_t, h);
+        ll[e] = __builtin_bit_cast(uint16_t, l);
+      }
+      *(uint4*)(xs_hi + m * L.xstride + k8) =
+          uint4{hl[0] | (hl[1] << 16), hl[2] | (hl[3] << 16), hl[4] | (hl[5] << 16), hl[6] | (hl[7] << 16)};
+      *(uint4*)(xs_lo + m * L.xstride + k8) =
+          uint4{ll[0] | (ll[1] << 16), ll[2] | (ll[3] << 16), ll[4] | (ll[5] << 16), ll[6] | (ll[7] << 16)};
+      // 4 consecutive threads cover one block of 32 (kchunk / 8 is a multiple of 32)
+      bs += __shfl_xor(bs, 1, 64);
+      bs += __shfl_xor(bs, 2, 64);
+      if ((k8 & 31) == 0) xsum[(k8 / 32) * 16 + m] = bs;
+      if (k8 == 0) xunscale[m] = ldexpf(1.0f, -sh);
+    }
+  } else {
+    // ---- prologue: x'[m][k0 .. k0+kchunk) -> bf16 hi/lo in LDS
+    for (int i = tid; i < M * (kchunk / 8); i += THREADS) {
+      const int m = i / (kchunk / 8);
+      const int k8 = (i % (kchunk / 8)) * 8;
+      float v[8];
+      xprime(m, k8, v);
+      // q4 codes pair nibble p with nibble p+4 inside a packed dword, so the
+      // activation slots are permuted the same way: (0,4,1,5,2,6,3,7)
+      uint32_t hi[8], lo[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int src = (FMT == W_Q4) ? ((e & 1) ? (e >> 1) + 4 : (e >> 1)) : e;
+        split_bf16(v[src], hi[e], lo[e]);
+      }
+      uint4 H, Lo;
+      H.x = hi[0] | (hi[1] << 16); H.y = hi[2] | (hi[3] << 16);
+      H.z = hi[4] | (hi[5] << 16); H.w = hi[6] | (hi[7] << 16);
+      Lo.x = lo[0] | (lo[1] << 16); Lo.y = lo[2] | (lo[3] << 16);
+      Lo.z = lo[4] | (lo[5] << 16); Lo.w = lo[6] | (lo[7] << 16);
+      *(uint4*)(xs_hi + m * L.xstride + k8) = H;
+      *(uint4*)(xs_lo + m * L.xstride + k8) = Lo;
+      if (FMT == W_Q4) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s += v[e];
+        // 8 consecutive threads cover one group of 64: reduce over them
+        s += __shfl_xor(s, 1, 64);
+        s += __shfl_xor(s, 2, 64);
+        s += __shfl_xor(s, 4, 64);
+        if ((k8 & 63) == 0) xsum[m * ng + k8 / 64] = s;
+      }
     }
   }
   if (FMT == W_Q4) {
@@ -173,37 +282,12 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(SkinnyArgs a) {
       qsc[i] = bf16_to_f32(a.sc[seg][srow]);
     }
   }
-  if (FMT == W_Q8) {  // the block scales of this K chunk, transposed
-    const int nbk = kchunk / 32;
-    for (int i = tid; i < rows * nbk; i += THREADS) {
-      const int lr = i / nbk, b = i % nbk;
-      int seg, srow;
-      map_row(a, block, lr, seg, srow);
-      qsc[b * L.sstride + lr] = a.sf[seg][(size_t)srow * (a.K / 32) + k0 / 32 + b];
-    }
-  }
   __syncthreads();
 
   // ---- main loop: each wave owns T row tiles of 16 rows
-  const int r16 = lane & 15;  // A row / B column / D column
-  const int j4 = lane >> 4;   // k group of 8
   f32x4 acc[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const bool col_on = r16 < M;
-
-  const unsigned char* wrow[T];
-#pragma unroll
-  for (int t = 0; t < T; ++t) {
-    int seg, srow;
-    map_row(a, block, (wave * T + t) * 16 + r16, seg, srow);
-    if (FMT == W_Q4)
-      wrow[t] = (const unsigned char*)a.w[seg] + (size_t)srow * (a.K / 2) + k0 / 2;
-    else if (FMT == W_I8 || FMT == W_Q8)
-      wrow[t] = (const unsigned char*)a.w[seg] + (size_t)srow * a.K + k0;
-    else
-      wrow[t] = (const unsigned char*)a.w[seg] + (size_t)srow * a.K * 2 + (size_t)k0 * 2;
-  }
 
   if (FMT == W_BF16) {
     for (int kk = 0; kk < kchunk; kk += KSTEP) {
@@ -228,81 +312,92 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(SkinnyArgs a) {
         }
       }
     }
-  } else if (FMT == W_I8 || FMT == W_Q8) {
-    // Activation column r16 of the MFMA B operand: rows past M read row 0
-    // (their outputs are never stored), so the reads need no branch.
-    const int xrow = col_on ? r16 : 0;
-    // Two register buffers: the weights of the next 256 k are loaded while
-    // this 256 k is multiplied.
-    u32x2 wqa[T][8], wqb[T][8];
-    auto load = [&](u32x2 (&wq)[T][8], int kk) {
-#pragma unroll
-      for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-          wq[t][s] = __builtin_nontemporal_load((const u32x2*)(wrow[t] + kk + 32 * s + 8 * j4));
-      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the multiplies
-    };
-    auto mul = [&](const u32x2 (&wq)[T][8], int kk) {
+  } else if (I8F) {
+    // Codes as fp16 without a conversion: byte q ^ 0x80 = q + 128 becomes the
+    // low byte of an fp16 whose high byte is 0x64, i.e. 1024 + q + 128 (fp16
+    // integers are exact up to 2048), so the MFMA sums (1152 + q) x and
+    // 1152 * sum x is subtracted.  One v_perm places two codes.  The
+    // activations are the A operand and the codes the B operand, so a lane's
+    // four results share one weight row (r16 of the tile) and one scale:
+    // D[m = 4 j4 + v][n = r16].
+    auto mul = [&](const u32x4 (&wq)[T][4], const u32x4 (&sq)[T][2], int kk) {
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const u32x4 bh = *(const u32x4*)(xs_hi + xrow * L.xstride + kk + 32 * s + 8 * j4);
-        const u32x4 bl = *(const u32x4*)(xs_lo + xrow * L.xstride + kk + 32 * s + 8 * j4);
-        f32x4 ag[T];
-#pragma unroll
-        for (int t = 0; t < T; ++t) ag[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const f16x8 Xh = __builtin_bit_cast(f16x8, *(const u32x4*)(xs_hi + xrow * L.xstride + kk + 32 * s + 8 * j4));
+        const f16x8 Xl = __builtin_bit_cast(f16x8, *(const u32x4*)(xs_lo + xrow * L.xstride + kk + 32 * s + 8 * j4));
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-          // 8 int8 codes -> 8 exact bf16 values: an integer of at most 8 bits
-          // is exact in fp32 and in the upper half of its fp32 bit pattern;
-          // v_perm packs the upper halves of two values into one dword.
-          uint32_t f[8];
+          // this lane's codes of k-step s: weight row r16, columns 32 s + 8 j4 .. + 7
+          const uint32_t u0 = ((s & 1) ? wq[t][s >> 1].z : wq[t][s >> 1].x) ^ 0x80808080u;
+          const uint32_t u1 = ((s & 1) ? wq[t][s >> 1].w : wq[t][s >> 1].y) ^ 0x80808080u;
+          const u32x4 bv = {__builtin_amdgcn_perm(0x64646464u, u0, 0x04010400u),
+                            __builtin_amdgcn_perm(0x64646464u, u0, 0x04030402u),
+                            __builtin_amdgcn_perm(0x64646464u, u1, 0x04010400u),
+                            __builtin_amdgcn_perm(0x64646464u, u1, 0x04030402u)};
+          const f16x8 B = __builtin_bit_cast(f16x8, bv);
+          if constexpr (FMT == W_Q8) {
+            // the block's sum of (1152 + q) x, then - 1152 x summed by two more
+            // MFMAs with a constant operand, so the offset leaves inside the
+            // block sum; then the block scale of the lane's weight row
+            const f16x8 C = __builtin_bit_cast(f16x8, u32x4{0xE480E480u, 0xE480E480u, 0xE480E480u, 0xE480E480u});
+            f32x4 ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(Xh, B, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(Xl, B, ag, 0, 0, 0);
+            ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(Xh, C, ag, 0, 0, 0);
+            ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(Xl, C, ag, 0, 0, 0);
+            const float sb = __uint_as_float(sq[t][s >> 2][s & 3]);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t word = e < 4 ? wq[t][s].x : wq[t][s].y;
-            f[e] = __float_as_uint((float)(int)(int8_t)((word >> (8 * (e & 3))) & 0xFFu));
-          }
-          const u32x4 av = {__builtin_amdgcn_perm(f[1], f[0], 0x07060302u), __builtin_amdgcn_perm(f[3], f[2], 0x07060302u),
-                            __builtin_amdgcn_perm(f[5], f[4], 0x07060302u), __builtin_amdgcn_perm(f[7], f[6], 0x07060302u)};
-          const bf16x8 A = __builtin_bit_cast(bf16x8, av);
-          f32x4& d = (FMT == W_Q8) ? ag[t] : acc[t];
-          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, bh), d, 0, 0, 0);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, bl), d, 0, 0, 0);
-        }
-        if (FMT == W_Q8) {  // k-step s is block (kk / 32 + s): lane holds rows 4 j4 + v
-#pragma unroll
-          for (int t = 0; t < T; ++t) {
-            const float4 sb = *(const float4*)(qsc + (kk / 32 + s) * L.sstride + (wave * T + t) * 16 + 4 * j4);
-            acc[t][0] += sb.x * ag[t][0];
-            acc[t][1] += sb.y * ag[t][1];
-            acc[t][2] += sb.z * ag[t][2];
-            acc[t][3] += sb.w * ag[t][3];
+            for (int v = 0; v < 4; ++v) acc[t][v] += sb * ag[v];
+          } else {
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Xh, B, acc[t], 0, 0, 0);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Xl, B, acc[t], 0, 0, 0);
           }
         }
       }
     };
     // (loads stay outside branches inside the loop, so that each wait
     // counts only the loads of the buffer it needs)
-    load(wqa, 0);
     int kk = 0;
     for (; kk + 2 * KSTEP < kchunk; kk += 2 * KSTEP) {
-      load(wqb, kk + KSTEP);
-      mul(wqa, kk);
-      load(wqa, kk + 2 * KSTEP);
-      mul(wqb, kk + KSTEP);
+      load(wqb, sqb, kk + KSTEP);
+      mul(wqa, sqa, kk);
+      load(wqa, sqa, kk + 2 * KSTEP);
+      mul(wqb, sqb, kk + KSTEP);
     }
     if (kk + KSTEP < kchunk) {  // two passes left (kchunk is a multiple of 256)
-      load(wqb, kk + KSTEP);
-      mul(wqa, kk);
-      mul(wqb, kk + KSTEP);
+      load(wqb, sqb, kk + KSTEP);
+      mul(wqa, sqa, kk);
+      mul(wqb, sqb, kk + KSTEP);
     } else {
-      mul(wqa, kk);
+      mul(wqa, sqa, kk);
     }
-    if (FMT == W_I8) {  // row scales: lane holds rows 4 j4 + v of each tile
+    // activation row m = 4 j4 + v: undo its power of two; i8: the code offset
+    // and the weight row's scale
+    const float* xunscale = (const float*)(lds + L.xsc) + 16;
+    float sx[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (FMT == W_I8) {
+      // sum x of rows 4 j4 + v over the chunk: the 16 lanes of a j4 group
+      // take every 16th block, then a butterfly over them (fixed order)
+      for (int b = r16; b < nbk; b += 16) {
+        const float4 xs4 = *(const float4*)(xsum + b * 16 + 4 * j4);
+        sx[0] += xs4.x; sx[1] += xs4.y; sx[2] += xs4.z; sx[3] += xs4.w;
+      }
 #pragma unroll
-      for (int t = 0; t < T; ++t)
+      for (int v = 0; v < 4; ++v)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[t][v] *= qsc[(wave * T + t) * 16 + 4 * j4 + v];
+        for (int o = 1; o < 16; o <<= 1) sx[v] += __shfl_xor(sx[v], o, 64);
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = 4 * j4 + v;
+      const float us = xunscale[m];
+      if constexpr (FMT == W_I8) {
+        const float c = 1152.0f * sx[v];
+#pragma unroll
+        for (int t = 0; t < T; ++t) acc[t][v] = (acc[t][v] - c) * qsc[(wave * T + t) * 16 + r16] * us;
+      } else {
+#pragma unroll
+        for (int t = 0; t < T; ++t) acc[t][v] *= us;
+      }
     }
   } else {  // W_Q4: per group of 64: lane k range 64g + 16 j4 + 8 t2 + e, t2 in {0,1}
     for (int kk = 0; kk < kchunk; kk += KSTEP) {
@@ -352,14 +447,17 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(SkinnyArgs a) {
     }
   }
 
-  // ---- D[n][m]: lane holds rows 4*j4+v of each tile, column m = r16
+  // ---- D[n][m]: lane holds rows 4*j4+v of each tile, column m = r16 (int8
+  // codes: activation rows m = 4*j4+v, weight row r16 of each tile)
   const int nb = gridDim.x;
+  auto res_m = [&](int v) { return I8F ? 4 * j4 + v : r16; };
+  auto res_n = [&](int t, int v) { return (wave * T + t) * 16 + (I8F ? r16 : 4 * j4 + v); };
   if (a.ksplit == 1) {
 #pragma unroll
     for (int t = 0; t < T; ++t)
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        if (col_on) fin[r16 * rows + (wave * T + t) * 16 + 4 * j4 + v] = acc[t][v];
+        if (res_m(v) < M) fin[res_m(v) * rows + res_n(t, v)] = acc[t][v];
     __syncthreads();
   } else {
     // partials [ks][M][nb*rows]
@@ -368,9 +466,8 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(SkinnyArgs a) {
     for (int t = 0; t < T; ++t)
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        if (col_on)
-          coh_store(a.part + ((size_t)ks * M + r16) * ldp + (size_t)block * rows + (wave * T + t) * 16 + 4 * j4 + v,
-                    acc[t][v]);
+        if (res_m(v) < M)
+          coh_store(a.part + ((size_t)ks * M + res_m(v)) * ldp + (size_t)block * rows + res_n(t, v), acc[t][v]);
     if (!last_block_arrive(a.counters + 1 + block, a.ksplit, misc)) return;
     for (int i = tid; i < M * rows; i += THREADS) {
       const int m = i / rows, lr = i % rows;

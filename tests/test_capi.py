@@ -75,14 +75,19 @@ def test_workspace_sizes_and_call_order(dpk):
 
 
 @pytest.mark.parametrize("fmt", ["FMT_I8", "FMT_Q8"])
-def test_int8_code_formats_keep_only_the_fp16_prefill_copy(dpk, fmt):
-    """int8 codes are streamed as stored: the prep buffer holds the fp16
-    prefill operands and no fragment-order decode copy (nor a tiled head)."""
+def test_int8_code_formats_prep_holds_fp16_operands_and_fragment_order_codes(dpk, fmt):
+    """The prep buffer of an int8-code model holds the fp16 prefill operands
+    (2 bytes per weight) and a fragment-order copy of the codes (1 byte per
+    weight, the tied head included; q8 also its block scales); per-row i8
+    scales are read where the caller keeps them."""
     h = dpk.create(cfg_ok(dpk, weight_format=getattr(dpk, fmt)))
     try:
         kv, sc, pr = dpk.workspace_size(h)
-        per_layer = (4096 * 1024 + 1024 * 2048 + 2 * 3072 * 1024 + 1024 * 3072) * 2
-        assert pr == 2 * per_layer and kv == 2 * 2 * 2 * 8 * 640 * 128 * 2
+        per_layer = 4096 * 1024 + 1024 * 2048 + 2 * 3072 * 1024 + 1024 * 3072  # weights
+        # q8: and a fragment-order copy of its fp32 block scales (4 bytes per 32 weights)
+        per_w = 1 + (4 / 32 if fmt == "FMT_Q8" else 0)
+        assert pr == 2 * (per_layer * 2 + per_layer * per_w) + 151936 * 1024 * per_w
+        assert kv == 2 * 2 * 2 * 8 * 640 * 128 * 2
     finally:
         dpk.destroy(h)
 
