@@ -140,6 +140,19 @@ def dequant_q8(q: np.ndarray, scales_f32: np.ndarray, dtype=torch.float64) -> to
     return (torch.from_numpy(q.astype(np.float64)) * torch.repeat_interleave(s, 32, dim=1)).to(dtype)
 
 
+def dequant_q40(packed: np.ndarray, d_f16: np.ndarray, dtype=torch.float64) -> torch.Tensor:
+    """w = d * (c - 8) for GGUF-style 4-bit blocks of 32 weights (oxinfer docs
+    page, "Build and run", the q4 quantization flag: blocks of 32, 4-bit codes,
+    an fp16 scale).  Byte j of a block's 16 holds code j in its low nibble and
+    code j + 16 in its high nibble.  In float64."""
+    rows, half = packed.shape
+    b = packed.reshape(rows, half // 16, 16).astype(np.int64)
+    codes = np.concatenate([b & 0xF, b >> 4], axis=2)  # [rows, blocks, 32]
+    d = np.ascontiguousarray(d_f16, dtype=np.float16).astype(np.float64)
+    w = d[..., None] * (codes.astype(np.float64) - 8.0)
+    return torch.from_numpy(w.reshape(rows, half * 2)).to(dtype)
+
+
 class OracleModel:
     """The decoder with weights taken exactly as stored (bf16 widen exactly)."""
 
@@ -160,6 +173,8 @@ class OracleModel:
             return dequant_i8(self.w[name + ".q"], self.w[name + ".scales"], self.dtype)
         if cfg.weight_format == "q8" and name + ".q" in self.w:
             return dequant_q8(self.w[name + ".q"], self.w[name + ".scales"], self.dtype)
+        if cfg.weight_format == "q4_0" and name + ".q" in self.w:
+            return dequant_q40(self.w[name + ".q"], self.w[name + ".scales"], self.dtype)
         a = self.w[name]
         if a.dtype == np.uint16:
             return torch.from_numpy(synth.bf16_bits_to_f32(a)).to(self.dtype)
@@ -193,6 +208,9 @@ class OracleModel:
         if cfg.weight_format == "q8":
             sel = np.array(ids, dtype=np.int64)
             return dequant_q8(self.w["embed_tokens.q"][sel], self.w["embed_tokens.scales"][sel], self.dtype)
+        if cfg.weight_format == "q4_0":
+            sel = np.array(ids, dtype=np.int64)
+            return dequant_q40(self.w["embed_tokens.q"][sel], self.w["embed_tokens.scales"][sel], self.dtype)
         E = self.w["embed_tokens"]
         rows = E[np.array(ids, dtype=np.int64)]
         if rows.dtype == np.uint16:

@@ -26,6 +26,14 @@ checkpoint.  Storage formats:
   float32 scales): scale = max |w| / 127 over the block (float32),
   q = round(w / scale) clipped to [-127, 127].  A tensor ``name`` becomes
   ``name.q`` int8 ``[out, in]`` and ``name.scales`` float32 ``[out, in/32]``.
+* ``q4_0`` - GGUF-style 4-bit blocks of 32 along the input dimension with one
+  fp16 scale d each (oxinfer docs page, "Build and run", the q4 quantization
+  flag; its pre-quantized files hold two codes per byte plus fp16 scales):
+  w = d * (c - 8), c in 0..15; d = fp16(max |w| / 7) over the block,
+  c = clip(round(w / d), -8, 7) + 8.  Within a block's 16 bytes, byte j holds
+  element j in its low nibble and element j + 16 in its high nibble.  A tensor
+  ``name`` becomes ``name.q`` uint8 ``[out, in/2]`` and ``name.scales``
+  float16 ``[out, in/32]``.
 """
 from __future__ import annotations
 
@@ -138,7 +146,7 @@ class ModelConfig:
     head_dim: int
     intermediate: int
     vocab: int
-    weight_format: str     # "f32" | "bf16" | "q4" | "i8" | "q8"
+    weight_format: str     # "f32" | "bf16" | "q4" | "i8" | "q8" | "q4_0"
     qk_norm: bool
     tied: bool
     rms_eps: float = 1e-6
@@ -205,9 +213,12 @@ Q8B_I8 = Q8B.with_(family="q8b_i8", weight_format="i8")
 # Q8 block variants (32 weights per float32 scale)
 Q06B_Q8 = Q06B.with_(family="q06b_q8", weight_format="q8")
 Q8B_Q8 = Q8B.with_(family="q8b_q8", weight_format="q8")
+# GGUF-style Q4_0 variants (32 weights per fp16 scale, codes 0..15 around 8)
+Q06B_Q40 = Q06B.with_(family="q06b_q40", weight_format="q4_0")
+Q8B_Q40 = Q8B.with_(family="q8b_q40", weight_format="q4_0")
 
 CONFIGS = {"tiny": TINY, "q06b": Q06B, "q06b_q4": Q06B_Q4, "q8b": Q8B, "q06b_i8": Q06B_I8, "q8b_i8": Q8B_I8,
-           "q06b_q8": Q06B_Q8, "q8b_q8": Q8B_Q8}
+           "q06b_q8": Q06B_Q8, "q8b_q8": Q8B_Q8, "q06b_q40": Q06B_Q40, "q8b_q40": Q8B_Q40}
 
 
 def _gain(cfg: ModelConfig, seed: int, name: str, shape) -> np.ndarray:
@@ -249,6 +260,14 @@ def _linear(cfg: ModelConfig, seed: int, name: str, shape) -> Dict[str, np.ndarr
         sc = (np.abs(w).max(axis=2) / np.float32(127.0)).astype(np.float32)
         q = np.clip(np.rint(w / np.where(sc > 0, sc, np.float32(1.0))[..., None]), -127, 127)
         return {name + ".q": q.astype(np.int8).reshape(rows, cols), name + ".scales": sc}
+    if cfg.weight_format == "q4_0":
+        assert cols % 32 == 0
+        w = normal_f32(key_of(seed, tag), shape, cfg.init_std).reshape(rows, cols // 32, 32)
+        d = (np.abs(w).max(axis=2) / np.float32(7.0)).astype(np.float16)
+        d32 = d.astype(np.float32)
+        c = np.clip(np.rint(w / np.where(d32 > 0, d32, np.float32(1.0))[..., None]), -8, 7).astype(np.int32) + 8
+        packed = (c[..., :16] | (c[..., 16:] << 4)).astype(np.uint8)  # byte j: elements j and j + 16
+        return {name + ".q": packed.reshape(rows, cols // 2), name + ".scales": d}
     if cfg.weight_format == "q4":
         assert cols % 64 == 0
         return {

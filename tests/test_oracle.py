@@ -577,6 +577,57 @@ def test_q8_model_equals_f64_weight_model_with_the_dequantized_weights(synth_bui
     assert float((a - b).abs().max()) == 0.0
 
 
+def test_q40_dequant_hand_values_nibble_order_and_requant(synth_built):
+    """Byte j of a block holds code j (low nibble) and code j + 16 (high
+    nibble); w = d * (c - 8) with the block's fp16 d (a swapped nibble order,
+    a missing -8 or a scale indexed by column fails)."""
+    from oracle.decoder import dequant_q40
+    packed = np.full((1, 32), 0x88, dtype=np.uint8)  # two blocks, every code 8 -> w = 0
+    packed[0, 0] = 0x3F   # block 0: element 0 code 15, element 16 code 3
+    packed[0, 15] = 0x08  # element 15 code 8, element 31 code 0
+    packed[0, 16] = 0xA1  # block 1: element 32 code 1, element 48 code 10
+    d = np.array([[0.5, 0.25]], dtype=np.float16)
+    W = dequant_q40(packed, d)
+    assert W[0, 0] == 3.5 and W[0, 16] == -2.5 and W[0, 15] == 0.0 and W[0, 31] == -4.0
+    assert W[0, 32] == -1.75 and W[0, 48] == 0.5
+    assert int((W != 0).sum()) == 5
+    cfg = synth.Q06B.with_(family="q40pin", weight_format="q4_0", n_layers=1, vocab=512)
+    w = synth.make_weights(cfg, 3)
+    for name in ("layers.0.mlp.down_proj", "embed_tokens"):
+        q, d = w[name + ".q"], w[name + ".scales"]
+        assert q.dtype == np.uint8 and d.dtype == np.float16 and d.shape == (q.shape[0], q.shape[1] // 16)
+        s = torch.repeat_interleave(torch.from_numpy(d.astype(np.float64)), 32, dim=1)
+        Wd = dequant_q40(q, d)
+        ref = synth.normal_f32(synth.key_of(3, cfg.family + "/" + name), Wd.shape, cfg.init_std)
+        # requantisation returns the codes, and each weight is within half a
+        # step of its draw (a block's largest magnitude maps to code 1 or 15)
+        b = q.reshape(q.shape[0], -1, 16).astype(np.int64)
+        codes = np.concatenate([b & 0xF, b >> 4], axis=2).reshape(Wd.shape)
+        assert torch.equal(torch.round(Wd / s).to(torch.int64) + 8, torch.from_numpy(codes))
+        assert float((Wd - torch.from_numpy(ref).double()).abs().div(s).max()) <= 0.5 + 1e-3
+        assert set(np.unique(np.abs(codes.reshape(codes.shape[0], -1, 32) - 8).max(axis=2))) <= {7, 8}
+
+
+def test_q40_model_equals_f64_weight_model_with_the_dequantized_weights(synth_built):
+    from oracle.decoder import dequant_q40
+    cfg = synth.Q06B.with_(family="q40pin2", weight_format="q4_0", n_layers=2, vocab=512, hidden=256, n_heads=4,
+                           n_kv_heads=2, intermediate=512)
+    w = synth.make_weights(cfg, 1)
+    f = {}
+    for k, v in w.items():
+        if k.endswith(".q"):
+            f[k[:-2]] = dequant_q40(v, w[k[:-2] + ".scales"]).numpy()
+        elif not k.endswith(".scales"):
+            f[k] = synth.bf16_bits_to_f32(v)
+    cf = cfg.with_(weight_format="f32")
+    prompt = synth.prompt_ids(cfg, 12, 0)
+    ma = oracle.OracleModel(cfg, w)
+    a = ma.forward_block(ma.new_cache(12), prompt, 0)
+    mb = oracle.OracleModel(cf, f)
+    b = mb.forward_block(mb.new_cache(12), prompt, 0)
+    assert float((a - b).abs().max()) == 0.0
+
+
 def test_i8_model_equals_f32_model_with_the_dequantized_weights(synth_built):
     """scale (bf16, 8 significant bits) times q (int8) is exact in fp32, so
     the int8 model must equal an fp32-format model holding those products."""
