@@ -71,6 +71,8 @@ WORKLOADS = {
                                    "(incl. head): prefill 2048, then 64 greedy decode steps"),
     "q8b_q8": ("q8b_q8", 2048, 64, "Qwen3-8B-shaped decoder, int8 linears in blocks of 32 with an fp32 scale each "
                                    "(incl. head): prefill 2048, then 64 greedy decode steps"),
+    "q8b_q40": ("q8b_q40", 2048, 64, "Qwen3-8B-shaped decoder, GGUF-style Q4_0 linears (blocks of 32 four-bit codes, "
+                                     "fp16 scale; incl. head): prefill 2048, then 64 greedy decode steps"),
 }
 
 
@@ -330,7 +332,8 @@ def run_workload(dpk, name, steps, warmup, seed, flags, decode_steps=None, profi
     H, L, d = cfg.hidden, cfg.n_layers, cfg.head_dim
     n_lin = cfg.n_linear_params()
     head_params = cfg.vocab * H
-    wbytes = {"bf16": 2.0, "f32": 4.0, "q4": 0.5 + 4.0 / 64, "i8": 1.0 + 2.0 / H, "q8": 1.0 + 4.0 / 32}[cfg.weight_format]
+    wbytes = {"bf16": 2.0, "f32": 4.0, "q4": 0.5 + 4.0 / 64, "i8": 1.0 + 2.0 / H, "q8": 1.0 + 4.0 / 32,
+              "q4_0": 0.5 + 2.0 / 32}[cfg.weight_format]
     kv_elt = 4 if cfg.weight_format == "f32" else 2
     kv_per_pos = 2 * L * cfg.n_kv_heads * d * kv_elt
     mean_ctx = P + (N + 1) / 2.0

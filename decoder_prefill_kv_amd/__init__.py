@@ -21,9 +21,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "_dpk.so")
 
 DPK_OK, DPK_EINVAL, DPK_ERANGE, DPK_ESTATE, DPK_ENOMEM, DPK_EHIP = 0, -1, -2, -3, -4, -5
-FMT_F32, FMT_BF16, FMT_Q4G64, FMT_I8, FMT_Q8 = 0, 1, 2, 3, 4
+FMT_F32, FMT_BF16, FMT_Q4G64, FMT_I8, FMT_Q8, FMT_Q40 = 0, 1, 2, 3, 4, 5
 FLAG_PREFILL_STREAM = 1
-DT_F32, DT_BF16, DT_U32, DT_I8 = 0, 1, 2, 3
+DT_F32, DT_BF16, DT_U32, DT_I8, DT_U8, DT_F16 = 0, 1, 2, 3, 4, 5
 SYMBOLS = ["dpk_create", "dpk_workspace_size", "dpk_bind_workspace", "dpk_load_weights", "dpk_prefill",
            "dpk_prefill_at", "dpk_decode_step", "dpk_verify", "dpk_seq_length", "dpk_check_device_errors",
            "dpk_test_set_barrier_abort", "dpk_profile_begin", "dpk_profile_end", "dpk_spec_generate", "dpk_sample",
@@ -291,7 +291,7 @@ def destroy(model: int):
 
 
 # ------------------------------------------------------------------ convenience
-_FMT = {"f32": FMT_F32, "bf16": FMT_BF16, "q4": FMT_Q4G64, "i8": FMT_I8, "q8": FMT_Q8}
+_FMT = {"f32": FMT_F32, "bf16": FMT_BF16, "q4": FMT_Q4G64, "i8": FMT_I8, "q8": FMT_Q8, "q4_0": FMT_Q40}
 
 
 def make_config(mc, max_batch: int, max_seq: int, max_rows: int = 512, flags: int = 0) -> Config:
@@ -310,6 +310,10 @@ def _dtype_code(a: np.ndarray) -> int:
         return DT_U32
     if a.dtype == np.int8:
         return DT_I8
+    if a.dtype == np.uint8:
+        return DT_U8
+    if a.dtype == np.float16:
+        return DT_F16
     raise TypeError(a.dtype)
 
 

@@ -44,7 +44,7 @@ struct RowParam {
 };
 
 // Weight formats of the linear layers.
-enum WFmt : int { W_F32 = 0, W_BF16 = 1, W_Q4 = 2, W_I8 = 3, W_Q8 = 4 };
+enum WFmt : int { W_F32 = 0, W_BF16 = 1, W_Q4 = 2, W_I8 = 3, W_Q8 = 4, W_Q40 = 5 };
 
 DPK_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 DPK_DEV float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }

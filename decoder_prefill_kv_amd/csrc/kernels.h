@@ -135,6 +135,14 @@ hipError_t launch_tile_i8(const int8_t* src, int8_t* dst, int N, int K, hipStrea
 // fragment-order copy of q8 block scales [N][K/32]: per 16-row tile and 256
 // columns, 512 bytes holding row r's 8 scales at r * 32
 hipError_t launch_tile_q8s(const float* src, float* dst, int N, int K, hipStream_t stream);
+// the same for Q4_0 fp16 scales (widened to fp32, exact)
+hipError_t launch_tile_q40s(const uint16_t* src, float* dst, int N, int K, hipStream_t stream);
+// fragment-order copy of Q4_0 codes (GGUF blocks: byte j of a block's 16 holds
+// codes j and j + 16): per 16-row tile and 256 columns 2 KB, lane l's dword of
+// k-step s at (s / 4) * 1024 + l * 16 + (s % 4) * 4, its nibble n holding
+// element 2n (n < 4) or 2 (n - 4) + 1 of columns 32 s + 8 (l / 16) .. + 7
+hipError_t launch_tile_q40(const uint8_t* src, uint32_t* dst, int N, int K, hipStream_t stream);
+hipError_t launch_q40_to_f16(const uint8_t* q, const uint16_t* d, int rows, int K, _Float16* dst, hipStream_t stream);
 
 // ---- decode attention (split-K over the context, merged in-kernel)
 struct AttnDecodeArgs {
@@ -188,7 +196,7 @@ hipError_t launch_rope_table(float* cos_t, float* sin_t, int max_seq, int d, dou
                              hipStream_t stream);
 // h[m] = E[token_m] (fp32 / bf16 / q4 table); rs[m] = rsqrt(mean(h^2)+eps) if rs != null;
 // sq[m] = sum(h^2) if sq != null
-// sc: bf16 scales (q4 groups, i8 rows) or fp32 block scales (q8)
+// sc: bf16 scales (q4 groups, i8 rows), fp32 block scales (q8) or fp16 ones (q4_0)
 hipError_t launch_embed(int M, int H, int fmt, const void* table, const void* sc, const uint16_t* bi,
                         const RowParam* rp, const int32_t* ids_dev, int vocab, float* h, float* rs,
                         float eps, int* err_flag, hipStream_t stream, float* sq = nullptr);

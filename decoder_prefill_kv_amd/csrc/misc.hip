@@ -44,6 +44,11 @@ __global__ void embed_kernel(int H, int fmt, const void* table, const void* scp,
       v = bf16_to_f32(sc[tok]) * (float)((const int8_t*)table)[(size_t)tok * H + k];
     } else if (fmt == W_Q8) {  // int8 in blocks of 32 with an fp32 scale each
       v = ((const float*)scp)[(size_t)tok * (H / 32) + k / 32] * (float)((const int8_t*)table)[(size_t)tok * H + k];
+    } else if (fmt == W_Q40) {  // 4-bit blocks of 32 around 8, fp16 scale; byte j: codes j, j + 16
+      const int i = k & 31;
+      const uint8_t b = ((const uint8_t*)table)[(size_t)tok * (H / 2) + (k / 32) * 16 + (i & 15)];
+      const int c = i < 16 ? (b & 0xF) : (b >> 4);
+      v = (float)__builtin_bit_cast(_Float16, sc[(size_t)tok * (H / 32) + k / 32]) * (float)(c - 8);
     } else {  // MLX 4-bit: w = s * c + b, group 64 along the row
       const uint32_t word = ((const uint32_t*)table)[(size_t)tok * (H / 8) + k / 8];
       const float c = (float)((word >> (4 * (k & 7))) & 0xF);
@@ -393,6 +398,48 @@ __global__ void tile_q8s_kernel(const float* src, float* dst, int N, int K) {
   }
 }
 
+__global__ void tile_q40s_kernel(const uint16_t* src, float* dst, int N, int K) {
+  const size_t n = (size_t)N * (K / 32);
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    const int s = (int)(i & 7), r = (int)((i >> 3) & 15);
+    const size_t tk = i >> 7, kt = tk % (K / 256), rt = tk / (K / 256);
+    dst[i] = (float)__builtin_bit_cast(_Float16, src[(16 * rt + r) * (size_t)(K / 32) + 8 * kt + s]);
+  }
+}
+
+// one thread per output dword (lane l, k-step s of a tile and 256 columns)
+__global__ void tile_q40_kernel(const uint8_t* src, uint32_t* dst, int N, int K) {
+  const size_t n = (size_t)N * K / 8;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    // i = ((rt * (K / 256) + kt) * 2 + p) * 256 + l * 4 + (s % 4), s = 4 p + s % 4
+    const int sl = (int)(i & 3), l = (int)((i >> 2) & 63), p = (int)((i >> 8) & 1);
+    const size_t tk = i >> 9, kt = tk % (K / 256), rt = tk / (K / 256);
+    const int s = 4 * p + sl;
+    const size_t row = 16 * rt + (l & 15);
+    const uint8_t* blk = src + row * (size_t)(K / 2) + (8 * kt + s) * 16;  // block 8 kt + s of the row
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int ib = 8 * (l >> 4) + e;  // index inside the block
+      const uint32_t c = ib < 16 ? (blk[ib] & 0xF) : (blk[ib - 16] >> 4);
+      const int n = (e & 1) ? 4 + (e >> 1) : (e >> 1);  // nibble slot of element e
+      w |= c << (4 * n);
+    }
+    dst[i] = w;
+  }
+}
+
+__global__ void q40_to_f16_kernel(const uint8_t* q, const uint16_t* d, int rows, int K, _Float16* dst) {
+  const size_t n = (size_t)rows * K;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    const size_t b = i / 32;  // block of the flat array (K % 32 == 0)
+    const int ib = (int)(i & 31);
+    const uint8_t byte = q[b * 16 + (ib & 15)];
+    const int c = ib < 16 ? (byte & 0xF) : (byte >> 4);
+    dst[i] = (_Float16)((float)__builtin_bit_cast(_Float16, d[b]) * (float)(c - 8));
+  }
+}
+
 __global__ void q8_to_f16_kernel(const int8_t* q, const float* sf, int rows, int K, _Float16* dst) {
   const size_t n = (size_t)rows * K;
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
@@ -516,6 +563,23 @@ hipError_t launch_tile_i8(const int8_t* src, int8_t* dst, int N, int K, hipStrea
 hipError_t launch_tile_q8s(const float* src, float* dst, int N, int K, hipStream_t stream) {
   if (N % 16 || K % 256) return hipErrorInvalidValue;
   launch(tile_q8s_kernel, dim3(grid_for((size_t)N * (K / 32), 256)), dim3(256), 0, stream, src, dst, N, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_q40s(const uint16_t* src, float* dst, int N, int K, hipStream_t stream) {
+  if (N % 16 || K % 256) return hipErrorInvalidValue;
+  launch(tile_q40s_kernel, dim3(grid_for((size_t)N * (K / 32), 256)), dim3(256), 0, stream, src, dst, N, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_q40(const uint8_t* src, uint32_t* dst, int N, int K, hipStream_t stream) {
+  if (N % 16 || K % 256) return hipErrorInvalidValue;
+  launch(tile_q40_kernel, dim3(grid_for((size_t)N * K / 8, 256)), dim3(256), 0, stream, src, dst, N, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_q40_to_f16(const uint8_t* q, const uint16_t* d, int rows, int K, _Float16* dst, hipStream_t stream) {
+  launch(q40_to_f16_kernel, dim3(grid_for((size_t)rows * K, 256)), dim3(256), 0, stream, q, d, rows, K, dst);
   return hipGetLastError();
 }
 

@@ -40,7 +40,7 @@ struct LinearW {
   const void* w = nullptr;        // bf16 / f32 data or q4 codes
   const uint16_t* sc = nullptr;   // q4
   const uint16_t* bi = nullptr;   // q4
-  const float* sf = nullptr;      // q8 block scales [rows][cols/32]
+  const float* sf = nullptr;      // q8 block scales [rows][cols/32] (q4_0: fp16 bits)
   int rows = 0, cols = 0;
   // decode copy in fragment order (prep buffer): bf16 or q4 codes, q4 (s, b)
   const void* wt = nullptr;
@@ -218,6 +218,7 @@ ScratchLayout scratch_layout(const dpk_config& c) {
 size_t tiled_bytes(const dpk_config& c, size_t rows, size_t cols) {
   if (c.weight_format == DPK_FMT_I8) return up(rows * cols);  // int8 codes
   if (c.weight_format == DPK_FMT_Q8) return up(rows * cols) + up(rows * (cols / 32) * 4);  // codes + block scales
+  if (c.weight_format == DPK_FMT_Q40) return up(rows * cols / 2) + up(rows * (cols / 32) * 4);
   if (c.weight_format == DPK_FMT_BF16) return up(rows * cols * 2);
   return up(rows * cols / 2) + up(rows * (cols / 64) * 4);  // codes + (s, b) pairs
 }
@@ -292,17 +293,25 @@ struct ProfScope {
 
 double wbytes_per_elem(int fmt) {
   return fmt == DPK_FMT_F32 ? 4.0 : fmt == DPK_FMT_BF16 ? 2.0 : fmt == DPK_FMT_I8 ? 1.0 :
-         fmt == DPK_FMT_Q8 ? 1.0 + 4.0 / 32.0 : 0.5 + 4.0 / 64.0;
+         fmt == DPK_FMT_Q8 ? 1.0 + 4.0 / 32.0 : fmt == DPK_FMT_Q40 ? 0.5 + 2.0 / 32.0 : 0.5 + 4.0 / 64.0;
 }
 
-// Kernel weight format of the model's linear layers (bf16 / q4 / i8 / q8 models).
+// Kernel weight format of the model's linear layers (bf16 / q4 / i8 / q8 / q4_0 models).
 int wfmt(const dpk_model* md) {
-  return md->fmt == DPK_FMT_Q4G64 ? W_Q4 : md->fmt == DPK_FMT_I8 ? W_I8 : md->fmt == DPK_FMT_Q8 ? W_Q8 : W_BF16;
+  switch (md->fmt) {
+    case DPK_FMT_Q4G64: return W_Q4;
+    case DPK_FMT_I8: return W_I8;
+    case DPK_FMT_Q8: return W_Q8;
+    case DPK_FMT_Q40: return W_Q40;
+    default: return W_BF16;
+  }
 }
 
-// Scales the embedding gather takes: fp32 block scales (q8) or bf16 ones.
+bool int_code_fmt(int fmt) { return fmt == DPK_FMT_I8 || fmt == DPK_FMT_Q8 || fmt == DPK_FMT_Q40; }
+
+// Scales the embedding gather takes: fp32 (q8) or fp16 (q4_0) block scales, or bf16 ones.
 const void* embed_scales(const dpk_model* md) {
-  return md->fmt == DPK_FMT_Q8 ? (const void*)md->embed.sf : (const void*)md->embed.sc;
+  return (md->fmt == DPK_FMT_Q8 || md->fmt == DPK_FMT_Q40) ? (const void*)md->embed.sf : (const void*)md->embed.sc;
 }
 
 dpk_status check_ready(const dpk_model* md) {
@@ -334,7 +343,7 @@ dpk_status upload_rows(dpk_model* md, const RowParam* rows, int n, hipStream_t s
 // and fewer, longer ones measured faster (8B shapes, 256 / 512 / 1024 / 2048 /
 // 4096 workgroups: gate/up 21.8 / 21.8 / 23.0 / 25.5 / 37.2 us).
 int choose_ksplit(int K, int nblocks, int M, int rows, int fmt) {
-  const long target = (fmt == W_I8 || fmt == W_Q8) ? SKINNY_I8_WG_TARGET : 1024;
+  const long target = (fmt == W_I8 || fmt == W_Q8 || fmt == W_Q40) ? SKINNY_I8_WG_TARGET : 1024;
   int best = 0;
   for (int ks = 1; ks <= KSPLIT_MAX; ks *= 2) {
     if (K % (ks * 256) != 0) break;
@@ -358,7 +367,7 @@ dpk_status skinny(dpk_model* md, int cls, int M, const float* x, int ldx, const 
   int n = 0;
   for (int i = 0; i < 3; ++i) {
     const LinearW& s = segs[i < nseg ? i : nseg - 1];
-    a.w[i] = (a.fmt == W_I8 || a.fmt == W_Q8) ? s.wt : s.w;
+    a.w[i] = int_code_fmt(md->fmt) ? s.wt : s.w;
     a.sc[i] = s.sc;
     a.bi[i] = s.bi;
     a.sf[i] = (const float*)s.sbt;
@@ -848,7 +857,7 @@ dpk_status head(dpk_model* md, int rows, const float* x, const float* rs, const 
   h.K = H;
   h.fmt = wfmt(md);
   for (int i = 0; i < 3; ++i) {
-    h.w[i] = (h.fmt == W_I8 || h.fmt == W_Q8) ? hw.wt : hw.w;
+    h.w[i] = int_code_fmt(md->fmt) ? hw.wt : hw.w;
     h.sc[i] = hw.sc;
     h.bi[i] = hw.bi;
     h.sf[i] = (const float*)hw.sbt;
@@ -1079,10 +1088,10 @@ dpk_status dpk_create(const dpk_config* cfg, dpk_model** out) {
   if (c.n_heads / c.n_kv_heads > 8) return fail(DPK_EINVAL, "at most 8 query heads per KV head");
   if (c.hidden % 256 || c.intermediate % 256 || (c.n_heads * c.head_dim) % 256)
     return fail(DPK_EINVAL, "hidden, intermediate and n_heads*head_dim must be multiples of 256");
-  if (c.weight_format < 0 || c.weight_format > 4) return fail(DPK_EINVAL, "unknown weight_format");
-  if (c.weight_format != DPK_FMT_F32 && c.head_dim != 128) return fail(DPK_EINVAL, "bf16/q4/i8/q8 need head_dim 128");
-  if (c.weight_format != DPK_FMT_F32 && !c.qk_norm) return fail(DPK_EINVAL, "bf16/q4/i8/q8 path needs qk_norm");
-  if (c.weight_format != DPK_FMT_F32 && c.vocab % 64) return fail(DPK_EINVAL, "bf16/q4/i8/q8 need vocab % 64 == 0");
+  if (c.weight_format < 0 || c.weight_format > 5) return fail(DPK_EINVAL, "unknown weight_format");
+  if (c.weight_format != DPK_FMT_F32 && c.head_dim != 128) return fail(DPK_EINVAL, "non-f32 formats need head_dim 128");
+  if (c.weight_format != DPK_FMT_F32 && !c.qk_norm) return fail(DPK_EINVAL, "non-f32 formats need qk_norm");
+  if (c.weight_format != DPK_FMT_F32 && c.vocab % 64) return fail(DPK_EINVAL, "non-f32 formats need vocab % 64 == 0");
   if (c.max_batch < 1 || c.max_seq < 1 || c.max_rows < SKINNY_MAX)
     return fail(DPK_EINVAL, "max_batch, max_seq >= 1 and max_rows >= 16 required");
   if (!(c.rms_eps >= 0.0f) || !(c.rope_theta > 0.0)) return fail(DPK_EINVAL, "bad eps / theta");
@@ -1214,6 +1223,9 @@ dpk_status dpk_load_weights(dpk_model* md, const dpk_tensor* t, int32_t n, void*
     } else if (fmt == DPK_FMT_Q8) {
       want[name + ".q"] = {DPK_DT_I8, rows, cols, &lw->w, false};
       want[name + ".scales"] = {DPK_DT_F32, rows, cols / 32, (const void**)&lw->sf, false};
+    } else if (fmt == DPK_FMT_Q40) {
+      want[name + ".q"] = {DPK_DT_U8, rows, cols / 2, &lw->w, false};
+      want[name + ".scales"] = {DPK_DT_F16, rows, cols / 32, (const void**)&lw->sf, false};
     } else if (fmt == DPK_FMT_Q4G64) {
       want[name + ".codes"] = {DPK_DT_U32, rows, cols / 8, &lw->w, false};
       want[name + ".scales"] = {DPK_DT_BF16, rows, cols / 64, (const void**)&lw->sc, false};
@@ -1269,6 +1281,8 @@ dpk_status dpk_load_weights(dpk_model* md, const dpk_tensor* t, int32_t n, void*
       if (fmt == DPK_FMT_BF16) return launch_bf16_to_f16((const uint16_t*)w.w, dst, (size_t)w.rows * w.cols, st);
       if (fmt == DPK_FMT_I8) return launch_i8_to_f16((const int8_t*)w.w, w.sc, w.rows, w.cols, dst, st);
       if (fmt == DPK_FMT_Q8) return launch_q8_to_f16((const int8_t*)w.w, w.sf, w.rows, w.cols, dst, st);
+      if (fmt == DPK_FMT_Q40)
+        return launch_q40_to_f16((const uint8_t*)w.w, (const uint16_t*)w.sf, w.rows, w.cols, dst, st);
       return launch_q4_to_f16((const uint32_t*)w.w, w.sc, w.bi, w.rows, w.cols, dst, st);
     };
     for (int l = 0; l < c.n_layers; ++l) {
@@ -1294,6 +1308,14 @@ dpk_status dpk_load_weights(dpk_model* md, const dpk_tensor* t, int32_t n, void*
     // fragment-order decode copies
     auto tile = [&](LinearW& w) -> hipError_t {
       w.wt = p;
+      if (fmt == DPK_FMT_Q40) {  // codes + block scales (widened to fp32)
+        p += up((size_t)w.rows * w.cols / 2);
+        const hipError_t e = launch_tile_q40((const uint8_t*)w.w, (uint32_t*)w.wt, w.rows, w.cols, st);
+        if (e != hipSuccess) return e;
+        w.sbt = p;
+        p += up((size_t)w.rows * (w.cols / 32) * 4);
+        return launch_tile_q40s((const uint16_t*)w.sf, (float*)w.sbt, w.rows, w.cols, st);
+      }
       if (fmt == DPK_FMT_I8 || fmt == DPK_FMT_Q8) {  // codes (+ q8 block scales); i8 row scales are read as given
         p += up((size_t)w.rows * w.cols);
         const hipError_t e = launch_tile_i8((const int8_t*)w.w, (int8_t*)w.wt, w.rows, w.cols, st);

@@ -24,8 +24,11 @@
 // [2^14, 2^15), undone on the sums), and sum (1152 + q) x - 1152 sum x gives
 // sum q x.  The row scale multiplies the finished sum; a block scale
 // multiplies each MFMA k-step's sum (one k-step is one block):
-//   acc += s_b * (sum_{k in b} (1152 + q) x + sum_{k in b} (-1152) x),
-// the second sum from two more MFMAs with a constant operand.
+//   acc += s_b * (sum_{k in b} (1152 + q) x - 1152 sum_{k in b} x),
+// the block's MFMAs starting from the staged - 1152 sum x.  GGUF-style
+// 4-bit blocks (Q4_0: w = d (c - 8), 32 codes per fp16 d; oxinfer docs, "Build
+// and run": the q4 flag) take the same path with fp16 1024 + c (a nibble
+// under 0x640) and the offset 1032.
 //
 // Grid: x = row blocks, y = K splits.  The workgroup that finishes a row block
 // last sums the K-split partials in a fixed order (deterministic) and runs the
@@ -57,7 +60,7 @@ __host__ __device__ inline SkinnyLds skinny_lds_layout(int M, int kchunk, int ro
   L.xs_lo = off; off += M * L.xstride * 2;
   off = (off + 15) & ~15;
   int ng = kchunk / 64;
-  const bool i8f = fmt == W_I8 || fmt == W_Q8;
+  const bool i8f = fmt == W_I8 || fmt == W_Q8 || fmt == W_Q40;
   // q4: [M][kchunk/64] sums of x'; int8 codes: [kchunk/32][16] sums of the
   // scaled x' per block of 32, then 16 row maxima and 16 row unscales
   L.xsum = off; off += (fmt == W_Q4 ? M * ng * 4 : i8f ? (kchunk / 32) * 16 * 4 : 0);
@@ -111,7 +114,10 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(SkinnyArgs a) {
   const int wave = tid >> 6, lane = tid & 63;
   const int ng = kchunk / 64;
 
-  constexpr bool I8F = FMT == W_I8 || FMT == W_Q8;
+  constexpr bool I8F = FMT == W_I8 || FMT == W_Q8 || FMT == W_Q40;  // integer codes
+  constexpr bool BLK = FMT == W_Q8 || FMT == W_Q40;                   // a scale per 32 columns
+  constexpr int TB = FMT == W_Q40 ? 2048 : 4096;  // code bytes per 16-row tile and 256 columns
+  constexpr float OFF = FMT == W_Q40 ? 1032.0f : 1152.0f;  // the codes' fp16 value minus the weight's code
   const int nbk = kchunk / 32;  // int8 formats: blocks of 32 columns in the chunk
   const int r16 = lane & 15;    // A row / B column / D column
   const int j4 = lane >> 4;     // k group of 8
@@ -128,24 +134,25 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(SkinnyArgs a) {
     map_row(a, block, (wave * T + t) * 16 + r16, seg, srow);
     if (FMT == W_Q4)
       wrow[t] = (const unsigned char*)a.w[seg] + (size_t)srow * (a.K / 2) + k0 / 2;
-    else if (I8F) {  // fragment-order codes: this tile's 4 KB per 256 columns, this lane's 16 bytes
-      wrow[t] = (const unsigned char*)a.w[seg] + ((size_t)(srow >> 4) * (a.K / 256) + k0 / 256) * 4096 + lane * 16;
-      if (FMT == W_Q8)  // fragment-order block scales: 512 bytes per tile and 256 columns, row r16's 8 at r16 * 32
+    else if (I8F) {  // fragment-order codes: this tile's 4 / 2 KB per 256 columns, this lane's 16 bytes
+      wrow[t] = (const unsigned char*)a.w[seg] + ((size_t)(srow >> 4) * (a.K / 256) + k0 / 256) * TB + lane * 16;
+      if (BLK)  // fragment-order block scales: 512 bytes per tile and 256 columns, row r16's 8 at r16 * 32
         srow_sf[t] = (const unsigned char*)a.sf[seg] + ((size_t)(srow >> 4) * (a.K / 256) + k0 / 256) * 512 + r16 * 32;
     } else
       wrow[t] = (const unsigned char*)a.w[seg] + (size_t)srow * a.K * 2 + (size_t)k0 * 2;
   }
-  // int8 codes: two register buffers of 256 columns (a wave reads 1 KB in
-  // one 16-byte-per-lane load); the first is requested before the prologue,
-  // the next while the current one is multiplied
-  // (q8: with the 8 block scales of the lane's weight row)
+  // integer codes: two register buffers of 256 columns (a wave reads 1 KB in
+  // one 16-byte-per-lane load: two k-steps of int8 codes, four of 4-bit ones);
+  // the first is requested before the prologue, the next while the current
+  // one is multiplied (block formats: with the 8 scales of the lane's row)
   u32x4 wqa[T][4], wqb[T][4], sqa[T][2], sqb[T][2];
   auto load = [&](u32x4 (&wq)[T][4], u32x4 (&sq)[T][2], int kk) {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
 #pragma unroll
-      for (int p = 0; p < 4; ++p) wq[t][p] = __builtin_nontemporal_load((const u32x4*)(wrow[t] + kk * 16 + p * 1024));
-      if constexpr (FMT == W_Q8) {
+      for (int p = 0; p < TB / 1024; ++p)
+        wq[t][p] = __builtin_nontemporal_load((const u32x4*)(wrow[t] + kk * (TB / 256) + p * 1024));
+      if constexpr (BLK) {
         sq[t][0] = __builtin_nontemporal_load((const u32x4*)(srow_sf[t] + kk * 2));
         sq[t][1] = __builtin_nontemporal_load((const u32x4*)(srow_sf[t] + kk * 2 + 16));
       }
@@ -225,7 +232,8 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(SkinnyArgs a) {
       // 4 consecutive threads cover one block of 32 (kchunk / 8 is a multiple of 32)
       bs += __shfl_xor(bs, 1, 64);
       bs += __shfl_xor(bs, 2, 64);
-      if ((k8 & 31) == 0) xsum[(k8 / 32) * 16 + m] = bs;
+      // (block formats keep - o * sum, the accumulator a block's MFMAs start from)
+      if ((k8 & 31) == 0) xsum[(k8 / 32) * 16 + m] = BLK ? -OFF * bs : bs;
       if (k8 == 0) xunscale[m] = ldexpf(1.0f, -sh);
     }
   } else {
@@ -325,25 +333,35 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(SkinnyArgs a) {
       for (int s = 0; s < 8; ++s) {
         const f16x8 Xh = __builtin_bit_cast(f16x8, *(const u32x4*)(xs_hi + xrow * L.xstride + kk + 32 * s + 8 * j4));
         const f16x8 Xl = __builtin_bit_cast(f16x8, *(const u32x4*)(xs_lo + xrow * L.xstride + kk + 32 * s + 8 * j4));
+        // block formats: - o sum x of rows 4 j4 .. + 3 over block kk / 32 + s
+        const f32x4 c0 = BLK ? *(const f32x4*)(xsum + (kk / 32 + s) * 16 + 4 * j4) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < T; ++t) {
           // this lane's codes of k-step s: weight row r16, columns 32 s + 8 j4 .. + 7
-          const uint32_t u0 = ((s & 1) ? wq[t][s >> 1].z : wq[t][s >> 1].x) ^ 0x80808080u;
-          const uint32_t u1 = ((s & 1) ? wq[t][s >> 1].w : wq[t][s >> 1].y) ^ 0x80808080u;
-          const u32x4 bv = {__builtin_amdgcn_perm(0x64646464u, u0, 0x04010400u),
-                            __builtin_amdgcn_perm(0x64646464u, u0, 0x04030402u),
-                            __builtin_amdgcn_perm(0x64646464u, u1, 0x04010400u),
-                            __builtin_amdgcn_perm(0x64646464u, u1, 0x04030402u)};
+          u32x4 bv;
+          if constexpr (FMT == W_Q40) {
+            // 4-bit: one dword, nibble n holding element 2n (n < 4) or
+            // 2 (n - 4) + 1, so each shift and mask gives elements 2p, 2p + 1
+            // as fp16 1024 + c
+            const uint32_t w = wq[t][s >> 2][s & 3];
+            bv = u32x4{0x64006400u | (w & 0x000F000Fu), 0x64006400u | ((w >> 4) & 0x000F000Fu),
+                       0x64006400u | ((w >> 8) & 0x000F000Fu), 0x64006400u | ((w >> 12) & 0x000F000Fu)};
+          } else {
+            const uint32_t u0 = ((s & 1) ? wq[t][s >> 1].z : wq[t][s >> 1].x) ^ 0x80808080u;
+            const uint32_t u1 = ((s & 1) ? wq[t][s >> 1].w : wq[t][s >> 1].y) ^ 0x80808080u;
+            bv = u32x4{__builtin_amdgcn_perm(0x64646464u, u0, 0x04010400u),
+                       __builtin_amdgcn_perm(0x64646464u, u0, 0x04030402u),
+                       __builtin_amdgcn_perm(0x64646464u, u1, 0x04010400u),
+                       __builtin_amdgcn_perm(0x64646464u, u1, 0x04030402u)};
+          }
           const f16x8 B = __builtin_bit_cast(f16x8, bv);
-          if constexpr (FMT == W_Q8) {
-            // the block's sum of (1152 + q) x, then - 1152 x summed by two more
-            // MFMAs with a constant operand, so the offset leaves inside the
-            // block sum; then the block scale of the lane's weight row
-            const f16x8 C = __builtin_bit_cast(f16x8, u32x4{0xE480E480u, 0xE480E480u, 0xE480E480u, 0xE480E480u});
-            f32x4 ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(Xh, B, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          if constexpr (BLK) {
+            // the block's sum of (o + q) x started from - o sum x (o = 1152
+            // for int8 codes, 1032 for 4-bit codes around 8, staged per row
+            // and block), so the offset leaves inside the block sum; then the
+            // block scale of the lane's weight row
+            f32x4 ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(Xh, B, c0, 0, 0, 0);
             ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(Xl, B, ag, 0, 0, 0);
-            ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(Xh, C, ag, 0, 0, 0);
-            ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(Xl, C, ag, 0, 0, 0);
             const float sb = __uint_as_float(sq[t][s >> 2][s & 3]);
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[t][v] += sb * ag[v];
@@ -652,6 +670,8 @@ hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t stream) {
   else if (a.fmt == W_I8 && tiles == 2) launch((skinny_kernel<W_I8, 2>), grid, block, lds, stream, a);
   else if (a.fmt == W_Q8 && tiles == 1) launch((skinny_kernel<W_Q8, 1>), grid, block, lds, stream, a);
   else if (a.fmt == W_Q8 && tiles == 2) launch((skinny_kernel<W_Q8, 2>), grid, block, lds, stream, a);
+  else if (a.fmt == W_Q40 && tiles == 1) launch((skinny_kernel<W_Q40, 1>), grid, block, lds, stream, a);
+  else if (a.fmt == W_Q40 && tiles == 2) launch((skinny_kernel<W_Q40, 2>), grid, block, lds, stream, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -63,14 +63,18 @@ typedef enum {
                         Decoded by the weight-streaming GEMV (one launch per kernel), prefilled
                         through the fp16 GEMMs ("LLMs on the ANE", section "Quantized weights":
                         int8 weights) */
-  DPK_FMT_Q8 = 4     /* int8 in blocks of 32 weights along the input dim, one fp32 scale per
+  DPK_FMT_Q8 = 4,    /* int8 in blocks of 32 weights along the input dim, one fp32 scale per
                         block (w = scale[n][k / 32] * q[n][k]); fp16 KV cache.  Decoded by the
                         weight-streaming GEMV, prefilled through the fp16 GEMMs (oxinfer docs,
                         "Build and run": the q8 quantization of streamed weights) */
+  DPK_FMT_Q40 = 5    /* GGUF-style Q4_0: blocks of 32 four-bit codes c along the input dim with
+                        one fp16 scale d, w = d * (c - 8); fp16 KV cache.  Decoded by the
+                        weight-streaming GEMV, prefilled through the fp16 GEMMs (oxinfer docs,
+                        "Build and run": the q4 quantization) */
 } dpk_format;
 
 /* Element types of dpk_tensor entries. */
-typedef enum { DPK_DT_F32 = 0, DPK_DT_BF16 = 1, DPK_DT_U32 = 2, DPK_DT_I8 = 3 } dpk_dtype;
+typedef enum { DPK_DT_F32 = 0, DPK_DT_BF16 = 1, DPK_DT_U32 = 2, DPK_DT_I8 = 3, DPK_DT_U8 = 4, DPK_DT_F16 = 5 } dpk_dtype;
 
 typedef struct {
   int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, intermediate, vocab;
@@ -114,6 +118,10 @@ typedef struct {
  * and "<name>.scales" BF16 [out, 1].  In DPK_FMT_Q8 each linear tensor
  * (including embed_tokens / lm_head) is "<name>.q" I8 [out, in] and
  * "<name>.scales" F32 [out, in/32] (the scale of codes 32j .. 32j+31 of a row).
+ * In DPK_FMT_Q40 each linear tensor (including embed_tokens / lm_head) is
+ * "<name>.q" U8 [out, in/2] (per block of 32 codes, 16 bytes: byte j holds code
+ * j in its low nibble and code j + 16 in its high nibble) and "<name>.scales"
+ * F16 [out, in/32].
  */
 typedef struct {
   const char* name;
@@ -127,7 +135,7 @@ typedef struct dpk_model dpk_model;
 /* Validate the configuration and create a handle.  Supported shapes:
  * head_dim 64 or 128, n_heads a multiple of n_kv_heads with at most 8 query
  * heads per KV head, hidden and intermediate multiples of 256; bf16 / q4 /
- * i8 / q8 models need head_dim 128, per-head QK-norm and vocab % 64 == 0.  Does not touch the GPU. */
+ * i8 / q8 / q4_0 models need head_dim 128, per-head QK-norm and vocab % 64 == 0.  Does not touch the GPU. */
 dpk_status dpk_create(const dpk_config* cfg, dpk_model** out);
 
 /* Bytes of the three caller-provided device buffers:

@@ -11,7 +11,7 @@ import torch
 import oracle
 import synth
 
-TOL = {"f32": 1e-4, "bf16": 2e-2, "q4": 2e-2, "i8": 2e-2, "q8": 2e-2}
+TOL = {"f32": 1e-4, "bf16": 2e-2, "q4": 2e-2, "i8": 2e-2, "q8": 2e-2, "q4_0": 2e-2}
 
 
 def oracle_greedy(cfg, weights, prompt, n_steps):

@@ -40,7 +40,7 @@ def cfg_ok(dpk, **kw):
 
 
 @pytest.mark.parametrize("bad", [dict(head_dim=96), dict(n_kv_heads=3), dict(hidden=1000),
-                                 dict(max_rows=8), dict(weight_format=7), dict(weight_format=5), dict(vocab=0),
+                                 dict(max_rows=8), dict(weight_format=7), dict(weight_format=6), dict(vocab=0),
                                  dict(n_heads=32, n_kv_heads=2), dict(vocab=151937)])
 def test_create_rejects_bad_config(dpk, bad):
     with pytest.raises(dpk.DpkError) as e:
@@ -74,7 +74,7 @@ def test_workspace_sizes_and_call_order(dpk):
         dpk.destroy(h)
 
 
-@pytest.mark.parametrize("fmt", ["FMT_I8", "FMT_Q8"])
+@pytest.mark.parametrize("fmt", ["FMT_I8", "FMT_Q8", "FMT_Q40"])
 def test_int8_code_formats_prep_holds_fp16_operands_and_fragment_order_codes(dpk, fmt):
     """The prep buffer of an int8-code model holds the fp16 prefill operands
     (2 bytes per weight) and a fragment-order copy of the codes (1 byte per
@@ -84,8 +84,9 @@ def test_int8_code_formats_prep_holds_fp16_operands_and_fragment_order_codes(dpk
     try:
         kv, sc, pr = dpk.workspace_size(h)
         per_layer = 4096 * 1024 + 1024 * 2048 + 2 * 3072 * 1024 + 1024 * 3072  # weights
-        # q8: and a fragment-order copy of its fp32 block scales (4 bytes per 32 weights)
-        per_w = 1 + (4 / 32 if fmt == "FMT_Q8" else 0)
+        # q8 / q4_0: and a fragment-order copy of the block scales (fp32, 4 bytes per 32 weights);
+        # q4_0 codes take half a byte
+        per_w = {"FMT_I8": 1, "FMT_Q8": 1 + 4 / 32, "FMT_Q40": 0.5 + 4 / 32}[fmt]
         assert pr == 2 * (per_layer * 2 + per_layer * per_w) + 151936 * 1024 * per_w
         assert kv == 2 * 2 * 2 * 8 * 640 * 128 * 2
     finally:

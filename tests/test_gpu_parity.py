@@ -59,6 +59,11 @@ CASES = [
     ("q06b_q8-L2-stream", synth.Q06B_Q8.with_(n_layers=2), 37, 6, dict(flags=STREAM)),
     ("q8b_q8-L1-v4096-gemm", synth.Q8B_Q8.with_(n_layers=1, vocab=4096), 21, 5, {}),
     ("q8b_q8-L2-v4096-chunked", synth.Q8B_Q8.with_(n_layers=2, vocab=4096), 300, 4, dict(max_rows=128)),
+    # GGUF-style Q4_0 blocks: the same paths with 4-bit codes around 8 and fp16 scales
+    ("q06b_q40-L2-gemm", synth.Q06B_Q40.with_(n_layers=2), 40, 8, {}),
+    ("q06b_q40-L2-stream", synth.Q06B_Q40.with_(n_layers=2), 37, 6, dict(flags=STREAM)),
+    ("q8b_q40-L1-v4096-gemm", synth.Q8B_Q40.with_(n_layers=1, vocab=4096), 21, 5, {}),
+    ("q8b_q40-L2-v4096-chunked", synth.Q8B_Q40.with_(n_layers=2, vocab=4096), 300, 4, dict(max_rows=128)),
 ]
 
 
@@ -139,6 +144,7 @@ PATH_CASES = [
     ("tiny-f32", synth.TINY, False),
     ("q06b_i8-L1", synth.Q06B_I8.with_(n_layers=1), False),
     ("q06b_q8-L1", synth.Q06B_Q8.with_(n_layers=1), False),
+    ("q06b_q40-L1", synth.Q06B_Q40.with_(n_layers=1), False),
 ]
 
 
@@ -188,6 +194,7 @@ VERIFY_CASES = [
     ("q8b-L1-v4096-k15", synth.Q8B.with_(n_layers=1, vocab=4096), 500, 15),
     ("q06b_i8-L2-k5", synth.Q06B_I8.with_(n_layers=2), 70, 5),
     ("q06b_q8-L2-k5", synth.Q06B_Q8.with_(n_layers=2), 70, 5),
+    ("q06b_q40-L2-k5", synth.Q06B_Q40.with_(n_layers=2), 70, 5),
 ]
 
 
@@ -290,6 +297,7 @@ BATCH16_CASES = [
     ("q06b_q4-L2-v4096-M16", synth.Q06B_Q4.with_(n_layers=2, vocab=4096), [40 + 13 * b for b in range(16)]),
     ("q06b_i8-L2-v4096-M16", synth.Q06B_I8.with_(n_layers=2, vocab=4096), [40 + 13 * b for b in range(16)]),
     ("q06b_q8-L2-v4096-M16", synth.Q06B_Q8.with_(n_layers=2, vocab=4096), [40 + 13 * b for b in range(16)]),
+    ("q06b_q40-L2-v4096-M16", synth.Q06B_Q40.with_(n_layers=2, vocab=4096), [40 + 13 * b for b in range(16)]),
 ]
 
 
