@@ -188,6 +188,10 @@ class OracleModel:
             self._cache[name] = t
         return t
 
+    def _kv(self, x: torch.Tensor) -> torch.Tensor:
+        """What the cache holds for new keys / values x [..., d]."""
+        return quantize_kv(x) if self.cfg.kv_i8 else x
+
     def head_name(self) -> str:
         return "embed_tokens" if self.cfg.tied else "lm_head"
 
@@ -246,8 +250,8 @@ class OracleModel:
                 k = rms_norm(k, self.W(p + "self_attn.k_norm"), cfg.rms_eps)
             q = apply_rope(q, pos, cfg.rope_theta)
             k = apply_rope(k, pos, cfg.rope_theta)
-            cache.k[l][:, start:T, :] = k.transpose(0, 1)
-            cache.v[l][:, start:T, :] = v.transpose(0, 1)
+            cache.k[l][:, start:T, :] = self._kv(k.transpose(0, 1))
+            cache.v[l][:, start:T, :] = self._kv(v.transpose(0, 1))
             o = torch.empty(M, Hq, d, dtype=self.dtype)
             for hh in range(Hq):
                 g = hh // G
@@ -286,8 +290,8 @@ class OracleModel:
                 k = rms_norm(k, self.W(p + "self_attn.k_norm"), cfg.rms_eps)
             q = apply_rope(q, posv, cfg.rope_theta)[0]                # [Hq, d]
             k = apply_rope(k, posv, cfg.rope_theta)[0]                # [Hkv, d]
-            cache.k[l][:, pos, :] = k
-            cache.v[l][:, pos, :] = v
+            cache.k[l][:, pos, :] = self._kv(k)
+            cache.v[l][:, pos, :] = self._kv(v)
             o = torch.empty(Hq, d, dtype=self.dtype)
             for hh in range(Hq):
                 g = hh // G
@@ -304,6 +308,17 @@ class OracleModel:
         cache.length = pos + 1
         xn = rms_norm(x, self.W("norm"), cfg.rms_eps)
         return torch.mv(self.W(self.head_name()), xn)               # [V]
+
+
+def quantize_kv(x: torch.Tensor) -> torch.Tensor:
+    """The value an int8 KV cache returns for x [..., d]: each position's
+    head vector is held as int8 codes q = round(x / s) (clipped to +-127) with
+    one float32 scale s = max |x| / 127 (Butter notes, architecture: the
+    affine-quantized KV cache; here the affine map's offset is zero), and
+    read back as s * q.  An all-zero vector has s = 0 and reads back zeros."""
+    s = (x.abs().amax(dim=-1, keepdim=True).double() / 127.0).float().double()
+    q = torch.clamp(torch.round(x.double() / torch.where(s > 0, s, torch.ones_like(s))), -127, 127)
+    return (s * q).to(x.dtype)
 
 
 class KVCache:

@@ -154,6 +154,7 @@ class ModelConfig:
     init_std: float = 0.02
     q4_scale_std: float = 0.003
     gain_std: float = 0.0  # 0 -> every norm gain is exactly 1.0
+    kv_i8: bool = False    # KV cache held as int8 codes, one scale per position and KV head
 
     @property
     def q_dim(self) -> int:

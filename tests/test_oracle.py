@@ -628,6 +628,45 @@ def test_q40_model_equals_f64_weight_model_with_the_dequantized_weights(synth_bu
     assert float((a - b).abs().max()) == 0.0
 
 
+def test_kv_i8_quantization_hand_values_and_properties():
+    """int8 KV cache: per head vector s = fp32(max|x| / 127), q = round(x / s)
+    half to even, clipped to +-127; read back s * q."""
+    from oracle.decoder import quantize_kv
+    x = torch.tensor([[1.0, -0.5, 0.25, 0.0], [0.0, 0.0, 0.0, 0.0], [-2.0, 1.0, 0.0, 0.0]], dtype=torch.float64)
+    y = quantize_kv(x)
+    s0 = float(np.float32(1.0 / 127.0))
+    assert y[0].tolist() == [127 * s0, -64 * s0, 32 * s0, 0.0]  # -63.5 and 31.75 round to -64 and 32
+    assert y[1].tolist() == [0.0] * 4
+    s2 = float(np.float32(2.0 / 127.0))
+    assert y[2].tolist() == [-127 * s2, 64 * s2, 0.0, 0.0]  # 63.5 rounds half to even: 64
+    g = torch.Generator().manual_seed(5)
+    x = torch.randn(3, 7, 128, generator=g, dtype=torch.float64) * torch.rand(3, 7, 1, generator=g, dtype=torch.float64)
+    y = quantize_kv(x)
+    s = (x.abs().amax(-1, keepdim=True) / 127).float().double()
+    assert float(((x - y).abs() / s).max()) <= 0.5 + 1e-6          # within half a step
+    assert torch.equal(y.abs().amax(-1, keepdim=True), 127 * s)     # the largest maps to +-127
+    assert torch.equal(quantize_kv(y), y)                           # idempotent
+    assert torch.equal(quantize_kv(4 * x), 4 * y)                   # power-of-two scale invariance
+
+
+def test_kv_i8_cache_holds_the_quantized_vectors_per_position_and_head(synth_built):
+    """Layer 0's keys and values do not depend on the cache, so the int8
+    cache must hold exactly the quantized float cache, vector by vector; the
+    logits move by a bounded amount."""
+    from oracle.decoder import quantize_kv
+    cfg = synth.Q06B.with_(family="kvq", n_layers=2, vocab=512, hidden=256, n_heads=4, n_kv_heads=2, intermediate=512)
+    w = synth.make_weights(cfg, 2)
+    prompt = synth.prompt_ids(cfg, 20, 0)
+    mf, mq = oracle.OracleModel(cfg, w), oracle.OracleModel(cfg.with_(kv_i8=True), w)
+    cf, cq = mf.new_cache(24), mq.new_cache(24)
+    lf, lq = mf.forward_block(cf, prompt, 0), mq.forward_block(cq, prompt, 0)
+    sf, sq = mf.forward_step(cf, 7, 20), mq.forward_step(cq, 7, 20)
+    for a, b in ((cf.k[0], cq.k[0]), (cf.v[0], cq.v[0])):
+        assert torch.equal(quantize_kv(a[:, :21, :]), b[:, :21, :])
+        assert not torch.equal(a[:, :21, :], b[:, :21, :])
+    assert 0 < float((lf - lq).abs().max()) < 0.05 and 0 < float((sf - sq).abs().max()) < 0.05
+
+
 def test_i8_model_equals_f32_model_with_the_dequantized_weights(synth_built):
     """scale (bf16, 8 significant bits) times q (int8) is exact in fp32, so
     the int8 model must equal an fp32-format model holding those products."""
