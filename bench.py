@@ -228,7 +228,7 @@ def bench_verify(dpk, cfg, w, seed, flags, K=5, rounds=24, warm=4):
     dec.close()
     H, L, d = cfg.hidden, cfg.n_layers, cfg.head_dim
     wbytes = (cfg.n_linear_params() + cfg.vocab * H) * 2.0
-    kv = (P + K + 1) * 2 * L * cfg.n_kv_heads * d * 2.0
+    kv = (P + K + 1) * 2 * L * cfg.n_kv_heads * d * (1 + 4.0 / d if cfg.kv_i8 else 2.0)
     return {"workload": "verify K=%d (M=%d rows) over the KV cache of an %d-token prompt" % (K, K + 1, P),
             "passes_per_s": round(1.0 / vt, 2), "ms_per_pass": round(vt * 1e3, 3),
             "hbm_frac": round((wbytes + kv) / vt / 1e9 / HBM_PEAK_GBS, 4),
@@ -266,14 +266,14 @@ def bench_batch16(dpk, cfg, w, seed, flags, B=16, P=4096, N=32):
     dec.close()
     H, L, d = cfg.hidden, cfg.n_layers, cfg.head_dim
     wbytes = (cfg.n_linear_params() + cfg.vocab * H) * 2.0
-    kv = B * (P + 1 + N / 2.0) * 2 * L * cfg.n_kv_heads * d * 2.0
+    kv = B * (P + 1 + N / 2.0) * 2 * L * cfg.n_kv_heads * d * (1 + 4.0 / d if cfg.kv_i8 else 2.0)
     return {"workload": "batched decode: %d sequences x %d-token KV caches, %d steps" % (B, P, N),
             "tok_s": round(B / dt, 1), "ms_per_step": round(dt * 1e3, 3),
             "hbm_frac": round((wbytes + kv) / dt / 1e9 / HBM_PEAK_GBS, 4),
             "kernel_classes_us_per_step": classes}
 
 
-def run_workload(dpk, name, steps, warmup, seed, flags, decode_steps=None, profile=True, w=None):
+def run_workload(dpk, name, steps, warmup, seed, flags, decode_steps=None, profile=True, w=None, kv_i8=False):
     """Prefill + greedy batch-1 decode of one workload: steps timed passes after
     warmup untimed ones.  Returns (result dict, host weights)."""
     import torch
@@ -282,6 +282,8 @@ def run_workload(dpk, name, steps, warmup, seed, flags, decode_steps=None, profi
     if decode_steps is not None:
         N = decode_steps
     cfg = synth.CONFIGS[cname]
+    if kv_i8:
+        cfg = cfg.with_(kv_i8=True)
     t0 = time.time()
     if w is None:
         w = synth.make_weights(cfg, seed)
@@ -334,7 +336,7 @@ def run_workload(dpk, name, steps, warmup, seed, flags, decode_steps=None, profi
     head_params = cfg.vocab * H
     wbytes = {"bf16": 2.0, "f32": 4.0, "q4": 0.5 + 4.0 / 64, "i8": 1.0 + 2.0 / H, "q8": 1.0 + 4.0 / 32,
               "q4_0": 0.5 + 2.0 / 32}[cfg.weight_format]
-    kv_elt = 4 if cfg.weight_format == "f32" else 2
+    kv_elt = 4 if cfg.weight_format == "f32" else (1 + 4.0 / cfg.head_dim if cfg.kv_i8 else 2)
     kv_per_pos = 2 * L * cfg.n_kv_heads * d * kv_elt
     mean_ctx = P + (N + 1) / 2.0
     decode_bytes_tok = (n_lin + head_params) * wbytes + kv_per_pos * mean_ctx
@@ -403,6 +405,9 @@ def main():
     ap.add_argument("--decode-path", choices=["auto", "multi"], default="auto",
                     help="auto: one persistent launch per decode step where the shapes allow it; "
                          "multi: one launch per kernel")
+    ap.add_argument("--kv-i8", action="store_true",
+                    help="int8 KV cache (one fp32 scale per position and KV head); decode then runs one launch "
+                         "per kernel; the verify and batch-16 extras use it too")
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="override the workload's decode step count (for counter runs; not a bench figure)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -422,7 +427,7 @@ def main():
     flags = 2 if args.decode_path == "multi" else 0  # DPK_FLAG_DECODE_MULTI
     try:
         head, w, cfg, prompt = run_workload(dpk, args.workload, args.steps, args.warmup, args.seed, flags,
-                                            args.decode_steps, not args.no_profile)
+                                            args.decode_steps, not args.no_profile, kv_i8=args.kv_i8)
         extra = {}
         if not args.no_extra and args.workload == "q8b" and args.decode_steps is None:
             log("[bench] verify K=5 over an 8192-token cache ...")
@@ -466,7 +471,8 @@ def main():
         "dtype": "bf16" if cfg.weight_format == "bf16" else cfg.weight_format,
         "data": "synthetic (seeded N(0,0.02) weights, uniform random prompt ids)",
         "config": {"workload": head["workload"], "prompt_tokens": head["prompt_tokens"],
-                   "decode_steps": head["decode_steps"], "batch": 1, "decode_path": args.decode_path},
+                   "decode_steps": head["decode_steps"], "batch": 1, "decode_path": args.decode_path,
+                   "kv_cache": "int8 + fp32 scale per position" if args.kv_i8 else "fp16"},
         "prefill_dtype": "fp16 operands, fp32 accumulation",
     }
     for k in ("decode_tok_s", "prefill_tok_s", "prefill_ms", "decode_ms_per_token", "decode_hbm_frac",

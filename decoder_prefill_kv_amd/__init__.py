@@ -23,6 +23,7 @@ _SO = os.path.join(_HERE, "_dpk.so")
 DPK_OK, DPK_EINVAL, DPK_ERANGE, DPK_ESTATE, DPK_ENOMEM, DPK_EHIP = 0, -1, -2, -3, -4, -5
 FMT_F32, FMT_BF16, FMT_Q4G64, FMT_I8, FMT_Q8, FMT_Q40 = 0, 1, 2, 3, 4, 5
 FLAG_PREFILL_STREAM = 1
+FLAG_KV_I8 = 4
 DT_F32, DT_BF16, DT_U32, DT_I8, DT_U8, DT_F16 = 0, 1, 2, 3, 4, 5
 SYMBOLS = ["dpk_create", "dpk_workspace_size", "dpk_bind_workspace", "dpk_load_weights", "dpk_prefill",
            "dpk_prefill_at", "dpk_decode_step", "dpk_verify", "dpk_seq_length", "dpk_check_device_errors",
@@ -295,7 +296,10 @@ _FMT = {"f32": FMT_F32, "bf16": FMT_BF16, "q4": FMT_Q4G64, "i8": FMT_I8, "q8": F
 
 
 def make_config(mc, max_batch: int, max_seq: int, max_rows: int = 512, flags: int = 0) -> Config:
-    """dpk_config from any object with the decoder shape attributes."""
+    """dpk_config from any object with the decoder shape attributes (an int8
+    KV cache when the object's ``kv_i8`` is true)."""
+    if getattr(mc, "kv_i8", False):
+        flags |= FLAG_KV_I8
     return Config(mc.n_layers, mc.hidden, mc.n_heads, mc.n_kv_heads, mc.head_dim, mc.intermediate, mc.vocab,
                   float(mc.rms_eps), float(mc.rope_theta), int(bool(mc.qk_norm)), int(bool(mc.tied)),
                   _FMT[mc.weight_format], max_batch, max_seq, max_rows, flags)

@@ -20,6 +20,13 @@
 //
 // MFMA 16x16x32 lane layout: A lane l holds row l%16, k = 8(l/16)..+7; B lane l
 // holds column l%16, the same k; D lane l holds rows 4(l/16)+v, column l%16.
+//
+// int8 cache (KV8): each position's K and V head vectors are int8 codes with
+// one fp32 scale.  The codes enter the MFMAs as the fp16 integers 1152 + q (the
+// byte q ^ 0x80 under the high byte 0x64); S starts from -1152 sum_d q_c per
+// column and is then multiplied by the key's scale; each value's scale is
+// folded into P (P'), and 1152 sum_p P' per column, carried with the online
+// rescale, comes off O at the end.
 #include "common.h"
 #include "kernels.h"
 
@@ -38,8 +45,17 @@ DPK_DEV void split_f16(float x, _Float16& hi, _Float16& lo) {
   lo = (_Float16)(x - (float)hi);
 }
 
-template <int D, bool RAW>
+// 8 int8 codes -> fp16 1152 + q (exact)
+DPK_DEV u32x4 codes_f16(u32x2 w) {
+  const uint32_t u0 = w.x ^ 0x80808080u, u1 = w.y ^ 0x80808080u;
+  return u32x4{__builtin_amdgcn_perm(0x64646464u, u0, 0x04010400u), __builtin_amdgcn_perm(0x64646464u, u0, 0x04030402u),
+               __builtin_amdgcn_perm(0x64646464u, u1, 0x04010400u), __builtin_amdgcn_perm(0x64646464u, u1, 0x04030402u)};
+}
+
+template <int D, bool RAW, bool KV8>
 __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArgs a) {
+  static_assert(!KV8 || D == 128, "int8 cache: head_dim 128");
+  using Frag = typename std::conditional<KV8, u32x2, u32x4>::type;  // 8 cache elements
   const int chunk_id = blockIdx.x, g = blockIdx.y;
   // rows m .. m + R - 1 (one sequence when R > 1); column c = r G + head
   const int SH = a.share > 1 ? a.share : 1;
@@ -67,9 +83,16 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
   __shared__ float knew[D], vnew[D];
   __shared__ float wst[NW][2][16];     // per wave: max, sum per column
   __shared__ float ow[NW][D][16];      // per wave: O^T partial
+  __shared__ float qsum[16];           // int8 cache: sum of q hi + lo per column
+  __shared__ __attribute__((aligned(16))) int8_t knew8[KV8 ? D : 16], vnew8[KV8 ? D : 16];
+  __shared__ float newsc[2];           // int8 cache: scales of the own position's key / value
 
-  const _Float16* Kb = (const _Float16*)a.kv.base + kv_slab(a.kv, rp.seq, a.layer, 0, g);
-  const _Float16* Vb = (const _Float16*)a.kv.base + kv_slab(a.kv, rp.seq, a.layer, 1, g);
+  // (element pointers: fp16, or int8 codes with per-position scales)
+  using Elt = typename std::conditional<KV8, int8_t, _Float16>::type;
+  const Elt* Kb = (const Elt*)a.kv.base + kv_slab(a.kv, rp.seq, a.layer, 0, g);
+  const Elt* Vb = (const Elt*)a.kv.base + kv_slab(a.kv, rp.seq, a.layer, 1, g);
+  const float* Ksc = KV8 ? a.kv.scales + kv_scale_slab(a.kv, rp.seq, a.layer, 0, g) : nullptr;
+  const float* Vsc = KV8 ? a.kv.scales + kv_scale_slab(a.kv, rp.seq, a.layer, 1, g) : nullptr;
   constexpr bool raw = RAW;  // a.qkv_raw != nullptr
   const bool own = raw && rp.pos >= c0 && rp.pos < c1;
 
@@ -119,21 +142,31 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
   // group j4 positions 8 j4 .. + 7 (its k range of P^T in the P V product)
   // and V^T is read as one 8-position (16-byte) group per lane; an 8-position
   // group stays inside the slab row (max_seq % 64 == 0).
-  auto load = [&](u32x4 (&kf)[2][D / 32], u32x4 (&vf)[D / 16], int s) {
+  // int8 cache: the scales of the lane's 8 positions sp + 8 j4 .. + 7 (the
+  // same group as its V fragment; a group past the context reads the last
+  // whole group's, and those positions are masked)
+  auto load = [&](Frag (&kf)[2][D / 32], Frag (&vf)[D / 16], f32x4 (&sc8)[4], int s) {
     const int sp = c0 + s * STEP + 32 * wave;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int p = min(sp + 8 * (r16 >> 2) + 4 * t + (r16 & 3), c1 - 1);
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) kf[t][ks] = *(const u32x4*)(Kb + (size_t)p * D + 32 * ks + 8 * j4);
+      for (int ks = 0; ks < D / 32; ++ks) kf[t][ks] = *(const Frag*)(Kb + (size_t)p * D + 32 * ks + 8 * j4);
     }
     const int p8 = min(sp + 8 * j4, (c1 - 1) & ~7);
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) vf[dt] = *(const u32x4*)(Vb + (size_t)(dt * 16 + r16) * a.kv.max_seq + p8);
+    for (int dt = 0; dt < D / 16; ++dt) vf[dt] = *(const Frag*)(Vb + (size_t)(dt * 16 + r16) * a.kv.max_seq + p8);
+    if constexpr (KV8) {
+      sc8[0] = *(const f32x4*)(Ksc + p8);
+      sc8[1] = *(const f32x4*)(Ksc + p8 + 4);
+      sc8[2] = *(const f32x4*)(Vsc + p8);
+      sc8[3] = *(const f32x4*)(Vsc + p8 + 4);
+    }
   };
-  u32x4 kA[2][D / 32], vA[D / 16], kB[2][D / 32], vB[D / 16];
-  load(kA, vA, 0);
-  if (nsteps > 1) load(kB, vB, 1);
+  Frag kA[2][D / 32], vA[D / 16], kB[2][D / 32], vB[D / 16];
+  f32x4 sA[4], sB[4];
+  load(kA, vA, sA, 0);
+  if (nsteps > 1) load(kB, vB, sB, 1);
 
   // ---- q (and in raw mode the new key/value) -> LDS
   if constexpr (!raw) {
@@ -172,11 +205,36 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
     if (own && tid < D) vnew[tid] = vv;
   }
   lds_barrier();  // an LDS-only barrier: the cache loads stay in flight
-  if (own)
-    for (int e = tid; e < D; e += THREADS) {
-      kv_store(a.kv, kv_offset(a.kv, rp.seq, a.layer, 0, g, e, rp.pos), knew[e]);
-      kv_store(a.kv, kv_offset(a.kv, rp.seq, a.layer, 1, g, e, rp.pos), vnew[e]);
+  if (own) {
+    if constexpr (KV8) {  // wave 0: codes and scales of the new key and value, to the cache and LDS
+      if (wave == 0) {
+        float q0, q1;
+        float sk = kv_quant_i8(knew[lane], knew[lane + 64], q0, q1);
+        knew8[lane] = (int8_t)q0;
+        knew8[lane + 64] = (int8_t)q1;
+        int8_t* kb = (int8_t*)a.kv.base + kv_slab(a.kv, rp.seq, a.layer, 0, g) + (size_t)rp.pos * D;
+        kb[lane] = (int8_t)q0;
+        kb[lane + 64] = (int8_t)q1;
+        const float sv = kv_quant_i8(vnew[lane], vnew[lane + 64], q0, q1);
+        vnew8[lane] = (int8_t)q0;
+        vnew8[lane + 64] = (int8_t)q1;
+        int8_t* vb = (int8_t*)a.kv.base + kv_slab(a.kv, rp.seq, a.layer, 1, g);
+        vb[(size_t)lane * a.kv.max_seq + rp.pos] = (int8_t)q0;
+        vb[(size_t)(lane + 64) * a.kv.max_seq + rp.pos] = (int8_t)q1;
+        if (lane == 0) {
+          newsc[0] = sk;
+          newsc[1] = sv;
+          a.kv.scales[kv_scale_slab(a.kv, rp.seq, a.layer, 0, g) + rp.pos] = sk;
+          a.kv.scales[kv_scale_slab(a.kv, rp.seq, a.layer, 1, g) + rp.pos] = sv;
+        }
+      }
+    } else {
+      for (int e = tid; e < D; e += THREADS) {
+        kv_store(a.kv, kv_offset(a.kv, rp.seq, a.layer, 0, g, e, rp.pos), knew[e]);
+        kv_store(a.kv, kv_offset(a.kv, rp.seq, a.layer, 1, g, e, rp.pos), vnew[e]);
+      }
     }
+  }
 
   // q as fp16 hi + lo, kept in LDS (the B fragments are re-read every step:
   // registers are what the two steps of cache fragments in flight need)
@@ -187,17 +245,67 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
     (&ql16[0][0])[i] = l;
   }
   lds_barrier();
+  if constexpr (KV8) {  // per column, the sum of the q parts the MFMAs multiply (waves 0 .. 7: columns 2w, 2w + 1)
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const int col = 2 * wave + cc;
+      float qs2 = (float)qh16[col][lane] + (float)ql16[col][lane] + (float)qh16[col][lane + 64] +
+                  (float)ql16[col][lane + 64];
+      qs2 = wave_sum(qs2);
+      if (lane == 0) qsum[col] = qs2;
+    }
+    lds_barrier();
+  }
+  const float cq = KV8 ? -1152.0f * qsum[r16] : 0.f;  // the S accumulator's start (int8 cache)
+  float corr = 0.f;  // int8 cache: 1152 sum_p P' of the lane's column, online-rescaled
 
   // ---- the steps, online softmax per column (log2 domain)
   float mrun = -INFINITY, lrun = 0.f;
   f32x4 o[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto step = [&](u32x4 (&kf)[2][D / 32], u32x4 (&vf)[D / 16], int s) {
+  auto step = [&](Frag (&kf)[2][D / 32], Frag (&vf)[D / 16], f32x4 (&sc8)[4], int s) {
     const int sp = c0 + s * STEP + 32 * wave;
-    if (own) {  // the new position inside this wave's fragments comes from knew / vnew
+    float sk[8], sv[8];  // int8 cache: scales of the lane's positions sp + 8 j4 + i (values past the context: 0)
+    if constexpr (KV8) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        sk[i] = sc8[i >> 2][i & 3];
+        sv[i] = (sp + 8 * j4 + i < c1) ? sc8[2 + (i >> 2)][i & 3] : 0.f;
+      }
+    }
+    if constexpr (KV8) {  // int8 cache: the new position's codes and scales come from LDS
       const int off = rp.pos - sp;
-      if (off >= 0 && off < 32) {
+      if (own && off >= 0 && off < 32) {
+        const int kt = (off % 8) / 4, kr = 4 * (off / 8) + off % 4;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          if (t == kt && r16 == kr) {
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks) kf[t][ks] = *(const Frag*)&knew8[32 * ks + 8 * j4];
+          }
+        const int e8 = off % 8;
+        if (j4 == off / 8) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (i == e8) {
+              sk[i] = newsc[0];
+              sv[i] = newsc[1];
+            }
+          const uint32_t sh = 8u * (e8 & 3), keep = ~(0xFFu << sh);
+#pragma unroll
+          for (int dt = 0; dt < D / 16; ++dt) {
+            const uint32_t b = (uint32_t)(uint8_t)vnew8[dt * 16 + r16] << sh;
+            if (e8 < 4)
+              vf[dt].x = (vf[dt].x & keep) | b;
+            else
+              vf[dt].y = (vf[dt].y & keep) | b;
+          }
+        }
+      }
+    } else {  // the new position inside this wave's fragments comes from knew / vnew
+      const int off = rp.pos - sp;
+      if (own && off >= 0 && off < 32) {
         // compile-time fragment indices only (runtime ones would spill the arrays)
         const int kt = (off % 8) / 4, kr = 4 * (off / 8) + off % 4;
 #pragma unroll
@@ -227,14 +335,22 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
     f32x4 sc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sc[t] = f32x4{cq, cq, cq, cq};
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) {
-        const f16x8 A = __builtin_bit_cast(f16x8, kf[t][ks]);
+        f16x8 A;
+        if constexpr (KV8)
+          A = __builtin_bit_cast(f16x8, codes_f16(kf[t][ks]));
+        else
+          A = __builtin_bit_cast(f16x8, kf[t][ks]);
         const f16x8 qh = *(const f16x8*)&qh16[r16][32 * ks + 8 * j4];
         const f16x8 ql = *(const f16x8*)&ql16[r16][32 * ks + 8 * j4];
         sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qh, sc[t], 0, 0, 0);
         sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, ql, sc[t], 0, 0, 0);
+      }
+      if constexpr (KV8) {  // the keys' scales (lane rows 4 j4 + v of tile t: positions 8 j4 + 4 t + v)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sc[t][v] *= sk[4 * t + v];
       }
     }
     // mask (positions sp + 8 j4 + 4 t + v past the column's context), step max
@@ -263,6 +379,12 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
     sum += __shfl_xor(sum, 32, 64);
     lrun = lrun * alpha + sum;
     mrun = mnew;
+    if constexpr (KV8) {  // P' = P times the value's scale
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sc[t][v] *= sv[4 * t + v];
+    }
     // O^T = alpha O^T + V^T P^T (k slots 0..3 from tile 0, 4..7 from tile 1)
     f16x8 ph, pl;
 #pragma unroll
@@ -275,14 +397,27 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
       ph[4 + v] = h1;
       pl[4 + v] = l1;
     }
+    if constexpr (KV8) {  // 1152 sum_p P' of the column (the parts the MFMAs take)
+      float cs = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) cs += (float)ph[i] + (float)pl[i];
+      cs += __shfl_xor(cs, 16, 64);
+      cs += __shfl_xor(cs, 32, 64);
+      corr = corr * alpha + 1152.0f * cs;
+    }
     // V positions past the context may hold any bits (0 * NaN): masked with
-    // ANDs (no branch, so the wait counts stay exact)
+    // ANDs (no branch, so the wait counts stay exact); int8 codes are always
+    // finite as fp16 and meet P' = 0 there
     const int nv = c1 - sp - 8 * j4;
     auto mk = [nv](int e) { return nv >= e + 2 ? 0xffffffffu : (nv == e + 1 ? 0x0000ffffu : 0u); };
     const u32x4 vm = {mk(0), mk(2), mk(4), mk(6)};
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      const u32x4 w = vf[dt] & vm;
+      u32x4 w;
+      if constexpr (KV8)
+        w = codes_f16(vf[dt]);
+      else
+        w = vf[dt] & vm;
       const f16x8 A = __builtin_bit_cast(f16x8, w);
 #pragma unroll
       for (int v = 0; v < 4; ++v) o[dt][v] *= alpha;
@@ -291,12 +426,18 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
     }
   };
   for (int s = 0; s < nsteps; s += 2) {
-    step(kA, vA, s);
-    if (s + 2 < nsteps) load(kA, vA, s + 2);
+    step(kA, vA, sA, s);
+    if (s + 2 < nsteps) load(kA, vA, sA, s + 2);
     if (s + 1 < nsteps) {
-      step(kB, vB, s + 1);
-      if (s + 3 < nsteps) load(kB, vB, s + 3);
+      step(kB, vB, sB, s + 1);
+      if (s + 3 < nsteps) load(kB, vB, sB, s + 3);
     }
+  }
+  if constexpr (KV8) {  // the code offset of the values (lane: column r16 of every O^T tile)
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) o[dt][v] -= corr;
   }
 
   // ---- combine the waves (per column = query head)
@@ -399,24 +540,31 @@ int attn_decode_mfma_chunk(int max_ctx, int units, int n_cu) {
 }
 
 hipError_t launch_attn_decode_mfma(const AttnDecodeArgs& a, hipStream_t stream) {
-  if (a.kv.is_f32 || a.n_heads % a.n_kv || a.n_heads / a.n_kv > 16 || a.max_chunks > MAXCH || a.kv.max_seq % 64 ||
+  if (a.kv.is_f32 || (a.kv.i8 && a.d != 128) || a.n_heads % a.n_kv || a.n_heads / a.n_kv > 16 ||
+      a.max_chunks > MAXCH || a.kv.max_seq % 64 ||
       a.chunk < STEP || a.chunk % STEP || (a.max_chunks > 1 && !a.merge))
     return hipErrorInvalidValue;
   const int sh = a.share > 1 ? a.share : 1;
   if (sh > 1 && (a.qkv_raw || sh * (a.n_heads / a.n_kv) > 16)) return hipErrorInvalidValue;
   dim3 grid(a.max_chunks, a.n_kv, (a.M + sh - 1) / sh);
   const bool raw = a.qkv_raw != nullptr;
-  if (a.d == 128) {
+  if (a.d == 128 && a.kv.i8) {
     if (raw)
-      launch(attn_decode_mfma_kernel<128, true>, grid, dim3(THREADS), 0, stream, a);
+      launch(attn_decode_mfma_kernel<128, true, true>, grid, dim3(THREADS), 0, stream, a);
     else
-      launch(attn_decode_mfma_kernel<128, false>, grid, dim3(THREADS), 0, stream, a);
+      launch(attn_decode_mfma_kernel<128, false, true>, grid, dim3(THREADS), 0, stream, a);
+    if (a.merge) launch(attn_merge_kernel<128>, dim3(a.n_heads, a.M), dim3(128), 0, stream, a);
+  } else if (a.d == 128) {
+    if (raw)
+      launch(attn_decode_mfma_kernel<128, true, false>, grid, dim3(THREADS), 0, stream, a);
+    else
+      launch(attn_decode_mfma_kernel<128, false, false>, grid, dim3(THREADS), 0, stream, a);
     if (a.merge) launch(attn_merge_kernel<128>, dim3(a.n_heads, a.M), dim3(128), 0, stream, a);
   } else if (a.d == 64) {
     if (raw)
-      launch(attn_decode_mfma_kernel<64, true>, grid, dim3(THREADS), 0, stream, a);
+      launch(attn_decode_mfma_kernel<64, true, false>, grid, dim3(THREADS), 0, stream, a);
     else
-      launch(attn_decode_mfma_kernel<64, false>, grid, dim3(THREADS), 0, stream, a);
+      launch(attn_decode_mfma_kernel<64, false, false>, grid, dim3(THREADS), 0, stream, a);
     if (a.merge) launch(attn_merge_kernel<64>, dim3(a.n_heads, a.M), dim3(64), 0, stream, a);
   } else {
     return hipErrorInvalidValue;

@@ -16,6 +16,9 @@
 // (two MFMAs per product), so the only 16-bit rounding left is that of the
 // cached K and V.
 //
+// int8 cache (KV8): the tiles are staged as fp16 s * q, s the position's scale
+// (one more fp16 rounding, of the same size as the fp16 cache's own).
+//
 // Workgroup: 4 waves, each one query head x 32 query rows; the heads of a
 // workgroup share one KV head, so each K / V^T tile (64 keys) is staged in LDS
 // once for all of them.
@@ -33,7 +36,10 @@ constexpr int KSTR = D + 8;     // halfs per K row in LDS
 constexpr int VSTR = BKV + 8;   // halfs per V^T row in LDS
 constexpr float LOG2E = 1.4426950408889634f;
 
-__global__ __launch_bounds__(THREADS, 2) void attn_prefill_kernel(AttnPrefillArgs a, int heads_per_wg, int rb_per_wg,
+// (int8 cache: one workgroup per CU -- the staging registers of the codes and
+// scales do not fit beside the fp16 kernel's 254 at two)
+template <bool KV8>
+__global__ __launch_bounds__(THREADS, KV8 ? 1 : 2) void attn_prefill_kernel(AttnPrefillArgs a, int heads_per_wg, int rb_per_wg,
                                                                     int n_rb, int n_hg) {
   __shared__ __attribute__((aligned(16))) _Float16 Ks[BKV][KSTR];
   __shared__ __attribute__((aligned(16))) _Float16 Vs[D][VSTR];
@@ -97,15 +103,35 @@ __global__ __launch_bounds__(THREADS, 2) void attn_prefill_kernel(AttnPrefillArg
   // an 8-key load stays inside the row.
   u32x4 kreg[4];
   f16x8 vreg[4];
+  // int8 cache: codes (8 per piece) and the scales of their key(s)
+  const int8_t* K8 = (const int8_t*)a.kv.base + kv_slab(a.kv, a.seq, a.layer, 0, g);
+  const int8_t* V8 = (const int8_t*)a.kv.base + kv_slab(a.kv, a.seq, a.layer, 1, g);
+  const float* Ksc = KV8 ? a.kv.scales + kv_scale_slab(a.kv, a.seq, a.layer, 0, g) : nullptr;
+  const float* Vsc = KV8 ? a.kv.scales + kv_scale_slab(a.kv, a.seq, a.layer, 1, g) : nullptr;
+  // (a thread's V pieces share their 8 keys: idx & 7 == tid & 7)
+  u32x2 kq[4], vq[4];
+  float ksf[4];
+  f32x4 vsf[2];
   auto gload = [&](int k0) {
     const bool tail = k0 + BKV > kend;  // uniform: only the last tile has keys past kend
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int idx = tid + THREADS * i;  // 0..1023
       const int kr = idx >> 4, kc = (idx & 15) * 8;
-      kreg[i] = *(const u32x4*)(Kg + (size_t)(tail ? min(k0 + kr, kend - 1) : k0 + kr) * D + kc);
+      const int krow = tail ? min(k0 + kr, kend - 1) : k0 + kr;
       const int vr = idx >> 3, vc = (idx & 7) * 8;
-      vreg[i] = *(const f16x8*)(Vg + (size_t)vr * a.kv.max_seq + k0 + vc);
+      if constexpr (KV8) {
+        kq[i] = *(const u32x2*)(K8 + (size_t)krow * D + kc);
+        ksf[i] = Ksc[krow];
+        vq[i] = *(const u32x2*)(V8 + (size_t)vr * a.kv.max_seq + k0 + vc);
+        if (i == 0) {
+          vsf[0] = *(const f32x4*)(Vsc + k0 + vc);
+          vsf[1] = *(const f32x4*)(Vsc + k0 + vc + 4);
+        }
+      } else {
+        kreg[i] = *(const u32x4*)(Kg + (size_t)krow * D + kc);
+        vreg[i] = *(const f16x8*)(Vg + (size_t)vr * a.kv.max_seq + k0 + vc);
+      }
     }
   };
   auto lstore = [&](int k0) {
@@ -114,8 +140,19 @@ __global__ __launch_bounds__(THREADS, 2) void attn_prefill_kernel(AttnPrefillArg
     for (int i = 0; i < 4; ++i) {
       const int idx = tid + THREADS * i;
       const int kr = idx >> 4, kc = (idx & 15) * 8;
-      *(u32x4*)&Ks[kr][kc] = kreg[i];
       const int vr = idx >> 3, vc = (idx & 7) * 8;
+      if constexpr (KV8) {  // s * q as fp16
+        f16x8 kk, v8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t kw = e < 4 ? kq[i].x : kq[i].y, vw = e < 4 ? vq[i].x : vq[i].y;
+          kk[e] = (_Float16)(ksf[i] * (float)(int8_t)(kw >> (8 * (e & 3))));
+          v8[e] = (_Float16)(vsf[e >> 2][e & 3] * (float)(int8_t)(vw >> (8 * (e & 3))));
+        }
+        kreg[i] = __builtin_bit_cast(u32x4, kk);
+        vreg[i] = v8;
+      }
+      *(u32x4*)&Ks[kr][kc] = kreg[i];
       // keys at or past kend are zeroed (the cache there may hold any bit
       // pattern, and 0 * NaN would poison O); only the last tile has any
       f16x8 vv = vreg[i];
@@ -252,7 +289,10 @@ hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t stream) {
   const int rbpw = 4 / hpw;
   const int n_rb = (a.M + 32 * rbpw - 1) / (32 * rbpw);
   const int n_hg = a.n_heads / hpw;
-  launch(attn_prefill_kernel, dim3(n_rb * n_hg), dim3(THREADS), 0, stream, a, hpw, rbpw, n_rb, n_hg);
+  if (a.kv.i8)
+    launch(attn_prefill_kernel<true>, dim3(n_rb * n_hg), dim3(THREADS), 0, stream, a, hpw, rbpw, n_rb, n_hg);
+  else
+    launch(attn_prefill_kernel<false>, dim3(n_rb * n_hg), dim3(THREADS), 0, stream, a, hpw, rbpw, n_rb, n_hg);
   return hipGetLastError();
 }
 

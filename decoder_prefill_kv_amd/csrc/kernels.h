@@ -12,6 +12,8 @@ struct KVDesc {
   void* base;
   int is_f32;
   int n_layers, n_kv, max_seq, d;
+  int i8;         // int8 codes at base (same element layout), one fp32 scale per position in scales
+  float* scales;  // int8 cache: [seq][layer][K|V][head][max_seq]
 };
 
 __host__ __device__ inline size_t kv_slab(const KVDesc& kv, int seq, int layer, int which, int head) {
@@ -22,6 +24,33 @@ __host__ __device__ inline size_t kv_offset(const KVDesc& kv, int seq, int layer
                                             int e, int pos) {
   const size_t s = kv_slab(kv, seq, layer, which, head);
   return which == 0 ? s + (size_t)pos * kv.d + e : s + (size_t)e * kv.max_seq + pos;
+}
+__host__ __device__ inline size_t kv_scale_slab(const KVDesc& kv, int seq, int layer, int which, int head) {
+  return ((((size_t)seq * kv.n_layers + layer) * 2 + which) * kv.n_kv + head) * (size_t)kv.max_seq;
+}
+// int8 cache: one position's head vector (d == 128) held by a wave, elements
+// lane and lane + 64, quantized to codes round(x / s), s = max |x| / 127
+// (clipped to +-127; s = 0 stores zeros), codes and scale stored
+DPK_DEV float kv_quant_i8(float x0, float x1, float& q0, float& q1) {  // returns s (wave-uniform)
+  const float m = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+  const float s = m / 127.0f;
+  q0 = s > 0.f ? fminf(fmaxf(rintf(x0 / s), -127.f), 127.f) : 0.f;
+  q1 = s > 0.f ? fminf(fmaxf(rintf(x1 / s), -127.f), 127.f) : 0.f;
+  return s;
+}
+DPK_DEV void kv_put_i8(const KVDesc& kv, int seq, int layer, int which, int head, int pos, float x0, float x1,
+                       int lane) {
+  float q0, q1;
+  const float s = kv_quant_i8(x0, x1, q0, q1);
+  int8_t* b = (int8_t*)kv.base + kv_slab(kv, seq, layer, which, head);
+  if (which == 0) {
+    b[(size_t)pos * 128 + lane] = (int8_t)q0;
+    b[(size_t)pos * 128 + lane + 64] = (int8_t)q1;
+  } else {
+    b[(size_t)lane * kv.max_seq + pos] = (int8_t)q0;
+    b[(size_t)(lane + 64) * kv.max_seq + pos] = (int8_t)q1;
+  }
+  if (lane == 0) kv.scales[kv_scale_slab(kv, seq, layer, which, head) + pos] = s;
 }
 DPK_DEV void kv_store(const KVDesc& kv, size_t off, float v) {
   if (kv.is_f32)

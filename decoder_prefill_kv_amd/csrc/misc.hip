@@ -183,6 +183,13 @@ __global__ __launch_bounds__(256) void qk_rope_kv_rows_kernel(const float* qkv, 
   const RowParam r0 = rp[m0];
   if (hh >= n_heads + n_kv) {  // v head -> V^T slab
     const int vh = hh - n_heads - n_kv;
+    if (kv.i8) {  // int8 cache: one wave per position (codes + scale)
+      for (int rr = wave; rr < rows; rr += 4) {
+        const float* src = qkv + (size_t)(m0 + rr) * ld + (size_t)hh * D;
+        kv_put_i8(kv, r0.seq, layer, 1, vh, r0.pos + rr, src[lane], src[lane + HD], lane);
+      }
+      return;
+    }
     for (int i = tid; i < rows * D; i += 256) {
       const int rr = i / D, e = i % D;
       vt[e][rr] = (_Float16)qkv[(size_t)(m0 + rr) * ld + (size_t)hh * D + e];
@@ -230,6 +237,8 @@ __global__ __launch_bounds__(256) void qk_rope_kv_rows_kernel(const float* qkv, 
       qh[o + lane + HD] = h2;
       ql[o + lane] = (_Float16)(y1 - (float)h1);
       ql[o + lane + HD] = (_Float16)(y2 - (float)h2);
+    } else if (kv.i8) {
+      kv_put_i8(kv, r0.seq, layer, 0, hh - n_heads, pos, y1, y2, lane);
     } else {
       _Float16* kb = (_Float16*)kv.base + kv_slab(kv, r0.seq, layer, 0, hh - n_heads) + (size_t)pos * D;
       kb[lane] = (_Float16)y1;
@@ -250,6 +259,10 @@ __global__ void qk_rope_kv_kernel(const float* qkv, int n_heads, int n_kv, int d
   const int hd2 = d / 2;
   if (hh >= n_heads + n_kv) {  // v head -> V^T slab
     const int vh = hh - n_heads - n_kv;
+    if (kv.i8) {  // (d == 128)
+      kv_put_i8(kv, r.seq, layer, 1, vh, r.pos, src[lane], src[lane + 64], lane);
+      return;
+    }
     for (int e = lane; e < d; e += 64) kv_store(kv, kv_offset(kv, r.seq, layer, 1, vh, e, r.pos), src[e]);
     return;
   }
@@ -293,6 +306,8 @@ __global__ void qk_rope_kv_kernel(const float* qkv, int n_heads, int n_kv, int d
         ((float*)q_out)[o + e] = y1;
         ((float*)q_out)[o + e + hd2] = y2;
       }
+    } else if (kv.i8) {  // (d == 128: one element pair per lane)
+      kv_put_i8(kv, r.seq, layer, 0, hh - n_heads, r.pos, y1, y2, lane);
     } else {
       const int kh = hh - n_heads;
       const size_t o = kv_offset(kv, r.seq, layer, 0, kh, 0, r.pos);

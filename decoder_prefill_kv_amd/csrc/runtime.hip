@@ -239,9 +239,16 @@ size_t prep_bytes(const dpk_config& c) {
 // 64-key tiles never leave a row
 int kv_seq(const dpk_config& c) { return (c.max_seq + 63) / 64 * 64; }
 
-size_t kv_bytes(const dpk_config& c) {
-  const size_t elt = c.weight_format == DPK_FMT_F32 ? 4 : 2;
+// int8 cache: codes, then at a 256-byte boundary one fp32 scale per position and slab
+size_t kv_code_bytes(const dpk_config& c) {
+  const size_t elt = c.weight_format == DPK_FMT_F32 ? 4 : (c.flags & DPK_FLAG_KV_I8) ? 1 : 2;
   return (size_t)c.max_batch * c.n_layers * 2 * c.n_kv_heads * kv_seq(c) * c.head_dim * elt;
+}
+
+size_t kv_bytes(const dpk_config& c) {
+  const size_t codes = kv_code_bytes(c);
+  if (!(c.flags & DPK_FLAG_KV_I8)) return codes;
+  return up(codes) + (size_t)c.max_batch * c.n_layers * 2 * c.n_kv_heads * kv_seq(c) * 4;
 }
 
 #define HIP_TRY(expr)                                                                  \
@@ -467,7 +474,7 @@ dpk_status attn_decode(dpk_model* md, int M, int max_ctx, const float* q, float*
     a.eps = c.rms_eps;
   }
   {
-    const double elt = md->kvd.is_f32 ? 4 : 2;
+    const double elt = md->kvd.is_f32 ? 4 : md->kvd.i8 ? 1 + 4.0 / c.head_dim : 2;
     const double kvb = kv_positions * 2.0 * c.n_kv_heads * c.head_dim * elt;
     const double io = 2.0 * M * c.n_heads * c.head_dim * 4;
     ProfScope ps(md, st, K_ATTN_DECODE, kvb + io, 4.0 * kv_positions * c.n_heads * c.head_dim);
@@ -727,7 +734,7 @@ int mega_o_rt(const dpk_model* md, int M) {
 // per CU.
 size_t mega_lds_for(dpk_model* md, int M, int max_ctx) {
   const dpk_config& c = md->cfg;
-  if ((c.flags & DPK_FLAG_DECODE_MULTI) || !md->mega_layers) return 0;
+  if ((c.flags & (DPK_FLAG_DECODE_MULTI | DPK_FLAG_KV_I8)) || !md->mega_layers) return 0;
   if (c.head_dim != 128 || c.n_heads % c.n_kv_heads) return 0;
   const int G = c.n_heads / c.n_kv_heads;
   if (G != 1 && G != 2 && G != 4) return 0;
@@ -953,7 +960,7 @@ dpk_status forward_gemm(dpk_model* md, int M, int start, int seq, bool want_head
   // the QKV epilogue takes QK-norm / RoPE / the cache write when the
   // projection runs on full 256 x 256 tiles (a narrow-tile grid splits a head
   // over two waves)
-  const bool qkv_fused = d == 128 && !gemm_prefers_narrow(M, md->Nqkv, md->n_cu);
+  const bool qkv_fused = d == 128 && !gemm_prefers_narrow(M, md->Nqkv, md->n_cu) && !md->kvd.i8;
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& L = md->layers[l];
     {
@@ -1092,6 +1099,8 @@ dpk_status dpk_create(const dpk_config* cfg, dpk_model** out) {
   if (c.weight_format != DPK_FMT_F32 && c.head_dim != 128) return fail(DPK_EINVAL, "non-f32 formats need head_dim 128");
   if (c.weight_format != DPK_FMT_F32 && !c.qk_norm) return fail(DPK_EINVAL, "non-f32 formats need qk_norm");
   if (c.weight_format != DPK_FMT_F32 && c.vocab % 64) return fail(DPK_EINVAL, "non-f32 formats need vocab % 64 == 0");
+  if ((c.flags & DPK_FLAG_KV_I8) && c.weight_format == DPK_FMT_F32)
+    return fail(DPK_EINVAL, "the int8 KV cache needs a non-f32 weight format");
   if (c.max_batch < 1 || c.max_seq < 1 || c.max_rows < SKINNY_MAX)
     return fail(DPK_EINVAL, "max_batch, max_seq >= 1 and max_rows >= 16 required");
   if (!(c.rms_eps >= 0.0f) || !(c.rope_theta > 0.0)) return fail(DPK_EINVAL, "bad eps / theta");
@@ -1133,6 +1142,8 @@ dpk_status dpk_bind_workspace(dpk_model* md, void* kv, void* scratch, void* prep
   md->kvd.n_kv = c.n_kv_heads;
   md->kvd.max_seq = kv_seq(c);
   md->kvd.d = c.head_dim;
+  md->kvd.i8 = (c.flags & DPK_FLAG_KV_I8) ? 1 : 0;
+  md->kvd.scales = md->kvd.i8 ? (float*)((char*)kv + up(kv_code_bytes(c))) : nullptr;
   md->rope_cos = (float*)(s + L.rope_cos);
   md->rope_sin = (float*)(s + L.rope_sin);
   md->rows_dev = (RowParam*)(s + L.rows);

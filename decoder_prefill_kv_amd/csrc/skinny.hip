@@ -567,6 +567,10 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(SkinnyArgs a) {
       const RowParam rp = a.rows_param[m];
       const float* f = fin + m * rows;
       if (seg == 2) {  // v: V^T layout [d][max_seq]
+        if (a.kv.i8) {  // int8 cache (d == 128): wave 0 quantizes the vector
+          if (tid < 64) kv_put_i8(a.kv, rp.seq, a.layer, 1, head, rp.pos, f[tid], f[tid + 64], tid);
+          continue;
+        }
         for (int e = tid; e < d; e += THREADS) {
           const size_t off = kv_offset(a.kv, rp.seq, a.layer, 1, head, e, rp.pos);
           kv_store(a.kv, off, f[e]);
@@ -591,6 +595,8 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(SkinnyArgs a) {
           float* q = a.qout + ((size_t)m * a.n_heads + head) * d;
           q[e] = y1;
           q[e + hd2] = y2;
+        } else if (a.kv.i8) {  // (d == 128: wave 0, one element pair per lane)
+          kv_put_i8(a.kv, rp.seq, a.layer, 0, head, rp.pos, y1, y2, tid);
         } else {
           kv_store(a.kv, kv_offset(a.kv, rp.seq, a.layer, 0, head, 0, rp.pos) + e, y1);
           kv_store(a.kv, kv_offset(a.kv, rp.seq, a.layer, 0, head, 0, rp.pos) + e + hd2, y2);

@@ -101,6 +101,16 @@ typedef struct {
  * a device error (dpk_check_device_errors) instead of hanging.  Callers that
  * share the GPU with other kernels may prefer this flag. */
 #define DPK_FLAG_DECODE_MULTI 2
+/* KV cache as int8: each position's K and V head vectors are int8 codes with one
+ * fp32 scale, s = max|x| / 127, q = round(x / s) clipped to +-127, read back as s * q
+ * (Butter notes, architecture: an affine-quantized KV cache; here its offset is
+ * zero).  Needs a non-fp32 weight format (head_dim 128).  The kv buffer then holds
+ * the codes in the fp16 cache's element layout at one byte each, followed (at a
+ * 256-byte boundary) by the scales [max_batch][n_layers][K|V][n_kv][S] fp32.
+ * Decode steps run one launch per kernel (the persistent step keeps the fp16
+ * cache), and the prefill's QKV projection hands QK-norm / RoPE and the cache
+ * write to a separate kernel. */
+#define DPK_FLAG_KV_I8 4
 
 /*
  * One weight tensor.  Names (transformers-style):

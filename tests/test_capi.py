@@ -93,6 +93,23 @@ def test_int8_code_formats_prep_holds_fp16_operands_and_fragment_order_codes(dpk
         dpk.destroy(h)
 
 
+def test_int8_kv_cache_sizes_and_format_check(dpk):
+    """int8 KV cache: one byte per cached element, then (at a 256-byte
+    boundary) one fp32 scale per position of every slab; refused for fp32
+    weights."""
+    h = dpk.create(cfg_ok(dpk, flags=dpk.FLAG_KV_I8))
+    try:
+        kv, sc, pr = dpk.workspace_size(h)
+        codes = 2 * 2 * 2 * 8 * 640 * 128
+        assert kv == (codes + 255) // 256 * 256 + 2 * 2 * 2 * 8 * 640 * 4
+    finally:
+        dpk.destroy(h)
+    with pytest.raises(dpk.DpkError) as e:
+        dpk.create(cfg_ok(dpk, weight_format=dpk.FMT_F32, head_dim=64, n_heads=4, n_kv_heads=2, hidden=256,
+                          intermediate=768, vocab=4096, qk_norm=0, flags=dpk.FLAG_KV_I8))
+    assert e.value.status == dpk.DPK_EINVAL
+
+
 def test_fp32_format_needs_no_prep(dpk):
     h = dpk.create(cfg_ok(dpk, weight_format=dpk.FMT_F32, head_dim=64, n_heads=4, n_kv_heads=2, hidden=256,
                           intermediate=768, vocab=4096, qk_norm=0, tied_embedding=0))

@@ -59,6 +59,11 @@ CASES = [
     ("q06b_q8-L2-stream", synth.Q06B_Q8.with_(n_layers=2), 37, 6, dict(flags=STREAM)),
     ("q8b_q8-L1-v4096-gemm", synth.Q8B_Q8.with_(n_layers=1, vocab=4096), 21, 5, {}),
     ("q8b_q8-L2-v4096-chunked", synth.Q8B_Q8.with_(n_layers=2, vocab=4096), 300, 4, dict(max_rows=128)),
+    # int8 KV cache: prefill (GEMM, streamed, chunked over the cache), decode; bf16 and Q8 weights
+    ("q06b-kvi8-L2-gemm", synth.Q06B.with_(n_layers=2, kv_i8=True), 40, 8, {}),
+    ("q06b-kvi8-L2-stream", synth.Q06B.with_(n_layers=2, kv_i8=True), 37, 6, dict(flags=STREAM)),
+    ("q8b-kvi8-L1-v4096-chunked", synth.Q8B.with_(n_layers=1, vocab=4096, kv_i8=True), 300, 6, dict(max_rows=128)),
+    ("q06b_q8-kvi8-L2-gemm", synth.Q06B_Q8.with_(n_layers=2, kv_i8=True), 40, 8, {}),
     # GGUF-style Q4_0 blocks: the same paths with 4-bit codes around 8 and fp16 scales
     ("q06b_q40-L2-gemm", synth.Q06B_Q40.with_(n_layers=2), 40, 8, {}),
     ("q06b_q40-L2-stream", synth.Q06B_Q40.with_(n_layers=2), 37, 6, dict(flags=STREAM)),
@@ -145,6 +150,7 @@ PATH_CASES = [
     ("q06b_i8-L1", synth.Q06B_I8.with_(n_layers=1), False),
     ("q06b_q8-L1", synth.Q06B_Q8.with_(n_layers=1), False),
     ("q06b_q40-L1", synth.Q06B_Q40.with_(n_layers=1), False),
+    ("q06b-kvi8-L1", synth.Q06B.with_(n_layers=1, kv_i8=True), False),
 ]
 
 
@@ -167,6 +173,61 @@ def test_decode_path_taken(dpk, name, cfg, persistent):
     assert ("decode.step" in stats) == persistent, sorted(stats)
     if persistent:
         assert not any(k.startswith("gemv.") or k.startswith("attn.") for k in stats), sorted(stats)
+
+
+KV_I8_CASES = [
+    # (name, config, decoder flags): the cache writers are the prefill rows kernel
+    # and the decode attention (bf16), the streamed prefill's per-row kernel, and
+    # the int8-code GEMV's QKV epilogue (Q8 weights)
+    ("bf16-gemm", synth.Q06B.with_(n_layers=2, kv_i8=True), 0),
+    ("bf16-stream", synth.Q06B.with_(n_layers=2, kv_i8=True), STREAM),
+    ("q8-gemm", synth.Q06B_Q8.with_(n_layers=2, kv_i8=True), 0),
+]
+
+
+@pytest.mark.parametrize("name,cfg,flags", KV_I8_CASES, ids=[c[0] for c in KV_I8_CASES])
+def test_int8_kv_cache_holds_the_oracle_codes(dpk, name, cfg, flags):
+    """The int8 cache itself, read back from the device: layer 0's keys and
+    values (which do not depend on the cache) after a 40-token prefill and 4
+    decode steps, against the oracle's quantized cache -- scales within fp32
+    rounding, codes equal but for rare +-1 at near-ties."""
+    w = synth.make_weights(cfg, 0)
+    P, N = 40, 4
+    prompt = synth.prompt_ids(cfg, P, 0)
+    m, run = oracle_greedy(cfg, w, prompt, N)
+    dec = dpk.Decoder(cfg, w, max_batch=1, max_seq=P + N + 8, max_rows=64, flags=flags)
+    lg, am = dec.logits_buffer(1), dec.argmax_buffer(1)
+    dec.prefill(0, [int(t) for t in prompt], lg, am)
+    for s in range(N):
+        dec.decode_step([0], [run["ids"][s]], [P + s], am, lg)
+    torch.cuda.synchronize()
+    dpk.check_device_errors(dec.handle)
+    raw = dec.kv.cpu().numpy()
+    dec.close()
+    L, Hkv, d = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
+    S = (P + N + 8 + 63) // 64 * 64
+    n = L * 2 * Hkv * S * d  # one sequence slot
+    codes = raw[:n].view(np.int8).reshape(L, 2, Hkv, S, d)
+    off = (n + 255) // 256 * 256
+    scales = raw[off:off + L * 2 * Hkv * S * 4].view(np.float32).reshape(L, 2, Hkv, S)
+    T = P + N
+    for which, ref in ((0, run["cache"].k[0]), (1, run["cache"].v[0])):
+        ref = ref[:, :T, :].numpy()                                   # [Hkv, T, d], values s * q
+        gs = scales[0, which, :, :T].astype(np.float64)              # [Hkv, T]
+        gq = codes[0, which] if which == 0 else codes[0, which].reshape(Hkv, d, S).transpose(0, 2, 1)
+        gq = gq[:, :T, :].astype(np.int64)
+        rs = np.abs(ref).max(axis=2) / 127.0                         # the oracle's scale (s * 127 = max |s q|)
+        # bf16 weights are exact in the fp16 prefill copy; Q8's s * q is rounded
+        # to fp16 there (2^-11 relative per weight), which moves k and v as much
+        rtol = 2e-5 if cfg.weight_format == "bf16" else 2e-3
+        rel = float((np.abs(gs - rs) / np.maximum(rs, 1e-30)).max())
+        print("\n[kv-i8] %s %s: scale rel. diff %.3g" % (name, "KV"[which], rel), flush=True)
+        assert rel <= rtol, "%s %d: scales %.3g" % (name, which, rel)
+        rq = np.rint(ref / np.where(rs > 0, rs, 1.0)[..., None]).astype(np.int64)
+        diff = np.abs(gq - rq)
+        print("[kv-i8] %s %s: codes off by one %.4f" % (name, "KV"[which], float(diff.mean())), flush=True)
+        assert diff.max() <= 1 and diff.mean() < (5e-3 if cfg.weight_format == "bf16" else 5e-2), \
+            "%s %d: codes differ (%d, %.4f)" % (name, which, int(diff.max()), float(diff.mean()))
 
 
 def test_prefill_without_outputs_then_decode(dpk):
@@ -195,6 +256,8 @@ VERIFY_CASES = [
     ("q06b_i8-L2-k5", synth.Q06B_I8.with_(n_layers=2), 70, 5),
     ("q06b_q8-L2-k5", synth.Q06B_Q8.with_(n_layers=2), 70, 5),
     ("q06b_q40-L2-k5", synth.Q06B_Q40.with_(n_layers=2), 70, 5),
+    ("q06b-kvi8-L2-k5", synth.Q06B.with_(n_layers=2, kv_i8=True), 70, 5),
+    ("q8b-kvi8-L1-v4096-k15", synth.Q8B.with_(n_layers=1, vocab=4096, kv_i8=True), 500, 15),
 ]
 
 
@@ -298,6 +361,7 @@ BATCH16_CASES = [
     ("q06b_i8-L2-v4096-M16", synth.Q06B_I8.with_(n_layers=2, vocab=4096), [40 + 13 * b for b in range(16)]),
     ("q06b_q8-L2-v4096-M16", synth.Q06B_Q8.with_(n_layers=2, vocab=4096), [40 + 13 * b for b in range(16)]),
     ("q06b_q40-L2-v4096-M16", synth.Q06B_Q40.with_(n_layers=2, vocab=4096), [40 + 13 * b for b in range(16)]),
+    ("q06b-kvi8-L2-v4096-M16", synth.Q06B.with_(n_layers=2, vocab=4096, kv_i8=True), [40 + 13 * b for b in range(16)]),
 ]
 
 
