@@ -141,6 +141,8 @@ DPK_DEV void embed_phase(const MegaArgs& a, const RowParam* rows, int wg, int nw
           const uint32_t word = ((const uint32_t*)a.emb)[(size_t)tok * (a.H / 8) + col / 8];
           const size_t gi = (size_t)tok * (a.H / 64) + col / 64;
           v = bf16_to_f32(a.emb_sc[gi]) * (float)((word >> (4 * (col & 7))) & 0xFu) + bf16_to_f32(a.emb_bi[gi]);
+        } else if (a.fmt == W_I8) {  // int8 with one bf16 scale per row
+          v = bf16_to_f32(a.emb_sc[tok]) * (float)((const int8_t*)a.emb)[(size_t)tok * a.H + col];
         } else {
           v = bf16_to_f32(((const uint16_t*)a.emb)[(size_t)tok * a.H + col]);
         }
@@ -830,9 +832,9 @@ __global__ __launch_bounds__(MT, 1) void decode_step_kernel(MegaArgs a) {
   }
 }
 
-// Built variants: bf16 at 256 columns per iteration for G = 1, 2, 4; bf16
-// and 4-bit at 128 columns for G = 2, 4; bf16 with and without the fused O
-// projection.
+// Built variants: bf16 and int8 (one scale per row) at 256 columns per
+// iteration for G = 1, 2, 4; bf16 and 4-bit at 128 columns for G = 2, 4; bf16
+// with and without the fused O projection.
 template <bool FO>
 const void* mega_kernel_fo(int G, int fmt, bool small) {
   if (fmt == W_BF16 && !small) {
@@ -842,6 +844,12 @@ const void* mega_kernel_fo(int G, int fmt, bool small) {
       case 4: return (const void*)decode_step_kernel<4, W_BF16, false, FO>;
       default: return nullptr;
     }
+  }
+  if (fmt == W_I8 && !small && !FO) {  // int8 codes, one scale per row: the 256-column variant only
+    if (G == 1) return (const void*)decode_step_kernel<1, W_I8, false, false>;
+    if (G == 2) return (const void*)decode_step_kernel<2, W_I8, false, false>;
+    if (G == 4) return (const void*)decode_step_kernel<4, W_I8, false, false>;
+    return nullptr;
   }
   if (!small) return nullptr;
   if (fmt == W_BF16) {

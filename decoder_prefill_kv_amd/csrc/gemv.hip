@@ -62,6 +62,7 @@ __global__ void tile_q4_kernel(const uint32_t* codes, const uint16_t* sc, const 
 // Waves per workgroup: 8 when K splits into eight parts of whole iterations,
 // else 4.
 int gemv_waves(int K, int tiles, int fmt) {
+  if (fmt == W_I8) return K % (8 * 64 * (8 / tiles)) == 0 ? 8 : 4;  // 64 (8/T) columns per iteration on 8 waves
   const int per_iter = (fmt == W_Q4) ? 64 * (4 / tiles > 0 ? 4 / tiles : 1) : 32 * (8 / tiles);
   return (K % (8 * per_iter) == 0 && K / 8 >= per_iter) ? 8 : 4;
 }
@@ -107,6 +108,10 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
   const int W = gemv_waves(a.K, a.tiles, a.fmt);
   const size_t lds = gemv_lds_bytes(a.M, a.K, a.tiles, a.fmt);
   if (lds > 64 * 1024) return hipErrorInvalidValue;
+  if (a.fmt != W_BF16) {  // each wave's K part must hold whole iterations (64 GU columns, as gemv_body sets GU)
+    const int gu = (a.fmt == W_I8 && W == 8) ? 8 / a.tiles : (4 / a.tiles > 0 ? 4 / a.tiles : 1);
+    if ((a.K / W) % (64 * gu) != 0 || a.K / W < 64 * gu) return hipErrorInvalidValue;
+  }
 #define DPK_GEMV_CASE(F, T, WV)                                                            \
   if (a.fmt == F && a.tiles == T && W == WV) {                                            \
     launch((gemv_kernel<F, T, WV>), grid, dim3(64 * WV), lds, stream, a);    \
@@ -124,6 +129,12 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
   DPK_GEMV_CASE(W_Q4, 1, 8)
   DPK_GEMV_CASE(W_Q4, 2, 8)
   DPK_GEMV_CASE(W_Q4, 4, 8)
+  DPK_GEMV_CASE(W_I8, 1, 4)
+  DPK_GEMV_CASE(W_I8, 2, 4)
+  DPK_GEMV_CASE(W_I8, 4, 4)
+  DPK_GEMV_CASE(W_I8, 1, 8)
+  DPK_GEMV_CASE(W_I8, 2, 8)
+  DPK_GEMV_CASE(W_I8, 4, 8)
 #undef DPK_GEMV_CASE
   return hipErrorInvalidValue;
 }

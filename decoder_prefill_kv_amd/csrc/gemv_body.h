@@ -168,11 +168,14 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
   // bf16: k-steps of 32 per iteration (XG holds its activations in registers
   // as well, so a one-tile XG wave loads half as much per iteration)
   constexpr int U = (XG && T == 1 && !KI) ? 4 : gemv_bf16_u<T, KI>();
-  constexpr int GU = KI ? KI / 64 : 4 / T > 0 ? 4 / T : 1;  // 4-bit: groups of 64 per iteration
+  // 4-bit: groups of 64 per iteration; int8 on eight waves: blocks of 64
+  // columns, twice the 4-bit count (the same bytes per iteration)
+  constexpr int GU = KI ? KI / 64 : (FMT == W_I8 && WAVES == 8) ? 8 / T : 4 / T > 0 ? 4 / T : 1;
   static_assert(KI % 64 == 0, "whole 4-bit groups per iteration");
   const int nit = (FMT == W_BF16) ? kq / (32 * U) : kq / (64 * GU);
   const unsigned char* wp[T];   // this wave's stream inside each 16-row tile
-  const unsigned char* sbp[T];  // 4-bit: scale/bias stream
+  const unsigned char* sbp[T];  // 4-bit: scale/bias stream; int8: the tile's row scales (bf16)
+  uint32_t rsc[T][2];           // int8: bf16 scales of rows 4 j4 .. 4 j4 + 3 of each tile
   auto set_tile = [&](int tile) {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -181,6 +184,11 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
       if (FMT == W_BF16) {
         // block (rt, s) at ((rt * K/32) + s) * 1024; this wave starts at s = k0/32
         wp[t] = (const unsigned char*)a.w[seg] + (rt * (KF / 32) + (KO + k0) / 32) * 1024 + lane * 16;
+      } else if (FMT == W_I8) {
+        // int8 codes block (rt, g) (16 rows x 64 columns) at ((rt * K/64) + g) * 1024,
+        // lane l's 16 bytes: MFMA k-steps 2g and 2g + 1 of row l % 16
+        wp[t] = (const unsigned char*)a.w[seg] + (rt * (KF / 64) + (KO + k0) / 64) * 1024 + lane * 16;
+        sbp[t] = (const unsigned char*)a.sb[seg] + (rt * 16 + 4 * j4) * 2;
       } else {
         // codes block (rt, g) at ((rt * K/64) + g) * 512; scales (rt, g) at * 64
         wp[t] = (const unsigned char*)a.w[seg] + (rt * (KF / 64) + (KO + k0) / 64) * 512 + lane * 8;
@@ -211,6 +219,14 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
         xl[u] = *(const u32x4*)(a.xb_lo + xrow + ((size_t)(it * U + u) << 9));
       }
     }
+  };
+  // int8: GU blocks of 64 columns per iteration, into the u32x4 buffers
+  auto load_i8 = [&](u32x4 (&q)[T][GU], int it) {
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int u = 0; u < GU; ++u)
+        q[t][u] = __builtin_nontemporal_load(gmem((const u32x4*)(wp[t] + (size_t)(it * GU + u) * 1024)));
   };
   auto load_q4 = [&](u32x2 (&c)[T][GU], u32x4 (&sv)[T][GU], int it) {
 #pragma unroll
@@ -262,6 +278,15 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
     if constexpr (FMT == W_BF16) {
       load_bf(b0, xh0, xl0, 0);
       if (nit > 1) load_bf(b1, xh1, xl1, 1);
+    } else if constexpr (FMT == W_I8) {
+      load_i8(s0, 0);
+      if (nit > 1) load_i8(s1, 1);
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const u32x2 r = *gmem((const u32x2*)sbp[t]);
+        rsc[t][0] = r[0];
+        rsc[t][1] = r[1];
+      }
     } else {
       load_q4(c0, s0, 0);
       if (nit > 1) load_q4(c1, s1, 1);
@@ -449,6 +474,38 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
     }
   };
 
+  // int8: lane (row r16, k group j4) holds codes 32 h + 8 j4 .. + 7 of each
+  // 64-column block (h = 0, 1); each becomes the exact bf16 value q (an
+  // integer of at most 8 bits is exact in fp32 and in the upper half of its
+  // bits), the row scale multiplies the finished tile
+  auto compute_i8 = [&](f32x4 (&acc)[T], const u32x4 (&q)[T][GU], int it) {
+#pragma unroll
+    for (int u = 0; u < GU; ++u) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        u32x4 bh = {0u, 0u, 0u, 0u}, bl = {0u, 0u, 0u, 0u};
+        const int kl = (it * GU + u) * 64 + 32 * h + 8 * j4;
+        if (col_on) {
+          bh = *(const u32x4*)(xs_hi + r16 * xstride + kl);
+          bl = *(const u32x4*)(xs_lo + r16 * xstride + kl);
+        }
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const uint32_t w0 = h ? q[t][u][2] : q[t][u][0], w1 = h ? q[t][u][3] : q[t][u][1];
+          uint32_t f[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            f[e] = __float_as_uint((float)(int)(int8_t)(((e < 4 ? w0 : w1) >> (8 * (e & 3))) & 0xFFu));
+          const u32x4 av = {__builtin_amdgcn_perm(f[1], f[0], 0x07060302u), __builtin_amdgcn_perm(f[3], f[2], 0x07060302u),
+                            __builtin_amdgcn_perm(f[5], f[4], 0x07060302u), __builtin_amdgcn_perm(f[7], f[6], 0x07060302u)};
+          const bf16x8 A = __builtin_bit_cast(bf16x8, av);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, bh), acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, bl), acc[t], 0, 0, 0);
+        }
+      }
+    }
+  };
+
   const int nb = nwg;
   float best_v[16];
   int best_i[16];
@@ -592,6 +649,18 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
         if (it + 1 < nit) compute_bf(acc, b1, xh1, xl1, it + 1);
       }
       in_pf = false;
+    } else if constexpr (FMT == W_I8) {
+      for (int it = 0; it < nit; it += 2) {
+        if (it + 1 < nit && !(two && it == 0)) load_i8(s1, it + 1);
+        compute_i8(acc, s0, it);
+        if (it + 2 < nit) load_i8(s0, it + 2);
+        if (it + 1 < nit) compute_i8(acc, s1, it + 1);
+      }
+      // the tile's row scales (lane rows 4 j4 + v), before the next tile's loads replace them
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[t][v] *= (v & 1) ? bf16hi_to_f32(rsc[t][v >> 1]) : bf16lo_to_f32(rsc[t][v >> 1]);
     } else {
       for (int it = 0; it < nit; it += 2) {
         if (it + 1 < nit && !(two && it == 0)) load_q4(c1, s1, it + 1);

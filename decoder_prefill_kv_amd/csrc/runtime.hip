@@ -499,7 +499,7 @@ GemvArgs gemv_args(dpk_model* md, int M, const float* x, int ldx, const float* s
   for (int i = 0; i < 3; ++i) {
     const LinearW& sg = segs[i < nseg ? i : nseg - 1];
     a.w[i] = sg.wt;
-    a.sb[i] = sg.sbt;
+    a.sb[i] = md->fmt == DPK_FMT_I8 ? (const void*)sg.sc : sg.sbt;  // int8: the bf16 row scales as given
     if (i < nseg) n += sg.rows;
     a.seg_end[i] = n;
     a.seg_rows[i] = sg.rows;
@@ -641,7 +641,7 @@ dpk_status forward_batch(dpk_model* md, int M, int max_ctx, const int32_t* ids_d
 
 // Can a decode step of M rows run on the whole-K GEMV kernels?
 bool decode_fits(const dpk_model* md, int M) {
-  if (md->fmt != DPK_FMT_BF16 && md->fmt != DPK_FMT_Q4G64) return false;
+  if (md->fmt != DPK_FMT_BF16 && md->fmt != DPK_FMT_Q4G64 && md->fmt != DPK_FMT_I8) return false;
   const dpk_config& c = md->cfg;
   const int fmt = wfmt(md);
   for (int K : {c.hidden, c.n_heads * c.head_dim, c.intermediate}) {
@@ -703,6 +703,10 @@ int mega_variant(const dpk_model* md) {
     return 0;
   if ((md->fmt == DPK_FMT_BF16 || md->fmt == DPK_FMT_Q4G64) && H % 1024 == 0 && Qd % 1024 == 0 && I % 1024 == 0)
     return 1;
+  // int8 codes with one scale per row: 256 columns per iteration on eight waves only
+  if (md->fmt == DPK_FMT_I8 && gemv_waves(H, 1, W_I8) == 8 && gemv_waves(Qd, 1, W_I8) == 8 &&
+      gemv_waves(H, 2, W_I8) == 8 && gemv_waves(I, 1, W_I8) == 8)
+    return 0;
   return -1;
 }
 

@@ -110,6 +110,7 @@ PERSISTENT_CFGS = [
     ("h2048-g2-L2-v4096", H2048_G2, 250),
     ("q8b-L1-v4096-ctx4100", synth.Q8B.with_(n_layers=1, vocab=4096), 4080),
     ("q06b_q4-L1-v4096-ctx4100", synth.Q06B_Q4.with_(n_layers=1, vocab=4096), 4080),
+    ("q8b_i8-L2-v4096", synth.Q8B_I8.with_(n_layers=2, vocab=4096), 250),    # int8 codes, one scale per row
 ]
 
 
@@ -151,6 +152,7 @@ PATH_CASES = [
     ("q06b_q8-L1", synth.Q06B_Q8.with_(n_layers=1), False),
     ("q06b_q40-L1", synth.Q06B_Q40.with_(n_layers=1), False),
     ("q06b-kvi8-L1", synth.Q06B.with_(n_layers=1, kv_i8=True), False),
+    ("q8b_i8-L1-v4096", synth.Q8B_I8.with_(n_layers=1, vocab=4096), True),
 ]
 
 
