@@ -315,6 +315,35 @@ BATCHED_PERSISTENT = [("q06b-L2", synth.Q06B.with_(n_layers=2)), ("q06b_q4-L2", 
                       ("h2048-g4-L2-v4096", H2048_G4), ("h2048-g2-L2-v4096", H2048_G2)]
 
 
+def test_batched_decode_int8_8b_rows(dpk):
+    """Two sequences of an 8B-shaped int8 model decoded together (contexts of
+    one and two chunks).  At 8B shapes the persistent step takes one row (the
+    staged activations of two do not fit its LDS), so two rows take the
+    one-launch-per-kernel path; batch-1 steps of the same model the
+    persistent one."""
+    cfg = synth.Q8B_I8.with_(n_layers=1, vocab=4096)
+    w = synth.make_weights(cfg, 0)
+    lens, N = [200, 300], 3
+    prompts = [synth.prompt_ids(cfg, L, 0, index=b) for b, L in enumerate(lens)]
+    runs = [oracle_greedy(cfg, w, p, N)[1] for p in prompts]
+    dec = dpk.Decoder(cfg, w, max_batch=2, max_seq=320, max_rows=256)
+    for b in range(2):
+        dec.prefill(b, [int(t) for t in prompts[b]])
+    lg, am = dec.logits_buffer(2), dec.argmax_buffer(2)
+    for s in range(N):
+        toks = [runs[b]["ids"][s] for b in range(2)]
+        if s == 0:
+            dpk.profile_begin(dec.handle, 10000)
+        dec.decode_step([0, 1], toks, [lens[b] + s for b in range(2)], am, lg)
+        if s == 0:
+            stats = dpk.profile_end(dec.handle)
+            assert "decode.step" not in stats and "gemv.gate_up" in stats, sorted(stats)
+        for b in range(2):
+            compare_logits(lg[b].cpu(), runs[b]["logits"][s + 1], TOL["i8"], "int8 row %d step %d" % (b, s))
+    dpk.check_device_errors(dec.handle)
+    dec.close()
+
+
 @pytest.mark.parametrize("name,cfg", BATCHED_PERSISTENT, ids=[c[0] for c in BATCHED_PERSISTENT])
 def test_batched_persistent_decode_long_contexts(dpk, name, cfg):
     """Three sequences decoded together through the persistent step (M = 3
