@@ -758,7 +758,7 @@ template <int G, int FMT, bool SMALL, bool FO>
 __global__ __launch_bounds__(MT, 1) void decode_step_kernel(MegaArgs a) {
   // (the lm_head of a narrow model goes in 32-row tiles: one 128-column
   // iteration per 16 rows would leave a wave a single 4 KB load in flight)
-  constexpr int KI = SMALL ? 128 : 0, TQ = SMALL ? 1 : 2, TH = SMALL ? 2 : 1;
+  constexpr int KI = SMALL ? 128 : 0, TQ = SMALL ? 1 : 2, TH = SMALL ? 2 : (FMT == W_I8 ? MEGA_HEAD_I8_TILES : 1);
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int wg = blockIdx.x, nwg = gridDim.x;
   Barrier bar{a.bar, a.bar + MEGA_BAR_ABORT, (unsigned)nwg, 0u};

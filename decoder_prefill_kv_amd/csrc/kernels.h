@@ -99,6 +99,9 @@ struct SkinnyArgs {
 };
 
 size_t skinny_lds_bytes(int M, int kchunk, int rows, int fmt);
+// 16-row tiles per lm_head tile of the persistent step with int8 weights
+// (measured, 8B: 1 / 2 / 4 -> head phase 130.4 / 112.6 / 110.7 us)
+constexpr int MEGA_HEAD_I8_TILES = 2;
 
 // ---- decode GEMV with the whole K in one workgroup (gemv.hip)
 // Weights are given in the re-tiled fragment layout (launch_tile_bf16 /

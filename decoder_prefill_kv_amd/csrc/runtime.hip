@@ -655,6 +655,7 @@ bool decode_fits(const dpk_model* md, int M) {
 // parameters are in md->rows_dev: every layer is QKV GEMV -> attention (with
 // QK-norm, RoPE and the KV write) -> O GEMV + residual -> gate/up GEMV +
 // SwiGLU -> down GEMV + residual; then the lm_head with the greedy argmax.
+constexpr int HEAD_I8_TILES = 4;  // the one-launch-per-kernel int8 lm_head's 16-row tiles per tile
 dpk_status forward_decode(dpk_model* md, int M, int max_ctx, const int32_t* ids_dev, float* logits, int32_t* argmax,
                           hipStream_t st, double kv_positions) {
   const dpk_config& c = md->cfg;
@@ -687,8 +688,9 @@ dpk_status forward_decode(dpk_model* md, int M, int max_ctx, const int32_t* ids_
       return s;
   }
   float* dst = logits ? logits : md->sink;
-  return gemv(md, K_GEMV_HEAD, M, md->h, H, md->sq, sq_nb, md->final_norm, &md->head, 1, EPI_HEAD, false, 1, dst,
-              c.vocab, nullptr, argmax, st);
+  // (int8: 64-row tiles; fewer tiles per workgroup measured faster: 0.6B head 78.8 -> 46.3 us)
+  return gemv(md, K_GEMV_HEAD, M, md->h, H, md->sq, sq_nb, md->final_norm, &md->head, 1, EPI_HEAD, false,
+              md->fmt == DPK_FMT_I8 ? HEAD_I8_TILES : 1, dst, c.vocab, nullptr, argmax, st);
 }
 
 // GEMV tiling of the persistent decode kernel for the loaded model: 0 when
@@ -755,7 +757,7 @@ size_t mega_lds_for(dpk_model* md, int M, int max_ctx) {
   }
   for (size_t b : {gemv_lds_bytes_waves(M, H, var ? 1 : 2, fmt, 8), gemv_lds_bytes_waves(M, Qd, 1, fmt, 8),
                    gemv_lds_bytes_waves(M, H, 2, fmt, 8), gemv_lds_bytes_waves(M, I, 1, fmt, 8),
-                   gemv_lds_bytes_waves(M, H, 1, fmt, 8)})
+                   gemv_lds_bytes_waves(M, H, fmt == W_I8 ? MEGA_HEAD_I8_TILES : 1, fmt, 8)})
     lds = b > lds ? b : lds;
   // + the staged layer / head arguments and row parameters, + (bf16) the
   // GEMVs' prefetch slots
