@@ -166,8 +166,10 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
   auto tile_rt = [&](int tile, int t, int& seg) -> size_t { return gemv_tile_rt<T>(a, tile, t, seg); };
 
   // bf16: k-steps of 32 per iteration (XG holds its activations in registers
-  // as well, so a one-tile XG wave loads half as much per iteration)
-  constexpr int U = (XG && T == 1 && !KI) ? 4 : gemv_bf16_u<T, KI>();
+  // as well: a one-tile XG wave loads half as much per iteration, a two-tile
+  // one a quarter -- measured faster for the 16-row QKV and lm_head GEMVs, and
+  // it leaves the 8-wave variant without register spills)
+  constexpr int U = (XG && T == 1 && !KI) ? 4 : (XG && T == 2 && !KI) ? 2 : gemv_bf16_u<T, KI>();
   // 4-bit: groups of 64 per iteration; int8 on eight waves: blocks of 64
   // columns, twice the 4-bit count (the same bytes per iteration)
   constexpr int GU = KI ? KI / 64 : (FMT == W_I8 && WAVES == 8) ? 8 / T : 4 / T > 0 ? 4 / T : 1;
