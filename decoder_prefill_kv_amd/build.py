@@ -8,7 +8,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "_dpk.so")
-SOURCES = ["runtime.hip", "skinny.hip", "gemv.hip", "attn_decode.hip", "attn_decode_mfma.hip", "misc.hip", "gemm.hip", "attn_prefill.hip", "decode_step.hip", "sample.hip"]
+SOURCES = ["runtime.hip", "skinny.hip", "gemv.hip", "attn_decode.hip", "attn_decode_mfma.hip", "misc.hip", "gemm.hip", "attn_prefill.hip", "decode_step.hip", "decode_step_kv8.hip", "sample.hip"]
 BUILD = os.path.join(HERE, "_build")
 # per-source additions: the int8 GEMV keeps its MFMA results in ordinary VGPRs
 # (its block scales read each k-step's result, which from AGPRs costs a copy)

@@ -45,13 +45,6 @@ DPK_DEV void split_f16(float x, _Float16& hi, _Float16& lo) {
   lo = (_Float16)(x - (float)hi);
 }
 
-// 8 int8 codes -> fp16 1152 + q (exact)
-DPK_DEV u32x4 codes_f16(u32x2 w) {
-  const uint32_t u0 = w.x ^ 0x80808080u, u1 = w.y ^ 0x80808080u;
-  return u32x4{__builtin_amdgcn_perm(0x64646464u, u0, 0x04010400u), __builtin_amdgcn_perm(0x64646464u, u0, 0x04030402u),
-               __builtin_amdgcn_perm(0x64646464u, u1, 0x04010400u), __builtin_amdgcn_perm(0x64646464u, u1, 0x04030402u)};
-}
-
 template <int D, bool RAW, bool KV8>
 __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArgs a) {
   static_assert(!KV8 || D == 128, "int8 cache: head_dim 128");
@@ -340,7 +333,7 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
       for (int ks = 0; ks < D / 32; ++ks) {
         f16x8 A;
         if constexpr (KV8)
-          A = __builtin_bit_cast(f16x8, codes_f16(kf[t][ks]));
+          A = __builtin_bit_cast(f16x8, kv_codes_f16(kf[t][ks]));
         else
           A = __builtin_bit_cast(f16x8, kf[t][ks]);
         const f16x8 qh = *(const f16x8*)&qh16[r16][32 * ks + 8 * j4];
@@ -415,7 +408,7 @@ __global__ __launch_bounds__(THREADS) void attn_decode_mfma_kernel(AttnDecodeArg
     for (int dt = 0; dt < D / 16; ++dt) {
       u32x4 w;
       if constexpr (KV8)
-        w = codes_f16(vf[dt]);
+        w = kv_codes_f16(vf[dt]);
       else
         w = vf[dt] & vm;
       const f16x8 A = __builtin_bit_cast(f16x8, w);

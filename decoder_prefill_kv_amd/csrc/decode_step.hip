@@ -432,7 +432,13 @@ DPK_DEV bool o_phase(const MegaArgs& a, const RowParam* rows, int layer, const G
 
 // Returns whether the gate/up GEMV's LDS-prefetched iteration was loaded
 // here (FO: o_phase).
-template <int G, bool FO, int KI, typename Sync>
+// KV8: the cache holds int8 codes with one fp32 scale per position and head
+// vector.  The codes enter the MFMAs as the fp16 integers 1152 + q; S starts
+// from -1152 times the column's sum of the q parts and is multiplied by the
+// keys' scales; the values' scales are folded into P (P'), and 1152 times the
+// column's sum of P' comes off O at the end.  The new position is quantized
+// here (per head vector, as the cache stores it) and attended in that form.
+template <int G, bool FO, int KI, bool KV8, typename Sync>
 DPK_DEV bool attn_phase(const MegaArgs& a, const RowParam* rows, int layer, const uint16_t* qn, const uint16_t* kn,
                         const GemvArgs* Lo, const GemvArgs* Lgu, unsigned char* lds, unsigned char* pf,
                         const Barrier& bar, int wg, int nwg, Sync&& sync) {
@@ -445,6 +451,14 @@ DPK_DEV bool attn_phase(const MegaArgs& a, const RowParam* rows, int layer, cons
   float* wst = (float*)lds + G * D + 2 * D;  // [AW][2][G]
   float* ow = wst + AW * 2 * G;         // [AW][D][G]
   int* flag = (int*)(ow + AW * D * G);
+  // KV8, in the 4 D bytes between vn16 and wst: the new position's codes,
+  // the columns' q sums and the new key's / value's scales
+  int8_t* knew8 = (int8_t*)(vn16 + D);  // [D]
+  int8_t* vnew8 = knew8 + D;            // [D]
+  float* qsum = (float*)(vnew8 + D);    // [16]
+  float* newsc = qsum + 16;             // [2]
+  using Frag = typename std::conditional<KV8, u32x2, u32x4>::type;  // 8 cache elements
+  using Elt = typename std::conditional<KV8, int8_t, _Float16>::type;
 
   const int tid = opaque_tid(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform over the wave
@@ -455,8 +469,9 @@ DPK_DEV bool attn_phase(const MegaArgs& a, const RowParam* rows, int layer, cons
   // K tile t row r is position 8 (r / 4) + 4 t + r % 4 of the wave's 32, so the
   // S accumulators give lane group j4 positions 8 j4 .. + 7 (its k range of P^T
   // in the P V product) and V^T is read as one 8-position group per lane
-  u32x4 kf[2][D / 32];
-  u32x4 vf[D / 16];
+  Frag kf[2][D / 32];
+  Frag vf[D / 16];
+  f32x4 sc8[4];  // KV8: scales of the lane's 8 positions (its V group): keys, then values
   float cs = 0.f, sn = 0.f;  // this wave's RoPE values
   uint16_t gr0 = 0, gr1 = 0;  // and its QK-norm gains (bf16)
 
@@ -470,8 +485,8 @@ DPK_DEV bool attn_phase(const MegaArgs& a, const RowParam* rows, int layer, cons
     const int ctx = rp.pos + 1;
     const int c0 = chunk * ACH, c1 = min(ctx, c0 + ACH);
     const int wp0 = c0 + 32 * wave;
-    const _Float16* Kb = (const _Float16*)a.kv.base + kv_slab(a.kv, rp.seq, layer, 0, g);
-    const _Float16* Vb = (const _Float16*)a.kv.base + kv_slab(a.kv, rp.seq, layer, 1, g);
+    const Elt* Kb = (const Elt*)a.kv.base + kv_slab(a.kv, rp.seq, layer, 0, g);
+    const Elt* Vb = (const Elt*)a.kv.base + kv_slab(a.kv, rp.seq, layer, 1, g);
     // unconditional loads: positions past the context read the last one's
     // address (K rows are masked in S, V groups where they are used); an
     // 8-position group stays inside the slab row (max_seq % 64 == 0)
@@ -480,11 +495,19 @@ DPK_DEV bool attn_phase(const MegaArgs& a, const RowParam* rows, int layer, cons
     for (int t = 0; t < 2; ++t) {
       const int p = min(wp0 + 8 * (r16 >> 2) + 4 * t + (r16 & 3), plast);
 #pragma unroll
-      for (int s = 0; s < D / 32; ++s) kf[t][s] = *(const u32x4*)(Kb + (size_t)p * D + 32 * s + 8 * j4);
+      for (int s = 0; s < D / 32; ++s) kf[t][s] = *(const Frag*)(Kb + (size_t)p * D + 32 * s + 8 * j4);
     }
     const int p8 = min(wp0 + 8 * j4, plast & ~7);
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) vf[dt] = *(const u32x4*)(Vb + (size_t)(dt * 16 + r16) * a.kv.max_seq + p8);
+    for (int dt = 0; dt < D / 16; ++dt) vf[dt] = *(const Frag*)(Vb + (size_t)(dt * 16 + r16) * a.kv.max_seq + p8);
+    if constexpr (KV8) {  // (a group past the context reads the last whole group's scales: masked)
+      const float* Ksc = a.kv.scales + kv_scale_slab(a.kv, rp.seq, layer, 0, g);
+      const float* Vsc = a.kv.scales + kv_scale_slab(a.kv, rp.seq, layer, 1, g);
+      sc8[0] = *(const f32x4*)(Ksc + p8);
+      sc8[1] = *(const f32x4*)(Ksc + p8 + 4);
+      sc8[2] = *(const f32x4*)(Vsc + p8);
+      sc8[3] = *(const f32x4*)(Vsc + p8 + 4);
+    }
     // (unconditional too: a gain that does not exist reads a dummy address,
     // and the values are converted where they are used)
     cs = a.rope_cos[(size_t)rp.pos * (D / 2) + lane];
@@ -533,24 +556,97 @@ DPK_DEV bool attn_phase(const MegaArgs& a, const RowParam* rows, int layer, cons
       const float x1 = xa * r * g0, x2 = xb * r * g1;
       const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
       if (wave < G) {
-        _Float16 h, l;
+        _Float16 h, l, h2, l2;
         split_f16(y1 * a.scale * LOG2E, h, l);
         qh16[wave * D + lane] = h;
         ql16[wave * D + lane] = l;
-        split_f16(y2 * a.scale * LOG2E, h, l);
-        qh16[wave * D + lane + 64] = h;
-        ql16[wave * D + lane + 64] = l;
+        split_f16(y2 * a.scale * LOG2E, h2, l2);
+        qh16[wave * D + lane + 64] = h2;
+        ql16[wave * D + lane + 64] = l2;
+        if constexpr (KV8) {  // the column's sum of the q parts the MFMAs multiply
+          const float qs = wave_sum((float)h + (float)l + (float)h2 + (float)l2);
+          if (lane == 0) qsum[wave] = qs;
+        }
+      } else if constexpr (KV8) {  // the new key's codes and scale: to the cache and LDS
+        float c0, c1;
+        const float sk = kv_quant_i8(y1, y2, c0, c1);
+        knew8[lane] = (int8_t)c0;
+        knew8[lane + 64] = (int8_t)c1;
+        int8_t* kb = (int8_t*)a.kv.base + kv_slab(a.kv, rp.seq, layer, 0, g) + (size_t)rp.pos * D;
+        kb[lane] = (int8_t)c0;
+        kb[lane + 64] = (int8_t)c1;
+        if (lane == 0) {
+          newsc[0] = sk;
+          a.kv.scales[kv_scale_slab(a.kv, rp.seq, layer, 0, g) + rp.pos] = sk;
+        }
       } else {
         kn16[lane] = (_Float16)y1;
         kn16[lane + 64] = (_Float16)y2;
       }
     } else if (wave == G + 1 && own) {
       const uint32_t v = row + (uint32_t)((a.n_heads + a.n_kv + g) * D);
-      vn16[lane] = (_Float16)cload(q0, v + lane);
-      vn16[lane + 64] = (_Float16)cload(q0, v + lane + 64);
+      if constexpr (KV8) {  // the new value's codes and scale: to the cache and LDS
+        float c0, c1;
+        const float sv = kv_quant_i8(cload(q0, v + lane), cload(q0, v + lane + 64), c0, c1);
+        vnew8[lane] = (int8_t)c0;
+        vnew8[lane + 64] = (int8_t)c1;
+        int8_t* vb = (int8_t*)a.kv.base + kv_slab(a.kv, rp.seq, layer, 1, g);
+        vb[(size_t)lane * a.kv.max_seq + rp.pos] = (int8_t)c0;
+        vb[(size_t)(lane + 64) * a.kv.max_seq + rp.pos] = (int8_t)c1;
+        if (lane == 0) {
+          newsc[1] = sv;
+          a.kv.scales[kv_scale_slab(a.kv, rp.seq, layer, 1, g) + rp.pos] = sv;
+        }
+      } else {
+        vn16[lane] = (_Float16)cload(q0, v + lane);
+        vn16[lane + 64] = (_Float16)cload(q0, v + lane + 64);
+      }
     }
     __syncthreads();
-    if (own) {
+    // KV8: the scales of the lane's positions wp0 + 8 j4 + i (values past the
+    // context: 0, so P' is 0 there)
+    float sk[KV8 ? 8 : 1], sv[KV8 ? 8 : 1];
+    if constexpr (KV8) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        sk[i] = sc8[i >> 2][i & 3];
+        sv[i] = (wp0 + 8 * j4 + i < c1) ? sc8[2 + (i >> 2)][i & 3] : 0.f;
+      }
+      if (own) {
+        // the new position inside this wave's fragments: its codes and scales
+        // from LDS (compile-time fragment indices only)
+        const int off = rp.pos - wp0;
+        if (off >= 0 && off < 32) {
+          const int kt = (off % 8) / 4, kr = 4 * (off / 8) + off % 4;
+          if (r16 == kr) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+              if (t == kt) {
+#pragma unroll
+                for (int s = 0; s < D / 32; ++s) kf[t][s] = *(const Frag*)(knew8 + 32 * s + 8 * j4);
+              }
+          }
+          const int e8 = off % 8;
+          if (j4 == off / 8) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+              if (i == e8) {
+                sk[i] = newsc[0];
+                sv[i] = newsc[1];
+              }
+            const uint32_t sh = 8u * (e8 & 3), keep = ~(0xFFu << sh);
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) {
+              const uint32_t b = (uint32_t)(uint8_t)vnew8[dt * 16 + r16] << sh;
+              if (e8 < 4)
+                vf[dt].x = (vf[dt].x & keep) | b;
+              else
+                vf[dt].y = (vf[dt].y & keep) | b;
+            }
+          }
+        }
+      }
+    } else if (own) {
       for (int e = tid; e < D; e += MT) {
         kv_store(a.kv, kv_offset(a.kv, rp.seq, layer, 0, g, e, rp.pos), (float)kn16[e]);
         kv_store(a.kv, kv_offset(a.kv, rp.seq, layer, 1, g, e, rp.pos), (float)vn16[e]);
@@ -600,15 +696,24 @@ DPK_DEV bool attn_phase(const MegaArgs& a, const RowParam* rows, int layer, cons
         ql[s] = *(const f16x8*)(ql16 + qc * D + 32 * s + 8 * j4);
       }
     }
+    const float cq = KV8 ? -1152.0f * qsum[r16 < G ? r16 : G - 1] : 0.f;  // S's start (int8 cache)
     f32x4 sc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sc[t] = f32x4{cq, cq, cq, cq};
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) {
-        const f16x8 A = __builtin_bit_cast(f16x8, kf[t][s]);
+        f16x8 A;
+        if constexpr (KV8)
+          A = __builtin_bit_cast(f16x8, kv_codes_f16(kf[t][s]));
+        else
+          A = __builtin_bit_cast(f16x8, kf[t][s]);
         sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qh[s], sc[t], 0, 0, 0);
         sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, ql[s], sc[t], 0, 0, 0);
+      }
+      if constexpr (KV8) {  // the keys' scales (lane rows 4 j4 + v of tile t: positions 8 j4 + 4 t + v)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sc[t][v] *= sk[4 * t + v];
       }
     }
     // mask (positions 8 j4 + 4 t + v past the context), column max / sum
@@ -633,6 +738,12 @@ DPK_DEV bool attn_phase(const MegaArgs& a, const RowParam* rows, int layer, cons
       }
     sum += __shfl_xor(sum, 16, 64);
     sum += __shfl_xor(sum, 32, 64);
+    if constexpr (KV8) {  // P' = P times the value's scale
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sc[t][v] *= sv[4 * t + v];
+    }
 
     // ---- O^T = V^T P^T over the 32 positions (k slots 0..3 from tile 0, 4..7 from tile 1)
     f32x4 o[D / 16];
@@ -648,18 +759,36 @@ DPK_DEV bool attn_phase(const MegaArgs& a, const RowParam* rows, int layer, cons
         ph[4 + v] = h1;
         pl[4 + v] = l1;
       }
+      // KV8: 1152 times the column's sum of P' (the parts the MFMAs take)
+      float corr = 0.f;
+      if constexpr (KV8) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) corr += (float)ph[i] + (float)pl[i];
+        corr += __shfl_xor(corr, 16, 64);
+        corr += __shfl_xor(corr, 32, 64);
+        corr *= 1152.0f;
+      }
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
         o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        u32x4 w = vf[dt];
-        if (wp0 + 32 > c1) {  // positions past the context may hold any bits (0 * NaN)
-          const int n = c1 - wp0 - 8 * j4;
-          auto mk = [n](int e) { return n >= e + 2 ? 0xffffffffu : (n == e + 1 ? 0x0000ffffu : 0u); };
-          w = u32x4{w.x & mk(0), w.y & mk(2), w.z & mk(4), w.w & mk(6)};
+        u32x4 w;
+        if constexpr (KV8) {  // (int8 codes are finite as fp16 and meet P' = 0 past the context)
+          w = kv_codes_f16(vf[dt]);
+        } else {
+          w = vf[dt];
+          if (wp0 + 32 > c1) {  // positions past the context may hold any bits (0 * NaN)
+            const int n = c1 - wp0 - 8 * j4;
+            auto mk = [n](int e) { return n >= e + 2 ? 0xffffffffu : (n == e + 1 ? 0x0000ffffu : 0u); };
+            w = u32x4{w.x & mk(0), w.y & mk(2), w.z & mk(4), w.w & mk(6)};
+          }
         }
         const f16x8 A = __builtin_bit_cast(f16x8, w);
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, ph, o[dt], 0, 0, 0);
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pl, o[dt], 0, 0, 0);
+        if constexpr (KV8) {  // the values' code offset (lane: column r16)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) o[dt][v] -= corr;
+        }
       }
     }
 
@@ -754,7 +883,8 @@ DPK_DEV bool attn_phase(const MegaArgs& a, const RowParam* rows, int layer, cons
 //
 // FO (bf16, a.oacc set): attention and the O projection are one phase (see
 // attn_phase), and gate/up and down fold the fixed-point O sums into h.
-template <int G, int FMT, bool SMALL, bool FO>
+// KV8: the KV cache holds int8 codes with per-vector scales (a.kv.i8).
+template <int G, int FMT, bool SMALL, bool FO, bool KV8>
 __global__ __launch_bounds__(MT, 1) void decode_step_kernel(MegaArgs a) {
   // (the lm_head of a narrow model goes in 32-row tiles: one 128-column
   // iteration per 16 rows would leave a wave a single 4 KB load in flight)
@@ -812,7 +942,7 @@ __global__ __launch_bounds__(MT, 1) void decode_step_kernel(MegaArgs a) {
     const MegaLayer& L = *Ls;
     gemv_body<FMT, TQ, 8, true, false, KI, PF>(L.qkv, a.M, lds, wg, nwg, sync, pf);
     closing = MP_QKV;
-    const bool gu_pf = attn_phase<G, FO, KI>(a, Rs, l, L.qn, L.kn, &L.o, &L.gu, lds, pf, bar, wg, nwg, sync);
+    const bool gu_pf = attn_phase<G, FO, KI, KV8>(a, Rs, l, L.qn, L.kn, &L.o, &L.gu, lds, pf, bar, wg, nwg, sync);
     closing = MP_ATTN;
     if constexpr (!FO) {
       gemv_body<FMT, 1, 8, true, false, KI, PF>(L.o, a.M, lds, wg, nwg, sync, pf);
@@ -832,36 +962,65 @@ __global__ __launch_bounds__(MT, 1) void decode_step_kernel(MegaArgs a) {
   }
 }
 
-// Built variants: bf16 and int8 (one scale per row) at 256 columns per
-// iteration for G = 1, 2, 4; bf16 and 4-bit at 128 columns for G = 2, 4; bf16
-// with and without the fused O projection.
+#ifdef DPK_DECODE_STEP_KV8_TU
+}  // namespace
+
+// The variants over an int8 KV cache (256 columns per iteration): bf16 with
+// the fused O projection and int8 weights (one scale per row), G = 1, 2, 4.
+const void* mega_kernel_kv8(int G, int fmt, bool small, bool fo) {
+  if (small) return nullptr;
+  if (fmt == W_BF16 && fo) {
+    if (G == 1) return (const void*)decode_step_kernel<1, W_BF16, false, true, true>;
+    if (G == 2) return (const void*)decode_step_kernel<2, W_BF16, false, true, true>;
+    if (G == 4) return (const void*)decode_step_kernel<4, W_BF16, false, true, true>;
+  } else if (fmt == W_I8 && !fo) {
+    if (G == 1) return (const void*)decode_step_kernel<1, W_I8, false, false, true>;
+    if (G == 2) return (const void*)decode_step_kernel<2, W_I8, false, false, true>;
+    if (G == 4) return (const void*)decode_step_kernel<4, W_I8, false, false, true>;
+  }
+  return nullptr;
+}
+
+}  // namespace dpk
+#else
+// Built variants (fp16 KV cache): bf16 and int8 (one scale per row) at 256
+// columns per iteration for G = 1, 2, 4; bf16 and 4-bit at 128 columns for
+// G = 2, 4; bf16 with and without the fused O projection.  The int8-cache
+// variants are built in a translation unit of their own (mega_kernel_kv8).
 template <bool FO>
 const void* mega_kernel_fo(int G, int fmt, bool small) {
   if (fmt == W_BF16 && !small) {
     switch (G) {
-      case 1: return (const void*)decode_step_kernel<1, W_BF16, false, FO>;
-      case 2: return (const void*)decode_step_kernel<2, W_BF16, false, FO>;
-      case 4: return (const void*)decode_step_kernel<4, W_BF16, false, FO>;
+      case 1: return (const void*)decode_step_kernel<1, W_BF16, false, FO, false>;
+      case 2: return (const void*)decode_step_kernel<2, W_BF16, false, FO, false>;
+      case 4: return (const void*)decode_step_kernel<4, W_BF16, false, FO, false>;
       default: return nullptr;
     }
   }
   if (fmt == W_I8 && !small && !FO) {  // int8 codes, one scale per row: the 256-column variant only
-    if (G == 1) return (const void*)decode_step_kernel<1, W_I8, false, false>;
-    if (G == 2) return (const void*)decode_step_kernel<2, W_I8, false, false>;
-    if (G == 4) return (const void*)decode_step_kernel<4, W_I8, false, false>;
+    if (G == 1) return (const void*)decode_step_kernel<1, W_I8, false, false, false>;
+    if (G == 2) return (const void*)decode_step_kernel<2, W_I8, false, false, false>;
+    if (G == 4) return (const void*)decode_step_kernel<4, W_I8, false, false, false>;
     return nullptr;
   }
   if (!small) return nullptr;
   if (fmt == W_BF16) {
-    if (G == 2) return (const void*)decode_step_kernel<2, W_BF16, true, FO>;
-    if (G == 4) return (const void*)decode_step_kernel<4, W_BF16, true, FO>;
+    if (G == 2) return (const void*)decode_step_kernel<2, W_BF16, true, FO, false>;
+    if (G == 4) return (const void*)decode_step_kernel<4, W_BF16, true, FO, false>;
   } else if (fmt == W_Q4 && !FO) {
-    if (G == 2) return (const void*)decode_step_kernel<2, W_Q4, true, false>;
-    if (G == 4) return (const void*)decode_step_kernel<4, W_Q4, true, false>;
+    if (G == 2) return (const void*)decode_step_kernel<2, W_Q4, true, false, false>;
+    if (G == 4) return (const void*)decode_step_kernel<4, W_Q4, true, false, false>;
   }
   return nullptr;
 }
-const void* mega_kernel_for(int G, int fmt, bool small, bool fo) {
+
+}  // namespace
+
+const void* mega_kernel_kv8(int G, int fmt, bool small, bool fo);
+
+namespace {
+const void* mega_kernel_for(int G, int fmt, bool small, bool fo, bool kv8) {
+  if (kv8) return mega_kernel_kv8(G, fmt, small, fo);
   return fo ? mega_kernel_fo<true>(G, fmt, small) : mega_kernel_fo<false>(G, fmt, small);
 }
 
@@ -882,9 +1041,9 @@ int mega_threads() { return MT; }
 int mega_attn_chunk() { return ACH; }
 
 // Workgroups per CU the kernel can keep resident with lds bytes of LDS (0 if
-// the kernel does not exist for G, fmt, small).
-int mega_occupancy(int G, int fmt, bool small, bool fo, size_t lds) {
-  const void* k = mega_kernel_for(G, fmt, small, fo);
+// the kernel does not exist for G, fmt, small, fo, kv8).
+int mega_occupancy(int G, int fmt, bool small, bool fo, bool kv8, size_t lds) {
+  const void* k = mega_kernel_for(G, fmt, small, fo, kv8);
   if (!k) return 0;
   int nb = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k, MT, lds) != hipSuccess) return 0;
@@ -892,7 +1051,7 @@ int mega_occupancy(int G, int fmt, bool small, bool fo, size_t lds) {
 }
 
 hipError_t launch_decode_step(const MegaArgs& a, int G, int n_wg, size_t lds, hipStream_t stream) {
-  const void* k = mega_kernel_for(G, a.fmt, a.small != 0, a.oacc != nullptr);
+  const void* k = mega_kernel_for(G, a.fmt, a.small != 0, a.oacc != nullptr, a.kv.i8 != 0);
   if (!k || n_wg < 1 || a.M < 1 || a.M > 16) return hipErrorInvalidValue;
   MegaArgs copy = a;
   void* args[] = {&copy};
@@ -905,3 +1064,4 @@ hipError_t launch_decode_step(const MegaArgs& a, int G, int n_wg, size_t lds, hi
 }
 
 }  // namespace dpk
+#endif

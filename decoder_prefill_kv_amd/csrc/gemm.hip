@@ -308,6 +308,26 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs a) {
     }
   }
 
+  // int8 codes as B: each column times its weight row's scale
+  if (a.rs[0]) {
+    const int c32 = lane & 31;
+#pragma unroll
+    for (int j = 0; j < JB; ++j) {
+      float sc;
+      if constexpr (EPI == GEMM_SWIGLU_F16) {  // blocks 0, 1 gate, 2, 3 up, at the same rows
+        sc = bf16_to_f32(a.rs[j >> 1][n0 + wn * 64 + (j & 1) * 32 + c32]);
+      } else {
+        const int n = n0 + wn * (BNT / 2) + j * 32 + c32;
+        const int sg = (n >= a.rs_end[0]) + (n >= a.rs_end[1]);
+        sc = bf16_to_f32(a.rs[sg][n - (sg == 0 ? 0 : a.rs_end[sg - 1])]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] *= sc;
+    }
+  }
+
   // epilogue: lane holds C[row][col], col = lane % 32,
   // row = 8 * (v / 4) + 4 * (lane / 32) + v % 4 inside each 32 x 32 block
   const int hi4 = (lane >> 5) * 4;

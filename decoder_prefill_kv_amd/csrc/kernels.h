@@ -38,6 +38,13 @@ DPK_DEV float kv_quant_i8(float x0, float x1, float& q0, float& q1) {  // return
   q1 = s > 0.f ? fminf(fmaxf(rintf(x1 / s), -127.f), 127.f) : 0.f;
   return s;
 }
+// 8 int8 cache codes -> the fp16 integers 1152 + q (exact: the byte q ^ 0x80
+// under the high byte 0x64), the form the attention MFMAs take them in
+DPK_DEV u32x4 kv_codes_f16(u32x2 w) {
+  const uint32_t u0 = w.x ^ 0x80808080u, u1 = w.y ^ 0x80808080u;
+  return u32x4{__builtin_amdgcn_perm(0x64646464u, u0, 0x04010400u), __builtin_amdgcn_perm(0x64646464u, u0, 0x04030402u),
+               __builtin_amdgcn_perm(0x64646464u, u1, 0x04010400u), __builtin_amdgcn_perm(0x64646464u, u1, 0x04030402u)};
+}
 DPK_DEV void kv_put_i8(const KVDesc& kv, int seq, int layer, int which, int head, int pos, float x0, float x1,
                        int lane) {
   float q0, q1;
@@ -293,6 +300,13 @@ struct GemmArgs {
   const float* rope_sin;
   _Float16* q16;                  // hi plane [M][n_heads][128], then the lo plane
   KVDesc kv;
+  // int8 weights with one scale per output row: B (and B2) hold the codes
+  // themselves (exact in fp16) and each product column is multiplied by its
+  // row's bf16 scale before the epilogue: rows [0, rs_end[0]) of B take rs[0],
+  // then rs[1] up to rs_end[1], then rs[2]; SWIGLU: rs[0] gate, rs[1] up.
+  // rs[0] null: no scaling.
+  const uint16_t* rs[3];
+  int rs_end[2];
 };
 constexpr int GEMM_MAX_SPLITS = 2;
 constexpr size_t GEMM_WS_TILES = 768;             // partial tiles the workspace holds
@@ -375,7 +389,7 @@ size_t mega_attn_lds_bytes(int G);
 size_t mega_o_lds_bytes(int M, int G, int rt);
 int mega_threads();
 int mega_attn_chunk();
-int mega_occupancy(int G, int fmt, bool small, bool fo, size_t lds);
+int mega_occupancy(int G, int fmt, bool small, bool fo, bool kv8, size_t lds);
 hipError_t launch_decode_step(const MegaArgs& a, int G, int n_wg, size_t lds, hipStream_t stream);
 
 // ---------------------------------------------------------------- sampling (sample.hip)

@@ -384,7 +384,7 @@ __global__ void f32_to_f16_kernel(const float* src, _Float16* dst, size_t n) {
 __global__ void i8_to_f16_kernel(const int8_t* q, const uint16_t* sc, int rows, int K, _Float16* dst) {
   const size_t n = (size_t)rows * K;
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-    dst[i] = (_Float16)(bf16_to_f32(sc[i / K]) * (float)q[i]);
+    dst[i] = sc ? (_Float16)(bf16_to_f32(sc[i / K]) * (float)q[i]) : (_Float16)q[i];  // (sc null: the codes)
 }
 
 // dst[((rt * (K / 256) + kt) * 4 + p) * 1024 + l * 16 + 8 h + e] =

@@ -734,13 +734,14 @@ int mega_o_rt(const dpk_model* md, int M) {
 }
 
 // LDS bytes of the persistent decode kernel for M rows, or 0 if the model or
-// M does not fit it: bf16 or 4-bit weights, head_dim 128, 1, 2 or 4 query
+// M does not fit it: bf16, 4-bit or int8-per-row weights (with an int8 KV
+// cache: bf16 with the fused O projection, or int8), head_dim 128, 1, 2 or 4 query
 // heads per KV head (2 or 4 for the 128-column tiling), every GEMV on eight
 // waves, LDS within the device's per-workgroup limit, one resident workgroup
 // per CU.
 size_t mega_lds_for(dpk_model* md, int M, int max_ctx) {
   const dpk_config& c = md->cfg;
-  if ((c.flags & (DPK_FLAG_DECODE_MULTI | DPK_FLAG_KV_I8)) || !md->mega_layers) return 0;
+  if ((c.flags & DPK_FLAG_DECODE_MULTI) || !md->mega_layers) return 0;
   if (c.head_dim != 128 || c.n_heads % c.n_kv_heads) return 0;
   const int G = c.n_heads / c.n_kv_heads;
   if (G != 1 && G != 2 && G != 4) return 0;
@@ -763,7 +764,9 @@ size_t mega_lds_for(dpk_model* md, int M, int max_ctx) {
   // GEMVs' prefetch slots
   lds = (lds + 15) / 16 * 16 + MEGA_ARGS_LDS + (fmt == W_BF16 ? MEGA_PF_LDS : 0);
   if (lds > (size_t)md->lds_max) return 0;
-  if (mega_occupancy(G, fmt, var == 1, mega_o_rt(md, M) > 0, lds) < 1) return 0;
+  // (an int8 KV cache: the 256-column variants with bf16 weights and the
+  // fused O projection, or int8 weights; mega_occupancy is 0 for the others)
+  if (mega_occupancy(G, fmt, var == 1, mega_o_rt(md, M) > 0, (c.flags & DPK_FLAG_KV_I8) != 0, lds) < 1) return 0;
   return lds;
 }
 
@@ -967,6 +970,20 @@ dpk_status forward_gemm(dpk_model* md, int M, int start, int seq, bool want_head
   // projection runs on full 256 x 256 tiles (a narrow-tile grid splits a head
   // over two waves)
   const bool qkv_fused = d == 128 && !gemm_prefers_narrow(M, md->Nqkv, md->n_cu) && !md->kvd.i8;
+  // int8 weights, one scale per row: the fp16 copies hold the codes and the
+  // GEMMs scale their product columns (rs: the segments' bf16 row scales)
+  const bool row_sc = md->fmt == DPK_FMT_I8;
+  auto set_rs = [&](GemmArgs& g, const LinearW* a, const LinearW* b, const LinearW* c3) {
+    g.rs_end[0] = g.rs_end[1] = 1 << 30;
+    if (!row_sc) return;
+    g.rs[0] = a->sc;
+    g.rs[1] = b ? b->sc : nullptr;
+    g.rs[2] = c3 ? c3->sc : nullptr;
+    if (c3) {
+      g.rs_end[0] = a->rows;
+      g.rs_end[1] = a->rows + b->rows;
+    }
+  };
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& L = md->layers[l];
     {
@@ -977,6 +994,7 @@ dpk_status forward_gemm(dpk_model* md, int M, int start, int seq, bool want_head
     GemmArgs g{};
     g.M = M; g.N = md->Nqkv; g.K = 2 * H; g.Kb = H;
     g.A = md->y16; g.lda = 2 * H; g.B = L.qkv16; g.ldb = H;
+    set_rs(g, &L.q, &L.k, &L.v);
     if (qkv_fused) {
       // QK-norm, RoPE, the q hi / lo split and the KV-cache write in the epilogue
       g.epi = GEMM_QKV_F16;
@@ -1007,6 +1025,7 @@ dpk_status forward_gemm(dpk_model* md, int M, int start, int seq, bool want_head
     g = GemmArgs{};
     g.M = M; g.N = H; g.K = 2 * Qd; g.Kb = Qd;
     g.A = md->o16; g.lda = 2 * Qd; g.B = L.o16; g.ldb = Qd;
+    set_rs(g, &L.o, nullptr, nullptr);
     g.epi = GEMM_ADD_F32; g.C = md->h; g.ldc = H;
     if ((s2 = gemm_prof(K_GEMM_O, g))) return s2;
     {
@@ -1016,11 +1035,13 @@ dpk_status forward_gemm(dpk_model* md, int M, int start, int seq, bool want_head
     g = GemmArgs{};
     g.M = M; g.N = I; g.K = H;
     g.A = md->y16; g.lda = H; g.B = L.gate16; g.B2 = L.up16; g.ldb = H;
+    set_rs(g, &L.gate, &L.up, nullptr);
     g.epi = GEMM_SWIGLU_F16; g.C16 = md->act16; g.ldc16 = I;
     if ((s2 = gemm_prof(K_GEMM_GATEUP, g))) return s2;
     g = GemmArgs{};
     g.M = M; g.N = H; g.K = I;
     g.A = md->act16; g.lda = I; g.B = L.down16; g.ldb = I;
+    set_rs(g, &L.down, nullptr, nullptr);
     g.epi = GEMM_ADD_F32; g.C = md->h; g.ldc = H;
     if ((s2 = gemm_prof(K_GEMM_DOWN, g))) return s2;
   }
@@ -1296,7 +1317,8 @@ dpk_status dpk_load_weights(dpk_model* md, const dpk_tensor* t, int32_t n, void*
     char* p = (char*)md->prep;
     auto conv = [&](const LinearW& w, _Float16* dst) -> hipError_t {
       if (fmt == DPK_FMT_BF16) return launch_bf16_to_f16((const uint16_t*)w.w, dst, (size_t)w.rows * w.cols, st);
-      if (fmt == DPK_FMT_I8) return launch_i8_to_f16((const int8_t*)w.w, w.sc, w.rows, w.cols, dst, st);
+      // int8 per row: the codes (exact in fp16); the GEMMs apply the row scales
+      if (fmt == DPK_FMT_I8) return launch_i8_to_f16((const int8_t*)w.w, nullptr, w.rows, w.cols, dst, st);
       if (fmt == DPK_FMT_Q8) return launch_q8_to_f16((const int8_t*)w.w, w.sf, w.rows, w.cols, dst, st);
       if (fmt == DPK_FMT_Q40)
         return launch_q40_to_f16((const uint8_t*)w.w, (const uint16_t*)w.sf, w.rows, w.cols, dst, st);

@@ -63,6 +63,11 @@ CASES = [
     ("q06b-kvi8-L2-gemm", synth.Q06B.with_(n_layers=2, kv_i8=True), 40, 8, {}),
     ("q06b-kvi8-L2-stream", synth.Q06B.with_(n_layers=2, kv_i8=True), 37, 6, dict(flags=STREAM)),
     ("q8b-kvi8-L1-v4096-chunked", synth.Q8B.with_(n_layers=1, vocab=4096, kv_i8=True), 300, 6, dict(max_rows=128)),
+    # the persistent step over the int8 cache (bf16 weights with the fused O
+    # projection, int8 weights): positions crossing a 256-position chunk boundary
+    ("q8b-kvi8-L2-v4096-persistent", synth.Q8B.with_(n_layers=2, vocab=4096, kv_i8=True), 510, 6, dict(max_rows=256)),
+    ("q8b_i8-kvi8-L2-v4096-persistent", synth.Q8B_I8.with_(n_layers=2, vocab=4096, kv_i8=True), 250, 8,
+     dict(max_rows=256)),
     ("q06b_q8-kvi8-L2-gemm", synth.Q06B_Q8.with_(n_layers=2, kv_i8=True), 40, 8, {}),
     # GGUF-style Q4_0 blocks: the same paths with 4-bit codes around 8 and fp16 scales
     ("q06b_q40-L2-gemm", synth.Q06B_Q40.with_(n_layers=2), 40, 8, {}),
@@ -152,6 +157,8 @@ PATH_CASES = [
     ("q06b_q8-L1", synth.Q06B_Q8.with_(n_layers=1), False),
     ("q06b_q40-L1", synth.Q06B_Q40.with_(n_layers=1), False),
     ("q06b-kvi8-L1", synth.Q06B.with_(n_layers=1, kv_i8=True), False),
+    ("q8b-kvi8-L1-v4096", synth.Q8B.with_(n_layers=1, vocab=4096, kv_i8=True), True),
+    ("q8b_i8-kvi8-L1-v4096", synth.Q8B_I8.with_(n_layers=1, vocab=4096, kv_i8=True), True),
     ("q8b_i8-L1-v4096", synth.Q8B_I8.with_(n_layers=1, vocab=4096), True),
 ]
 
@@ -184,6 +191,8 @@ KV_I8_CASES = [
     ("bf16-gemm", synth.Q06B.with_(n_layers=2, kv_i8=True), 0),
     ("bf16-stream", synth.Q06B.with_(n_layers=2, kv_i8=True), STREAM),
     ("q8-gemm", synth.Q06B_Q8.with_(n_layers=2, kv_i8=True), 0),
+    # (8B shapes: the decode positions written by the persistent step)
+    ("bf16-8b-persistent", synth.Q8B.with_(n_layers=1, vocab=4096, kv_i8=True), 0),
 ]
 
 
