@@ -143,6 +143,11 @@ DPK_DEV void embed_phase(const MegaArgs& a, const RowParam* rows, int wg, int nw
           v = bf16_to_f32(a.emb_sc[gi]) * (float)((word >> (4 * (col & 7))) & 0xFu) + bf16_to_f32(a.emb_bi[gi]);
         } else if (a.fmt == W_I8) {  // int8 with one bf16 scale per row
           v = bf16_to_f32(a.emb_sc[tok]) * (float)((const int8_t*)a.emb)[(size_t)tok * a.H + col];
+        } else if (a.fmt == W_Q40) {  // blocks of 32 codes around 8, fp16 scale; byte j: codes j, j + 16
+          const int i = col & 31;
+          const uint8_t b = ((const uint8_t*)a.emb)[(size_t)tok * (a.H / 2) + (col / 32) * 16 + (i & 15)];
+          const int c = i < 16 ? (b & 0xF) : (b >> 4);
+          v = (float)__builtin_bit_cast(_Float16, a.emb_sc[(size_t)tok * (a.H / 32) + col / 32]) * (float)(c - 8);
         } else {
           v = bf16_to_f32(((const uint16_t*)a.emb)[(size_t)tok * a.H + col]);
         }
@@ -888,7 +893,7 @@ template <int G, int FMT, bool SMALL, bool FO, bool KV8>
 __global__ __launch_bounds__(MT, 1) void decode_step_kernel(MegaArgs a) {
   // (the lm_head of a narrow model goes in 32-row tiles: one 128-column
   // iteration per 16 rows would leave a wave a single 4 KB load in flight)
-  constexpr int KI = SMALL ? 128 : 0, TQ = SMALL ? 1 : 2, TH = SMALL ? 2 : (FMT == W_I8 ? MEGA_HEAD_I8_TILES : 1);
+  constexpr int KI = SMALL ? 128 : 0, TQ = SMALL ? 1 : 2, TH = mega_head_tiles(FMT, SMALL), TGU = mega_gu_tiles(FMT);
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int wg = blockIdx.x, nwg = gridDim.x;
   Barrier bar{a.bar, a.bar + MEGA_BAR_ABORT, (unsigned)nwg, 0u};
@@ -948,7 +953,7 @@ __global__ __launch_bounds__(MT, 1) void decode_step_kernel(MegaArgs a) {
       gemv_body<FMT, 1, 8, true, false, KI, PF>(L.o, a.M, lds, wg, nwg, sync, pf);
       closing = MP_O;
     }
-    gemv_body<FMT, 2, 8, true, false, KI, PF, FO>(L.gu, a.M, lds, wg, nwg, sync, pf, gu_pf);
+    gemv_body<FMT, TGU, 8, true, false, KI, PF, FO>(L.gu, a.M, lds, wg, nwg, sync, pf, gu_pf);
     closing = MP_GATEUP;
     gemv_body<FMT, 1, 8, true, false, KI, PF, FO>(L.down, a.M, lds, wg, nwg, sync, pf);
     closing = MP_DOWN;
@@ -966,7 +971,8 @@ __global__ __launch_bounds__(MT, 1) void decode_step_kernel(MegaArgs a) {
 }  // namespace
 
 // The variants over an int8 KV cache (256 columns per iteration): bf16 with
-// the fused O projection and int8 weights (one scale per row), G = 1, 2, 4.
+// the fused O projection, int8 weights (one scale per row) and Q4_0 weights,
+// G = 1, 2, 4.
 const void* mega_kernel_kv8(int G, int fmt, bool small, bool fo) {
   if (small) return nullptr;
   if (fmt == W_BF16 && fo) {
@@ -977,14 +983,18 @@ const void* mega_kernel_kv8(int G, int fmt, bool small, bool fo) {
     if (G == 1) return (const void*)decode_step_kernel<1, W_I8, false, false, true>;
     if (G == 2) return (const void*)decode_step_kernel<2, W_I8, false, false, true>;
     if (G == 4) return (const void*)decode_step_kernel<4, W_I8, false, false, true>;
+  } else if (fmt == W_Q40 && !fo) {
+    if (G == 1) return (const void*)decode_step_kernel<1, W_Q40, false, false, true>;
+    if (G == 2) return (const void*)decode_step_kernel<2, W_Q40, false, false, true>;
+    if (G == 4) return (const void*)decode_step_kernel<4, W_Q40, false, false, true>;
   }
   return nullptr;
 }
 
 }  // namespace dpk
 #else
-// Built variants (fp16 KV cache): bf16 and int8 (one scale per row) at 256
-// columns per iteration for G = 1, 2, 4; bf16 and 4-bit at 128 columns for
+// Built variants (fp16 KV cache): bf16, int8 (one scale per row) and Q4_0 at
+// 256 columns per iteration for G = 1, 2, 4; bf16 and 4-bit at 128 columns for
 // G = 2, 4; bf16 with and without the fused O projection.  The int8-cache
 // variants are built in a translation unit of their own (mega_kernel_kv8).
 template <bool FO>
@@ -1001,6 +1011,12 @@ const void* mega_kernel_fo(int G, int fmt, bool small) {
     if (G == 1) return (const void*)decode_step_kernel<1, W_I8, false, false, false>;
     if (G == 2) return (const void*)decode_step_kernel<2, W_I8, false, false, false>;
     if (G == 4) return (const void*)decode_step_kernel<4, W_I8, false, false, false>;
+    return nullptr;
+  }
+  if (fmt == W_Q40 && !small && !FO) {  // Q4_0 blocks: 256-column chunks
+    if (G == 1) return (const void*)decode_step_kernel<1, W_Q40, false, false, false>;
+    if (G == 2) return (const void*)decode_step_kernel<2, W_Q40, false, false, false>;
+    if (G == 4) return (const void*)decode_step_kernel<4, W_Q40, false, false, false>;
     return nullptr;
   }
   if (!small) return nullptr;

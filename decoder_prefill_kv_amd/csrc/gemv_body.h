@@ -47,7 +47,7 @@ __host__ __device__ inline int gemv_lds_layout(int M, int K, int RB, int fmt, in
   off += WAVES * 2 * M * xstride * 2;
   off = (off + 15) & ~15;
   *xsum_off = off;
-  off += (fmt == W_Q4 ? M * (K / 64) * 4 : 0);
+  off += (fmt == W_Q4 ? M * (K / 64) * 4 : fmt == W_Q40 ? M * (K / 32) * 4 : 0);
   off = (off + 15) & ~15;
   *red_off = off;
   off += WAVES * M * RB * 4;
@@ -138,6 +138,7 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
                        unsigned char* pf = nullptr, bool pf_ready = false) {
   static_assert(!PF || (FMT == W_BF16 && !XG), "LDS prefetch is for staged-x bf16 GEMVs");
   static_assert(!XG || FMT == W_BF16, "ready-made activations are for bf16 weights");
+  static_assert(FMT != W_Q40 || KI == 0, "Q4_0: whole 128-column halves per iteration");
   constexpr int RB = 16 * T;
   constexpr int THREADS = 64 * WAVES;
   const int K = a.K;                      // columns this call reduces over
@@ -174,7 +175,10 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
   // columns, twice the 4-bit count (the same bytes per iteration)
   constexpr int GU = KI ? KI / 64 : (FMT == W_I8 && WAVES == 8) ? 8 / T : 4 / T > 0 ? 4 / T : 1;
   static_assert(KI % 64 == 0, "whole 4-bit groups per iteration");
-  const int nit = (FMT == W_BF16) ? kq / (32 * U) : kq / (64 * GU);
+  // Q4_0: QH halves of 128 columns (4 blocks of 32 each) per tile and
+  // iteration, 4 KB of codes per wave and iteration
+  constexpr int QH = 4 / T > 0 ? 4 / T : 1;
+  const int nit = (FMT == W_BF16) ? kq / (32 * U) : (FMT == W_Q40) ? kq / (128 * QH) : kq / (64 * GU);
   const unsigned char* wp[T];   // this wave's stream inside each 16-row tile
   const unsigned char* sbp[T];  // 4-bit: scale/bias stream; int8: the tile's row scales (bf16)
   uint32_t rsc[T][2];           // int8: bf16 scales of rows 4 j4 .. 4 j4 + 3 of each tile
@@ -191,6 +195,13 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
         // lane l's 16 bytes: MFMA k-steps 2g and 2g + 1 of row l % 16
         wp[t] = (const unsigned char*)a.w[seg] + (rt * (KF / 64) + (KO + k0) / 64) * 1024 + lane * 16;
         sbp[t] = (const unsigned char*)a.sb[seg] + (rt * 16 + 4 * j4) * 2;
+      } else if (FMT == W_Q40) {
+        // Q4_0 codes of chunk (rt, c) (16 rows x 256 columns) at ((rt * K/256) + c) * 2048,
+        // lane l's 16 bytes at l * 16 of each 1 KB half (blocks 0-3, then 4-7); the
+        // blocks' scales (fp32) of row r at ((rt * K/256 + c) * 16 + r) * 32
+        const size_t ch = rt * (KF / 256) + (KO + k0) / 256;
+        wp[t] = (const unsigned char*)a.w[seg] + ch * 2048 + lane * 16;
+        sbp[t] = (const unsigned char*)a.sb[seg] + (ch * 16 + r16) * 32;
       } else {
         // codes block (rt, g) at ((rt * K/64) + g) * 512; scales (rt, g) at * 64
         wp[t] = (const unsigned char*)a.w[seg] + (rt * (KF / 64) + (KO + k0) / 64) * 512 + lane * 8;
@@ -201,6 +212,8 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
   u32x4 b0[T][U], b1[T][U];
   u32x2 c0[T][GU], c1[T][GU];
   u32x4 s0[T][GU], s1[T][GU];
+  u32x4 qc0[T][QH], qc1[T][QH];  // Q4_0: the halves' codes (4 blocks each)
+  f32x4 qs0[T][QH], qs1[T][QH];  // and lane row r16's 4 block scales of each
   // XG: each iteration's activation fragments are loaded with its weights, so
   // one wait covers both and the next iteration's loads stay in flight.  Rows
   // past M read row M - 1 (their results are never stored).
@@ -229,6 +242,18 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
 #pragma unroll
       for (int u = 0; u < GU; ++u)
         q[t][u] = __builtin_nontemporal_load(gmem((const u32x4*)(wp[t] + (size_t)(it * GU + u) * 1024)));
+  };
+  // (half gh of the wave's part: chunk gh / 2, 1 KB half gh % 2 of its codes,
+  // 16 bytes of the row's scales)
+  auto load_q40 = [&](u32x4 (&q)[T][QH], f32x4 (&z)[T][QH], int it) {
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int h = 0; h < QH; ++h) {
+        const int gh = it * QH + h;
+        q[t][h] = __builtin_nontemporal_load(gmem((const u32x4*)(wp[t] + (size_t)(gh >> 1) * 2048 + (gh & 1) * 1024)));
+        z[t][h] = __builtin_nontemporal_load(gmem((const f32x4*)(sbp[t] + (size_t)(gh >> 1) * 512 + (gh & 1) * 16)));
+      }
   };
   auto load_q4 = [&](u32x2 (&c)[T][GU], u32x4 (&sv)[T][GU], int it) {
 #pragma unroll
@@ -280,6 +305,9 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
     if constexpr (FMT == W_BF16) {
       load_bf(b0, xh0, xl0, 0);
       if (nit > 1) load_bf(b1, xh1, xl1, 1);
+    } else if constexpr (FMT == W_Q40) {
+      load_q40(qc0, qs0, 0);
+      if (nit > 1) load_q40(qc1, qs1, 1);
     } else if constexpr (FMT == W_I8) {
       load_i8(s0, 0);
       if (nit > 1) load_i8(s1, 1);
@@ -396,6 +424,15 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
       s += __shfl_xor(s, 2, 64);
       s += __shfl_xor(s, 4, 64);
       if ((kl & 63) == 0) xsum[m * ng + (k0 + kl) / 64] = s;
+    } else if (FMT == W_Q40) {
+      // per block of 32 (four lanes' 8 columns), the sum of the hi + lo parts
+      // the MFMAs multiply, so that the code offset cancels exactly
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += __uint_as_float(hi[e] << 16) + __uint_as_float(lo[e] << 16);
+      s += __shfl_xor(s, 1, 64);
+      s += __shfl_xor(s, 2, 64);
+      if ((kl & 31) == 0) xsum[m * (K / 32) + (k0 + kl) / 32] = s;
     }
     return ss;
   };
@@ -476,6 +513,57 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
     }
   };
 
+  // Q4_0 (blocks of 32 four-bit codes c around 8 with one scale s each:
+  // w = s (c - 8)): the activations are the MFMA's A operand and the codes its
+  // B operand, so D lane l holds activation rows 4 j4 + v of weight row r16 and
+  // takes one block scale.  Lane (r16, j4) of block b holds the codes of
+  // columns 32 b + 8 j4 .. + 7 (nibble slots 0-3: even elements, 4-7: odd),
+  // which enter as the exact bf16 values 128 + c; the block's MFMAs start
+  // from -136 times the sum of the same hi + lo activation parts, so the
+  // offset cancels up to the fp32 accumulation, leaving one scale FMA per
+  // block (for one activation row, only D row 0 is kept).
+  auto compute_q40 = [&](f32x4 (&acc)[T], const u32x4 (&q)[T][QH], const f32x4 (&z)[T][QH], int it) {
+#pragma unroll
+    for (int hb = 0; hb < 4 * QH; ++hb) {
+      const int h = hb >> 2, b = hb & 3;  // block b of half it * QH + h
+      u32x4 xh = {0u, 0u, 0u, 0u}, xl = {0u, 0u, 0u, 0u};
+      const int kl = (it * QH + h) * 128 + 32 * b + 8 * j4;
+      if (col_on) {
+        xh = *(const u32x4*)(xs_hi + r16 * xstride + kl);
+        xl = *(const u32x4*)(xs_lo + r16 * xstride + kl);
+      }
+      const bf16x8 Ah = __builtin_bit_cast(bf16x8, xh), Al = __builtin_bit_cast(bf16x8, xl);
+      const int xb = (k0 + (it * QH + h) * 128) / 32 + b;  // the block's index in xsum rows
+      f32x4 init = {0.f, 0.f, 0.f, 0.f};
+      if (M == 1) {
+        const float x0 = xsum[xb];
+        init[0] = j4 == 0 ? -136.0f * x0 : 0.f;
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int m = 4 * j4 + v;
+          init[v] = m < M ? -136.0f * xsum[m * (K / 32) + xb] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const uint32_t w = q[t][h][b];
+        const u32x4 bv = {0x43004300u | (w & 0x000F000Fu), 0x43004300u | ((w >> 4) & 0x000F000Fu),
+                          0x43004300u | ((w >> 8) & 0x000F000Fu), 0x43004300u | ((w >> 12) & 0x000F000Fu)};
+        const bf16x8 B = __builtin_bit_cast(bf16x8, bv);
+        f32x4 ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ah, B, init, 0, 0, 0);
+        ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Al, B, ag, 0, 0, 0);
+        const float sc = z[t][h][b];
+        if (M == 1) {  // (one activation row: only D row 0 is used)
+          acc[t][0] += sc * ag[0];
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[t][v] += sc * ag[v];
+        }
+      }
+    }
+  };
+
   // int8: lane (row r16, k group j4) holds codes 32 h + 8 j4 .. + 7 of each
   // 64-column block (h = 0, 1); each becomes the exact bf16 value q (an
   // integer of at most 8 bits is exact in fp32 and in the upper half of its
@@ -537,8 +625,13 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
 #pragma unroll
     for (int t = 0; t < T; ++t)
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        if (col_on) red[(r16 * RB + t * 16 + 4 * j4 + v) * WAVES + wave] = acc[t][v];
+      for (int v = 0; v < 4; ++v) {
+        if constexpr (FMT == W_Q40) {  // (D lane: activation row 4 j4 + v, weight row r16)
+          if (4 * j4 + v < M) red[((4 * j4 + v) * RB + t * 16 + r16) * WAVES + wave] = acc[t][v];
+        } else if (col_on) {
+          red[(r16 * RB + t * 16 + 4 * j4 + v) * WAVES + wave] = acc[t][v];
+        }
+      }
     lds_barrier();
     auto result = [&](const int i) -> float {
       float v = lds_sum(red + i * WAVES);
@@ -651,6 +744,13 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
         if (it + 1 < nit) compute_bf(acc, b1, xh1, xl1, it + 1);
       }
       in_pf = false;
+    } else if constexpr (FMT == W_Q40) {
+      for (int it = 0; it < nit; it += 2) {
+        if (it + 1 < nit && !(two && it == 0)) load_q40(qc1, qs1, it + 1);
+        compute_q40(acc, qc0, qs0, it);
+        if (it + 2 < nit) load_q40(qc0, qs0, it + 2);
+        if (it + 1 < nit) compute_q40(acc, qc1, qs1, it + 1);
+      }
     } else if constexpr (FMT == W_I8) {
       for (int it = 0; it < nit; it += 2) {
         if (it + 1 < nit && !(two && it == 0)) load_i8(s1, it + 1);

@@ -109,6 +109,15 @@ size_t skinny_lds_bytes(int M, int kchunk, int rows, int fmt);
 // 16-row tiles per lm_head tile of the persistent step with int8 weights
 // (measured, 8B: 1 / 2 / 4 -> head phase 130.4 / 112.6 / 110.7 us)
 constexpr int MEGA_HEAD_I8_TILES = 2;
+// Q4_0 in the persistent step: 16-row tiles per gate / up tile and per lm_head
+// tile (the head's 64-row tiles stream four iterations deep; 96-row gate / up
+// tiles, one per compute unit at 2 x 12288 rows, spill registers)
+constexpr int MEGA_GU_Q40_TILES = 2, MEGA_HEAD_Q40_TILES = 4;
+// 16-row tiles per gate / up and lm_head tile of the persistent step
+constexpr int mega_gu_tiles(int fmt) { return fmt == W_Q40 ? MEGA_GU_Q40_TILES : 2; }
+constexpr int mega_head_tiles(int fmt, bool small) {
+  return small ? 2 : fmt == W_I8 ? MEGA_HEAD_I8_TILES : fmt == W_Q40 ? MEGA_HEAD_Q40_TILES : 1;
+}
 
 // ---- decode GEMV with the whole K in one workgroup (gemv.hip)
 // Weights are given in the re-tiled fragment layout (launch_tile_bf16 /
@@ -181,7 +190,9 @@ hipError_t launch_tile_q40s(const uint16_t* src, float* dst, int N, int K, hipSt
 // k-step s at (s / 4) * 1024 + l * 16 + (s % 4) * 4, its nibble n holding
 // element 2n (n < 4) or 2 (n - 4) + 1 of columns 32 s + 8 (l / 16) .. + 7
 hipError_t launch_tile_q40(const uint8_t* src, uint32_t* dst, int N, int K, hipStream_t stream);
-hipError_t launch_q40_to_f16(const uint8_t* q, const uint16_t* d, int rows, int K, _Float16* dst, hipStream_t stream);
+// lo: the residual w - fp16(w) of each weight instead of fp16(w) (likewise below)
+hipError_t launch_q40_to_f16(const uint8_t* q, const uint16_t* d, int rows, int K, _Float16* dst, hipStream_t stream,
+                             bool lo = false);
 
 // ---- decode attention (split-K over the context, merged in-kernel)
 struct AttnDecodeArgs {
@@ -266,9 +277,10 @@ hipError_t launch_add(int n, const float* in, float* out, hipStream_t stream);
 hipError_t launch_bf16_to_f16(const uint16_t* src, _Float16* dst, size_t n, hipStream_t stream);
 hipError_t launch_i8_to_f16(const int8_t* q, const uint16_t* sc, int rows, int K, _Float16* dst,
                             hipStream_t stream);
-hipError_t launch_q8_to_f16(const int8_t* q, const float* sf, int rows, int K, _Float16* dst, hipStream_t stream);
+hipError_t launch_q8_to_f16(const int8_t* q, const float* sf, int rows, int K, _Float16* dst, hipStream_t stream,
+                            bool lo = false);
 hipError_t launch_q4_to_f16(const uint32_t* codes, const uint16_t* sc, const uint16_t* bi, int rows, int K,
-                            _Float16* dst, hipStream_t stream);
+                            _Float16* dst, hipStream_t stream, bool lo = false);
 hipError_t launch_f32_to_f16(const float* src, _Float16* dst, size_t n, hipStream_t stream);
 
 // ---- prefill GEMM (fp16 MFMA): C[m][n] = sum_k A[m][k] B[n][k]
@@ -345,10 +357,11 @@ struct MegaArgs {
   int M, n_layers, H, vocab;
   const MegaLayer* layers;
   GemvArgs head;
-  int fmt;                           // W_BF16 or W_Q4 (every linear, the embedding included)
+  int fmt;                           // W_BF16, W_Q4, W_I8 or W_Q40 (every linear, the embedding included)
   int small;                         // GEMVs reduce 128 columns per wave and iteration (rows of 1024 k)
   const void* emb;                   // bf16 [vocab][H], or 4-bit codes [vocab][H / 8] words
-  const uint16_t* emb_sc;            // 4-bit: per-64 scales / biases [vocab][H / 64]
+  const uint16_t* emb_sc;            // MLX 4-bit: per-64 scales / biases [vocab][H / 64]; int8: the
+                                     //   bf16 row scales; Q4_0: the fp16 block scales [vocab][H / 32]
   const uint16_t* emb_bi;
   RowParam rows[16];                 // the rows' token / position / slot (by value: no upload per step)
   const int32_t* ids_dev;            // token ids, or null: rp[m].token

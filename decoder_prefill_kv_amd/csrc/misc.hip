@@ -444,25 +444,33 @@ __global__ void tile_q40_kernel(const uint8_t* src, uint32_t* dst, int N, int K)
   }
 }
 
-__global__ void q40_to_f16_kernel(const uint8_t* q, const uint16_t* d, int rows, int K, _Float16* dst) {
+// The dequantizing copies: the value (exact in fp32) rounded to fp16, or
+// with lo set what that rounding left (w - fp16(w), exact in fp16 for these
+// formats' few significant bits)
+DPK_DEV _Float16 f16_part(float w, int lo) {
+  const _Float16 h = (_Float16)w;
+  return lo ? (_Float16)(w - (float)h) : h;
+}
+
+__global__ void q40_to_f16_kernel(const uint8_t* q, const uint16_t* d, int rows, int K, _Float16* dst, int lo) {
   const size_t n = (size_t)rows * K;
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
     const size_t b = i / 32;  // block of the flat array (K % 32 == 0)
     const int ib = (int)(i & 31);
     const uint8_t byte = q[b * 16 + (ib & 15)];
     const int c = ib < 16 ? (byte & 0xF) : (byte >> 4);
-    dst[i] = (_Float16)((float)__builtin_bit_cast(_Float16, d[b]) * (float)(c - 8));
+    dst[i] = f16_part((float)__builtin_bit_cast(_Float16, d[b]) * (float)(c - 8), lo);
   }
 }
 
-__global__ void q8_to_f16_kernel(const int8_t* q, const float* sf, int rows, int K, _Float16* dst) {
+__global__ void q8_to_f16_kernel(const int8_t* q, const float* sf, int rows, int K, _Float16* dst, int lo) {
   const size_t n = (size_t)rows * K;
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-    dst[i] = (_Float16)(sf[i / 32] * (float)q[i]);  // K % 32 == 0: block i / 32 of the flat array
+    dst[i] = f16_part(sf[i / 32] * (float)q[i], lo);  // K % 32 == 0: block i / 32 of the flat array
 }
 
 __global__ void q4_to_f16_kernel(const uint32_t* codes, const uint16_t* sc, const uint16_t* bi, int rows, int K,
-                                 _Float16* dst) {
+                                 _Float16* dst, int lo) {
   const size_t n = (size_t)rows * K;
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
     const size_t r = i / K;
@@ -470,7 +478,7 @@ __global__ void q4_to_f16_kernel(const uint32_t* codes, const uint16_t* sc, cons
     const uint32_t word = codes[r * (K / 8) + k / 8];
     const float c = (float)((word >> (4 * (k & 7))) & 0xF);
     const size_t g = r * (K / 64) + k / 64;
-    dst[i] = (_Float16)(bf16_to_f32(sc[g]) * c + bf16_to_f32(bi[g]));
+    dst[i] = f16_part(bf16_to_f32(sc[g]) * c + bf16_to_f32(bi[g]), lo);
   }
 }
 
@@ -593,20 +601,22 @@ hipError_t launch_tile_q40(const uint8_t* src, uint32_t* dst, int N, int K, hipS
   return hipGetLastError();
 }
 
-hipError_t launch_q40_to_f16(const uint8_t* q, const uint16_t* d, int rows, int K, _Float16* dst, hipStream_t stream) {
-  launch(q40_to_f16_kernel, dim3(grid_for((size_t)rows * K, 256)), dim3(256), 0, stream, q, d, rows, K, dst);
+hipError_t launch_q40_to_f16(const uint8_t* q, const uint16_t* d, int rows, int K, _Float16* dst, hipStream_t stream,
+                             bool lo) {
+  launch(q40_to_f16_kernel, dim3(grid_for((size_t)rows * K, 256)), dim3(256), 0, stream, q, d, rows, K, dst, (int)lo);
   return hipGetLastError();
 }
 
-hipError_t launch_q8_to_f16(const int8_t* q, const float* sf, int rows, int K, _Float16* dst, hipStream_t stream) {
-  launch(q8_to_f16_kernel, dim3(grid_for((size_t)rows * K, 256)), dim3(256), 0, stream, q, sf, rows, K, dst);
+hipError_t launch_q8_to_f16(const int8_t* q, const float* sf, int rows, int K, _Float16* dst, hipStream_t stream,
+                            bool lo) {
+  launch(q8_to_f16_kernel, dim3(grid_for((size_t)rows * K, 256)), dim3(256), 0, stream, q, sf, rows, K, dst, (int)lo);
   return hipGetLastError();
 }
 
 hipError_t launch_q4_to_f16(const uint32_t* codes, const uint16_t* sc, const uint16_t* bi, int rows, int K,
-                            _Float16* dst, hipStream_t stream) {
+                            _Float16* dst, hipStream_t stream, bool lo) {
   launch(q4_to_f16_kernel, dim3(grid_for((size_t)rows * K, 256)), dim3(256), 0, stream, codes, sc, bi,
-                     rows, K, dst);
+                     rows, K, dst, (int)lo);
   return hipGetLastError();
 }
 

@@ -55,6 +55,7 @@ struct LayerW {
   const void* k_norm = nullptr;
   // prefill operands (fp16, in the prep buffer)
   _Float16 *qkv16 = nullptr, *o16 = nullptr, *gate16 = nullptr, *up16 = nullptr, *down16 = nullptr;
+  _Float16* kvlo16 = nullptr;  // block formats over an int8 cache: w - fp16(w) of the K and V rows
 };
 
 }  // namespace
@@ -223,12 +224,24 @@ size_t tiled_bytes(const dpk_config& c, size_t rows, size_t cols) {
   return up(rows * cols / 2) + up(rows * (cols / 64) * 4);  // codes + (s, b) pairs
 }
 
+// Block-scaled weights (MLX 4-bit, Q8, Q4_0) whose prefill copy rounds each
+// weight to fp16, over an int8 KV cache: the K and V projections also get the
+// rounding residual, so the keys and values the cache quantizes come from the
+// exact weights (the rounding of the copy alone moved enough of them across a
+// code boundary to take an 8B-shaped Q4_0 prefill to 0.03 from the exact
+// logits, against 0.006 over the fp16 cache).
+bool kv_lo_copy(const dpk_config& c) {
+  return (c.flags & DPK_FLAG_KV_I8) &&
+         (c.weight_format == DPK_FMT_Q4G64 || c.weight_format == DPK_FMT_Q8 || c.weight_format == DPK_FMT_Q40);
+}
+
 size_t prep_bytes(const dpk_config& c) {
   if (c.weight_format == DPK_FMT_F32) return 0;
   const size_t H = c.hidden, I = c.intermediate, d = c.head_dim;
   const size_t Nqkv = (c.n_heads + 2 * c.n_kv_heads) * d, Qd = (size_t)c.n_heads * d, KVd = (size_t)c.n_kv_heads * d;
   // fp16 prefill operands
   size_t per = up(Nqkv * H * 2) + up(H * Qd * 2) + 2 * up(I * H * 2) + up(H * I * 2);
+  if (kv_lo_copy(c)) per += up(2 * KVd * H * 2);
   // decode copies
   per += tiled_bytes(c, Qd, H) + 2 * tiled_bytes(c, KVd, H) + tiled_bytes(c, H, Qd) + 2 * tiled_bytes(c, I, H) +
          tiled_bytes(c, H, I);
@@ -694,9 +707,9 @@ dpk_status forward_decode(dpk_model* md, int M, int max_ctx, const int32_t* ids_
 }
 
 // GEMV tiling of the persistent decode kernel for the loaded model: 0 when
-// every GEMV row splits over eight waves at 256 columns per iteration (bf16),
-// 1 at 128 columns (every row length a multiple of 1024; bf16 or 4-bit), -1
-// when neither fits.
+// every GEMV row splits over eight waves at 256 columns per iteration (bf16,
+// int8 per row, Q4_0), 1 at 128 columns (every row length a multiple of 1024;
+// bf16 or MLX 4-bit), -1 when neither fits.
 int mega_variant(const dpk_model* md) {
   const dpk_config& c = md->cfg;
   const int H = c.hidden, Qd = c.n_heads * c.head_dim, I = c.intermediate;
@@ -708,6 +721,11 @@ int mega_variant(const dpk_model* md) {
   // int8 codes with one scale per row: 256 columns per iteration on eight waves only
   if (md->fmt == DPK_FMT_I8 && gemv_waves(H, 1, W_I8) == 8 && gemv_waves(Qd, 1, W_I8) == 8 &&
       gemv_waves(H, 2, W_I8) == 8 && gemv_waves(I, 1, W_I8) == 8)
+    return 0;
+  // Q4_0: 512 (one-tile GEMVs: O, down) or 256 columns or fewer per wave and
+  // iteration on eight waves; gate / up in 96-row and the lm_head in 64-row tiles
+  if (md->fmt == DPK_FMT_Q40 && H % 2048 == 0 && Qd % 4096 == 0 && I % 4096 == 0 &&
+      (2 * I) % (16 * MEGA_GU_Q40_TILES) == 0 && c.vocab % (16 * MEGA_HEAD_Q40_TILES) == 0)
     return 0;
   return -1;
 }
@@ -734,8 +752,8 @@ int mega_o_rt(const dpk_model* md, int M) {
 }
 
 // LDS bytes of the persistent decode kernel for M rows, or 0 if the model or
-// M does not fit it: bf16, 4-bit or int8-per-row weights (with an int8 KV
-// cache: bf16 with the fused O projection, or int8), head_dim 128, 1, 2 or 4 query
+// M does not fit it: bf16, MLX 4-bit, int8-per-row or Q4_0 weights (with an
+// int8 KV cache: bf16 with the fused O projection, int8 or Q4_0), head_dim 128, 1, 2 or 4 query
 // heads per KV head (2 or 4 for the 128-column tiling), every GEMV on eight
 // waves, LDS within the device's per-workgroup limit, one resident workgroup
 // per CU.
@@ -745,7 +763,7 @@ size_t mega_lds_for(dpk_model* md, int M, int max_ctx) {
   if (c.head_dim != 128 || c.n_heads % c.n_kv_heads) return 0;
   const int G = c.n_heads / c.n_kv_heads;
   if (G != 1 && G != 2 && G != 4) return 0;
-  if (!decode_fits(md, M)) return 0;
+  if (md->fmt != DPK_FMT_Q40 && !decode_fits(md, M)) return 0;  // (Q4_0: the persistent step only)
   const int var = mega_variant(md);
   if (var < 0) return 0;
   const int fmt = wfmt(md);
@@ -757,8 +775,8 @@ size_t mega_lds_for(dpk_model* md, int M, int max_ctx) {
     if (ob > lds) lds = ob;
   }
   for (size_t b : {gemv_lds_bytes_waves(M, H, var ? 1 : 2, fmt, 8), gemv_lds_bytes_waves(M, Qd, 1, fmt, 8),
-                   gemv_lds_bytes_waves(M, H, 2, fmt, 8), gemv_lds_bytes_waves(M, I, 1, fmt, 8),
-                   gemv_lds_bytes_waves(M, H, fmt == W_I8 ? MEGA_HEAD_I8_TILES : 1, fmt, 8)})
+                   gemv_lds_bytes_waves(M, H, mega_gu_tiles(fmt), fmt, 8), gemv_lds_bytes_waves(M, I, 1, fmt, 8),
+                   gemv_lds_bytes_waves(M, H, mega_head_tiles(fmt, var == 1), fmt, 8)})
     lds = b > lds ? b : lds;
   // + the staged layer / head arguments and row parameters, + (bf16) the
   // GEMVs' prefetch slots
@@ -821,7 +839,7 @@ dpk_status forward_mega(dpk_model* md, int M, int max_ctx, size_t lds, const Row
   a.fmt = wfmt(md);
   a.small = mega_variant(md) == 1;
   a.emb = md->embed.w;
-  a.emb_sc = md->embed.sc;
+  a.emb_sc = (const uint16_t*)embed_scales(md);
   a.emb_bi = md->embed.bi;
   if (M > 16) return fail(DPK_EINVAL, "internal: persistent step of more than 16 rows");
   for (int m = 0; m < M; ++m) a.rows[m] = rows[m];
@@ -1007,6 +1025,13 @@ dpk_status forward_gemm(dpk_model* md, int M, int start, int seq, bool want_head
     } else {
       g.epi = GEMM_STORE_F32; g.C = md->qkv; g.ldc = md->Nqkv;
       if ((s2 = gemm_prof(K_GEMM_QKV, g))) return s2;
+      if (L.kvlo16) {  // + the K and V rows' rounding residuals (block formats over an int8 cache)
+        GemmArgs g2{};
+        g2.M = M; g2.N = 2 * c.n_kv_heads * d; g2.K = 2 * H; g2.Kb = H;
+        g2.A = md->y16; g2.lda = 2 * H; g2.B = L.kvlo16; g2.ldb = H;
+        g2.epi = GEMM_ADD_F32; g2.C = md->qkv + Qd; g2.ldc = md->Nqkv;
+        if ((s2 = gemm_prof(K_GEMM_QKV, g2))) return s2;
+      }
       ProfScope ps(md, st, K_QK_ROPE_KV, (double)M * md->Nqkv * 6, 0);
       HIP_TRY(launch_qk_rope_kv(M, md->qkv, c.n_heads, c.n_kv_heads, d, c.qk_norm, L.q_norm, L.k_norm, 0, c.rms_eps,
                                 md->rope_cos, md->rope_sin, md->rows_dev, md->q16, 2, md->kvd, l, st));
@@ -1315,14 +1340,14 @@ dpk_status dpk_load_weights(dpk_model* md, const dpk_tensor* t, int32_t n, void*
   hipStream_t st = (hipStream_t)stream;
   if (fmt != DPK_FMT_F32) {
     char* p = (char*)md->prep;
-    auto conv = [&](const LinearW& w, _Float16* dst) -> hipError_t {
+    auto conv = [&](const LinearW& w, _Float16* dst, bool lo = false) -> hipError_t {
       if (fmt == DPK_FMT_BF16) return launch_bf16_to_f16((const uint16_t*)w.w, dst, (size_t)w.rows * w.cols, st);
       // int8 per row: the codes (exact in fp16); the GEMMs apply the row scales
       if (fmt == DPK_FMT_I8) return launch_i8_to_f16((const int8_t*)w.w, nullptr, w.rows, w.cols, dst, st);
-      if (fmt == DPK_FMT_Q8) return launch_q8_to_f16((const int8_t*)w.w, w.sf, w.rows, w.cols, dst, st);
+      if (fmt == DPK_FMT_Q8) return launch_q8_to_f16((const int8_t*)w.w, w.sf, w.rows, w.cols, dst, st, lo);
       if (fmt == DPK_FMT_Q40)
-        return launch_q40_to_f16((const uint8_t*)w.w, (const uint16_t*)w.sf, w.rows, w.cols, dst, st);
-      return launch_q4_to_f16((const uint32_t*)w.w, w.sc, w.bi, w.rows, w.cols, dst, st);
+        return launch_q40_to_f16((const uint8_t*)w.w, (const uint16_t*)w.sf, w.rows, w.cols, dst, st, lo);
+      return launch_q4_to_f16((const uint32_t*)w.w, w.sc, w.bi, w.rows, w.cols, dst, st, lo);
     };
     for (int l = 0; l < c.n_layers; ++l) {
       LayerW& L = md->layers[l];
@@ -1343,6 +1368,12 @@ dpk_status dpk_load_weights(dpk_model* md, const dpk_tensor* t, int32_t n, void*
       L.down16 = (_Float16*)p;
       HIP_TRY(conv(L.down, L.down16));
       p += up((size_t)H * I * 2);
+      if (kv_lo_copy(c)) {
+        L.kvlo16 = (_Float16*)p;
+        HIP_TRY(conv(L.k, L.kvlo16, true));
+        HIP_TRY(conv(L.v, L.kvlo16 + (size_t)KVd * H, true));
+        p += up((size_t)2 * KVd * H * 2);
+      }
     }
     // fragment-order decode copies
     auto tile = [&](LinearW& w) -> hipError_t {

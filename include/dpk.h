@@ -151,11 +151,15 @@ dpk_status dpk_create(const dpk_config* cfg, dpk_model** out);
 /* Bytes of the three caller-provided device buffers:
  *   kv:      max_batch x n_layers x {K, V} x n_kv_heads x S x head_dim elements with
  *            S = max_seq rounded up to a multiple of 64 (fp32 for DPK_FMT_F32, fp16
- *            otherwise); K rows per position, V stored transposed (positions
- *            contiguous per channel);
+ *            otherwise, int8 codes with DPK_FLAG_KV_I8 followed by the fp32 scales);
+ *            K rows per position, V stored transposed (positions contiguous per
+ *            channel);
  *   scratch: activations, partial sums, counters, RoPE tables (256-byte aligned);
- *   prep:    fp16 copy of the linear layers used as prefill MFMA operands
- *            (0 for DPK_FMT_F32). */
+ *   prep:    fp16 copy of the linear layers used as prefill MFMA operands (int8
+ *            per row: the codes themselves), the fragment-order copies the decode
+ *            GEMVs stream, and for block-scaled formats over an int8 cache the
+ *            fp16 rounding residuals of the K and V projections (0 for
+ *            DPK_FMT_F32). */
 dpk_status dpk_workspace_size(const dpk_model* m, size_t* kv_bytes, size_t* scratch_bytes,
                               size_t* prep_bytes);
 

@@ -93,6 +93,24 @@ def test_int8_code_formats_prep_holds_fp16_operands_and_fragment_order_codes(dpk
         dpk.destroy(h)
 
 
+@pytest.mark.parametrize("fmt,lo", [("FMT_BF16", False), ("FMT_I8", False), ("FMT_Q8", True), ("FMT_Q40", True),
+                                    ("FMT_Q4G64", True)])
+def test_int8_kv_cache_adds_kv_residuals_for_block_formats(dpk, fmt, lo):
+    """Over an int8 KV cache the prep buffer of a block-scaled model (MLX
+    4-bit, Q8, Q4_0) also holds the fp16 rounding residuals of the K and V
+    projections (2 bytes per weight of those rows); exact fp16 copies (bf16,
+    int8 codes) need none."""
+    sizes = []
+    for flags in (0, dpk.FLAG_KV_I8):
+        h = dpk.create(cfg_ok(dpk, weight_format=getattr(dpk, fmt), flags=flags))
+        try:
+            sizes.append(dpk.workspace_size(h)[2])
+        finally:
+            dpk.destroy(h)
+    kv_rows = 2 * 8 * 128  # K and V rows of a layer (8 KV heads of 128)
+    assert sizes[1] - sizes[0] == (2 * kv_rows * 1024 * 2 if lo else 0)
+
+
 def test_int8_kv_cache_sizes_and_format_check(dpk):
     """int8 KV cache: one byte per cached element, then (at a 256-byte
     boundary) one fp32 scale per position of every slab; refused for fp32

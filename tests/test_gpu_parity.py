@@ -74,6 +74,14 @@ CASES = [
     ("q06b_q40-L2-stream", synth.Q06B_Q40.with_(n_layers=2), 37, 6, dict(flags=STREAM)),
     ("q8b_q40-L1-v4096-gemm", synth.Q8B_Q40.with_(n_layers=1, vocab=4096), 21, 5, {}),
     ("q8b_q40-L2-v4096-chunked", synth.Q8B_Q40.with_(n_layers=2, vocab=4096), 300, 4, dict(max_rows=128)),
+    # Q4_0 in the persistent step (decode positions crossing a 256-position
+    # chunk), over the fp16 and the int8 cache (the prefill's K and V then
+    # include the fp16 copy's rounding residuals)
+    ("q8b_q40-L2-v4096-persistent", synth.Q8B_Q40.with_(n_layers=2, vocab=4096), 250, 8, dict(max_rows=256)),
+    ("q8b_q40-kvi8-L2-v4096-persistent", synth.Q8B_Q40.with_(n_layers=2, vocab=4096, kv_i8=True), 250, 8,
+     dict(max_rows=256)),
+    ("q8b_q40-kvi8-L2-v4096-short", synth.Q8B_Q40.with_(n_layers=2, vocab=4096, kv_i8=True), 40, 4, {}),
+    ("q06b_q4-kvi8-L2-gemm", synth.Q06B_Q4.with_(n_layers=2, kv_i8=True), 40, 4, {}),
 ]
 
 
@@ -116,6 +124,7 @@ PERSISTENT_CFGS = [
     ("q8b-L1-v4096-ctx4100", synth.Q8B.with_(n_layers=1, vocab=4096), 4080),
     ("q06b_q4-L1-v4096-ctx4100", synth.Q06B_Q4.with_(n_layers=1, vocab=4096), 4080),
     ("q8b_i8-L2-v4096", synth.Q8B_I8.with_(n_layers=2, vocab=4096), 250),    # int8 codes, one scale per row
+    ("q8b_q40-L2-v4096", synth.Q8B_Q40.with_(n_layers=2, vocab=4096), 250),  # Q4_0 blocks
 ]
 
 
@@ -159,6 +168,8 @@ PATH_CASES = [
     ("q06b-kvi8-L1", synth.Q06B.with_(n_layers=1, kv_i8=True), False),
     ("q8b-kvi8-L1-v4096", synth.Q8B.with_(n_layers=1, vocab=4096, kv_i8=True), True),
     ("q8b_i8-kvi8-L1-v4096", synth.Q8B_I8.with_(n_layers=1, vocab=4096, kv_i8=True), True),
+    ("q8b_q40-L1-v4096", synth.Q8B_Q40.with_(n_layers=1, vocab=4096), True),
+    ("q8b_q8-L1-v4096", synth.Q8B_Q8.with_(n_layers=1, vocab=4096), False),
     ("q8b_i8-L1-v4096", synth.Q8B_I8.with_(n_layers=1, vocab=4096), True),
 ]
 
