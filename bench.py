@@ -29,18 +29,18 @@ MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 matrix throughput
 # (--copy-probe): FETCH_SIZE x 2.0, WRITE_SIZE x 1.0.  A figure is only
 # reported while the kernel's sources are the ones it was taken on.
 TRAFFIC = {
-    ("q8b", "decode.step"): {"fetch_kib": 7563906.8, "write_kib": 50617.4, "fetch_factor": 2.0, "write_factor": 1.0,
+    ("q8b", "decode.step"): {"fetch_kib": 7563828.1, "write_kib": 50617.4, "fetch_factor": 2.0, "write_factor": 1.0,
                              "sources": ["decoder_prefill_kv_amd/csrc/decode_step.hip",
                                          "decoder_prefill_kv_amd/csrc/gemv_body.h",
                                          "decoder_prefill_kv_amd/csrc/common.h",
                                          "decoder_prefill_kv_amd/csrc/kernels.h"],
-                             "sha256": "157760266d420c7c7374075e7c0ee3c58c7dba1757dc133fb7beb87837ecfcfb"},
+                             "sha256": "7925154e337f7b6f6a661da047242b129a76192699644b1c3c8fe7a0823aa08a"},
     # the prefill gate+up GEMM (M = 2048): operands re-read from HBM ~3.5x
-    ("q8b", "gemm.gate_up"): {"fetch_kib": 381042.8, "write_kib": 49152.6, "fetch_factor": 2.0, "write_factor": 1.0,
+    ("q8b", "gemm.gate_up"): {"fetch_kib": 379342.1, "write_kib": 57601.0, "fetch_factor": 2.0, "write_factor": 1.0,
                               "sources": ["decoder_prefill_kv_amd/csrc/gemm.hip",
                                           "decoder_prefill_kv_amd/csrc/common.h",
                                           "decoder_prefill_kv_amd/csrc/kernels.h"],
-                              "sha256": "e7d0729d0db0be76ccec5f401e5066106645a1cdd6f77d00b59482dcd9fc2814"},
+                              "sha256": "69645ccb86410fdc7c044202d33c3e22fb511ac28628d41aa125018b2afdfdd8"},
 }
 
 
@@ -357,7 +357,8 @@ def run_workload(dpk, name, steps, warmup, seed, flags, decode_steps=None, profi
         avg_s = v["total_ms"] / 1e3 / v["launches"]
         ach = v["bytes"] / v["launches"] / avg_s / 1e9
         roof = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name, dom),
+                "frac": round(ach / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(name + ("+kv_i8" if cfg.kv_i8 else ""), dom),
                 "bytes_per_launch": v["bytes"] / v["launches"], "avg_launch_us": round(avg_s * 1e6, 2)}
         gem = {k: v for k, v in stats.items() if k.startswith("gemm")}
         if gem:
@@ -367,7 +368,7 @@ def run_workload(dpk, name, steps, warmup, seed, flags, decode_steps=None, profi
             achg = g["flops"] / g["launches"] / avg_g / 1e12
             roof_prefill = {"bound": "mfma", "kernel": domg, "achieved": round(achg, 1), "peak": MFMA_PEAK_TFLOPS,
                             "unit": "TFLOP/s", "frac": round(achg / MFMA_PEAK_TFLOPS, 4),
-                            "traffic": measured_traffic(name, domg),
+                            "traffic": measured_traffic(name + ("+kv_i8" if cfg.kv_i8 else ""), domg),
                             "flops_per_launch": g["flops"] / g["launches"], "avg_launch_us": round(avg_g * 1e6, 2)}
     dec.close()
     del dec

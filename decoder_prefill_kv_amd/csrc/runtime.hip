@@ -870,7 +870,8 @@ dpk_status forward_mega(dpk_model* md, int M, int max_ctx, size_t lds, const Row
   const double Qd = (double)c.n_heads * c.head_dim;
   const double params = (double)c.n_layers * ((double)md->Nqkv * H + H * Qd + 3.0 * c.intermediate * H) +
                         (double)c.vocab * H;
-  const double kvb = (kv_positions + M) * 2.0 * c.n_kv_heads * c.head_dim * 2.0 * c.n_layers;
+  const double kv_elt = md->kvd.i8 ? 1 + 4.0 / c.head_dim : 2.0;  // (int8 cache: codes + one fp32 scale per vector)
+  const double kvb = (kv_positions + M) * 2.0 * c.n_kv_heads * c.head_dim * kv_elt * c.n_layers;
   ProfScope ps(md, st, K_DECODE_STEP, params * wbytes_per_elem(md->fmt) + kvb,
                2.0 * M * params + 4.0 * kv_positions * Qd * c.n_layers);
   if (md->prof) md->prof_step_kv += kv_positions + M;
