@@ -143,6 +143,9 @@ DPK_DEV void embed_phase(const MegaArgs& a, const RowParam* rows, int wg, int nw
           v = bf16_to_f32(a.emb_sc[gi]) * (float)((word >> (4 * (col & 7))) & 0xFu) + bf16_to_f32(a.emb_bi[gi]);
         } else if (a.fmt == W_I8) {  // int8 with one bf16 scale per row
           v = bf16_to_f32(a.emb_sc[tok]) * (float)((const int8_t*)a.emb)[(size_t)tok * a.H + col];
+        } else if (a.fmt == W_Q8) {  // int8 in blocks of 32 with an fp32 scale each
+          v = ((const float*)a.emb_sc)[(size_t)tok * (a.H / 32) + col / 32] *
+              (float)((const int8_t*)a.emb)[(size_t)tok * a.H + col];
         } else if (a.fmt == W_Q40) {  // blocks of 32 codes around 8, fp16 scale; byte j: codes j, j + 16
           const int i = col & 31;
           const uint8_t b = ((const uint8_t*)a.emb)[(size_t)tok * (a.H / 2) + (col / 32) * 16 + (i & 15)];
@@ -971,8 +974,8 @@ __global__ __launch_bounds__(MT, 1) void decode_step_kernel(MegaArgs a) {
 }  // namespace
 
 // The variants over an int8 KV cache (256 columns per iteration): bf16 with
-// the fused O projection, int8 weights (one scale per row) and Q4_0 weights,
-// G = 1, 2, 4.
+// the fused O projection, int8 weights (one scale per row), Q8 and Q4_0
+// weights, G = 1, 2, 4.
 const void* mega_kernel_kv8(int G, int fmt, bool small, bool fo) {
   if (small) return nullptr;
   if (fmt == W_BF16 && fo) {
@@ -987,14 +990,18 @@ const void* mega_kernel_kv8(int G, int fmt, bool small, bool fo) {
     if (G == 1) return (const void*)decode_step_kernel<1, W_Q40, false, false, true>;
     if (G == 2) return (const void*)decode_step_kernel<2, W_Q40, false, false, true>;
     if (G == 4) return (const void*)decode_step_kernel<4, W_Q40, false, false, true>;
+  } else if (fmt == W_Q8 && !fo) {
+    if (G == 1) return (const void*)decode_step_kernel<1, W_Q8, false, false, true>;
+    if (G == 2) return (const void*)decode_step_kernel<2, W_Q8, false, false, true>;
+    if (G == 4) return (const void*)decode_step_kernel<4, W_Q8, false, false, true>;
   }
   return nullptr;
 }
 
 }  // namespace dpk
 #else
-// Built variants (fp16 KV cache): bf16, int8 (one scale per row) and Q4_0 at
-// 256 columns per iteration for G = 1, 2, 4; bf16 and 4-bit at 128 columns for
+// Built variants (fp16 KV cache): bf16, int8 (one scale per row), Q8 and Q4_0
+// at 256 columns per iteration for G = 1, 2, 4; bf16 and 4-bit at 128 columns for
 // G = 2, 4; bf16 with and without the fused O projection.  The int8-cache
 // variants are built in a translation unit of their own (mega_kernel_kv8).
 template <bool FO>
@@ -1017,6 +1024,12 @@ const void* mega_kernel_fo(int G, int fmt, bool small) {
     if (G == 1) return (const void*)decode_step_kernel<1, W_Q40, false, false, false>;
     if (G == 2) return (const void*)decode_step_kernel<2, W_Q40, false, false, false>;
     if (G == 4) return (const void*)decode_step_kernel<4, W_Q40, false, false, false>;
+    return nullptr;
+  }
+  if (fmt == W_Q8 && !small && !FO) {  // Q8 blocks: 256-column chunks of scales
+    if (G == 1) return (const void*)decode_step_kernel<1, W_Q8, false, false, false>;
+    if (G == 2) return (const void*)decode_step_kernel<2, W_Q8, false, false, false>;
+    if (G == 4) return (const void*)decode_step_kernel<4, W_Q8, false, false, false>;
     return nullptr;
   }
   if (!small) return nullptr;

@@ -138,7 +138,7 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
                        unsigned char* pf = nullptr, bool pf_ready = false) {
   static_assert(!PF || (FMT == W_BF16 && !XG), "LDS prefetch is for staged-x bf16 GEMVs");
   static_assert(!XG || FMT == W_BF16, "ready-made activations are for bf16 weights");
-  static_assert(FMT != W_Q40 || KI == 0, "Q4_0: whole 128-column halves per iteration");
+  static_assert((FMT != W_Q40 && FMT != W_Q8) || KI == 0, "Q4_0 / Q8: whole blocks per iteration");
   constexpr int RB = 16 * T;
   constexpr int THREADS = 64 * WAVES;
   const int K = a.K;                      // columns this call reduces over
@@ -178,7 +178,13 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
   // Q4_0: QH halves of 128 columns (4 blocks of 32 each) per tile and
   // iteration, 4 KB of codes per wave and iteration
   constexpr int QH = 4 / T > 0 ? 4 / T : 1;
-  const int nit = (FMT == W_BF16) ? kq / (32 * U) : (FMT == W_Q40) ? kq / (128 * QH) : kq / (64 * GU);
+  // Q8: NG8 groups of 64 columns (2 blocks of 32 each) per tile and iteration,
+  // 4 KB of codes per wave and iteration
+  constexpr int NG8 = 4 / T > 0 ? 4 / T : 1;
+  const int nit = (FMT == W_BF16) ? kq / (32 * U)
+                  : (FMT == W_Q40) ? kq / (128 * QH)
+                  : (FMT == W_Q8)  ? kq / (64 * NG8)
+                                   : kq / (64 * GU);
   const unsigned char* wp[T];   // this wave's stream inside each 16-row tile
   const unsigned char* sbp[T];  // 4-bit: scale/bias stream; int8: the tile's row scales (bf16)
   uint32_t rsc[T][2];           // int8: bf16 scales of rows 4 j4 .. 4 j4 + 3 of each tile
@@ -195,6 +201,12 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
         // lane l's 16 bytes: MFMA k-steps 2g and 2g + 1 of row l % 16
         wp[t] = (const unsigned char*)a.w[seg] + (rt * (KF / 64) + (KO + k0) / 64) * 1024 + lane * 16;
         sbp[t] = (const unsigned char*)a.sb[seg] + (rt * 16 + 4 * j4) * 2;
+      } else if (FMT == W_Q8) {
+        // Q8 codes: block (rt, g) (16 rows x 64 columns) at ((rt * K/64) + g) * 1024, lane
+        // l's 16 bytes: codes 32 h + 8 (l / 16) .. + 7 of row l % 16 (h = 0, 1); the blocks'
+        // fp32 scales as for Q4_0 (row r's 8 of 256 columns at 32 r of the chunk's 512 bytes)
+        wp[t] = (const unsigned char*)a.w[seg] + (rt * (KF / 64) + (KO + k0) / 64) * 1024 + lane * 16;
+        sbp[t] = (const unsigned char*)a.sb[seg] + ((rt * (KF / 256) + (KO + k0) / 256) * 16 + r16) * 32;
       } else if (FMT == W_Q40) {
         // Q4_0 codes of chunk (rt, c) (16 rows x 256 columns) at ((rt * K/256) + c) * 2048,
         // lane l's 16 bytes at l * 16 of each 1 KB half (blocks 0-3, then 4-7); the
@@ -213,6 +225,8 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
   u32x2 c0[T][GU], c1[T][GU];
   u32x4 s0[T][GU], s1[T][GU];
   u32x4 qc0[T][QH], qc1[T][QH];  // Q4_0: the halves' codes (4 blocks each)
+  u32x4 g8c0[T][NG8], g8c1[T][NG8];  // Q8: the groups' codes (2 blocks each)
+  u32x2 g8s0[T][NG8], g8s1[T][NG8];  // and lane row r16's 2 block scales of each (fp32 bits)
   f32x4 qs0[T][QH], qs1[T][QH];  // and lane row r16's 4 block scales of each
   // XG: each iteration's activation fragments are loaded with its weights, so
   // one wait covers both and the next iteration's loads stay in flight.  Rows
@@ -253,6 +267,17 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
         const int gh = it * QH + h;
         q[t][h] = __builtin_nontemporal_load(gmem((const u32x4*)(wp[t] + (size_t)(gh >> 1) * 2048 + (gh & 1) * 1024)));
         z[t][h] = __builtin_nontemporal_load(gmem((const f32x4*)(sbp[t] + (size_t)(gh >> 1) * 512 + (gh & 1) * 16)));
+      }
+  };
+  // (group gg of the wave's part: codes at gg KB, scales of chunk gg / 4 at 8 (gg % 4))
+  auto load_q8 = [&](u32x4 (&q)[T][NG8], u32x2 (&z)[T][NG8], int it) {
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int u = 0; u < NG8; ++u) {
+        const int gg = it * NG8 + u;
+        q[t][u] = __builtin_nontemporal_load(gmem((const u32x4*)(wp[t] + (size_t)gg * 1024)));
+        z[t][u] = __builtin_nontemporal_load(gmem((const u32x2*)(sbp[t] + (size_t)(gg >> 2) * 512 + (gg & 3) * 8)));
       }
   };
   auto load_q4 = [&](u32x2 (&c)[T][GU], u32x4 (&sv)[T][GU], int it) {
@@ -308,6 +333,9 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
     } else if constexpr (FMT == W_Q40) {
       load_q40(qc0, qs0, 0);
       if (nit > 1) load_q40(qc1, qs1, 1);
+    } else if constexpr (FMT == W_Q8) {
+      load_q8(g8c0, g8s0, 0);
+      if (nit > 1) load_q8(g8c1, g8s1, 1);
     } else if constexpr (FMT == W_I8) {
       load_i8(s0, 0);
       if (nit > 1) load_i8(s1, 1);
@@ -564,6 +592,47 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
     }
   };
 
+  // Q8 (blocks of 32 int8 codes q with one fp32 scale s each: w = s q): the
+  // same transposed roles as Q4_0; each lane's 8 codes of a block become exact
+  // bf16 values (an integer of at most 8 bits is exact in fp32 and in the
+  // upper half of its bits), and one FMA per block applies the scale.
+  auto compute_q8 = [&](f32x4 (&acc)[T], const u32x4 (&q)[T][NG8], const u32x2 (&z)[T][NG8], int it) {
+#pragma unroll
+    for (int u = 0; u < NG8; ++u) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        u32x4 xh = {0u, 0u, 0u, 0u}, xl = {0u, 0u, 0u, 0u};
+        const int kl = (it * NG8 + u) * 64 + 32 * h + 8 * j4;
+        if (col_on) {
+          xh = *(const u32x4*)(xs_hi + r16 * xstride + kl);
+          xl = *(const u32x4*)(xs_lo + r16 * xstride + kl);
+        }
+        const bf16x8 Ah = __builtin_bit_cast(bf16x8, xh), Al = __builtin_bit_cast(bf16x8, xl);
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const uint32_t w0 = h ? q[t][u][2] : q[t][u][0], w1 = h ? q[t][u][3] : q[t][u][1];
+          uint32_t f[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            f[e] = __float_as_uint((float)(int)(int8_t)(((e < 4 ? w0 : w1) >> (8 * (e & 3))) & 0xFFu));
+          const u32x4 bv = {__builtin_amdgcn_perm(f[1], f[0], 0x07060302u), __builtin_amdgcn_perm(f[3], f[2], 0x07060302u),
+                            __builtin_amdgcn_perm(f[5], f[4], 0x07060302u), __builtin_amdgcn_perm(f[7], f[6], 0x07060302u)};
+          const bf16x8 B = __builtin_bit_cast(bf16x8, bv);
+          f32x4 ag = {0.f, 0.f, 0.f, 0.f};
+          ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ah, B, ag, 0, 0, 0);
+          ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Al, B, ag, 0, 0, 0);
+          const float sc = __uint_as_float(z[t][u][h]);
+          if (M == 1) {  // (one activation row: only D row 0 is used)
+            acc[t][0] += sc * ag[0];
+          } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[t][v] += sc * ag[v];
+          }
+        }
+      }
+    }
+  };
+
   // int8: lane (row r16, k group j4) holds codes 32 h + 8 j4 .. + 7 of each
   // 64-column block (h = 0, 1); each becomes the exact bf16 value q (an
   // integer of at most 8 bits is exact in fp32 and in the upper half of its
@@ -626,7 +695,7 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
     for (int t = 0; t < T; ++t)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        if constexpr (FMT == W_Q40) {  // (D lane: activation row 4 j4 + v, weight row r16)
+        if constexpr (FMT == W_Q40 || FMT == W_Q8) {  // (D lane: activation row 4 j4 + v, weight row r16)
           if (4 * j4 + v < M) red[((4 * j4 + v) * RB + t * 16 + r16) * WAVES + wave] = acc[t][v];
         } else if (col_on) {
           red[(r16 * RB + t * 16 + 4 * j4 + v) * WAVES + wave] = acc[t][v];
@@ -750,6 +819,13 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
         compute_q40(acc, qc0, qs0, it);
         if (it + 2 < nit) load_q40(qc0, qs0, it + 2);
         if (it + 1 < nit) compute_q40(acc, qc1, qs1, it + 1);
+      }
+    } else if constexpr (FMT == W_Q8) {
+      for (int it = 0; it < nit; it += 2) {
+        if (it + 1 < nit && !(two && it == 0)) load_q8(g8c1, g8s1, it + 1);
+        compute_q8(acc, g8c0, g8s0, it);
+        if (it + 2 < nit) load_q8(g8c0, g8s0, it + 2);
+        if (it + 1 < nit) compute_q8(acc, g8c1, g8s1, it + 1);
       }
     } else if constexpr (FMT == W_I8) {
       for (int it = 0; it < nit; it += 2) {

@@ -708,7 +708,7 @@ dpk_status forward_decode(dpk_model* md, int M, int max_ctx, const int32_t* ids_
 
 // GEMV tiling of the persistent decode kernel for the loaded model: 0 when
 // every GEMV row splits over eight waves at 256 columns per iteration (bf16,
-// int8 per row, Q4_0), 1 at 128 columns (every row length a multiple of 1024;
+// int8 per row, Q8, Q4_0), 1 at 128 columns (every row length a multiple of 1024;
 // bf16 or MLX 4-bit), -1 when neither fits.
 int mega_variant(const dpk_model* md) {
   const dpk_config& c = md->cfg;
@@ -726,6 +726,11 @@ int mega_variant(const dpk_model* md) {
   // iteration on eight waves; gate / up in 96-row and the lm_head in 64-row tiles
   if (md->fmt == DPK_FMT_Q40 && H % 2048 == 0 && Qd % 4096 == 0 && I % 4096 == 0 &&
       (2 * I) % (16 * MEGA_GU_Q40_TILES) == 0 && c.vocab % (16 * MEGA_HEAD_Q40_TILES) == 0)
+    return 0;
+  // Q8: 256 columns or fewer per wave and iteration, whole 256-column chunks of
+  // block scales per wave; the lm_head in 64-row tiles
+  if (md->fmt == DPK_FMT_Q8 && H % 2048 == 0 && Qd % 2048 == 0 && I % 2048 == 0 &&
+      c.vocab % (16 * mega_head_tiles(W_Q8, false)) == 0)
     return 0;
   return -1;
 }
@@ -752,8 +757,8 @@ int mega_o_rt(const dpk_model* md, int M) {
 }
 
 // LDS bytes of the persistent decode kernel for M rows, or 0 if the model or
-// M does not fit it: bf16, MLX 4-bit, int8-per-row or Q4_0 weights (with an
-// int8 KV cache: bf16 with the fused O projection, int8 or Q4_0), head_dim 128, 1, 2 or 4 query
+// M does not fit it: bf16, MLX 4-bit, int8-per-row, Q8 or Q4_0 weights (with an
+// int8 KV cache: bf16 with the fused O projection, int8, Q8 or Q4_0), head_dim 128, 1, 2 or 4 query
 // heads per KV head (2 or 4 for the 128-column tiling), every GEMV on eight
 // waves, LDS within the device's per-workgroup limit, one resident workgroup
 // per CU.
@@ -763,7 +768,8 @@ size_t mega_lds_for(dpk_model* md, int M, int max_ctx) {
   if (c.head_dim != 128 || c.n_heads % c.n_kv_heads) return 0;
   const int G = c.n_heads / c.n_kv_heads;
   if (G != 1 && G != 2 && G != 4) return 0;
-  if (md->fmt != DPK_FMT_Q40 && !decode_fits(md, M)) return 0;  // (Q4_0: the persistent step only)
+  // (Q8, Q4_0: the persistent step only)
+  if (md->fmt != DPK_FMT_Q40 && md->fmt != DPK_FMT_Q8 && !decode_fits(md, M)) return 0;
   const int var = mega_variant(md);
   if (var < 0) return 0;
   const int fmt = wfmt(md);

@@ -82,6 +82,10 @@ CASES = [
      dict(max_rows=256)),
     ("q8b_q40-kvi8-L2-v4096-short", synth.Q8B_Q40.with_(n_layers=2, vocab=4096, kv_i8=True), 40, 4, {}),
     ("q06b_q4-kvi8-L2-gemm", synth.Q06B_Q4.with_(n_layers=2, kv_i8=True), 40, 4, {}),
+    # Q8 in the persistent step, over the fp16 and the int8 cache
+    ("q8b_q8-L2-v4096-persistent", synth.Q8B_Q8.with_(n_layers=2, vocab=4096), 250, 8, dict(max_rows=256)),
+    ("q8b_q8-kvi8-L2-v4096-persistent", synth.Q8B_Q8.with_(n_layers=2, vocab=4096, kv_i8=True), 250, 8,
+     dict(max_rows=256)),
 ]
 
 
@@ -125,6 +129,7 @@ PERSISTENT_CFGS = [
     ("q06b_q4-L1-v4096-ctx4100", synth.Q06B_Q4.with_(n_layers=1, vocab=4096), 4080),
     ("q8b_i8-L2-v4096", synth.Q8B_I8.with_(n_layers=2, vocab=4096), 250),    # int8 codes, one scale per row
     ("q8b_q40-L2-v4096", synth.Q8B_Q40.with_(n_layers=2, vocab=4096), 250),  # Q4_0 blocks
+    ("q8b_q8-L2-v4096", synth.Q8B_Q8.with_(n_layers=2, vocab=4096), 250),    # Q8 blocks
 ]
 
 
@@ -169,7 +174,7 @@ PATH_CASES = [
     ("q8b-kvi8-L1-v4096", synth.Q8B.with_(n_layers=1, vocab=4096, kv_i8=True), True),
     ("q8b_i8-kvi8-L1-v4096", synth.Q8B_I8.with_(n_layers=1, vocab=4096, kv_i8=True), True),
     ("q8b_q40-L1-v4096", synth.Q8B_Q40.with_(n_layers=1, vocab=4096), True),
-    ("q8b_q8-L1-v4096", synth.Q8B_Q8.with_(n_layers=1, vocab=4096), False),
+    ("q8b_q8-L1-v4096", synth.Q8B_Q8.with_(n_layers=1, vocab=4096), True),
     ("q8b_i8-L1-v4096", synth.Q8B_I8.with_(n_layers=1, vocab=4096), True),
 ]
 
