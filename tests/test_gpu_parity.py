@@ -86,6 +86,18 @@ CASES = [
     ("q8b_q8-L2-v4096-persistent", synth.Q8B_Q8.with_(n_layers=2, vocab=4096), 250, 8, dict(max_rows=256)),
     ("q8b_q8-kvi8-L2-v4096-persistent", synth.Q8B_Q8.with_(n_layers=2, vocab=4096, kv_i8=True), 250, 8,
      dict(max_rows=256)),
+    # the persistent step's other query-group sizes: the int8 cache with 2 and 1
+    # query heads per KV head (bf16, fused O projection), Q4_0 with 2, Q8 with 1
+    ("h2048-g2-kvi8-L2-v4096-persistent",
+     synth.Q8B.with_(n_layers=2, hidden=2048, n_heads=16, n_kv_heads=8, intermediate=4096, vocab=4096, kv_i8=True),
+     250, 6, dict(max_rows=256)),
+    ("h2048-g1-kvi8-L2-v4096-persistent",
+     synth.Q8B.with_(n_layers=2, hidden=2048, n_heads=16, n_kv_heads=16, intermediate=4096, vocab=4096, kv_i8=True),
+     250, 6, dict(max_rows=256)),
+    ("q8b_q40-g2-L2-v4096-persistent", synth.Q8B_Q40.with_(n_layers=2, n_kv_heads=16, intermediate=4096, vocab=4096),
+     250, 6, dict(max_rows=256)),
+    ("q8b_q8-g1-L2-v4096-persistent", synth.Q8B_Q8.with_(n_layers=2, n_kv_heads=32, intermediate=4096, vocab=4096),
+     250, 6, dict(max_rows=256)),
 ]
 
 
@@ -175,6 +187,9 @@ PATH_CASES = [
     ("q8b_i8-kvi8-L1-v4096", synth.Q8B_I8.with_(n_layers=1, vocab=4096, kv_i8=True), True),
     ("q8b_q40-L1-v4096", synth.Q8B_Q40.with_(n_layers=1, vocab=4096), True),
     ("q8b_q8-L1-v4096", synth.Q8B_Q8.with_(n_layers=1, vocab=4096), True),
+    ("h2048-g1-kvi8-L1-v4096",
+     synth.Q8B.with_(n_layers=1, hidden=2048, n_heads=16, n_kv_heads=16, intermediate=4096, vocab=4096, kv_i8=True), True),
+    ("q8b_q8-g1-L1-v4096", synth.Q8B_Q8.with_(n_layers=1, n_kv_heads=32, intermediate=4096, vocab=4096), True),
     ("q8b_i8-L1-v4096", synth.Q8B_I8.with_(n_layers=1, vocab=4096), True),
 ]
 
