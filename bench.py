@@ -29,18 +29,18 @@ MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 matrix throughput
 # (--copy-probe): FETCH_SIZE x 2.0, WRITE_SIZE x 1.0.  A figure is only
 # reported while the kernel's sources are the ones it was taken on.
 TRAFFIC = {
-    ("q8b", "decode.step"): {"fetch_kib": 7563804.8, "write_kib": 50617.4, "fetch_factor": 2.0, "write_factor": 1.0,
+    ("q8b", "decode.step"): {"fetch_kib": 7563797.3, "write_kib": 50617.4, "fetch_factor": 2.0, "write_factor": 1.0,
                              "sources": ["decoder_prefill_kv_amd/csrc/decode_step.hip",
                                          "decoder_prefill_kv_amd/csrc/gemv_body.h",
                                          "decoder_prefill_kv_amd/csrc/common.h",
                                          "decoder_prefill_kv_amd/csrc/kernels.h"],
-                             "sha256": "57a450b2220df365ccab5485073abe09a8cc059189efb7b785280dfcba597148"},
+                             "sha256": "3b49d659bf368dd6580afa4c45e55f9e0f782f0a638ad2688283a1c2c44dd3c5"},
     # the prefill gate+up GEMM (M = 2048): operands re-read from HBM ~3.5x
-    ("q8b", "gemm.gate_up"): {"fetch_kib": 380812.3, "write_kib": 57600.3, "fetch_factor": 2.0, "write_factor": 1.0,
+    ("q8b", "gemm.gate_up"): {"fetch_kib": 380115.7, "write_kib": 57600.2, "fetch_factor": 2.0, "write_factor": 1.0,
                               "sources": ["decoder_prefill_kv_amd/csrc/gemm.hip",
                                           "decoder_prefill_kv_amd/csrc/common.h",
                                           "decoder_prefill_kv_amd/csrc/kernels.h"],
-                              "sha256": "11cdf55885cebca4f3aa6a25ef4b27f277c3a65071a9c0f565338a27ef9a1fd8"},
+                              "sha256": "15c777aa1a76b008eef2c4f3647196fc80532306c426484492dda718c3d82c7a"},
 }
 
 

@@ -224,10 +224,10 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
   u32x4 b0[T][U], b1[T][U];
   u32x2 c0[T][GU], c1[T][GU];
   u32x4 s0[T][GU], s1[T][GU];
-  u32x4 qc0[T][QH], qc1[T][QH];  // Q4_0: the halves' codes (4 blocks each)
+  u32x4 qc0[T][QH], qc1[T][QH];      // Q4_0: the halves' codes (4 blocks each)
+  f32x4 qs0[T][QH], qs1[T][QH];      //   and lane row r16's 4 block scales of each
   u32x4 g8c0[T][NG8], g8c1[T][NG8];  // Q8: the groups' codes (2 blocks each)
-  u32x2 g8s0[T][NG8], g8s1[T][NG8];  // and lane row r16's 2 block scales of each (fp32 bits)
-  f32x4 qs0[T][QH], qs1[T][QH];  // and lane row r16's 4 block scales of each
+  u32x2 g8s0[T][NG8], g8s1[T][NG8];  //   and lane row r16's 2 block scales of each (fp32 bits)
   // XG: each iteration's activation fragments are loaded with its weights, so
   // one wait covers both and the next iteration's loads stay in flight.  Rows
   // past M read row M - 1 (their results are never stored).

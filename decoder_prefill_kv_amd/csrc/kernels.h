@@ -109,14 +109,15 @@ size_t skinny_lds_bytes(int M, int kchunk, int rows, int fmt);
 // 16-row tiles per lm_head tile of the persistent step with int8 weights
 // (measured, 8B: 1 / 2 / 4 -> head phase 130.4 / 112.6 / 110.7 us)
 constexpr int MEGA_HEAD_I8_TILES = 2;
-// Q4_0 and Q8 in the persistent step: 16-row tiles per gate / up tile and per lm_head
-// tile (the head's 64-row tiles stream four iterations deep; 96-row gate / up
-// tiles, one per compute unit at 2 x 12288 rows, spill registers)
-constexpr int MEGA_GU_Q40_TILES = 2, MEGA_HEAD_Q40_TILES = 4;
+// Block formats (Q8, Q4_0) in the persistent step: 16-row tiles per gate / up
+// tile and per lm_head tile (the head's 64-row tiles stream four iterations
+// deep; 96-row gate / up tiles, one per compute unit at 2 x 12288 rows, spill
+// registers)
+constexpr int MEGA_GU_BLK_TILES = 2, MEGA_HEAD_BLK_TILES = 4;
 // 16-row tiles per gate / up and lm_head tile of the persistent step
-constexpr int mega_gu_tiles(int fmt) { return fmt == W_Q40 ? MEGA_GU_Q40_TILES : 2; }
+constexpr int mega_gu_tiles(int fmt) { return (fmt == W_Q40 || fmt == W_Q8) ? MEGA_GU_BLK_TILES : 2; }
 constexpr int mega_head_tiles(int fmt, bool small) {
-  return small ? 2 : fmt == W_I8 ? MEGA_HEAD_I8_TILES : (fmt == W_Q40 || fmt == W_Q8) ? MEGA_HEAD_Q40_TILES : 1;
+  return small ? 2 : fmt == W_I8 ? MEGA_HEAD_I8_TILES : (fmt == W_Q40 || fmt == W_Q8) ? MEGA_HEAD_BLK_TILES : 1;
 }
 
 // ---- decode GEMV with the whole K in one workgroup (gemv.hip)
@@ -359,7 +360,8 @@ struct MegaArgs {
   GemvArgs head;
   int fmt;                           // W_BF16, W_Q4, W_I8, W_Q8 or W_Q40 (every linear, the embedding included)
   int small;                         // GEMVs reduce 128 columns per wave and iteration (rows of 1024 k)
-  const void* emb;                   // bf16 [vocab][H], or 4-bit codes [vocab][H / 8] words
+  const void* emb;                   // bf16 [vocab][H], MLX 4-bit codes [vocab][H / 8] words, int8 / Q8
+                                     //   codes [vocab][H], or Q4_0 codes [vocab][H / 2] bytes
   const uint16_t* emb_sc;            // MLX 4-bit: per-64 scales / biases [vocab][H / 64]; int8: the
                                      //   bf16 row scales; Q4_0: the fp16 block scales [vocab][H / 32];
                                      //   Q8: the fp32 block scales [vocab][H / 32]

@@ -725,12 +725,12 @@ int mega_variant(const dpk_model* md) {
   // Q4_0: 512 (one-tile GEMVs: O, down) or 256 columns or fewer per wave and
   // iteration on eight waves; gate / up in 96-row and the lm_head in 64-row tiles
   if (md->fmt == DPK_FMT_Q40 && H % 2048 == 0 && Qd % 4096 == 0 && I % 4096 == 0 &&
-      (2 * I) % (16 * MEGA_GU_Q40_TILES) == 0 && c.vocab % (16 * MEGA_HEAD_Q40_TILES) == 0)
+      (2 * I) % (16 * mega_gu_tiles(W_Q40)) == 0 && c.vocab % (16 * mega_head_tiles(W_Q40, false)) == 0)
     return 0;
   // Q8: 256 columns or fewer per wave and iteration, whole 256-column chunks of
   // block scales per wave; the lm_head in 64-row tiles
   if (md->fmt == DPK_FMT_Q8 && H % 2048 == 0 && Qd % 2048 == 0 && I % 2048 == 0 &&
-      c.vocab % (16 * mega_head_tiles(W_Q8, false)) == 0)
+      (2 * I) % (16 * mega_gu_tiles(W_Q8)) == 0 && c.vocab % (16 * mega_head_tiles(W_Q8, false)) == 0)
     return 0;
   return -1;
 }
