@@ -445,6 +445,13 @@ def main():
                 extra[name] = r
                 log("[bench] %s: decode %.1f tok/s, prefill %.0f tok/s"
                     % (name, r["decode_tok_s"], r["prefill_tok_s"]))
+            # the 8B-shaped model with integer-code weights (prefill 2048 + 64 decode steps)
+            for name in ("q8b_i8", "q8b_q8", "q8b_q40"):
+                r, _, _, _ = run_workload(dpk, name, 1, 1, args.seed, flags)
+                extra[name] = r
+                log("[bench] %s: decode %.1f tok/s, prefill %.0f tok/s"
+                    % (name, r["decode_tok_s"], r["prefill_tok_s"]))
+                torch.cuda.empty_cache()
     except DeviceError as e:
         print("bench.py: device-side error, no result reported: %s" % e, file=sys.stderr, flush=True)
         sys.exit(3)
