@@ -384,6 +384,37 @@ def test_batched_decode_int8_8b_rows(dpk):
     dec.close()
 
 
+@pytest.mark.parametrize("name,cfg", [("q8", synth.Q8B_Q8.with_(n_layers=1, vocab=4096)),
+                                      ("q4_0", synth.Q8B_Q40.with_(n_layers=1, vocab=4096))], ids=["q8", "q4_0"])
+def test_batched_persistent_decode_block_formats_8b_rows(dpk, name, cfg):
+    """Two sequences of an 8B-shaped Q8 / Q4_0 model decoded together in one
+    persistent launch (contexts of one and two chunks): the block modes' D rows
+    1..M-1, which batch-1 steps never use."""
+    w = synth.make_weights(cfg, 0)
+    lens, N = [200, 300], 3
+    prompts = [synth.prompt_ids(cfg, L, 0, index=b) for b, L in enumerate(lens)]
+    runs = [oracle_greedy(cfg, w, p, N)[1] for p in prompts]
+    dec = dpk.Decoder(cfg, w, max_batch=2, max_seq=320, max_rows=256)
+    for b in range(2):
+        dec.prefill(b, [int(t) for t in prompts[b]])
+    lg, am = dec.logits_buffer(2), dec.argmax_buffer(2)
+    worst = 0.0
+    for s in range(N):
+        toks = [runs[b]["ids"][s] for b in range(2)]
+        if s == 0:
+            dpk.profile_begin(dec.handle, 10000)
+        dec.decode_step([0, 1], toks, [lens[b] + s for b in range(2)], am, lg)
+        if s == 0:
+            stats = dpk.profile_end(dec.handle)
+            assert "decode.step" in stats, sorted(stats)
+        for b in range(2):
+            worst = max(worst, compare_logits(lg[b].cpu(), runs[b]["logits"][s + 1], TOL[cfg.weight_format],
+                                              "%s row %d step %d" % (name, b, s)))
+    dpk.check_device_errors(dec.handle)
+    dec.close()
+    print("\n[parity] %s 2-row persistent worst max-abs %.3g" % (name, worst), flush=True)
+
+
 @pytest.mark.parametrize("name,cfg", BATCHED_PERSISTENT, ids=[c[0] for c in BATCHED_PERSISTENT])
 def test_batched_persistent_decode_long_contexts(dpk, name, cfg):
     """Three sequences decoded together through the persistent step (M = 3
