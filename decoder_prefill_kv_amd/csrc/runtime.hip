@@ -768,8 +768,9 @@ size_t mega_lds_for(dpk_model* md, int M, int max_ctx) {
   if (c.head_dim != 128 || c.n_heads % c.n_kv_heads) return 0;
   const int G = c.n_heads / c.n_kv_heads;
   if (G != 1 && G != 2 && G != 4) return 0;
-  // (Q8, Q4_0: the persistent step only)
-  if (md->fmt != DPK_FMT_Q40 && md->fmt != DPK_FMT_Q8 && !decode_fits(md, M)) return 0;
+  // (the integer-code formats are bounded by the LDS check below alone: their
+  // one-launch-per-kernel GEMVs are not the gemv_kernel decode_fits sizes)
+  if (md->fmt != DPK_FMT_Q40 && md->fmt != DPK_FMT_Q8 && md->fmt != DPK_FMT_I8 && !decode_fits(md, M)) return 0;
   const int var = mega_variant(md);
   if (var < 0) return 0;
   const int fmt = wfmt(md);

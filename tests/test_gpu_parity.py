@@ -356,11 +356,9 @@ BATCHED_PERSISTENT = [("q06b-L2", synth.Q06B.with_(n_layers=2)), ("q06b_q4-L2", 
 
 
 def test_batched_decode_int8_8b_rows(dpk):
-    """Two sequences of an 8B-shaped int8 model decoded together (contexts of
-    one and two chunks).  At 8B shapes the persistent step takes one row (the
-    staged activations of two do not fit its LDS), so two rows take the
-    one-launch-per-kernel path; batch-1 steps of the same model the
-    persistent one."""
+    """Two sequences of an 8B-shaped int8 model decoded together in one
+    persistent launch (contexts of one and two chunks; the staged activations
+    of two rows fit its LDS beside the int8 mode's buffers)."""
     cfg = synth.Q8B_I8.with_(n_layers=1, vocab=4096)
     w = synth.make_weights(cfg, 0)
     lens, N = [200, 300], 3
@@ -377,7 +375,7 @@ def test_batched_decode_int8_8b_rows(dpk):
         dec.decode_step([0, 1], toks, [lens[b] + s for b in range(2)], am, lg)
         if s == 0:
             stats = dpk.profile_end(dec.handle)
-            assert "decode.step" not in stats and "gemv.gate_up" in stats, sorted(stats)
+            assert "decode.step" in stats, sorted(stats)
         for b in range(2):
             compare_logits(lg[b].cpu(), runs[b]["logits"][s + 1], TOL["i8"], "int8 row %d step %d" % (b, s))
     dpk.check_device_errors(dec.handle)
