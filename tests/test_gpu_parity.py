@@ -86,6 +86,10 @@ CASES = [
     ("q8b_q8-L2-v4096-persistent", synth.Q8B_Q8.with_(n_layers=2, vocab=4096), 250, 8, dict(max_rows=256)),
     ("q8b_q8-kvi8-L2-v4096-persistent", synth.Q8B_Q8.with_(n_layers=2, vocab=4096, kv_i8=True), 250, 8,
      dict(max_rows=256)),
+    # the int8 cache at a long context in the persistent step: 16 attention
+    # chunks per (row, KV head) and their merge
+    ("q8b-kvi8-L1-v4096-ctx4100", synth.Q8B.with_(n_layers=1, vocab=4096, kv_i8=True), 4080, 4,
+     dict(max_rows=2048)),
     # the persistent step's other query-group sizes: the int8 cache with 2 and 1
     # query heads per KV head (bf16, fused O projection), Q4_0 with 2, Q8 with 1
     ("h2048-g2-kvi8-L2-v4096-persistent",
