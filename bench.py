@@ -35,6 +35,24 @@ TRAFFIC = {
                                          "decoder_prefill_kv_amd/csrc/common.h",
                                          "decoder_prefill_kv_amd/csrc/kernels.h"],
                              "sha256": "3b49d659bf368dd6580afa4c45e55f9e0f782f0a638ad2688283a1c2c44dd3c5"},
+    # the same step over the int8 cache and with integer-code weights (the Q4_0 copy's
+    # block scales are widened to fp32: 0.47 GB per launch beyond the format's fp16 scales)
+    ("q8b+kv_i8", "decode.step"): {"fetch_kib": 7500143.2, "write_kib": 50599.4, "fetch_factor": 2.0, "write_factor": 1.0,
+                             "sources": ["decoder_prefill_kv_amd/csrc/decode_step.hip", "decoder_prefill_kv_amd/csrc/gemv_body.h",
+                              "decoder_prefill_kv_amd/csrc/common.h", "decoder_prefill_kv_amd/csrc/kernels.h"],
+                             "sha256": "3b49d659bf368dd6580afa4c45e55f9e0f782f0a638ad2688283a1c2c44dd3c5"},
+    ("q8b_i8", "decode.step"): {"fetch_kib": 3874268.4, "write_kib": 14347.1, "fetch_factor": 2.0, "write_factor": 1.0,
+                             "sources": ["decoder_prefill_kv_amd/csrc/decode_step.hip", "decoder_prefill_kv_amd/csrc/gemv_body.h",
+                              "decoder_prefill_kv_amd/csrc/common.h", "decoder_prefill_kv_amd/csrc/kernels.h"],
+                             "sha256": "3b49d659bf368dd6580afa4c45e55f9e0f782f0a638ad2688283a1c2c44dd3c5"},
+    ("q8b_q8", "decode.step"): {"fetch_kib": 4485503.8, "write_kib": 14347.1, "fetch_factor": 2.0, "write_factor": 1.0,
+                             "sources": ["decoder_prefill_kv_amd/csrc/decode_step.hip", "decoder_prefill_kv_amd/csrc/gemv_body.h",
+                              "decoder_prefill_kv_amd/csrc/common.h", "decoder_prefill_kv_amd/csrc/kernels.h"],
+                             "sha256": "3b49d659bf368dd6580afa4c45e55f9e0f782f0a638ad2688283a1c2c44dd3c5"},
+    ("q8b_q40", "decode.step"): {"fetch_kib": 2498204.0, "write_kib": 14347.1, "fetch_factor": 2.0, "write_factor": 1.0,
+                             "sources": ["decoder_prefill_kv_amd/csrc/decode_step.hip", "decoder_prefill_kv_amd/csrc/gemv_body.h",
+                              "decoder_prefill_kv_amd/csrc/common.h", "decoder_prefill_kv_amd/csrc/kernels.h"],
+                             "sha256": "3b49d659bf368dd6580afa4c45e55f9e0f782f0a638ad2688283a1c2c44dd3c5"},
     # the prefill gate+up GEMM (M = 2048): operands re-read from HBM ~3.5x
     ("q8b", "gemm.gate_up"): {"fetch_kib": 380115.7, "write_kib": 57600.2, "fetch_factor": 2.0, "write_factor": 1.0,
                               "sources": ["decoder_prefill_kv_amd/csrc/gemm.hip",
