@@ -53,6 +53,15 @@ TRAFFIC = {
                              "sources": ["decoder_prefill_kv_amd/csrc/decode_step.hip", "decoder_prefill_kv_amd/csrc/gemv_body.h",
                               "decoder_prefill_kv_amd/csrc/common.h", "decoder_prefill_kv_amd/csrc/kernels.h"],
                              "sha256": "3b49d659bf368dd6580afa4c45e55f9e0f782f0a638ad2688283a1c2c44dd3c5"},
+    # the 0.6B-shaped steps (128 columns per wave and iteration; bf16, MLX 4-bit)
+    ("q06b", "decode.step"): {"fetch_kib": 618302.1, "write_kib": 4896.1, "fetch_factor": 2.0, "write_factor": 1.0,
+                             "sources": ["decoder_prefill_kv_amd/csrc/decode_step.hip", "decoder_prefill_kv_amd/csrc/gemv_body.h",
+                              "decoder_prefill_kv_amd/csrc/common.h", "decoder_prefill_kv_amd/csrc/kernels.h"],
+                             "sha256": "3b49d659bf368dd6580afa4c45e55f9e0f782f0a638ad2688283a1c2c44dd3c5"},
+    ("q06b_q4", "decode.step"): {"fetch_kib": 287295.0, "write_kib": 6492.1, "fetch_factor": 2.0, "write_factor": 1.0,
+                             "sources": ["decoder_prefill_kv_amd/csrc/decode_step.hip", "decoder_prefill_kv_amd/csrc/gemv_body.h",
+                              "decoder_prefill_kv_amd/csrc/common.h", "decoder_prefill_kv_amd/csrc/kernels.h"],
+                             "sha256": "3b49d659bf368dd6580afa4c45e55f9e0f782f0a638ad2688283a1c2c44dd3c5"},
     # the prefill gate+up GEMM (M = 2048): operands re-read from HBM ~3.5x
     ("q8b", "gemm.gate_up"): {"fetch_kib": 380115.7, "write_kib": 57600.2, "fetch_factor": 2.0, "write_factor": 1.0,
                               "sources": ["decoder_prefill_kv_amd/csrc/gemm.hip",
