@@ -29,45 +29,44 @@ MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 matrix throughput
 # (--copy-probe): FETCH_SIZE x 2.0, WRITE_SIZE x 1.0.  A figure is only
 # reported while the kernel's sources are the ones it was taken on.
 TRAFFIC = {
-    ("q8b", "decode.step"): {"fetch_kib": 7563797.3, "write_kib": 50617.4, "fetch_factor": 2.0, "write_factor": 1.0,
+    ("q8b", "decode.step"): {"fetch_kib": 7564262.2, "write_kib": 50617.4, "fetch_factor": 2.0, "write_factor": 1.0,
                              "sources": ["decoder_prefill_kv_amd/csrc/decode_step.hip",
                                          "decoder_prefill_kv_amd/csrc/gemv_body.h",
                                          "decoder_prefill_kv_amd/csrc/common.h",
                                          "decoder_prefill_kv_amd/csrc/kernels.h"],
-                             "sha256": "3b49d659bf368dd6580afa4c45e55f9e0f782f0a638ad2688283a1c2c44dd3c5"},
-    # the same step over the int8 cache and with integer-code weights (the Q4_0 copy's
-    # block scales are widened to fp32: 0.47 GB per launch beyond the format's fp16 scales)
-    ("q8b+kv_i8", "decode.step"): {"fetch_kib": 7500143.2, "write_kib": 50599.4, "fetch_factor": 2.0, "write_factor": 1.0,
+                             "sha256": "212dea11b5b1a96a50e615972a01152afb8b5188ebfb41ebb412ef6c38db2cd0"},
+    # the same step over the int8 cache and with integer-code weights
+    ("q8b+kv_i8", "decode.step"): {"fetch_kib": 7500119.2, "write_kib": 50599.4, "fetch_factor": 2.0, "write_factor": 1.0,
                              "sources": ["decoder_prefill_kv_amd/csrc/decode_step.hip", "decoder_prefill_kv_amd/csrc/gemv_body.h",
                               "decoder_prefill_kv_amd/csrc/common.h", "decoder_prefill_kv_amd/csrc/kernels.h"],
-                             "sha256": "3b49d659bf368dd6580afa4c45e55f9e0f782f0a638ad2688283a1c2c44dd3c5"},
-    ("q8b_i8", "decode.step"): {"fetch_kib": 3874268.4, "write_kib": 14347.1, "fetch_factor": 2.0, "write_factor": 1.0,
+                             "sha256": "212dea11b5b1a96a50e615972a01152afb8b5188ebfb41ebb412ef6c38db2cd0"},
+    ("q8b_i8", "decode.step"): {"fetch_kib": 3874079.6, "write_kib": 14347.1, "fetch_factor": 2.0, "write_factor": 1.0,
                              "sources": ["decoder_prefill_kv_amd/csrc/decode_step.hip", "decoder_prefill_kv_amd/csrc/gemv_body.h",
                               "decoder_prefill_kv_amd/csrc/common.h", "decoder_prefill_kv_amd/csrc/kernels.h"],
-                             "sha256": "3b49d659bf368dd6580afa4c45e55f9e0f782f0a638ad2688283a1c2c44dd3c5"},
-    ("q8b_q8", "decode.step"): {"fetch_kib": 4485503.8, "write_kib": 14347.1, "fetch_factor": 2.0, "write_factor": 1.0,
+                             "sha256": "212dea11b5b1a96a50e615972a01152afb8b5188ebfb41ebb412ef6c38db2cd0"},
+    ("q8b_q8", "decode.step"): {"fetch_kib": 4486667.4, "write_kib": 14347.1, "fetch_factor": 2.0, "write_factor": 1.0,
                              "sources": ["decoder_prefill_kv_amd/csrc/decode_step.hip", "decoder_prefill_kv_amd/csrc/gemv_body.h",
                               "decoder_prefill_kv_amd/csrc/common.h", "decoder_prefill_kv_amd/csrc/kernels.h"],
-                             "sha256": "3b49d659bf368dd6580afa4c45e55f9e0f782f0a638ad2688283a1c2c44dd3c5"},
-    ("q8b_q40", "decode.step"): {"fetch_kib": 2498204.0, "write_kib": 14347.1, "fetch_factor": 2.0, "write_factor": 1.0,
+                             "sha256": "212dea11b5b1a96a50e615972a01152afb8b5188ebfb41ebb412ef6c38db2cd0"},
+    ("q8b_q40", "decode.step"): {"fetch_kib": 2258004.6, "write_kib": 14347.1, "fetch_factor": 2.0, "write_factor": 1.0,
                              "sources": ["decoder_prefill_kv_amd/csrc/decode_step.hip", "decoder_prefill_kv_amd/csrc/gemv_body.h",
                               "decoder_prefill_kv_amd/csrc/common.h", "decoder_prefill_kv_amd/csrc/kernels.h"],
-                             "sha256": "3b49d659bf368dd6580afa4c45e55f9e0f782f0a638ad2688283a1c2c44dd3c5"},
+                             "sha256": "212dea11b5b1a96a50e615972a01152afb8b5188ebfb41ebb412ef6c38db2cd0"},
     # the 0.6B-shaped steps (128 columns per wave and iteration; bf16, MLX 4-bit)
-    ("q06b", "decode.step"): {"fetch_kib": 618302.1, "write_kib": 4896.1, "fetch_factor": 2.0, "write_factor": 1.0,
+    ("q06b", "decode.step"): {"fetch_kib": 618285.7, "write_kib": 4896.1, "fetch_factor": 2.0, "write_factor": 1.0,
                              "sources": ["decoder_prefill_kv_amd/csrc/decode_step.hip", "decoder_prefill_kv_amd/csrc/gemv_body.h",
                               "decoder_prefill_kv_amd/csrc/common.h", "decoder_prefill_kv_amd/csrc/kernels.h"],
-                             "sha256": "3b49d659bf368dd6580afa4c45e55f9e0f782f0a638ad2688283a1c2c44dd3c5"},
-    ("q06b_q4", "decode.step"): {"fetch_kib": 287295.0, "write_kib": 6492.1, "fetch_factor": 2.0, "write_factor": 1.0,
+                             "sha256": "212dea11b5b1a96a50e615972a01152afb8b5188ebfb41ebb412ef6c38db2cd0"},
+    ("q06b_q4", "decode.step"): {"fetch_kib": 287341.5, "write_kib": 6492.1, "fetch_factor": 2.0, "write_factor": 1.0,
                              "sources": ["decoder_prefill_kv_amd/csrc/decode_step.hip", "decoder_prefill_kv_amd/csrc/gemv_body.h",
                               "decoder_prefill_kv_amd/csrc/common.h", "decoder_prefill_kv_amd/csrc/kernels.h"],
-                             "sha256": "3b49d659bf368dd6580afa4c45e55f9e0f782f0a638ad2688283a1c2c44dd3c5"},
+                             "sha256": "212dea11b5b1a96a50e615972a01152afb8b5188ebfb41ebb412ef6c38db2cd0"},
     # the prefill gate+up GEMM (M = 2048): operands re-read from HBM ~3.5x
-    ("q8b", "gemm.gate_up"): {"fetch_kib": 380115.7, "write_kib": 57600.2, "fetch_factor": 2.0, "write_factor": 1.0,
+    ("q8b", "gemm.gate_up"): {"fetch_kib": 380246.7, "write_kib": 57600.4, "fetch_factor": 2.0, "write_factor": 1.0,
                               "sources": ["decoder_prefill_kv_amd/csrc/gemm.hip",
                                           "decoder_prefill_kv_amd/csrc/common.h",
                                           "decoder_prefill_kv_amd/csrc/kernels.h"],
-                              "sha256": "15c777aa1a76b008eef2c4f3647196fc80532306c426484492dda718c3d82c7a"},
+                              "sha256": "b45210dd7044baea62beaf1d0aa34b5186e72ef00b5c1ecda1fda5cdfcf2ba71"},
 }
 
 

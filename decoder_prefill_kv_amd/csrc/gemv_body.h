@@ -210,10 +210,10 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
       } else if (FMT == W_Q40) {
         // Q4_0 codes of chunk (rt, c) (16 rows x 256 columns) at ((rt * K/256) + c) * 2048,
         // lane l's 16 bytes at l * 16 of each 1 KB half (blocks 0-3, then 4-7); the
-        // blocks' scales (fp32) of row r at ((rt * K/256 + c) * 16 + r) * 32
+        // blocks' scales (fp16) of row r at ((rt * K/256 + c) * 16 + r) * 16
         const size_t ch = rt * (KF / 256) + (KO + k0) / 256;
         wp[t] = (const unsigned char*)a.w[seg] + ch * 2048 + lane * 16;
-        sbp[t] = (const unsigned char*)a.sb[seg] + (ch * 16 + r16) * 32;
+        sbp[t] = (const unsigned char*)a.sb[seg] + (ch * 16 + r16) * 16;
       } else {
         // codes block (rt, g) at ((rt * K/64) + g) * 512; scales (rt, g) at * 64
         wp[t] = (const unsigned char*)a.w[seg] + (rt * (KF / 64) + (KO + k0) / 64) * 512 + lane * 8;
@@ -225,7 +225,7 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
   u32x2 c0[T][GU], c1[T][GU];
   u32x4 s0[T][GU], s1[T][GU];
   u32x4 qc0[T][QH], qc1[T][QH];      // Q4_0: the halves' codes (4 blocks each)
-  f32x4 qs0[T][QH], qs1[T][QH];      //   and lane row r16's 4 block scales of each
+  u32x2 qs0[T][QH], qs1[T][QH];      //   and lane row r16's 4 block scales of each (fp16)
   u32x4 g8c0[T][NG8], g8c1[T][NG8];  // Q8: the groups' codes (2 blocks each)
   u32x2 g8s0[T][NG8], g8s1[T][NG8];  //   and lane row r16's 2 block scales of each (fp32 bits)
   // XG: each iteration's activation fragments are loaded with its weights, so
@@ -258,15 +258,15 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
         q[t][u] = __builtin_nontemporal_load(gmem((const u32x4*)(wp[t] + (size_t)(it * GU + u) * 1024)));
   };
   // (half gh of the wave's part: chunk gh / 2, 1 KB half gh % 2 of its codes,
-  // 16 bytes of the row's scales)
-  auto load_q40 = [&](u32x4 (&q)[T][QH], f32x4 (&z)[T][QH], int it) {
+  // 8 bytes of the row's scales)
+  auto load_q40 = [&](u32x4 (&q)[T][QH], u32x2 (&z)[T][QH], int it) {
 #pragma unroll
     for (int t = 0; t < T; ++t)
 #pragma unroll
       for (int h = 0; h < QH; ++h) {
         const int gh = it * QH + h;
         q[t][h] = __builtin_nontemporal_load(gmem((const u32x4*)(wp[t] + (size_t)(gh >> 1) * 2048 + (gh & 1) * 1024)));
-        z[t][h] = __builtin_nontemporal_load(gmem((const f32x4*)(sbp[t] + (size_t)(gh >> 1) * 512 + (gh & 1) * 16)));
+        z[t][h] = __builtin_nontemporal_load(gmem((const u32x2*)(sbp[t] + (size_t)(gh >> 1) * 256 + (gh & 1) * 8)));
       }
   };
   // (group gg of the wave's part: codes at gg KB, scales of chunk gg / 4 at 8 (gg % 4))
@@ -550,7 +550,7 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
   // from -136 times the sum of the same hi + lo activation parts, so the
   // offset cancels up to the fp32 accumulation, leaving one scale FMA per
   // block (for one activation row, only D row 0 is kept).
-  auto compute_q40 = [&](f32x4 (&acc)[T], const u32x4 (&q)[T][QH], const f32x4 (&z)[T][QH], int it) {
+  auto compute_q40 = [&](f32x4 (&acc)[T], const u32x4 (&q)[T][QH], const u32x2 (&z)[T][QH], int it) {
 #pragma unroll
     for (int hb = 0; hb < 4 * QH; ++hb) {
       const int h = hb >> 2, b = hb & 3;  // block b of half it * QH + h
@@ -581,7 +581,8 @@ DPK_DEV void gemv_body(const GemvArgs& a, const int M, unsigned char* lds, const
         const bf16x8 B = __builtin_bit_cast(bf16x8, bv);
         f32x4 ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ah, B, init, 0, 0, 0);
         ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Al, B, ag, 0, 0, 0);
-        const float sc = z[t][h][b];
+        const uint32_t zw = z[t][h][b >> 1];
+        const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)((b & 1) ? (zw >> 16) : (zw & 0xFFFFu)));
         if (M == 1) {  // (one activation row: only D row 0 is used)
           acc[t][0] += sc * ag[0];
         } else {

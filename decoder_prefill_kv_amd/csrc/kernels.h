@@ -184,8 +184,9 @@ hipError_t launch_tile_i8(const int8_t* src, int8_t* dst, int N, int K, hipStrea
 // fragment-order copy of q8 block scales [N][K/32]: per 16-row tile and 256
 // columns, 512 bytes holding row r's 8 scales at r * 32
 hipError_t launch_tile_q8s(const float* src, float* dst, int N, int K, hipStream_t stream);
-// the same for Q4_0 fp16 scales (widened to fp32, exact)
-hipError_t launch_tile_q40s(const uint16_t* src, float* dst, int N, int K, hipStream_t stream);
+// the same layout for Q4_0's fp16 scales, kept fp16: 256 bytes per tile and 256
+// columns, row r's 8 at r * 16
+hipError_t launch_tile_q40s(const uint16_t* src, uint16_t* dst, int N, int K, hipStream_t stream);
 // fragment-order copy of Q4_0 codes (GGUF blocks: byte j of a block's 16 holds
 // codes j and j + 16): per 16-row tile and 256 columns 2 KB, lane l's dword of
 // k-step s at (s / 4) * 1024 + l * 16 + (s % 4) * 4, its nibble n holding

@@ -413,12 +413,12 @@ __global__ void tile_q8s_kernel(const float* src, float* dst, int N, int K) {
   }
 }
 
-__global__ void tile_q40s_kernel(const uint16_t* src, float* dst, int N, int K) {
+__global__ void tile_q40s_kernel(const uint16_t* src, uint16_t* dst, int N, int K) {
   const size_t n = (size_t)N * (K / 32);
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
     const int s = (int)(i & 7), r = (int)((i >> 3) & 15);
     const size_t tk = i >> 7, kt = tk % (K / 256), rt = tk / (K / 256);
-    dst[i] = (float)__builtin_bit_cast(_Float16, src[(16 * rt + r) * (size_t)(K / 32) + 8 * kt + s]);
+    dst[i] = src[(16 * rt + r) * (size_t)(K / 32) + 8 * kt + s];  // (fp16 bits, as given)
   }
 }
 
@@ -589,7 +589,7 @@ hipError_t launch_tile_q8s(const float* src, float* dst, int N, int K, hipStream
   return hipGetLastError();
 }
 
-hipError_t launch_tile_q40s(const uint16_t* src, float* dst, int N, int K, hipStream_t stream) {
+hipError_t launch_tile_q40s(const uint16_t* src, uint16_t* dst, int N, int K, hipStream_t stream) {
   if (N % 16 || K % 256) return hipErrorInvalidValue;
   launch(tile_q40s_kernel, dim3(grid_for((size_t)N * (K / 32), 256)), dim3(256), 0, stream, src, dst, N, K);
   return hipGetLastError();

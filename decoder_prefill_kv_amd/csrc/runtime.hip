@@ -219,7 +219,7 @@ ScratchLayout scratch_layout(const dpk_config& c) {
 size_t tiled_bytes(const dpk_config& c, size_t rows, size_t cols) {
   if (c.weight_format == DPK_FMT_I8) return up(rows * cols);  // int8 codes
   if (c.weight_format == DPK_FMT_Q8) return up(rows * cols) + up(rows * (cols / 32) * 4);  // codes + block scales
-  if (c.weight_format == DPK_FMT_Q40) return up(rows * cols / 2) + up(rows * (cols / 32) * 4);
+  if (c.weight_format == DPK_FMT_Q40) return up(rows * cols / 2) + up(rows * (cols / 32) * 2);  // + fp16 scales
   if (c.weight_format == DPK_FMT_BF16) return up(rows * cols * 2);
   return up(rows * cols / 2) + up(rows * (cols / 64) * 4);  // codes + (s, b) pairs
 }
@@ -1386,13 +1386,13 @@ dpk_status dpk_load_weights(dpk_model* md, const dpk_tensor* t, int32_t n, void*
     // fragment-order decode copies
     auto tile = [&](LinearW& w) -> hipError_t {
       w.wt = p;
-      if (fmt == DPK_FMT_Q40) {  // codes + block scales (widened to fp32)
+      if (fmt == DPK_FMT_Q40) {  // codes + block scales (fp16)
         p += up((size_t)w.rows * w.cols / 2);
         const hipError_t e = launch_tile_q40((const uint8_t*)w.w, (uint32_t*)w.wt, w.rows, w.cols, st);
         if (e != hipSuccess) return e;
         w.sbt = p;
-        p += up((size_t)w.rows * (w.cols / 32) * 4);
-        return launch_tile_q40s((const uint16_t*)w.sf, (float*)w.sbt, w.rows, w.cols, st);
+        p += up((size_t)w.rows * (w.cols / 32) * 2);
+        return launch_tile_q40s((const uint16_t*)w.sf, (uint16_t*)w.sbt, w.rows, w.cols, st);
       }
       if (fmt == DPK_FMT_I8 || fmt == DPK_FMT_Q8) {  // codes (+ q8 block scales); i8 row scales are read as given
         p += up((size_t)w.rows * w.cols);

@@ -118,6 +118,7 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(SkinnyArgs a) {
   constexpr bool BLK = FMT == W_Q8 || FMT == W_Q40;                   // a scale per 32 columns
   constexpr int TB = FMT == W_Q40 ? 2048 : 4096;  // code bytes per 16-row tile and 256 columns
   constexpr float OFF = FMT == W_Q40 ? 1032.0f : 1152.0f;  // the codes' fp16 value minus the weight's code
+  constexpr int SB = FMT == W_Q40 ? 2 : 4;  // bytes per block scale in the fragment-order copy
   const int nbk = kchunk / 32;  // int8 formats: blocks of 32 columns in the chunk
   const int r16 = lane & 15;    // A row / B column / D column
   const int j4 = lane >> 4;     // k group of 8
@@ -136,8 +137,10 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(SkinnyArgs a) {
       wrow[t] = (const unsigned char*)a.w[seg] + (size_t)srow * (a.K / 2) + k0 / 2;
     else if (I8F) {  // fragment-order codes: this tile's 4 / 2 KB per 256 columns, this lane's 16 bytes
       wrow[t] = (const unsigned char*)a.w[seg] + ((size_t)(srow >> 4) * (a.K / 256) + k0 / 256) * TB + lane * 16;
-      if (BLK)  // fragment-order block scales: 512 bytes per tile and 256 columns, row r16's 8 at r16 * 32
-        srow_sf[t] = (const unsigned char*)a.sf[seg] + ((size_t)(srow >> 4) * (a.K / 256) + k0 / 256) * 512 + r16 * 32;
+      if (BLK)  // fragment-order block scales per tile and 256 columns, row r16's 8: Q8 fp32 (512 bytes,
+                // at r16 * 32), Q4_0 fp16 (256 bytes, at r16 * 16)
+        srow_sf[t] = (const unsigned char*)a.sf[seg] + ((size_t)(srow >> 4) * (a.K / 256) + k0 / 256) * (SB * 128) +
+                     r16 * (SB * 8);
     } else
       wrow[t] = (const unsigned char*)a.w[seg] + (size_t)srow * a.K * 2 + (size_t)k0 * 2;
   }
@@ -153,8 +156,8 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(SkinnyArgs a) {
       for (int p = 0; p < TB / 1024; ++p)
         wq[t][p] = __builtin_nontemporal_load((const u32x4*)(wrow[t] + kk * (TB / 256) + p * 1024));
       if constexpr (BLK) {
-        sq[t][0] = __builtin_nontemporal_load((const u32x4*)(srow_sf[t] + kk * 2));
-        sq[t][1] = __builtin_nontemporal_load((const u32x4*)(srow_sf[t] + kk * 2 + 16));
+        sq[t][0] = __builtin_nontemporal_load((const u32x4*)(srow_sf[t] + kk * SB / 2));
+        if constexpr (SB == 4) sq[t][1] = __builtin_nontemporal_load((const u32x4*)(srow_sf[t] + kk * 2 + 16));
       }
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of what follows
@@ -362,7 +365,13 @@ __global__ __launch_bounds__(THREADS) void skinny_kernel(SkinnyArgs a) {
             // block scale of the lane's weight row
             f32x4 ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(Xh, B, c0, 0, 0, 0);
             ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(Xl, B, ag, 0, 0, 0);
-            const float sb = __uint_as_float(sq[t][s >> 2][s & 3]);
+            float sb;
+            if constexpr (SB == 4) {
+              sb = __uint_as_float(sq[t][s >> 2][s & 3]);
+            } else {  // (fp16: half s % 2 of word s / 2)
+              const uint32_t wd = sq[t][0][s >> 1];
+              sb = (float)__builtin_bit_cast(_Float16, (uint16_t)((s & 1) ? (wd >> 16) : (wd & 0xFFFFu)));
+            }
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[t][v] += sb * ag[v];
           } else {

@@ -84,9 +84,9 @@ def test_int8_code_formats_prep_holds_fp16_operands_and_fragment_order_codes(dpk
     try:
         kv, sc, pr = dpk.workspace_size(h)
         per_layer = 4096 * 1024 + 1024 * 2048 + 2 * 3072 * 1024 + 1024 * 3072  # weights
-        # q8 / q4_0: and a fragment-order copy of the block scales (fp32, 4 bytes per 32 weights);
+        # q8 / q4_0: and a fragment-order copy of the block scales (4 / 2 bytes per 32 weights);
         # q4_0 codes take half a byte
-        per_w = {"FMT_I8": 1, "FMT_Q8": 1 + 4 / 32, "FMT_Q40": 0.5 + 4 / 32}[fmt]
+        per_w = {"FMT_I8": 1, "FMT_Q8": 1 + 4 / 32, "FMT_Q40": 0.5 + 2 / 32}[fmt]
         assert pr == 2 * (per_layer * 2 + per_layer * per_w) + 151936 * 1024 * per_w
         assert kv == 2 * 2 * 2 * 8 * 640 * 128 * 2
     finally:
