@@ -973,11 +973,18 @@ __global__ __launch_bounds__(MT, 1) void decode_step_kernel(MegaArgs a) {
 #ifdef DPK_DECODE_STEP_KV8_TU
 }  // namespace
 
-// The variants over an int8 KV cache (256 columns per iteration): bf16 with
+// The variants over an int8 KV cache: at 256 columns per iteration bf16 with
 // the fused O projection, int8 weights (one scale per row), Q8 and Q4_0
-// weights, G = 1, 2, 4.
+// weights, G = 1, 2, 4; at 128 columns bf16 and MLX 4-bit, G = 2, 4.
 const void* mega_kernel_kv8(int G, int fmt, bool small, bool fo) {
-  if (small) return nullptr;
+  if (small) {  // 128 columns per iteration: bf16 and MLX 4-bit, G = 2, 4, the O projection a GEMV
+    if (fo) return nullptr;
+    if (fmt == W_BF16 && G == 2) return (const void*)decode_step_kernel<2, W_BF16, true, false, true>;
+    if (fmt == W_BF16 && G == 4) return (const void*)decode_step_kernel<4, W_BF16, true, false, true>;
+    if (fmt == W_Q4 && G == 2) return (const void*)decode_step_kernel<2, W_Q4, true, false, true>;
+    if (fmt == W_Q4 && G == 4) return (const void*)decode_step_kernel<4, W_Q4, true, false, true>;
+    return nullptr;
+  }
   if (fmt == W_BF16 && fo) {
     if (G == 1) return (const void*)decode_step_kernel<1, W_BF16, false, true, true>;
     if (G == 2) return (const void*)decode_step_kernel<2, W_BF16, false, true, true>;

@@ -86,6 +86,10 @@ CASES = [
     ("q8b_q8-L2-v4096-persistent", synth.Q8B_Q8.with_(n_layers=2, vocab=4096), 250, 8, dict(max_rows=256)),
     ("q8b_q8-kvi8-L2-v4096-persistent", synth.Q8B_Q8.with_(n_layers=2, vocab=4096, kv_i8=True), 250, 8,
      dict(max_rows=256)),
+    # the 128-column persistent step over the int8 cache (0.6B shapes, bf16 and
+    # MLX 4-bit), contexts of three attention chunks
+    ("q06b-kvi8-L2-persistent-ctx600", synth.Q06B.with_(n_layers=2, kv_i8=True), 590, 8, dict(max_rows=256)),
+    ("q06b_q4-kvi8-L2-persistent-ctx600", synth.Q06B_Q4.with_(n_layers=2, kv_i8=True), 590, 8, dict(max_rows=256)),
     # the int8 cache at a long context in the persistent step: 16 attention
     # chunks per (row, KV head) and their merge
     ("q8b-kvi8-L1-v4096-ctx4100", synth.Q8B.with_(n_layers=1, vocab=4096, kv_i8=True), 4080, 4,
@@ -186,7 +190,7 @@ PATH_CASES = [
     ("q06b_i8-L1", synth.Q06B_I8.with_(n_layers=1), False),
     ("q06b_q8-L1", synth.Q06B_Q8.with_(n_layers=1), False),
     ("q06b_q40-L1", synth.Q06B_Q40.with_(n_layers=1), False),
-    ("q06b-kvi8-L1", synth.Q06B.with_(n_layers=1, kv_i8=True), False),
+    ("q06b-kvi8-L1", synth.Q06B.with_(n_layers=1, kv_i8=True), True),
     ("q8b-kvi8-L1-v4096", synth.Q8B.with_(n_layers=1, vocab=4096, kv_i8=True), True),
     ("q8b_i8-kvi8-L1-v4096", synth.Q8B_I8.with_(n_layers=1, vocab=4096, kv_i8=True), True),
     ("q8b_q40-L1-v4096", synth.Q8B_Q40.with_(n_layers=1, vocab=4096), True),
