@@ -29,38 +29,38 @@ MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 matrix throughput
 # (--copy-probe): FETCH_SIZE x 2.0, WRITE_SIZE x 1.0.  A figure is only
 # reported while the kernel's sources are the ones it was taken on.
 TRAFFIC = {
-    ("q8b", "decode.step"): {"fetch_kib": 7564262.2, "write_kib": 50617.4, "fetch_factor": 2.0, "write_factor": 1.0,
+    ("q8b", "decode.step"): {"fetch_kib": 7563807.7, "write_kib": 50617.4, "fetch_factor": 2.0, "write_factor": 1.0,
                              "sources": ["decoder_prefill_kv_amd/csrc/decode_step.hip",
                                          "decoder_prefill_kv_amd/csrc/gemv_body.h",
                                          "decoder_prefill_kv_amd/csrc/common.h",
                                          "decoder_prefill_kv_amd/csrc/kernels.h"],
-                             "sha256": "212dea11b5b1a96a50e615972a01152afb8b5188ebfb41ebb412ef6c38db2cd0"},
+                             "sha256": "f2cb8946b099d6d586e5a6d70c67de03aa622fac7dd0567e7a091f16a2995818"},
     # the same step over the int8 cache and with integer-code weights
-    ("q8b+kv_i8", "decode.step"): {"fetch_kib": 7500119.2, "write_kib": 50599.4, "fetch_factor": 2.0, "write_factor": 1.0,
+    ("q8b+kv_i8", "decode.step"): {"fetch_kib": 7500108.5, "write_kib": 50599.4, "fetch_factor": 2.0, "write_factor": 1.0,
                              "sources": ["decoder_prefill_kv_amd/csrc/decode_step.hip", "decoder_prefill_kv_amd/csrc/gemv_body.h",
                               "decoder_prefill_kv_amd/csrc/common.h", "decoder_prefill_kv_amd/csrc/kernels.h"],
-                             "sha256": "212dea11b5b1a96a50e615972a01152afb8b5188ebfb41ebb412ef6c38db2cd0"},
-    ("q8b_i8", "decode.step"): {"fetch_kib": 3874079.6, "write_kib": 14347.1, "fetch_factor": 2.0, "write_factor": 1.0,
+                             "sha256": "f2cb8946b099d6d586e5a6d70c67de03aa622fac7dd0567e7a091f16a2995818"},
+    ("q8b_i8", "decode.step"): {"fetch_kib": 3874082.5, "write_kib": 14347.1, "fetch_factor": 2.0, "write_factor": 1.0,
                              "sources": ["decoder_prefill_kv_amd/csrc/decode_step.hip", "decoder_prefill_kv_amd/csrc/gemv_body.h",
                               "decoder_prefill_kv_amd/csrc/common.h", "decoder_prefill_kv_amd/csrc/kernels.h"],
-                             "sha256": "212dea11b5b1a96a50e615972a01152afb8b5188ebfb41ebb412ef6c38db2cd0"},
-    ("q8b_q8", "decode.step"): {"fetch_kib": 4486667.4, "write_kib": 14347.1, "fetch_factor": 2.0, "write_factor": 1.0,
+                             "sha256": "f2cb8946b099d6d586e5a6d70c67de03aa622fac7dd0567e7a091f16a2995818"},
+    ("q8b_q8", "decode.step"): {"fetch_kib": 4486450.6, "write_kib": 14347.1, "fetch_factor": 2.0, "write_factor": 1.0,
                              "sources": ["decoder_prefill_kv_amd/csrc/decode_step.hip", "decoder_prefill_kv_amd/csrc/gemv_body.h",
                               "decoder_prefill_kv_amd/csrc/common.h", "decoder_prefill_kv_amd/csrc/kernels.h"],
-                             "sha256": "212dea11b5b1a96a50e615972a01152afb8b5188ebfb41ebb412ef6c38db2cd0"},
-    ("q8b_q40", "decode.step"): {"fetch_kib": 2258004.6, "write_kib": 14347.1, "fetch_factor": 2.0, "write_factor": 1.0,
+                             "sha256": "f2cb8946b099d6d586e5a6d70c67de03aa622fac7dd0567e7a091f16a2995818"},
+    ("q8b_q40", "decode.step"): {"fetch_kib": 2258180.2, "write_kib": 14347.1, "fetch_factor": 2.0, "write_factor": 1.0,
                              "sources": ["decoder_prefill_kv_amd/csrc/decode_step.hip", "decoder_prefill_kv_amd/csrc/gemv_body.h",
                               "decoder_prefill_kv_amd/csrc/common.h", "decoder_prefill_kv_amd/csrc/kernels.h"],
-                             "sha256": "212dea11b5b1a96a50e615972a01152afb8b5188ebfb41ebb412ef6c38db2cd0"},
+                             "sha256": "f2cb8946b099d6d586e5a6d70c67de03aa622fac7dd0567e7a091f16a2995818"},
     # the 0.6B-shaped steps (128 columns per wave and iteration; bf16, MLX 4-bit)
-    ("q06b", "decode.step"): {"fetch_kib": 618285.7, "write_kib": 4896.1, "fetch_factor": 2.0, "write_factor": 1.0,
+    ("q06b", "decode.step"): {"fetch_kib": 618300.4, "write_kib": 4896.1, "fetch_factor": 2.0, "write_factor": 1.0,
                              "sources": ["decoder_prefill_kv_amd/csrc/decode_step.hip", "decoder_prefill_kv_amd/csrc/gemv_body.h",
                               "decoder_prefill_kv_amd/csrc/common.h", "decoder_prefill_kv_amd/csrc/kernels.h"],
-                             "sha256": "212dea11b5b1a96a50e615972a01152afb8b5188ebfb41ebb412ef6c38db2cd0"},
-    ("q06b_q4", "decode.step"): {"fetch_kib": 287341.5, "write_kib": 6492.1, "fetch_factor": 2.0, "write_factor": 1.0,
+                             "sha256": "f2cb8946b099d6d586e5a6d70c67de03aa622fac7dd0567e7a091f16a2995818"},
+    ("q06b_q4", "decode.step"): {"fetch_kib": 287342.3, "write_kib": 6492.1, "fetch_factor": 2.0, "write_factor": 1.0,
                              "sources": ["decoder_prefill_kv_amd/csrc/decode_step.hip", "decoder_prefill_kv_amd/csrc/gemv_body.h",
                               "decoder_prefill_kv_amd/csrc/common.h", "decoder_prefill_kv_amd/csrc/kernels.h"],
-                             "sha256": "212dea11b5b1a96a50e615972a01152afb8b5188ebfb41ebb412ef6c38db2cd0"},
+                             "sha256": "f2cb8946b099d6d586e5a6d70c67de03aa622fac7dd0567e7a091f16a2995818"},
     # the prefill gate+up GEMM (M = 2048): operands re-read from HBM ~3.5x
     ("q8b", "gemm.gate_up"): {"fetch_kib": 380246.7, "write_kib": 57600.4, "fetch_factor": 2.0, "write_factor": 1.0,
                               "sources": ["decoder_prefill_kv_amd/csrc/gemm.hip",
